@@ -184,17 +184,21 @@ def unpermute_reduce(Y: np.ndarray, slot_to_row: np.ndarray, w: np.ndarray) -> n
 def fp8_roundtrip_bf16(x: np.ndarray) -> np.ndarray:
     """FP8 E4M3 activations dequantized to bf16 (per-tensor scale), float64 result.
 
-    s_a = fp32(amax / 448) (1 if amax == 0); c = E4M3_RNE(min(|fp32(x / s_a)|, 448))
-    with the sign of x; x' = bf16(fp32(E4M3[c] * s_a)).
+    s_a = fp32(amax / 448) with amax over the finite entries (1 if that amax is 0);
+    c = E4M3_RNE(min(|fp32(x / s_a)|, 448)) with the sign of x (so +-Inf saturates
+    to +-448); x' = bf16(fp32(E4M3[c] * s_a)); NaN stays NaN.
     """
     x = np.asarray(x, dtype=np.float32)
-    amax = np.float32(np.abs(x).max()) if x.size else np.float32(0)
+    fin = np.abs(x[np.isfinite(x)])
+    amax = np.float32(fin.max()) if fin.size else np.float32(0)
     s_a = np.float32(1.0) if amax == 0 else np.float32(amax / np.float32(nvfp4.E4M3_MAX))
-    r = (x / s_a).astype(np.float32)
-    mag = nvfp4.e4m3_rne(np.minimum(np.abs(r), np.float32(nvfp4.E4M3_MAX)))
+    with np.errstate(invalid="ignore"):
+        r = (x / s_a).astype(np.float32)
+    mag = nvfp4.e4m3_rne(np.minimum(np.abs(np.nan_to_num(r, nan=0.0)), np.float32(nvfp4.E4M3_MAX)))
     v = np.where(np.signbit(r), -1.0, 1.0) * nvfp4.E4M3_TABLE[mag]
     prod = (v.astype(np.float32) * s_a).astype(np.float32)
-    return bf16_round(prod.astype(np.float64))
+    out = bf16_round(prod.astype(np.float64))
+    return np.where(np.isnan(x), np.nan, out)
 
 
 def quantize_rows_nvfp4(x: np.ndarray, g=None):

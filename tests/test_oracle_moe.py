@@ -222,3 +222,10 @@ def test_fp8_roundtrip_matches_torch_cast_path():
     q = (xt / s).clamp(-448, 448).to(torch.float8_e4m3fn).float()
     ref = (q * s).to(torch.bfloat16).double().numpy()
     np.testing.assert_array_equal(got, ref)
+
+
+def test_fp8_roundtrip_nonfinite_inputs():
+    x = np.array([[1.0, -2.0, np.inf, np.nan, -np.inf, 0.5]], dtype=np.float32)
+    got = moe.fp8_roundtrip_bf16(x)
+    assert got[0, 1] == -2.0 and got[0, 2] == 2.0 and got[0, 4] == -2.0   # +-Inf saturate to +-448 * s_a
+    assert np.isnan(got[0, 3]) and got[0, 0] == 1.0 and got[0, 5] == 0.5
