@@ -1,0 +1,223 @@
+/*
+ * nvfp4moe.h -- C ABI of libnvfp4moe.so, the NVFP4 block-scaled mixture-of-experts
+ * hot path for AMD Instinct MI355X (gfx950).
+ *
+ * The layer this library computes, one call per stage:
+ *
+ *   logits --moe_route_permute--> top-k ids/weights, per-expert row offsets, permutation
+ *   x      --moe_grouped_gemm_nvfp4(EPI_SWIGLU)--> h = silu(x W_gate^T) * (x W_up^T)  per expert
+ *   h      --moe_grouped_gemm_nvfp4(EPI_NONE)  --> Y = h W_down^T                    per expert
+ *   Y      --moe_unpermute_reduce--> out[t] = sum_j w[t,j] * Y[row of slot (t,j)]
+ *
+ * plus nvfp4_quantize (weights offline; W4A4 activations and h per forward) and
+ * act_fp8_e4m3_roundtrip (FP8 E4M3 activations dequantized to bf16).
+ *
+ * Sources for what is computed (web pages; section names):
+ *   [P1] "Native FP4 Is Slower Than Emulated FP4: A Kernel-Maturity Measurement on
+ *        First-Generation Workstation Blackwell", section 1 (512 experts, 22 active;
+ *        NVFP4 = FP4 weights with FP8 activations).
+ *   [P2] "The Benchmark That Confirmed the Ceiling: NVFP4 Cutlass on sm_120",
+ *        section "The NVFP4 Pivot" (NVFP4 = FP4 values, one E4M3 scale per 16;
+ *        W4A16 = dequantize FP4 to 16-bit and multiply; W4A4 = FP4 x FP4) and
+ *        section "Roofline Awareness" (half a byte per FP4 parameter).
+ *   [P3] "The 2x Gap: Diagnosing Suboptimal FP4 GEMM Kernels on Blackwell SM120",
+ *        sections "The Investigation So Far" (256 experts, top-8, ~16 tokens per
+ *        expert at decode) and "Discovering the sgl_kernel Alternative" (a scaled
+ *        FP4 GEMM takes two FP4-packed operands, their block scales, an alpha and an
+ *        output dtype; a fused MoE gathers tokens to experts and scatters them back).
+ *   [P4] "The 24% Ceiling: Diagnosing the Limits of NVFP4 Quantization on Blackwell
+ *        SM120 GPUs", sections "The Core Insight" and "The Decision" (W4A16 versus
+ *        true W4A4 grouped GEMM for the MoE).
+ *
+ * NVFP4 storage of a matrix [R, C] (groups of 16 along C, the GEMM's K):
+ *   packed  uint8 [R, C/2]   E2M1 codes, element 2i in the LOW nibble of byte i
+ *   scales  uint8 [R, C/16]  OCP E4M3FN codes (bias 7, NaN = 0x7F/0xFF, max 448)
+ *   g       float32          per-tensor scale; value = E2M1[q] * E4M3[s] * g
+ * A batch of B matrices is stored back to back ([B, R, C/2], [B, R, C/16], g[B]).
+ *
+ * Conventions shared by every call:
+ *   - Every tensor pointer is DEVICE memory owned by the caller; the library
+ *     allocates nothing. Scratch memory comes in through (ws, ws_bytes); its size
+ *     is given by the matching *_workspace_size query and it need not be zeroed.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = default stream) and
+ *     never synchronize the device. Outputs are valid once the stream reaches them.
+ *   - Arguments are validated on the host before any HIP call. A bad argument
+ *     returns NVFP4MOE_ERR_INVALID_ARG (a too-small workspace NVFP4MOE_ERR_WORKSPACE)
+ *     and launches nothing; a failed launch returns NVFP4MOE_ERR_HIP. The message is
+ *     available from nvfp4moe_last_error() on the calling thread. There is no
+ *     fallback path: a call either runs its kernels or reports why not.
+ *   - Results are deterministic: the same inputs give the same bytes (no
+ *     order-dependent floating-point atomics anywhere).
+ *   - Data-dependent sizes (rows per expert, active experts) stay on the device;
+ *     the host passes only upper bounds.
+ *   - The library keeps no state besides the thread-local error message and the
+ *     last dispatch code; concurrent calls on different streams are safe.
+ */
+#ifndef NVFP4MOE_H
+#define NVFP4MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  NVFP4MOE_OK = 0,
+  NVFP4MOE_ERR_INVALID_ARG = 1,
+  NVFP4MOE_ERR_UNSUPPORTED = 2,
+  NVFP4MOE_ERR_WORKSPACE = 3,
+  NVFP4MOE_ERR_HIP = 4
+} nvfp4moe_status;
+
+/* [P2] "The NVFP4 Pivot", [P4] "The Decision": weight-only FP4 with 16-bit
+ * activations, or FP4 weights and FP4 activations. */
+typedef enum { NVFP4MOE_W4A16 = 0, NVFP4MOE_W4A4 = 1 } nvfp4moe_mode;
+
+typedef enum { NVFP4MOE_EPI_NONE = 0, NVFP4MOE_EPI_SWIGLU = 1 } nvfp4moe_epilogue;
+
+typedef enum { NVFP4MOE_F32 = 0, NVFP4MOE_BF16 = 1 } nvfp4moe_dtype;
+
+/* Kernel family chosen by the last moe_grouped_gemm_nvfp4 call on this thread. */
+typedef enum {
+  NVFP4MOE_PATH_NONE = 0,
+  NVFP4MOE_PATH_STREAM = 1, /* small-M weight-streaming kernel (HBM-bound regime)   */
+  NVFP4MOE_PATH_MFMA = 2    /* large-M LDS-tiled MFMA kernel (compute-bound regime) */
+} nvfp4moe_path;
+
+/* ---------------------------------------------------------------------------
+ * nvfp4_quantize -- quantize B float matrices [R, C] to NVFP4.  [P2] "The NVFP4 Pivot".
+ *
+ *   x        device, x_dtype (F32 or BF16), [B, R, C] row-major.
+ *   B, R, C  1 <= B <= 65535, R >= 1, C >= 32 and C % 32 == 0; x 16-byte aligned,
+ *            packed 16-byte aligned, scales 2-byte aligned.
+ *   g_in     device float[B] or NULL. If given, used as the global scales.
+ *   amax_in  device float[B] or NULL. If g_in is NULL and amax_in is given,
+ *            g[b] = amax_in[b] / 2688 (or 1 when amax_in[b] == 0); amax_in must be
+ *            the max |x| over the finite entries of matrix b.
+ *            If both are NULL, the amax is computed on the device.
+ *   packed   device uint8 [B, R, C/2]  (output)
+ *   scales   device uint8 [B, R, C/16] (output)
+ *   g_out    device float[B]           (output) the global scales used.
+ *   ws       workspace of nvfp4_quantize_workspace_size(B, R, C) bytes.
+ *
+ * Rule, in float32 with round-to-nearest-even (all steps on the device):
+ *   g = amax / 2688 (2688 = 6 * 448; 1 if amax == 0);
+ *   per 16-group: a NaN/Inf in the group -> scale 0x7F and codes 0;
+ *                 amax_g == 0 -> scale 0, codes +-0;
+ *                 else s = E4M3(min(amax_g / (6 g), 448)), S = E4M3[s] * g,
+ *                      q_i = E2M1(w_i / S) saturating at 6, sign bit from w_i.
+ * ------------------------------------------------------------------------- */
+nvfp4moe_status nvfp4_quantize(const void* x, nvfp4moe_dtype x_dtype, int64_t B, int64_t R,
+                               int64_t C, const float* g_in, const float* amax_in,
+                               uint8_t* packed, uint8_t* scales, float* g_out, void* ws,
+                               size_t ws_bytes, void* stream);
+size_t nvfp4_quantize_workspace_size(int64_t B, int64_t R, int64_t C);
+
+/* ---------------------------------------------------------------------------
+ * moe_route_permute -- router + histogram + stable permutation.
+ * [P3] "The Investigation So Far" (top-8 of 256), [P1] section 1 (top-22 of 512),
+ * [P3] "Discovering the sgl_kernel Alternative" (expert scatter/gather).
+ *
+ *   logits          device float [T, E], finite.
+ *   T, E, k         1 <= T, 1 <= k <= min(E, 64), E <= 1024, T * k <= 2^24.
+ *   topk_ids        device int32 [T, k]  (output) experts by descending logit, ties to
+ *                   the lower id.
+ *   topk_w          device float [T, k]  (output) softmax over E, renormalised over the
+ *                   k kept experts (computed in float64, stored as float32).
+ *   expert_offsets  device int32 [E + 1] (output) exclusive prefix sum of rows per expert.
+ *   sorted_slot     device int32 [T * k] (output) row r holds slot s = t * k + j; rows of
+ *                   one expert keep ascending slot order (stable counting sort).
+ *   slot_to_row     device int32 [T * k] (output) inverse of sorted_slot.
+ *   active_experts  device int32 [E]     (output) experts with >= 1 row, ascending, in
+ *                   entries [0, n_active); the rest are set to -1.
+ *   n_active        device int32 [1]     (output)
+ *   ws, ws_bytes    moe_route_permute_workspace_size(T, E, k) bytes (currently 0).
+ * ------------------------------------------------------------------------- */
+nvfp4moe_status moe_route_permute(const float* logits, int32_t T, int32_t E, int32_t k,
+                                  int32_t* topk_ids, float* topk_w, int32_t* expert_offsets,
+                                  int32_t* sorted_slot, int32_t* slot_to_row,
+                                  int32_t* active_experts, int32_t* n_active, void* ws,
+                                  size_t ws_bytes, void* stream);
+size_t moe_route_permute_workspace_size(int32_t T, int32_t E, int32_t k);
+
+/* ---------------------------------------------------------------------------
+ * moe_grouped_gemm_nvfp4 -- per expert e, rows expert_offsets[e] .. expert_offsets[e+1]:
+ *     P = A_rows . W_e^T  (float32 accumulation of exact products) * w_g[e] (* a_g[0])
+ *     EPI_NONE  : out = P                                  [rows, Nw]
+ *     EPI_SWIGLU: out = silu(P[:, :Nw/2]) * P[:, Nw/2:]    [rows, Nw/2]
+ * [P3] "Discovering the sgl_kernel Alternative" (operands, block scales, alpha, out
+ * dtype), [P2] "The NVFP4 Pivot" and [P4] "The Decision" (W4A16 / W4A4).
+ *
+ *   mode        W4A16: a is bf16 [a_rows, K]; a_scales and a_g are ignored (may be NULL).
+ *               W4A4 : a is NVFP4 packed uint8 [a_rows, K/2] with a_scales uint8
+ *                      [a_rows, K/16] and a_g device float[1].
+ *   a_rows      rows of a.
+ *   gather_index, gather_div
+ *               NULL: GEMM row r reads a row r (a_rows must equal rows).
+ *               else: GEMM row r reads a row gather_index[r] / gather_div, e.g.
+ *                     sorted_slot with gather_div = k to gather token rows.
+ *   w_packed    device uint8 [E, Nw, K/2]; w_scales uint8 [E, Nw, K/16]; w_g float [E].
+ *   expert_offsets, active_experts, n_active  as written by moe_route_permute (for a
+ *               dense GEMM: E = 1, offsets {0, rows}, active {0}, n_active {1}).
+ *   E, rows, Nw, K  1 <= E <= 1024; rows = expert_offsets[E] >= 1; Nw >= 32, Nw % 32 == 0
+ *               (EPI_SWIGLU: gate rows 0..Nw/2-1, up rows Nw/2..Nw-1); K >= 32, K % 32 == 0;
+ *               rows * max(K, Nw) < 2^31. a and w_packed 16-byte aligned, scale arrays
+ *               2-byte aligned.
+ *   out         device, out_dtype (F32 or BF16), [rows, EPI_SWIGLU ? Nw/2 : Nw].
+ *   out_amax    device float[1] or NULL: if given, set to max |out| over the call (exact;
+ *               used to pick the global scale when out is quantized next).
+ *   ws          moe_grouped_gemm_workspace_size(mode, a_rows, rows, E, Nw, K) bytes.
+ * ------------------------------------------------------------------------- */
+nvfp4moe_status moe_grouped_gemm_nvfp4(nvfp4moe_mode mode, nvfp4moe_epilogue epi,
+                                       const void* a, const uint8_t* a_scales, const float* a_g,
+                                       int64_t a_rows, const int32_t* gather_index,
+                                       int32_t gather_div, const uint8_t* w_packed,
+                                       const uint8_t* w_scales, const float* w_g,
+                                       const int32_t* expert_offsets,
+                                       const int32_t* active_experts, const int32_t* n_active,
+                                       int32_t E, int32_t rows, int32_t Nw, int32_t K, void* out,
+                                       nvfp4moe_dtype out_dtype, float* out_amax, void* ws,
+                                       size_t ws_bytes, void* stream);
+size_t moe_grouped_gemm_workspace_size(nvfp4moe_mode mode, int64_t a_rows, int32_t rows,
+                                       int32_t E, int32_t Nw, int32_t K);
+
+/* ---------------------------------------------------------------------------
+ * moe_unpermute_reduce -- out[t, :] = bf16( sum_{j<k} topk_w[t, j] * y[slot_to_row[t*k+j], :] )
+ * accumulated in float32 in ascending j. [P3] "Discovering the sgl_kernel Alternative"
+ * (results scattered back from the experts to the tokens).
+ *
+ *   y           device, y_dtype (F32 or BF16), [T * k, H].
+ *   slot_to_row device int32 [T * k]; topk_w device float [T, k].
+ *   T, k, H     T >= 1, k >= 1, H >= 8, H % 8 == 0, T * k * H < 2^31; y, out 16-byte aligned.
+ *   out         device bf16 [T, H].
+ * ------------------------------------------------------------------------- */
+nvfp4moe_status moe_unpermute_reduce(const void* y, nvfp4moe_dtype y_dtype,
+                                     const int32_t* slot_to_row, const float* topk_w, int32_t T,
+                                     int32_t k, int32_t H, void* out, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * act_fp8_e4m3_roundtrip -- FP8 E4M3 activations dequantized to bf16, per-tensor scale.
+ * [P1] section 1 ("FP4 weights with FP8 activations").
+ *   s_a = amax(|x|) / 448 (1 if amax == 0);  out = bf16( E4M3(min(|x / s_a|, 448)) * s_a )
+ *   with the sign of x (float32 steps, round-to-nearest-even).
+ *   x, out   device bf16 [n], 16-byte aligned (may alias); n >= 8, n % 8 == 0.
+ *   ws       act_fp8_e4m3_roundtrip_workspace_size(n) bytes.
+ * ------------------------------------------------------------------------- */
+nvfp4moe_status act_fp8_e4m3_roundtrip(const void* x, int64_t n, void* out, void* ws,
+                                       size_t ws_bytes, void* stream);
+size_t act_fp8_e4m3_roundtrip_workspace_size(int64_t n);
+
+/* Thread-local message describing the last non-OK status ("" if none). Never NULL. */
+const char* nvfp4moe_last_error(void);
+/* nvfp4moe_path of the last moe_grouped_gemm_nvfp4 call on this thread. */
+int nvfp4moe_last_dispatch(void);
+/* ABI version of this header (major * 100 + minor). */
+int nvfp4moe_abi_version(void);
+
+#ifdef __cplusplus
+} /* extern "C" */
+#endif
+
+#endif /* NVFP4MOE_H */

@@ -1,0 +1,77 @@
+// 16-bit activations for the f16 MFMA path (gfx950).
+//
+// W4A16 multiplies 16-bit activations by FP4 weights dequantized to 16 bits ("The 24%
+// Ceiling", section "The Core Insight"). gfx950 has no packed bf16 multiply, but it has
+// an exact, cheap NVFP4 -> f16 decode (one convert and one packed f16 multiply per two
+// weights), so the GEMMs run on f16 MFMA. bf16 activations have float32's exponent range
+// and f16 does not; each row is therefore scaled by a power of two 2^-p chosen so that
+// its largest finite magnitude lies in [2^14, 2^15). Scaling by a power of two and the
+// bf16 -> f16 conversion are exact for every value within 2^31 of the row maximum (f16
+// keeps 11 significant bits, bf16 has 8); the GEMM epilogue multiplies by 2^p again.
+// Non-finite values stay Inf/NaN.
+//
+// One workgroup per row: pass 1 finds the row's finite amax, pass 2 converts (the row is
+// re-read from L2). Traffic: 2 bytes read + 2 bytes written per element.
+#include "common.h"
+#include "kernels.h"
+
+namespace nvfp4moe {
+
+namespace {
+
+constexpr int kPrepThreads = 256;
+
+__global__ __launch_bounds__(kPrepThreads) void act_prep_kernel(const uint16_t* __restrict__ a,
+                                                                int K,
+                                                                _Float16* __restrict__ a16,
+                                                                int* __restrict__ rexp) {
+  const int64_t r = blockIdx.x;
+  const uint16_t* row = a + r * (int64_t)K;
+  _Float16* orow = a16 + r * (int64_t)K;
+  const int nvec = K / 8;
+  float m = 0.0f;
+  for (int i = threadIdx.x; i < nvec; i += kPrepThreads) {
+    uint4 q = *reinterpret_cast<const uint4*>(row + 8 * i);
+    uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float lo = fabsf(bf16_to_f32(w[j] & 0xffffu)), hi = fabsf(bf16_to_f32(w[j] >> 16));
+      m = fmaxf(m, lo <= 3.402823466e38f ? lo : 0.0f);
+      m = fmaxf(m, hi <= 3.402823466e38f ? hi : 0.0f);
+    }
+  }
+  __shared__ float red[kPrepThreads / kWave];
+  m = wave_max(m);
+  if ((threadIdx.x % kWave) == 0) red[threadIdx.x / kWave] = m;
+  __syncthreads();
+  float amax = red[0];
+  for (int w = 1; w < kPrepThreads / kWave; ++w) amax = fmaxf(amax, red[w]);
+  int p = 0;
+  if (amax > 0.0f) {
+    int ex;
+    (void)frexpf(amax, &ex);  // amax = f * 2^ex, f in [0.5, 1)
+    p = ex - 15;              // amax * 2^-p in [2^14, 2^15)
+  }
+  if (threadIdx.x == 0) rexp[r] = p;
+  for (int i = threadIdx.x; i < nvec; i += kPrepThreads) {
+    uint4 q = *reinterpret_cast<const uint4*>(row + 8 * i);
+    uint32_t w[4] = {q.x, q.y, q.z, q.w};
+    f16x8 o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      o[2 * j] = (_Float16)ldexpf(bf16_to_f32(w[j] & 0xffffu), -p);
+      o[2 * j + 1] = (_Float16)ldexpf(bf16_to_f32(w[j] >> 16), -p);
+    }
+    *reinterpret_cast<f16x8*>(orow + 8 * i) = o;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_act_prep(const uint16_t* a, int64_t rows, int K, _Float16* a16, int* rexp,
+                           hipStream_t stream) {
+  act_prep_kernel<<<(unsigned)rows, kPrepThreads, 0, stream>>>(a, K, a16, rexp);
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4moe

@@ -1,0 +1,295 @@
+// C ABI of libnvfp4moe (declared in include/nvfp4moe.h): argument validation on the host,
+// workspace carving, kernel-path dispatch, and status/error reporting. No call allocates
+// memory or synchronizes the device.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+
+#include "kernels.h"
+#include "nvfp4moe.h"
+
+using namespace nvfp4moe;
+
+namespace {
+
+thread_local std::string g_last_error;
+thread_local int g_last_dispatch = NVFP4MOE_PATH_NONE;
+
+nvfp4moe_status fail(nvfp4moe_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+nvfp4moe_status ok() {
+  g_last_error.clear();
+  return NVFP4MOE_OK;
+}
+
+nvfp4moe_status hip_status(hipError_t e, const char* where) {
+  if (e == hipSuccess) return ok();
+  return fail(NVFP4MOE_ERR_HIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+__global__ void zero_f32_kernel(float* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0.0f;
+}
+
+// Workspace layout of moe_grouped_gemm_nvfp4 (W4A16): f16 activations, row exponents.
+struct GemmWs {
+  size_t a16_bytes, rexp_bytes, total;
+};
+GemmWs gemm_ws_layout(nvfp4moe_mode mode, int64_t a_rows, int32_t K) {
+  GemmWs w{0, 0, 0};
+  if (mode == NVFP4MOE_W4A16) {
+    w.a16_bytes = round_up((size_t)a_rows * (size_t)K * 2);
+    w.rexp_bytes = round_up((size_t)a_rows * 4);
+  }
+  w.total = w.a16_bytes + w.rexp_bytes;
+  return w;
+}
+
+// Kernel path override for tests/measurement: NVFP4MOE_FORCE_PATH=stream|mfma.
+int forced_path() {
+  const char* s = std::getenv("NVFP4MOE_FORCE_PATH");
+  if (!s) return NVFP4MOE_PATH_NONE;
+  if (!std::strcmp(s, "stream")) return NVFP4MOE_PATH_STREAM;
+  if (!std::strcmp(s, "mfma")) return NVFP4MOE_PATH_MFMA;
+  return NVFP4MOE_PATH_NONE;
+}
+
+}  // namespace
+
+hipError_t nvfp4moe::launch_zero_f32(float* p, int n, hipStream_t stream) {
+  zero_f32_kernel<<<(n + 255) / 256, 256, 0, stream>>>(p, n);
+  return hipGetLastError();
+}
+
+extern "C" {
+
+const char* nvfp4moe_last_error(void) { return g_last_error.c_str(); }
+int nvfp4moe_last_dispatch(void) { return g_last_dispatch; }
+int nvfp4moe_abi_version(void) { return 100; }
+
+// ------------------------------------------------------------------ quantize
+size_t nvfp4_quantize_workspace_size(int64_t B, int64_t R, int64_t C) {
+  if (B < 1 || R < 1 || C < 1) return 0;
+  return round_up(quantize_ws_bytes(B, R, C));
+}
+
+nvfp4moe_status nvfp4_quantize(const void* x, nvfp4moe_dtype x_dtype, int64_t B, int64_t R,
+                               int64_t C, const float* g_in, const float* amax_in,
+                               uint8_t* packed, uint8_t* scales, float* g_out, void* ws,
+                               size_t ws_bytes, void* stream) {
+  if (!x || !packed || !scales || !g_out)
+    return fail(NVFP4MOE_ERR_INVALID_ARG, "nvfp4_quantize: null tensor pointer");
+  if (x_dtype != NVFP4MOE_F32 && x_dtype != NVFP4MOE_BF16)
+    return fail(NVFP4MOE_ERR_INVALID_ARG, "nvfp4_quantize: x_dtype must be F32 or BF16");
+  if (B < 1 || R < 1 || C < 32 || C % 32 != 0)
+    return fail(NVFP4MOE_ERR_INVALID_ARG,
+                "nvfp4_quantize: need B >= 1, R >= 1, C >= 32 and C %% 32 == 0 (B=%lld R=%lld C=%lld)",
+                (long long)B, (long long)R, (long long)C);
+  if (B > 65535 || (double)B * (double)R * (double)C > 4.0e12)
+    return fail(NVFP4MOE_ERR_INVALID_ARG, "nvfp4_quantize: tensor too large");
+  if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(scales, 2) || !aligned(g_out, 4))
+    return fail(NVFP4MOE_ERR_INVALID_ARG,
+                "nvfp4_quantize: x and packed must be 16-byte aligned, scales 2-byte aligned");
+  if (!g_in && !amax_in) {
+    const size_t need = nvfp4_quantize_workspace_size(B, R, C);
+    if (!ws || ws_bytes < need)
+      return fail(NVFP4MOE_ERR_WORKSPACE, "nvfp4_quantize: workspace of %zu bytes needed, %zu given",
+                  need, ws_bytes);
+  }
+  return hip_status(launch_quantize(x, x_dtype == NVFP4MOE_BF16, B, R, C, g_in, amax_in, packed,
+                                    scales, g_out, ws, static_cast<hipStream_t>(stream)),
+                    "nvfp4_quantize");
+}
+
+// ------------------------------------------------------------------ route + permute
+size_t moe_route_permute_workspace_size(int32_t T, int32_t E, int32_t k) {
+  (void)T;
+  (void)E;
+  (void)k;
+  return 0;
+}
+
+nvfp4moe_status moe_route_permute(const float* logits, int32_t T, int32_t E, int32_t k,
+                                  int32_t* topk_ids, float* topk_w, int32_t* expert_offsets,
+                                  int32_t* sorted_slot, int32_t* slot_to_row,
+                                  int32_t* active_experts, int32_t* n_active, void* ws,
+                                  size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  if (!logits || !topk_ids || !topk_w || !expert_offsets || !sorted_slot || !slot_to_row ||
+      !active_experts || !n_active)
+    return fail(NVFP4MOE_ERR_INVALID_ARG, "moe_route_permute: null tensor pointer");
+  if (T < 1 || E < 1 || E > kMaxExperts || k < 1 || k > E || k > kMaxTopK)
+    return fail(NVFP4MOE_ERR_INVALID_ARG,
+                "moe_route_permute: need T >= 1, 1 <= k <= min(E, %d), E <= %d (T=%d E=%d k=%d)",
+                kMaxTopK, kMaxExperts, T, E, k);
+  if ((int64_t)T * k > (1 << 24))
+    return fail(NVFP4MOE_ERR_INVALID_ARG, "moe_route_permute: T * k must be <= 2^24");
+  return hip_status(launch_route_permute(logits, T, E, k, topk_ids, topk_w, expert_offsets,
+                                         sorted_slot, slot_to_row, active_experts, n_active,
+                                         static_cast<hipStream_t>(stream)),
+                    "moe_route_permute");
+}
+
+// ------------------------------------------------------------------ grouped GEMM
+size_t moe_grouped_gemm_workspace_size(nvfp4moe_mode mode, int64_t a_rows, int32_t rows,
+                                       int32_t E, int32_t Nw, int32_t K) {
+  (void)rows;
+  (void)E;
+  (void)Nw;
+  if (a_rows < 1 || K < 1) return 0;
+  return gemm_ws_layout(mode, a_rows, K).total;
+}
+
+nvfp4moe_status moe_grouped_gemm_nvfp4(nvfp4moe_mode mode, nvfp4moe_epilogue epi,
+                                       const void* a, const uint8_t* a_scales, const float* a_g,
+                                       int64_t a_rows, const int32_t* gather_index,
+                                       int32_t gather_div, const uint8_t* w_packed,
+                                       const uint8_t* w_scales, const float* w_g,
+                                       const int32_t* expert_offsets,
+                                       const int32_t* active_experts, const int32_t* n_active,
+                                       int32_t E, int32_t rows, int32_t Nw, int32_t K, void* out,
+                                       nvfp4moe_dtype out_dtype, float* out_amax, void* ws,
+                                       size_t ws_bytes, void* stream) {
+  const char* fn = "moe_grouped_gemm_nvfp4";
+  if (mode != NVFP4MOE_W4A16 && mode != NVFP4MOE_W4A4)
+    return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: bad mode %d", fn, (int)mode);
+  if (epi != NVFP4MOE_EPI_NONE && epi != NVFP4MOE_EPI_SWIGLU)
+    return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: bad epilogue %d", fn, (int)epi);
+  if (out_dtype != NVFP4MOE_F32 && out_dtype != NVFP4MOE_BF16)
+    return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: out_dtype must be F32 or BF16", fn);
+  if (!a || !w_packed || !w_scales || !w_g || !expert_offsets || !active_experts || !n_active || !out)
+    return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: null tensor pointer", fn);
+  if (mode == NVFP4MOE_W4A4 && (!a_scales || !a_g))
+    return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: W4A4 needs a_scales and a_g", fn);
+  if (E < 1 || E > kMaxExperts)
+    return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: need 1 <= E <= %d (E=%d)", fn, kMaxExperts, E);
+  if (rows < 1 || a_rows < 1)
+    return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: need rows >= 1 and a_rows >= 1", fn);
+  if (Nw < 32 || Nw % 32 != 0)
+    return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: need Nw >= 32 and Nw %% 32 == 0 (Nw=%d)", fn, Nw);
+  if (K < 32 || K % 32 != 0)
+    return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: need K >= 32 and K %% 32 == 0 (K=%d)", fn, K);
+  if ((int64_t)rows * (K > Nw ? K : Nw) >= (int64_t(1) << 31))
+    return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: rows * max(K, Nw) must be < 2^31", fn);
+  if (a_rows * (int64_t)K >= (int64_t(1) << 40))
+    return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: a_rows * K too large", fn);
+  if (!gather_index && a_rows != rows)
+    return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: without gather_index a_rows must equal rows", fn);
+  if (gather_index && gather_div < 1)
+    return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: gather_div must be >= 1", fn);
+  if (!aligned(a, 16) || !aligned(w_packed, 16) || !aligned(w_scales, 2) ||
+      (a_scales && !aligned(a_scales, 2)) || !aligned(out, out_dtype == NVFP4MOE_F32 ? 4 : 2))
+    return fail(NVFP4MOE_ERR_INVALID_ARG,
+                "%s: a and w_packed must be 16-byte aligned, scale arrays 2-byte aligned", fn);
+  const GemmWs lay = gemm_ws_layout(mode, a_rows, K);
+  if (lay.total && (!ws || ws_bytes < lay.total))
+    return fail(NVFP4MOE_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn,
+                lay.total, ws_bytes);
+  if (lay.total && !aligned(ws, 16))
+    return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: workspace must be 16-byte aligned", fn);
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  GemmArgs g{};
+  g.w4a4 = mode == NVFP4MOE_W4A4;
+  g.gather_index = gather_index;
+  g.gather_div = gather_div < 1 ? 1 : gather_div;
+  g.w_packed = w_packed;
+  g.w_scales = w_scales;
+  g.w_g = w_g;
+  g.expert_offsets = expert_offsets;
+  g.active = active_experts;
+  g.n_active = n_active;
+  g.E = E;
+  g.rows = rows;
+  g.Nw = Nw;
+  g.K = K;
+  g.swiglu = epi == NVFP4MOE_EPI_SWIGLU;
+  g.out = out;
+  g.out_bf16 = out_dtype == NVFP4MOE_BF16;
+  g.out_amax = out_amax;
+
+  hipError_t err = hipSuccess;
+  if (out_amax) err = launch_zero_f32(out_amax, 1, s);
+  if (err != hipSuccess) return hip_status(err, fn);
+  if (mode == NVFP4MOE_W4A16) {
+    char* base = static_cast<char*>(ws);
+    g.a16 = reinterpret_cast<_Float16*>(base);
+    g.rexp = reinterpret_cast<int*>(base + lay.a16_bytes);
+    err = launch_act_prep(static_cast<const uint16_t*>(a), a_rows, K, const_cast<_Float16*>(g.a16),
+                          const_cast<int*>(g.rexp), s);
+    if (err != hipSuccess) return hip_status(err, fn);
+  } else {
+    g.a_packed = static_cast<const uint8_t*>(a);
+    g.a_scales = a_scales;
+    g.a_g = a_g;
+  }
+  int path = forced_path();
+  if (path == NVFP4MOE_PATH_MFMA)
+    return fail(NVFP4MOE_ERR_UNSUPPORTED, "%s: the MFMA path is not built in this version", fn);
+  path = NVFP4MOE_PATH_STREAM;
+  g_last_dispatch = path;
+  return hip_status(launch_gemm_stream(g, s), fn);
+}
+
+// ------------------------------------------------------------------ unpermute-reduce
+nvfp4moe_status moe_unpermute_reduce(const void* y, nvfp4moe_dtype y_dtype,
+                                     const int32_t* slot_to_row, const float* topk_w, int32_t T,
+                                     int32_t k, int32_t H, void* out, void* stream) {
+  const char* fn = "moe_unpermute_reduce";
+  if (!y || !slot_to_row || !topk_w || !out)
+    return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: null tensor pointer", fn);
+  if (y_dtype != NVFP4MOE_F32 && y_dtype != NVFP4MOE_BF16)
+    return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: y_dtype must be F32 or BF16", fn);
+  if (T < 1 || k < 1 || H < 8 || H % 8 != 0)
+    return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: need T >= 1, k >= 1, H >= 8, H %% 8 == 0", fn);
+  if ((int64_t)T * k * H >= (int64_t(1) << 31))
+    return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: T * k * H must be < 2^31", fn);
+  if (!aligned(y, 16) || !aligned(out, 16))
+    return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: y and out must be 16-byte aligned", fn);
+  return hip_status(launch_unpermute_reduce(y, y_dtype == NVFP4MOE_BF16, slot_to_row, topk_w, T, k,
+                                            H, static_cast<uint16_t*>(out),
+                                            static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+// ------------------------------------------------------------------ FP8 activations
+size_t act_fp8_e4m3_roundtrip_workspace_size(int64_t n) {
+  if (n < 1) return 0;
+  return round_up(fp8_roundtrip_ws_bytes(n));
+}
+
+nvfp4moe_status act_fp8_e4m3_roundtrip(const void* x, int64_t n, void* out, void* ws,
+                                       size_t ws_bytes, void* stream) {
+  const char* fn = "act_fp8_e4m3_roundtrip";
+  if (!x || !out) return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: null tensor pointer", fn);
+  if (n < 8 || n % 8 != 0 || n > (int64_t(1) << 40))
+    return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: need n >= 8 and n %% 8 == 0", fn);
+  if (!aligned(x, 16) || !aligned(out, 16))
+    return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: x and out must be 16-byte aligned", fn);
+  const size_t need = act_fp8_e4m3_roundtrip_workspace_size(n);
+  if (!ws || ws_bytes < need)
+    return fail(NVFP4MOE_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
+                ws_bytes);
+  return hip_status(launch_fp8_roundtrip(x, n, out, ws, static_cast<hipStream_t>(stream)), fn);
+}
+
+}  // extern "C"

@@ -1,0 +1,102 @@
+// Device helpers shared by the gfx950 kernels of libnvfp4moe.
+//
+// Number formats (NVFP4 = FP4 E2M1 values with one E4M3 scale per 16 elements and a
+// float32 per-tensor scale; "The Benchmark That Confirmed the Ceiling: NVFP4 Cutlass on
+// sm_120", section "The NVFP4 Pivot"):
+//   E2M1 : s.ee.m, bias 1, values {0, .5, 1, 1.5, 2, 3, 4, 6}; element 2i of a row is the
+//          low nibble of byte i.
+//   E4M3 : OCP E4M3FN, bias 7, NaN = 0x7F / 0xFF, max 448 (gfx950's native FP8).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4moe {
+
+typedef _Float16 f16;
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+// ------------------------------------------------------------------ bf16
+__device__ __forceinline__ float bf16_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
+
+// float32 -> bf16 bits, round to nearest even; NaN stays (quiet) NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// ------------------------------------------------------------------ E4M3
+// E4M3FN byte -> float32 (exact; NaN for 0x7F/0xFF) with the hardware OCP FP8 convert.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t byte) {
+  return __builtin_amdgcn_cvt_f32_fp8((int)byte, 0);
+}
+
+// Nearest E4M3 code (0..0x7E) to r in [0, 448], ties to the even code.
+// Below 2^-6 the grid is uniform with step 2^-9 (subnormals), so the code is the
+// integer nearest to r * 2^9 (ties to even; code 8 is 2^-6, the first normal).
+// Above, keep 3 mantissa bits of the float32 with round-half-even on the dropped
+// 20 bits; a carry moves into the exponent field, which is what E4M3 needs.
+__device__ __forceinline__ uint32_t e4m3_rne(float r) {
+  if (r < 0.015625f) return (uint32_t)__builtin_rintf(r * 512.0f);
+  uint32_t u = __float_as_uint(r);
+  u += 0x7ffffu + ((u >> 20) & 1u);
+  return (((u >> 23) - 120u) << 3) | ((u >> 20) & 7u);
+}
+
+// ------------------------------------------------------------------ E2M1
+// Magnitude code 0..7 of the E2M1 value nearest to x >= 0 (ties to the even code,
+// saturating at 6). The grid {0,.5,1,1.5,2,3,4,6} has midpoints .25,.75,1.25,1.75,
+// 2.5,3.5,5; a midpoint rounds down when the lower neighbour's code is even.
+__device__ __forceinline__ uint32_t e2m1_rne_mag(float x) {
+  return (uint32_t)(x > 0.25f) + (uint32_t)(x >= 0.75f) + (uint32_t)(x > 1.25f) +
+         (uint32_t)(x >= 1.75f) + (uint32_t)(x > 2.5f) + (uint32_t)(x >= 3.5f) +
+         (uint32_t)(x > 5.0f);
+}
+
+// ------------------------------------------------------------------ NVFP4 -> f16
+// Eight E2M1 codes (one dword, element 0 in the low nibble) times an f16 block scale,
+// as eight f16 values. The hardware convert produces the E2M1 values exactly (scale
+// 1.0); the product E2M1 * E4M3 has at most 6 significant bits and lies in
+// [2^-10, 2688], so the f16 multiply is exact as well. A NaN scale gives NaN.
+__device__ __forceinline__ f16x8 decode8(uint32_t w, f16x2 s2) {
+  f16x2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * s2;
+  f16x2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * s2;
+  f16x2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * s2;
+  f16x2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * s2;
+  return (f16x8){a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// Two consecutive E4M3 scale bytes (low byte first) -> their values as f16 pairs
+// (s0, s0) and (s1, s1). E4M3 values are exact in f16.
+__device__ __forceinline__ void decode_scale_pair(uint32_t two, f16x2& s0, f16x2& s1) {
+  f32x2 f = __builtin_amdgcn_cvt_pk_f32_fp8((int)two, false);
+  f16 h0 = (f16)f[0], h1 = (f16)f[1];
+  s0 = (f16x2){h0, h0};
+  s1 = (f16x2){h1, h1};
+}
+
+// ------------------------------------------------------------------ wave helpers
+__device__ __forceinline__ float wave_max(float v) {
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+
+// Max of |v| as float bits; NaN (any sign) compares above every finite value and Inf.
+__device__ __forceinline__ uint32_t abs_bits(float v) { return __float_as_uint(v) & 0x7fffffffu; }
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  for (int o = 32; o > 0; o >>= 1) {
+    uint32_t w = __shfl_xor(v, o, kWave);
+    v = v > w ? v : w;
+  }
+  return v;
+}
+
+}  // namespace nvfp4moe

@@ -1,0 +1,63 @@
+// Internal launch interface between the C ABI layer (api.hip) and the kernel files.
+// Every launcher only enqueues work on `stream` and returns hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace nvfp4moe {
+
+// ---- quantize.hip
+size_t quantize_ws_bytes(int64_t B, int64_t R, int64_t C);
+hipError_t launch_quantize(const void* x, bool x_bf16, int64_t B, int64_t R, int64_t C,
+                           const float* g_in, const float* amax_in, uint8_t* packed,
+                           uint8_t* scales, float* g_out, void* ws, hipStream_t stream);
+size_t fp8_roundtrip_ws_bytes(int64_t n);
+hipError_t launch_fp8_roundtrip(const void* x, int64_t n, void* out, void* ws, hipStream_t stream);
+
+// ---- route.hip
+constexpr int kMaxExperts = 1024;
+constexpr int kMaxTopK = 64;
+hipError_t launch_route_permute(const float* logits, int T, int E, int k, int* topk_ids,
+                                float* topk_w, int* expert_offsets, int* sorted_slot,
+                                int* slot_to_row, int* active_experts, int* n_active,
+                                hipStream_t stream);
+
+// ---- act_prep.hip: bf16 rows -> f16 rows scaled by 2^-p (max |x| in [2^14, 2^15)) + p
+hipError_t launch_act_prep(const uint16_t* a, int64_t rows, int K, _Float16* a16, int* rexp,
+                           hipStream_t stream);
+
+// ---- grouped GEMM kernels
+struct GemmArgs {
+  int w4a4;                        // 0: W4A16 (a16 + rexp), 1: W4A4 (a_packed + a_scales + a_g)
+  const _Float16* a16;             // [a_rows, K] f16, row r scaled by 2^-rexp[r]
+  const int* rexp;                 // [a_rows]
+  const uint8_t* a_packed;         // [a_rows, K/2]
+  const uint8_t* a_scales;         // [a_rows, K/16]
+  const float* a_g;                // [1]
+  const int* gather_index;         // [rows] or null
+  int gather_div;
+  const uint8_t* w_packed;         // [E, Nw, K/2]
+  const uint8_t* w_scales;         // [E, Nw, K/16]
+  const float* w_g;                // [E]
+  const int* expert_offsets;       // [E+1]
+  const int* active;               // [E]
+  const int* n_active;             // [1]
+  int E, rows, Nw, K;
+  int swiglu;
+  void* out;
+  int out_bf16;
+  float* out_amax;                 // null or [1], zeroed before the GEMM
+};
+hipError_t launch_gemm_stream(const GemmArgs& a, hipStream_t stream);
+hipError_t launch_gemm_mfma(const GemmArgs& a, void* ws, size_t ws_bytes, hipStream_t stream);
+size_t gemm_mfma_ws_bytes(int rows, int Nw, int E);
+hipError_t launch_zero_f32(float* p, int n, hipStream_t stream);
+
+// ---- reduce.hip
+hipError_t launch_unpermute_reduce(const void* y, bool y_bf16, const int* slot_to_row,
+                                   const float* topk_w, int T, int k, int H, uint16_t* out,
+                                   hipStream_t stream);
+
+}  // namespace nvfp4moe

@@ -1,0 +1,258 @@
+// NVFP4 quantization and the FP8 E4M3 activation round trip (gfx950).
+//
+// NVFP4 ("The Benchmark That Confirmed the Ceiling: NVFP4 Cutlass on sm_120", section
+// "The NVFP4 Pivot"): one E4M3 scale per 16 consecutive elements of a row, E2M1 codes,
+// and a float32 per-tensor scale g. Per matrix, in float32 with round-to-nearest-even:
+//   g = amax / 2688 over the finite entries (1 if that amax is 0), unless given;
+//   per 16-group: any NaN/Inf -> scale 0x7F, codes 0;  amax_g == 0 -> scale 0, codes +-0;
+//   else s = E4M3(min(amax_g / (6 g), 448)), S = E4M3[s] * g, q = E2M1(|w| / S) with the
+//   sign bit of w.
+// FP8 activations ("Native FP4 Is Slower Than Emulated FP4", section 1): x -> E4M3 with a
+// per-tensor scale amax / 448, back to bf16.
+//
+// Memory traffic: one read of x for the amax, one read of x plus 9/16 byte per element
+// written for the codes; every access is a 16-byte vector access.
+#include "common.h"
+#include "kernels.h"
+
+namespace nvfp4moe {
+
+namespace {
+
+constexpr int kAmaxThreads = 256;
+constexpr int kQuantThreads = 256;
+
+template <typename T>
+struct Vec8;  // eight consecutive elements as float
+template <>
+struct Vec8<float> {
+  static __device__ __forceinline__ void load(const float* p, float v[8]) {
+    float4 a = *reinterpret_cast<const float4*>(p);
+    float4 b = *reinterpret_cast<const float4*>(p + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  }
+};
+template <>
+struct Vec8<uint16_t> {
+  static __device__ __forceinline__ void load(const uint16_t* p, float v[8]) {
+    uint4 a = *reinterpret_cast<const uint4*>(p);
+    uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = bf16_to_f32(w[i] & 0xffffu);
+      v[2 * i + 1] = bf16_to_f32(w[i] >> 16);
+    }
+  }
+};
+
+__device__ __forceinline__ float finite_abs(float v) {
+  float a = fabsf(v);
+  return (a <= 3.402823466e38f) ? a : 0.0f;  // Inf and NaN fail the compare
+}
+
+// Partial max of |x| over the finite entries: grid (nblk, B); matrix b has n elements
+// (n % 8 == 0); block j scans the 8-element vectors j, j + nblk, ... of matrix b.
+template <typename T>
+__global__ __launch_bounds__(kAmaxThreads) void amax_partial_kernel(const T* __restrict__ x,
+                                                                    int64_t n, int nblk,
+                                                                    float* __restrict__ partial) {
+  const int b = blockIdx.y;
+  const T* xb = x + (size_t)b * (size_t)n;
+  const int64_t nvec = n / 8;
+  float m = 0.0f;
+  for (int64_t i = (int64_t)blockIdx.x * kAmaxThreads + threadIdx.x; i < nvec;
+       i += (int64_t)nblk * kAmaxThreads) {
+    float v[8];
+    Vec8<T>::load(xb + i * 8, v);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m = fmaxf(m, finite_abs(v[j]));
+  }
+  __shared__ float red[kAmaxThreads / kWave];
+  m = wave_max(m);
+  if ((threadIdx.x % kWave) == 0) red[threadIdx.x / kWave] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float r = red[0];
+    for (int w = 1; w < kAmaxThreads / kWave; ++w) r = fmaxf(r, red[w]);
+    partial[(size_t)b * nblk + blockIdx.x] = r;
+  }
+}
+
+// g[b] from (in order of precedence) g_in, amax_in, or the partial maxima.
+// mode 0: quantizer global scale amax/2688; mode 1: FP8 activation scale amax/448.
+__global__ __launch_bounds__(kWave) void finalize_scale_kernel(const float* __restrict__ g_in,
+                                                               const float* __restrict__ amax_in,
+                                                               const float* __restrict__ partial,
+                                                               int nblk, float denom,
+                                                               float* __restrict__ g_out) {
+  const int b = blockIdx.x;
+  float g;
+  if (g_in) {
+    g = g_in[b];
+  } else {
+    float a;
+    if (amax_in) {
+      a = amax_in[b];
+    } else {
+      a = 0.0f;
+      for (int i = threadIdx.x; i < nblk; i += kWave) a = fmaxf(a, partial[(size_t)b * nblk + i]);
+      a = wave_max(a);
+    }
+    g = (a == 0.0f) ? 1.0f : __fdiv_rn(a, denom);
+  }
+  if (threadIdx.x == 0) g_out[b] = g;
+}
+
+// One thread per 32 consecutive elements of a row (two 16-groups): reads 32 elements,
+// writes 16 packed bytes and 2 scale bytes.
+template <typename T>
+__global__ __launch_bounds__(kQuantThreads) void quantize_kernel(const T* __restrict__ x,
+                                                                 int64_t n_per_mat,
+                                                                 int64_t total_units,
+                                                                 const float* __restrict__ g,
+                                                                 uint8_t* __restrict__ packed,
+                                                                 uint8_t* __restrict__ scales) {
+  const int64_t u = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x;
+  if (u >= total_units) return;
+  const int64_t e0 = u * 32;               // first element (flat over all matrices)
+  const int64_t b = e0 / n_per_mat;        // matrix index
+  const float gb = g[b];
+  const float six_g = 6.0f * gb;
+  uint32_t out_words[4];
+  uint32_t sc_bytes = 0;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    float v[16];
+    Vec8<T>::load(x + e0 + 16 * h, v);
+    Vec8<T>::load(x + e0 + 16 * h + 8, v + 8);
+    float amax = 0.0f;
+    bool finite = true;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float a = fabsf(v[i]);
+      finite = finite && (a <= 3.402823466e38f);
+      amax = fmaxf(amax, finite_abs(v[i]));
+    }
+    uint32_t s;
+    float S;
+    if (!finite) {
+      s = 0x7f;
+      S = 0.0f;
+    } else if (amax == 0.0f) {
+      s = 0;
+      S = 0.0f;
+    } else {
+      float ratio = fminf(__fdiv_rn(amax, six_g), 448.0f);
+      s = e4m3_rne(ratio);
+      S = e4m3_to_f32(s) * gb;
+    }
+    sc_bytes |= s << (8 * h);
+    uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      uint32_t code = 0;
+      if (finite) {
+        uint32_t sign = (__float_as_uint(v[i]) >> 31) << 3;
+        uint32_t mag = (S == 0.0f) ? 0u : e2m1_rne_mag(__fdiv_rn(fabsf(v[i]), S));
+        code = sign | mag;
+      }
+      if (i < 8) w0 |= code << (4 * i);
+      else w1 |= code << (4 * (i - 8));
+    }
+    out_words[2 * h] = w0;
+    out_words[2 * h + 1] = w1;
+  }
+  *reinterpret_cast<uint4*>(packed + e0 / 2) =
+      make_uint4(out_words[0], out_words[1], out_words[2], out_words[3]);
+  *reinterpret_cast<uint16_t*>(scales + e0 / 16) = (uint16_t)sc_bytes;
+}
+
+// FP8 E4M3 round trip of 8 bf16 values per thread.
+__global__ __launch_bounds__(kQuantThreads) void fp8_roundtrip_kernel(const uint16_t* __restrict__ x,
+                                                                      int64_t nvec,
+                                                                      const float* __restrict__ s_a,
+                                                                      uint16_t* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x;
+  if (i >= nvec) return;
+  const float s = s_a[0];
+  float v[8];
+  Vec8<uint16_t>::load(x + i * 8, v);
+  uint32_t w[4];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    uint32_t bits;
+    if (v[j] != v[j]) {
+      bits = 0x7fc0u;
+    } else {
+      float r = __fdiv_rn(v[j], s);
+      float mag = e4m3_to_f32(e4m3_rne(fminf(fabsf(r), 448.0f)));
+      float q = (__float_as_uint(r) >> 31) ? -mag : mag;
+      bits = f32_to_bf16(q * s);
+    }
+    if (j & 1) w[j / 2] |= bits << 16;
+    else w[j / 2] = bits;
+  }
+  *reinterpret_cast<uint4*>(out + i * 8) = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+inline int amax_blocks(int64_t n) {
+  int64_t nb = (n / 8 + kAmaxThreads * 8 - 1) / (kAmaxThreads * 8);
+  if (nb < 1) nb = 1;
+  if (nb > 256) nb = 256;
+  return (int)nb;
+}
+
+}  // namespace
+
+size_t quantize_ws_bytes(int64_t B, int64_t R, int64_t C) {
+  return (size_t)B * (size_t)amax_blocks(R * C) * sizeof(float);
+}
+
+hipError_t launch_quantize(const void* x, bool x_bf16, int64_t B, int64_t R, int64_t C,
+                           const float* g_in, const float* amax_in, uint8_t* packed,
+                           uint8_t* scales, float* g_out, void* ws, hipStream_t stream) {
+  const int64_t n = R * C;
+  const int nblk = amax_blocks(n);
+  float* partial = static_cast<float*>(ws);
+  if (!g_in && !amax_in) {
+    dim3 grid(nblk, (unsigned)B);
+    if (x_bf16)
+      amax_partial_kernel<uint16_t><<<grid, kAmaxThreads, 0, stream>>>(
+          static_cast<const uint16_t*>(x), n, nblk, partial);
+    else
+      amax_partial_kernel<float><<<grid, kAmaxThreads, 0, stream>>>(static_cast<const float*>(x),
+                                                                      n, nblk, partial);
+  }
+  finalize_scale_kernel<<<(unsigned)B, kWave, 0, stream>>>(g_in, amax_in, partial, nblk, 2688.0f,
+                                                            g_out);
+  const int64_t units = B * n / 32;
+  const int64_t blocks = (units + kQuantThreads - 1) / kQuantThreads;
+  if (x_bf16)
+    quantize_kernel<uint16_t><<<(unsigned)blocks, kQuantThreads, 0, stream>>>(
+        static_cast<const uint16_t*>(x), n, units, g_out, packed, scales);
+  else
+    quantize_kernel<float><<<(unsigned)blocks, kQuantThreads, 0, stream>>>(
+        static_cast<const float*>(x), n, units, g_out, packed, scales);
+  return hipGetLastError();
+}
+
+size_t fp8_roundtrip_ws_bytes(int64_t n) {
+  return ((size_t)amax_blocks(n) + 64) * sizeof(float);
+}
+
+hipError_t launch_fp8_roundtrip(const void* x, int64_t n, void* out, void* ws, hipStream_t stream) {
+  const int nblk = amax_blocks(n);
+  float* partial = static_cast<float*>(ws);
+  float* s_a = partial + nblk + 32;  // keep apart from the partials
+  amax_partial_kernel<uint16_t><<<dim3(nblk, 1), kAmaxThreads, 0, stream>>>(
+      static_cast<const uint16_t*>(x), n, nblk, partial);
+  finalize_scale_kernel<<<1, kWave, 0, stream>>>(nullptr, nullptr, partial, nblk, 448.0f, s_a);
+  const int64_t nvec = n / 8;
+  fp8_roundtrip_kernel<<<(unsigned)((nvec + kQuantThreads - 1) / kQuantThreads), kQuantThreads, 0,
+                         stream>>>(static_cast<const uint16_t*>(x), nvec, s_a,
+                                   static_cast<uint16_t*>(out));
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4moe

@@ -1,0 +1,70 @@
+// Unpermute + weighted top-k reduce (gfx950).
+//
+// The scatter half of the MoE's expert scatter/gather ("The 2x Gap: Diagnosing Suboptimal
+// FP4 GEMM Kernels on Blackwell SM120", section "Discovering the sgl_kernel Alternative"):
+//   out[t, :] = bf16( sum_{j<k} w[t, j] * Y[slot_to_row[t*k + j], :] ),
+// float32 fused multiply-adds in ascending j, so the result does not depend on thread
+// timing. HBM-bound: k rows of Y read and one bf16 row written per token; each thread
+// handles 8 consecutive columns with 16/32-byte vector accesses.
+#include "common.h"
+#include "kernels.h"
+
+namespace nvfp4moe {
+
+namespace {
+
+constexpr int kRedThreads = 256;
+
+template <bool YBF16>
+__global__ __launch_bounds__(kRedThreads) void unpermute_reduce_kernel(const void* __restrict__ y,
+                                                                       const int* __restrict__ slot_to_row,
+                                                                       const float* __restrict__ topk_w,
+                                                                       int k, int H,
+                                                                       uint16_t* __restrict__ out) {
+  const int cblocks = (H / 8 + kRedThreads - 1) / kRedThreads;
+  const int t = blockIdx.x / cblocks;
+  const int c = ((blockIdx.x - t * cblocks) * kRedThreads + threadIdx.x) * 8;
+  if (c >= H) return;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < k; ++j) {
+    const size_t row = (size_t)slot_to_row[(size_t)t * k + j];
+    const float w = topk_w[(size_t)t * k + j];
+    float v[8];
+    if (YBF16) {
+      uint4 q = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(y) + row * H + c);
+      uint32_t u[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[2 * i] = bf16_to_f32(u[i] & 0xffffu);
+        v[2 * i + 1] = bf16_to_f32(u[i] >> 16);
+      }
+    } else {
+      const float* yr = static_cast<const float*>(y) + row * H + c;
+      float4 a = *reinterpret_cast<const float4*>(yr);
+      float4 b = *reinterpret_cast<const float4*>(yr + 4);
+      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+      v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = fmaf(w, v[i], acc[i]);
+  }
+  uint32_t o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = f32_to_bf16(acc[2 * i]) | (f32_to_bf16(acc[2 * i + 1]) << 16);
+  *reinterpret_cast<uint4*>(out + (size_t)t * H + c) = make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+}  // namespace
+
+hipError_t launch_unpermute_reduce(const void* y, bool y_bf16, const int* slot_to_row,
+                                   const float* topk_w, int T, int k, int H, uint16_t* out,
+                                   hipStream_t stream) {
+  const unsigned grid = (unsigned)((H / 8 + kRedThreads - 1) / kRedThreads) * (unsigned)T;
+  if (y_bf16)
+    unpermute_reduce_kernel<true><<<grid, kRedThreads, 0, stream>>>(y, slot_to_row, topk_w, k, H, out);
+  else
+    unpermute_reduce_kernel<false><<<grid, kRedThreads, 0, stream>>>(y, slot_to_row, topk_w, k, H, out);
+  return hipGetLastError();
+}
+
+}  // namespace nvfp4moe

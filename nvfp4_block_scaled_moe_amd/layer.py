@@ -1,0 +1,92 @@
+"""The MoE layer as a sequence of C ABI calls (route -> up/gate + SwiGLU -> down -> reduce).
+
+This module only sequences the library calls and allocates their outputs with torch; all
+arithmetic runs in the HIP kernels behind include/nvfp4moe.h.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import torch
+
+from . import inputs, ops
+
+
+@dataclass
+class NVFP4Experts:
+    """NVFP4 expert weights: W13_e = [2F, H] (gate rows first), W2_e = [H, F]."""
+    w13_packed: torch.Tensor   # uint8 [E, 2F, H/2]
+    w13_scales: torch.Tensor   # uint8 [E, 2F, H/16]
+    w13_g: torch.Tensor        # f32 [E]
+    w2_packed: torch.Tensor    # uint8 [E, H, F/2]
+    w2_scales: torch.Tensor    # uint8 [E, H, F/16]
+    w2_g: torch.Tensor         # f32 [E]
+
+    @property
+    def E(self):
+        return self.w13_packed.shape[0]
+
+    def w13(self, e):
+        return self.w13_packed[e], self.w13_scales[e], self.w13_g[e]
+
+    def w2(self, e):
+        return self.w2_packed[e], self.w2_scales[e], self.w2_g[e]
+
+
+def quantize_experts(wl: inputs.Workload, device="cuda", experts=None) -> NVFP4Experts:
+    """Generate the workload's seeded FP32 expert weights one expert at a time on ``device``
+    and quantize each with the library's nvfp4_quantize."""
+    E, H, F = wl.E, wl.H, wl.F
+    experts = range(E) if experts is None else experts
+    u8 = dict(dtype=torch.uint8, device=device)
+    w = NVFP4Experts(
+        torch.zeros((E, 2 * F, H // 2), **u8), torch.zeros((E, 2 * F, H // 16), **u8),
+        torch.ones((E,), dtype=torch.float32, device=device),
+        torch.zeros((E, H, F // 2), **u8), torch.zeros((E, H, F // 16), **u8),
+        torch.ones((E,), dtype=torch.float32, device=device))
+    for e in experts:
+        ops.nvfp4_quantize(inputs.expert_weight_fp32(wl, "w13", e, device),
+                           out=(w.w13_packed[e], w.w13_scales[e], w.w13_g[e:e + 1]))
+        ops.nvfp4_quantize(inputs.expert_weight_fp32(wl, "w2", e, device),
+                           out=(w.w2_packed[e], w.w2_scales[e], w.w2_g[e:e + 1]))
+    return w
+
+
+def moe_forward(x: torch.Tensor, logits: torch.Tensor, k: int, w: NVFP4Experts, mode: int = ops.W4A16,
+                fp8_acts: bool = False, keep: bool = False):
+    """One MoE layer forward. ``x`` bf16 [T, H]; ``logits`` f32 [T, E].
+
+    Returns the bf16 output [T, H]; with ``keep`` a dict of every stage's tensors.
+    """
+    st = {}
+    if fp8_acts:
+        x = ops.act_fp8_e4m3_roundtrip(x)
+        st["x_fp8"] = x
+    r = ops.moe_route_permute(logits, k)
+    st.update(r)
+    T = x.shape[0]
+    S = T * k
+    common = dict(expert_offsets=r["expert_offsets"], active_experts=r["active_experts"],
+                  n_active=r["n_active"])
+    if mode == ops.W4A16:
+        h = ops.moe_grouped_gemm_nvfp4(ops.W4A16, ops.EPI_SWIGLU, x, w.w13_packed, w.w13_scales, w.w13_g,
+                                       gather_index=r["sorted_slot"], gather_div=k, rows=S,
+                                       out_dtype=torch.bfloat16, **common)
+        y = ops.moe_grouped_gemm_nvfp4(ops.W4A16, ops.EPI_NONE, h, w.w2_packed, w.w2_scales, w.w2_g,
+                                       rows=S, out_dtype=torch.float32, **common)
+    else:
+        xq, xs, xg = ops.nvfp4_quantize(x)
+        st.update(xq=xq, xs=xs, xg=xg)
+        h, amax = ops.moe_grouped_gemm_nvfp4(ops.W4A4, ops.EPI_SWIGLU, xq, w.w13_packed, w.w13_scales,
+                                             w.w13_g, a_scales=xs, a_g=xg, gather_index=r["sorted_slot"],
+                                             gather_div=k, rows=S, out_dtype=torch.float32,
+                                             want_amax=True, **common)
+        hq, hs, hg = ops.nvfp4_quantize(h, amax=amax)
+        st.update(h_amax=amax, hq=hq, hs=hs, hg=hg)
+        y = ops.moe_grouped_gemm_nvfp4(ops.W4A4, ops.EPI_NONE, hq, w.w2_packed, w.w2_scales, w.w2_g,
+                                       a_scales=hs, a_g=hg, rows=S, out_dtype=torch.float32, **common)
+    out = ops.moe_unpermute_reduce(y, r["slot_to_row"], r["topk_w"])
+    if keep:
+        st.update(h=h, y=y, out=out)
+        return out, st
+    return out

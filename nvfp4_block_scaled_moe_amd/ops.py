@@ -1,0 +1,155 @@
+"""Thin PyTorch binding of libnvfp4moe: one function per C ABI call, same names.
+
+Only argument marshalling happens here: tensors are checked for device/dtype/shape,
+outputs and workspaces are allocated with torch (device memory and streams are all torch
+is used for), and the C call is made on the current HIP stream. Every step of the
+computation runs in the library's HIP kernels; a failed call raises NVFP4MoEError.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import BF16, EPI_NONE, EPI_SWIGLU, F32, W4A4, W4A16  # noqa: F401
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dev(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("all tensors must be on the GPU")
+
+
+def _ws(nbytes, device):
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+_DT = {torch.float32: F32, torch.bfloat16: BF16}
+
+
+def nvfp4_quantize(x: torch.Tensor, g: torch.Tensor | None = None, amax: torch.Tensor | None = None,
+                   out: tuple | None = None):
+    """Quantize [R, C] or [B, R, C] float32/bf16 to NVFP4 -> (packed, scales, g[B]).
+
+    ``g``: optional device float[B] global scales; ``amax``: optional device float[B]
+    finite max |x| per matrix (used when ``g`` is None); ``out``: optional preallocated
+    (packed [B, R, C/2], scales [B, R, C/16], g [B]) to write into (contiguous views).
+    """
+    _dev(x, g, amax)
+    squeeze = x.dim() == 2
+    x3 = x.unsqueeze(0) if squeeze else x
+    x3 = x3.contiguous()
+    B, R, C = x3.shape
+    lib = _lib.load()
+    if out is not None:
+        packed, scales, g_out = out
+        assert packed.is_contiguous() and scales.is_contiguous() and g_out.is_contiguous()
+        assert packed.numel() == B * R * C // 2 and scales.numel() == B * R * C // 16 and g_out.numel() == B
+    else:
+        packed = torch.empty((B, R, C // 2), dtype=torch.uint8, device=x.device)
+        scales = torch.empty((B, R, C // 16), dtype=torch.uint8, device=x.device)
+        g_out = torch.empty((B,), dtype=torch.float32, device=x.device)
+    ws = _ws(lib.nvfp4_quantize_workspace_size(B, R, C), x.device)
+    st = lib.nvfp4_quantize(_ptr(x3), _DT[x3.dtype], B, R, C, _ptr(g), _ptr(amax), _ptr(packed),
+                            _ptr(scales), _ptr(g_out), _ptr(ws), ws.numel(), _stream())
+    _lib.check("nvfp4_quantize", st)
+    if squeeze and out is None:
+        return packed[0], scales[0], g_out
+    return packed, scales, g_out
+
+
+def moe_route_permute(logits: torch.Tensor, k: int):
+    """Router + permutation. Returns a dict of device tensors (see include/nvfp4moe.h)."""
+    _dev(logits)
+    logits = logits.contiguous().float()
+    T, E = logits.shape
+    dev = logits.device
+    i32 = dict(dtype=torch.int32, device=dev)
+    out = dict(
+        topk_ids=torch.empty((T, k), **i32),
+        topk_w=torch.empty((T, k), dtype=torch.float32, device=dev),
+        expert_offsets=torch.empty((E + 1,), **i32),
+        sorted_slot=torch.empty((T * k,), **i32),
+        slot_to_row=torch.empty((T * k,), **i32),
+        active_experts=torch.empty((E,), **i32),
+        n_active=torch.empty((1,), **i32),
+    )
+    lib = _lib.load()
+    st = lib.moe_route_permute(_ptr(logits), T, E, k, _ptr(out["topk_ids"]), _ptr(out["topk_w"]),
+                               _ptr(out["expert_offsets"]), _ptr(out["sorted_slot"]),
+                               _ptr(out["slot_to_row"]), _ptr(out["active_experts"]),
+                               _ptr(out["n_active"]), None, 0, _stream())
+    _lib.check("moe_route_permute", st)
+    return out
+
+
+def moe_grouped_gemm_nvfp4(mode: int, epi: int, a: torch.Tensor, w_packed: torch.Tensor,
+                           w_scales: torch.Tensor, w_g: torch.Tensor, expert_offsets: torch.Tensor,
+                           active_experts: torch.Tensor, n_active: torch.Tensor, *,
+                           a_scales: torch.Tensor | None = None, a_g: torch.Tensor | None = None,
+                           gather_index: torch.Tensor | None = None, gather_div: int = 1,
+                           rows: int | None = None, out_dtype=torch.bfloat16,
+                           want_amax: bool = False, out: torch.Tensor | None = None):
+    """Grouped NVFP4 GEMM (+ SwiGLU). ``w_packed`` [E, Nw, K/2]; ``a`` bf16 [a_rows, K]
+    (W4A16) or packed uint8 [a_rows, K/2] (W4A4). Returns out (and amax when asked)."""
+    _dev(a, w_packed, w_scales, w_g, expert_offsets, active_experts, n_active, a_scales, a_g, gather_index)
+    E, Nw, Kh = w_packed.shape
+    K = Kh * 2
+    a_rows = a.shape[0]
+    if rows is None:
+        rows = gather_index.numel() if gather_index is not None else a_rows
+    ncol = Nw // 2 if epi == EPI_SWIGLU else Nw
+    if out is None:
+        out = torch.empty((rows, ncol), dtype=out_dtype, device=a.device)
+    amax = torch.empty((1,), dtype=torch.float32, device=a.device) if want_amax else None
+    lib = _lib.load()
+    ws = _ws(lib.moe_grouped_gemm_workspace_size(mode, a_rows, rows, E, Nw, K), a.device)
+    st = lib.moe_grouped_gemm_nvfp4(
+        mode, epi, _ptr(a), _ptr(a_scales), _ptr(a_g), a_rows, _ptr(gather_index), int(gather_div),
+        _ptr(w_packed), _ptr(w_scales), _ptr(w_g), _ptr(expert_offsets), _ptr(active_experts),
+        _ptr(n_active), E, rows, Nw, K, _ptr(out), _DT[out.dtype], _ptr(amax), _ptr(ws), ws.numel(),
+        _stream())
+    _lib.check("moe_grouped_gemm_nvfp4", st)
+    return (out, amax) if want_amax else out
+
+
+def moe_unpermute_reduce(y: torch.Tensor, slot_to_row: torch.Tensor, topk_w: torch.Tensor,
+                         out: torch.Tensor | None = None):
+    """out[t] = bf16(sum_j topk_w[t, j] * y[slot_to_row[t*k + j]])."""
+    _dev(y, slot_to_row, topk_w)
+    T, k = topk_w.shape
+    H = y.shape[1]
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=y.device)
+    lib = _lib.load()
+    st = lib.moe_unpermute_reduce(_ptr(y), _DT[y.dtype], _ptr(slot_to_row), _ptr(topk_w), T, k, H,
+                                  _ptr(out), _stream())
+    _lib.check("moe_unpermute_reduce", st)
+    return out
+
+
+def act_fp8_e4m3_roundtrip(x: torch.Tensor, out: torch.Tensor | None = None):
+    """FP8 E4M3 (per-tensor scale) round trip of bf16 activations, returned as bf16."""
+    _dev(x)
+    x = x.contiguous()
+    if out is None:
+        out = torch.empty_like(x)
+    lib = _lib.load()
+    n = x.numel()
+    ws = _ws(lib.act_fp8_e4m3_roundtrip_workspace_size(n), x.device)
+    st = lib.act_fp8_e4m3_roundtrip(_ptr(x), n, _ptr(out), _ptr(ws), ws.numel(), _stream())
+    _lib.check("act_fp8_e4m3_roundtrip", st)
+    return out
+
+
+def last_dispatch() -> int:
+    return _lib.load().nvfp4moe_last_dispatch()

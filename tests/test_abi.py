@@ -1,0 +1,111 @@
+"""CPU-only checks of the C ABI library: it loads, exports every symbol the header declares,
+and rejects bad arguments on the host before any HIP call (so no GPU is needed)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from nvfp4_block_scaled_moe_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4moe.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"\b(?:nvfp4moe_status|size_t|const char\*|int)\s+(\w+)\s*\(", text)
+    return sorted(set(names))
+
+
+def test_header_declares_the_calls():
+    names = declared_functions()
+    for want in ["nvfp4_quantize", "moe_route_permute", "moe_grouped_gemm_nvfp4",
+                 "moe_unpermute_reduce", "act_fp8_e4m3_roundtrip", "nvfp4moe_last_error"]:
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib.load()
+    names = declared_functions()
+    assert set(names) == set(_lib.SIGNATURES), "binding signatures out of sync with the header"
+    for n in names:
+        assert hasattr(lib, n)
+    assert lib.nvfp4moe_abi_version() == 100
+
+
+FAKE = ctypes.c_void_p(1 << 20)      # aligned, never dereferenced: validation fails first
+MISALIGNED = ctypes.c_void_p((1 << 20) + 2)
+
+
+def _err(st):
+    return st, _lib.load().nvfp4moe_last_error().decode()
+
+
+def test_quantize_rejects_bad_arguments():
+    lib = _lib.load()
+    st, msg = _err(lib.nvfp4_quantize(None, _lib.F32, 1, 4, 32, None, None, FAKE, FAKE, FAKE, FAKE, 1 << 20, None))
+    assert st == _lib.ERR_INVALID_ARG and "null" in msg
+    st, msg = _err(lib.nvfp4_quantize(FAKE, _lib.F32, 1, 4, 48, None, None, FAKE, FAKE, FAKE, FAKE, 1 << 20, None))
+    assert st == _lib.ERR_INVALID_ARG and "C % 32" in msg
+    st, _ = _err(lib.nvfp4_quantize(FAKE, 7, 1, 4, 32, None, None, FAKE, FAKE, FAKE, FAKE, 1 << 20, None))
+    assert st == _lib.ERR_INVALID_ARG
+    st, _ = _err(lib.nvfp4_quantize(MISALIGNED, _lib.F32, 1, 4, 32, None, None, FAKE, FAKE, FAKE, FAKE, 1 << 20, None))
+    assert st == _lib.ERR_INVALID_ARG
+    need = lib.nvfp4_quantize_workspace_size(1, 4, 32)
+    st, msg = _err(lib.nvfp4_quantize(FAKE, _lib.F32, 1, 4, 32, None, None, FAKE, FAKE, FAKE, FAKE, need - 1, None))
+    assert st == _lib.ERR_WORKSPACE and "workspace" in msg
+
+
+def test_route_permute_rejects_bad_arguments():
+    lib = _lib.load()
+    args = lambda T, E, k: (FAKE, T, E, k, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None)
+    for T, E, k in [(0, 8, 2), (4, 8, 9), (4, 8, 0), (4, 2048, 8), (4, 256, 65), (1 << 22, 256, 8)]:
+        st, _ = _err(lib.moe_route_permute(*args(T, E, k)))
+        assert st == _lib.ERR_INVALID_ARG, (T, E, k)
+
+
+def _gemm(lib, mode=_lib.W4A16, epi=_lib.EPI_SWIGLU, a=FAKE, a_scales=None, a_g=None, a_rows=16,
+          gidx=None, gdiv=1, E=8, rows=16, Nw=64, K=64, out_dtype=_lib.BF16, ws=FAKE, ws_bytes=1 << 30):
+    return lib.moe_grouped_gemm_nvfp4(mode, epi, a, a_scales, a_g, a_rows, gidx, gdiv, FAKE, FAKE, FAKE,
+                                      FAKE, FAKE, FAKE, E, rows, Nw, K, FAKE, out_dtype, None, ws,
+                                      ws_bytes, None)
+
+
+def test_grouped_gemm_rejects_bad_arguments():
+    lib = _lib.load()
+    bad = [
+        dict(mode=5), dict(epi=3), dict(out_dtype=9), dict(a=None), dict(mode=_lib.W4A4),
+        dict(E=0), dict(E=2000), dict(rows=0), dict(Nw=48), dict(Nw=16), dict(K=40), dict(K=0),
+        dict(a_rows=8), dict(gidx=FAKE, gdiv=0), dict(a=MISALIGNED), dict(rows=1 << 26, a_rows=1 << 26, K=64, Nw=64),
+    ]
+    for kw in bad:
+        st, _ = _err(_gemm(lib, **kw))
+        assert st == _lib.ERR_INVALID_ARG, kw
+    need = lib.moe_grouped_gemm_workspace_size(_lib.W4A16, 16, 16, 8, 64, 64)
+    assert need >= 16 * 64 * 2
+    st, _ = _err(_gemm(lib, ws_bytes=need - 1))
+    assert st == _lib.ERR_WORKSPACE
+
+
+def test_unpermute_reduce_and_fp8_reject_bad_arguments():
+    lib = _lib.load()
+    assert lib.moe_unpermute_reduce(FAKE, _lib.F32, FAKE, FAKE, 4, 2, 12, FAKE, None) == _lib.ERR_INVALID_ARG
+    assert lib.moe_unpermute_reduce(FAKE, _lib.F32, FAKE, FAKE, 0, 2, 16, FAKE, None) == _lib.ERR_INVALID_ARG
+    assert lib.moe_unpermute_reduce(None, _lib.F32, FAKE, FAKE, 4, 2, 16, FAKE, None) == _lib.ERR_INVALID_ARG
+    assert lib.act_fp8_e4m3_roundtrip(FAKE, 12, FAKE, FAKE, 1 << 20, None) == _lib.ERR_INVALID_ARG
+    assert lib.act_fp8_e4m3_roundtrip(FAKE, 64, FAKE, FAKE, 0, None) == _lib.ERR_WORKSPACE
+
+
+def test_last_error_is_thread_local_and_cleared():
+    import threading
+    lib = _lib.load()
+    lib.moe_route_permute(*(FAKE, 0, 8, 2, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, 0, None))
+    assert lib.nvfp4moe_last_error()
+    seen = []
+    th = threading.Thread(target=lambda: seen.append(lib.nvfp4moe_last_error()))
+    th.start()
+    th.join()
+    assert seen == [b""]
+

@@ -1,0 +1,241 @@
+"""GPU parity: every C ABI call against the oracle on the same seeded inputs.
+
+Integer/byte outputs (codes, scales, ids, offsets, permutation) must match bit for bit;
+floating-point outputs must be within the stated relative Frobenius bounds (W4A16 1e-3,
+W4A4 2e-2) of the float64 oracle fed identical dequantized operands, with the oracle
+rounded to the output dtype at the same points. Every GPU output is also scanned for
+NaN/Inf.
+"""
+import numpy as np
+import pytest
+import torch
+
+from nvfp4_block_scaled_moe_amd import inputs, ops
+from oracle import moe as omoe
+from oracle import nvfp4 as onv
+from tests.gpu_util import assert_finite, np_, rel_fro, say
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+W4A16_TOL = 1e-3
+W4A4_TOL = 2e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.init()
+
+
+# ------------------------------------------------------------------ quantize
+def _special_matrix(R, C, seed):
+    x = inputs.random_fp32((R, C), seed, std=0.02)
+    x[0, :16] = 0.0
+    x[0, 3] = -0.0
+    if R > 1 and C >= 64:
+        x[1, 16:32] *= 1e-7                       # subnormal E4M3 scales
+        x[1, 40] = float("nan")
+        x[1, 50] = float("inf")
+        x[1, 33] = 5.0                            # sets the global scale
+    return x
+
+
+@pytest.mark.parametrize("R,C,dt", [(16, 64, torch.float32), (33, 96, torch.float32),
+                                    (128, 6144, torch.float32), (7, 32, torch.bfloat16),
+                                    (256, 2048, torch.bfloat16)])
+def test_quantize_bit_exact(R, C, dt):
+    say("quantize", R, C, dt)
+    x = _special_matrix(R, C, R * 1000 + C).to(dt)
+    p, s, g = ops.nvfp4_quantize(x.to(DEV))
+    torch.cuda.synchronize()
+    po, so, go = onv.quantize(x.float().numpy())
+    assert np.array_equal(np_(s), so)
+    assert np.array_equal(np_(p), po)
+    assert np_(g)[0] == go
+
+
+def test_quantize_batched_static_and_amax_paths():
+    say("quantize batched / g_in / amax_in")
+    x = torch.stack([inputs.random_fp32((24, 128), 100 + b, std=0.02 * (b + 1)) for b in range(3)])
+    p, s, g = ops.nvfp4_quantize(x.to(DEV))
+    gs = torch.tensor([1e-4, 3e-5, 2.0 ** -12], dtype=torch.float32)
+    p2, s2, g2 = ops.nvfp4_quantize(x.to(DEV), g=gs.to(DEV))
+    amax = x.abs().amax(dim=(1, 2))
+    p3, s3, g3 = ops.nvfp4_quantize(x.to(DEV), amax=amax.to(DEV))
+    torch.cuda.synchronize()
+    for b in range(3):
+        po, so, go = onv.quantize(x[b].numpy())
+        assert np.array_equal(np_(p[b]), po) and np.array_equal(np_(s[b]), so) and np_(g)[b] == go
+        assert np.array_equal(np_(p3[b]), po) and np.array_equal(np_(s3[b]), so) and np_(g3)[b] == go
+        po2, so2, _ = onv.quantize(x[b].numpy(), g=gs[b].item())
+        assert np.array_equal(np_(p2[b]), po2) and np.array_equal(np_(s2[b]), so2)
+        assert np_(g2)[b] == np.float32(gs[b].item())
+
+
+def test_fp8_roundtrip_bit_exact():
+    say("fp8 roundtrip")
+    x = (inputs.random_fp32((64, 256), 7) * 3).to(torch.bfloat16)
+    x[0, 0] = float("inf")
+    x[0, 1] = float("nan")
+    x[0, 2] = -float("inf")
+    got = np_(ops.act_fp8_e4m3_roundtrip(x.to(DEV)))
+    want = omoe.fp8_roundtrip_bf16(x.float().numpy())
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+    m = ~np.isnan(want)
+    assert np.array_equal(got[m], want[m])
+
+
+# ------------------------------------------------------------------ routing
+ROUTE_CASES = [(16, 8, 2, 0.0), (1, 256, 8, 0.0), (8, 256, 8, 0.0), (16, 256, 8, 0.0),
+               (64, 256, 8, 0.0), (512, 256, 8, 0.0), (1, 512, 22, 0.0), (4, 512, 22, 0.0),
+               (64, 512, 22, 0.0), (8192, 256, 8, 1.1), (5, 8, 8, 0.0), (3, 1, 1, 0.0),
+               (37, 1024, 64, 0.0)]
+
+
+@pytest.mark.parametrize("T,E,k,zipf", ROUTE_CASES)
+def test_route_permute_bit_exact(T, E, k, zipf):
+    say("route", T, E, k, zipf)
+    wl = inputs.Workload("route_test", T=T, E=E, k=k, H=64, F=64, mode="w4a16", zipf=zipf)
+    lg = inputs.router_logits(wl)
+    if T >= 2:
+        lg[1, :] = 0.25                           # an all-tie row
+    r = ops.moe_route_permute(lg.to(DEV), k)
+    torch.cuda.synchronize()
+    ids, w = omoe.route(lg.numpy(), k)
+    perm = omoe.permute(ids, E)
+    assert np.array_equal(np_(r["topk_ids"]), ids)
+    np.testing.assert_allclose(np_(r["topk_w"]), w, rtol=1e-6, atol=0)
+    assert np.array_equal(np_(r["expert_offsets"]), perm["offsets"])
+    assert np.array_equal(np_(r["sorted_slot"]), perm["sorted_slot"])
+    assert np.array_equal(np_(r["slot_to_row"]), perm["slot_to_row"])
+    na = int(np_(r["n_active"])[0])
+    assert na == len(perm["active"])
+    act = np_(r["active_experts"])
+    assert np.array_equal(act[:na], perm["active"]) and np.all(act[na:] == -1)
+
+
+def test_route_permute_is_deterministic():
+    say("route determinism")
+    wl = inputs.WORKLOADS["prefill"]
+    lg = inputs.router_logits(wl).to(DEV)
+    a = ops.moe_route_permute(lg, wl.k)
+    b = ops.moe_route_permute(lg, wl.k)
+    for key in a:
+        assert torch.equal(a[key], b[key]), key
+
+
+# ------------------------------------------------------------------ grouped GEMM
+def _problem(counts, Nw, K, seed, mode=ops.W4A16, T=None, k=None):
+    """Random grouped-GEMM problem with the given rows per expert (0 allowed)."""
+    E = len(counts)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    rows = int(offsets[-1])
+    active = np.array([e for e in range(E) if counts[e] > 0] + [-1] * (E - sum(c > 0 for c in counts)), np.int32)
+    n_active = np.array([sum(c > 0 for c in counts)], np.int32)
+    w = torch.stack([inputs.random_fp32((Nw, K), seed + 17 * e, std=0.02) for e in range(E)])
+    wp, ws, wg = ops.nvfp4_quantize(w.to(DEV))
+    d = dict(E=E, rows=rows, offsets=offsets, active=active, n_active=n_active, wp=wp, ws=ws, wg=wg,
+             W=[onv.dequantize(np_(wp[e]), np_(ws[e]), np_(wg)[e]) for e in range(E)])
+    if T is None:
+        a = inputs.random_fp32((rows, K), seed + 1).to(torch.bfloat16)
+        d.update(a=a, gidx=None, gdiv=1, A=a.float().numpy().astype(np.float64))
+    else:
+        a = inputs.random_fp32((T, K), seed + 1).to(torch.bfloat16)
+        gidx = np.random.default_rng(seed).integers(0, T * k, size=rows).astype(np.int32)
+        d.update(a=a, gidx=torch.from_numpy(gidx), gdiv=k,
+                 A=a.float().numpy().astype(np.float64)[gidx // k])
+    if mode == ops.W4A4:
+        aq, as_, ag = ops.nvfp4_quantize(a.to(DEV))
+        d.update(aq=aq, as_=as_, ag=ag)
+        Aq = onv.dequantize(np_(aq), np_(as_), np_(ag)[0])
+        d["A"] = Aq if d["gidx"] is None else Aq[d["gidx"].numpy() // k]
+    return d
+
+
+def _run_gemm(d, mode, epi, out_dtype):
+    t = lambda a: torch.from_numpy(a).to(DEV)
+    kw = dict(rows=d["rows"], out_dtype=out_dtype, gather_div=d["gdiv"],
+              gather_index=None if d["gidx"] is None else d["gidx"].to(DEV))
+    if mode == ops.W4A4:
+        a = d["aq"]
+        kw.update(a_scales=d["as_"], a_g=d["ag"])
+    else:
+        a = d["a"].to(DEV)
+    out = ops.moe_grouped_gemm_nvfp4(mode, epi, a, d["wp"], d["ws"], d["wg"], t(d["offsets"]),
+                                     t(d["active"]), t(d["n_active"]), **kw)
+    torch.cuda.synchronize()
+    return np_(out)
+
+
+GEMM_CASES = [
+    # counts per expert, Nw, K
+    ([3, 0, 16, 17, 1], 64, 64),
+    ([40, 0, 2], 160, 96),          # > 32 rows (two token passes), K % 128 != 0, Nw/16 = 10
+    ([5, 33, 0, 0, 64], 1024, 256),
+    ([1] * 8, 256, 512),
+    ([12, 20], 96, 6144),
+    ([1, 2, 3], 2048, 6144),
+]
+
+
+@pytest.mark.parametrize("counts,Nw,K", GEMM_CASES)
+@pytest.mark.parametrize("epi", [ops.EPI_NONE, ops.EPI_SWIGLU])
+def test_grouped_gemm_w4a16(counts, Nw, K, epi):
+    say("gemm w4a16", counts, Nw, K, epi)
+    d = _problem(counts, Nw, K, seed=Nw + K)
+    want = omoe.grouped_gemm(d["A"], d["offsets"], d["W"], "swiglu" if epi else "none")
+    got32 = _run_gemm(d, ops.W4A16, epi, torch.float32)
+    assert ops.last_dispatch() in (1, 2)
+    assert_finite(got32)
+    r = rel_fro(got32, want)
+    assert r <= W4A16_TOL and r < 1e-5, r
+    got16 = _run_gemm(d, ops.W4A16, epi, torch.bfloat16)
+    assert_finite(got16)
+    assert rel_fro(got16, omoe.bf16_round(want)) <= W4A16_TOL
+
+
+def test_grouped_gemm_w4a16_gather():
+    say("gemm gather")
+    d = _problem([7, 0, 30, 9], 128, 256, seed=5, T=20, k=3)
+    want = omoe.grouped_gemm(d["A"], d["offsets"], d["W"], "swiglu")
+    got = _run_gemm(d, ops.W4A16, ops.EPI_SWIGLU, torch.float32)
+    assert rel_fro(got, want) < 1e-5
+
+
+@pytest.mark.parametrize("counts,Nw,K", GEMM_CASES[:4])
+def test_grouped_gemm_w4a4(counts, Nw, K):
+    say("gemm w4a4", counts, Nw, K)
+    d = _problem(counts, Nw, K, seed=3 * Nw + K, mode=ops.W4A4)
+    for epi in (ops.EPI_NONE, ops.EPI_SWIGLU):
+        want = omoe.grouped_gemm(d["A"], d["offsets"], d["W"], "swiglu" if epi else "none")
+        got = _run_gemm(d, ops.W4A4, epi, torch.float32)
+        assert_finite(got)
+        r = rel_fro(got, want)
+        assert r <= W4A4_TOL and r < 1e-5, r      # identical NVFP4 operands: exact products
+
+
+def test_grouped_gemm_amax_output():
+    say("gemm amax")
+    d = _problem([9, 4], 64, 128, seed=11)
+    t = lambda a: torch.from_numpy(a).to(DEV)
+    out, amax = ops.moe_grouped_gemm_nvfp4(ops.W4A16, ops.EPI_SWIGLU, d["a"].to(DEV), d["wp"], d["ws"], d["wg"],
+                                           t(d["offsets"]), t(d["active"]), t(d["n_active"]),
+                                           out_dtype=torch.float32, want_amax=True)
+    torch.cuda.synchronize()
+    assert np_(amax)[0] == np.abs(np_(out)).max()
+
+
+# ------------------------------------------------------------------ reduce
+@pytest.mark.parametrize("T,k,H,ydt", [(16, 2, 256, torch.float32), (7, 22, 64, torch.bfloat16),
+                                       (512, 8, 6144, torch.float32)])
+def test_unpermute_reduce(T, k, H, ydt):
+    say("reduce", T, k, H, ydt)
+    rng = np.random.default_rng(T + k + H)
+    y = inputs.random_fp32((T * k, H), T * k).to(ydt)
+    s2r = rng.permutation(T * k).astype(np.int32)
+    w = rng.random((T, k)).astype(np.float32)
+    got = np_(ops.moe_unpermute_reduce(y.to(DEV), torch.from_numpy(s2r).to(DEV), torch.from_numpy(w).to(DEV)))
+    want = omoe.bf16_round(omoe.unpermute_reduce(y.float().numpy().astype(np.float64), s2r, w.astype(np.float64)))
+    assert_finite(got)
+    assert rel_fro(got, want) <= W4A16_TOL
