@@ -1,0 +1,265 @@
+"""Benchmark of the NVFP4 MoE hot path on one MI355X.
+
+A step is one whole MoE layer forward over one batch: route + permute -> up/gate grouped
+GEMM with fused SwiGLU -> down grouped GEMM -> weighted unpermute-reduce, all through the
+C ABI. Default workload: the decode MoE layer with 256 experts, top-8, 512 tokens
+(~16 rows per expert), hidden 6144, expert FFN 2048, NVFP4 weights, bf16 activations
+(W4A16) -- the workload behind the pages' "0.8-55 TFLOPS at per-expert M=16-64" ("The 2x
+Gap", section "The Investigation So Far").
+
+Prints ONE JSON line: throughput (algorithmic TFLOP/s of the layer), the dominant kernel's
+HBM roofline (weight+scale+activation bytes per launch / launch time from HIP events
+recorded on the kernels' stream inside the timed region), and the oracle's CPU rate on a
+bounded sample of the same workload.
+
+Usage: python bench.py [--steps K] [--warmup W] [--tokens T] [--workload NAME]
+       [--no-cpu-baseline] [--sweep FILE] [--copy-calibration]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0      # dense; the f16 MFMA runs at the same rate
+FP4_PEAK_TFLOPS = 10100.0
+PAGES_DECODE_TFLOPS = (0.8, 55.0)   # RTX PRO 6000 (SM120), FP4, per-expert M=16-64
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="decode")
+    p.add_argument("--tokens", type=int, default=None)
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=12.0)
+    p.add_argument("--sweep", default=None, help="also write per-T results of the workload's sweep to FILE")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="run a plain 1 GiB device copy (for scaling HBM counters) and exit")
+    return p.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              "(see DESIGN.md for how the layer would shard); use --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    from nvfp4_block_scaled_moe_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    from nvfp4_block_scaled_moe_amd import inputs, layer, ops
+
+    dev = "cuda"
+    if args.copy_calibration:
+        a = torch.empty(1 << 28, dtype=torch.float32, device=dev)   # 1 GiB
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": a.numel() * 4, "copy_calibration_bytes_written": b.numel() * 4}))
+        return
+
+    wl = inputs.WORKLOADS[args.workload]
+    T = args.tokens or wl.T
+    mode = ops.W4A16 if wl.mode == "w4a16" else ops.W4A4
+    t0 = time.time()
+    w = layer.quantize_experts(wl, dev)
+    x = inputs.activations_bf16(wl, T).to(dev)
+    lg = inputs.router_logits(wl, T).to(dev)
+    torch.cuda.synchronize()
+    setup_s = time.time() - t0
+    print(f"[bench] setup {setup_s:.1f}s: {wl.name} T={T} E={wl.E} k={wl.k} H={wl.H} F={wl.F} mode={wl.mode}",
+          file=sys.stderr, flush=True)
+
+    res = measure(torch, ops, layer, wl, w, x, lg, T, mode, args.steps, args.warmup)
+    line = dict(
+        metric="MoE NVFP4 grouped-GEMM TFLOPS + weight GB/s vs tokens/expert, % roofline",
+        value=round(res["tflops"], 2), unit="TFLOP/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
+        ms_per_step=round(res["ms_per_step"], 4), higher_is_better=True, scaling="weak",
+        vs_baseline=(round(res["tflops"] / PAGES_DECODE_TFLOPS[1], 2)
+                     if (wl.name == "decode" and T == 512) else None),
+        dtype="f16", data="synthetic",
+        config=dict(workload=describe(wl, T), tokens=T, experts=wl.E, top_k=wl.k, hidden=wl.H,
+                    ffn=wl.F, mode=wl.mode.upper(), tokens_per_expert=round(T * wl.k / wl.E, 3),
+                    touched_experts=res["touched"], compute="NVFP4 weights decoded exactly to f16, "
+                    "v_mfma_f32_16x16x32_f16, fp32 accumulation"),
+        weight_GBps=round(res["weight_gbs"], 1),
+        weight_hbm_frac=round(res["weight_gbs"] / HBM_PEAK_GBS, 4),
+        stage_us=res["stage_us"],
+        roofline=res["roofline"],
+        baseline_context=("pages: 0.8-55 TFLOPS for FP4 MoE GEMMs at per-expert M=16-64 (256 experts, "
+                          "top-8, 512 concurrent) on RTX PRO 6000 Blackwell SM120; vs_baseline divides by 55"),
+    )
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(torch, wl, w, x, lg, T, mode, args.cpu_seconds)
+    else:
+        line["cpu_baseline"] = None
+    if args.sweep:
+        rows = []
+        for Ts in wl.sweep or (T,):
+            xs = inputs.activations_bf16(wl, Ts).to(dev)
+            ls = inputs.router_logits(wl, Ts).to(dev)
+            r = measure(torch, ops, layer, wl, w, xs, ls, Ts, mode, max(5, args.steps // 2), 2, graph=True)
+            rows.append(dict(tokens=Ts, tokens_per_expert=Ts * wl.k / wl.E, **{k: v for k, v in r.items()}))
+            print(f"[bench] sweep T={Ts}: {r['tflops']:.1f} TFLOP/s, weights {r['weight_gbs']:.0f} GB/s",
+                  file=sys.stderr, flush=True)
+        with open(args.sweep, "w") as f:
+            json.dump(dict(workload=wl.name, rows=rows), f, indent=1)
+    print(json.dumps(line), flush=True)
+
+
+def describe(wl, T):
+    return (f"{wl.name} MoE layer: {wl.E} experts, top-{wl.k}, {T} tokens, hidden {wl.H}, "
+            f"expert FFN {wl.F}, {wl.mode.upper()}" + (", FP8 activations" if wl.act == "fp8" else "")
+            + (f", Zipf({wl.zipf}) routing bias" if wl.zipf else ""))
+
+
+def layer_work(wl, T, touched):
+    S = T * wl.k
+    flops = 2.0 * S * (2 * wl.F * wl.H + wl.H * wl.F)
+    w13 = touched * (2 * wl.F) * wl.H * 9 / 16          # packed (1/2 B) + E4M3 scales (1/16 B)
+    w2 = touched * wl.H * wl.F * 9 / 16
+    return flops, w13, w2
+
+
+def measure(torch, ops, layer, wl, w, x, lg, T, mode, steps, warmup, graph=False):
+    """Time `steps` layer forwards; HIP events on the current stream bracket every stage."""
+    k = wl.k
+    fp8 = wl.act == "fp8"
+    S = T * k
+    r = ops.moe_route_permute(lg, k)
+    torch.cuda.synchronize()
+    touched = int(r["n_active"].item())
+    flops, w13_bytes, w2_bytes = layer_work(wl, T, touched)
+
+    def step(ev=None):
+        mark = (lambda i: ev[i].record()) if ev else (lambda i: None)
+        mark(0)
+        xx = ops.act_fp8_e4m3_roundtrip(x) if fp8 else x
+        rr = ops.moe_route_permute(lg, k)
+        mark(1)
+        common = dict(expert_offsets=rr["expert_offsets"], active_experts=rr["active_experts"],
+                      n_active=rr["n_active"])
+        if mode == ops.W4A16:
+            h = ops.moe_grouped_gemm_nvfp4(ops.W4A16, ops.EPI_SWIGLU, xx, w.w13_packed, w.w13_scales, w.w13_g,
+                                           gather_index=rr["sorted_slot"], gather_div=k, rows=S,
+                                           out_dtype=torch.bfloat16, **common)
+            mark(2)
+            y = ops.moe_grouped_gemm_nvfp4(ops.W4A16, ops.EPI_NONE, h, w.w2_packed, w.w2_scales, w.w2_g,
+                                           rows=S, out_dtype=torch.float32, **common)
+        else:
+            xq, xs, xg = ops.nvfp4_quantize(xx)
+            h, amax = ops.moe_grouped_gemm_nvfp4(ops.W4A4, ops.EPI_SWIGLU, xq, w.w13_packed, w.w13_scales,
+                                                 w.w13_g, a_scales=xs, a_g=xg, gather_index=rr["sorted_slot"],
+                                                 gather_div=k, rows=S, out_dtype=torch.float32,
+                                                 want_amax=True, **common)
+            mark(2)
+            hq, hs, hg = ops.nvfp4_quantize(h, amax=amax)
+            y = ops.moe_grouped_gemm_nvfp4(ops.W4A4, ops.EPI_NONE, hq, w.w2_packed, w.w2_scales, w.w2_g,
+                                           a_scales=hs, a_g=hg, rows=S, out_dtype=torch.float32, **common)
+        mark(3)
+        out = ops.moe_unpermute_reduce(y, rr["slot_to_row"], rr["topk_w"])
+        mark(4)
+        return out
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    if graph:
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        g.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            g.replay()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        stage = None
+    else:
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            step(evs[i])
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / steps
+        names = ["route_permute", "up_gate_swiglu", "down", "unpermute_reduce"]
+        stage = {n: round(1e3 * sum(e[j].elapsed_time(e[j + 1]) for e in evs) / steps, 2)
+                 for j, n in enumerate(names)}
+    act_in = T * wl.H * 2
+    h_bytes = S * wl.F * (2 if mode == ops.W4A16 else 4)
+    up_bytes = w13_bytes + act_in + h_bytes
+    res = dict(ms_per_step=ms, tflops=flops / (ms * 1e-3) / 1e12,
+               weight_gbs=(w13_bytes + w2_bytes) / (ms * 1e-3) / 1e9, touched=touched, stage_us=stage)
+    if stage:
+        up_us = stage["up_gate_swiglu"]
+        ach = up_bytes / (up_us * 1e-6) / 1e9
+        res["roofline"] = dict(
+            bound="hbm", kernel="gemm_stream_kernel (up/gate + SwiGLU)", achieved=round(ach, 1),
+            peak=HBM_PEAK_GBS, unit="GB/s", frac=round(ach / HBM_PEAK_GBS, 4), traffic=None,
+            bytes_per_launch=int(up_bytes), launch_us=up_us,
+            bytes_note="W13 packed+scales of touched experts (9/16 B/weight) + bf16 activations in + h out")
+    return res
+
+
+def cpu_baseline(torch, wl, w, x, lg, T, mode, seconds):
+    """The oracle (float64 NumPy) on a bounded sample of the same layer: per-expert
+    dequantize + up/gate GEMM + SwiGLU + down GEMM for as many active experts as fit in
+    about `seconds`, scaled to TFLOP/s of algorithmic work."""
+    import numpy as np
+    from oracle import moe as omoe
+    from oracle import nvfp4 as onv
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    lgn = lg.cpu().numpy()
+    ids, rw = omoe.route(lgn, wl.k)
+    perm = omoe.permute(ids, wl.E)
+    xs = x.float().cpu().numpy().astype(np.float64)
+    tok = perm["sorted_slot"] // wl.k
+    offsets = perm["offsets"]
+    order = [int(e) for e in perm["active"]]
+    done_rows, done_experts, flops = 0, 0, 0.0
+    t_total = 0.0
+    for e in order:
+        q13 = (w.w13_packed[e].cpu().numpy(), w.w13_scales[e].cpu().numpy(), w.w13_g[e].item())
+        q2 = (w.w2_packed[e].cpu().numpy(), w.w2_scales[e].cpu().numpy(), w.w2_g[e].item())
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        t0 = time.perf_counter()
+        A = xs[tok[r0:r1]]
+        h = omoe.bf16_round(omoe.swiglu(A @ onv.dequantize(*q13).T))
+        _ = h @ onv.dequantize(*q2).T
+        t_total += time.perf_counter() - t0
+        done_rows += r1 - r0
+        done_experts += 1
+        flops += 2.0 * (r1 - r0) * 3 * wl.F * wl.H
+        if t_total >= seconds:
+            break
+    return dict(value=round(flops / t_total / 1e12, 6), unit="TFLOP/s", cores=int(threads), kind="oracle",
+                sample=f"{done_experts} of {len(order)} active experts ({done_rows} of {T * wl.k} routed rows) "
+                       f"of the same layer: float64 dequantize + up/gate + SwiGLU + down, {t_total:.1f} s")
+
+
+if __name__ == "__main__":
+    main()

@@ -163,7 +163,8 @@ size_t moe_route_permute_workspace_size(int32_t T, int32_t E, int32_t k);
  *               dense GEMM: E = 1, offsets {0, rows}, active {0}, n_active {1}).
  *   E, rows, Nw, K  1 <= E <= 1024; rows = expert_offsets[E] >= 1; Nw >= 32, Nw % 32 == 0
  *               (EPI_SWIGLU: gate rows 0..Nw/2-1, up rows Nw/2..Nw-1); K >= 32, K % 32 == 0;
- *               rows * max(K, Nw) < 2^31. a and w_packed 16-byte aligned, scale arrays
+ *               rows * max(K, Nw) < 2^31, a_rows * K * 2 < 2^31, Nw * K / 2 < 2^31.
+ *               a and w_packed 16-byte aligned, scale arrays
  *               2-byte aligned.
  *   out         device, out_dtype (F32 or BF16), [rows, EPI_SWIGLU ? Nw/2 : Nw].
  *   out_amax    device float[1] or NULL: if given, set to max |out| over the call (exact;

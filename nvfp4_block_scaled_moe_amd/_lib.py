@@ -10,7 +10,8 @@ import ctypes
 import os
 import threading
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libnvfp4moe.so")
+LIB_PATH = os.environ.get("NVFP4MOE_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                          "libnvfp4moe.so")
 
 # enums (include/nvfp4moe.h)
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)

@@ -10,6 +10,12 @@
 // keeps 11 significant bits, bf16 has 8); the GEMM epilogue multiplies by 2^p again.
 // Non-finite values stay Inf/NaN.
 //
+// Output layout (the GEMM's operand order): rows padded with zeros to K128 = K rounded up
+// to 128, and inside every 128-wide chunk the 8-element pieces are transposed: logical
+// k = 32*g + 8*j + i is stored at 32*j + 8*g + i. The GEMM lane group g feeds MFMA j with
+// logical k 32g+8j..+7, so the four lane groups of one token read 64 contiguous bytes per
+// load instruction (one cache line instead of four).
+//
 // One workgroup per row: pass 1 finds the row's finite amax, pass 2 converts (the row is
 // re-read from L2). Traffic: 2 bytes read + 2 bytes written per element.
 #include "common.h"
@@ -26,8 +32,9 @@ __global__ __launch_bounds__(kPrepThreads) void act_prep_kernel(const uint16_t* 
                                                                 _Float16* __restrict__ a16,
                                                                 int* __restrict__ rexp) {
   const int64_t r = blockIdx.x;
+  const int K128 = (K + 127) & ~127;
   const uint16_t* row = a + r * (int64_t)K;
-  _Float16* orow = a16 + r * (int64_t)K;
+  _Float16* orow = a16 + r * (int64_t)K128;
   const int nvec = K / 8;
   float m = 0.0f;
   for (int i = threadIdx.x; i < nvec; i += kPrepThreads) {
@@ -53,16 +60,20 @@ __global__ __launch_bounds__(kPrepThreads) void act_prep_kernel(const uint16_t* 
     p = ex - 15;              // amax * 2^-p in [2^14, 2^15)
   }
   if (threadIdx.x == 0) rexp[r] = p;
-  for (int i = threadIdx.x; i < nvec; i += kPrepThreads) {
-    uint4 q = *reinterpret_cast<const uint4*>(row + 8 * i);
-    uint32_t w[4] = {q.x, q.y, q.z, q.w};
-    f16x8 o;
+  for (int i = threadIdx.x; i < K128 / 8; i += kPrepThreads) {
+    f16x8 o = (f16x8){0, 0, 0, 0, 0, 0, 0, 0};
+    if (i < nvec) {
+      uint4 q = *reinterpret_cast<const uint4*>(row + 8 * i);
+      uint32_t w[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      o[2 * j] = (_Float16)ldexpf(bf16_to_f32(w[j] & 0xffffu), -p);
-      o[2 * j + 1] = (_Float16)ldexpf(bf16_to_f32(w[j] >> 16), -p);
+      for (int j = 0; j < 4; ++j) {
+        o[2 * j] = (_Float16)ldexpf(bf16_to_f32(w[j] & 0xffffu), -p);
+        o[2 * j + 1] = (_Float16)ldexpf(bf16_to_f32(w[j] >> 16), -p);
+      }
     }
-    *reinterpret_cast<f16x8*>(orow + 8 * i) = o;
+    // piece i = 16 * c + 4 * g + j (logical k = 128 c + 32 g + 8 j) -> physical 16 c + 4 j + g
+    const int c = i >> 4, g = (i >> 2) & 3, jj = i & 3;
+    *reinterpret_cast<f16x8*>(orow + 8 * (16 * c + 4 * jj + g)) = o;
   }
 }
 

@@ -56,7 +56,8 @@ struct GemmWs {
 GemmWs gemm_ws_layout(nvfp4moe_mode mode, int64_t a_rows, int32_t K) {
   GemmWs w{0, 0, 0};
   if (mode == NVFP4MOE_W4A16) {
-    w.a16_bytes = round_up((size_t)a_rows * (size_t)K * 2);
+    const size_t K128 = ((size_t)K + 127) / 128 * 128;  // rows padded to whole 128-k chunks
+    w.a16_bytes = round_up((size_t)a_rows * K128 * 2);
     w.rexp_bytes = round_up((size_t)a_rows * 4);
   }
   w.total = w.a16_bytes + w.rexp_bytes;
@@ -190,8 +191,10 @@ nvfp4moe_status moe_grouped_gemm_nvfp4(nvfp4moe_mode mode, nvfp4moe_epilogue epi
     return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: need K >= 32 and K %% 32 == 0 (K=%d)", fn, K);
   if ((int64_t)rows * (K > Nw ? K : Nw) >= (int64_t(1) << 31))
     return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: rows * max(K, Nw) must be < 2^31", fn);
-  if (a_rows * (int64_t)K >= (int64_t(1) << 40))
-    return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: a_rows * K too large", fn);
+  if (a_rows * (int64_t)((K + 127) / 128 * 128) * 2 >= (int64_t(1) << 31))
+    return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: a_rows * K * 2 must be < 2^31", fn);
+  if ((int64_t)Nw * (K / 2) >= (int64_t(1) << 31))
+    return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: Nw * K / 2 must be < 2^31", fn);
   if (!gather_index && a_rows != rows)
     return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: without gather_index a_rows must equal rows", fn);
   if (gather_index && gather_div < 1)
@@ -222,6 +225,7 @@ nvfp4moe_status moe_grouped_gemm_nvfp4(nvfp4moe_mode mode, nvfp4moe_epilogue epi
   g.rows = rows;
   g.Nw = Nw;
   g.K = K;
+  g.a_rows = (int)a_rows;
   g.swiglu = epi == NVFP4MOE_EPI_SWIGLU;
   g.out = out;
   g.out_bf16 = out_dtype == NVFP4MOE_BF16;

@@ -45,6 +45,7 @@ struct GemmArgs {
   const int* active;               // [E]
   const int* n_active;             // [1]
   int E, rows, Nw, K;
+  int a_rows;                       // rows of the activation tensor (< 2^31 bytes of it)
   int swiglu;
   void* out;
   int out_bf16;
