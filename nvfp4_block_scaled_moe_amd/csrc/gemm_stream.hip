@@ -6,29 +6,32 @@
 // used by at most a few rows and the kernel is bound by HBM bandwidth on weight + scale
 // bytes (9/16 byte per weight). The design streams each weight exactly once:
 //
-//   * Workgroup = WAVES wavefronts = one (expert, block of 16*RB weight rows) tile; the
-//     waves split K in 128-wide chunks (wave w takes chunks w, w+WAVES, ...), so the
-//     activation fragments a wave needs are needed by no other wave of the workgroup.
-//   * Each lane loads 16 bytes of one weight row per chunk (32 FP4 codes); lanes
-//     16g..16g+15 take 16 consecutive rows at k-offset 32g. Loads go through buffer
-//     resources: 32-bit offsets, the row-block offset in an SGPR, and out-of-range offsets
-//     returning zero, which handles the K tail and padded token lanes without branches.
-//   * The tile's E4M3 scales are copied to LDS once with coalesced 16-byte loads; per chunk
-//     a lane reads its two scale bytes from LDS. (Reading them from memory per chunk costs
-//     a cache-line access per 2 bytes and starved the L1.)
-//   * Activations (W4A16) come from the f16 copy written in MFMA operand order, so the four
-//     lane groups of a token read one contiguous 64-byte piece per load instruction.
-//   * Software pipelining: the fragments of the wave's next chunk are in flight while the
-//     current chunk is decoded and multiplied (two register buffers).
+//   * Workgroup = WAVES wavefronts = one (expert, block of 16*RBW*WAVES weight rows) tile.
+//     Each wave owns RBW blocks of 16 rows over the whole K range (for SwiGLU: matching
+//     gate and up blocks), so its FP32 accumulators hold finished dot products and the
+//     epilogue needs no cross-wave reduction.
+//   * Weights: each lane loads 16 bytes (32 FP4 codes) of one row per 128-wide K chunk;
+//     lanes 16g..16g+15 take 16 consecutive rows at k-offset 32g, so one wave load reads
+//     16 rows x 64 contiguous bytes. Loads go through buffer resources (32-bit offsets,
+//     block offsets in SGPRs, out-of-range offsets read zero) into a register ring
+//     kDepth chunks deep; a ring entry is re-filled as soon as it has been decoded.
+//   * Activations (the MFMA B operand) are shared by the waves: per chunk the workgroup
+//     copies the 16 or 32 token rows' 128-k slice into a two-slot LDS ring with one
+//     16-byte load per thread, then every wave reads its fragments from LDS. W4A16
+//     activations come from an f16 copy written in MFMA operand order; W4A4 activations
+//     are FP4 and are decoded like the weights. LDS rows are XOR-swizzled per token so the
+//     fragment reads are bank-conflict free.
+//   * Weight scales: per 1024-k window each lane loads 16 bytes of its row's E4M3 scales
+//     (one load per window instead of a 2-byte load per chunk) into a wave-private LDS
+//     area, from which it reads the two scales of each chunk.
 //   * Decode in registers: hardware FP4 -> f16 convert and one packed f16 multiply by the
 //     block scale per two weights. Both steps are exact (E2M1 * E4M3 has <= 6 significant
 //     bits), so the MFMA sees exactly the dequantized weights.
-//   * v_mfma_f32_16x16x32_f16 with the weights as the 16x32 A operand and up to 16 token
-//     rows as the 32x16 B operand, FP32 accumulation in registers over the wave's K range.
-//     Rows of an expert beyond 16*TBM are handled in further passes.
-//   * The K partial sums of the waves are added in LDS in a fixed order (deterministic);
-//     the epilogue applies the float32 global scales (w_g, and a_g for W4A4, or the
-//     power-of-two row scale of the f16 activations), SwiGLU when asked, and stores.
+//   * v_mfma_f32_16x16x32_f16 with the weights as the 16x32 A operand and 16 token rows as
+//     the 32x16 B operand, FP32 accumulation in registers over all of K. Experts with more
+//     than 32 rows are handled in further 32-row passes.
+//   * Epilogue per wave: float32 global scales (w_g; a_g for W4A4, or the power-of-two
+//     row scale of the f16 activations), SwiGLU when asked, 8- or 16-byte stores.
 //   * Tiles are numbered expert-major and handed out XCD-major (workgroup i runs on XCD
 //     i mod 8), so the tiles of one expert, which share its activation rows, share an L2.
 #include <cstdio>
@@ -41,8 +44,12 @@ namespace nvfp4moe {
 
 namespace {
 
-constexpr int kChunk = 128;              // k per lane-load round (16 bytes of FP4 per lane)
+constexpr int kChunk = 128;              // k per chunk (16 bytes of FP4 per lane)
+constexpr int kWin = 8;                  // chunks per scale window (1024 k)
+constexpr int kDepth = 4;                // weight chunks in flight per wave
+constexpr int kSPitch = 80;              // LDS pitch of a 64-byte scale row (bank spread)
 constexpr uint32_t kOOB = 0x80000000u;   // buffer offset past every resource: loads return 0
+constexpr uint32_t kNoDst = 0xffffffffu;
 constexpr int kRsrcFlags = 0x00020000;   // raw buffer resource word 3 for gfx9 (32-bit data)
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -57,29 +64,27 @@ __device__ __forceinline__ uint32_t ld16(__amdgpu_buffer_rsrc_t r, uint32_t voff
   return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
 }
 
-template <int RB, int NTB, bool A4>
-struct Frag {
-  u32x4 w[RB];               // 32 FP4 weights of this lane's row, per row block
-  u32x4 b[NTB][A4 ? 1 : 4];  // W4A16: 4 x 8 f16 activations; W4A4: 32 FP4 codes
-  uint32_t bs[NTB];          // W4A4: two E4M3 activation scales
-};
-
 template <int N>
 struct Int {
   static constexpr int value = N;
 };
 
-// LDS row pitch of the staged weight scales (16-byte aligned, padded against bank conflicts).
-__host__ __device__ constexpr int scale_pitch(int Ks) { return ((Ks + 15) & ~15) + 16; }
+template <int TBM, bool A4>
+struct Ring {
+  // per slot: (16*TBM tokens) x (256 B of f16 per token | 64 B of FP4 codes), then for
+  // W4A4 the tokens' 8 scale bytes of the chunk
+  static constexpr int kTokBytes = A4 ? 64 : 256;
+  static constexpr int kCodes = 16 * TBM * kTokBytes;
+  static constexpr int kSlot = kCodes + (A4 ? 16 * TBM * 8 : 0);
+  static constexpr int kBytes = 2 * kSlot;
+};
 
-template <int RB, int WAVES, int TBM, bool SWIGLU, bool A4>
-__global__ __launch_bounds__(WAVES * kWave) void gemm_stream_kernel(const GemmArgs p,
-                                                                    int tiles_per_expert,
-                                                                    int total_tiles) {
-  static_assert(RB % 2 == 0, "row blocks come in pairs");
-  static_assert(TBM == 2, "token blocks per pass");
+template <int RBW, int WAVES, int TBM, bool SWIGLU, bool A4>
+__global__ __launch_bounds__(WAVES* kWave) void gemm_stream_kernel(const GemmArgs p, int tiles_per_expert,
+                                                                   int total_tiles) {
+  static_assert(RBW % 2 == 0, "row blocks per wave come in pairs");
+  using R = Ring<TBM, A4>;
   constexpr int NT = WAVES * kWave;
-  constexpr int PER_BLK = TBM * 256;  // floats of one 16-row block for TBM token blocks
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -97,26 +102,35 @@ __global__ __launch_bounds__(WAVES * kWave) void gemm_stream_kernel(const GemmAr
   const int K = p.K, Nw = p.Nw, Kh = K >> 1, Ks = K >> 4;
   const int K128 = (K + 127) & ~127;
   const int F = Nw >> 1;
-  const int Ksp = scale_pitch(Ks);
-  unsigned char* sc = smem;                                    // [16*RB][Ksp] weight scales
-  float* red = reinterpret_cast<float*>(smem + 16 * RB * Ksp);  // [WAVES][2][PER_BLK]
+  const int nch = (K + kChunk - 1) / kChunk;
+  const int nwin = (nch + kWin - 1) / kWin;
 
-  // Weight rows: tile row 0, lane row of block 0, and the (uniform) row offset of block b.
-  const int row0 = SWIGLU ? nb * 8 * RB : nb * 16 * RB;
+  unsigned char* ring = smem;                                           // [2][R::kSlot]
+  unsigned char* sws = smem + R::kBytes + wave * (2 * RBW * 16 * kSPitch);  // wave's scales
+
+  // First row of this wave's block b (the lane adds l16).
   auto blkrow = [&](int b) -> int {
-    if (SWIGLU) return b < RB / 2 ? 16 * b : F + 16 * (b - RB / 2);
-    return 16 * b;
+    if (SWIGLU) {
+      constexpr int hb = RBW / 2;
+      const int gate0 = (nb * WAVES + wave) * 16 * hb;
+      return b < hb ? gate0 + 16 * b : F + gate0 + 16 * (b - hb);
+    }
+    return (nb * WAVES + wave) * 16 * RBW + 16 * b;
   };
-  const unsigned char* wsc = p.w_scales + (size_t)e * Nw * Ks;
   const __amdgpu_buffer_rsrc_t wr =
       make_rsrc(p.w_packed + (size_t)e * Nw * Kh, (uint32_t)Nw * (uint32_t)Kh);
-  const uint32_t wlane = (uint32_t)(row0 + l16) * Kh + 16 * g;
+  const __amdgpu_buffer_rsrc_t sr =
+      make_rsrc(p.w_scales + (size_t)e * Nw * Ks, (uint32_t)Nw * (uint32_t)Ks);
+  const uint32_t wlane = (uint32_t)(blkrow(0) + l16) * Kh + 16 * g;
+  const uint32_t slane = (uint32_t)(blkrow(0) + l16) * Ks + 16 * g;
+  uint32_t wsoff[RBW], ssoff[RBW];
+#pragma unroll
+  for (int b = 0; b < RBW; ++b) {
+    wsoff[b] = __builtin_amdgcn_readfirstlane((uint32_t)(blkrow(b) - blkrow(0)) * Kh);
+    ssoff[b] = __builtin_amdgcn_readfirstlane((uint32_t)(blkrow(b) - blkrow(0)) * Ks);
+  }
   const float alpha = A4 ? p.w_g[e] * p.a_g[0] : p.w_g[e];
-  const int nch = (K + kChunk - 1) / kChunk;
-  const int n_it = (nch + WAVES - 1) / WAVES;  // chunk rounds per wave (same for all waves)
-  uint32_t amax_bits = 0;
 
-  // Activation resources sized to the real tensors, so kOOB offsets read zero.
   __amdgpu_buffer_rsrc_t ar, asr;
   if (A4) {
     ar = make_rsrc(p.a_packed, (uint32_t)p.a_rows * (uint32_t)Kh);
@@ -126,104 +140,141 @@ __global__ __launch_bounds__(WAVES * kWave) void gemm_stream_kernel(const GemmAr
     asr = ar;
   }
 
-  // Stage the tile's weight scales in LDS with coalesced loads (once per tile).
-  auto stage_scales = [&]() {
-    if ((Ks & 15) == 0) {
-      const int per_row = Ks >> 4;
-      for (int u = tid; u < 16 * RB * per_row; u += NT) {
-        const int lr = u / per_row, cu = u - lr * per_row;
-        const int row = row0 + blkrow(lr >> 4) + (lr & 15);
-        *reinterpret_cast<uint4*>(sc + lr * Ksp + 16 * cu) =
-            *reinterpret_cast<const uint4*>(wsc + (size_t)row * Ks + 16 * cu);
-      }
-    } else {
-      const int per_row = Ks >> 1;
-      for (int u = tid; u < 16 * RB * per_row; u += NT) {
-        const int lr = u / per_row, cu = u - lr * per_row;
-        const int row = row0 + blkrow(lr >> 4) + (lr & 15);
-        *reinterpret_cast<uint16_t*>(sc + lr * Ksp + 2 * cu) =
-            *reinterpret_cast<const uint16_t*>(wsc + (size_t)row * Ks + 2 * cu);
-      }
-    }
-  };
+  // Activation staging roles: thread -> (token, 16-byte piece) of a chunk slice.
+  constexpr int TPT = A4 ? 4 : 16;             // threads per token
+  constexpr int TPR = NT / TPT;                // tokens per round
+  constexpr int ROUNDS = (16 * TBM + TPR - 1) / TPR;
 
-  bool staged = false;
+  uint32_t amax_bits = 0;
   for (int tc = 0; tc < M; tc += 16 * TBM) {
     const int ntb = __builtin_amdgcn_readfirstlane(min(TBM, (M - tc + 15) >> 4));
-    // B-operand row offsets of this lane (token column l16 of each token block).
-    uint32_t boff[TBM], bsoff[TBM];
+    uint32_t bsrc[ROUNDS], bdst[ROUNDS], bssrc[ROUNDS], bsdst[ROUNDS];
 #pragma unroll
-    for (int tb = 0; tb < TBM; ++tb) {
-      const int t = tc + 16 * tb + l16;
-      const int r = r0 + t;
-      const uint32_t arow = (t < M) ? (uint32_t)(p.gather_index ? p.gather_index[r] / p.gather_div : r) : 0u;
-      const bool ok = t < M;
+    for (int rr = 0; rr < ROUNDS; ++rr) {
+      const int tk = rr * TPR + tid / TPT;       // token within the pass
+      const int pc = tid % TPT;                  // 16-byte piece of the token's slice
+      const int t = tc + tk;
+      const bool ok = tk < 16 * TBM && t < M;
+      const uint32_t arow = ok ? (uint32_t)(p.gather_index ? p.gather_index[r0 + t] / p.gather_div : r0 + t) : 0u;
+      bssrc[rr] = kOOB;
+      bsdst[rr] = kNoDst;
       if (A4) {
-        boff[tb] = ok ? arow * (uint32_t)Kh + 16 * g : kOOB;
-        bsoff[tb] = ok ? arow * (uint32_t)Ks + 2 * g : kOOB;
+        bsrc[rr] = ok ? arow * (uint32_t)Kh + 16 * pc : kOOB;
+        bdst[rr] = tk * R::kTokBytes + 16 * (pc ^ (tk & 3));
+        if (tk < 16 * TBM && pc == 0) {   // one thread per token also stages its 8 scale bytes
+          bssrc[rr] = ok ? arow * (uint32_t)Ks : kOOB;
+          bsdst[rr] = R::kCodes + tk * 8;
+        }
       } else {
-        boff[tb] = ok ? (arow * (uint32_t)K128 + 8 * g) * 2 : kOOB;
-        bsoff[tb] = 0;
+        bsrc[rr] = ok ? (arow * (uint32_t)K128 + 8 * pc) * 2 : kOOB;
+        bdst[rr] = tk * R::kTokBytes + 16 * (pc ^ (tk & 15));
       }
+      if (tk >= 16 * TBM) bdst[rr] = kNoDst;
     }
 
-    f32x4 acc[RB][TBM];
+    f32x4 acc[RBW][TBM];
 #pragma unroll
-    for (int b = 0; b < RB; ++b)
+    for (int b = 0; b < RBW; ++b)
 #pragma unroll
       for (int tb = 0; tb < TBM; ++tb) acc[b][tb] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
     auto kloop = [&](auto ntb_tag) {
       constexpr int NTB = decltype(ntb_tag)::value;
-      auto load = [&](Frag<RB, NTB, A4>& f, int it) {
-        const int c = wave + it * WAVES;
+      constexpr int RND = (16 * NTB + TPR - 1) / TPR;
+      u32x4 bst[RND];
+      uint32_t bsc[RND][2];
+      auto b_issue = [&](int c) {
+        // f16 rows are zero-padded to whole chunks; FP4 rows are not, so W4A4 pieces and
+        // scale pairs past K read zero (a neighbouring row's NaN scale must not leak in).
+        const bool cin = c < nch;
         const int kc = c * kChunk;
-        const bool kin = c < nch && (kc + 32 * g) < K;   // this lane group's 32 k are inside K
-        const uint32_t wo = kin ? wlane + (uint32_t)(kc >> 1) : kOOB;
 #pragma unroll
-        for (int b = 0; b < RB; ++b) f.w[b] = ld128(wr, wo, (uint32_t)blkrow(b) * Kh);
+        for (int rr = 0; rr < RND; ++rr) {
+          const bool in = A4 ? cin && (kc + 32 * (tid % TPT)) < K : cin;
+          const uint32_t step = A4 ? (uint32_t)kc / 2 : (uint32_t)kc * 2;
+          bst[rr] = ld128(ar, in ? bsrc[rr] + step : kOOB, 0);
+        }
+        if (A4) {
 #pragma unroll
-        for (int tb = 0; tb < NTB; ++tb) {
-          if (A4) {
-            f.b[tb][0] = ld128(ar, kin ? boff[tb] + (uint32_t)(kc >> 1) : kOOB, 0);
-            f.bs[tb] = ld16(asr, kin ? bsoff[tb] + (uint32_t)(kc >> 4) : kOOB, 0);
-          } else {
-            // padded rows: only chunks past the end need the out-of-range offset
-            const uint32_t o = c < nch ? boff[tb] + (uint32_t)kc * 2 : kOOB;
+          for (int rr = 0; rr < RND; ++rr) {
+            const uint32_t so = bssrc[rr] + (uint32_t)kc / 16;
+            uint32_t v[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) f.b[tb][j] = ld128(ar, o, 64 * j);
-            f.bs[tb] = 0;
+            for (int q = 0; q < 4; ++q) v[q] = ld16(asr, (cin && kc + 32 * q < K) ? so : kOOB, 2 * q);
+            bsc[rr][0] = v[0] | (v[1] << 16);
+            bsc[rr][1] = v[2] | (v[3] << 16);
           }
         }
       };
-      auto compute = [&](const Frag<RB, NTB, A4>& f, int it) {
-        const int kc = (wave + it * WAVES) * kChunk;
+      auto b_commit = [&](int slot) {
+        unsigned char* base = ring + slot * R::kSlot;
+#pragma unroll
+        for (int rr = 0; rr < RND; ++rr)
+          if (bdst[rr] != kNoDst) *reinterpret_cast<u32x4*>(base + bdst[rr]) = bst[rr];
+        if (A4) {
+#pragma unroll
+          for (int rr = 0; rr < RND; ++rr)
+            if (bsdst[rr] != kNoDst) *reinterpret_cast<uint2*>(base + bsdst[rr]) = make_uint2(bsc[rr][0], bsc[rr][1]);
+        }
+      };
+      u32x4 sst[RBW];
+      auto s_issue = [&](int w) {
+        const bool win = w < nwin && (w * kWin * kChunk + 256 * g) < K;
+        const uint32_t so = win ? slane + (uint32_t)(w * kWin * kChunk) / 16 : kOOB;
+        if ((Ks & 3) == 0) {   // dword-aligned scale rows: one 16-byte load per block
+#pragma unroll
+          for (int b = 0; b < RBW; ++b) sst[b] = ld128(sr, so, ssoff[b]);
+        } else {               // K % 64 != 0: rows are only 2-byte aligned
+#pragma unroll
+          for (int b = 0; b < RBW; ++b)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              sst[b][q] = ld16(sr, so, ssoff[b] + 4 * q) | (ld16(sr, so, ssoff[b] + 4 * q + 2) << 16);
+        }
+      };
+      auto s_commit = [&](int w) {
+        unsigned char* base = sws + (w & 1) * (RBW * 16 * kSPitch);
+#pragma unroll
+        for (int b = 0; b < RBW; ++b)
+          *reinterpret_cast<u32x4*>(base + (16 * b + l16) * kSPitch + 16 * g) = sst[b];
+      };
+      u32x4 wring[kDepth][RBW];
+      auto w_issue = [&](u32x4& dst, int c, int b) {
+        const bool kin = c < nch && (c * kChunk + 32 * g) < K;
+        dst = ld128(wr, kin ? wlane + (uint32_t)(c * kChunk) / 2 : kOOB, wsoff[b]);
+      };
+      auto compute = [&](u32x4 (&wv)[RBW], int c) {
+        const unsigned char* base = ring + (c & 1) * R::kSlot;
+        const unsigned char* sbase = sws + ((c / kWin) & 1) * (RBW * 16 * kSPitch);
+        const int soff = (c % kWin) * 8 + 2 * g;
+        const bool sin = (c * kChunk + 32 * g) < K;   // past K: weights read zero, so must scales
         f16x8 bf[NTB][4];
 #pragma unroll
         for (int tb = 0; tb < NTB; ++tb) {
+          const int tk = 16 * tb + l16;
           if (A4) {
+            const u32x4 q = *reinterpret_cast<const u32x4*>(base + tk * R::kTokBytes + 16 * (g ^ (tk & 3)));
+            const uint32_t sc2 = *reinterpret_cast<const uint16_t*>(base + R::kCodes + tk * 8 + 2 * g);
             f16x2 s0, s1;
-            decode_scale_pair(f.bs[tb], s0, s1);
-            bf[tb][0] = decode8(f.b[tb][0][0], s0);
-            bf[tb][1] = decode8(f.b[tb][0][1], s0);
-            bf[tb][2] = decode8(f.b[tb][0][2], s1);
-            bf[tb][3] = decode8(f.b[tb][0][3], s1);
+            decode_scale_pair(sc2, s0, s1);
+            bf[tb][0] = decode8(q[0], s0);
+            bf[tb][1] = decode8(q[1], s0);
+            bf[tb][2] = decode8(q[2], s1);
+            bf[tb][3] = decode8(q[3], s1);
           } else {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) bf[tb][j] = __builtin_bit_cast(f16x8, f.b[tb][j]);
+            for (int j = 0; j < 4; ++j)
+              bf[tb][j] = *reinterpret_cast<const f16x8*>(base + tk * R::kTokBytes + 16 * ((4 * j + g) ^ (tk & 15)));
           }
         }
-        // Scales of the lane's 32 k: two bytes in LDS (zero past the end of K, as the
-        // weights read there are zero too).
-        const int soff = (kc >> 4) + 2 * g;
-        const bool sin = (kc + 32 * g) < K;
 #pragma unroll
-        for (int b = 0; b < RB; ++b) {
-          const uint32_t sv = sin ? *reinterpret_cast<const uint16_t*>(sc + (16 * b + l16) * Ksp + soff) : 0u;
+        for (int b = 0; b < RBW; ++b) {
+          const uint32_t sv = sin ? *reinterpret_cast<const uint16_t*>(sbase + (16 * b + l16) * kSPitch + soff) : 0u;
           f16x2 s0, s1;
           decode_scale_pair(sv, s0, s1);
-          const f16x8 w0 = decode8(f.w[b][0], s0), w1 = decode8(f.w[b][1], s0);
-          const f16x8 w2 = decode8(f.w[b][2], s1), w3 = decode8(f.w[b][3], s1);
+          const f16x8 w0 = decode8(wv[b][0], s0), w1 = decode8(wv[b][1], s0);
+          const f16x8 w2 = decode8(wv[b][2], s1), w3 = decode8(wv[b][3], s1);
+          w_issue(wv[b], c + kDepth, b);   // this ring entry is free again
 #pragma unroll
           for (int tb = 0; tb < NTB; ++tb) {
             acc[b][tb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(w0, bf[tb][0], acc[b][tb], 0, 0, 0);
@@ -233,79 +284,80 @@ __global__ __launch_bounds__(WAVES * kWave) void gemm_stream_kernel(const GemmAr
           }
         }
       };
-      // Two-deep software pipeline over this wave's chunks.
-      Frag<RB, NTB, A4> f0, f1;
-      load(f0, 0);
-      if (!staged) {        // first pass: the scale copy overlaps the first weight loads
-        stage_scales();
-        __syncthreads();
-        staged = true;
+
+      // prologue: scales of window 0, activations of chunk 0, weights of chunks 0..kDepth-1
+      s_issue(0);
+      b_issue(0);
+#pragma unroll
+      for (int d = 0; d < kDepth; ++d)
+#pragma unroll
+        for (int b = 0; b < RBW; ++b) w_issue(wring[d][b], d, b);
+      s_commit(0);
+      b_commit(0);
+      __syncthreads();
+      for (int c0 = 0; c0 < nwin * kWin; c0 += kWin) {   // whole windows; chunks past K are zero
+        s_issue(c0 / kWin + 1);
+#pragma unroll
+        for (int u = 0; u < kWin; ++u) {
+          const int c = c0 + u;
+          b_issue(c + 1);
+          compute(wring[u % kDepth], c);
+          b_commit((c + 1) & 1);
+          if (u == kWin - 1) s_commit(c0 / kWin + 1);
+          __syncthreads();
+        }
       }
-      int it = 0;
-      for (; it + 1 < n_it; it += 2) {
-        load(f1, it + 1);
-        compute(f0, it);
-        load(f0, it + 2);   // past the last round the offsets are out of range: loads return 0
-        compute(f1, it + 1);
-      }
-      if (it < n_it) compute(f0, it);
     };
     if (ntb == 1) kloop(Int<1>{});
-    else kloop(Int<2>{});
+    else kloop(Int<TBM>{});
 
-    // Cross-wave K reduction (fixed order) and epilogue, two row blocks at a time.
-    // D layout of v_mfma_f32_16x16x32: lane l holds rows 4*(l/16)+i, column l%16.
+    // Epilogue: lane l holds rows 4*(l/16)+i of each block, token column l%16.
 #pragma unroll
-    for (int q = 0; q < RB / 2; ++q) {
-      const int b0 = q, b1 = q + RB / 2;
-      float* my0 = red + (wave * 2 + 0) * PER_BLK + lane * 4;
-      float* my1 = red + (wave * 2 + 1) * PER_BLK + lane * 4;
-#pragma unroll
-      for (int tb = 0; tb < TBM; ++tb) {
-        *reinterpret_cast<f32x4*>(my0 + tb * 256) = acc[b0][tb];
-        *reinterpret_cast<f32x4*>(my1 + tb * 256) = acc[b1][tb];
-      }
-      __syncthreads();
-      for (int idx = tid; idx < ntb * 256; idx += NT) {
-        const int tb = idx >> 8, ln = (idx >> 2) & 63, i = idx & 3;
-        const int t = tc + 16 * tb + (ln & 15);
-        if (t >= M) continue;
-        float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-        for (int w = 0; w < WAVES; ++w) {
-          s0 += red[(w * 2 + 0) * PER_BLK + idx];
-          s1 += red[(w * 2 + 1) * PER_BLK + idx];
-        }
+    for (int tb = 0; tb < TBM; ++tb) {
+      const int t = tc + 16 * tb + l16;
+      if (tb < ntb && t < M) {
         const int row = r0 + t;
-        int pexp = 0;
-        if (!A4) {
-          const int a_r = p.gather_index ? p.gather_index[row] / p.gather_div : row;
-          pexp = p.rexp[a_r];
-        }
-        const float v0 = ldexpf(s0 * alpha, pexp);
-        const float v1 = ldexpf(s1 * alpha, pexp);
-        const int coff = 4 * (ln >> 4) + i;
+        const int pexp = A4 ? 0 : p.rexp[p.gather_index ? p.gather_index[row] / p.gather_div : row];
         if (SWIGLU) {
-          const float h = v0 / (1.0f + expf(-v0)) * v1;
-          const size_t o = (size_t)row * F + nb * 8 * RB + 16 * q + coff;
-          if (p.out_bf16) static_cast<uint16_t*>(p.out)[o] = (uint16_t)f32_to_bf16(h);
-          else static_cast<float*>(p.out)[o] = h;
-          amax_bits = max(amax_bits, abs_bits(h));
-        } else {
-          const size_t o0 = (size_t)row * Nw + nb * 16 * RB + 16 * b0 + coff;
-          const size_t o1 = (size_t)row * Nw + nb * 16 * RB + 16 * b1 + coff;
-          if (p.out_bf16) {
-            static_cast<uint16_t*>(p.out)[o0] = (uint16_t)f32_to_bf16(v0);
-            static_cast<uint16_t*>(p.out)[o1] = (uint16_t)f32_to_bf16(v1);
-          } else {
-            static_cast<float*>(p.out)[o0] = v0;
-            static_cast<float*>(p.out)[o1] = v1;
+#pragma unroll
+          for (int b = 0; b < RBW / 2; ++b) {
+            float h[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float gv = ldexpf(acc[b][tb][i] * alpha, pexp);
+              const float uv = ldexpf(acc[b + RBW / 2][tb][i] * alpha, pexp);
+              h[i] = gv / (1.0f + expf(-gv)) * uv;
+              amax_bits = max(amax_bits, abs_bits(h[i]));
+            }
+            const size_t o = (size_t)row * F + blkrow(b) + 4 * g;
+            if (p.out_bf16)
+              *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + o) =
+                  make_uint2(f32_to_bf16(h[0]) | (f32_to_bf16(h[1]) << 16),
+                             f32_to_bf16(h[2]) | (f32_to_bf16(h[3]) << 16));
+            else
+              *reinterpret_cast<float4*>(static_cast<float*>(p.out) + o) = make_float4(h[0], h[1], h[2], h[3]);
           }
-          amax_bits = max(amax_bits, max(abs_bits(v0), abs_bits(v1)));
+        } else {
+#pragma unroll
+          for (int b = 0; b < RBW; ++b) {
+            float v[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              v[i] = ldexpf(acc[b][tb][i] * alpha, pexp);
+              amax_bits = max(amax_bits, abs_bits(v[i]));
+            }
+            const size_t o = (size_t)row * Nw + blkrow(b) + 4 * g;
+            if (p.out_bf16)
+              *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + o) =
+                  make_uint2(f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16),
+                             f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16));
+            else
+              *reinterpret_cast<float4*>(static_cast<float*>(p.out) + o) = make_float4(v[0], v[1], v[2], v[3]);
+          }
         }
       }
-      __syncthreads();
     }
+    __syncthreads();   // the LDS rings are reused by the next pass
   }
 
   if (p.out_amax) {
@@ -314,32 +366,35 @@ __global__ __launch_bounds__(WAVES * kWave) void gemm_stream_kernel(const GemmAr
   }
 }
 
-template <int RB, int WAVES, bool SWIGLU, bool A4>
+template <int RBW, int WAVES, bool SWIGLU, bool A4>
 hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
   constexpr int TBM = 2;
-  const int tiles_per_expert = a.Nw / (16 * RB);
+  const int rows_per_tile = 16 * RBW * WAVES;
+  const int tiles_per_expert = a.Nw / rows_per_tile;
   const int max_active = a.E < a.rows ? a.E : a.rows;
   const int total = max_active * tiles_per_expert;
   const int grid = (total + 7) / 8 * 8;
-  const size_t shmem = (size_t)16 * RB * scale_pitch(a.K / 16) + (size_t)WAVES * 2 * TBM * 256 * sizeof(float);
-  gemm_stream_kernel<RB, WAVES, TBM, SWIGLU, A4>
-      <<<grid, WAVES * kWave, shmem, stream>>>(a, tiles_per_expert, total);
+  const size_t shmem = (size_t)Ring<TBM, A4>::kBytes + (size_t)WAVES * 2 * RBW * 16 * kSPitch;
+  gemm_stream_kernel<RBW, WAVES, TBM, SWIGLU, A4><<<grid, WAVES * kWave, shmem, stream>>>(a, tiles_per_expert, total);
   return hipGetLastError();
 }
 
-// Tile shape (row blocks per tile, waves per workgroup). NVFP4MOE_STREAM_TILE=<rb>x<waves>
-// overrides the default for tuning; a shape that does not divide Nw falls back to RB=2.
+// Tile shape: RBW row blocks of 16 per wave, WAVES waves. NVFP4MOE_STREAM_TILE=<rbw>x<waves>
+// overrides the default for tuning; a shape must divide Nw (16 * RBW * WAVES rows), and
+// the 2x1 shape (32 rows) divides every valid Nw.
 template <bool SWIGLU, bool A4>
 hipError_t launch_sw(const GemmArgs& a, hipStream_t stream) {
-  const int blocks16 = a.Nw / 16;  // even, since Nw % 32 == 0
-  int rb = 4, waves = 4;
-  if (const char* s = std::getenv("NVFP4MOE_STREAM_TILE")) std::sscanf(s, "%dx%d", &rb, &waves);
-  if (blocks16 % rb != 0) rb = blocks16 % 4 == 0 ? 4 : 2;
-  if (rb == 8 && waves == 4) return launch_cfg<8, 4, SWIGLU, A4>(a, stream);
-  if (rb == 8 && waves == 2) return launch_cfg<8, 2, SWIGLU, A4>(a, stream);
-  if (rb == 4 && waves == 8) return launch_cfg<4, 8, SWIGLU, A4>(a, stream);
-  if (rb == 4 && waves == 2) return launch_cfg<4, 2, SWIGLU, A4>(a, stream);
-  if (rb == 4) return launch_cfg<4, 4, SWIGLU, A4>(a, stream);
+  int rbw = 2, waves = 4;
+  if (const char* s = std::getenv("NVFP4MOE_STREAM_TILE")) std::sscanf(s, "%dx%d", &rbw, &waves);
+  if (a.Nw % (16 * rbw * waves) != 0) {
+    rbw = 2;
+    waves = a.Nw % 128 == 0 ? 4 : a.Nw % 64 == 0 ? 2 : 1;
+  }
+  if (waves == 1) return launch_cfg<2, 1, SWIGLU, A4>(a, stream);
+  if (rbw == 4 && waves == 4) return launch_cfg<4, 4, SWIGLU, A4>(a, stream);
+  if (rbw == 2 && waves == 8) return launch_cfg<2, 8, SWIGLU, A4>(a, stream);
+  if (rbw == 4 && waves == 2) return launch_cfg<4, 2, SWIGLU, A4>(a, stream);
+  if (rbw == 2 && waves == 2) return launch_cfg<2, 2, SWIGLU, A4>(a, stream);
   return launch_cfg<2, 4, SWIGLU, A4>(a, stream);
 }
 
