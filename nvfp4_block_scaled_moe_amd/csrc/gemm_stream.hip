@@ -181,9 +181,13 @@ __global__ __launch_bounds__(WAVES* kWave) void gemm_stream_kernel(const GemmArg
     auto kloop = [&](auto ntb_tag) {
       constexpr int NTB = decltype(ntb_tag)::value;
       constexpr int RND = (16 * NTB + TPR - 1) / TPR;
-      u32x4 bst[RND];
-      uint32_t bsc[RND][2];
-      auto b_issue = [&](int c) {
+      // kDepth staging register sets: activations of chunk c+kDepth are requested just
+      // before its weights. Vector-memory counters retire in issue order, so a staging set
+      // that is committed one step before use would make the wave wait for every weight
+      // chunk requested before it; at equal depth the commit never waits on weights.
+      u32x4 bst[kDepth][RND];
+      uint32_t bsc[kDepth][RND][2];
+      auto b_issue = [&](int set, int c) {
         // f16 rows are zero-padded to whole chunks; FP4 rows are not, so W4A4 pieces and
         // scale pairs past K read zero (a neighbouring row's NaN scale must not leak in).
         const bool cin = c < nch;
@@ -192,7 +196,7 @@ __global__ __launch_bounds__(WAVES* kWave) void gemm_stream_kernel(const GemmArg
         for (int rr = 0; rr < RND; ++rr) {
           const bool in = A4 ? cin && (kc + 32 * (tid % TPT)) < K : cin;
           const uint32_t step = A4 ? (uint32_t)kc / 2 : (uint32_t)kc * 2;
-          bst[rr] = ld128(ar, in ? bsrc[rr] + step : kOOB, 0);
+          bst[set][rr] = ld128(ar, in ? bsrc[rr] + step : kOOB, 0);
         }
         if (A4) {
 #pragma unroll
@@ -201,20 +205,21 @@ __global__ __launch_bounds__(WAVES* kWave) void gemm_stream_kernel(const GemmArg
             uint32_t v[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q) v[q] = ld16(asr, (cin && kc + 32 * q < K) ? so : kOOB, 2 * q);
-            bsc[rr][0] = v[0] | (v[1] << 16);
-            bsc[rr][1] = v[2] | (v[3] << 16);
+            bsc[set][rr][0] = v[0] | (v[1] << 16);
+            bsc[set][rr][1] = v[2] | (v[3] << 16);
           }
         }
       };
-      auto b_commit = [&](int slot) {
+      auto b_commit = [&](int set, int slot) {
         unsigned char* base = ring + slot * R::kSlot;
 #pragma unroll
         for (int rr = 0; rr < RND; ++rr)
-          if (bdst[rr] != kNoDst) *reinterpret_cast<u32x4*>(base + bdst[rr]) = bst[rr];
+          if (bdst[rr] != kNoDst) *reinterpret_cast<u32x4*>(base + bdst[rr]) = bst[set][rr];
         if (A4) {
 #pragma unroll
           for (int rr = 0; rr < RND; ++rr)
-            if (bsdst[rr] != kNoDst) *reinterpret_cast<uint2*>(base + bsdst[rr]) = make_uint2(bsc[rr][0], bsc[rr][1]);
+            if (bsdst[rr] != kNoDst)
+              *reinterpret_cast<uint2*>(base + bsdst[rr]) = make_uint2(bsc[set][rr][0], bsc[set][rr][1]);
         }
       };
       u32x4 sst[RBW];
@@ -267,42 +272,50 @@ __global__ __launch_bounds__(WAVES* kWave) void gemm_stream_kernel(const GemmArg
               bf[tb][j] = *reinterpret_cast<const f16x8*>(base + tk * R::kTokBytes + 16 * ((4 * j + g) ^ (tk & 15)));
           }
         }
+        // Decode every block of the chunk (each ring entry is re-filled right after its
+        // decode), then issue the MFMAs k-step-major so that consecutive MFMAs update
+        // different accumulators and do not wait on each other.
+        f16x8 wf[RBW][4];
 #pragma unroll
         for (int b = 0; b < RBW; ++b) {
           const uint32_t sv = sin ? *reinterpret_cast<const uint16_t*>(sbase + (16 * b + l16) * kSPitch + soff) : 0u;
           f16x2 s0, s1;
           decode_scale_pair(sv, s0, s1);
-          const f16x8 w0 = decode8(wv[b][0], s0), w1 = decode8(wv[b][1], s0);
-          const f16x8 w2 = decode8(wv[b][2], s1), w3 = decode8(wv[b][3], s1);
+          wf[b][0] = decode8(wv[b][0], s0);
+          wf[b][1] = decode8(wv[b][1], s0);
+          wf[b][2] = decode8(wv[b][2], s1);
+          wf[b][3] = decode8(wv[b][3], s1);
           w_issue(wv[b], c + kDepth, b);   // this ring entry is free again
-#pragma unroll
-          for (int tb = 0; tb < NTB; ++tb) {
-            acc[b][tb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(w0, bf[tb][0], acc[b][tb], 0, 0, 0);
-            acc[b][tb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(w1, bf[tb][1], acc[b][tb], 0, 0, 0);
-            acc[b][tb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(w2, bf[tb][2], acc[b][tb], 0, 0, 0);
-            acc[b][tb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(w3, bf[tb][3], acc[b][tb], 0, 0, 0);
-          }
         }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int b = 0; b < RBW; ++b)
+#pragma unroll
+            for (int tb = 0; tb < NTB; ++tb)
+              acc[b][tb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf[b][j], bf[tb][j], acc[b][tb], 0, 0, 0);
       };
 
-      // prologue: scales of window 0, activations of chunk 0, weights of chunks 0..kDepth-1
+      // prologue: scales of window 0, then activations and weights of chunks 0..kDepth-1
       s_issue(0);
-      b_issue(0);
 #pragma unroll
-      for (int d = 0; d < kDepth; ++d)
+      for (int d = 0; d < kDepth; ++d) {
+        b_issue(d, d);
 #pragma unroll
         for (int b = 0; b < RBW; ++b) w_issue(wring[d][b], d, b);
+      }
       s_commit(0);
-      b_commit(0);
+      b_commit(0, 0);
       __syncthreads();
+      // Chunk c: LDS slot c&1, staging set and weight ring entry c % kDepth.
       for (int c0 = 0; c0 < nwin * kWin; c0 += kWin) {   // whole windows; chunks past K are zero
         s_issue(c0 / kWin + 1);
 #pragma unroll
         for (int u = 0; u < kWin; ++u) {
           const int c = c0 + u;
-          b_issue(c + 1);
-          compute(wring[u % kDepth], c);
-          b_commit((c + 1) & 1);
+          b_issue(u % kDepth, c + kDepth);         // set u%kDepth was committed last step
+          compute(wring[u % kDepth], c);           // requests weights of chunk c+kDepth
+          b_commit((u + 1) % kDepth, (c + 1) & 1);
           if (u == kWin - 1) s_commit(c0 / kWin + 1);
           __syncthreads();
         }
