@@ -16,7 +16,7 @@
 // logical k 32g+8j..+7, so the four lane groups of one token read 64 contiguous bytes per
 // load instruction (one cache line instead of four).
 //
-// One workgroup per row: pass 1 finds the row's finite amax, pass 2 converts (the row is
+// One workgroup per row (bf16 input): pass 1 finds the row's finite amax, pass 2 converts (the row is
 // re-read from L2). Traffic: 2 bytes read + 2 bytes written per element.
 #include "common.h"
 #include "kernels.h"
@@ -77,7 +77,51 @@ __global__ __launch_bounds__(kPrepThreads) void act_prep_kernel(const uint16_t* 
   }
 }
 
+// NVFP4 activations -> f16 for the large-M path. Each thread decodes one 32-element group
+// (16 bytes of codes and its two E4M3 scales) exactly, as E2M1 value times block scale (<= 6
+// significant bits, magnitudes 2^-10 .. 2688, all exact in f16), into the layout above; the
+// per-tensor scale is applied in the GEMM epilogue, so rexp = 0. Groups past K are zero.
+__global__ __launch_bounds__(kPrepThreads) void act_prep_fp4_kernel(const uint8_t* __restrict__ packed,
+                                                                    const uint8_t* __restrict__ scales,
+                                                                    int64_t rows, int K,
+                                                                    _Float16* __restrict__ a16,
+                                                                    int* __restrict__ rexp) {
+  const int K128 = (K + 127) & ~127;
+  const int gpr = K128 / 32;   // groups per padded row
+  const int64_t i = (int64_t)blockIdx.x * kPrepThreads + threadIdx.x;
+  if (i >= rows * gpr) return;
+  const int64_t r = i / gpr;
+  const int q = (int)(i - r * gpr);   // group: logical k 32q .. 32q+31
+  const int c = q >> 2, g = q & 3;
+  _Float16* orow = a16 + r * (int64_t)K128;
+  f16x8 o[4];
+  if (32 * q < K) {
+    const uint4 w = *reinterpret_cast<const uint4*>(packed + r * (int64_t)(K / 2) + 16 * q);
+    const uint32_t sv = *reinterpret_cast<const uint16_t*>(scales + r * (int64_t)(K / 16) + 2 * q);
+    f16x2 s0, s1;
+    decode_scale_pair(sv, s0, s1);
+    o[0] = decode8(w.x, s0);
+    o[1] = decode8(w.y, s0);
+    o[2] = decode8(w.z, s1);
+    o[3] = decode8(w.w, s1);
+  } else {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) o[j] = (f16x8){0, 0, 0, 0, 0, 0, 0, 0};
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) *reinterpret_cast<f16x8*>(orow + 8 * (16 * c + 4 * j + g)) = o[j];
+  if (q == 0) rexp[r] = 0;
+}
+
 }  // namespace
+
+hipError_t launch_act_prep_fp4(const uint8_t* packed, const uint8_t* scales, int64_t rows, int K,
+                               _Float16* a16, int* rexp, hipStream_t stream) {
+  const int64_t n = rows * (((K + 127) & ~127) / 32);
+  act_prep_fp4_kernel<<<(unsigned)((n + kPrepThreads - 1) / kPrepThreads), kPrepThreads, 0, stream>>>(
+      packed, scales, rows, K, a16, rexp);
+  return hipGetLastError();
+}
 
 hipError_t launch_act_prep(const uint16_t* a, int64_t rows, int K, _Float16* a16, int* rexp,
                            hipStream_t stream) {

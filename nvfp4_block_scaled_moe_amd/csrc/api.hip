@@ -49,21 +49,6 @@ __global__ void zero_f32_kernel(float* p, int n) {
   if (i < n) p[i] = 0.0f;
 }
 
-// Workspace layout of moe_grouped_gemm_nvfp4 (W4A16): f16 activations, row exponents.
-struct GemmWs {
-  size_t a16_bytes, rexp_bytes, total;
-};
-GemmWs gemm_ws_layout(nvfp4moe_mode mode, int64_t a_rows, int32_t K) {
-  GemmWs w{0, 0, 0};
-  if (mode == NVFP4MOE_W4A16) {
-    const size_t K128 = ((size_t)K + 127) / 128 * 128;  // rows padded to whole 128-k chunks
-    w.a16_bytes = round_up((size_t)a_rows * K128 * 2);
-    w.rexp_bytes = round_up((size_t)a_rows * 4);
-  }
-  w.total = w.a16_bytes + w.rexp_bytes;
-  return w;
-}
-
 // Kernel path override for tests/measurement: NVFP4MOE_FORCE_PATH=stream|mfma.
 int forced_path() {
   const char* s = std::getenv("NVFP4MOE_FORCE_PATH");
@@ -71,6 +56,46 @@ int forced_path() {
   if (!std::strcmp(s, "stream")) return NVFP4MOE_PATH_STREAM;
   if (!std::strcmp(s, "mfma")) return NVFP4MOE_PATH_MFMA;
   return NVFP4MOE_PATH_NONE;
+}
+
+// Mean rows per expert from which the m-tiled MFMA path is used: below it every weight
+// byte feeds too few rows for the MFMA tile to pay, and the weight-streaming path wins.
+constexpr int64_t kLargeMeanRows = 64;
+
+// Path of one grouped GEMM, decided on the host from the sizes alone (the per-expert row
+// counts live on the device): NVFP4MOE_PATH_STREAM or _MFMA, or NONE if a forced path
+// cannot run this shape.
+int gemm_path(int32_t rows, int32_t E, int32_t Nw) {
+  const int forced = forced_path();
+  const bool large_ok = large_supports(Nw);
+  if (forced == NVFP4MOE_PATH_MFMA) return large_ok ? NVFP4MOE_PATH_MFMA : NVFP4MOE_PATH_NONE;
+  if (forced == NVFP4MOE_PATH_STREAM) return NVFP4MOE_PATH_STREAM;
+  const int64_t groups = E < rows ? E : rows;
+  return large_ok && (int64_t)rows >= kLargeMeanRows * groups ? NVFP4MOE_PATH_MFMA : NVFP4MOE_PATH_STREAM;
+}
+
+// Workspace layout of moe_grouped_gemm_nvfp4: f16 activations in MFMA operand order and
+// their row exponents (W4A16 on both paths, W4A4 on the MFMA path), and the m-tile
+// schedule of the MFMA path.
+struct GemmWs {
+  size_t a16_bytes, rexp_bytes, sched_bytes, total;
+  int max_mtiles;
+};
+GemmWs gemm_ws_layout(int path, nvfp4moe_mode mode, int64_t a_rows, int32_t rows, int32_t E, int32_t K) {
+  GemmWs w{0, 0, 0, 0, 0};
+  if (mode == NVFP4MOE_W4A16 || path == NVFP4MOE_PATH_MFMA) {
+    const size_t K128 = ((size_t)K + 127) / 128 * 128;  // rows padded to whole 128-k chunks
+    w.a16_bytes = round_up((size_t)a_rows * K128 * 2);
+    w.rexp_bytes = round_up((size_t)a_rows * 4);
+  }
+  if (path == NVFP4MOE_PATH_MFMA) {
+    const int bm = large_rows_per_mtile();
+    // sum over experts of ceil(M_e / bm) <= ceil(rows / bm) + (number of non-empty experts)
+    w.max_mtiles = (rows + bm - 1) / bm + (E < rows ? E : rows);
+    w.sched_bytes = 2 * round_up((size_t)w.max_mtiles * 4) + kAlign;
+  }
+  w.total = w.a16_bytes + w.rexp_bytes + w.sched_bytes;
+  return w;
 }
 
 }  // namespace
@@ -153,11 +178,8 @@ nvfp4moe_status moe_route_permute(const float* logits, int32_t T, int32_t E, int
 // ------------------------------------------------------------------ grouped GEMM
 size_t moe_grouped_gemm_workspace_size(nvfp4moe_mode mode, int64_t a_rows, int32_t rows,
                                        int32_t E, int32_t Nw, int32_t K) {
-  (void)rows;
-  (void)E;
-  (void)Nw;
-  if (a_rows < 1 || K < 1) return 0;
-  return gemm_ws_layout(mode, a_rows, K).total;
+  if (a_rows < 1 || rows < 1 || E < 1 || K < 1) return 0;
+  return gemm_ws_layout(gemm_path(rows, E, Nw), mode, a_rows, rows, E, K).total;
 }
 
 nvfp4moe_status moe_grouped_gemm_nvfp4(nvfp4moe_mode mode, nvfp4moe_epilogue epi,
@@ -203,7 +225,10 @@ nvfp4moe_status moe_grouped_gemm_nvfp4(nvfp4moe_mode mode, nvfp4moe_epilogue epi
       (a_scales && !aligned(a_scales, 2)) || !aligned(out, out_dtype == NVFP4MOE_F32 ? 4 : 2))
     return fail(NVFP4MOE_ERR_INVALID_ARG,
                 "%s: a and w_packed must be 16-byte aligned, scale arrays 2-byte aligned", fn);
-  const GemmWs lay = gemm_ws_layout(mode, a_rows, K);
+  const int path = gemm_path(rows, E, Nw);
+  if (path == NVFP4MOE_PATH_NONE)
+    return fail(NVFP4MOE_ERR_UNSUPPORTED, "%s: the forced MFMA path needs Nw %% 256 == 0 (Nw=%d)", fn, Nw);
+  const GemmWs lay = gemm_ws_layout(path, mode, a_rows, rows, E, K);
   if (lay.total && (!ws || ws_bytes < lay.total))
     return fail(NVFP4MOE_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn,
                 lay.total, ws_bytes);
@@ -234,23 +259,32 @@ nvfp4moe_status moe_grouped_gemm_nvfp4(nvfp4moe_mode mode, nvfp4moe_epilogue epi
   hipError_t err = hipSuccess;
   if (out_amax) err = launch_zero_f32(out_amax, 1, s);
   if (err != hipSuccess) return hip_status(err, fn);
-  if (mode == NVFP4MOE_W4A16) {
-    char* base = static_cast<char*>(ws);
+  char* base = static_cast<char*>(ws);
+  if (lay.a16_bytes) {
     g.a16 = reinterpret_cast<_Float16*>(base);
     g.rexp = reinterpret_cast<int*>(base + lay.a16_bytes);
+  }
+  if (mode == NVFP4MOE_W4A16) {
     err = launch_act_prep(static_cast<const uint16_t*>(a), a_rows, K, const_cast<_Float16*>(g.a16),
                           const_cast<int*>(g.rexp), s);
-    if (err != hipSuccess) return hip_status(err, fn);
   } else {
     g.a_packed = static_cast<const uint8_t*>(a);
     g.a_scales = a_scales;
     g.a_g = a_g;
+    if (path == NVFP4MOE_PATH_MFMA)
+      err = launch_act_prep_fp4(g.a_packed, a_scales, a_rows, K, const_cast<_Float16*>(g.a16),
+                                const_cast<int*>(g.rexp), s);
   }
-  int path = forced_path();
-  if (path == NVFP4MOE_PATH_MFMA)
-    return fail(NVFP4MOE_ERR_UNSUPPORTED, "%s: the MFMA path is not built in this version", fn);
-  path = NVFP4MOE_PATH_STREAM;
+  if (err != hipSuccess) return hip_status(err, fn);
   g_last_dispatch = path;
+  if (path == NVFP4MOE_PATH_MFMA) {
+    char* sched = base + lay.a16_bytes + lay.rexp_bytes;
+    const size_t arr = round_up((size_t)lay.max_mtiles * 4);
+    g.sched_e = reinterpret_cast<const int*>(sched);
+    g.sched_r = reinterpret_cast<const int*>(sched + arr);
+    g.sched_n = reinterpret_cast<const int*>(sched + 2 * arr);
+    return hip_status(launch_gemm_large(g, lay.max_mtiles, s), fn);
+  }
   return hip_status(launch_gemm_stream(g, s), fn);
 }
 

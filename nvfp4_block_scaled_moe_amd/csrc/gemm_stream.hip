@@ -79,10 +79,19 @@ struct Ring {
   static constexpr int kBytes = 2 * kSlot;
 };
 
-template <int RBW, int WAVES, int TBM, bool SWIGLU, bool A4>
+// LARGE = false: small-M path; a workgroup owns (expert, row tile) and loops over the
+//   expert's rows 16*TBM at a time.
+// LARGE = true: large-M path; a workgroup owns (m-tile, row tile), where the m-tiles (16*TBM
+//   consecutive rows of one expert) come from the device-side schedule built by
+//   mtile_schedule_kernel, so every workgroup does one pass and large experts spread over
+//   many workgroups. Activations are always f16 there (W4A4 activations are decoded exactly
+//   to f16 beforehand).
+template <int RBW, int WAVES, int TBM, int WDEPTH, int BDEPTH, bool LARGE, bool SWIGLU, bool A4>
 __global__ __launch_bounds__(WAVES* kWave) void gemm_stream_kernel(const GemmArgs p, int tiles_per_expert,
                                                                    int total_tiles) {
   static_assert(RBW % 2 == 0, "row blocks per wave come in pairs");
+  static_assert(!(LARGE && A4), "the large-M path reads f16 activations");
+  static_assert(kWin % WDEPTH == 0 && kWin % BDEPTH == 0, "ring depths divide the scale window");
   using R = Ring<TBM, A4>;
   constexpr int NT = WAVES * kWave;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -93,12 +102,20 @@ __global__ __launch_bounds__(WAVES* kWave) void gemm_stream_kernel(const GemmArg
   const int per_xcd = gridDim.x >> 3;
   const int tile = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
   if (tile >= total_tiles) return;
-  const int aidx = tile / tiles_per_expert;
-  const int nb = tile - aidx * tiles_per_expert;
-  if (aidx >= p.n_active[0]) return;
-  const int e = p.active[aidx];
+  const int aidx = tile / tiles_per_expert;        // active-expert slot, or m-tile (LARGE)
+  const int nb = tile - aidx * tiles_per_expert;   // row tile
+  int e, tc_begin = 0;
+  if (LARGE) {
+    if (aidx >= p.sched_n[0]) return;
+    e = p.sched_e[aidx];
+    tc_begin = p.sched_r[aidx];
+  } else {
+    if (aidx >= p.n_active[0]) return;
+    e = p.active[aidx];
+  }
   const int r0 = p.expert_offsets[e];
   const int M = p.expert_offsets[e + 1] - r0;
+  const int tc_end = LARGE ? min(M, tc_begin + 16 * TBM) : M;
   const int K = p.K, Nw = p.Nw, Kh = K >> 1, Ks = K >> 4;
   const int K128 = (K + 127) & ~127;
   const int F = Nw >> 1;
@@ -129,7 +146,7 @@ __global__ __launch_bounds__(WAVES* kWave) void gemm_stream_kernel(const GemmArg
     wsoff[b] = __builtin_amdgcn_readfirstlane((uint32_t)(blkrow(b) - blkrow(0)) * Kh);
     ssoff[b] = __builtin_amdgcn_readfirstlane((uint32_t)(blkrow(b) - blkrow(0)) * Ks);
   }
-  const float alpha = A4 ? p.w_g[e] * p.a_g[0] : p.w_g[e];
+  const float alpha = (A4 || p.w4a4) ? p.w_g[e] * p.a_g[0] : p.w_g[e];
 
   __amdgpu_buffer_rsrc_t ar, asr;
   if (A4) {
@@ -146,7 +163,7 @@ __global__ __launch_bounds__(WAVES* kWave) void gemm_stream_kernel(const GemmArg
   constexpr int ROUNDS = (16 * TBM + TPR - 1) / TPR;
 
   uint32_t amax_bits = 0;
-  for (int tc = 0; tc < M; tc += 16 * TBM) {
+  for (int tc = tc_begin; tc < tc_end; tc += 16 * TBM) {
     const int ntb = __builtin_amdgcn_readfirstlane(min(TBM, (M - tc + 15) >> 4));
     uint32_t bsrc[ROUNDS], bdst[ROUNDS], bssrc[ROUNDS], bsdst[ROUNDS];
 #pragma unroll
@@ -181,12 +198,14 @@ __global__ __launch_bounds__(WAVES* kWave) void gemm_stream_kernel(const GemmArg
     auto kloop = [&](auto ntb_tag) {
       constexpr int NTB = decltype(ntb_tag)::value;
       constexpr int RND = (16 * NTB + TPR - 1) / TPR;
-      // kDepth staging register sets: activations of chunk c+kDepth are requested just
-      // before its weights. Vector-memory counters retire in issue order, so a staging set
-      // that is committed one step before use would make the wave wait for every weight
-      // chunk requested before it; at equal depth the commit never waits on weights.
-      u32x4 bst[kDepth][RND];
-      uint32_t bsc[kDepth][RND][2];
+      // BDEPTH staging register sets: activations of chunk c+BDEPTH are requested just
+      // before the weights of chunk c+WDEPTH. Vector-memory counters retire in issue order,
+      // so a staging set that is committed one step after its request would make the wave
+      // wait for every weight chunk requested before it; with BDEPTH == WDEPTH the commit
+      // never waits on weights. (The large-M path has more compute per chunk than a weight
+      // chunk takes to arrive and uses a shallower activation ring.)
+      u32x4 bst[BDEPTH][RND];
+      uint32_t bsc[BDEPTH][RND][2];
       auto b_issue = [&](int set, int c) {
         // f16 rows are zero-padded to whole chunks; FP4 rows are not, so W4A4 pieces and
         // scale pairs past K read zero (a neighbouring row's NaN scale must not leak in).
@@ -243,7 +262,7 @@ __global__ __launch_bounds__(WAVES* kWave) void gemm_stream_kernel(const GemmArg
         for (int b = 0; b < RBW; ++b)
           *reinterpret_cast<u32x4*>(base + (16 * b + l16) * kSPitch + 16 * g) = sst[b];
       };
-      u32x4 wring[kDepth][RBW];
+      u32x4 wring[WDEPTH][RBW];
       auto w_issue = [&](u32x4& dst, int c, int b) {
         const bool kin = c < nch && (c * kChunk + 32 * g) < K;
         dst = ld128(wr, kin ? wlane + (uint32_t)(c * kChunk) / 2 : kOOB, wsoff[b]);
@@ -253,28 +272,9 @@ __global__ __launch_bounds__(WAVES* kWave) void gemm_stream_kernel(const GemmArg
         const unsigned char* sbase = sws + ((c / kWin) & 1) * (RBW * 16 * kSPitch);
         const int soff = (c % kWin) * 8 + 2 * g;
         const bool sin = (c * kChunk + 32 * g) < K;   // past K: weights read zero, so must scales
-        f16x8 bf[NTB][4];
-#pragma unroll
-        for (int tb = 0; tb < NTB; ++tb) {
-          const int tk = 16 * tb + l16;
-          if (A4) {
-            const u32x4 q = *reinterpret_cast<const u32x4*>(base + tk * R::kTokBytes + 16 * (g ^ (tk & 3)));
-            const uint32_t sc2 = *reinterpret_cast<const uint16_t*>(base + R::kCodes + tk * 8 + 2 * g);
-            f16x2 s0, s1;
-            decode_scale_pair(sc2, s0, s1);
-            bf[tb][0] = decode8(q[0], s0);
-            bf[tb][1] = decode8(q[1], s0);
-            bf[tb][2] = decode8(q[2], s1);
-            bf[tb][3] = decode8(q[3], s1);
-          } else {
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-              bf[tb][j] = *reinterpret_cast<const f16x8*>(base + tk * R::kTokBytes + 16 * ((4 * j + g) ^ (tk & 15)));
-          }
-        }
         // Decode every block of the chunk (each ring entry is re-filled right after its
         // decode), then issue the MFMAs k-step-major so that consecutive MFMAs update
-        // different accumulators and do not wait on each other.
+        // different accumulators and the activation fragments are read once per k-step.
         f16x8 wf[RBW][4];
 #pragma unroll
         for (int b = 0; b < RBW; ++b) {
@@ -285,44 +285,64 @@ __global__ __launch_bounds__(WAVES* kWave) void gemm_stream_kernel(const GemmArg
           wf[b][1] = decode8(wv[b][1], s0);
           wf[b][2] = decode8(wv[b][2], s1);
           wf[b][3] = decode8(wv[b][3], s1);
-          w_issue(wv[b], c + kDepth, b);   // this ring entry is free again
+          w_issue(wv[b], c + WDEPTH, b);   // this ring entry is free again
+        }
+        u32x4 aq[A4 ? NTB : 1];
+        f16x2 as0[A4 ? NTB : 1], as1[A4 ? NTB : 1];
+        if (A4) {
+#pragma unroll
+          for (int tb = 0; tb < NTB; ++tb) {
+            const int tk = 16 * tb + l16;
+            aq[tb] = *reinterpret_cast<const u32x4*>(base + tk * R::kTokBytes + 16 * (g ^ (tk & 3)));
+            decode_scale_pair(*reinterpret_cast<const uint16_t*>(base + R::kCodes + tk * 8 + 2 * g), as0[tb], as1[tb]);
+          }
         }
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 4; ++j) {
+          f16x8 bj[NTB];
+#pragma unroll
+          for (int tb = 0; tb < NTB; ++tb) {
+            const int tk = 16 * tb + l16;
+            if (A4) bj[tb] = decode8(aq[tb][j], j < 2 ? as0[tb] : as1[tb]);
+            else bj[tb] = *reinterpret_cast<const f16x8*>(base + tk * R::kTokBytes + 16 * ((4 * j + g) ^ (tk & 15)));
+          }
 #pragma unroll
           for (int b = 0; b < RBW; ++b)
 #pragma unroll
             for (int tb = 0; tb < NTB; ++tb)
-              acc[b][tb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf[b][j], bf[tb][j], acc[b][tb], 0, 0, 0);
+              acc[b][tb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf[b][j], bj[tb], acc[b][tb], 0, 0, 0);
+        }
       };
 
-      // prologue: scales of window 0, then activations and weights of chunks 0..kDepth-1
+      // prologue: scales of window 0, then activations and weights of the first chunks
       s_issue(0);
 #pragma unroll
-      for (int d = 0; d < kDepth; ++d) {
-        b_issue(d, d);
+      for (int d = 0; d < (WDEPTH > BDEPTH ? WDEPTH : BDEPTH); ++d) {
+        if (d < BDEPTH) b_issue(d, d);
+        if (d < WDEPTH) {
 #pragma unroll
-        for (int b = 0; b < RBW; ++b) w_issue(wring[d][b], d, b);
+          for (int b = 0; b < RBW; ++b) w_issue(wring[d][b], d, b);
+        }
       }
       s_commit(0);
       b_commit(0, 0);
       __syncthreads();
-      // Chunk c: LDS slot c&1, staging set and weight ring entry c % kDepth.
+      // Chunk c: LDS slot c&1, staging set c % BDEPTH and weight ring entry c % WDEPTH.
       for (int c0 = 0; c0 < nwin * kWin; c0 += kWin) {   // whole windows; chunks past K are zero
         s_issue(c0 / kWin + 1);
 #pragma unroll
         for (int u = 0; u < kWin; ++u) {
           const int c = c0 + u;
-          b_issue(u % kDepth, c + kDepth);         // set u%kDepth was committed last step
-          compute(wring[u % kDepth], c);           // requests weights of chunk c+kDepth
-          b_commit((u + 1) % kDepth, (c + 1) & 1);
+          b_issue(u % BDEPTH, c + BDEPTH);         // set u%BDEPTH was committed last step
+          compute(wring[u % WDEPTH], c);           // requests weights of chunk c+WDEPTH
+          b_commit((u + 1) % BDEPTH, (c + 1) & 1);
           if (u == kWin - 1) s_commit(c0 / kWin + 1);
           __syncthreads();
         }
       }
     };
-    if (ntb == 1) kloop(Int<1>{});
-    else kloop(Int<TBM>{});
+    if (LARGE || ntb == TBM) kloop(Int<TBM>{});
+    else kloop(Int<1>{});
 
     // Epilogue: lane l holds rows 4*(l/16)+i of each block, token column l%16.
 #pragma unroll
@@ -388,7 +408,8 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
   const int total = max_active * tiles_per_expert;
   const int grid = (total + 7) / 8 * 8;
   const size_t shmem = (size_t)Ring<TBM, A4>::kBytes + (size_t)WAVES * 2 * RBW * 16 * kSPitch;
-  gemm_stream_kernel<RBW, WAVES, TBM, SWIGLU, A4><<<grid, WAVES * kWave, shmem, stream>>>(a, tiles_per_expert, total);
+  gemm_stream_kernel<RBW, WAVES, TBM, kDepth, kDepth, false, SWIGLU, A4>
+      <<<grid, WAVES * kWave, shmem, stream>>>(a, tiles_per_expert, total);
   return hipGetLastError();
 }
 
@@ -411,7 +432,85 @@ hipError_t launch_sw(const GemmArgs& a, hipStream_t stream) {
   return launch_cfg<2, 4, SWIGLU, A4>(a, stream);
 }
 
+// ---- large-M path
+// Tile: RBW row blocks per wave x WAVES waves (16*RBW*WAVES weight rows) by 16*TBM rows of
+// one expert. NVFP4MOE_LARGE_TILE=<rbw>x<waves> selects a built shape for tuning.
+constexpr int kLTBM = 8;
+
+// m-tiles of bm rows over the active experts (one workgroup, n_active <= 1024):
+// sched_e[i] = expert, sched_r[i] = first row within the expert, sched_n[0] = count
+// (at most max_tiles, the length of sched_e and sched_r).
+__global__ __launch_bounds__(1024) void mtile_schedule_kernel(const int* __restrict__ offsets,
+                                                             const int* __restrict__ active,
+                                                             const int* __restrict__ n_active, int E,
+                                                             int bm, int max_tiles, int* __restrict__ sched_e,
+                                                             int* __restrict__ sched_r,
+                                                             int* __restrict__ sched_n) {
+  __shared__ int wsum[1024 / kWave];
+  const int a = threadIdx.x, lane = a & 63, wave = a >> 6;
+  const int na = min(n_active[0], E);
+  int e = 0, cnt = 0;
+  if (a < na) {
+    e = active[a];
+    cnt = (offsets[e + 1] - offsets[e] + bm - 1) / bm;
+  }
+  int incl = cnt;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int v = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += v;
+  }
+  if (lane == kWave - 1) wsum[wave] = incl;
+  __syncthreads();
+  int before = 0, total = 0;
+  for (int w = 0; w < 1024 / kWave; ++w) {
+    if (w < wave) before += wsum[w];
+    total += wsum[w];
+  }
+  const int base = before + incl - cnt;
+  for (int i = 0; i < cnt && base + i < max_tiles; ++i) {
+    sched_e[base + i] = e;
+    sched_r[base + i] = i * bm;
+  }
+  if (a == 0) sched_n[0] = min(total, max_tiles);
+}
+
+template <int RBW, int WAVES, int WDEPTH, bool SWIGLU>
+hipError_t launch_large_cfg(const GemmArgs& a, int max_mtiles, hipStream_t stream) {
+  const auto kern = &gemm_stream_kernel<RBW, WAVES, kLTBM, WDEPTH, 2, true, SWIGLU, false>;
+  const size_t shmem = (size_t)Ring<kLTBM, false>::kBytes + (size_t)WAVES * 2 * RBW * 16 * kSPitch;
+  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
+  if (attr != hipSuccess) return attr;
+  mtile_schedule_kernel<<<1, 1024, 0, stream>>>(a.expert_offsets, a.active, a.n_active, a.E, 16 * kLTBM,
+                                                max_mtiles, const_cast<int*>(a.sched_e),
+                                                const_cast<int*>(a.sched_r), const_cast<int*>(a.sched_n));
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int ntiles_n = a.Nw / (16 * RBW * WAVES);
+  const int total = max_mtiles * ntiles_n;
+  const int grid = (total + 7) / 8 * 8;
+  kern<<<grid, WAVES * kWave, shmem, stream>>>(a, ntiles_n, total);
+  return hipGetLastError();
+}
+
+template <bool SWIGLU>
+hipError_t launch_large(const GemmArgs& a, int max_mtiles, hipStream_t stream) {
+  int rbw = 4, waves = 4;
+  if (const char* s = std::getenv("NVFP4MOE_LARGE_TILE")) std::sscanf(s, "%dx%d", &rbw, &waves);
+  if (rbw == 2 && waves == 8) return launch_large_cfg<2, 8, 4, SWIGLU>(a, max_mtiles, stream);
+  if (rbw == 2 && waves == 4) return launch_large_cfg<2, 4, 4, SWIGLU>(a, max_mtiles, stream);
+  return launch_large_cfg<4, 4, 2, SWIGLU>(a, max_mtiles, stream);
+}
+
 }  // namespace
+
+int large_rows_per_mtile() { return 16 * kLTBM; }
+bool large_supports(int Nw) { return Nw % 256 == 0; }   // every large tile shape is <= 256 rows
+
+hipError_t launch_gemm_large(const GemmArgs& a, int max_mtiles, hipStream_t stream) {
+  return a.swiglu ? launch_large<true>(a, max_mtiles, stream) : launch_large<false>(a, max_mtiles, stream);
+}
 
 hipError_t launch_gemm_stream(const GemmArgs& a, hipStream_t stream) {
   if (a.swiglu) return a.w4a4 ? launch_sw<true, true>(a, stream) : launch_sw<true, false>(a, stream);

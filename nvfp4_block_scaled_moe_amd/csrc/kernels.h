@@ -27,6 +27,10 @@ hipError_t launch_route_permute(const float* logits, int T, int E, int k, int* t
 // ---- act_prep.hip: bf16 rows -> f16 rows scaled by 2^-p (max |x| in [2^14, 2^15)) + p
 hipError_t launch_act_prep(const uint16_t* a, int64_t rows, int K, _Float16* a16, int* rexp,
                            hipStream_t stream);
+// NVFP4 rows (codes + E4M3 scales) -> the same f16 layout, decoded exactly (E2M1 * E4M3, the
+// global scale stays in the GEMM epilogue); rexp = 0.
+hipError_t launch_act_prep_fp4(const uint8_t* packed, const uint8_t* scales, int64_t rows, int K,
+                               _Float16* a16, int* rexp, hipStream_t stream);
 
 // ---- grouped GEMM kernels
 struct GemmArgs {
@@ -50,10 +54,16 @@ struct GemmArgs {
   void* out;
   int out_bf16;
   float* out_amax;                 // null or [1], zeroed before the GEMM
+  const int* sched_e;              // large-M path: m-tile -> expert   (workspace)
+  const int* sched_r;              // large-M path: m-tile -> first row (workspace)
+  const int* sched_n;              // large-M path: number of m-tiles  (workspace)
 };
 hipError_t launch_gemm_stream(const GemmArgs& a, hipStream_t stream);
-hipError_t launch_gemm_mfma(const GemmArgs& a, void* ws, size_t ws_bytes, hipStream_t stream);
-size_t gemm_mfma_ws_bytes(int rows, int Nw, int E);
+// large-M path: rows per m-tile, the Nw it supports, and the launcher (max_mtiles is the host
+// bound ceil(rows / rows_per_mtile) + min(E, rows) on the schedule length).
+int large_rows_per_mtile();
+bool large_supports(int Nw);
+hipError_t launch_gemm_large(const GemmArgs& a, int max_mtiles, hipStream_t stream);
 hipError_t launch_zero_f32(float* p, int n, hipStream_t stream);
 
 // ---- reduce.hip

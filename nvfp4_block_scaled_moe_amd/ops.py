@@ -12,7 +12,8 @@ import ctypes
 import torch
 
 from . import _lib
-from ._lib import BF16, EPI_NONE, EPI_SWIGLU, F32, W4A4, W4A16  # noqa: F401
+from ._lib import (BF16, EPI_NONE, EPI_SWIGLU, F32, PATH_MFMA, PATH_NONE, PATH_STREAM,  # noqa: F401
+                   W4A4, W4A16)
 
 
 def _ptr(t):

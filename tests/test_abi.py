@@ -89,6 +89,26 @@ def test_grouped_gemm_rejects_bad_arguments():
     assert st == _lib.ERR_WORKSPACE
 
 
+def test_grouped_gemm_workspace_follows_the_path(monkeypatch):
+    """The m-tiled path needs f16 activations (also for W4A4) and its m-tile schedule; the
+    size query and the call pick the path by the same rule, and a forced MFMA path that
+    cannot run the shape is refused before any work is queued."""
+    lib = _lib.load()
+    ws = lib.moe_grouped_gemm_workspace_size
+    monkeypatch.delenv("NVFP4MOE_FORCE_PATH", raising=False)
+    assert ws(_lib.W4A4, 512, 512, 64, 256, 256) == 0                 # 8 rows/expert: streaming
+    big = ws(_lib.W4A4, 8192, 8192, 64, 256, 256)                      # 128 rows/expert: MFMA
+    assert big >= 8192 * 256 * 2 + 8192 * 4 + 2 * (8192 // 128 + 64) * 4
+    assert ws(_lib.W4A16, 8192, 8192, 64, 256, 256) == big
+    assert ws(_lib.W4A4, 8192, 8192, 64, 160, 256) == 0                # Nw % 256 != 0: streaming
+    monkeypatch.setenv("NVFP4MOE_FORCE_PATH", "mfma")
+    assert ws(_lib.W4A4, 512, 512, 64, 256, 256) > 512 * 256 * 2
+    st, msg = _err(_gemm(lib, Nw=96))
+    assert st == _lib.ERR_UNSUPPORTED and "256" in msg
+    monkeypatch.setenv("NVFP4MOE_FORCE_PATH", "stream")
+    assert ws(_lib.W4A4, 8192, 8192, 64, 256, 256) == 0
+
+
 def test_unpermute_reduce_and_fp8_reject_bad_arguments():
     lib = _lib.load()
     assert lib.moe_unpermute_reduce(FAKE, _lib.F32, FAKE, FAKE, 4, 2, 12, FAKE, None) == _lib.ERR_INVALID_ARG

@@ -226,6 +226,79 @@ def test_grouped_gemm_amax_output():
     assert np_(amax)[0] == np.abs(np_(out)).max()
 
 
+# ------------------------------------------------------------------ grouped GEMM, large-M path
+# The m-tiled MFMA path (128-row m-tiles from a device-side schedule) is chosen by size;
+# these cases force it, so they also cover shapes the size rule would send elsewhere.
+MFMA_CASES = [
+    ([3, 0, 16, 17, 1], 256, 64),        # every m-tile ragged, K < one chunk
+    ([200, 0, 130, 1], 512, 96),         # several m-tiles per expert, K % 128 != 0
+    ([129, 127, 0, 300], 256, 1024),     # m-tile boundaries at 128 +- 1
+    ([600], 768, 256),                   # one expert, three 256-row tiles (SwiGLU F = 384)
+    ([1, 70, 3], 2048, 6144),            # full model K
+]
+
+
+@pytest.mark.parametrize("counts,Nw,K", MFMA_CASES)
+@pytest.mark.parametrize("mode", [ops.W4A16, ops.W4A4])
+def test_grouped_gemm_mfma_path(counts, Nw, K, mode, monkeypatch):
+    say("gemm mfma", counts, Nw, K, mode)
+    monkeypatch.setenv("NVFP4MOE_FORCE_PATH", "mfma")
+    d = _problem(counts, Nw, K, seed=7 * Nw + K + mode, mode=mode)
+    for epi in (ops.EPI_NONE, ops.EPI_SWIGLU):
+        want = omoe.grouped_gemm(d["A"], d["offsets"], d["W"], "swiglu" if epi else "none")
+        got32 = _run_gemm(d, mode, epi, torch.float32)
+        assert ops.last_dispatch() == ops.PATH_MFMA
+        assert_finite(got32)
+        r = rel_fro(got32, want)
+        assert r < 1e-5, r        # identical operands on both sides: only summation order differs
+        got16 = _run_gemm(d, mode, epi, torch.bfloat16)
+        assert rel_fro(got16, omoe.bf16_round(want)) <= W4A16_TOL
+
+
+@pytest.mark.parametrize("tile", ["2x8", "2x4", "4x4"])
+def test_grouped_gemm_mfma_tile_shapes(tile, monkeypatch):
+    say("gemm mfma tile", tile)
+    monkeypatch.setenv("NVFP4MOE_FORCE_PATH", "mfma")
+    monkeypatch.setenv("NVFP4MOE_LARGE_TILE", tile)
+    d = _problem([150, 0, 40, 270], 512, 640, seed=31)
+    for epi in (ops.EPI_NONE, ops.EPI_SWIGLU):
+        want = omoe.grouped_gemm(d["A"], d["offsets"], d["W"], "swiglu" if epi else "none")
+        got = _run_gemm(d, ops.W4A16, epi, torch.float32)
+        assert ops.last_dispatch() == ops.PATH_MFMA
+        assert rel_fro(got, want) < 1e-5
+
+
+@pytest.mark.parametrize("mode", [ops.W4A16, ops.W4A4])
+def test_grouped_gemm_mfma_gather(mode, monkeypatch):
+    say("gemm mfma gather", mode)
+    monkeypatch.setenv("NVFP4MOE_FORCE_PATH", "mfma")
+    d = _problem([7, 0, 300, 9], 256, 256, seed=5, T=120, k=3, mode=mode)
+    want = omoe.grouped_gemm(d["A"], d["offsets"], d["W"], "swiglu")
+    got = _run_gemm(d, mode, ops.EPI_SWIGLU, torch.float32)
+    assert ops.last_dispatch() == ops.PATH_MFMA
+    assert rel_fro(got, want) < 1e-5
+
+
+def test_grouped_gemm_path_choice_by_size(monkeypatch):
+    """Mean rows per expert >= 64 selects the MFMA path; both paths agree on it."""
+    say("gemm path choice")
+    monkeypatch.delenv("NVFP4MOE_FORCE_PATH", raising=False)
+    big = _problem([100, 60, 0, 96], 256, 256, seed=9)          # 256 rows over 4 experts
+    got_auto = _run_gemm(big, ops.W4A16, ops.EPI_SWIGLU, torch.float32)
+    assert ops.last_dispatch() == ops.PATH_MFMA
+    monkeypatch.setenv("NVFP4MOE_FORCE_PATH", "stream")
+    got_stream = _run_gemm(big, ops.W4A16, ops.EPI_SWIGLU, torch.float32)
+    assert ops.last_dispatch() == ops.PATH_STREAM
+    assert rel_fro(got_auto, got_stream) < 1e-5
+    monkeypatch.delenv("NVFP4MOE_FORCE_PATH")
+    small = _problem([10, 20, 0, 30], 256, 256, seed=9)
+    _run_gemm(small, ops.W4A16, ops.EPI_SWIGLU, torch.float32)
+    assert ops.last_dispatch() == ops.PATH_STREAM
+    odd = _problem([300, 300], 160, 256, seed=9)                # Nw % 256 != 0: streaming path
+    _run_gemm(odd, ops.W4A16, ops.EPI_NONE, torch.float32)
+    assert ops.last_dispatch() == ops.PATH_STREAM
+
+
 # ------------------------------------------------------------------ reduce
 @pytest.mark.parametrize("T,k,H,ydt", [(16, 2, 256, torch.float32), (7, 22, 64, torch.bfloat16),
                                        (512, 8, 6144, torch.float32)])
