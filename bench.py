@@ -88,6 +88,9 @@ def main():
     print(f"[bench] setup {setup_s:.1f}s: {wl.name} T={T} E={wl.E} k={wl.k} H={wl.H} F={wl.F} mode={wl.mode}",
           file=sys.stderr, flush=True)
 
+    if wl.name == "dense":
+        print(json.dumps(dense_line(torch, ops, inputs, wl, args, T)), flush=True)
+        return
     res = measure(torch, ops, layer, wl, w, x, lg, T, mode, args.steps, args.warmup)
     line = dict(
         metric="MoE NVFP4 grouped-GEMM TFLOPS + weight GB/s vs tokens/expert, % roofline",
@@ -102,7 +105,7 @@ def main():
                     "v_mfma_f32_16x16x32_f16, fp32 accumulation"),
         weight_GBps=round(res["weight_gbs"], 1),
         weight_hbm_frac=round(res["weight_gbs"] / HBM_PEAK_GBS, 4),
-        stage_us=res["stage_us"],
+        stage_us=res["stage_us"], up_gemm_path=res["up_path"],
         roofline=res.get("roofline"),
         baseline_context=("pages: 0.8-55 TFLOPS for FP4 MoE GEMMs at per-expert M=16-64 (256 experts, "
                           "top-8, 512 concurrent) on RTX PRO 6000 Blackwell SM120; vs_baseline divides by 55"),
@@ -173,6 +176,8 @@ def measure(torch, ops, layer, wl, w, x, lg, T, mode, steps, warmup, graph=False
     touched = int(r["n_active"].item())
     flops, w13_bytes, w2_bytes = layer_work(wl, T, touched)
 
+    paths = {}
+
     def step(ev=None):
         mark = (lambda i: ev[i].record()) if ev else (lambda i: None)
         mark(0)
@@ -182,30 +187,37 @@ def measure(torch, ops, layer, wl, w, x, lg, T, mode, steps, warmup, graph=False
         common = dict(expert_offsets=rr["expert_offsets"], active_experts=rr["active_experts"],
                       n_active=rr["n_active"])
         if mode == ops.W4A16:
+            mark(2)
             h = ops.moe_grouped_gemm_nvfp4(ops.W4A16, ops.EPI_SWIGLU, xx, w.w13_packed, w.w13_scales, w.w13_g,
                                            gather_index=rr["sorted_slot"], gather_div=k, rows=S,
                                            out_dtype=torch.bfloat16, **common)
-            mark(2)
+            mark(3)
+            paths["up"] = ops.last_dispatch()
+            mark(4)
             y = ops.moe_grouped_gemm_nvfp4(ops.W4A16, ops.EPI_NONE, h, w.w2_packed, w.w2_scales, w.w2_g,
                                            rows=S, out_dtype=torch.float32, **common)
         else:
             xq, xs, xg = ops.nvfp4_quantize(xx)
+            mark(2)
             h, amax = ops.moe_grouped_gemm_nvfp4(ops.W4A4, ops.EPI_SWIGLU, xq, w.w13_packed, w.w13_scales,
                                                  w.w13_g, a_scales=xs, a_g=xg, gather_index=rr["sorted_slot"],
                                                  gather_div=k, rows=S, out_dtype=torch.float32,
                                                  want_amax=True, **common)
-            mark(2)
+            mark(3)
+            paths["up"] = ops.last_dispatch()
             hq, hs, hg = ops.nvfp4_quantize(h, amax=amax)
+            mark(4)
             y = ops.moe_grouped_gemm_nvfp4(ops.W4A4, ops.EPI_NONE, hq, w.w2_packed, w.w2_scales, w.w2_g,
                                            a_scales=hs, a_g=hg, rows=S, out_dtype=torch.float32, **common)
-        mark(3)
+        mark(5)
         out = ops.moe_unpermute_reduce(y, rr["slot_to_row"], rr["topk_w"])
-        mark(4)
+        mark(6)
         return out
 
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    up_path = paths["up"]
     if graph:
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
@@ -219,30 +231,93 @@ def measure(torch, ops, layer, wl, w, x, lg, T, mode, steps, warmup, graph=False
         ms = (time.perf_counter() - t0) * 1e3 / steps
         stage = None
     else:
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(steps)]
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(steps)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(steps):
             step(evs[i])
         torch.cuda.synchronize()
         ms = (time.perf_counter() - t0) * 1e3 / steps
-        names = ["route_permute", "up_gate_swiglu", "down", "unpermute_reduce"]
+        names = ["route_permute", "quantize_x", "up_gate_swiglu", "quantize_h", "down", "unpermute_reduce"]
         stage = {n: round(1e3 * sum(e[j].elapsed_time(e[j + 1]) for e in evs) / steps, 2)
                  for j, n in enumerate(names)}
-    act_in = T * wl.H * 2
+    act_in = T * wl.H * (2 if mode == ops.W4A16 else 9 / 16)
     h_bytes = S * wl.F * (2 if mode == ops.W4A16 else 4)
     up_bytes = w13_bytes + act_in + h_bytes
+    up_flops = 2.0 * S * 2 * wl.F * wl.H
     res = dict(ms_per_step=ms, tflops=flops / (ms * 1e-3) / 1e12,
-               weight_gbs=(w13_bytes + w2_bytes) / (ms * 1e-3) / 1e9, touched=touched, stage_us=stage)
+               weight_gbs=(w13_bytes + w2_bytes) / (ms * 1e-3) / 1e9, touched=touched, stage_us=stage,
+               up_path="mfma" if up_path == ops.PATH_MFMA else "stream")
     if stage:
         up_us = stage["up_gate_swiglu"]
-        ach = up_bytes / (up_us * 1e-6) / 1e9
-        res["roofline"] = dict(
-            bound="hbm", kernel="gemm_stream_kernel (up/gate + SwiGLU)", achieved=round(ach, 1),
-            peak=HBM_PEAK_GBS, unit="GB/s", frac=round(ach / HBM_PEAK_GBS, 4), traffic=None,
-            bytes_per_launch=int(up_bytes), launch_us=up_us,
-            bytes_note="W13 packed+scales of touched experts (9/16 B/weight) + bf16 activations in + h out")
+        if up_path == ops.PATH_MFMA:
+            ach = up_flops / (up_us * 1e-6) / 1e12
+            res["roofline"] = dict(
+                bound="mfma", kernel="gemm_stream_kernel large-M (up/gate + SwiGLU)", achieved=round(ach, 1),
+                peak=BF16_PEAK_TFLOPS, unit="TFLOP/s", frac=round(ach / BF16_PEAK_TFLOPS, 4), traffic=None,
+                flops_per_launch=up_flops, launch_us=up_us,
+                flops_note="2*S*2F*H useful flops (rows of ragged m-tiles padded on the GPU are not counted); "
+                           "f16 MFMA peak")
+        else:
+            ach = up_bytes / (up_us * 1e-6) / 1e9
+            res["roofline"] = dict(
+                bound="hbm", kernel="gemm_stream_kernel (up/gate + SwiGLU)", achieved=round(ach, 1),
+                peak=HBM_PEAK_GBS, unit="GB/s", frac=round(ach / HBM_PEAK_GBS, 4), traffic=None,
+                bytes_per_launch=int(up_bytes), launch_us=up_us,
+                bytes_note="W13 packed+scales of touched experts (9/16 B/weight) + activations in + h out")
     return res
+
+
+def dense_line(torch, ops, inputs, wl, args, M):
+    """The dense NVFP4 GEMM Y[M,N] = A[M,K] W[N,K]^T (E = 1, no SwiGLU) in W4A16 and W4A4,
+    beside torch.mm on bf16 copies of the same operands. A is bf16 for W4A16; for W4A4 it is
+    quantized to NVFP4 before the timed region (the pages compare the GEMMs alone)."""
+    dev = "cuda"
+    N, K = wl.F, wl.H
+    wq, ws_, wg = ops.nvfp4_quantize(inputs.expert_weight_fp32(wl, "dense", 0, dev).unsqueeze(0))
+    a = inputs.activations_bf16(wl, M).to(dev)
+    aq, as_, ag = ops.nvfp4_quantize(a)
+    one = torch.tensor([0, M], dtype=torch.int32, device=dev)
+    act = torch.zeros(1, dtype=torch.int32, device=dev)
+    na = torch.ones(1, dtype=torch.int32, device=dev)
+    wbf = inputs.expert_weight_fp32(wl, "dense", 0, dev).to(torch.bfloat16)
+    flops = 2.0 * M * N * K
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e3 / args.steps      # us per call
+
+    common = dict(expert_offsets=one, active_experts=act, n_active=na, out_dtype=torch.bfloat16)
+    t16 = timed(lambda: ops.moe_grouped_gemm_nvfp4(ops.W4A16, ops.EPI_NONE, a, wq, ws_, wg, **common))
+    path16 = ops.last_dispatch()
+    t4 = timed(lambda: ops.moe_grouped_gemm_nvfp4(ops.W4A4, ops.EPI_NONE, aq, wq, ws_, wg, a_scales=as_,
+                                                  a_g=ag, **common))
+    tmm = timed(lambda: torch.mm(a, wbf.t()))
+    tf = lambda us: flops / (us * 1e-6) / 1e12
+    return dict(
+        metric="MoE NVFP4 grouped-GEMM TFLOPS + weight GB/s vs tokens/expert, % roofline",
+        value=round(tf(t16), 2), unit="TFLOP/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
+        ms_per_step=round(t16 / 1e3, 5), higher_is_better=True, scaling="weak", vs_baseline=None,
+        dtype="f16", data="synthetic",
+        config=dict(workload=f"dense NVFP4 GEMM M={M} N={N} K={K}, W4A16 (bf16 activations)", M=M, N=N, K=K,
+                    path="mfma" if path16 == ops.PATH_MFMA else "stream"),
+        w4a4_tflops=round(tf(t4), 2), w4a4_us=round(t4, 2),
+        torch_mm_bf16_tflops=round(tf(tmm), 2), torch_mm_bf16_us=round(tmm, 2),
+        roofline=dict(bound="mfma", kernel="moe_grouped_gemm_nvfp4 call (activation prep + GEMM)",
+                      achieved=round(tf(t16), 1), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                      frac=round(tf(t16) / BF16_PEAK_TFLOPS, 4), traffic=None),
+        baseline_context="pages: 437 TFLOPS FP4 vs 225 TFLOPS BF16 at M=512 on RTX PRO 6000 (SM120)",
+        cpu_baseline=None,
+    )
 
 
 def cpu_baseline(torch, wl, w, x, lg, T, mode, seconds):

@@ -1,0 +1,101 @@
+// Pieces shared by the two grouped-GEMM kernels (gemm_stream.hip, gemm_large.hip): buffer
+// loads and the epilogue.
+#pragma once
+
+#include "common.h"
+#include "kernels.h"
+
+namespace nvfp4moe {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kChunk = 128;              // k per chunk (16 bytes of FP4 per lane)
+constexpr uint32_t kOOB = 0x80000000u;   // buffer offset past every resource: loads return 0
+constexpr int kRsrcFlags = 0x00020000;   // raw buffer resource word 3 for gfx9 (32-bit data)
+
+template <int N>
+struct Int {
+  static constexpr int value = N;
+};
+
+// Raw buffer resource over [base, base + bytes): 32-bit offsets, loads past the end read 0.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcFlags);
+}
+__device__ __forceinline__ u32x4 ld128(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+}
+__device__ __forceinline__ uint32_t ld16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+}
+
+// Epilogue of one wave's tile: RBW blocks of 16 weight rows x TBM blocks of 16 GEMM rows,
+// with MFMA 16x16 output layout (lane l holds weight rows 4*(l/16)+i of each block, GEMM
+// row l%16 of each token block). GEMM rows tc .. tc+16*ntb-1 of the expert (those < M) are
+// written: out = acc * alpha * 2^pexp, where pexp is the activation row's power-of-two
+// scale (W4A16) or 0; with SwiGLU the first RBW/2 blocks are gate rows and the others the
+// matching up rows, and silu(gate) * up is written to column blkrow(b) of the F-wide output.
+// Returns the running max of |written value| as float bits.
+template <int RBW, int TBM, bool SWIGLU, typename BlkRow>
+__device__ __forceinline__ uint32_t store_tile(const GemmArgs& p, const f32x4 (&acc)[RBW][TBM], int tc,
+                                               int ntb, int M, int r0, float alpha, bool row_exp,
+                                               BlkRow blkrow, int lane, uint32_t amax_bits) {
+  const int l16 = lane & 15, g = lane >> 4;
+  const int Nw = p.Nw, F = Nw >> 1;
+#pragma unroll
+  for (int tb = 0; tb < TBM; ++tb) {
+    const int t = tc + 16 * tb + l16;
+    if (tb < ntb && t < M) {
+      const int row = r0 + t;
+      const int pexp = row_exp ? p.rexp[p.gather_index ? p.gather_index[row] / p.gather_div : row] : 0;
+      if (SWIGLU) {
+#pragma unroll
+        for (int b = 0; b < RBW / 2; ++b) {
+          float h[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float gv = ldexpf(acc[b][tb][i] * alpha, pexp);
+            const float uv = ldexpf(acc[b + RBW / 2][tb][i] * alpha, pexp);
+            h[i] = gv / (1.0f + expf(-gv)) * uv;
+            amax_bits = max(amax_bits, abs_bits(h[i]));
+          }
+          const size_t o = (size_t)row * F + blkrow(b) + 4 * g;
+          if (p.out_bf16)
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + o) =
+                make_uint2(f32_to_bf16(h[0]) | (f32_to_bf16(h[1]) << 16),
+                           f32_to_bf16(h[2]) | (f32_to_bf16(h[3]) << 16));
+          else
+            *reinterpret_cast<float4*>(static_cast<float*>(p.out) + o) = make_float4(h[0], h[1], h[2], h[3]);
+        }
+      } else {
+#pragma unroll
+        for (int b = 0; b < RBW; ++b) {
+          float v[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            v[i] = ldexpf(acc[b][tb][i] * alpha, pexp);
+            amax_bits = max(amax_bits, abs_bits(v[i]));
+          }
+          const size_t o = (size_t)row * Nw + blkrow(b) + 4 * g;
+          if (p.out_bf16)
+            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + o) =
+                make_uint2(f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16),
+                           f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16));
+          else
+            *reinterpret_cast<float4*>(static_cast<float*>(p.out) + o) = make_float4(v[0], v[1], v[2], v[3]);
+        }
+      }
+    }
+  }
+  return amax_bits;
+}
+
+// Wave-reduced amax of the tile, merged into *out_amax (float bits of non-negative values
+// order like the values).
+__device__ __forceinline__ void merge_amax(float* out_amax, uint32_t amax_bits, int lane) {
+  if (!out_amax) return;
+  amax_bits = wave_max_u32(amax_bits);
+  if (lane == 0 && amax_bits) atomicMax(reinterpret_cast<unsigned int*>(out_amax), amax_bits);
+}
+
+}  // namespace nvfp4moe

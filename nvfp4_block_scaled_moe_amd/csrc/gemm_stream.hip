@@ -37,37 +37,16 @@
 #include <cstdio>
 #include <cstdlib>
 
-#include "common.h"
-#include "kernels.h"
+#include "gemm_common.h"
 
 namespace nvfp4moe {
 
 namespace {
 
-constexpr int kChunk = 128;              // k per chunk (16 bytes of FP4 per lane)
 constexpr int kWin = 8;                  // chunks per scale window (1024 k)
 constexpr int kDepth = 4;                // weight chunks in flight per wave
 constexpr int kSPitch = 80;              // LDS pitch of a 64-byte scale row (bank spread)
-constexpr uint32_t kOOB = 0x80000000u;   // buffer offset past every resource: loads return 0
 constexpr uint32_t kNoDst = 0xffffffffu;
-constexpr int kRsrcFlags = 0x00020000;   // raw buffer resource word 3 for gfx9 (32-bit data)
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcFlags);
-}
-__device__ __forceinline__ u32x4 ld128(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
-}
-__device__ __forceinline__ uint32_t ld16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
-}
-
-template <int N>
-struct Int {
-  static constexpr int value = N;
-};
 
 template <int TBM, bool A4>
 struct Ring {
@@ -79,18 +58,10 @@ struct Ring {
   static constexpr int kBytes = 2 * kSlot;
 };
 
-// LARGE = false: small-M path; a workgroup owns (expert, row tile) and loops over the
-//   expert's rows 16*TBM at a time.
-// LARGE = true: large-M path; a workgroup owns (m-tile, row tile), where the m-tiles (16*TBM
-//   consecutive rows of one expert) come from the device-side schedule built by
-//   mtile_schedule_kernel, so every workgroup does one pass and large experts spread over
-//   many workgroups. Activations are always f16 there (W4A4 activations are decoded exactly
-//   to f16 beforehand).
-template <int RBW, int WAVES, int TBM, int WDEPTH, int BDEPTH, bool LARGE, bool SWIGLU, bool A4>
+template <int RBW, int WAVES, int TBM, int WDEPTH, int BDEPTH, bool SWIGLU, bool A4>
 __global__ __launch_bounds__(WAVES* kWave) void gemm_stream_kernel(const GemmArgs p, int tiles_per_expert,
                                                                    int total_tiles) {
   static_assert(RBW % 2 == 0, "row blocks per wave come in pairs");
-  static_assert(!(LARGE && A4), "the large-M path reads f16 activations");
   static_assert(kWin % WDEPTH == 0 && kWin % BDEPTH == 0, "ring depths divide the scale window");
   using R = Ring<TBM, A4>;
   constexpr int NT = WAVES * kWave;
@@ -102,20 +73,12 @@ __global__ __launch_bounds__(WAVES* kWave) void gemm_stream_kernel(const GemmArg
   const int per_xcd = gridDim.x >> 3;
   const int tile = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
   if (tile >= total_tiles) return;
-  const int aidx = tile / tiles_per_expert;        // active-expert slot, or m-tile (LARGE)
+  const int aidx = tile / tiles_per_expert;        // active-expert slot
   const int nb = tile - aidx * tiles_per_expert;   // row tile
-  int e, tc_begin = 0;
-  if (LARGE) {
-    if (aidx >= p.sched_n[0]) return;
-    e = p.sched_e[aidx];
-    tc_begin = p.sched_r[aidx];
-  } else {
-    if (aidx >= p.n_active[0]) return;
-    e = p.active[aidx];
-  }
+  if (aidx >= p.n_active[0]) return;
+  const int e = p.active[aidx];
   const int r0 = p.expert_offsets[e];
   const int M = p.expert_offsets[e + 1] - r0;
-  const int tc_end = LARGE ? min(M, tc_begin + 16 * TBM) : M;
   const int K = p.K, Nw = p.Nw, Kh = K >> 1, Ks = K >> 4;
   const int K128 = (K + 127) & ~127;
   const int F = Nw >> 1;
@@ -146,7 +109,7 @@ __global__ __launch_bounds__(WAVES* kWave) void gemm_stream_kernel(const GemmArg
     wsoff[b] = __builtin_amdgcn_readfirstlane((uint32_t)(blkrow(b) - blkrow(0)) * Kh);
     ssoff[b] = __builtin_amdgcn_readfirstlane((uint32_t)(blkrow(b) - blkrow(0)) * Ks);
   }
-  const float alpha = (A4 || p.w4a4) ? p.w_g[e] * p.a_g[0] : p.w_g[e];
+  const float alpha = A4 ? p.w_g[e] * p.a_g[0] : p.w_g[e];
 
   __amdgpu_buffer_rsrc_t ar, asr;
   if (A4) {
@@ -163,7 +126,7 @@ __global__ __launch_bounds__(WAVES* kWave) void gemm_stream_kernel(const GemmArg
   constexpr int ROUNDS = (16 * TBM + TPR - 1) / TPR;
 
   uint32_t amax_bits = 0;
-  for (int tc = tc_begin; tc < tc_end; tc += 16 * TBM) {
+  for (int tc = 0; tc < M; tc += 16 * TBM) {
     const int ntb = __builtin_amdgcn_readfirstlane(min(TBM, (M - tc + 15) >> 4));
     uint32_t bsrc[ROUNDS], bdst[ROUNDS], bssrc[ROUNDS], bsdst[ROUNDS];
 #pragma unroll
@@ -263,11 +226,12 @@ __global__ __launch_bounds__(WAVES* kWave) void gemm_stream_kernel(const GemmArg
           *reinterpret_cast<u32x4*>(base + (16 * b + l16) * kSPitch + 16 * g) = sst[b];
       };
       u32x4 wring[WDEPTH][RBW];
-      auto w_issue = [&](u32x4& dst, int c, int b) {
+      auto w_issue = [&](int d, int c, int b) {
         const bool kin = c < nch && (c * kChunk + 32 * g) < K;
-        dst = ld128(wr, kin ? wlane + (uint32_t)(c * kChunk) / 2 : kOOB, wsoff[b]);
+        wring[d][b] = ld128(wr, kin ? wlane + (uint32_t)(c * kChunk) / 2 : kOOB, wsoff[b]);
       };
-      auto compute = [&](u32x4 (&wv)[RBW], int c) {
+      auto compute = [&](int d, int c) {
+        u32x4 (&wv)[RBW] = wring[d];
         const unsigned char* base = ring + (c & 1) * R::kSlot;
         const unsigned char* sbase = sws + ((c / kWin) & 1) * (RBW * 16 * kSPitch);
         const int soff = (c % kWin) * 8 + 2 * g;
@@ -285,7 +249,7 @@ __global__ __launch_bounds__(WAVES* kWave) void gemm_stream_kernel(const GemmArg
           wf[b][1] = decode8(wv[b][1], s0);
           wf[b][2] = decode8(wv[b][2], s1);
           wf[b][3] = decode8(wv[b][3], s1);
-          w_issue(wv[b], c + WDEPTH, b);   // this ring entry is free again
+          w_issue(d, c + WDEPTH, b);   // this ring entry is free again
         }
         u32x4 aq[A4 ? NTB : 1];
         f16x2 as0[A4 ? NTB : 1], as1[A4 ? NTB : 1];
@@ -321,7 +285,7 @@ __global__ __launch_bounds__(WAVES* kWave) void gemm_stream_kernel(const GemmArg
         if (d < BDEPTH) b_issue(d, d);
         if (d < WDEPTH) {
 #pragma unroll
-          for (int b = 0; b < RBW; ++b) w_issue(wring[d][b], d, b);
+          for (int b = 0; b < RBW; ++b) w_issue(d, d, b);
         }
       }
       s_commit(0);
@@ -334,69 +298,21 @@ __global__ __launch_bounds__(WAVES* kWave) void gemm_stream_kernel(const GemmArg
         for (int u = 0; u < kWin; ++u) {
           const int c = c0 + u;
           b_issue(u % BDEPTH, c + BDEPTH);         // set u%BDEPTH was committed last step
-          compute(wring[u % WDEPTH], c);           // requests weights of chunk c+WDEPTH
+          compute(u % WDEPTH, c);                  // requests weights of chunk c+WDEPTH
           b_commit((u + 1) % BDEPTH, (c + 1) & 1);
           if (u == kWin - 1) s_commit(c0 / kWin + 1);
           __syncthreads();
         }
       }
     };
-    if (LARGE || ntb == TBM) kloop(Int<TBM>{});
+    if (ntb == TBM) kloop(Int<TBM>{});
     else kloop(Int<1>{});
 
-    // Epilogue: lane l holds rows 4*(l/16)+i of each block, token column l%16.
-#pragma unroll
-    for (int tb = 0; tb < TBM; ++tb) {
-      const int t = tc + 16 * tb + l16;
-      if (tb < ntb && t < M) {
-        const int row = r0 + t;
-        const int pexp = A4 ? 0 : p.rexp[p.gather_index ? p.gather_index[row] / p.gather_div : row];
-        if (SWIGLU) {
-#pragma unroll
-          for (int b = 0; b < RBW / 2; ++b) {
-            float h[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float gv = ldexpf(acc[b][tb][i] * alpha, pexp);
-              const float uv = ldexpf(acc[b + RBW / 2][tb][i] * alpha, pexp);
-              h[i] = gv / (1.0f + expf(-gv)) * uv;
-              amax_bits = max(amax_bits, abs_bits(h[i]));
-            }
-            const size_t o = (size_t)row * F + blkrow(b) + 4 * g;
-            if (p.out_bf16)
-              *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + o) =
-                  make_uint2(f32_to_bf16(h[0]) | (f32_to_bf16(h[1]) << 16),
-                             f32_to_bf16(h[2]) | (f32_to_bf16(h[3]) << 16));
-            else
-              *reinterpret_cast<float4*>(static_cast<float*>(p.out) + o) = make_float4(h[0], h[1], h[2], h[3]);
-          }
-        } else {
-#pragma unroll
-          for (int b = 0; b < RBW; ++b) {
-            float v[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              v[i] = ldexpf(acc[b][tb][i] * alpha, pexp);
-              amax_bits = max(amax_bits, abs_bits(v[i]));
-            }
-            const size_t o = (size_t)row * Nw + blkrow(b) + 4 * g;
-            if (p.out_bf16)
-              *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + o) =
-                  make_uint2(f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16),
-                             f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16));
-            else
-              *reinterpret_cast<float4*>(static_cast<float*>(p.out) + o) = make_float4(v[0], v[1], v[2], v[3]);
-          }
-        }
-      }
-    }
+    amax_bits = store_tile<RBW, TBM, SWIGLU>(p, acc, tc, ntb, M, r0, alpha, !A4, blkrow, lane, amax_bits);
     __syncthreads();   // the LDS rings are reused by the next pass
   }
 
-  if (p.out_amax) {
-    amax_bits = wave_max_u32(amax_bits);
-    if (lane == 0 && amax_bits) atomicMax(reinterpret_cast<unsigned int*>(p.out_amax), amax_bits);
-  }
+  merge_amax(p.out_amax, amax_bits, lane);
 }
 
 template <int RBW, int WAVES, bool SWIGLU, bool A4>
@@ -408,7 +324,7 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
   const int total = max_active * tiles_per_expert;
   const int grid = (total + 7) / 8 * 8;
   const size_t shmem = (size_t)Ring<TBM, A4>::kBytes + (size_t)WAVES * 2 * RBW * 16 * kSPitch;
-  gemm_stream_kernel<RBW, WAVES, TBM, kDepth, kDepth, false, SWIGLU, A4>
+  gemm_stream_kernel<RBW, WAVES, TBM, kDepth, kDepth, SWIGLU, A4>
       <<<grid, WAVES * kWave, shmem, stream>>>(a, tiles_per_expert, total);
   return hipGetLastError();
 }
@@ -432,85 +348,7 @@ hipError_t launch_sw(const GemmArgs& a, hipStream_t stream) {
   return launch_cfg<2, 4, SWIGLU, A4>(a, stream);
 }
 
-// ---- large-M path
-// Tile: RBW row blocks per wave x WAVES waves (16*RBW*WAVES weight rows) by 16*TBM rows of
-// one expert. NVFP4MOE_LARGE_TILE=<rbw>x<waves> selects a built shape for tuning.
-constexpr int kLTBM = 8;
-
-// m-tiles of bm rows over the active experts (one workgroup, n_active <= 1024):
-// sched_e[i] = expert, sched_r[i] = first row within the expert, sched_n[0] = count
-// (at most max_tiles, the length of sched_e and sched_r).
-__global__ __launch_bounds__(1024) void mtile_schedule_kernel(const int* __restrict__ offsets,
-                                                             const int* __restrict__ active,
-                                                             const int* __restrict__ n_active, int E,
-                                                             int bm, int max_tiles, int* __restrict__ sched_e,
-                                                             int* __restrict__ sched_r,
-                                                             int* __restrict__ sched_n) {
-  __shared__ int wsum[1024 / kWave];
-  const int a = threadIdx.x, lane = a & 63, wave = a >> 6;
-  const int na = min(n_active[0], E);
-  int e = 0, cnt = 0;
-  if (a < na) {
-    e = active[a];
-    cnt = (offsets[e + 1] - offsets[e] + bm - 1) / bm;
-  }
-  int incl = cnt;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int v = __shfl_up(incl, o, kWave);
-    if (lane >= o) incl += v;
-  }
-  if (lane == kWave - 1) wsum[wave] = incl;
-  __syncthreads();
-  int before = 0, total = 0;
-  for (int w = 0; w < 1024 / kWave; ++w) {
-    if (w < wave) before += wsum[w];
-    total += wsum[w];
-  }
-  const int base = before + incl - cnt;
-  for (int i = 0; i < cnt && base + i < max_tiles; ++i) {
-    sched_e[base + i] = e;
-    sched_r[base + i] = i * bm;
-  }
-  if (a == 0) sched_n[0] = min(total, max_tiles);
-}
-
-template <int RBW, int WAVES, int WDEPTH, bool SWIGLU>
-hipError_t launch_large_cfg(const GemmArgs& a, int max_mtiles, hipStream_t stream) {
-  const auto kern = &gemm_stream_kernel<RBW, WAVES, kLTBM, WDEPTH, 2, true, SWIGLU, false>;
-  const size_t shmem = (size_t)Ring<kLTBM, false>::kBytes + (size_t)WAVES * 2 * RBW * 16 * kSPitch;
-  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
-  if (attr != hipSuccess) return attr;
-  mtile_schedule_kernel<<<1, 1024, 0, stream>>>(a.expert_offsets, a.active, a.n_active, a.E, 16 * kLTBM,
-                                                max_mtiles, const_cast<int*>(a.sched_e),
-                                                const_cast<int*>(a.sched_r), const_cast<int*>(a.sched_n));
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const int ntiles_n = a.Nw / (16 * RBW * WAVES);
-  const int total = max_mtiles * ntiles_n;
-  const int grid = (total + 7) / 8 * 8;
-  kern<<<grid, WAVES * kWave, shmem, stream>>>(a, ntiles_n, total);
-  return hipGetLastError();
-}
-
-template <bool SWIGLU>
-hipError_t launch_large(const GemmArgs& a, int max_mtiles, hipStream_t stream) {
-  int rbw = 4, waves = 4;
-  if (const char* s = std::getenv("NVFP4MOE_LARGE_TILE")) std::sscanf(s, "%dx%d", &rbw, &waves);
-  if (rbw == 2 && waves == 8) return launch_large_cfg<2, 8, 4, SWIGLU>(a, max_mtiles, stream);
-  if (rbw == 2 && waves == 4) return launch_large_cfg<2, 4, 4, SWIGLU>(a, max_mtiles, stream);
-  return launch_large_cfg<4, 4, 2, SWIGLU>(a, max_mtiles, stream);
-}
-
 }  // namespace
-
-int large_rows_per_mtile() { return 16 * kLTBM; }
-bool large_supports(int Nw) { return Nw % 256 == 0; }   // every large tile shape is <= 256 rows
-
-hipError_t launch_gemm_large(const GemmArgs& a, int max_mtiles, hipStream_t stream) {
-  return a.swiglu ? launch_large<true>(a, max_mtiles, stream) : launch_large<false>(a, max_mtiles, stream);
-}
 
 hipError_t launch_gemm_stream(const GemmArgs& a, hipStream_t stream) {
   if (a.swiglu) return a.w4a4 ? launch_sw<true, true>(a, stream) : launch_sw<true, false>(a, stream);
