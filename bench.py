@@ -188,26 +188,26 @@ def measure(torch, ops, layer, wl, w, x, lg, T, mode, steps, warmup, graph=False
                       n_active=rr["n_active"])
         if mode == ops.W4A16:
             mark(2)
-            h = ops.moe_grouped_gemm_nvfp4(ops.W4A16, ops.EPI_SWIGLU, xx, w.w13_packed, w.w13_scales, w.w13_g,
+            h = ops.moe_grouped_gemm_nvfp4(ops.W4A16, ops.EPI_SWIGLU, xx, w.w13_t,
                                            gather_index=rr["sorted_slot"], gather_div=k, rows=S,
                                            out_dtype=torch.bfloat16, **common)
             mark(3)
             paths["up"] = ops.last_dispatch()
             mark(4)
-            y = ops.moe_grouped_gemm_nvfp4(ops.W4A16, ops.EPI_NONE, h, w.w2_packed, w.w2_scales, w.w2_g,
+            y = ops.moe_grouped_gemm_nvfp4(ops.W4A16, ops.EPI_NONE, h, w.w2_t,
                                            rows=S, out_dtype=torch.float32, **common)
         else:
             xq, xs, xg = ops.nvfp4_quantize(xx)
             mark(2)
-            h, amax = ops.moe_grouped_gemm_nvfp4(ops.W4A4, ops.EPI_SWIGLU, xq, w.w13_packed, w.w13_scales,
-                                                 w.w13_g, a_scales=xs, a_g=xg, gather_index=rr["sorted_slot"],
+            h, amax = ops.moe_grouped_gemm_nvfp4(ops.W4A4, ops.EPI_SWIGLU, xq, w.w13_t,
+                                                 a_scales=xs, a_g=xg, gather_index=rr["sorted_slot"],
                                                  gather_div=k, rows=S, out_dtype=torch.float32,
                                                  want_amax=True, **common)
             mark(3)
             paths["up"] = ops.last_dispatch()
             hq, hs, hg = ops.nvfp4_quantize(h, amax=amax)
             mark(4)
-            y = ops.moe_grouped_gemm_nvfp4(ops.W4A4, ops.EPI_NONE, hq, w.w2_packed, w.w2_scales, w.w2_g,
+            y = ops.moe_grouped_gemm_nvfp4(ops.W4A4, ops.EPI_NONE, hq, w.w2_t,
                                            a_scales=hs, a_g=hg, rows=S, out_dtype=torch.float32, **common)
         mark(5)
         out = ops.moe_unpermute_reduce(y, rr["slot_to_row"], rr["topk_w"])
@@ -274,7 +274,7 @@ def dense_line(torch, ops, inputs, wl, args, M):
     quantized to NVFP4 before the timed region (the pages compare the GEMMs alone)."""
     dev = "cuda"
     N, K = wl.F, wl.H
-    wq, ws_, wg = ops.nvfp4_quantize(inputs.expert_weight_fp32(wl, "dense", 0, dev).unsqueeze(0))
+    wt = ops.nvfp4_weights_tile(*ops.nvfp4_quantize(inputs.expert_weight_fp32(wl, "dense", 0, dev).unsqueeze(0)))
     a = inputs.activations_bf16(wl, M).to(dev)
     aq, as_, ag = ops.nvfp4_quantize(a)
     one = torch.tensor([0, M], dtype=torch.int32, device=dev)
@@ -297,9 +297,9 @@ def dense_line(torch, ops, inputs, wl, args, M):
         return e0.elapsed_time(e1) * 1e3 / args.steps      # us per call
 
     common = dict(expert_offsets=one, active_experts=act, n_active=na, out_dtype=torch.bfloat16)
-    t16 = timed(lambda: ops.moe_grouped_gemm_nvfp4(ops.W4A16, ops.EPI_NONE, a, wq, ws_, wg, **common))
+    t16 = timed(lambda: ops.moe_grouped_gemm_nvfp4(ops.W4A16, ops.EPI_NONE, a, wt, **common))
     path16 = ops.last_dispatch()
-    t4 = timed(lambda: ops.moe_grouped_gemm_nvfp4(ops.W4A4, ops.EPI_NONE, aq, wq, ws_, wg, a_scales=as_,
+    t4 = timed(lambda: ops.moe_grouped_gemm_nvfp4(ops.W4A4, ops.EPI_NONE, aq, wt, a_scales=as_,
                                                   a_g=ag, **common))
     tmm = timed(lambda: torch.mm(a, wbf.t()))
     tf = lambda us: flops / (us * 1e-6) / 1e12

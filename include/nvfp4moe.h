@@ -116,6 +116,36 @@ nvfp4moe_status nvfp4_quantize(const void* x, nvfp4moe_dtype x_dtype, int64_t B,
 size_t nvfp4_quantize_workspace_size(int64_t B, int64_t R, int64_t C);
 
 /* ---------------------------------------------------------------------------
+ * nvfp4_weights_tile -- reorder NVFP4 weight matrices (the row-major storage above) into
+ * the tiled storage that moe_grouped_gemm_nvfp4 reads. A pure permutation of the bytes
+ * plus zero padding (no value changes); run once per weight set, like the quantization.
+ * The format is the pages' ([P2] "The NVFP4 Pivot"); only the byte order differs.
+ *
+ *   packed, scales  device uint8 [B, R, C/2] and [B, R, C/16] as written by nvfp4_quantize;
+ *                   packed 16-byte aligned, scales 2-byte aligned.
+ *   B, R, C         1 <= B <= 65535, R >= 16, R % 16 == 0, C >= 32, C % 32 == 0,
+ *                   B * R * C / 2 < 2^40.
+ *   tiled_codes     device uint8 [B * nvfp4_tiled_codes_bytes(R, C)]  (output), 16-byte aligned
+ *   tiled_scales    device uint8 [B * nvfp4_tiled_scales_bytes(R, C)] (output), 16-byte aligned
+ *
+ * Layout, with rb = row / 16, r = row % 16, nch = ceil(C / 128), nwin = ceil(C / 1024):
+ *   codes : 1 KB tile per (matrix b, rb, chunk c) at ((b * R/16 + rb) * nch + c) * 1024;
+ *           bytes 16 (16 g + r) .. +15 of the tile are the codes of columns
+ *           128 c + 32 g .. +31 of the row (g = 0..3), zero past C.
+ *   scales: 1 KB tile per (matrix b, rb, window w) at ((b * R/16 + rb) * nwin + w) * 1024;
+ *           bytes 16 (16 g + r) + 2 u and + 2 u + 1 are the scales of columns
+ *           128 (8 w + u) + 32 g + {0..15} and {16..31} of the row (u = 0..7), zero past C.
+ * (One GPU wave then reads a 16-row x 128-column block of codes, in the lane order of the
+ * matrix-core operand, as 1 KB of contiguous memory.)
+ * ------------------------------------------------------------------------- */
+nvfp4moe_status nvfp4_weights_tile(const uint8_t* packed, const uint8_t* scales, int64_t B, int64_t R,
+                                   int64_t C, uint8_t* tiled_codes, uint8_t* tiled_scales, void* stream);
+/* Bytes of one tiled [R, C] matrix: (R/16) * ceil(C/128) * 1024 codes, (R/16) * ceil(C/1024) *
+ * 1024 scales; 0 if R or C violate the constraints above. */
+size_t nvfp4_tiled_codes_bytes(int64_t R, int64_t C);
+size_t nvfp4_tiled_scales_bytes(int64_t R, int64_t C);
+
+/* ---------------------------------------------------------------------------
  * moe_route_permute -- router + histogram + stable permutation.
  * [P3] "The Investigation So Far" (top-8 of 256), [P1] section 1 (top-22 of 512),
  * [P3] "Discovering the sgl_kernel Alternative" (expert scatter/gather).
@@ -158,14 +188,17 @@ size_t moe_route_permute_workspace_size(int32_t T, int32_t E, int32_t k);
  *               NULL: GEMM row r reads a row r (a_rows must equal rows).
  *               else: GEMM row r reads a row gather_index[r] / gather_div, e.g.
  *                     sorted_slot with gather_div = k to gather token rows.
- *   w_packed    device uint8 [E, Nw, K/2]; w_scales uint8 [E, Nw, K/16]; w_g float [E].
+ *   w_packed, w_scales
+ *               device, the E expert matrices [Nw, K] in the tiled storage written by
+ *               nvfp4_weights_tile (expert e at e * nvfp4_tiled_codes_bytes(Nw, K) and
+ *               e * nvfp4_tiled_scales_bytes(Nw, K)); w_g float [E].
  *   expert_offsets, active_experts, n_active  as written by moe_route_permute (for a
  *               dense GEMM: E = 1, offsets {0, rows}, active {0}, n_active {1}).
  *   E, rows, Nw, K  1 <= E <= 1024; rows = expert_offsets[E] >= 1; Nw >= 32, Nw % 32 == 0
  *               (EPI_SWIGLU: gate rows 0..Nw/2-1, up rows Nw/2..Nw-1); K >= 32, K % 32 == 0;
- *               rows * max(K, Nw) < 2^31, a_rows * K * 2 < 2^31, Nw * K / 2 < 2^31.
- *               a and w_packed 16-byte aligned, scale arrays
- *               2-byte aligned.
+ *               rows * max(K, Nw) < 2^31, a_rows * K * 2 < 2^31, Nw * K / 2 < 2^31
+ *               (K rounded up to a multiple of 128 in the last two).
+ *               a, w_packed and w_scales 16-byte aligned, a_scales 2-byte aligned.
  *   out         device, out_dtype (F32 or BF16), [rows, EPI_SWIGLU ? Nw/2 : Nw].
  *   out_amax    device float[1] or NULL: if given, set to max |out| over the call (exact;
  *               used to pick the global scale when out is quantized next).

@@ -109,7 +109,7 @@ extern "C" {
 
 const char* nvfp4moe_last_error(void) { return g_last_error.c_str(); }
 int nvfp4moe_last_dispatch(void) { return g_last_dispatch; }
-int nvfp4moe_abi_version(void) { return 100; }
+int nvfp4moe_abi_version(void) { return 200; }
 
 // ------------------------------------------------------------------ quantize
 size_t nvfp4_quantize_workspace_size(int64_t B, int64_t R, int64_t C) {
@@ -175,6 +175,35 @@ nvfp4moe_status moe_route_permute(const float* logits, int32_t T, int32_t E, int
                     "moe_route_permute");
 }
 
+// ------------------------------------------------------------------ weight tiling
+size_t nvfp4_tiled_codes_bytes(int64_t R, int64_t C) {
+  if (R < 16 || R % 16 != 0 || C < 32 || C % 32 != 0) return 0;
+  return tiled_codes_bytes(R, C);
+}
+size_t nvfp4_tiled_scales_bytes(int64_t R, int64_t C) {
+  if (R < 16 || R % 16 != 0 || C < 32 || C % 32 != 0) return 0;
+  return tiled_scales_bytes(R, C);
+}
+
+nvfp4moe_status nvfp4_weights_tile(const uint8_t* packed, const uint8_t* scales, int64_t B, int64_t R,
+                                   int64_t C, uint8_t* tiled_codes, uint8_t* tiled_scales, void* stream) {
+  const char* fn = "nvfp4_weights_tile";
+  if (!packed || !scales || !tiled_codes || !tiled_scales)
+    return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: null tensor pointer", fn);
+  if (B < 1 || B > 65535 || R < 16 || R % 16 != 0 || C < 32 || C % 32 != 0)
+    return fail(NVFP4MOE_ERR_INVALID_ARG,
+                "%s: need 1 <= B <= 65535, R >= 16, R %% 16 == 0, C >= 32, C %% 32 == 0 (B=%lld R=%lld C=%lld)",
+                fn, (long long)B, (long long)R, (long long)C);
+  if (B * R * (C / 2) >= (int64_t(1) << 40) || R > (int64_t(1) << 30) || C > (int64_t(1) << 30))
+    return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: matrices too large", fn);
+  if (!aligned(packed, 16) || !aligned(scales, 2) || !aligned(tiled_codes, 16) || !aligned(tiled_scales, 16))
+    return fail(NVFP4MOE_ERR_INVALID_ARG,
+                "%s: packed and the tiled outputs must be 16-byte aligned, scales 2-byte aligned", fn);
+  return hip_status(launch_weights_tile(packed, scales, B, R, C, tiled_codes, tiled_scales,
+                                        static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
 // ------------------------------------------------------------------ grouped GEMM
 size_t moe_grouped_gemm_workspace_size(nvfp4moe_mode mode, int64_t a_rows, int32_t rows,
                                        int32_t E, int32_t Nw, int32_t K) {
@@ -215,16 +244,16 @@ nvfp4moe_status moe_grouped_gemm_nvfp4(nvfp4moe_mode mode, nvfp4moe_epilogue epi
     return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: rows * max(K, Nw) must be < 2^31", fn);
   if (a_rows * (int64_t)((K + 127) / 128 * 128) * 2 >= (int64_t(1) << 31))
     return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: a_rows * K * 2 must be < 2^31", fn);
-  if ((int64_t)Nw * (K / 2) >= (int64_t(1) << 31))
+  if ((int64_t)Nw * ((K + 127) / 128 * 64) >= (int64_t(1) << 31))
     return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: Nw * K / 2 must be < 2^31", fn);
   if (!gather_index && a_rows != rows)
     return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: without gather_index a_rows must equal rows", fn);
   if (gather_index && gather_div < 1)
     return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: gather_div must be >= 1", fn);
-  if (!aligned(a, 16) || !aligned(w_packed, 16) || !aligned(w_scales, 2) ||
+  if (!aligned(a, 16) || !aligned(w_packed, 16) || !aligned(w_scales, 16) ||
       (a_scales && !aligned(a_scales, 2)) || !aligned(out, out_dtype == NVFP4MOE_F32 ? 4 : 2))
     return fail(NVFP4MOE_ERR_INVALID_ARG,
-                "%s: a and w_packed must be 16-byte aligned, scale arrays 2-byte aligned", fn);
+                "%s: a and the tiled weights must be 16-byte aligned, a_scales 2-byte aligned", fn);
   const int path = gemm_path(rows, E, Nw);
   if (path == NVFP4MOE_PATH_NONE)
     return fail(NVFP4MOE_ERR_UNSUPPORTED, "%s: the forced MFMA path needs Nw %% 256 == 0 (Nw=%d)", fn, Nw);

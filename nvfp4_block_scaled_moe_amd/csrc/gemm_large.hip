@@ -36,13 +36,14 @@ namespace {
 constexpr int kTBM = 8;                    // 16-row blocks per m-tile
 constexpr int kRBW = 2;                    // 16-row weight blocks per wave
 constexpr int kSlots = 3;                  // LDS ring slots
+constexpr int kWin = 8;                    // chunks per scale tile
 constexpr int kTokBytes = 256;             // f16 activations of one row and chunk
 constexpr int kSlot = 16 * kTBM * kTokBytes;
 
 template <int WAVES, int WDEPTH, bool SWIGLU>
 __global__ __launch_bounds__(WAVES* kWave, 2) void gemm_large_kernel(const GemmArgs p, int ntiles_n,
                                                                      int total_tiles) {
-  static_assert(WDEPTH >= 2 && WDEPTH % 2 == 0, "the weight ring is read one chunk ahead; steps pair up");
+  static_assert(WDEPTH >= 2 && kWin % WDEPTH == 0, "the weight ring is read one chunk ahead; steps pair up");
   constexpr int NT = WAVES * kWave;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
 
@@ -58,26 +59,31 @@ __global__ __launch_bounds__(WAVES* kWave, 2) void gemm_large_kernel(const GemmA
   const int e = p.sched_e[mt], tc = p.sched_r[mt];
   const int r0 = p.expert_offsets[e];
   const int M = p.expert_offsets[e + 1] - r0;
-  const int K = p.K, Nw = p.Nw, Kh = K >> 1, Ks = K >> 4;
+  const int K = p.K, Nw = p.Nw;
   const int K128 = (K + 127) & ~127;
   const int F = Nw >> 1;
   const int nch = (K + kChunk - 1) / kChunk;
+  const int nwin = (nch + kWin - 1) / kWin;
   const int ntb = __builtin_amdgcn_readfirstlane(min(kTBM, (M - tc + 15) >> 4));
 
   auto blkrow = [&](int b) -> int {
     if (SWIGLU) return (b == 0 ? 0 : F) + (nb * WAVES + wave) * 16;
     return (nb * WAVES + wave) * 16 * kRBW + 16 * b;
   };
-  const __amdgpu_buffer_rsrc_t wr = make_rsrc(p.w_packed + (size_t)e * Nw * Kh, (uint32_t)Nw * (uint32_t)Kh);
-  const __amdgpu_buffer_rsrc_t sr = make_rsrc(p.w_scales + (size_t)e * Nw * Ks, (uint32_t)Nw * (uint32_t)Ks);
+  // Tiled weights (weights_tile.hip): lane l reads 16 bytes at 16 l of a 1 KB tile per
+  // (16-row block, chunk) of codes and per (16-row block, 8-chunk window) of scales.
+  const uint32_t wbytes = (uint32_t)(Nw / 16) * (uint32_t)nch * 1024u;
+  const uint32_t sbytes = (uint32_t)(Nw / 16) * (uint32_t)nwin * 1024u;
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(p.w_packed + (size_t)e * wbytes, wbytes);
+  const __amdgpu_buffer_rsrc_t sr = make_rsrc(p.w_scales + (size_t)e * sbytes, sbytes);
   const __amdgpu_buffer_rsrc_t ar = make_rsrc(p.a16, (uint32_t)p.a_rows * (uint32_t)K128 * 2u);
-  const uint32_t wlane = (uint32_t)(blkrow(0) + l16) * Kh + 16 * g;
-  const uint32_t slane = (uint32_t)(blkrow(0) + l16) * Ks + 2 * g;
+  const uint32_t wlane = (uint32_t)(blkrow(0) / 16) * (uint32_t)nch * 1024u + 16u * lane;
+  const uint32_t slane = (uint32_t)(blkrow(0) / 16) * (uint32_t)nwin * 1024u + 16u * lane;
   uint32_t wsoff[kRBW], ssoff[kRBW];
 #pragma unroll
   for (int b = 0; b < kRBW; ++b) {
-    wsoff[b] = __builtin_amdgcn_readfirstlane((uint32_t)(blkrow(b) - blkrow(0)) * Kh);
-    ssoff[b] = __builtin_amdgcn_readfirstlane((uint32_t)(blkrow(b) - blkrow(0)) * Ks);
+    wsoff[b] = __builtin_amdgcn_readfirstlane((uint32_t)((blkrow(b) - blkrow(0)) / 16) * (uint32_t)nch * 1024u);
+    ssoff[b] = __builtin_amdgcn_readfirstlane((uint32_t)((blkrow(b) - blkrow(0)) / 16) * (uint32_t)nwin * 1024u);
   }
   const float alpha = p.w4a4 ? p.w_g[e] * p.a_g[0] : p.w_g[e];
 
@@ -118,20 +124,25 @@ __global__ __launch_bounds__(WAVES* kWave, 2) void gemm_large_kernel(const GemmA
       }
     };
     u32x4 wring[WDEPTH][kRBW];
-    uint16_t sring[WDEPTH][kRBW];   // kept 16-bit: widening at load time would wait for the load
-    auto w_issue = [&](int d, int c) {
-      const bool kin = c < nch && (c * kChunk + 32 * g) < K;
+    auto w_issue = [&](int d, int c) {   // codes past K are zero in the tiles
 #pragma unroll
-      for (int b = 0; b < kRBW; ++b) {
-        wring[d][b] = ld128(wr, kin ? wlane + (uint32_t)c * 64u : kOOB, wsoff[b]);
-        sring[d][b] = __builtin_amdgcn_raw_buffer_load_b16(sr, kin ? slane + (uint32_t)c * 8u : kOOB, ssoff[b], 0);
-      }
+      for (int b = 0; b < kRBW; ++b) wring[d][b] = ld128(wr, c < nch ? wlane + (uint32_t)c * 1024u : kOOB, wsoff[b]);
+    };
+    // One 16-byte load per block and window holds the lane's two scale bytes for each of
+    // the window's 8 chunks; the current and the next window stay in registers.
+    u32x4 scur[kRBW], snext[kRBW];
+    auto s_issue = [&](int w) {
+#pragma unroll
+      for (int b = 0; b < kRBW; ++b) snext[b] = ld128(sr, w < nwin ? slane + (uint32_t)w * 1024u : kOOB, ssoff[b]);
     };
     f16x8 wf[kRBW][4], wfn[kRBW][4];   // decoded weights of chunks c and c+1
     f16x2 sc[kRBW][2];
-    auto scales = [&](int d) {
+    auto scales = [&](int u) {   // chunk u of the current window, u = 8: first of the next
 #pragma unroll
-      for (int b = 0; b < kRBW; ++b) decode_scale_pair(sring[d][b], sc[b][0], sc[b][1]);
+      for (int b = 0; b < kRBW; ++b) {
+        const uint32_t two = u < kWin ? scur[b][u >> 1] >> (16 * (u & 1)) : snext[b][0];
+        decode_scale_pair(two, sc[b][0], sc[b][1]);
+      }
     };
     auto decode = [&](f16x8 (&dst)[kRBW][4], int d, int j) {
 #pragma unroll
@@ -146,6 +157,7 @@ __global__ __launch_bounds__(WAVES* kWave, 2) void gemm_large_kernel(const GemmA
 
     // prologue: activations of chunks 0 and 1 into slots 0 and 1 (chunk 2 requested),
     // weights of chunks 0..WDEPTH-1 requested, chunk 0 decoded
+    s_issue(0);
     b_issue(0, 0);
 #pragma unroll
     for (int d = 0; d < WDEPTH; ++d) w_issue(d, d);
@@ -153,6 +165,8 @@ __global__ __launch_bounds__(WAVES* kWave, 2) void gemm_large_kernel(const GemmA
     b_issue(1, 1);
     b_commit(1, 1);
     b_issue(2, 0);
+#pragma unroll
+    for (int b = 0; b < kRBW; ++b) scur[b] = snext[b];
     scales(0);
 #pragma unroll
     for (int j = 0; j < 4; ++j) decode(wf, 0, j);
@@ -166,17 +180,18 @@ __global__ __launch_bounds__(WAVES* kWave, 2) void gemm_large_kernel(const GemmA
     // and those of chunk c+3 are requested. Vector-memory counters retire in order, so the
     // store waits only on requests at least one step old.
     int slot = 0;
-    for (int c0 = 0; c0 < nch; c0 += WDEPTH) {
+    for (int c0 = 0; c0 < nch; c0 += kWin) {       // one scale window per iteration
+      s_issue(c0 / kWin + 1);
 #pragma unroll
-      for (int u = 0; u < WDEPTH; ++u) {
+      for (int u = 0; u < kWin; ++u) {
         const int c = c0 + u;
         if (c < nch) {
-          const int dn = (u + 1) % WDEPTH;
+          const int d = u % WDEPTH, dn = (u + 1) % WDEPTH;
           const int slot1 = slot == kSlots - 1 ? 0 : slot + 1;
           const int slot2 = slot1 == kSlots - 1 ? 0 : slot1 + 1;
           b_issue(c + 3, (u + 1) & 1);             // c0 is even: chunk x uses set x % 2
-          w_issue(u, c + WDEPTH);                  // ring entry u (chunk c) was decoded last step
-          scales(dn);
+          w_issue(d, c + WDEPTH);                  // ring entry d (chunk c) was decoded last step
+          scales(u + 1);
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
             if (j < 3) b_read(bnext, slot, j + 1);
@@ -195,6 +210,10 @@ __global__ __launch_bounds__(WAVES* kWave, 2) void gemm_large_kernel(const GemmA
           for (int b = 0; b < kRBW; ++b)
 #pragma unroll
             for (int j = 0; j < 4; ++j) wf[b][j] = wfn[b][j];
+          if (u == kWin - 1) {
+#pragma unroll
+            for (int b = 0; b < kRBW; ++b) scur[b] = snext[b];
+          }
           __syncthreads();
           slot = slot1;
         }
@@ -267,13 +286,11 @@ hipError_t launch_cfg(const GemmArgs& a, int max_mtiles, hipStream_t stream) {
   return hipGetLastError();
 }
 
-// NVFP4MOE_LARGE_DEPTH=2|4 selects the weight ring depth (tuning).
+// Weight ring depth 2: the chunk after next is in flight while a chunk is decoded (a deeper
+// ring does not fit the 256 registers a wave has at two waves per SIMD).
 template <bool SWIGLU>
 hipError_t launch_sw(const GemmArgs& a, int max_mtiles, hipStream_t stream) {
-  int depth = 4;
-  if (const char* s = std::getenv("NVFP4MOE_LARGE_DEPTH")) depth = std::atoi(s);
-  if (depth == 2) return launch_cfg<8, 2, SWIGLU>(a, max_mtiles, stream);
-  return launch_cfg<8, 4, SWIGLU>(a, max_mtiles, stream);
+  return launch_cfg<8, 2, SWIGLU>(a, max_mtiles, stream);
 }
 
 }  // namespace

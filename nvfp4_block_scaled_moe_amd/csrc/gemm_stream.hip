@@ -43,9 +43,8 @@ namespace nvfp4moe {
 
 namespace {
 
-constexpr int kWin = 8;                  // chunks per scale window (1024 k)
+constexpr int kWin = 8;                  // chunks per scale tile (1024 k)
 constexpr int kDepth = 4;                // weight chunks in flight per wave
-constexpr int kSPitch = 80;              // LDS pitch of a 64-byte scale row (bank spread)
 constexpr uint32_t kNoDst = 0xffffffffu;
 
 template <int TBM, bool A4>
@@ -86,7 +85,6 @@ __global__ __launch_bounds__(WAVES* kWave) void gemm_stream_kernel(const GemmArg
   const int nwin = (nch + kWin - 1) / kWin;
 
   unsigned char* ring = smem;                                           // [2][R::kSlot]
-  unsigned char* sws = smem + R::kBytes + wave * (2 * RBW * 16 * kSPitch);  // wave's scales
 
   // First row of this wave's block b (the lane adds l16).
   auto blkrow = [&](int b) -> int {
@@ -97,17 +95,19 @@ __global__ __launch_bounds__(WAVES* kWave) void gemm_stream_kernel(const GemmArg
     }
     return (nb * WAVES + wave) * 16 * RBW + 16 * b;
   };
-  const __amdgpu_buffer_rsrc_t wr =
-      make_rsrc(p.w_packed + (size_t)e * Nw * Kh, (uint32_t)Nw * (uint32_t)Kh);
-  const __amdgpu_buffer_rsrc_t sr =
-      make_rsrc(p.w_scales + (size_t)e * Nw * Ks, (uint32_t)Nw * (uint32_t)Ks);
-  const uint32_t wlane = (uint32_t)(blkrow(0) + l16) * Kh + 16 * g;
-  const uint32_t slane = (uint32_t)(blkrow(0) + l16) * Ks + 16 * g;
+  // Tiled weights: 1 KB per (16-row block, chunk) of codes and per (16-row block, window)
+  // of scales; lane l reads the 16 bytes at 16 l of a tile.
+  const uint32_t wbytes = (uint32_t)(Nw / 16) * (uint32_t)nch * 1024u;
+  const uint32_t sbytes = (uint32_t)(Nw / 16) * (uint32_t)nwin * 1024u;
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(p.w_packed + (size_t)e * wbytes, wbytes);
+  const __amdgpu_buffer_rsrc_t sr = make_rsrc(p.w_scales + (size_t)e * sbytes, sbytes);
+  const uint32_t wlane = (uint32_t)(blkrow(0) / 16) * (uint32_t)nch * 1024u + 16u * lane;
+  const uint32_t slane = (uint32_t)(blkrow(0) / 16) * (uint32_t)nwin * 1024u + 16u * lane;
   uint32_t wsoff[RBW], ssoff[RBW];
 #pragma unroll
   for (int b = 0; b < RBW; ++b) {
-    wsoff[b] = __builtin_amdgcn_readfirstlane((uint32_t)(blkrow(b) - blkrow(0)) * Kh);
-    ssoff[b] = __builtin_amdgcn_readfirstlane((uint32_t)(blkrow(b) - blkrow(0)) * Ks);
+    wsoff[b] = __builtin_amdgcn_readfirstlane((uint32_t)((blkrow(b) - blkrow(0)) / 16) * (uint32_t)nch * 1024u);
+    ssoff[b] = __builtin_amdgcn_readfirstlane((uint32_t)((blkrow(b) - blkrow(0)) / 16) * (uint32_t)nwin * 1024u);
   }
   const float alpha = A4 ? p.w_g[e] * p.a_g[0] : p.w_g[e];
 
@@ -204,45 +204,27 @@ __global__ __launch_bounds__(WAVES* kWave) void gemm_stream_kernel(const GemmArg
               *reinterpret_cast<uint2*>(base + bsdst[rr]) = make_uint2(bsc[set][rr][0], bsc[set][rr][1]);
         }
       };
-      u32x4 sst[RBW];
+      // Scales: one 16-byte load per block and window holds the lane's two scale bytes for
+      // each of the window's 8 chunks; the current and the next window stay in registers.
+      u32x4 scur[RBW], snext[RBW];
       auto s_issue = [&](int w) {
-        const bool win = w < nwin && (w * kWin * kChunk + 256 * g) < K;
-        const uint32_t so = win ? slane + (uint32_t)(w * kWin * kChunk) / 16 : kOOB;
-        if ((Ks & 3) == 0) {   // dword-aligned scale rows: one 16-byte load per block
 #pragma unroll
-          for (int b = 0; b < RBW; ++b) sst[b] = ld128(sr, so, ssoff[b]);
-        } else {               // K % 64 != 0: rows are only 2-byte aligned
-#pragma unroll
-          for (int b = 0; b < RBW; ++b)
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-              sst[b][q] = ld16(sr, so, ssoff[b] + 4 * q) | (ld16(sr, so, ssoff[b] + 4 * q + 2) << 16);
-        }
-      };
-      auto s_commit = [&](int w) {
-        unsigned char* base = sws + (w & 1) * (RBW * 16 * kSPitch);
-#pragma unroll
-        for (int b = 0; b < RBW; ++b)
-          *reinterpret_cast<u32x4*>(base + (16 * b + l16) * kSPitch + 16 * g) = sst[b];
+        for (int b = 0; b < RBW; ++b) snext[b] = ld128(sr, w < nwin ? slane + (uint32_t)w * 1024u : kOOB, ssoff[b]);
       };
       u32x4 wring[WDEPTH][RBW];
-      auto w_issue = [&](int d, int c, int b) {
-        const bool kin = c < nch && (c * kChunk + 32 * g) < K;
-        wring[d][b] = ld128(wr, kin ? wlane + (uint32_t)(c * kChunk) / 2 : kOOB, wsoff[b]);
+      auto w_issue = [&](int d, int c, int b) {   // codes past K are zero in the tiles
+        wring[d][b] = ld128(wr, c < nch ? wlane + (uint32_t)c * 1024u : kOOB, wsoff[b]);
       };
-      auto compute = [&](int d, int c) {
+      auto compute = [&](int d, int c, int u) {    // u = c % kWin, a constant
         u32x4 (&wv)[RBW] = wring[d];
         const unsigned char* base = ring + (c & 1) * R::kSlot;
-        const unsigned char* sbase = sws + ((c / kWin) & 1) * (RBW * 16 * kSPitch);
-        const int soff = (c % kWin) * 8 + 2 * g;
-        const bool sin = (c * kChunk + 32 * g) < K;   // past K: weights read zero, so must scales
         // Decode every block of the chunk (each ring entry is re-filled right after its
         // decode), then issue the MFMAs k-step-major so that consecutive MFMAs update
         // different accumulators and the activation fragments are read once per k-step.
         f16x8 wf[RBW][4];
 #pragma unroll
         for (int b = 0; b < RBW; ++b) {
-          const uint32_t sv = sin ? *reinterpret_cast<const uint16_t*>(sbase + (16 * b + l16) * kSPitch + soff) : 0u;
+          const uint32_t sv = scur[b][u >> 1] >> (16 * (u & 1));   // scales of k past K are 0
           f16x2 s0, s1;
           decode_scale_pair(sv, s0, s1);
           wf[b][0] = decode8(wv[b][0], s0);
@@ -281,6 +263,8 @@ __global__ __launch_bounds__(WAVES* kWave) void gemm_stream_kernel(const GemmArg
       // prologue: scales of window 0, then activations and weights of the first chunks
       s_issue(0);
 #pragma unroll
+      for (int b = 0; b < RBW; ++b) scur[b] = snext[b];
+#pragma unroll
       for (int d = 0; d < (WDEPTH > BDEPTH ? WDEPTH : BDEPTH); ++d) {
         if (d < BDEPTH) b_issue(d, d);
         if (d < WDEPTH) {
@@ -288,7 +272,6 @@ __global__ __launch_bounds__(WAVES* kWave) void gemm_stream_kernel(const GemmArg
           for (int b = 0; b < RBW; ++b) w_issue(d, d, b);
         }
       }
-      s_commit(0);
       b_commit(0, 0);
       __syncthreads();
       // Chunk c: LDS slot c&1, staging set c % BDEPTH and weight ring entry c % WDEPTH.
@@ -298,9 +281,12 @@ __global__ __launch_bounds__(WAVES* kWave) void gemm_stream_kernel(const GemmArg
         for (int u = 0; u < kWin; ++u) {
           const int c = c0 + u;
           b_issue(u % BDEPTH, c + BDEPTH);         // set u%BDEPTH was committed last step
-          compute(u % WDEPTH, c);                  // requests weights of chunk c+WDEPTH
+          compute(u % WDEPTH, c, u);               // requests weights of chunk c+WDEPTH
           b_commit((u + 1) % BDEPTH, (c + 1) & 1);
-          if (u == kWin - 1) s_commit(c0 / kWin + 1);
+          if (u == kWin - 1) {
+#pragma unroll
+            for (int b = 0; b < RBW; ++b) scur[b] = snext[b];
+          }
           __syncthreads();
         }
       }
@@ -323,7 +309,7 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
   const int max_active = a.E < a.rows ? a.E : a.rows;
   const int total = max_active * tiles_per_expert;
   const int grid = (total + 7) / 8 * 8;
-  const size_t shmem = (size_t)Ring<TBM, A4>::kBytes + (size_t)WAVES * 2 * RBW * 16 * kSPitch;
+  const size_t shmem = (size_t)Ring<TBM, A4>::kBytes;
   gemm_stream_kernel<RBW, WAVES, TBM, kDepth, kDepth, SWIGLU, A4>
       <<<grid, WAVES * kWave, shmem, stream>>>(a, tiles_per_expert, total);
   return hipGetLastError();

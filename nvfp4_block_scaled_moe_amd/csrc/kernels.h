@@ -42,8 +42,8 @@ struct GemmArgs {
   const float* a_g;                // [1]
   const int* gather_index;         // [rows] or null
   int gather_div;
-  const uint8_t* w_packed;         // [E, Nw, K/2]
-  const uint8_t* w_scales;         // [E, Nw, K/16]
+  const uint8_t* w_packed;         // tiled codes, tiled_codes_bytes(Nw, K) per expert
+  const uint8_t* w_scales;         // tiled scales, tiled_scales_bytes(Nw, K) per expert
   const float* w_g;                // [E]
   const int* expert_offsets;       // [E+1]
   const int* active;               // [E]
@@ -59,6 +59,11 @@ struct GemmArgs {
   const int* sched_n;              // large-M path: number of m-tiles  (workspace)
 };
 hipError_t launch_gemm_stream(const GemmArgs& a, hipStream_t stream);
+// Tiled weight storage (weights_tile.hip): bytes per [R, C] matrix and the reordering.
+size_t tiled_codes_bytes(int64_t R, int64_t C);
+size_t tiled_scales_bytes(int64_t R, int64_t C);
+hipError_t launch_weights_tile(const uint8_t* packed, const uint8_t* scales, int64_t B, int64_t R, int64_t C,
+                               uint8_t* tiled_codes, uint8_t* tiled_scales, hipStream_t stream);
 // large-M path: rows per m-tile, the Nw it supports, and the launcher (max_mtiles is the host
 // bound ceil(rows / rows_per_mtile) + min(E, rows) on the schedule length).
 int large_rows_per_mtile();

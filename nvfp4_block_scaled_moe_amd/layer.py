@@ -14,13 +14,16 @@ from . import inputs, ops
 
 @dataclass
 class NVFP4Experts:
-    """NVFP4 expert weights: W13_e = [2F, H] (gate rows first), W2_e = [H, F]."""
+    """NVFP4 expert weights: W13_e = [2F, H] (gate rows first), W2_e = [H, F], in the pages'
+    row-major storage and, for the GEMMs, in the library's tiled storage."""
     w13_packed: torch.Tensor   # uint8 [E, 2F, H/2]
     w13_scales: torch.Tensor   # uint8 [E, 2F, H/16]
     w13_g: torch.Tensor        # f32 [E]
     w2_packed: torch.Tensor    # uint8 [E, H, F/2]
     w2_scales: torch.Tensor    # uint8 [E, H, F/16]
     w2_g: torch.Tensor         # f32 [E]
+    w13_t: ops.TiledWeights = None
+    w2_t: ops.TiledWeights = None
 
     @property
     def E(self):
@@ -35,7 +38,7 @@ class NVFP4Experts:
 
 def quantize_experts(wl: inputs.Workload, device="cuda", experts=None) -> NVFP4Experts:
     """Generate the workload's seeded FP32 expert weights one expert at a time on ``device``
-    and quantize each with the library's nvfp4_quantize."""
+    and quantize each with the library's nvfp4_quantize; then tile both weight sets."""
     E, H, F = wl.E, wl.H, wl.F
     experts = range(E) if experts is None else experts
     u8 = dict(dtype=torch.uint8, device=device)
@@ -49,6 +52,8 @@ def quantize_experts(wl: inputs.Workload, device="cuda", experts=None) -> NVFP4E
                            out=(w.w13_packed[e], w.w13_scales[e], w.w13_g[e:e + 1]))
         ops.nvfp4_quantize(inputs.expert_weight_fp32(wl, "w2", e, device),
                            out=(w.w2_packed[e], w.w2_scales[e], w.w2_g[e:e + 1]))
+    w.w13_t = ops.nvfp4_weights_tile(w.w13_packed, w.w13_scales, w.w13_g)
+    w.w2_t = ops.nvfp4_weights_tile(w.w2_packed, w.w2_scales, w.w2_g)
     return w
 
 
@@ -69,21 +74,21 @@ def moe_forward(x: torch.Tensor, logits: torch.Tensor, k: int, w: NVFP4Experts, 
     common = dict(expert_offsets=r["expert_offsets"], active_experts=r["active_experts"],
                   n_active=r["n_active"])
     if mode == ops.W4A16:
-        h = ops.moe_grouped_gemm_nvfp4(ops.W4A16, ops.EPI_SWIGLU, x, w.w13_packed, w.w13_scales, w.w13_g,
+        h = ops.moe_grouped_gemm_nvfp4(ops.W4A16, ops.EPI_SWIGLU, x, w.w13_t,
                                        gather_index=r["sorted_slot"], gather_div=k, rows=S,
                                        out_dtype=torch.bfloat16, **common)
-        y = ops.moe_grouped_gemm_nvfp4(ops.W4A16, ops.EPI_NONE, h, w.w2_packed, w.w2_scales, w.w2_g,
+        y = ops.moe_grouped_gemm_nvfp4(ops.W4A16, ops.EPI_NONE, h, w.w2_t,
                                        rows=S, out_dtype=torch.float32, **common)
     else:
         xq, xs, xg = ops.nvfp4_quantize(x)
         st.update(xq=xq, xs=xs, xg=xg)
-        h, amax = ops.moe_grouped_gemm_nvfp4(ops.W4A4, ops.EPI_SWIGLU, xq, w.w13_packed, w.w13_scales,
-                                             w.w13_g, a_scales=xs, a_g=xg, gather_index=r["sorted_slot"],
+        h, amax = ops.moe_grouped_gemm_nvfp4(ops.W4A4, ops.EPI_SWIGLU, xq, w.w13_t,
+                                             a_scales=xs, a_g=xg, gather_index=r["sorted_slot"],
                                              gather_div=k, rows=S, out_dtype=torch.float32,
                                              want_amax=True, **common)
         hq, hs, hg = ops.nvfp4_quantize(h, amax=amax)
         st.update(h_amax=amax, hq=hq, hs=hs, hg=hg)
-        y = ops.moe_grouped_gemm_nvfp4(ops.W4A4, ops.EPI_NONE, hq, w.w2_packed, w.w2_scales, w.w2_g,
+        y = ops.moe_grouped_gemm_nvfp4(ops.W4A4, ops.EPI_NONE, hq, w.w2_t,
                                        a_scales=hs, a_g=hg, rows=S, out_dtype=torch.float32, **common)
     out = ops.moe_unpermute_reduce(y, r["slot_to_row"], r["topk_w"])
     if keep:

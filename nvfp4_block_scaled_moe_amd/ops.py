@@ -8,6 +8,7 @@ computation runs in the library's HIP kernels; a failed call raises NVFP4MoEErro
 from __future__ import annotations
 
 import ctypes
+from dataclasses import dataclass
 
 import torch
 
@@ -68,6 +69,44 @@ def nvfp4_quantize(x: torch.Tensor, g: torch.Tensor | None = None, amax: torch.T
     return packed, scales, g_out
 
 
+@dataclass
+class TiledWeights:
+    """B NVFP4 matrices [R, C] in the tiled storage of nvfp4_weights_tile, with their
+    per-matrix global scales: what moe_grouped_gemm_nvfp4 takes as expert weights."""
+    codes: torch.Tensor    # uint8 [B, nvfp4_tiled_codes_bytes(R, C)]
+    scales: torch.Tensor   # uint8 [B, nvfp4_tiled_scales_bytes(R, C)]
+    g: torch.Tensor        # float32 [B]
+    R: int
+    C: int
+
+    @property
+    def B(self):
+        return self.codes.shape[0]
+
+
+def nvfp4_weights_tile(packed: torch.Tensor, scales: torch.Tensor, g: torch.Tensor) -> TiledWeights:
+    """Reorder NVFP4 weights packed [B, R, C/2] + scales [B, R, C/16] (or one [R, ...]
+    matrix) into the tiled storage the grouped GEMM reads; a byte permutation with zero
+    padding (include/nvfp4moe.h). ``g`` float32 [B] is carried along unchanged."""
+    _dev(packed, scales, g)
+    p3 = (packed.unsqueeze(0) if packed.dim() == 2 else packed).contiguous()
+    s3 = (scales.unsqueeze(0) if scales.dim() == 2 else scales).contiguous()
+    B, R, Ch = p3.shape
+    C = 2 * Ch
+    assert s3.shape == (B, R, C // 16), (s3.shape, p3.shape)
+    lib = _lib.load()
+    cb, sb = lib.nvfp4_tiled_codes_bytes(R, C), lib.nvfp4_tiled_scales_bytes(R, C)
+    if cb == 0 or sb == 0:
+        raise _lib.NVFP4MoEError("nvfp4_weights_tile", _lib.ERR_INVALID_ARG, f"unsupported shape R={R} C={C}")
+    codes = torch.empty((B, cb), dtype=torch.uint8, device=packed.device)
+    sc = torch.empty((B, sb), dtype=torch.uint8, device=packed.device)
+    st = lib.nvfp4_weights_tile(_ptr(p3), _ptr(s3), B, R, C, _ptr(codes), _ptr(sc), _stream())
+    _lib.check("nvfp4_weights_tile", st)
+    g = g.reshape(-1).float().contiguous()
+    assert g.numel() == B
+    return TiledWeights(codes, sc, g, R, C)
+
+
 def moe_route_permute(logits: torch.Tensor, k: int):
     """Router + permutation. Returns a dict of device tensors (see include/nvfp4moe.h)."""
     _dev(logits)
@@ -93,18 +132,17 @@ def moe_route_permute(logits: torch.Tensor, k: int):
     return out
 
 
-def moe_grouped_gemm_nvfp4(mode: int, epi: int, a: torch.Tensor, w_packed: torch.Tensor,
-                           w_scales: torch.Tensor, w_g: torch.Tensor, expert_offsets: torch.Tensor,
-                           active_experts: torch.Tensor, n_active: torch.Tensor, *,
+def moe_grouped_gemm_nvfp4(mode: int, epi: int, a: torch.Tensor, w: TiledWeights,
+                           expert_offsets: torch.Tensor, active_experts: torch.Tensor,
+                           n_active: torch.Tensor, *,
                            a_scales: torch.Tensor | None = None, a_g: torch.Tensor | None = None,
                            gather_index: torch.Tensor | None = None, gather_div: int = 1,
                            rows: int | None = None, out_dtype=torch.bfloat16,
                            want_amax: bool = False, out: torch.Tensor | None = None):
-    """Grouped NVFP4 GEMM (+ SwiGLU). ``w_packed`` [E, Nw, K/2]; ``a`` bf16 [a_rows, K]
-    (W4A16) or packed uint8 [a_rows, K/2] (W4A4). Returns out (and amax when asked)."""
-    _dev(a, w_packed, w_scales, w_g, expert_offsets, active_experts, n_active, a_scales, a_g, gather_index)
-    E, Nw, Kh = w_packed.shape
-    K = Kh * 2
+    """Grouped NVFP4 GEMM (+ SwiGLU). ``w``: E expert matrices [Nw, K] (tiled); ``a`` bf16
+    [a_rows, K] (W4A16) or packed uint8 [a_rows, K/2] (W4A4). Returns out (and amax)."""
+    _dev(a, w.codes, w.scales, w.g, expert_offsets, active_experts, n_active, a_scales, a_g, gather_index)
+    E, Nw, K = w.B, w.R, w.C
     a_rows = a.shape[0]
     if rows is None:
         rows = gather_index.numel() if gather_index is not None else a_rows
@@ -116,7 +154,7 @@ def moe_grouped_gemm_nvfp4(mode: int, epi: int, a: torch.Tensor, w_packed: torch
     ws = _ws(lib.moe_grouped_gemm_workspace_size(mode, a_rows, rows, E, Nw, K), a.device)
     st = lib.moe_grouped_gemm_nvfp4(
         mode, epi, _ptr(a), _ptr(a_scales), _ptr(a_g), a_rows, _ptr(gather_index), int(gather_div),
-        _ptr(w_packed), _ptr(w_scales), _ptr(w_g), _ptr(expert_offsets), _ptr(active_experts),
+        _ptr(w.codes), _ptr(w.scales), _ptr(w.g), _ptr(expert_offsets), _ptr(active_experts),
         _ptr(n_active), E, rows, Nw, K, _ptr(out), _DT[out.dtype], _ptr(amax), _ptr(ws), ws.numel(),
         _stream())
     _lib.check("moe_grouped_gemm_nvfp4", st)

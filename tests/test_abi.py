@@ -22,7 +22,8 @@ def declared_functions():
 def test_header_declares_the_calls():
     names = declared_functions()
     for want in ["nvfp4_quantize", "moe_route_permute", "moe_grouped_gemm_nvfp4",
-                 "moe_unpermute_reduce", "act_fp8_e4m3_roundtrip", "nvfp4moe_last_error"]:
+                 "moe_unpermute_reduce", "act_fp8_e4m3_roundtrip", "nvfp4moe_last_error",
+                 "nvfp4_weights_tile"]:
         assert want in names
 
 
@@ -32,7 +33,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(_lib.SIGNATURES), "binding signatures out of sync with the header"
     for n in names:
         assert hasattr(lib, n)
-    assert lib.nvfp4moe_abi_version() == 100
+    assert lib.nvfp4moe_abi_version() == 200
 
 
 FAKE = ctypes.c_void_p(1 << 20)      # aligned, never dereferenced: validation fails first
@@ -107,6 +108,23 @@ def test_grouped_gemm_workspace_follows_the_path(monkeypatch):
     assert st == _lib.ERR_UNSUPPORTED and "256" in msg
     monkeypatch.setenv("NVFP4MOE_FORCE_PATH", "stream")
     assert ws(_lib.W4A4, 8192, 8192, 64, 256, 256) == 0
+
+
+def test_weights_tile_sizes_and_argument_checks():
+    lib = _lib.load()
+    # closed forms: (R/16) * ceil(C/128) KB of codes, (R/16) * ceil(C/1024) KB of scales
+    assert lib.nvfp4_tiled_codes_bytes(4096, 7168) == 256 * 56 * 1024
+    assert lib.nvfp4_tiled_scales_bytes(4096, 7168) == 256 * 7 * 1024
+    assert lib.nvfp4_tiled_codes_bytes(16, 160) == 2 * 1024
+    assert lib.nvfp4_tiled_scales_bytes(48, 1056) == 3 * 2 * 1024
+    for R, C in [(8, 64), (24, 64), (16, 48), (16, 0)]:
+        assert lib.nvfp4_tiled_codes_bytes(R, C) == 0 and lib.nvfp4_tiled_scales_bytes(R, C) == 0
+    ok = (FAKE, FAKE, 1, 32, 64, FAKE, FAKE, None)
+    bad = [(None,) + ok[1:], ok[:2] + (0,) + ok[3:], ok[:3] + (24,) + ok[4:], ok[:4] + (48,) + ok[5:],
+           ok[:5] + (MISALIGNED,) + ok[6:], ok[:6] + (ctypes.c_void_p((1 << 20) + 2),) + ok[7:]]
+    for args in bad:
+        st, _ = _err(lib.nvfp4_weights_tile(*args))
+        assert st == _lib.ERR_INVALID_ARG, args
 
 
 def test_unpermute_reduce_and_fp8_reject_bad_arguments():

@@ -150,7 +150,8 @@ def test_dense_gemm_full_size(mode):
         kw.update(a_scales=as_, a_g=ag)
     else:
         a = x
-    out = ops.moe_grouped_gemm_nvfp4(mode, ops.EPI_NONE, a, wp, ws, wg, one([0, wl.T]), one([0]), one([1]), **kw)
+    wt = ops.nvfp4_weights_tile(wp, ws, wg)
+    out = ops.moe_grouped_gemm_nvfp4(mode, ops.EPI_NONE, a, wt, one([0, wl.T]), one([0]), one([1]), **kw)
     torch.cuda.synchronize()
     po, so, go = onv.quantize(wf.cpu().numpy())
     assert np.array_equal(np_(wp[0]), po) and np.array_equal(np_(ws[0]), so)

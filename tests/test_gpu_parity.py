@@ -73,6 +73,48 @@ def test_quantize_batched_static_and_amax_paths():
         assert np_(g2)[b] == np.float32(gs[b].item())
 
 
+# ------------------------------------------------------------------ weight tiling
+def _tile_reference(packed, scales):
+    """The tiled storage written out index by index from its definition (numpy, no kernel
+    code): codes tile (rb, c) lane 16g+r = codes of columns 128c+32g..+31 of row 16rb+r;
+    scales tile (rb, w) lane 16g+r byte 2u(+1) = scales of columns 128(8w+u)+32g(+16)."""
+    B, R, Ch = packed.shape
+    C = 2 * Ch
+    nch, nwin = -(-C // 128), -(-C // 1024)
+    codes = np.zeros((B, R // 16, nch, 64, 16), np.uint8)
+    sc = np.zeros((B, R // 16, nwin, 64, 16), np.uint8)
+    for b in range(B):
+        for row in range(R):
+            rb, r = divmod(row, 16)
+            for g in range(4):
+                lane = 16 * g + r
+                for c in range(nch):
+                    k0 = 128 * c + 32 * g
+                    if k0 < C:
+                        codes[b, rb, c, lane] = packed[b, row, k0 // 2:k0 // 2 + 16]
+                for w in range(nwin):
+                    for u in range(8):
+                        k0 = 128 * (8 * w + u) + 32 * g
+                        if k0 < C:
+                            sc[b, rb, w, lane, 2 * u:2 * u + 2] = scales[b, row, k0 // 16:k0 // 16 + 2]
+    return codes.reshape(B, -1), sc.reshape(B, -1)
+
+
+@pytest.mark.parametrize("B,R,C", [(1, 16, 32), (2, 48, 160), (3, 32, 1056), (1, 64, 2048)])
+def test_weights_tile_bit_exact(B, R, C):
+    say("tile", B, R, C)
+    rng = np.random.default_rng(B * 7 + R + C)
+    packed = rng.integers(0, 256, size=(B, R, C // 2), dtype=np.uint8)
+    scales = rng.integers(0, 256, size=(B, R, C // 16), dtype=np.uint8)
+    g = torch.arange(1, B + 1, dtype=torch.float32, device=DEV)
+    t = ops.nvfp4_weights_tile(torch.from_numpy(packed).to(DEV), torch.from_numpy(scales).to(DEV), g)
+    torch.cuda.synchronize()
+    want_c, want_s = _tile_reference(packed, scales)
+    assert np.array_equal(np_(t.codes), want_c)
+    assert np.array_equal(np_(t.scales), want_s)
+    assert (t.R, t.C, t.B) == (R, C, B) and np.array_equal(np_(t.g), np_(g))
+
+
 def test_fp8_roundtrip_bit_exact():
     say("fp8 roundtrip")
     x = (inputs.random_fp32((64, 256), 7) * 3).to(torch.bfloat16)
@@ -136,6 +178,7 @@ def _problem(counts, Nw, K, seed, mode=ops.W4A16, T=None, k=None):
     w = torch.stack([inputs.random_fp32((Nw, K), seed + 17 * e, std=0.02) for e in range(E)])
     wp, ws, wg = ops.nvfp4_quantize(w.to(DEV))
     d = dict(E=E, rows=rows, offsets=offsets, active=active, n_active=n_active, wp=wp, ws=ws, wg=wg,
+             wt=ops.nvfp4_weights_tile(wp, ws, wg),
              W=[onv.dequantize(np_(wp[e]), np_(ws[e]), np_(wg)[e]) for e in range(E)])
     if T is None:
         a = inputs.random_fp32((rows, K), seed + 1).to(torch.bfloat16)
@@ -162,8 +205,8 @@ def _run_gemm(d, mode, epi, out_dtype):
         kw.update(a_scales=d["as_"], a_g=d["ag"])
     else:
         a = d["a"].to(DEV)
-    out = ops.moe_grouped_gemm_nvfp4(mode, epi, a, d["wp"], d["ws"], d["wg"], t(d["offsets"]),
-                                     t(d["active"]), t(d["n_active"]), **kw)
+    out = ops.moe_grouped_gemm_nvfp4(mode, epi, a, d["wt"], t(d["offsets"]), t(d["active"]),
+                                     t(d["n_active"]), **kw)
     torch.cuda.synchronize()
     return np_(out)
 
@@ -219,7 +262,7 @@ def test_grouped_gemm_amax_output():
     say("gemm amax")
     d = _problem([9, 4], 64, 128, seed=11)
     t = lambda a: torch.from_numpy(a).to(DEV)
-    out, amax = ops.moe_grouped_gemm_nvfp4(ops.W4A16, ops.EPI_SWIGLU, d["a"].to(DEV), d["wp"], d["ws"], d["wg"],
+    out, amax = ops.moe_grouped_gemm_nvfp4(ops.W4A16, ops.EPI_SWIGLU, d["a"].to(DEV), d["wt"],
                                            t(d["offsets"]), t(d["active"]), t(d["n_active"]),
                                            out_dtype=torch.float32, want_amax=True)
     torch.cuda.synchronize()
