@@ -132,14 +132,17 @@ def main():
 
 def measured_traffic(wl, T):
     """HBM bytes per up/gate launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary
-    (copy-calibrated), or None when it does not cover this workload or the kernel source
-    has changed since the counters were taken."""
+    (copy-calibrated), or None when none covers this workload or the kernel source has
+    changed since the counters were taken."""
     import hashlib
     import re
-    if not (wl.name == "decode" and T == 512):
+    known = {("decode", 512): ("gemm_stream_decode512_traffic.md", "gemm_stream.hip"),
+             ("prefill", 8192): ("gemm_large_prefill8192_traffic.md", "gemm_large.hip")}
+    if (wl.name, T) not in known:
         return None
-    prof = os.path.join(ROOT, "profiles", "gemm_stream_decode512_traffic.md")
-    src = os.path.join(ROOT, "nvfp4_block_scaled_moe_amd", "csrc", "gemm_stream.hip")
+    prof_name, src_name = known[(wl.name, T)]
+    prof = os.path.join(ROOT, "profiles", prof_name)
+    src = os.path.join(ROOT, "nvfp4_block_scaled_moe_amd", "csrc", src_name)
     try:
         text = open(prof).read()
         sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]

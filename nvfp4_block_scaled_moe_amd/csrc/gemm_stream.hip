@@ -10,20 +10,20 @@
 //     Each wave owns RBW blocks of 16 rows over the whole K range (for SwiGLU: matching
 //     gate and up blocks), so its FP32 accumulators hold finished dot products and the
 //     epilogue needs no cross-wave reduction.
-//   * Weights: each lane loads 16 bytes (32 FP4 codes) of one row per 128-wide K chunk;
-//     lanes 16g..16g+15 take 16 consecutive rows at k-offset 32g, so one wave load reads
-//     16 rows x 64 contiguous bytes. Loads go through buffer resources (32-bit offsets,
-//     block offsets in SGPRs, out-of-range offsets read zero) into a register ring
-//     kDepth chunks deep; a ring entry is re-filled as soon as it has been decoded.
+//   * Weights, in the tiled storage of weights_tile.hip: per 128-wide K chunk each lane loads
+//     16 bytes (32 FP4 codes of one row), so one wave load reads a 16-row x 128-column block
+//     as 1 KB of contiguous memory. Loads go through buffer resources (32-bit offsets, block
+//     offsets in SGPRs, out-of-range offsets read zero) into a register ring kDepth chunks
+//     deep; a ring entry is re-filled as soon as it has been decoded.
 //   * Activations (the MFMA B operand) are shared by the waves: per chunk the workgroup
 //     copies the 16 or 32 token rows' 128-k slice into a two-slot LDS ring with one
 //     16-byte load per thread, then every wave reads its fragments from LDS. W4A16
 //     activations come from an f16 copy written in MFMA operand order; W4A4 activations
 //     are FP4 and are decoded like the weights. LDS rows are XOR-swizzled per token so the
 //     fragment reads are bank-conflict free.
-//   * Weight scales: per 1024-k window each lane loads 16 bytes of its row's E4M3 scales
-//     (one load per window instead of a 2-byte load per chunk) into a wave-private LDS
-//     area, from which it reads the two scales of each chunk.
+//   * Weight scales: one 16-byte load per lane, block and 1024-k window (the tiled scale
+//     storage) holds the lane's two scale bytes for each of the window's 8 chunks; the
+//     current and the next window stay in registers.
 //   * Decode in registers: hardware FP4 -> f16 convert and one packed f16 multiply by the
 //     block scale per two weights. Both steps are exact (E2M1 * E4M3 has <= 6 significant
 //     bits), so the MFMA sees exactly the dequantized weights.
