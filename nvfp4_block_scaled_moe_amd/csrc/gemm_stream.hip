@@ -44,7 +44,7 @@ namespace nvfp4moe {
 namespace {
 
 constexpr int kWin = 8;                  // chunks per scale tile (1024 k)
-constexpr int kDepth = 4;                // weight chunks in flight per wave
+constexpr int kDepth = 2;                // weight chunks in flight per wave (2 keeps 3 waves per SIMD)
 constexpr uint32_t kNoDst = 0xffffffffu;
 
 template <int TBM, bool A4>
