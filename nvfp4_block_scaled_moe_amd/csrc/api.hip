@@ -78,11 +78,12 @@ int gemm_path(int32_t rows, int32_t E, int32_t Nw) {
 // their row exponents (W4A16 on both paths, W4A4 on the MFMA path), and the m-tile
 // schedule of the MFMA path.
 struct GemmWs {
-  size_t a16_bytes, rexp_bytes, sched_bytes, total;
-  int max_mtiles;
+  size_t a16_bytes, rexp_bytes, sched_bytes, partial_bytes, total;
+  int max_mtiles, ksplit;
 };
-GemmWs gemm_ws_layout(int path, nvfp4moe_mode mode, int64_t a_rows, int32_t rows, int32_t E, int32_t K) {
-  GemmWs w{0, 0, 0, 0, 0};
+GemmWs gemm_ws_layout(int path, nvfp4moe_mode mode, int64_t a_rows, int32_t rows, int32_t E, int32_t Nw,
+                      int32_t K) {
+  GemmWs w{0, 0, 0, 0, 0, 0, 1};
   if (mode == NVFP4MOE_W4A16 || path == NVFP4MOE_PATH_MFMA) {
     const size_t K128 = ((size_t)K + 127) / 128 * 128;  // rows padded to whole 128-k chunks
     w.a16_bytes = round_up((size_t)a_rows * K128 * 2);
@@ -93,8 +94,10 @@ GemmWs gemm_ws_layout(int path, nvfp4moe_mode mode, int64_t a_rows, int32_t rows
     // sum over experts of ceil(M_e / bm) <= ceil(rows / bm) + (number of non-empty experts)
     w.max_mtiles = (rows + bm - 1) / bm + (E < rows ? E : rows);
     w.sched_bytes = 2 * round_up((size_t)w.max_mtiles * 4) + kAlign;
+    w.ksplit = large_ksplit(rows, E, Nw, K);
+    if (w.ksplit > 1) w.partial_bytes = round_up((size_t)w.ksplit * rows * Nw * 4);
   }
-  w.total = w.a16_bytes + w.rexp_bytes + w.sched_bytes;
+  w.total = w.a16_bytes + w.rexp_bytes + w.sched_bytes + w.partial_bytes;
   return w;
 }
 
@@ -208,7 +211,7 @@ nvfp4moe_status nvfp4_weights_tile(const uint8_t* packed, const uint8_t* scales,
 size_t moe_grouped_gemm_workspace_size(nvfp4moe_mode mode, int64_t a_rows, int32_t rows,
                                        int32_t E, int32_t Nw, int32_t K) {
   if (a_rows < 1 || rows < 1 || E < 1 || K < 1) return 0;
-  return gemm_ws_layout(gemm_path(rows, E, Nw), mode, a_rows, rows, E, K).total;
+  return gemm_ws_layout(gemm_path(rows, E, Nw), mode, a_rows, rows, E, Nw, K).total;
 }
 
 nvfp4moe_status moe_grouped_gemm_nvfp4(nvfp4moe_mode mode, nvfp4moe_epilogue epi,
@@ -257,7 +260,7 @@ nvfp4moe_status moe_grouped_gemm_nvfp4(nvfp4moe_mode mode, nvfp4moe_epilogue epi
   const int path = gemm_path(rows, E, Nw);
   if (path == NVFP4MOE_PATH_NONE)
     return fail(NVFP4MOE_ERR_UNSUPPORTED, "%s: the forced MFMA path needs Nw %% 256 == 0 (Nw=%d)", fn, Nw);
-  const GemmWs lay = gemm_ws_layout(path, mode, a_rows, rows, E, K);
+  const GemmWs lay = gemm_ws_layout(path, mode, a_rows, rows, E, Nw, K);
   if (lay.total && (!ws || ws_bytes < lay.total))
     return fail(NVFP4MOE_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn,
                 lay.total, ws_bytes);
@@ -312,6 +315,8 @@ nvfp4moe_status moe_grouped_gemm_nvfp4(nvfp4moe_mode mode, nvfp4moe_epilogue epi
     g.sched_e = reinterpret_cast<const int*>(sched);
     g.sched_r = reinterpret_cast<const int*>(sched + arr);
     g.sched_n = reinterpret_cast<const int*>(sched + 2 * arr);
+    g.ksplit = lay.ksplit;
+    g.partial = lay.partial_bytes ? reinterpret_cast<float*>(sched + lay.sched_bytes) : nullptr;
     return hip_status(launch_gemm_large(g, lay.max_mtiles, s), fn);
   }
   return hip_status(launch_gemm_stream(g, s), fn);

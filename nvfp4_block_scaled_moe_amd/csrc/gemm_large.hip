@@ -42,7 +42,7 @@ constexpr int kSlot = 16 * kTBM * kTokBytes;
 
 template <int WAVES, int WDEPTH, bool SWIGLU>
 __global__ __launch_bounds__(WAVES* kWave, 2) void gemm_large_kernel(const GemmArgs p, int ntiles_n,
-                                                                     int total_tiles) {
+                                                                     int tiles_per_split, int total_tiles) {
   static_assert(WDEPTH >= 2 && kWin % WDEPTH == 0, "the weight ring is read one chunk ahead; steps pair up");
   constexpr int NT = WAVES * kWave;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -53,8 +53,10 @@ __global__ __launch_bounds__(WAVES* kWave, 2) void gemm_large_kernel(const GemmA
   const int per_xcd = gridDim.x >> 3;
   const int tile = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
   if (tile >= total_tiles) return;
-  const int mt = tile / ntiles_n;            // m-tile
-  const int nb = tile - mt * ntiles_n;       // row tile
+  const int ks = tile / tiles_per_split;     // K slice
+  const int mn = tile - ks * tiles_per_split;
+  const int mt = mn / ntiles_n;              // m-tile
+  const int nb = mn - mt * ntiles_n;         // row tile
   if (mt >= p.sched_n[0]) return;
   const int e = p.sched_e[mt], tc = p.sched_r[mt];
   const int r0 = p.expert_offsets[e];
@@ -64,6 +66,11 @@ __global__ __launch_bounds__(WAVES* kWave, 2) void gemm_large_kernel(const GemmA
   const int F = Nw >> 1;
   const int nch = (K + kChunk - 1) / kChunk;
   const int nwin = (nch + kWin - 1) / kWin;
+  // K slice ks: whole scale windows [wlo, whi), chunks [clo, chi)
+  const int wps = (nwin + p.ksplit - 1) / p.ksplit;
+  const int wlo = ks * wps, whi = min(nwin, wlo + wps);
+  if (wlo >= whi) return;
+  const int clo = wlo * kWin, chi = min(nch, whi * kWin);
   const int ntb = __builtin_amdgcn_readfirstlane(min(kTBM, (M - tc + 15) >> 4));
 
   auto blkrow = [&](int b) -> int {
@@ -103,7 +110,7 @@ __global__ __launch_bounds__(WAVES* kWave, 2) void gemm_large_kernel(const GemmA
     }
     u32x4 bst[2][RND];   // two staging sets: chunk c's loads are in flight for two steps
     auto b_issue = [&](int c, int set) {   // set: c % 2, passed as a constant
-      const bool in = c < nch;
+      const bool in = c < chi;
 #pragma unroll
       for (int rr = 0; rr < RND; ++rr) bst[set][rr] = ld128(ar, in ? bsrc[rr] + (uint32_t)c * 256u : kOOB, 0);
     };
@@ -126,14 +133,14 @@ __global__ __launch_bounds__(WAVES* kWave, 2) void gemm_large_kernel(const GemmA
     u32x4 wring[WDEPTH][kRBW];
     auto w_issue = [&](int d, int c) {   // codes past K are zero in the tiles
 #pragma unroll
-      for (int b = 0; b < kRBW; ++b) wring[d][b] = ld128(wr, c < nch ? wlane + (uint32_t)c * 1024u : kOOB, wsoff[b]);
+      for (int b = 0; b < kRBW; ++b) wring[d][b] = ld128(wr, c < chi ? wlane + (uint32_t)c * 1024u : kOOB, wsoff[b]);
     };
     // One 16-byte load per block and window holds the lane's two scale bytes for each of
     // the window's 8 chunks; the current and the next window stay in registers.
     u32x4 scur[kRBW], snext[kRBW];
     auto s_issue = [&](int w) {
 #pragma unroll
-      for (int b = 0; b < kRBW; ++b) snext[b] = ld128(sr, w < nwin ? slane + (uint32_t)w * 1024u : kOOB, ssoff[b]);
+      for (int b = 0; b < kRBW; ++b) snext[b] = ld128(sr, w < whi ? slane + (uint32_t)w * 1024u : kOOB, ssoff[b]);
     };
     f16x8 wf[kRBW][4], wfn[kRBW][4];   // decoded weights of chunks c and c+1
     f16x2 sc[kRBW][2];
@@ -157,14 +164,14 @@ __global__ __launch_bounds__(WAVES* kWave, 2) void gemm_large_kernel(const GemmA
 
     // prologue: activations of chunks 0 and 1 into slots 0 and 1 (chunk 2 requested),
     // weights of chunks 0..WDEPTH-1 requested, chunk 0 decoded
-    s_issue(0);
-    b_issue(0, 0);
+    s_issue(wlo);
+    b_issue(clo, 0);                              // clo is a multiple of 8: chunk x uses set x % 2
 #pragma unroll
-    for (int d = 0; d < WDEPTH; ++d) w_issue(d, d);
+    for (int d = 0; d < WDEPTH; ++d) w_issue(d, clo + d);
     b_commit(0, 0);
-    b_issue(1, 1);
+    b_issue(clo + 1, 1);
     b_commit(1, 1);
-    b_issue(2, 0);
+    b_issue(clo + 2, 0);
 #pragma unroll
     for (int b = 0; b < kRBW; ++b) scur[b] = snext[b];
     scales(0);
@@ -180,12 +187,12 @@ __global__ __launch_bounds__(WAVES* kWave, 2) void gemm_large_kernel(const GemmA
     // and those of chunk c+3 are requested. Vector-memory counters retire in order, so the
     // store waits only on requests at least one step old.
     int slot = 0;
-    for (int c0 = 0; c0 < nch; c0 += kWin) {       // one scale window per iteration
+    for (int c0 = clo; c0 < chi; c0 += kWin) {     // one scale window per iteration
       s_issue(c0 / kWin + 1);
 #pragma unroll
       for (int u = 0; u < kWin; ++u) {
         const int c = c0 + u;
-        if (c < nch) {
+        if (c < chi) {
           const int d = u % WDEPTH, dn = (u + 1) % WDEPTH;
           const int slot1 = slot == kSlots - 1 ? 0 : slot + 1;
           const int slot2 = slot1 == kSlots - 1 ? 0 : slot1 + 1;
@@ -220,6 +227,20 @@ __global__ __launch_bounds__(WAVES* kWave, 2) void gemm_large_kernel(const GemmA
       }
     }
 
+    if (p.ksplit > 1) {   // raw partial sums; splitk_reduce_kernel applies the epilogue
+      float* part = p.partial + (size_t)ks * p.rows * Nw;
+#pragma unroll
+      for (int tb = 0; tb < kTBM; ++tb) {
+        const int t = tc + 16 * tb + l16;
+        if (tb < ntb && t < M) {
+#pragma unroll
+          for (int b = 0; b < kRBW; ++b)
+            *reinterpret_cast<float4*>(part + (size_t)(r0 + t) * Nw + blkrow(b) + 4 * g) =
+                make_float4(acc[b][tb][0], acc[b][tb][1], acc[b][tb][2], acc[b][tb][3]);
+        }
+      }
+      return;
+    }
     uint32_t amax_bits = store_tile<kRBW, kTBM, SWIGLU>(p, acc, tc, ntb, M, r0, alpha, !p.w4a4, blkrow, lane, 0u);
     merge_amax(p.out_amax, amax_bits, lane);
   };
@@ -227,6 +248,59 @@ __global__ __launch_bounds__(WAVES* kWave, 2) void gemm_large_kernel(const GemmA
   else if (ntb > 2) body(Int<4>{});
   else if (ntb == 2) body(Int<2>{});
   else body(Int<1>{});
+}
+
+// Split-K epilogue: out[row, col] from the fixed-order sum over K slices of the partial sums,
+// then the same arithmetic as the unsplit epilogue (store_tile). One thread per row and 4
+// output columns; the row's expert comes from a binary search in expert_offsets.
+template <bool SWIGLU>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const GemmArgs p) {
+  const int Nw = p.Nw, ncol = SWIGLU ? Nw / 2 : Nw, c4 = ncol / 4;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  uint32_t amax_bits = 0;
+  if (i < (int64_t)p.rows * c4) {
+    const int row = (int)(i / c4), col = 4 * (int)(i - (int64_t)row * c4);
+    int lo = 0, hi = p.E;                       // expert_offsets[lo] <= row < expert_offsets[hi]
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (p.expert_offsets[mid] <= row) lo = mid;
+      else hi = mid;
+    }
+    const float alpha = p.w4a4 ? p.w_g[lo] * p.a_g[0] : p.w_g[lo];
+    const int pexp = p.w4a4 ? 0 : p.rexp[p.gather_index ? p.gather_index[row] / p.gather_div : row];
+    const size_t slice = (size_t)p.rows * Nw;
+    const float* src = p.partial + (size_t)row * Nw + col;
+    float4 a = *reinterpret_cast<const float4*>(src);
+    float4 u = SWIGLU ? *reinterpret_cast<const float4*>(src + ncol) : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int s = 1; s < p.ksplit; ++s) {
+      const float4 v = *reinterpret_cast<const float4*>(src + s * slice);
+      a.x += v.x; a.y += v.y; a.z += v.z; a.w += v.w;
+      if (SWIGLU) {
+        const float4 w = *reinterpret_cast<const float4*>(src + s * slice + ncol);
+        u.x += w.x; u.y += w.y; u.z += w.z; u.w += w.w;
+      }
+    }
+    const float av[4] = {a.x, a.y, a.z, a.w}, uv[4] = {u.x, u.y, u.z, u.w};
+    float o[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (SWIGLU) {
+        const float gv = ldexpf(av[q] * alpha, pexp);
+        const float up = ldexpf(uv[q] * alpha, pexp);
+        o[q] = gv / (1.0f + expf(-gv)) * up;
+      } else {
+        o[q] = ldexpf(av[q] * alpha, pexp);
+      }
+      amax_bits = max(amax_bits, abs_bits(o[q]));
+    }
+    const size_t off = (size_t)row * ncol + col;
+    if (p.out_bf16)
+      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + off) =
+          make_uint2(f32_to_bf16(o[0]) | (f32_to_bf16(o[1]) << 16), f32_to_bf16(o[2]) | (f32_to_bf16(o[3]) << 16));
+    else
+      *reinterpret_cast<float4*>(static_cast<float*>(p.out) + off) = make_float4(o[0], o[1], o[2], o[3]);
+  }
+  merge_amax(p.out_amax, amax_bits, threadIdx.x & (kWave - 1));
 }
 
 // m-tiles of bm rows over the active experts (one workgroup, n_active <= 1024):
@@ -280,9 +354,15 @@ hipError_t launch_cfg(const GemmArgs& a, int max_mtiles, hipStream_t stream) {
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int ntiles_n = a.Nw / (16 * kRBW * WAVES);
-  const int total = max_mtiles * ntiles_n;
+  const int per_split = max_mtiles * ntiles_n;
+  const int total = per_split * a.ksplit;
   const int grid = (total + 7) / 8 * 8;
-  kern<<<grid, WAVES * kWave, shmem, stream>>>(a, ntiles_n, total);
+  kern<<<grid, WAVES * kWave, shmem, stream>>>(a, ntiles_n, per_split, total);
+  if (a.ksplit <= 1) return hipGetLastError();
+  const hipError_t e2 = hipGetLastError();
+  if (e2 != hipSuccess) return e2;
+  const int64_t n = (int64_t)a.rows * ((SWIGLU ? a.Nw / 2 : a.Nw) / 4);
+  splitk_reduce_kernel<SWIGLU><<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(a);
   return hipGetLastError();
 }
 
@@ -296,6 +376,19 @@ hipError_t launch_sw(const GemmArgs& a, int max_mtiles, hipStream_t stream) {
 }  // namespace
 
 int large_rows_per_mtile() { return 16 * kTBM; }
+
+// Split K (in whole 1024-column scale windows) when the m-tile x row-tile grid is under one
+// workgroup per CU; aim at two per CU. NVFP4MOE_LARGE_KSPLIT=<n> overrides (tests, tuning).
+int large_ksplit(int rows, int E, int Nw, int K) {
+  const int nwin = (K + kChunk * kWin - 1) / (kChunk * kWin);
+  const int tiles = ((rows + 16 * kTBM - 1) / (16 * kTBM) + (E < rows ? E : rows)) * (Nw / (16 * kRBW * 8));
+  int s = tiles >= 256 ? 1 : (512 + tiles - 1) / tiles;
+  if (const char* env = std::getenv("NVFP4MOE_LARGE_KSPLIT")) s = std::atoi(env);
+  if (s < 1) s = 1;
+  if (s > nwin) s = nwin;
+  const int wps = (nwin + s - 1) / s;   // windows per slice; no empty slices
+  return (nwin + wps - 1) / wps;
+}
 bool large_supports(int Nw) { return Nw % (16 * kRBW * 8) == 0; }
 
 hipError_t launch_gemm_large(const GemmArgs& a, int max_mtiles, hipStream_t stream) {

@@ -57,6 +57,8 @@ struct GemmArgs {
   const int* sched_e;              // large-M path: m-tile -> expert   (workspace)
   const int* sched_r;              // large-M path: m-tile -> first row (workspace)
   const int* sched_n;              // large-M path: number of m-tiles  (workspace)
+  float* partial;                  // large-M split-K: [ksplit, rows, Nw] fp32 partial sums (workspace)
+  int ksplit;                      // large-M: K slices (1: no split)
 };
 hipError_t launch_gemm_stream(const GemmArgs& a, hipStream_t stream);
 // Tiled weight storage (weights_tile.hip): bytes per [R, C] matrix and the reordering.
@@ -69,6 +71,8 @@ hipError_t launch_weights_tile(const uint8_t* packed, const uint8_t* scales, int
 int large_rows_per_mtile();
 bool large_supports(int Nw);
 hipError_t launch_gemm_large(const GemmArgs& a, int max_mtiles, hipStream_t stream);
+// K slices for the large-M path from the sizes alone (1 when the tiles fill the GPU).
+int large_ksplit(int rows, int E, int Nw, int K);
 hipError_t launch_zero_f32(float* p, int n, hipStream_t stream);
 
 // ---- reduce.hip

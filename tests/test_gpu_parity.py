@@ -311,6 +311,37 @@ def test_grouped_gemm_mfma_tile_shapes(tile, monkeypatch):
         assert rel_fro(got, want) < 1e-5
 
 
+@pytest.mark.parametrize("ksplit", ["1", "2", "3"])
+@pytest.mark.parametrize("mode", [ops.W4A16, ops.W4A4])
+def test_grouped_gemm_mfma_split_k(ksplit, mode, monkeypatch):
+    """K split into slices of whole 1024-column windows (partial sums reduced in a fixed
+    order by a second kernel that applies the epilogue); K = 3072 + 96 leaves a ragged last
+    window. amax of the output must equal max |out| exactly."""
+    say("gemm mfma split-k", ksplit, mode)
+    monkeypatch.setenv("NVFP4MOE_FORCE_PATH", "mfma")
+    monkeypatch.setenv("NVFP4MOE_LARGE_KSPLIT", ksplit)
+    d = _problem([300, 5, 0, 77], 512, 3168, seed=int(ksplit) + 10 * mode, mode=mode, T=250, k=2)
+    t = lambda a: torch.from_numpy(a).to(DEV)
+    for epi in (ops.EPI_NONE, ops.EPI_SWIGLU):
+        want = omoe.grouped_gemm(d["A"], d["offsets"], d["W"], "swiglu" if epi else "none")
+        got = _run_gemm(d, mode, epi, torch.float32)
+        assert ops.last_dispatch() == ops.PATH_MFMA
+        assert_finite(got)
+        assert rel_fro(got, want) < 1e-5
+    kw = dict(rows=d["rows"], gather_index=d["gidx"].to(DEV), gather_div=d["gdiv"], out_dtype=torch.bfloat16,
+              want_amax=True)
+    a = d["a"].to(DEV)
+    if mode == ops.W4A4:
+        a = d["aq"]
+        kw.update(a_scales=d["as_"], a_g=d["ag"])
+    out, amax = ops.moe_grouped_gemm_nvfp4(mode, ops.EPI_SWIGLU, a, d["wt"], t(d["offsets"]), t(d["active"]),
+                                           t(d["n_active"]), **kw)
+    torch.cuda.synchronize()
+    o = np_(out).astype(np.float32)
+    # amax is taken on the float32 values before the bf16 store
+    assert np_(amax)[0] >= np.abs(o).max() * (1 - 2 ** -8) and np_(amax)[0] <= np.abs(o).max() * (1 + 2 ** -8)
+
+
 @pytest.mark.parametrize("mode", [ops.W4A16, ops.W4A4])
 def test_grouped_gemm_mfma_gather(mode, monkeypatch):
     say("gemm mfma gather", mode)
