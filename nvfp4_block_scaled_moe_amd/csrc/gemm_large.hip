@@ -10,13 +10,14 @@
 //   * Workgroup = 8 waves = 256 weight rows (each wave: 2 blocks of 16 rows over all of K;
 //     for SwiGLU one gate and the matching up block) x one m-tile. A ragged m-tile runs with
 //     1, 2, 4 or 8 blocks of 16 rows.
-//   * Weights (MFMA A operand): each lane loads 16 bytes (32 FP4 codes) of its row per
-//     128-wide chunk and the two E4M3 scale bytes that cover them, WDEPTH chunks ahead, into
-//     registers; they are decoded exactly to f16 (hardware FP4 convert, one packed f16
-//     multiply by the block scale) one chunk ahead of use, interleaved with the MFMAs.
+//   * Weights (MFMA A operand), in the tiled storage of weights_tile.hip: each lane loads 16
+//     bytes (32 FP4 codes of its row) per 128-wide chunk, WDEPTH chunks ahead, and one
+//     16-byte scale load per 8 chunks, into registers; the codes are decoded exactly to f16
+//     (hardware FP4 convert, one packed f16 multiply by the block scale) one chunk ahead of
+//     use, interleaved with the MFMAs.
 //   * Activations (B operand): f16 rows in MFMA operand order (bf16 rows scaled per row by a
 //     power of two, or NVFP4 rows decoded exactly), staged per chunk through a three-slot
-//     LDS ring (one 16-byte load and store per thread and round). Three slots let every wave
+//     LDS ring by LDS DMA (16 bytes per thread and round, no registers). Three slots let every wave
 //     read the first fragments of chunk c+1 before the barrier that ends chunk c, so no
 //     MFMA waits for LDS after a barrier. XOR-swizzled rows keep the reads conflict free.
 //   * v_mfma_f32_16x16x32_f16, k-step-major: each B fragment read from LDS feeds both
@@ -99,28 +100,27 @@ __global__ __launch_bounds__(WAVES* kWave, 2) void gemm_large_kernel(const GemmA
     constexpr int TPT = 16;                          // threads per row (16 x 16 bytes)
     constexpr int TPR = NT / TPT;                    // rows per staging round
     constexpr int RND = (16 * NTB + TPR - 1) / TPR;
+    // Activation staging by LDS DMA (buffer_load ... lds): lane l of a wave writes the 16 bytes
+    // at block + 16 l of the slot, the wave's block holding 4 rows (4 x 256 B). The source of
+    // each lane is the logical piece that the row's XOR swizzle puts at that position, so the
+    // fragment reads stay conflict free; rows past the tile read zeros (kOOB).
     uint32_t bsrc[RND], bdst[RND];
 #pragma unroll
     for (int rr = 0; rr < RND; ++rr) {
-      const int tk = rr * TPR + tid / TPT, pc = tid % TPT, t = tc + tk;
+      const int tk = rr * TPR + wave * 4 + (lane >> 4), pp = lane & 15, t = tc + tk;
       const bool ok = tk < 16 * NTB && t < M;
       const uint32_t arow = ok ? (uint32_t)(p.gather_index ? p.gather_index[r0 + t] / p.gather_div : r0 + t) : 0u;
-      bsrc[rr] = ok ? (arow * (uint32_t)K128 + 8 * pc) * 2 : kOOB;
-      bdst[rr] = tk * kTokBytes + 16 * (pc ^ (tk & 15));   // tk < 128: inside the slot
+      bsrc[rr] = ok ? (arow * (uint32_t)K128 + 8 * (pp ^ (tk & 15))) * 2 : kOOB;
+      bdst[rr] = (rr * TPR + wave * 4) * kTokBytes;   // wave-uniform; rows < 128 stay in the slot
     }
-    u32x4 bst[2][RND];   // two staging sets: chunk c's loads are in flight for two steps
-    auto b_issue = [&](int c, int set) {   // set: c % 2, passed as a constant
+    static_assert(TPR == 4 * WAVES && RND * TPR <= 16 * kTBM, "4 rows per wave and round, inside one slot");
+    auto b_dma = [&](int c, int slot) {
       const bool in = c < chi;
 #pragma unroll
-      for (int rr = 0; rr < RND; ++rr) bst[set][rr] = ld128(ar, in ? bsrc[rr] + (uint32_t)c * 256u : kOOB, 0);
-    };
-    // Rows past the tile's rows are loaded as zeros (kOOB) and stored like the others: every
-    // store lands inside the slot, so the commit has no branch.
-    static_assert(RND * TPR <= 16 * kTBM, "staging rounds stay inside one slot");
-    auto b_commit = [&](int set, int slot) {
-      unsigned char* base = smem + slot * kSlot;
-#pragma unroll
-      for (int rr = 0; rr < RND; ++rr) *reinterpret_cast<u32x4*>(base + bdst[rr]) = bst[set][rr];
+      for (int rr = 0; rr < RND; ++rr)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            ar, (__attribute__((address_space(3))) void*)(smem + slot * kSlot + bdst[rr]), 16,
+            in ? bsrc[rr] + (uint32_t)c * 256u : kOOB, 0, 0, 0);
     };
     auto b_read = [&](f16x8 (&dst)[NTB], int slot, int j) {
       const unsigned char* base = smem + slot * kSlot;
@@ -162,16 +162,13 @@ __global__ __launch_bounds__(WAVES* kWave, 2) void gemm_large_kernel(const GemmA
 #pragma unroll
       for (int tb = 0; tb < kTBM; ++tb) acc[b][tb] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-    // prologue: activations of chunks 0 and 1 into slots 0 and 1 (chunk 2 requested),
-    // weights of chunks 0..WDEPTH-1 requested, chunk 0 decoded
+    // prologue: activations of the first two chunks into slots 0 and 1, weights of the first
+    // WDEPTH chunks requested, the first chunk decoded
     s_issue(wlo);
-    b_issue(clo, 0);                              // clo is a multiple of 8: chunk x uses set x % 2
+    b_dma(clo, 0);
 #pragma unroll
     for (int d = 0; d < WDEPTH; ++d) w_issue(d, clo + d);
-    b_commit(0, 0);
-    b_issue(clo + 1, 1);
-    b_commit(1, 1);
-    b_issue(clo + 2, 0);
+    b_dma(clo + 1, 1);
 #pragma unroll
     for (int b = 0; b < kRBW; ++b) scur[b] = snext[b];
     scales(0);
@@ -182,10 +179,10 @@ __global__ __launch_bounds__(WAVES* kWave, 2) void gemm_large_kernel(const GemmA
     b_read(bcur, 0, 0);
 
     // Step c: MFMAs of chunk c (LDS slot c % 3, decoded weights in wf) interleaved with the
-    // LDS reads of the next k-step and the decode of chunk c+1. Activations of chunk c+2,
-    // requested one step earlier, are stored to slot (c+2) % 3 before the step's barrier,
-    // and those of chunk c+3 are requested. Vector-memory counters retire in order, so the
-    // store waits only on requests at least one step old.
+    // LDS reads of the next k-step and the decode of chunk c+1, while the activations of chunk
+    // c+2 stream into slot (c+2) % 3. The barrier that ends the step waits for every load of
+    // the wave (LDS DMA is counted with the vector-memory loads), so chunk c+2 is in LDS for
+    // all waves when step c+1 prefetches its first fragments.
     int slot = 0;
     for (int c0 = clo; c0 < chi; c0 += kWin) {     // one scale window per iteration
       s_issue(c0 / kWin + 1);
@@ -196,7 +193,7 @@ __global__ __launch_bounds__(WAVES* kWave, 2) void gemm_large_kernel(const GemmA
           const int d = u % WDEPTH, dn = (u + 1) % WDEPTH;
           const int slot1 = slot == kSlots - 1 ? 0 : slot + 1;
           const int slot2 = slot1 == kSlots - 1 ? 0 : slot1 + 1;
-          b_issue(c + 3, (u + 1) & 1);             // c0 is even: chunk x uses set x % 2
+          b_dma(c + 2, slot2);                     // slot2 was last read in step c-1
           w_issue(d, c + WDEPTH);                  // ring entry d (chunk c) was decoded last step
           scales(u + 1);
 #pragma unroll
@@ -212,7 +209,6 @@ __global__ __launch_bounds__(WAVES* kWave, 2) void gemm_large_kernel(const GemmA
 #pragma unroll
             for (int tb = 0; tb < NTB; ++tb) bcur[tb] = bnext[tb];
           }
-          b_commit(u & 1, slot2);
 #pragma unroll
           for (int b = 0; b < kRBW; ++b)
 #pragma unroll
