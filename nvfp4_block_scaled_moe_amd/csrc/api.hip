@@ -95,8 +95,10 @@ GemmWs gemm_ws_layout(int path, nvfp4moe_mode mode, int64_t a_rows, int32_t rows
     w.max_mtiles = (rows + bm - 1) / bm + (E < rows ? E : rows);
     w.sched_bytes = 2 * round_up((size_t)w.max_mtiles * 4) + kAlign;
     w.ksplit = large_ksplit(rows, E, Nw, K);
-    if (w.ksplit > 1) w.partial_bytes = round_up((size_t)w.ksplit * rows * Nw * 4);
+  } else {
+    w.ksplit = stream_ksplit(rows, E, Nw, K);
   }
+  if (w.ksplit > 1) w.partial_bytes = round_up((size_t)w.ksplit * rows * Nw * 4);
   w.total = w.a16_bytes + w.rexp_bytes + w.sched_bytes + w.partial_bytes;
   return w;
 }
@@ -309,14 +311,17 @@ nvfp4moe_status moe_grouped_gemm_nvfp4(nvfp4moe_mode mode, nvfp4moe_epilogue epi
   }
   if (err != hipSuccess) return hip_status(err, fn);
   g_last_dispatch = path;
+  g.ksplit = lay.ksplit;
+  g.partial = lay.partial_bytes
+                  ? reinterpret_cast<float*>(base + lay.a16_bytes + lay.rexp_bytes + lay.sched_bytes)
+                  : nullptr;
   if (path == NVFP4MOE_PATH_MFMA) {
     char* sched = base + lay.a16_bytes + lay.rexp_bytes;
     const size_t arr = round_up((size_t)lay.max_mtiles * 4);
     g.sched_e = reinterpret_cast<const int*>(sched);
     g.sched_r = reinterpret_cast<const int*>(sched + arr);
     g.sched_n = reinterpret_cast<const int*>(sched + 2 * arr);
-    g.ksplit = lay.ksplit;
-    g.partial = lay.partial_bytes ? reinterpret_cast<float*>(sched + lay.sched_bytes) : nullptr;
+
     return hip_status(launch_gemm_large(g, lay.max_mtiles, s), fn);
   }
   return hip_status(launch_gemm_stream(g, s), fn);

@@ -99,4 +99,25 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return v;
 }
 
+// Wave-wide max of a uint32 through DPP moves (no LDS round trips): quad, half-row and row
+// steps leave every row's max in all its lanes, the row broadcasts fold rows 0..3 into
+// lane 63, which is read back as a wave-uniform value.
+__device__ __forceinline__ uint32_t dpp_max_u32(uint32_t v, int ctrl_id) {
+  uint32_t t;
+  switch (ctrl_id) {
+    case 0: t = (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0xb1, 0xf, 0xf, false); break;   // quad_perm 1,0,3,2
+    case 1: t = (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x4e, 0xf, 0xf, false); break;   // quad_perm 2,3,0,1
+    case 2: t = (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x141, 0xf, 0xf, false); break;  // row_half_mirror
+    case 3: t = (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x140, 0xf, 0xf, false); break;  // row_mirror
+    case 4: t = (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x142, 0xa, 0xf, false); break;  // row_bcast15
+    default: t = (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x143, 0xc, 0xf, false); break; // row_bcast31
+  }
+  return v > t ? v : t;
+}
+__device__ __forceinline__ uint32_t wave_max_u32_uniform(uint32_t v) {
+#pragma unroll
+  for (int s = 0; s < 6; ++s) v = dpp_max_u32(v, s);
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
 }  // namespace nvfp4moe

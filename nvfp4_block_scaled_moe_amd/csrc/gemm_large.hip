@@ -357,9 +357,7 @@ hipError_t launch_cfg(const GemmArgs& a, int max_mtiles, hipStream_t stream) {
   if (a.ksplit <= 1) return hipGetLastError();
   const hipError_t e2 = hipGetLastError();
   if (e2 != hipSuccess) return e2;
-  const int64_t n = (int64_t)a.rows * ((SWIGLU ? a.Nw / 2 : a.Nw) / 4);
-  splitk_reduce_kernel<SWIGLU><<<(unsigned)((n + 255) / 256), 256, 0, stream>>>(a);
-  return hipGetLastError();
+  return launch_splitk_reduce(a, stream);
 }
 
 // Weight ring depth 2: the chunk after next is in flight while a chunk is decoded (a deeper
@@ -370,6 +368,14 @@ hipError_t launch_sw(const GemmArgs& a, int max_mtiles, hipStream_t stream) {
 }
 
 }  // namespace
+
+hipError_t launch_splitk_reduce(const GemmArgs& a, hipStream_t stream) {
+  const int64_t n = (int64_t)a.rows * ((a.swiglu ? a.Nw / 2 : a.Nw) / 4);
+  const unsigned blocks = (unsigned)((n + 255) / 256);
+  if (a.swiglu) splitk_reduce_kernel<true><<<blocks, 256, 0, stream>>>(a);
+  else splitk_reduce_kernel<false><<<blocks, 256, 0, stream>>>(a);
+  return hipGetLastError();
+}
 
 int large_rows_per_mtile() { return 16 * kTBM; }
 

@@ -59,7 +59,7 @@ struct Ring {
 
 template <int RBW, int WAVES, int TBM, int WDEPTH, int BDEPTH, bool SWIGLU, bool A4>
 __global__ __launch_bounds__(WAVES* kWave) void gemm_stream_kernel(const GemmArgs p, int tiles_per_expert,
-                                                                   int total_tiles) {
+                                                                   int tiles_per_split, int total_tiles) {
   static_assert(RBW % 2 == 0, "row blocks per wave come in pairs");
   static_assert(kWin % WDEPTH == 0 && kWin % BDEPTH == 0, "ring depths divide the scale window");
   using R = Ring<TBM, A4>;
@@ -72,8 +72,10 @@ __global__ __launch_bounds__(WAVES* kWave) void gemm_stream_kernel(const GemmArg
   const int per_xcd = gridDim.x >> 3;
   const int tile = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
   if (tile >= total_tiles) return;
-  const int aidx = tile / tiles_per_expert;        // active-expert slot
-  const int nb = tile - aidx * tiles_per_expert;   // row tile
+  const int ks = tile / tiles_per_split;           // K slice
+  const int et = tile - ks * tiles_per_split;
+  const int aidx = et / tiles_per_expert;          // active-expert slot
+  const int nb = et - aidx * tiles_per_expert;     // row tile
   if (aidx >= p.n_active[0]) return;
   const int e = p.active[aidx];
   const int r0 = p.expert_offsets[e];
@@ -83,6 +85,11 @@ __global__ __launch_bounds__(WAVES* kWave) void gemm_stream_kernel(const GemmArg
   const int F = Nw >> 1;
   const int nch = (K + kChunk - 1) / kChunk;
   const int nwin = (nch + kWin - 1) / kWin;
+  // K slice ks: whole scale windows [wlo, whi), chunks [wlo * kWin, chi)
+  const int wps = (nwin + p.ksplit - 1) / p.ksplit;
+  const int wlo = ks * wps, whi = min(nwin, wlo + wps);
+  if (wlo >= whi) return;
+  const int chi = min(nch, whi * kWin);
 
   unsigned char* ring = smem;                                           // [2][R::kSlot]
 
@@ -172,7 +179,7 @@ __global__ __launch_bounds__(WAVES* kWave) void gemm_stream_kernel(const GemmArg
       auto b_issue = [&](int set, int c) {
         // f16 rows are zero-padded to whole chunks; FP4 rows are not, so W4A4 pieces and
         // scale pairs past K read zero (a neighbouring row's NaN scale must not leak in).
-        const bool cin = c < nch;
+        const bool cin = c < chi;
         const int kc = c * kChunk;
 #pragma unroll
         for (int rr = 0; rr < RND; ++rr) {
@@ -209,11 +216,11 @@ __global__ __launch_bounds__(WAVES* kWave) void gemm_stream_kernel(const GemmArg
       u32x4 scur[RBW], snext[RBW];
       auto s_issue = [&](int w) {
 #pragma unroll
-        for (int b = 0; b < RBW; ++b) snext[b] = ld128(sr, w < nwin ? slane + (uint32_t)w * 1024u : kOOB, ssoff[b]);
+        for (int b = 0; b < RBW; ++b) snext[b] = ld128(sr, w < whi ? slane + (uint32_t)w * 1024u : kOOB, ssoff[b]);
       };
       u32x4 wring[WDEPTH][RBW];
       auto w_issue = [&](int d, int c, int b) {   // codes past K are zero in the tiles
-        wring[d][b] = ld128(wr, c < nch ? wlane + (uint32_t)c * 1024u : kOOB, wsoff[b]);
+        wring[d][b] = ld128(wr, c < chi ? wlane + (uint32_t)c * 1024u : kOOB, wsoff[b]);
       };
       auto compute = [&](int d, int c, int u) {    // u = c % kWin, a constant
         u32x4 (&wv)[RBW] = wring[d];
@@ -261,21 +268,22 @@ __global__ __launch_bounds__(WAVES* kWave) void gemm_stream_kernel(const GemmArg
       };
 
       // prologue: scales of window 0, then activations and weights of the first chunks
-      s_issue(0);
+      const int clo = wlo * kWin;                   // a multiple of kWin: ring indices stay u % depth
+      s_issue(wlo);
 #pragma unroll
       for (int b = 0; b < RBW; ++b) scur[b] = snext[b];
 #pragma unroll
       for (int d = 0; d < (WDEPTH > BDEPTH ? WDEPTH : BDEPTH); ++d) {
-        if (d < BDEPTH) b_issue(d, d);
+        if (d < BDEPTH) b_issue(d, clo + d);
         if (d < WDEPTH) {
 #pragma unroll
-          for (int b = 0; b < RBW; ++b) w_issue(d, d, b);
+          for (int b = 0; b < RBW; ++b) w_issue(d, clo + d, b);
         }
       }
       b_commit(0, 0);
       __syncthreads();
       // Chunk c: LDS slot c&1, staging set c % BDEPTH and weight ring entry c % WDEPTH.
-      for (int c0 = 0; c0 < nwin * kWin; c0 += kWin) {   // whole windows; chunks past K are zero
+      for (int c0 = clo; c0 < whi * kWin; c0 += kWin) {   // whole windows; chunks past K are zero
         s_issue(c0 / kWin + 1);
 #pragma unroll
         for (int u = 0; u < kWin; ++u) {
@@ -294,7 +302,21 @@ __global__ __launch_bounds__(WAVES* kWave) void gemm_stream_kernel(const GemmArg
     if (ntb == TBM) kloop(Int<TBM>{});
     else kloop(Int<1>{});
 
-    amax_bits = store_tile<RBW, TBM, SWIGLU>(p, acc, tc, ntb, M, r0, alpha, !A4, blkrow, lane, amax_bits);
+    if (p.ksplit > 1) {   // raw partial sums; the split-K reduce applies the epilogue
+      float* part = p.partial + (size_t)ks * p.rows * Nw;
+#pragma unroll
+      for (int tb = 0; tb < TBM; ++tb) {
+        const int t = tc + 16 * tb + l16;
+        if (tb < ntb && t < M) {
+#pragma unroll
+          for (int b = 0; b < RBW; ++b)
+            *reinterpret_cast<float4*>(part + (size_t)(r0 + t) * Nw + blkrow(b) + 4 * g) =
+                make_float4(acc[b][tb][0], acc[b][tb][1], acc[b][tb][2], acc[b][tb][3]);
+        }
+      }
+    } else {
+      amax_bits = store_tile<RBW, TBM, SWIGLU>(p, acc, tc, ntb, M, r0, alpha, !A4, blkrow, lane, amax_bits);
+    }
     __syncthreads();   // the LDS rings are reused by the next pass
   }
 
@@ -307,12 +329,16 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
   const int rows_per_tile = 16 * RBW * WAVES;
   const int tiles_per_expert = a.Nw / rows_per_tile;
   const int max_active = a.E < a.rows ? a.E : a.rows;
-  const int total = max_active * tiles_per_expert;
+  const int per_split = max_active * tiles_per_expert;
+  const int total = per_split * a.ksplit;
   const int grid = (total + 7) / 8 * 8;
   const size_t shmem = (size_t)Ring<TBM, A4>::kBytes;
   gemm_stream_kernel<RBW, WAVES, TBM, kDepth, kDepth, SWIGLU, A4>
-      <<<grid, WAVES * kWave, shmem, stream>>>(a, tiles_per_expert, total);
-  return hipGetLastError();
+      <<<grid, WAVES * kWave, shmem, stream>>>(a, tiles_per_expert, per_split, total);
+  if (a.ksplit <= 1) return hipGetLastError();
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_splitk_reduce(a, stream);
 }
 
 // Tile shape: RBW row blocks of 16 per wave, WAVES waves. NVFP4MOE_STREAM_TILE=<rbw>x<waves>
@@ -335,6 +361,22 @@ hipError_t launch_sw(const GemmArgs& a, hipStream_t stream) {
 }
 
 }  // namespace
+
+// Split K (in whole 1024-column windows) when the grid would leave most CUs idle (under 128
+// workgroups, e.g. one expert with a few rows); the bound on the active experts is
+// min(E, rows). At 256 workgroups (one token over 8 experts) the unsplit kernel already
+// streams at ~4.8 TB/s and the extra reduce launch costs more than splitting gains (measured).
+// NVFP4MOE_STREAM_KSPLIT=<n> overrides (tests, tuning).
+int stream_ksplit(int rows, int E, int Nw, int K) {
+  const int nwin = (K + kChunk * kWin - 1) / (kChunk * kWin);
+  const int tiles = (E < rows ? E : rows) * (Nw / 128 > 0 ? Nw / 128 : 1);
+  int s = tiles >= 128 ? 1 : (512 + tiles - 1) / tiles;
+  if (const char* env = std::getenv("NVFP4MOE_STREAM_KSPLIT")) s = std::atoi(env);
+  if (s < 1) s = 1;
+  if (s > nwin) s = nwin;
+  const int wps = (nwin + s - 1) / s;
+  return (nwin + wps - 1) / wps;
+}
 
 hipError_t launch_gemm_stream(const GemmArgs& a, hipStream_t stream) {
   if (a.swiglu) return a.w4a4 ? launch_sw<true, true>(a, stream) : launch_sw<true, false>(a, stream);

@@ -61,6 +61,11 @@ struct GemmArgs {
   int ksplit;                      // large-M: K slices (1: no split)
 };
 hipError_t launch_gemm_stream(const GemmArgs& a, hipStream_t stream);
+// K slices for the small-M path from the sizes alone (1 unless the grid is tiny).
+int stream_ksplit(int rows, int E, int Nw, int K);
+// Split-K epilogue shared by both GEMM paths: out (and out_amax) from the fixed-order sum of
+// the ksplit partial-sum slices in a.partial.
+hipError_t launch_splitk_reduce(const GemmArgs& a, hipStream_t stream);
 // Tiled weight storage (weights_tile.hip): bytes per [R, C] matrix and the reordering.
 size_t tiled_codes_bytes(int64_t R, int64_t C);
 size_t tiled_scales_bytes(int64_t R, int64_t C);

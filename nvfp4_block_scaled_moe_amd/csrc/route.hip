@@ -71,15 +71,14 @@ __global__ __launch_bounds__(kRouterWaves* kWave) void router_kernel(const float
         be = e;
       }
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ov = __shfl_xor(bv, o, kWave);
-      const int oe = __shfl_xor(be, o, kWave);
-      if (better(ov, oe, bv, be)) {
-        bv = ov;
-        be = oe;
-      }
-    }
+    // wave argmax: the largest value (as an order-preserving uint32, zeros made +0 so that
+    // -0 == +0), then the lowest expert id among the lanes holding it
+    const float cv = bv == 0.0f ? 0.0f : bv;
+    const uint32_t ub = __float_as_uint(cv);
+    const uint32_t key = (ub & 0x80000000u) ? ~ub : (ub | 0x80000000u);
+    const uint32_t kmax = wave_max_u32_uniform(key);
+    be = (int)~wave_max_u32_uniform(key == kmax ? ~(uint32_t)be : 0u);
+    bv = __uint_as_float((kmax & 0x80000000u) ? (kmax & 0x7fffffffu) : ~kmax);
     if ((be % kWave) == lane) avail &= ~(1u << (be / kWave));
     if (lane == j) {
       selv = bv;

@@ -311,6 +311,34 @@ def test_grouped_gemm_mfma_tile_shapes(tile, monkeypatch):
         assert rel_fro(got, want) < 1e-5
 
 
+@pytest.mark.parametrize("ksplit", ["2", "4"])
+@pytest.mark.parametrize("mode", [ops.W4A16, ops.W4A4])
+def test_grouped_gemm_stream_split_k(ksplit, mode, monkeypatch):
+    """The small-M kernel with K split into window-aligned slices (the decode regime at a
+    handful of tokens): ragged last window, 0-row experts, > 32 rows (two passes), gather."""
+    say("gemm stream split-k", ksplit, mode)
+    monkeypatch.setenv("NVFP4MOE_FORCE_PATH", "stream")
+    monkeypatch.setenv("NVFP4MOE_STREAM_KSPLIT", ksplit)
+    d = _problem([3, 0, 40, 1, 9], 256, 3168, seed=int(ksplit) + 100 * mode, mode=mode, T=30, k=2)
+    t = lambda a: torch.from_numpy(a).to(DEV)
+    for epi in (ops.EPI_NONE, ops.EPI_SWIGLU):
+        want = omoe.grouped_gemm(d["A"], d["offsets"], d["W"], "swiglu" if epi else "none")
+        got = _run_gemm(d, mode, epi, torch.float32)
+        assert ops.last_dispatch() == ops.PATH_STREAM
+        assert_finite(got)
+        assert rel_fro(got, want) < 1e-5
+    kw = dict(rows=d["rows"], gather_index=d["gidx"].to(DEV), gather_div=d["gdiv"], out_dtype=torch.float32,
+              want_amax=True)
+    a = d["a"].to(DEV)
+    if mode == ops.W4A4:
+        a = d["aq"]
+        kw.update(a_scales=d["as_"], a_g=d["ag"])
+    out, amax = ops.moe_grouped_gemm_nvfp4(mode, ops.EPI_SWIGLU, a, d["wt"], t(d["offsets"]), t(d["active"]),
+                                           t(d["n_active"]), **kw)
+    torch.cuda.synchronize()
+    assert np_(amax)[0] == np.abs(np_(out)).max()
+
+
 @pytest.mark.parametrize("ksplit", ["1", "2", "3"])
 @pytest.mark.parametrize("mode", [ops.W4A16, ops.W4A4])
 def test_grouped_gemm_mfma_split_k(ksplit, mode, monkeypatch):
