@@ -341,8 +341,8 @@ template <int WAVES, int WDEPTH, bool SWIGLU>
 hipError_t launch_cfg(const GemmArgs& a, int max_mtiles, hipStream_t stream) {
   const auto kern = &gemm_large_kernel<WAVES, WDEPTH, SWIGLU>;
   const size_t shmem = (size_t)kSlots * kSlot;
-  static const hipError_t attr = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
+  static std::atomic<uint64_t> attr_done{0};
+  const hipError_t attr = ensure_dynamic_lds(reinterpret_cast<const void*>(kern), (int)shmem, attr_done);
   if (attr != hipSuccess) return attr;
   mtile_schedule_kernel<<<1, 1024, 0, stream>>>(a.expert_offsets, a.active, a.n_active, a.E, 16 * kTBM,
                                                 max_mtiles, const_cast<int*>(a.sched_e),

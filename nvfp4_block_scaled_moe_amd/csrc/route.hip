@@ -7,7 +7,9 @@
 // Alternative"): rows of one expert become contiguous so each expert runs one GEMM.
 //
 // Router: one wavefront per token. Each lane holds E/64 logits in registers; k rounds of
-// a wave-wide arg-max (ties to the lower id) pick the experts. The weights
+// a wave-wide arg-max (ties to the lower id) pick the experts. The arg-max is two DPP
+// max-reductions (no LDS round trips): of the value as an order-preserving uint32, then,
+// among the lanes holding that value, of the complemented expert id. The weights
 // exp(l_j - l_max) / sum_j' exp(l_j' - l_max) over the k kept logits equal softmax over E
 // followed by renormalisation; they are computed in float64 and rounded once.
 //
@@ -22,8 +24,6 @@
 //      Slots therefore land in ascending order within each expert: a stable counting sort.
 #include "common.h"
 #include "kernels.h"
-
-#include <mutex>
 
 namespace nvfp4moe {
 
@@ -188,8 +188,6 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(const int* __rest
   }
 }
 
-std::once_flag g_perm_attr_once;
-hipError_t g_perm_attr_err = hipSuccess;
 
 }  // namespace
 
@@ -210,12 +208,11 @@ hipError_t launch_route_permute(const float* logits, int T, int E, int k, int* t
   else
     router_kernel<16><<<rgrid, kRouterWaves * kWave, 0, stream>>>(logits, T, E, k, topk_ids, topk_w);
 
-  std::call_once(g_perm_attr_once, [] {
-    g_perm_attr_err = hipFuncSetAttribute(reinterpret_cast<const void*>(&permute_kernel),
-                                          hipFuncAttributeMaxDynamicSharedMemorySize,
-                                          (kPermWaves * kMaxExperts + 2 * kPermWaves) * (int)sizeof(int));
-  });
-  if (g_perm_attr_err != hipSuccess) return g_perm_attr_err;
+  static std::atomic<uint64_t> perm_attr_done{0};
+  const hipError_t attr = ensure_dynamic_lds(reinterpret_cast<const void*>(&permute_kernel),
+                                             (kPermWaves * kMaxExperts + 2 * kPermWaves) * (int)sizeof(int),
+                                             perm_attr_done);
+  if (attr != hipSuccess) return attr;
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
   const size_t shmem = (size_t)(kPermWaves * E + 2 * kPermWaves) * sizeof(int);
