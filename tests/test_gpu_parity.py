@@ -157,6 +157,25 @@ def test_route_permute_bit_exact(T, E, k, zipf):
     assert np.array_equal(act[:na], perm["active"]) and np.all(act[na:] == -1)
 
 
+@pytest.mark.parametrize("router", ["sort", "wave"])
+@pytest.mark.parametrize("T,E,k", [(5, 64, 64), (3, 100, 7), (300, 512, 22), (2, 1024, 64)])
+def test_both_routers_bit_exact(router, T, E, k, monkeypatch):
+    """Both router kernels (workgroup sort for few tokens, wave select for many) against
+    the oracle, each forced on shapes the size rule would give to the other; ties planted."""
+    say("router", router, T, E, k)
+    monkeypatch.setenv("NVFP4MOE_ROUTER", router)
+    lg = inputs.random_fp32((T, E), T * 31 + E)
+    lg[0, : min(E, 8)] = 1.5                    # equal logits at the top of row 0
+    if E > 40:
+        lg[-1, 40] = -0.0
+        lg[-1, 3] = 0.0
+    r = ops.moe_route_permute(lg.to(DEV), k)
+    torch.cuda.synchronize()
+    ids, w = omoe.route(lg.numpy(), k)
+    assert np.array_equal(np_(r["topk_ids"]), ids)
+    np.testing.assert_allclose(np_(r["topk_w"]), w, rtol=1e-6, atol=0)
+
+
 def test_route_permute_is_deterministic():
     say("route determinism")
     wl = inputs.WORKLOADS["prefill"]
