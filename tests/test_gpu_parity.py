@@ -257,6 +257,24 @@ def test_grouped_gemm_w4a16(counts, Nw, K, epi):
     assert rel_fro(got16, omoe.bf16_round(want)) <= W4A16_TOL
 
 
+@pytest.mark.parametrize("path", ["stream", "mfma"])
+def test_grouped_gemm_max_experts(path, monkeypatch):
+    """E = 1024 (the API maximum), most experts empty, a few with 1..300 rows; the active list
+    and the device m-tile schedule then span the whole expert range."""
+    say("gemm 1024 experts", path)
+    monkeypatch.setenv("NVFP4MOE_FORCE_PATH", path)
+    rng = np.random.default_rng(1024)
+    counts = [0] * 1024
+    for e, c in zip(rng.choice(1024, size=40, replace=False), rng.integers(1, 300, size=40)):
+        counts[int(e)] = int(c)
+    counts[1023] = 5
+    d = _problem(counts, 256, 64, seed=77)
+    want = omoe.grouped_gemm(d["A"], d["offsets"], d["W"], "swiglu")
+    got = _run_gemm(d, ops.W4A16, ops.EPI_SWIGLU, torch.float32)
+    assert ops.last_dispatch() == (ops.PATH_MFMA if path == "mfma" else ops.PATH_STREAM)
+    assert rel_fro(got, want) < 1e-5
+
+
 def test_grouped_gemm_w4a16_gather():
     say("gemm gather")
     d = _problem([7, 0, 30, 9], 128, 256, seed=5, T=20, k=3)
