@@ -16,8 +16,9 @@
 // logical k 32g+8j..+7, so the four lane groups of one token read 64 contiguous bytes per
 // load instruction (one cache line instead of four).
 //
-// One workgroup per row (bf16 input): pass 1 finds the row's finite amax, pass 2 converts (the row is
-// re-read from L2). Traffic: 2 bytes read + 2 bytes written per element.
+// One workgroup per row (bf16 input): the row is read once into registers (K up to 32768; longer
+// rows are read twice), its finite amax reduced, then converted. Traffic: 2 bytes read + 2 bytes
+// written per element.
 #include "common.h"
 #include "kernels.h"
 
@@ -27,10 +28,69 @@ namespace {
 
 constexpr int kPrepThreads = 256;
 
+// VPT = 16-byte vectors held per thread (K <= 8 * kPrepThreads * VPT): the row is read once
+// into registers, its amax reduced, then converted from the registers.
+template <int VPT>
 __global__ __launch_bounds__(kPrepThreads) void act_prep_kernel(const uint16_t* __restrict__ a,
                                                                 int K,
                                                                 _Float16* __restrict__ a16,
                                                                 int* __restrict__ rexp) {
+  const int64_t r = blockIdx.x;
+  const int K128 = (K + 127) & ~127;
+  const uint16_t* row = a + r * (int64_t)K;
+  _Float16* orow = a16 + r * (int64_t)K128;
+  const int nvec = K / 8;
+  uint4 q[VPT];
+  float m = 0.0f;
+#pragma unroll
+  for (int v = 0; v < VPT; ++v) {
+    const int i = threadIdx.x + v * kPrepThreads;
+    q[v] = i < nvec ? *reinterpret_cast<const uint4*>(row + 8 * i) : make_uint4(0u, 0u, 0u, 0u);
+    const uint32_t w[4] = {q[v].x, q[v].y, q[v].z, q[v].w};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float lo = fabsf(bf16_to_f32(w[j] & 0xffffu)), hi = fabsf(bf16_to_f32(w[j] >> 16));
+      m = fmaxf(m, lo <= 3.402823466e38f ? lo : 0.0f);
+      m = fmaxf(m, hi <= 3.402823466e38f ? hi : 0.0f);
+    }
+  }
+  __shared__ float red[kPrepThreads / kWave];
+  m = wave_max(m);
+  if ((threadIdx.x % kWave) == 0) red[threadIdx.x / kWave] = m;
+  __syncthreads();
+  float amax = red[0];
+  for (int w = 1; w < kPrepThreads / kWave; ++w) amax = fmaxf(amax, red[w]);
+  int p = 0;
+  if (amax > 0.0f) {
+    int ex;
+    (void)frexpf(amax, &ex);  // amax = f * 2^ex, f in [0.5, 1)
+    p = ex - 15;              // amax * 2^-p in [2^14, 2^15)
+  }
+  if (threadIdx.x == 0) rexp[r] = p;
+#pragma unroll
+  for (int v = 0; v < VPT; ++v) {
+    const int i = threadIdx.x + v * kPrepThreads;
+    if (i < K128 / 8) {
+      f16x8 o;
+      const uint32_t w[4] = {q[v].x, q[v].y, q[v].z, q[v].w};   // zeros past K
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        o[2 * j] = (_Float16)ldexpf(bf16_to_f32(w[j] & 0xffffu), -p);
+        o[2 * j + 1] = (_Float16)ldexpf(bf16_to_f32(w[j] >> 16), -p);
+      }
+      // piece i = 16 c + 4 g + j (logical k = 128 c + 32 g + 8 j) -> physical 16 c + 4 j + g
+      const int c = i >> 4, g = (i >> 2) & 3, jj = i & 3;
+      *reinterpret_cast<f16x8*>(orow + 8 * (16 * c + 4 * jj + g)) = o;
+    }
+  }
+}
+
+// Rows too long for registers: pass 1 finds the amax, pass 2 re-reads the row (from L2) and
+// converts.
+__global__ __launch_bounds__(kPrepThreads) void act_prep_loop_kernel(const uint16_t* __restrict__ a,
+                                                                     int K,
+                                                                     _Float16* __restrict__ a16,
+                                                                     int* __restrict__ rexp) {
   const int64_t r = blockIdx.x;
   const int K128 = (K + 127) & ~127;
   const uint16_t* row = a + r * (int64_t)K;
@@ -125,7 +185,13 @@ hipError_t launch_act_prep_fp4(const uint8_t* packed, const uint8_t* scales, int
 
 hipError_t launch_act_prep(const uint16_t* a, int64_t rows, int K, _Float16* a16, int* rexp,
                            hipStream_t stream) {
-  act_prep_kernel<<<(unsigned)rows, kPrepThreads, 0, stream>>>(a, K, a16, rexp);
+  // vectors per thread covering K128 / 8 pieces (padding pieces are written as zeros)
+  const int need = ((K + 127) / 128 * 16 + kPrepThreads - 1) / kPrepThreads;
+  if (need <= 2) act_prep_kernel<2><<<(unsigned)rows, kPrepThreads, 0, stream>>>(a, K, a16, rexp);
+  else if (need <= 4) act_prep_kernel<4><<<(unsigned)rows, kPrepThreads, 0, stream>>>(a, K, a16, rexp);
+  else if (need <= 8) act_prep_kernel<8><<<(unsigned)rows, kPrepThreads, 0, stream>>>(a, K, a16, rexp);
+  else if (need <= 16) act_prep_kernel<16><<<(unsigned)rows, kPrepThreads, 0, stream>>>(a, K, a16, rexp);
+  else act_prep_loop_kernel<<<(unsigned)rows, kPrepThreads, 0, stream>>>(a, K, a16, rexp);
   return hipGetLastError();
 }
 

@@ -238,6 +238,8 @@ GEMM_CASES = [
     ([1] * 8, 256, 512),
     ([12, 20], 96, 6144),
     ([1, 2, 3], 2048, 6144),
+    ([2, 1], 64, 32768),            # longest row the bf16 prep holds in registers
+    ([3, 5], 64, 32800),            # longer rows: the two-pass prep, K % 128 != 0
 ]
 
 
