@@ -29,6 +29,14 @@ __device__ __forceinline__ uint32_t ld16(__amdgpu_buffer_rsrc_t r, uint32_t voff
   return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
 }
 
+// Read of a kernel input that stays constant while the kernel runs, through the constant
+// address space: a wave-uniform read then becomes a scalar load, whose wait does not hold up
+// the vector-memory queue (a vector load's wait also waits for every load issued before it).
+template <typename T>
+__device__ __forceinline__ T ld_const(const T* p, int64_t i) {
+  return ((const __attribute__((address_space(4))) T*)p)[i];
+}
+
 // Epilogue of one wave's tile: RBW blocks of 16 weight rows x TBM blocks of 16 GEMM rows,
 // with MFMA 16x16 output layout (lane l holds weight rows 4*(l/16)+i of each block, GEMM
 // row l%16 of each token block). GEMM rows tc .. tc+16*ntb-1 of the expert (those < M) are
@@ -36,10 +44,11 @@ __device__ __forceinline__ uint32_t ld16(__amdgpu_buffer_rsrc_t r, uint32_t voff
 // scale (W4A16) or 0; with SwiGLU the first RBW/2 blocks are gate rows and the others the
 // matching up rows, and silu(gate) * up is written to column blkrow(b) of the F-wide output.
 // Returns the running max of |written value| as float bits.
+// pexp[tb] is the power-of-two exponent of the lane's GEMM row in token block tb.
 template <int RBW, int TBM, bool SWIGLU, typename BlkRow>
-__device__ __forceinline__ uint32_t store_tile(const GemmArgs& p, const f32x4 (&acc)[RBW][TBM], int tc,
-                                               int ntb, int M, int r0, float alpha, bool row_exp,
-                                               BlkRow blkrow, int lane, uint32_t amax_bits) {
+__device__ __forceinline__ uint32_t store_tile_exp(const GemmArgs& p, const f32x4 (&acc)[RBW][TBM], int tc,
+                                                   int ntb, int M, int r0, float alpha, const int (&pexps)[TBM],
+                                                   BlkRow blkrow, int lane, uint32_t amax_bits) {
   const int l16 = lane & 15, g = lane >> 4;
   const int Nw = p.Nw, F = Nw >> 1;
 #pragma unroll
@@ -47,7 +56,7 @@ __device__ __forceinline__ uint32_t store_tile(const GemmArgs& p, const f32x4 (&
     const int t = tc + 16 * tb + l16;
     if (tb < ntb && t < M) {
       const int row = r0 + t;
-      const int pexp = row_exp ? p.rexp[p.gather_index ? p.gather_index[row] / p.gather_div : row] : 0;
+      const int pexp = pexps[tb];
       if (SWIGLU) {
 #pragma unroll
         for (int b = 0; b < RBW / 2; ++b) {
@@ -88,6 +97,27 @@ __device__ __forceinline__ uint32_t store_tile(const GemmArgs& p, const f32x4 (&
     }
   }
   return amax_bits;
+}
+
+// Power-of-two exponent of each of the lane's GEMM rows (0 without row scales or past M).
+template <int TBM>
+__device__ __forceinline__ void row_exponents(const GemmArgs& p, int tc, int M, int r0, bool row_exp, int lane,
+                                              int (&pexps)[TBM]) {
+#pragma unroll
+  for (int tb = 0; tb < TBM; ++tb) {
+    const int t = tc + 16 * tb + (lane & 15);
+    const int row = r0 + t;
+    pexps[tb] = row_exp && t < M ? p.rexp[p.gather_index ? p.gather_index[row] / p.gather_div : row] : 0;
+  }
+}
+
+template <int RBW, int TBM, bool SWIGLU, typename BlkRow>
+__device__ __forceinline__ uint32_t store_tile(const GemmArgs& p, const f32x4 (&acc)[RBW][TBM], int tc,
+                                               int ntb, int M, int r0, float alpha, bool row_exp,
+                                               BlkRow blkrow, int lane, uint32_t amax_bits) {
+  int pexps[TBM];
+  row_exponents<TBM>(p, tc, M, r0, row_exp, lane, pexps);
+  return store_tile_exp<RBW, TBM, SWIGLU>(p, acc, tc, ntb, M, r0, alpha, pexps, blkrow, lane, amax_bits);
 }
 
 // Wave-reduced amax of the tile, merged into *out_amax (float bits of non-negative values

@@ -58,43 +58,39 @@ struct Ring {
 };
 
 template <int RBW, int WAVES, int TBM, int WDEPTH, int BDEPTH, bool SWIGLU, bool A4>
-__global__ __launch_bounds__(WAVES* kWave) void gemm_stream_kernel(const GemmArgs p, int tiles_per_expert,
-                                                                   int tiles_per_split, int total_tiles) {
+__global__ __launch_bounds__(WAVES* kWave) void gemm_stream_kernel(const GemmArgs p, int tiles_per_expert) {
   static_assert(RBW % 2 == 0, "row blocks per wave come in pairs");
   static_assert(kWin % WDEPTH == 0 && kWin % BDEPTH == 0, "ring depths divide the scale window");
+  static_assert(WDEPTH <= 2 && BDEPTH <= 2, "the next item's rows are ready from step kWin - 2 on");
   using R = Ring<TBM, A4>;
   constexpr int NT = WAVES * kWave;
+  constexpr int TROWS = 16 * TBM;               // GEMM rows per item
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  unsigned char* ring = smem;                   // [2][R::kSlot]
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g = lane >> 4;
-  const int per_xcd = gridDim.x >> 3;
-  const int tile = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
-  if (tile >= total_tiles) return;
-  const int ks = tile / tiles_per_split;           // K slice
-  const int et = tile - ks * tiles_per_split;
-  const int aidx = et / tiles_per_expert;          // active-expert slot
-  const int nb = et - aidx * tiles_per_expert;     // row tile
-  if (aidx >= p.n_active[0]) return;
-  const int e = p.active[aidx];
-  const int r0 = p.expert_offsets[e];
-  const int M = p.expert_offsets[e + 1] - r0;
   const int K = p.K, Nw = p.Nw, Kh = K >> 1, Ks = K >> 4;
   const int K128 = (K + 127) & ~127;
   const int F = Nw >> 1;
   const int nch = (K + kChunk - 1) / kChunk;
   const int nwin = (nch + kWin - 1) / kWin;
-  // K slice ks: whole scale windows [wlo, whi), chunks [wlo * kWin, chi)
-  const int wps = (nwin + p.ksplit - 1) / p.ksplit;
-  const int wlo = ks * wps, whi = min(nwin, wlo + wps);
-  if (wlo >= whi) return;
-  const int chi = min(nch, whi * kWin);
+  const int wps = (nwin + p.ksplit - 1) / p.ksplit;   // scale windows per K slice
 
-  unsigned char* ring = smem;                                           // [2][R::kSlot]
+  // One tile (K slice, active expert, row tile) per workgroup. The tiles of the experts that
+  // are actually active (known only here) are numbered slice-major, expert-major and split
+  // into 8 equal ranges, one per XCD (workgroup i runs on XCD i mod 8), so every XCD gets an
+  // equal share however few experts are active, and the tiles in flight on one XCD are
+  // neighbours that share their experts' activation rows in its L2.
+  const int per_split = ld_const(p.n_active, 0) * tiles_per_expert;
+  const int ntiles = per_split * p.ksplit;
+  const int per_xcd = (ntiles + 7) >> 3;
+  const int tile = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
+  if ((int)(blockIdx.x >> 3) >= per_xcd || tile >= ntiles) return;
 
-  // First row of this wave's block b (the lane adds l16).
-  auto blkrow = [&](int b) -> int {
+  // First row of block b of this wave in row tile nb (the lane adds l16).
+  auto blkrow = [&](int nb, int b) -> int {
     if (SWIGLU) {
       constexpr int hb = RBW / 2;
       const int gate0 = (nb * WAVES + wave) * 16 * hb;
@@ -103,21 +99,18 @@ __global__ __launch_bounds__(WAVES* kWave) void gemm_stream_kernel(const GemmArg
     return (nb * WAVES + wave) * 16 * RBW + 16 * b;
   };
   // Tiled weights: 1 KB per (16-row block, chunk) of codes and per (16-row block, window)
-  // of scales; lane l reads the 16 bytes at 16 l of a tile.
+  // of scales; lane l reads the 16 bytes at 16 l of a tile. The block offsets inside a row
+  // tile are the same for every tile.
   const uint32_t wbytes = (uint32_t)(Nw / 16) * (uint32_t)nch * 1024u;
   const uint32_t sbytes = (uint32_t)(Nw / 16) * (uint32_t)nwin * 1024u;
-  const __amdgpu_buffer_rsrc_t wr = make_rsrc(p.w_packed + (size_t)e * wbytes, wbytes);
-  const __amdgpu_buffer_rsrc_t sr = make_rsrc(p.w_scales + (size_t)e * sbytes, sbytes);
-  const uint32_t wlane = (uint32_t)(blkrow(0) / 16) * (uint32_t)nch * 1024u + 16u * lane;
-  const uint32_t slane = (uint32_t)(blkrow(0) / 16) * (uint32_t)nwin * 1024u + 16u * lane;
+  const uint32_t vlane = 16u * lane;
   uint32_t wsoff[RBW], ssoff[RBW];
 #pragma unroll
   for (int b = 0; b < RBW; ++b) {
-    wsoff[b] = __builtin_amdgcn_readfirstlane((uint32_t)((blkrow(b) - blkrow(0)) / 16) * (uint32_t)nch * 1024u);
-    ssoff[b] = __builtin_amdgcn_readfirstlane((uint32_t)((blkrow(b) - blkrow(0)) / 16) * (uint32_t)nwin * 1024u);
+    const uint32_t blk = (uint32_t)((blkrow(0, b) - blkrow(0, 0)) / 16);
+    wsoff[b] = __builtin_amdgcn_readfirstlane(blk * (uint32_t)nch * 1024u);
+    ssoff[b] = __builtin_amdgcn_readfirstlane(blk * (uint32_t)nwin * 1024u);
   }
-  const float alpha = A4 ? p.w_g[e] * p.a_g[0] : p.w_g[e];
-
   __amdgpu_buffer_rsrc_t ar, asr;
   if (A4) {
     ar = make_rsrc(p.a_packed, (uint32_t)p.a_rows * (uint32_t)Kh);
@@ -127,197 +120,296 @@ __global__ __launch_bounds__(WAVES* kWave) void gemm_stream_kernel(const GemmArg
     asr = ar;
   }
 
+  // The tile: K slice ks (whole scale windows [wlo, whi), chunks [wlo * kWin, chi)), expert e
+  // with GEMM rows r0 .. r0+M-1, row tile nb. All wave-uniform.
+  const int ks = tile / per_split;
+  const int aidx = (tile - ks * per_split) / tiles_per_expert;
+  const int nb = tile - ks * per_split - aidx * tiles_per_expert;
+  const int e = ld_const(p.active, aidx);
+  const int r0 = ld_const(p.expert_offsets, e);
+  const int M = ld_const(p.expert_offsets, e + 1) - r0;
+  const int wlo = ks * wps, whi = min(nwin, wlo + wps);
+  const int clo = wlo * kWin, chi = min(nch, whi * kWin);
+  const __amdgpu_buffer_rsrc_t wr = make_rsrc(p.w_packed + (size_t)e * wbytes, wbytes);
+  const __amdgpu_buffer_rsrc_t sr = make_rsrc(p.w_scales + (size_t)e * sbytes, sbytes);
+  const uint32_t wb = __builtin_amdgcn_readfirstlane((uint32_t)(blkrow(nb, 0) / 16) * (uint32_t)nch * 1024u);
+  const uint32_t sb = __builtin_amdgcn_readfirstlane((uint32_t)(blkrow(nb, 0) / 16) * (uint32_t)nwin * 1024u);
+
   // Activation staging roles: thread -> (token, 16-byte piece) of a chunk slice.
   constexpr int TPT = A4 ? 4 : 16;             // threads per token
   constexpr int TPR = NT / TPT;                // tokens per round
-  constexpr int ROUNDS = (16 * TBM + TPR - 1) / TPR;
-
-  uint32_t amax_bits = 0;
-  for (int tc = 0; tc < M; tc += 16 * TBM) {
-    const int ntb = __builtin_amdgcn_readfirstlane(min(TBM, (M - tc + 15) >> 4));
-    uint32_t bsrc[ROUNDS], bdst[ROUNDS], bssrc[ROUNDS], bsdst[ROUNDS];
+  constexpr int ROUNDS = (TROWS + TPR - 1) / TPR;
+  const int pc = tid % TPT;                    // 16-byte piece of the token's slice
+  uint32_t bdst[ROUNDS], bsdst[ROUNDS];
+#pragma unroll
+  for (int rr = 0; rr < ROUNDS; ++rr) {
+    const int tk = rr * TPR + tid / TPT;
+    bdst[rr] = tk >= TROWS ? kNoDst
+               : A4        ? tk * R::kTokBytes + 16 * (pc ^ (tk & 3))
+                           : tk * R::kTokBytes + 16 * (pc ^ (tk & 15));
+    bsdst[rr] = (A4 && tk < TROWS && pc == 0) ? R::kCodes + tk * 8 : kNoDst;
+  }
+  // Source offsets of this thread's staging pieces for an item, from the activation row of
+  // each of its tokens (arow < 0: no such row).
+  auto stage_src = [&](const int (&arow)[ROUNDS], uint32_t (&src)[ROUNDS], uint32_t (&ssrc)[ROUNDS]) {
 #pragma unroll
     for (int rr = 0; rr < ROUNDS; ++rr) {
-      const int tk = rr * TPR + tid / TPT;       // token within the pass
-      const int pc = tid % TPT;                  // 16-byte piece of the token's slice
-      const int t = tc + tk;
-      const bool ok = tk < 16 * TBM && t < M;
-      const uint32_t arow = ok ? (uint32_t)(p.gather_index ? p.gather_index[r0 + t] / p.gather_div : r0 + t) : 0u;
-      bssrc[rr] = kOOB;
-      bsdst[rr] = kNoDst;
+      const bool ok = arow[rr] >= 0;
+      const uint32_t a = (uint32_t)arow[rr];
       if (A4) {
-        bsrc[rr] = ok ? arow * (uint32_t)Kh + 16 * pc : kOOB;
-        bdst[rr] = tk * R::kTokBytes + 16 * (pc ^ (tk & 3));
-        if (tk < 16 * TBM && pc == 0) {   // one thread per token also stages its 8 scale bytes
-          bssrc[rr] = ok ? arow * (uint32_t)Ks : kOOB;
-          bsdst[rr] = R::kCodes + tk * 8;
-        }
+        src[rr] = ok ? a * (uint32_t)Kh + 16 * pc : kOOB;
+        ssrc[rr] = ok && pc == 0 ? a * (uint32_t)Ks : kOOB;
       } else {
-        bsrc[rr] = ok ? (arow * (uint32_t)K128 + 8 * pc) * 2 : kOOB;
-        bdst[rr] = tk * R::kTokBytes + 16 * (pc ^ (tk & 15));
+        src[rr] = ok ? (a * (uint32_t)K128 + 8 * pc) * 2 : kOOB;
+        ssrc[rr] = kOOB;
       }
-      if (tk >= 16 * TBM) bdst[rr] = kNoDst;
     }
+  };
+  // Activation row of each staging token of the pass starting at GEMM row tc of the tile's
+  // expert (-1 past its rows). The gather read is unconditional (row r0 when not needed) so
+  // that no branch splits the wait for it.
+  auto stage_rows = [&](int tc, int (&arow)[ROUNDS]) {
+#pragma unroll
+    for (int rr = 0; rr < ROUNDS; ++rr) {
+      const int tk = rr * TPR + tid / TPT;
+      const bool ok = tk < TROWS && tc + tk < M;
+      const int row = r0 + (ok ? tc + tk : 0);
+      const int src = p.gather_index ? p.gather_index[row] : row;
+      arow[rr] = ok ? src : -1;
+    }
+  };
+  auto source_rows = [&](int (&grow)[ROUNDS]) {
+    if (p.gather_index) {
+#pragma unroll
+      for (int rr = 0; rr < ROUNDS; ++rr) grow[rr] = grow[rr] >= 0 ? grow[rr] / p.gather_div : -1;
+    }
+  };
 
-    f32x4 acc[RBW][TBM];
+  // Register rings: activations (BDEPTH staging sets, committed to a two-slot LDS ring),
+  // weight codes (WDEPTH chunks) and weight scales (current and next window).
+  u32x4 bst[BDEPTH][ROUNDS];
+  uint32_t bsc[BDEPTH][ROUNDS][2];
+  u32x4 wring[WDEPTH][RBW];
+  u32x4 scur[RBW], snext[RBW];
+  // f16 rows are zero-padded to whole chunks; FP4 rows are not, so W4A4 pieces and scale
+  // pairs past K read zero (a neighbouring row's NaN scale must not leak in).
+  // A round whose tokens are all past the item's rows (16 * TPR * rr >= rows, wave-uniform)
+  // is neither loaded nor committed.
+  auto round_used = [&](int rr, int rows) { return rr == 0 || rr * TPR < rows; };
+  auto b_issue = [&](int set, const uint32_t (&src)[ROUNDS], const uint32_t (&ssrc)[ROUNDS], int rows, bool cin,
+                     int c) {
+    const int kc = c * kChunk;
+#pragma unroll
+    for (int rr = 0; rr < ROUNDS; ++rr) {
+      const bool in = A4 ? cin && (kc + 32 * pc) < K : cin;
+      const uint32_t step = A4 ? (uint32_t)kc / 2 : (uint32_t)kc * 2;
+      if (round_used(rr, rows)) bst[set][rr] = ld128(ar, in ? src[rr] + step : kOOB, 0);
+    }
+    if (A4) {
+#pragma unroll
+      for (int rr = 0; rr < ROUNDS; ++rr) {
+        if (!round_used(rr, rows)) continue;
+        const uint32_t so = ssrc[rr] + (uint32_t)kc / 16;
+        uint32_t v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = ld16(asr, (cin && kc + 32 * q < K) ? so : kOOB, 2 * q);
+        bsc[set][rr][0] = v[0] | (v[1] << 16);
+        bsc[set][rr][1] = v[2] | (v[3] << 16);
+      }
+    }
+  };
+  auto b_commit = [&](int set, int rows, int slot) {
+    unsigned char* base = ring + slot * R::kSlot;
+#pragma unroll
+    for (int rr = 0; rr < ROUNDS; ++rr)
+      if (round_used(rr, rows) && bdst[rr] != kNoDst) *reinterpret_cast<u32x4*>(base + bdst[rr]) = bst[set][rr];
+    if (A4) {
+#pragma unroll
+      for (int rr = 0; rr < ROUNDS; ++rr)
+        if (round_used(rr, rows) && bsdst[rr] != kNoDst)
+          *reinterpret_cast<uint2*>(base + bsdst[rr]) = make_uint2(bsc[set][rr][0], bsc[set][rr][1]);
+    }
+  };
+  // Scales: one 16-byte load per block and window holds the lane's two scale bytes for
+  // each of the window's 8 chunks.
+  auto s_issue = [&](const __amdgpu_buffer_rsrc_t& sr, uint32_t voff, uint32_t sbase) {
+#pragma unroll
+    for (int b = 0; b < RBW; ++b) snext[b] = ld128(sr, voff, sbase + ssoff[b]);
+  };
+  f32x4 acc[RBW][TBM];
+  // Chunk c (u = c % kWin): decode ring entry d, refill it from offset voff, then the
+  // MFMAs, k-step-major so that consecutive MFMAs update different accumulators and the
+  // activation fragments are read once per k-step.
+  // Chunk c (u = c % kWin): decode ring entry d, refill it from offset voff, then the
+  // MFMAs of token block 0 and, if the item has more than 16 rows (`two`, wave-uniform),
+  // of token block 1; k-step-major inside a block, so that consecutive MFMAs update
+  // different accumulators.
+  auto compute = [&](bool two, int d, int c, int u, uint32_t voff) {
+    static_assert(TBM == 2, "token blocks 0 and 1");
+    u32x4 (&wv)[RBW] = wring[d];
+    const unsigned char* base = ring + (c & 1) * R::kSlot;
+    f16x8 wf[RBW][4];
+#pragma unroll
+    for (int b = 0; b < RBW; ++b) {
+      const uint32_t sv = scur[b][u >> 1] >> (16 * (u & 1));   // scales of k past K are 0
+      f16x2 s0, s1;
+      decode_scale_pair(sv, s0, s1);
+      wf[b][0] = decode8(wv[b][0], s0);
+      wf[b][1] = decode8(wv[b][1], s0);
+      wf[b][2] = decode8(wv[b][2], s1);
+      wf[b][3] = decode8(wv[b][3], s1);
+      wv[b] = ld128(wr, voff, wb + wsoff[b]);   // this ring entry is free again
+    }
+    auto block = [&](int tb) {
+      const int tk = 16 * tb + l16;
+      u32x4 aq;
+      f16x2 as0, as1;
+      if (A4) {
+        aq = *reinterpret_cast<const u32x4*>(base + tk * R::kTokBytes + 16 * (g ^ (tk & 3)));
+        decode_scale_pair(*reinterpret_cast<const uint16_t*>(base + R::kCodes + tk * 8 + 2 * g), as0, as1);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const f16x8 bj = A4 ? decode8(aq[j], j < 2 ? as0 : as1)
+                            : *reinterpret_cast<const f16x8*>(base + tk * R::kTokBytes + 16 * ((4 * j + g) ^ (tk & 15)));
+#pragma unroll
+        for (int b = 0; b < RBW; ++b)
+          acc[b][tb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf[b][j], bj, acc[b][tb], 0, 0, 0);
+      }
+    };
+    block(0);
+    if (two) block(1);
+  };
+
+  // First pass: its rows, then the scales of the first window and the first chunks.
+  uint32_t bsrc[ROUNDS], bssrc[ROUNDS];
+  {
+    int arow[ROUNDS];
+    stage_rows(0, arow);
+    source_rows(arow);
+    stage_src(arow, bsrc, bssrc);
+    s_issue(sr, vlane + (uint32_t)wlo * 1024u, sb);
+#pragma unroll
+    for (int b = 0; b < RBW; ++b) scur[b] = snext[b];
+#pragma unroll
+    for (int d = 0; d < (WDEPTH > BDEPTH ? WDEPTH : BDEPTH); ++d) {
+      if (d < BDEPTH) b_issue(d, bsrc, bssrc, M, clo + d < chi, clo + d);
+      if (d < WDEPTH) {
+#pragma unroll
+        for (int b = 0; b < RBW; ++b)
+          wring[d][b] = ld128(wr, clo + d < chi ? vlane + (uint32_t)(clo + d) * 1024u : kOOB, wb + wsoff[b]);
+      }
+    }
+    b_commit(0, M, 0);
+    __syncthreads();
+  }
+
+  // Passes over up to TROWS GEMM rows (experts with more rows take several; each re-streams
+  // the tile's weights).
+  uint32_t amax_bits = 0;
+  const float alpha = A4 ? ld_const(p.w_g, e) * ld_const(p.a_g, 0) : ld_const(p.w_g, e);
+  auto blk = [&](int b) { return blkrow(nb, b); };
+  for (int tc = 0;; tc += TROWS) {
 #pragma unroll
     for (int b = 0; b < RBW; ++b)
 #pragma unroll
       for (int tb = 0; tb < TBM; ++tb) acc[b][tb] = (f32x4){0.f, 0.f, 0.f, 0.f};
-
-    auto kloop = [&](auto ntb_tag) {
-      constexpr int NTB = decltype(ntb_tag)::value;
-      constexpr int RND = (16 * NTB + TPR - 1) / TPR;
-      // BDEPTH staging register sets: activations of chunk c+BDEPTH are requested just
-      // before the weights of chunk c+WDEPTH. Vector-memory counters retire in issue order,
-      // so a staging set that is committed one step after its request would make the wave
-      // wait for every weight chunk requested before it; with BDEPTH == WDEPTH the commit
-      // never waits on weights. (The large-M path has more compute per chunk than a weight
-      // chunk takes to arrive and uses a shallower activation ring.)
-      u32x4 bst[BDEPTH][RND];
-      uint32_t bsc[BDEPTH][RND][2];
-      auto b_issue = [&](int set, int c) {
-        // f16 rows are zero-padded to whole chunks; FP4 rows are not, so W4A4 pieces and
-        // scale pairs past K read zero (a neighbouring row's NaN scale must not leak in).
-        const bool cin = c < chi;
-        const int kc = c * kChunk;
+    const int rows = M - tc;                // rows of the expert from tc on (> 0)
+    const bool two = rows > 16;             // token block 1 holds rows of this pass
+    const bool has_next = rows > TROWS;     // another pass follows
+    const int nrows = has_next ? rows - TROWS : 0;
+    // Every window but the last: chunk c uses LDS slot c & 1, staging set c % BDEPTH and
+    // weight ring entry c % WDEPTH (windows start at multiples of kWin); chunks past K read
+    // zero.
+    for (int c0 = clo; c0 < (whi - 1) * kWin; c0 += kWin) {
+      s_issue(sr, vlane + (uint32_t)(c0 / kWin + 1) * 1024u, sb);
 #pragma unroll
-        for (int rr = 0; rr < RND; ++rr) {
-          const bool in = A4 ? cin && (kc + 32 * (tid % TPT)) < K : cin;
-          const uint32_t step = A4 ? (uint32_t)kc / 2 : (uint32_t)kc * 2;
-          bst[set][rr] = ld128(ar, in ? bsrc[rr] + step : kOOB, 0);
+      for (int u = 0; u < kWin; ++u) {
+        const int c = c0 + u;
+        b_issue(u % BDEPTH, bsrc, bssrc, rows, c + BDEPTH < chi, c + BDEPTH);
+        compute(two, u % WDEPTH, c, u, c + WDEPTH < chi ? vlane + (uint32_t)(c + WDEPTH) * 1024u : kOOB);
+        b_commit((u + 1) % BDEPTH, rows, (c + 1) & 1);
+        if (u == kWin - 1) {
+#pragma unroll
+          for (int b = 0; b < RBW; ++b) scur[b] = snext[b];
         }
-        if (A4) {
-#pragma unroll
-          for (int rr = 0; rr < RND; ++rr) {
-            const uint32_t so = bssrc[rr] + (uint32_t)kc / 16;
-            uint32_t v[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) v[q] = ld16(asr, (cin && kc + 32 * q < K) ? so : kOOB, 2 * q);
-            bsc[set][rr][0] = v[0] | (v[1] << 16);
-            bsc[set][rr][1] = v[2] | (v[3] << 16);
-          }
-        }
-      };
-      auto b_commit = [&](int set, int slot) {
-        unsigned char* base = ring + slot * R::kSlot;
-#pragma unroll
-        for (int rr = 0; rr < RND; ++rr)
-          if (bdst[rr] != kNoDst) *reinterpret_cast<u32x4*>(base + bdst[rr]) = bst[set][rr];
-        if (A4) {
-#pragma unroll
-          for (int rr = 0; rr < RND; ++rr)
-            if (bsdst[rr] != kNoDst)
-              *reinterpret_cast<uint2*>(base + bsdst[rr]) = make_uint2(bsc[set][rr][0], bsc[set][rr][1]);
-        }
-      };
-      // Scales: one 16-byte load per block and window holds the lane's two scale bytes for
-      // each of the window's 8 chunks; the current and the next window stay in registers.
-      u32x4 scur[RBW], snext[RBW];
-      auto s_issue = [&](int w) {
-#pragma unroll
-        for (int b = 0; b < RBW; ++b) snext[b] = ld128(sr, w < whi ? slane + (uint32_t)w * 1024u : kOOB, ssoff[b]);
-      };
-      u32x4 wring[WDEPTH][RBW];
-      auto w_issue = [&](int d, int c, int b) {   // codes past K are zero in the tiles
-        wring[d][b] = ld128(wr, c < chi ? wlane + (uint32_t)c * 1024u : kOOB, wsoff[b]);
-      };
-      auto compute = [&](int d, int c, int u) {    // u = c % kWin, a constant
-        u32x4 (&wv)[RBW] = wring[d];
-        const unsigned char* base = ring + (c & 1) * R::kSlot;
-        // Decode every block of the chunk (each ring entry is re-filled right after its
-        // decode), then issue the MFMAs k-step-major so that consecutive MFMAs update
-        // different accumulators and the activation fragments are read once per k-step.
-        f16x8 wf[RBW][4];
-#pragma unroll
-        for (int b = 0; b < RBW; ++b) {
-          const uint32_t sv = scur[b][u >> 1] >> (16 * (u & 1));   // scales of k past K are 0
-          f16x2 s0, s1;
-          decode_scale_pair(sv, s0, s1);
-          wf[b][0] = decode8(wv[b][0], s0);
-          wf[b][1] = decode8(wv[b][1], s0);
-          wf[b][2] = decode8(wv[b][2], s1);
-          wf[b][3] = decode8(wv[b][3], s1);
-          w_issue(d, c + WDEPTH, b);   // this ring entry is free again
-        }
-        u32x4 aq[A4 ? NTB : 1];
-        f16x2 as0[A4 ? NTB : 1], as1[A4 ? NTB : 1];
-        if (A4) {
-#pragma unroll
-          for (int tb = 0; tb < NTB; ++tb) {
-            const int tk = 16 * tb + l16;
-            aq[tb] = *reinterpret_cast<const u32x4*>(base + tk * R::kTokBytes + 16 * (g ^ (tk & 3)));
-            decode_scale_pair(*reinterpret_cast<const uint16_t*>(base + R::kCodes + tk * 8 + 2 * g), as0[tb], as1[tb]);
-          }
-        }
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          f16x8 bj[NTB];
-#pragma unroll
-          for (int tb = 0; tb < NTB; ++tb) {
-            const int tk = 16 * tb + l16;
-            if (A4) bj[tb] = decode8(aq[tb][j], j < 2 ? as0[tb] : as1[tb]);
-            else bj[tb] = *reinterpret_cast<const f16x8*>(base + tk * R::kTokBytes + 16 * ((4 * j + g) ^ (tk & 15)));
-          }
-#pragma unroll
-          for (int b = 0; b < RBW; ++b)
-#pragma unroll
-            for (int tb = 0; tb < NTB; ++tb)
-              acc[b][tb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(wf[b][j], bj[tb], acc[b][tb], 0, 0, 0);
-        }
-      };
-
-      // prologue: scales of window 0, then activations and weights of the first chunks
-      const int clo = wlo * kWin;                   // a multiple of kWin: ring indices stay u % depth
-      s_issue(wlo);
-#pragma unroll
-      for (int b = 0; b < RBW; ++b) scur[b] = snext[b];
-#pragma unroll
-      for (int d = 0; d < (WDEPTH > BDEPTH ? WDEPTH : BDEPTH); ++d) {
-        if (d < BDEPTH) b_issue(d, clo + d);
-        if (d < WDEPTH) {
-#pragma unroll
-          for (int b = 0; b < RBW; ++b) w_issue(d, clo + d, b);
-        }
+        __syncthreads();
       }
-      b_commit(0, 0);
-      __syncthreads();
-      // Chunk c: LDS slot c&1, staging set c % BDEPTH and weight ring entry c % WDEPTH.
-      for (int c0 = clo; c0 < whi * kWin; c0 += kWin) {   // whole windows; chunks past K are zero
-        s_issue(c0 / kWin + 1);
+    }
+
+    // Last window: fetch the row scales of this pass's outputs and, if another pass follows,
+    // request its rows, its first window of scales and its first chunks, so that the ring
+    // does not drain between passes.
+    int pexps[TBM], erow[TBM], nrow[ROUNDS];
+    uint32_t nsrc[ROUNDS], nssrc[ROUNDS];
+    {
+      const int c0 = (whi - 1) * kWin;
 #pragma unroll
-        for (int u = 0; u < kWin; ++u) {
-          const int c = c0 + u;
-          b_issue(u % BDEPTH, c + BDEPTH);         // set u%BDEPTH was committed last step
-          compute(u % WDEPTH, c, u);               // requests weights of chunk c+WDEPTH
-          b_commit((u + 1) % BDEPTH, (c + 1) & 1);
-          if (u == kWin - 1) {
+      for (int u = 0; u < kWin; ++u) {
+        const int c = c0 + u;
+        if (u == 0) {
+          // activation rows of the lanes' outputs (unconditional reads, row r0 past M)
 #pragma unroll
-            for (int b = 0; b < RBW; ++b) scur[b] = snext[b];
+          for (int tb = 0; tb < TBM; ++tb) {
+            const int t = tc + 16 * tb + l16;
+            const int row = r0 + (t < M ? t : 0);
+            erow[tb] = !A4 && p.gather_index ? p.gather_index[row] : row;
           }
-          __syncthreads();
+          stage_rows(tc + TROWS, nrow);
         }
+        if (u == 2) {
+#pragma unroll
+          for (int tb = 0; tb < TBM; ++tb)
+            pexps[tb] = A4 ? 0 : p.rexp[p.gather_index ? erow[tb] / p.gather_div : erow[tb]];
+          s_issue(sr, has_next ? vlane + (uint32_t)wlo * 1024u : kOOB, sb);
+        }
+        if (u == kWin - 2) {
+          source_rows(nrow);
+          stage_src(nrow, nsrc, nssrc);
+        }
+        if (u + BDEPTH < kWin) {
+          b_issue(u % BDEPTH, bsrc, bssrc, rows, c + BDEPTH < chi, c + BDEPTH);
+        } else {
+          const int cn = clo + u + BDEPTH - kWin;
+          b_issue(u % BDEPTH, nsrc, nssrc, nrows, has_next && cn < chi, cn);
+        }
+        if (u + WDEPTH < kWin) {
+          compute(two, u % WDEPTH, c, u, c + WDEPTH < chi ? vlane + (uint32_t)(c + WDEPTH) * 1024u : kOOB);
+        } else {
+          const int cn = clo + u + WDEPTH - kWin;
+          compute(two, u % WDEPTH, c, u, has_next && cn < chi ? vlane + (uint32_t)cn * 1024u : kOOB);
+        }
+        // the set committed here holds chunk c + 1: the next pass's first chunk at u = kWin - 1
+        b_commit((u + 1) % BDEPTH, u + 1 < kWin ? rows : nrows, (c + 1) & 1);
+        if (u == kWin - 1) {
+#pragma unroll
+          for (int b = 0; b < RBW; ++b) scur[b] = snext[b];
+        }
+        __syncthreads();
       }
-    };
-    if (ntb == TBM) kloop(Int<TBM>{});
-    else kloop(Int<1>{});
+    }
 
     if (p.ksplit > 1) {   // raw partial sums; the split-K reduce applies the epilogue
       float* part = p.partial + (size_t)ks * p.rows * Nw;
 #pragma unroll
       for (int tb = 0; tb < TBM; ++tb) {
         const int t = tc + 16 * tb + l16;
-        if (tb < ntb && t < M) {
+        if (t < M) {
 #pragma unroll
           for (int b = 0; b < RBW; ++b)
-            *reinterpret_cast<float4*>(part + (size_t)(r0 + t) * Nw + blkrow(b) + 4 * g) =
+            *reinterpret_cast<float4*>(part + (size_t)(r0 + t) * Nw + blk(b) + 4 * g) =
                 make_float4(acc[b][tb][0], acc[b][tb][1], acc[b][tb][2], acc[b][tb][3]);
         }
       }
     } else {
-      amax_bits = store_tile<RBW, TBM, SWIGLU>(p, acc, tc, ntb, M, r0, alpha, !A4, blkrow, lane, amax_bits);
+      amax_bits = store_tile_exp<RBW, TBM, SWIGLU>(p, acc, tc, TBM, M, r0, alpha, pexps, blk, lane, amax_bits);
     }
-    __syncthreads();   // the LDS rings are reused by the next pass
+    if (!has_next) break;
+#pragma unroll
+    for (int rr = 0; rr < ROUNDS; ++rr) {
+      bsrc[rr] = nsrc[rr];
+      bssrc[rr] = nssrc[rr];
+    }
   }
 
   merge_amax(p.out_amax, amax_bits, lane);
@@ -329,12 +421,11 @@ hipError_t launch_cfg(const GemmArgs& a, hipStream_t stream) {
   const int rows_per_tile = 16 * RBW * WAVES;
   const int tiles_per_expert = a.Nw / rows_per_tile;
   const int max_active = a.E < a.rows ? a.E : a.rows;
-  const int per_split = max_active * tiles_per_expert;
-  const int total = per_split * a.ksplit;
+  const int total = max_active * tiles_per_expert * a.ksplit;   // bound on the tiles
   const int grid = (total + 7) / 8 * 8;
   const size_t shmem = (size_t)Ring<TBM, A4>::kBytes;
   gemm_stream_kernel<RBW, WAVES, TBM, kDepth, kDepth, SWIGLU, A4>
-      <<<grid, WAVES * kWave, shmem, stream>>>(a, tiles_per_expert, per_split, total);
+      <<<grid, WAVES * kWave, shmem, stream>>>(a, tiles_per_expert);
   if (a.ksplit <= 1) return hipGetLastError();
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
