@@ -42,8 +42,7 @@ constexpr int kTokBytes = 256;             // f16 activations of one row and chu
 constexpr int kSlot = 16 * kTBM * kTokBytes;
 
 template <int WAVES, int WDEPTH, bool SWIGLU>
-__global__ __launch_bounds__(WAVES* kWave, 2) void gemm_large_kernel(const GemmArgs p, int ntiles_n,
-                                                                     int tiles_per_split, int total_tiles) {
+__global__ __launch_bounds__(WAVES* kWave, 2) void gemm_large_kernel(const GemmArgs p, int ntiles_n) {
   static_assert(WDEPTH >= 2 && kWin % WDEPTH == 0, "the weight ring is read one chunk ahead; steps pair up");
   constexpr int NT = WAVES * kWave;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -51,17 +50,23 @@ __global__ __launch_bounds__(WAVES* kWave, 2) void gemm_large_kernel(const GemmA
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g = lane >> 4;
-  const int per_xcd = gridDim.x >> 3;
+  // Tiles (K slice, m-tile, row tile) of the m-tiles actually listed (known only here) are
+  // numbered slice-major and split into 8 equal ranges, one per XCD (workgroup i runs on XCD
+  // i mod 8): every XCD gets an equal share however far the list falls below the grid's bound,
+  // and the row tiles of one m-tile, which share its activation rows, and the m-tiles of one
+  // expert, which share its weights, run on one XCD and share its L2.
+  const int per_split = ld_const(p.sched_n, 0) * ntiles_n;
+  const int ntiles = per_split * p.ksplit;
+  const int per_xcd = (ntiles + 7) >> 3;
   const int tile = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
-  if (tile >= total_tiles) return;
-  const int ks = tile / tiles_per_split;     // K slice
-  const int mn = tile - ks * tiles_per_split;
+  if ((int)(blockIdx.x >> 3) >= per_xcd || tile >= ntiles) return;
+  const int ks = tile / per_split;           // K slice
+  const int mn = tile - ks * per_split;
   const int mt = mn / ntiles_n;              // m-tile
   const int nb = mn - mt * ntiles_n;         // row tile
-  if (mt >= p.sched_n[0]) return;
-  const int e = p.sched_e[mt], tc = p.sched_r[mt];
-  const int r0 = p.expert_offsets[e];
-  const int M = p.expert_offsets[e + 1] - r0;
+  const int e = ld_const(p.sched_e, mt), tc = ld_const(p.sched_r, mt);
+  const int r0 = ld_const(p.expert_offsets, e);
+  const int M = ld_const(p.expert_offsets, e + 1) - r0;
   const int K = p.K, Nw = p.Nw;
   const int K128 = (K + 127) & ~127;
   const int F = Nw >> 1;
@@ -93,7 +98,7 @@ __global__ __launch_bounds__(WAVES* kWave, 2) void gemm_large_kernel(const GemmA
     wsoff[b] = __builtin_amdgcn_readfirstlane((uint32_t)((blkrow(b) - blkrow(0)) / 16) * (uint32_t)nch * 1024u);
     ssoff[b] = __builtin_amdgcn_readfirstlane((uint32_t)((blkrow(b) - blkrow(0)) / 16) * (uint32_t)nwin * 1024u);
   }
-  const float alpha = p.w4a4 ? p.w_g[e] * p.a_g[0] : p.w_g[e];
+  const float alpha = p.w4a4 ? ld_const(p.w_g, e) * ld_const(p.a_g, 0) : ld_const(p.w_g, e);
 
   auto body = [&](auto ntb_tag) {
     constexpr int NTB = decltype(ntb_tag)::value;
@@ -350,10 +355,9 @@ hipError_t launch_cfg(const GemmArgs& a, int max_mtiles, hipStream_t stream) {
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int ntiles_n = a.Nw / (16 * kRBW * WAVES);
-  const int per_split = max_mtiles * ntiles_n;
-  const int total = per_split * a.ksplit;
+  const int total = max_mtiles * ntiles_n * a.ksplit;   // bound on the tiles
   const int grid = (total + 7) / 8 * 8;
-  kern<<<grid, WAVES * kWave, shmem, stream>>>(a, ntiles_n, per_split, total);
+  kern<<<grid, WAVES * kWave, shmem, stream>>>(a, ntiles_n);
   if (a.ksplit <= 1) return hipGetLastError();
   const hipError_t e2 = hipGetLastError();
   if (e2 != hipSuccess) return e2;
