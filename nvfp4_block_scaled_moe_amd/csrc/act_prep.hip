@@ -28,14 +28,61 @@ namespace {
 
 constexpr int kPrepThreads = 256;
 
+// The m-tile list (MtileSched) by one workgroup of kPrepThreads threads: thread a takes the
+// active-list slots 4a .. 4a+3 (kMaxExperts = 1024 slots), a workgroup scan gives each its
+// first list position, and it writes its experts' m-tiles in list order.
+__device__ void mtile_schedule_block(const MtileSched& s) {
+  static_assert(4 * kPrepThreads >= kMaxExperts, "four active-list slots per thread");
+  __shared__ int wsum[kPrepThreads / kWave];
+  const int a = threadIdx.x, lane = a & 63, wave = a >> 6;
+  const int na = min(s.n_active[0], s.E);
+  int e[4], cnt[4], tot = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int i = 4 * a + q;
+    e[q] = i < na ? s.active[i] : 0;
+    cnt[q] = i < na ? (s.offsets[e[q] + 1] - s.offsets[e[q]] + s.bm - 1) / s.bm : 0;
+    tot += cnt[q];
+  }
+  int incl = tot;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int v = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += v;
+  }
+  if (lane == kWave - 1) wsum[wave] = incl;
+  __syncthreads();
+  int before = 0, total = 0;
+  for (int w = 0; w < kPrepThreads / kWave; ++w) {
+    if (w < wave) before += wsum[w];
+    total += wsum[w];
+  }
+  int base = before + incl - tot;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    for (int i = 0; i < cnt[q] && base + i < s.max_tiles; ++i) {
+      s.sched_e[base + i] = e[q];
+      s.sched_r[base + i] = i * s.bm;
+    }
+    base += cnt[q];
+  }
+  if (a == 0) s.sched_n[0] = min(total, s.max_tiles);
+}
+
 // VPT = 16-byte vectors held per thread (K <= 8 * kPrepThreads * VPT): the row is read once
 // into registers, its amax reduced, then converted from the registers.
+// The workgroup past the rows (when sched.max_tiles > 0) builds the m-tile list instead.
 template <int VPT>
 __global__ __launch_bounds__(kPrepThreads) void act_prep_kernel(const uint16_t* __restrict__ a,
                                                                 int K,
                                                                 _Float16* __restrict__ a16,
-                                                                int* __restrict__ rexp) {
+                                                                int* __restrict__ rexp, int64_t rows,
+                                                                const MtileSched sched) {
   const int64_t r = blockIdx.x;
+  if (r >= rows) {
+    mtile_schedule_block(sched);
+    return;
+  }
   const int K128 = (K + 127) & ~127;
   const uint16_t* row = a + r * (int64_t)K;
   _Float16* orow = a16 + r * (int64_t)K128;
@@ -90,8 +137,13 @@ __global__ __launch_bounds__(kPrepThreads) void act_prep_kernel(const uint16_t* 
 __global__ __launch_bounds__(kPrepThreads) void act_prep_loop_kernel(const uint16_t* __restrict__ a,
                                                                      int K,
                                                                      _Float16* __restrict__ a16,
-                                                                     int* __restrict__ rexp) {
+                                                                     int* __restrict__ rexp, int64_t rows,
+                                                                     const MtileSched sched) {
   const int64_t r = blockIdx.x;
+  if (r >= rows) {
+    mtile_schedule_block(sched);
+    return;
+  }
   const int K128 = (K + 127) & ~127;
   const uint16_t* row = a + r * (int64_t)K;
   _Float16* orow = a16 + r * (int64_t)K128;
@@ -145,9 +197,14 @@ __global__ __launch_bounds__(kPrepThreads) void act_prep_fp4_kernel(const uint8_
                                                                     const uint8_t* __restrict__ scales,
                                                                     int64_t rows, int K,
                                                                     _Float16* __restrict__ a16,
-                                                                    int* __restrict__ rexp) {
+                                                                    int* __restrict__ rexp,
+                                                                    const MtileSched sched) {
   const int K128 = (K + 127) & ~127;
   const int gpr = K128 / 32;   // groups per padded row
+  if ((int64_t)blockIdx.x * kPrepThreads >= rows * gpr) {   // the workgroup past the groups
+    mtile_schedule_block(sched);
+    return;
+  }
   const int64_t i = (int64_t)blockIdx.x * kPrepThreads + threadIdx.x;
   if (i >= rows * gpr) return;
   const int64_t r = i / gpr;
@@ -176,22 +233,23 @@ __global__ __launch_bounds__(kPrepThreads) void act_prep_fp4_kernel(const uint8_
 }  // namespace
 
 hipError_t launch_act_prep_fp4(const uint8_t* packed, const uint8_t* scales, int64_t rows, int K,
-                               _Float16* a16, int* rexp, hipStream_t stream) {
+                               _Float16* a16, int* rexp, const MtileSched& sched, hipStream_t stream) {
   const int64_t n = rows * (((K + 127) & ~127) / 32);
-  act_prep_fp4_kernel<<<(unsigned)((n + kPrepThreads - 1) / kPrepThreads), kPrepThreads, 0, stream>>>(
-      packed, scales, rows, K, a16, rexp);
+  const unsigned blocks = (unsigned)((n + kPrepThreads - 1) / kPrepThreads) + (sched.max_tiles > 0 ? 1u : 0u);
+  act_prep_fp4_kernel<<<blocks, kPrepThreads, 0, stream>>>(packed, scales, rows, K, a16, rexp, sched);
   return hipGetLastError();
 }
 
 hipError_t launch_act_prep(const uint16_t* a, int64_t rows, int K, _Float16* a16, int* rexp,
-                           hipStream_t stream) {
+                           const MtileSched& sched, hipStream_t stream) {
   // vectors per thread covering K128 / 8 pieces (padding pieces are written as zeros)
   const int need = ((K + 127) / 128 * 16 + kPrepThreads - 1) / kPrepThreads;
-  if (need <= 2) act_prep_kernel<2><<<(unsigned)rows, kPrepThreads, 0, stream>>>(a, K, a16, rexp);
-  else if (need <= 4) act_prep_kernel<4><<<(unsigned)rows, kPrepThreads, 0, stream>>>(a, K, a16, rexp);
-  else if (need <= 8) act_prep_kernel<8><<<(unsigned)rows, kPrepThreads, 0, stream>>>(a, K, a16, rexp);
-  else if (need <= 16) act_prep_kernel<16><<<(unsigned)rows, kPrepThreads, 0, stream>>>(a, K, a16, rexp);
-  else act_prep_loop_kernel<<<(unsigned)rows, kPrepThreads, 0, stream>>>(a, K, a16, rexp);
+  const unsigned blocks = (unsigned)rows + (sched.max_tiles > 0 ? 1u : 0u);
+  if (need <= 2) act_prep_kernel<2><<<blocks, kPrepThreads, 0, stream>>>(a, K, a16, rexp, rows, sched);
+  else if (need <= 4) act_prep_kernel<4><<<blocks, kPrepThreads, 0, stream>>>(a, K, a16, rexp, rows, sched);
+  else if (need <= 8) act_prep_kernel<8><<<blocks, kPrepThreads, 0, stream>>>(a, K, a16, rexp, rows, sched);
+  else if (need <= 16) act_prep_kernel<16><<<blocks, kPrepThreads, 0, stream>>>(a, K, a16, rexp, rows, sched);
+  else act_prep_loop_kernel<<<blocks, kPrepThreads, 0, stream>>>(a, K, a16, rexp, rows, sched);
   return hipGetLastError();
 }
 

@@ -298,16 +298,27 @@ nvfp4moe_status moe_grouped_gemm_nvfp4(nvfp4moe_mode mode, nvfp4moe_epilogue epi
     g.a16 = reinterpret_cast<_Float16*>(base);
     g.rexp = reinterpret_cast<int*>(base + lay.a16_bytes);
   }
+  // The MFMA path's m-tile list is built by one extra workgroup of the activation prep launch.
+  MtileSched sched{};
+  if (path == NVFP4MOE_PATH_MFMA) {
+    char* sp = base + lay.a16_bytes + lay.rexp_bytes;
+    const size_t arr = round_up((size_t)lay.max_mtiles * 4);
+    g.sched_e = reinterpret_cast<const int*>(sp);
+    g.sched_r = reinterpret_cast<const int*>(sp + arr);
+    g.sched_n = reinterpret_cast<const int*>(sp + 2 * arr);
+    sched = MtileSched{expert_offsets, active_experts, n_active, E, large_rows_per_mtile(), lay.max_mtiles,
+                       const_cast<int*>(g.sched_e), const_cast<int*>(g.sched_r), const_cast<int*>(g.sched_n)};
+  }
   if (mode == NVFP4MOE_W4A16) {
     err = launch_act_prep(static_cast<const uint16_t*>(a), a_rows, K, const_cast<_Float16*>(g.a16),
-                          const_cast<int*>(g.rexp), s);
+                          const_cast<int*>(g.rexp), sched, s);
   } else {
     g.a_packed = static_cast<const uint8_t*>(a);
     g.a_scales = a_scales;
     g.a_g = a_g;
     if (path == NVFP4MOE_PATH_MFMA)
       err = launch_act_prep_fp4(g.a_packed, a_scales, a_rows, K, const_cast<_Float16*>(g.a16),
-                                const_cast<int*>(g.rexp), s);
+                                const_cast<int*>(g.rexp), sched, s);
   }
   if (err != hipSuccess) return hip_status(err, fn);
   g_last_dispatch = path;
@@ -315,15 +326,7 @@ nvfp4moe_status moe_grouped_gemm_nvfp4(nvfp4moe_mode mode, nvfp4moe_epilogue epi
   g.partial = lay.partial_bytes
                   ? reinterpret_cast<float*>(base + lay.a16_bytes + lay.rexp_bytes + lay.sched_bytes)
                   : nullptr;
-  if (path == NVFP4MOE_PATH_MFMA) {
-    char* sched = base + lay.a16_bytes + lay.rexp_bytes;
-    const size_t arr = round_up((size_t)lay.max_mtiles * 4);
-    g.sched_e = reinterpret_cast<const int*>(sched);
-    g.sched_r = reinterpret_cast<const int*>(sched + arr);
-    g.sched_n = reinterpret_cast<const int*>(sched + 2 * arr);
-
-    return hip_status(launch_gemm_large(g, lay.max_mtiles, s), fn);
-  }
+  if (path == NVFP4MOE_PATH_MFMA) return hip_status(launch_gemm_large(g, lay.max_mtiles, s), fn);
   return hip_status(launch_gemm_stream(g, s), fn);
 }
 

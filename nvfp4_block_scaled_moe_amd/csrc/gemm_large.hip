@@ -3,8 +3,9 @@
 // ("The 2x Gap: Diagnosing Suboptimal FP4 GEMM Kernels on Blackwell SM120", section "The
 // Pivot: Comparing FP4 Against BF16": at M=512 and beyond FP4 pays off through compute).
 //
-//   * m-tiles: 128 consecutive rows of one expert. mtile_schedule_kernel lists them on the
-//     device (expert, first row) for the active experts in order, so the grid needs no
+//   * m-tiles: 128 consecutive rows of one expert. One workgroup of the activation prep
+//     launch lists them on the device (expert, first row) for the active experts in order
+//     (act_prep.hip, MtileSched), so the grid needs no
 //     host-side knowledge of the per-expert counts: grid = (upper bound on the m-tile
 //     count) x (row tiles), and workgroups past the list exit at once.
 //   * Workgroup = 8 waves = 256 weight rows (each wave: 2 blocks of 16 rows over all of K;
@@ -305,42 +306,6 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const GemmArgs p) {
 }
 
 // m-tiles of bm rows over the active experts (one workgroup, n_active <= 1024):
-// sched_e[i] = expert, sched_r[i] = first row within the expert, sched_n[0] = count
-// (at most max_tiles, the length of sched_e and sched_r).
-__global__ __launch_bounds__(1024) void mtile_schedule_kernel(const int* __restrict__ offsets,
-                                                             const int* __restrict__ active,
-                                                             const int* __restrict__ n_active, int E,
-                                                             int bm, int max_tiles, int* __restrict__ sched_e,
-                                                             int* __restrict__ sched_r,
-                                                             int* __restrict__ sched_n) {
-  __shared__ int wsum[1024 / kWave];
-  const int a = threadIdx.x, lane = a & 63, wave = a >> 6;
-  const int na = min(n_active[0], E);
-  int e = 0, cnt = 0;
-  if (a < na) {
-    e = active[a];
-    cnt = (offsets[e + 1] - offsets[e] + bm - 1) / bm;
-  }
-  int incl = cnt;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int v = __shfl_up(incl, o, kWave);
-    if (lane >= o) incl += v;
-  }
-  if (lane == kWave - 1) wsum[wave] = incl;
-  __syncthreads();
-  int before = 0, total = 0;
-  for (int w = 0; w < 1024 / kWave; ++w) {
-    if (w < wave) before += wsum[w];
-    total += wsum[w];
-  }
-  const int base = before + incl - cnt;
-  for (int i = 0; i < cnt && base + i < max_tiles; ++i) {
-    sched_e[base + i] = e;
-    sched_r[base + i] = i * bm;
-  }
-  if (a == 0) sched_n[0] = min(total, max_tiles);
-}
 
 template <int WAVES, int WDEPTH, bool SWIGLU>
 hipError_t launch_cfg(const GemmArgs& a, int max_mtiles, hipStream_t stream) {
@@ -349,11 +314,6 @@ hipError_t launch_cfg(const GemmArgs& a, int max_mtiles, hipStream_t stream) {
   static std::atomic<uint64_t> attr_done{0};
   const hipError_t attr = ensure_dynamic_lds(reinterpret_cast<const void*>(kern), (int)shmem, attr_done);
   if (attr != hipSuccess) return attr;
-  mtile_schedule_kernel<<<1, 1024, 0, stream>>>(a.expert_offsets, a.active, a.n_active, a.E, 16 * kTBM,
-                                                max_mtiles, const_cast<int*>(a.sched_e),
-                                                const_cast<int*>(a.sched_r), const_cast<int*>(a.sched_n));
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
   const int ntiles_n = a.Nw / (16 * kRBW * WAVES);
   const int total = max_mtiles * ntiles_n * a.ksplit;   // bound on the tiles
   const int grid = (total + 7) / 8 * 8;
@@ -368,8 +328,12 @@ hipError_t launch_cfg(const GemmArgs& a, int max_mtiles, hipStream_t stream) {
 // ring does not fit the 256 registers a wave has at two waves per SIMD).
 template <bool SWIGLU>
 hipError_t launch_sw(const GemmArgs& a, int max_mtiles, hipStream_t stream) {
+  if (large_waves(a.rows, a.E, a.Nw) == 4) return launch_cfg<4, 2, SWIGLU>(a, max_mtiles, stream);
   return launch_cfg<8, 2, SWIGLU>(a, max_mtiles, stream);
 }
+
+// Bound on the m-tiles of a call (as sized on the host).
+int mtile_bound(int rows, int E) { return (rows + 16 * kTBM - 1) / (16 * kTBM) + (E < rows ? E : rows); }
 
 }  // namespace
 
@@ -383,12 +347,25 @@ hipError_t launch_splitk_reduce(const GemmArgs& a, hipStream_t stream) {
 
 int large_rows_per_mtile() { return 16 * kTBM; }
 
+// Waves per workgroup (row tiles of 32 x waves weight rows): 8, or 4 when the 8-wave grid
+// would have under 128 tiles (a small GEMM such as M = 512, N = 2048: twice the tiles, split K
+// three ways instead of six, measured 34.6 -> 31.8 us for GEMM and reduce).
+// NVFP4MOE_LARGE_WAVES=4|8 overrides (tests, tuning).
+int large_waves(int rows, int E, int Nw) {
+  int w = mtile_bound(rows, E) * (Nw / (16 * kRBW * 8)) < 128 ? 4 : 8;
+  if (const char* env = std::getenv("NVFP4MOE_LARGE_WAVES")) w = std::atoi(env) == 4 ? 4 : 8;
+  return w;
+}
+
 // Split K (in whole 1024-column scale windows) when the m-tile x row-tile grid is under one
-// workgroup per CU; aim at two per CU. NVFP4MOE_LARGE_KSPLIT=<n> overrides (tests, tuning).
+// workgroup per CU: aim at two 8-wave or one 4-wave workgroup per CU (measured best at
+// M = 512). NVFP4MOE_LARGE_KSPLIT=<n> overrides (tests, tuning).
 int large_ksplit(int rows, int E, int Nw, int K) {
   const int nwin = (K + kChunk * kWin - 1) / (kChunk * kWin);
-  const int tiles = ((rows + 16 * kTBM - 1) / (16 * kTBM) + (E < rows ? E : rows)) * (Nw / (16 * kRBW * 8));
-  int s = tiles >= 256 ? 1 : (512 + tiles - 1) / tiles;
+  const int waves = large_waves(rows, E, Nw);
+  const int tiles = mtile_bound(rows, E) * (Nw / (16 * kRBW * waves));
+  const int target = waves == 8 ? 512 : 256;
+  int s = tiles >= 256 ? 1 : (target + tiles - 1) / tiles;
   if (const char* env = std::getenv("NVFP4MOE_LARGE_KSPLIT")) s = std::atoi(env);
   if (s < 1) s = 1;
   if (s > nwin) s = nwin;

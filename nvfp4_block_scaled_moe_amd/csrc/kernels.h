@@ -24,13 +24,27 @@ hipError_t launch_route_permute(const float* logits, int T, int E, int k, int* t
                                 int* slot_to_row, int* active_experts, int* n_active,
                                 hipStream_t stream);
 
-// ---- act_prep.hip: bf16 rows -> f16 rows scaled by 2^-p (max |x| in [2^14, 2^15)) + p
+// ---- act_prep.hip
+// The m-tile list of the large-M path, built by one extra workgroup of the activation prep
+// launch (no launch of its own): for the active experts in list order, their m-tiles of bm
+// rows; sched_e[i] = expert, sched_r[i] = first row within the expert, sched_n[0] = count (at
+// most max_tiles, the length of sched_e and sched_r). max_tiles = 0: no list.
+struct MtileSched {
+  const int* offsets;
+  const int* active;
+  const int* n_active;
+  int E, bm, max_tiles;
+  int* sched_e;
+  int* sched_r;
+  int* sched_n;
+};
+// bf16 rows -> f16 rows scaled by 2^-p (max |x| in [2^14, 2^15)) + p
 hipError_t launch_act_prep(const uint16_t* a, int64_t rows, int K, _Float16* a16, int* rexp,
-                           hipStream_t stream);
+                           const MtileSched& sched, hipStream_t stream);
 // NVFP4 rows (codes + E4M3 scales) -> the same f16 layout, decoded exactly (E2M1 * E4M3, the
 // global scale stays in the GEMM epilogue); rexp = 0.
 hipError_t launch_act_prep_fp4(const uint8_t* packed, const uint8_t* scales, int64_t rows, int K,
-                               _Float16* a16, int* rexp, hipStream_t stream);
+                               _Float16* a16, int* rexp, const MtileSched& sched, hipStream_t stream);
 
 // ---- grouped GEMM kernels
 struct GemmArgs {
@@ -78,6 +92,8 @@ bool large_supports(int Nw);
 hipError_t launch_gemm_large(const GemmArgs& a, int max_mtiles, hipStream_t stream);
 // K slices for the large-M path from the sizes alone (1 when the tiles fill the GPU).
 int large_ksplit(int rows, int E, int Nw, int K);
+// Waves per large-M workgroup (8, or 4 for small grids), from the sizes alone.
+int large_waves(int rows, int E, int Nw);
 hipError_t launch_zero_f32(float* p, int n, hipStream_t stream);
 
 // ---- reduce.hip

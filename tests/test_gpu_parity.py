@@ -320,11 +320,13 @@ MFMA_CASES = [
 ]
 
 
+@pytest.mark.parametrize("waves", ["8", "4"])
 @pytest.mark.parametrize("counts,Nw,K", MFMA_CASES)
 @pytest.mark.parametrize("mode", [ops.W4A16, ops.W4A4])
-def test_grouped_gemm_mfma_path(counts, Nw, K, mode, monkeypatch):
-    say("gemm mfma", counts, Nw, K, mode)
+def test_grouped_gemm_mfma_path(counts, Nw, K, mode, waves, monkeypatch):
+    say("gemm mfma", counts, Nw, K, mode, waves)
     monkeypatch.setenv("NVFP4MOE_FORCE_PATH", "mfma")
+    monkeypatch.setenv("NVFP4MOE_LARGE_WAVES", waves)
     d = _problem(counts, Nw, K, seed=7 * Nw + K + mode, mode=mode)
     for epi in (ops.EPI_NONE, ops.EPI_SWIGLU):
         want = omoe.grouped_gemm(d["A"], d["offsets"], d["W"], "swiglu" if epi else "none")
@@ -337,11 +339,13 @@ def test_grouped_gemm_mfma_path(counts, Nw, K, mode, monkeypatch):
         assert rel_fro(got16, omoe.bf16_round(want)) <= W4A16_TOL
 
 
-@pytest.mark.parametrize("tile", ["2x8", "2x4", "4x4"])
-def test_grouped_gemm_mfma_tile_shapes(tile, monkeypatch):
-    say("gemm mfma tile", tile)
+@pytest.mark.parametrize("waves", ["8", "4"])
+def test_grouped_gemm_mfma_tile_shapes(waves, monkeypatch):
+    """Both workgroup shapes of the MFMA path: 8 waves (256 weight rows) and 4 (128 rows,
+    chosen for small grids)."""
+    say("gemm mfma waves", waves)
     monkeypatch.setenv("NVFP4MOE_FORCE_PATH", "mfma")
-    monkeypatch.setenv("NVFP4MOE_LARGE_TILE", tile)
+    monkeypatch.setenv("NVFP4MOE_LARGE_WAVES", waves)
     d = _problem([150, 0, 40, 270], 512, 640, seed=31)
     for epi in (ops.EPI_NONE, ops.EPI_SWIGLU):
         want = omoe.grouped_gemm(d["A"], d["offsets"], d["W"], "swiglu" if epi else "none")
@@ -378,15 +382,17 @@ def test_grouped_gemm_stream_split_k(ksplit, mode, monkeypatch):
     assert np_(amax)[0] == np.abs(np_(out)).max()
 
 
+@pytest.mark.parametrize("waves", ["8", "4"])
 @pytest.mark.parametrize("ksplit", ["1", "2", "3"])
 @pytest.mark.parametrize("mode", [ops.W4A16, ops.W4A4])
-def test_grouped_gemm_mfma_split_k(ksplit, mode, monkeypatch):
+def test_grouped_gemm_mfma_split_k(ksplit, mode, waves, monkeypatch):
     """K split into slices of whole 1024-column windows (partial sums reduced in a fixed
     order by a second kernel that applies the epilogue); K = 3072 + 96 leaves a ragged last
-    window. amax of the output must equal max |out| exactly."""
-    say("gemm mfma split-k", ksplit, mode)
+    window; both workgroup shapes. amax of the output must equal max |out| exactly."""
+    say("gemm mfma split-k", ksplit, mode, waves)
     monkeypatch.setenv("NVFP4MOE_FORCE_PATH", "mfma")
     monkeypatch.setenv("NVFP4MOE_LARGE_KSPLIT", ksplit)
+    monkeypatch.setenv("NVFP4MOE_LARGE_WAVES", waves)
     d = _problem([300, 5, 0, 77], 512, 3168, seed=int(ksplit) + 10 * mode, mode=mode, T=250, k=2)
     t = lambda a: torch.from_numpy(a).to(DEV)
     for epi in (ops.EPI_NONE, ops.EPI_SWIGLU):
