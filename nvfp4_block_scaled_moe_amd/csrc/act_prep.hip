@@ -71,15 +71,16 @@ __device__ void mtile_schedule_block(const MtileSched& s) {
 
 // VPT = 16-byte vectors held per thread (K <= 8 * kPrepThreads * VPT): the row is read once
 // into registers, its amax reduced, then converted from the registers.
-// The workgroup past the rows (when sched.max_tiles > 0) builds the m-tile list instead.
+// With sched.max_tiles > 0, workgroup 0 builds the m-tile list (dispatched first, its chain
+// of dependent reads overlaps the conversion) and workgroup r + 1 converts row r.
 template <int VPT>
 __global__ __launch_bounds__(kPrepThreads) void act_prep_kernel(const uint16_t* __restrict__ a,
                                                                 int K,
                                                                 _Float16* __restrict__ a16,
                                                                 int* __restrict__ rexp, int64_t rows,
                                                                 const MtileSched sched) {
-  const int64_t r = blockIdx.x;
-  if (r >= rows) {
+  const int64_t r = (int64_t)blockIdx.x - (sched.max_tiles > 0 ? 1 : 0);
+  if (r < 0) {
     mtile_schedule_block(sched);
     return;
   }
@@ -139,8 +140,8 @@ __global__ __launch_bounds__(kPrepThreads) void act_prep_loop_kernel(const uint1
                                                                      _Float16* __restrict__ a16,
                                                                      int* __restrict__ rexp, int64_t rows,
                                                                      const MtileSched sched) {
-  const int64_t r = blockIdx.x;
-  if (r >= rows) {
+  const int64_t r = (int64_t)blockIdx.x - (sched.max_tiles > 0 ? 1 : 0);
+  if (r < 0) {
     mtile_schedule_block(sched);
     return;
   }
@@ -201,11 +202,12 @@ __global__ __launch_bounds__(kPrepThreads) void act_prep_fp4_kernel(const uint8_
                                                                     const MtileSched sched) {
   const int K128 = (K + 127) & ~127;
   const int gpr = K128 / 32;   // groups per padded row
-  if ((int64_t)blockIdx.x * kPrepThreads >= rows * gpr) {   // the workgroup past the groups
+  const int64_t blk = (int64_t)blockIdx.x - (sched.max_tiles > 0 ? 1 : 0);
+  if (blk < 0) {   // workgroup 0 builds the m-tile list
     mtile_schedule_block(sched);
     return;
   }
-  const int64_t i = (int64_t)blockIdx.x * kPrepThreads + threadIdx.x;
+  const int64_t i = blk * kPrepThreads + threadIdx.x;
   if (i >= rows * gpr) return;
   const int64_t r = i / gpr;
   const int q = (int)(i - r * gpr);   // group: logical k 32q .. 32q+31

@@ -52,7 +52,8 @@ __device__ __forceinline__ float finite_abs(float v) {
 }
 
 // Partial max of |x| over the finite entries: grid (nblk, B); matrix b has n elements
-// (n % 8 == 0); block j scans the 8-element vectors j, j + nblk, ... of matrix b.
+// (n % 8 == 0); block j scans the 8-element vectors j, j + nblk, ... of matrix b, four
+// vectors per thread and step so that four loads are in flight.
 template <typename T>
 __global__ __launch_bounds__(kAmaxThreads) void amax_partial_kernel(const T* __restrict__ x,
                                                                     int64_t n, int nblk,
@@ -60,9 +61,19 @@ __global__ __launch_bounds__(kAmaxThreads) void amax_partial_kernel(const T* __r
   const int b = blockIdx.y;
   const T* xb = x + (size_t)b * (size_t)n;
   const int64_t nvec = n / 8;
+  const int64_t stride = (int64_t)nblk * kAmaxThreads;
   float m = 0.0f;
-  for (int64_t i = (int64_t)blockIdx.x * kAmaxThreads + threadIdx.x; i < nvec;
-       i += (int64_t)nblk * kAmaxThreads) {
+  int64_t i = (int64_t)blockIdx.x * kAmaxThreads + threadIdx.x;
+  for (; i + 3 * stride < nvec; i += 4 * stride) {
+    float v[4][8];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) Vec8<T>::load(xb + (i + q * stride) * 8, v[q]);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) m = fmaxf(m, finite_abs(v[q][j]));
+  }
+  for (; i < nvec; i += stride) {
     float v[8];
     Vec8<T>::load(xb + i * 8, v);
 #pragma unroll
@@ -196,10 +207,12 @@ __global__ __launch_bounds__(kQuantThreads) void fp8_roundtrip_kernel(const uint
   *reinterpret_cast<uint4*>(out + i * 8) = make_uint4(w[0], w[1], w[2], w[3]);
 }
 
+// Workgroups per matrix for the amax pass: about 8 vectors per thread, at most 2048 (8 per
+// CU), so that large activations keep enough loads in flight.
 inline int amax_blocks(int64_t n) {
   int64_t nb = (n / 8 + kAmaxThreads * 8 - 1) / (kAmaxThreads * 8);
   if (nb < 1) nb = 1;
-  if (nb > 256) nb = 256;
+  if (nb > 2048) nb = 2048;
   return (int)nb;
 }
 
