@@ -2,15 +2,17 @@
 
 Every case monkeypatches one oracle function with a subtly wrong version (a
 swapped nibble order, a dropped global scale, a transposed or wrong operand,
-the wrong tie rule, an unstable sort...) and runs the pin that should expose
-it; the pin must fail.
+the wrong tie rule, an unstable sort, a wrong MX exponent bias or rule...) and
+runs the pin that should expose it; the pin must fail.
 """
 import numpy as np
 import pytest
 
 import oracle.moe as moe
+import oracle.mxfp4 as mxfp4
 import oracle.nvfp4 as nvfp4
 import tests.test_oracle_moe as tm
+import tests.test_oracle_mxfp4 as tx
 import tests.test_oracle_nvfp4 as tn
 
 
@@ -83,6 +85,13 @@ MUTATIONS = [
     ("reduce indexes Y by slot, not row", moe, "unpermute_reduce",
      lambda Y, s2r, w: moe.__dict__["_orig_unpermute_reduce"](Y, np.arange(len(s2r)), w),
      tm.test_unpermute_reduce_gather_and_one_hot),
+    ("ue8m0 bias 126", mxfp4, "E8M0_TABLE", np.ldexp(1.0, np.arange(256) - 126),
+     tx.test_e8m0_table_matches_torch_cast),
+    ("mx shared exponent with emax 3", mxfp4, "E2M1_EMAX", 3, tx.test_grid_inputs_round_trip_exactly),
+    ("mx shared exponent rounds log2", mxfp4, "shared_exponent",
+     lambda a: np.maximum(np.round(np.log2(np.asarray(a, np.float64))).astype(np.int64) - 2, -127),
+     tx.test_grid_inputs_round_trip_exactly),
+    ("mx dequantize scale per 16", mxfp4, "GROUP", 16, tx.test_hand_examples),
 ]
 
 
