@@ -10,7 +10,9 @@
  *   Y      --moe_unpermute_reduce--> out[t] = sum_j w[t,j] * Y[row of slot (t,j)]
  *
  * plus nvfp4_quantize (weights offline; W4A4 activations and h per forward) and
- * act_fp8_e4m3_roundtrip (FP8 E4M3 activations dequantized to bf16).
+ * act_fp8_e4m3_roundtrip (FP8 E4M3 activations dequantized to bf16); and the MXFP4 variant
+ * (mxfp4_quantize, mxfp4_weights_tile, moe_grouped_gemm_mxfp4: group-32 UE8M0 scales, W4A4
+ * on the scaled FP4 matrix cores).
  *
  * Sources for what is computed (web pages; section names):
  *   [P1] "Native FP4 Is Slower Than Emulated FP4: A Kernel-Maturity Measurement on
@@ -242,6 +244,68 @@ nvfp4moe_status moe_unpermute_reduce(const void* y, nvfp4moe_dtype y_dtype,
 nvfp4moe_status act_fp8_e4m3_roundtrip(const void* x, int64_t n, void* out, void* ws,
                                        size_t ws_bytes, void* stream);
 size_t act_fp8_e4m3_roundtrip_workspace_size(int64_t n);
+
+/* ---------------------------------------------------------------------------
+ * MXFP4 variant: FP4 (E2M1, codes and packing as above) with one UE8M0 scale per 32
+ * elements and no per-tensor scale ([P2] "The NVFP4 Pivot": "MXFP4 (group-32, UE8M0)").
+ * UE8M0 code s is 2^(s - 127) (s = 0..254) and NaN for s = 255; a value decodes as
+ * E2M1[q] * 2^(s - 127).
+ *
+ * mxfp4_quantize -- quantize float rows [R, C] to MXFP4, per 32-group along C (the OCP MX
+ * v1.0 conversion rule): e = max(floor(log2 amax) - 2, -127), scale byte e + 127, codes
+ * E2M1_RNE_saturating(x * 2^-e) with the sign of x; NaN/Inf group -> scale 0xFF, codes 0;
+ * all-zero group -> scale 0, codes +-0.
+ *   x        device, x_dtype (F32 or BF16), [R, C] row-major, 16-byte aligned.
+ *   R, C     R >= 1, C >= 32, C % 32 == 0.
+ *   packed   device uint8 [R, C/2] (output), 16-byte aligned.
+ *   scales   device uint8 [R, C/32] (output).
+ * ------------------------------------------------------------------------- */
+nvfp4moe_status mxfp4_quantize(const void* x, nvfp4moe_dtype x_dtype, int64_t R, int64_t C, uint8_t* packed,
+                               uint8_t* scales, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * mxfp4_weights_tile -- reorder B MXFP4 matrices [R, C] (as written by mxfp4_quantize)
+ * into the storage moe_grouped_gemm_mxfp4 reads: the codes exactly as nvfp4_weights_tile
+ * tiles them (nvfp4_tiled_codes_bytes(R, C) per matrix), the scales in 1 KB tiles per
+ * (matrix b, row block rb, window w of 16 chunks of 128 columns) at
+ * ((b * R/16 + rb) * ceil(C/2048) + w) * 1024, where lane l = 16 g + r holds 16 bytes: at
+ * byte u the scale of columns 128 (16 w + u) + 32 g .. +31 of row 16 rb + r (zero where
+ * the columns are >= C). A permutation plus zero padding; no value changes.
+ *   B, R, C         1 <= B <= 65535, R >= 16, R % 16 == 0, C >= 32, C % 32 == 0,
+ *                   B * R * C / 2 < 2^40; packed and both outputs 16-byte aligned.
+ *   tiled_scales    device uint8 [B * mxfp4_tiled_scales_bytes(R, C)] (output).
+ * mxfp4_tiled_scales_bytes returns 0 for an invalid R or C.
+ * ------------------------------------------------------------------------- */
+size_t mxfp4_tiled_scales_bytes(int64_t R, int64_t C);
+nvfp4moe_status mxfp4_weights_tile(const uint8_t* packed, const uint8_t* scales, int64_t B, int64_t R, int64_t C,
+                                   uint8_t* tiled_codes, uint8_t* tiled_scales, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_grouped_gemm_mxfp4 -- W4A4 grouped GEMM with MXFP4 weights and activations:
+ * per expert e, rows expert_offsets[e] .. expert_offsets[e+1]:
+ *     P = A_rows . W_e^T  (float32 accumulation of the exact products E2M1 * 2^s)
+ *     EPI_NONE: out = P [rows, Nw];  EPI_SWIGLU: out = silu(P[:, :Nw/2]) * P[:, Nw/2:]
+ * on the scaled FP4 matrix cores (v_mfma_scale_f32_16x16x128_f8f6f4), whose operands are
+ * MXFP4 blocks as stored. [P2] "The NVFP4 Pivot" (MXFP4), [P3] "Discovering the sgl_kernel
+ * Alternative" (block-scaled FP4 GEMM on two FP4 operands).
+ *   a, a_scales  device uint8 [a_rows, K/2] and [a_rows, K/32] (mxfp4_quantize output); a
+ *                16-byte aligned.
+ *   gather_index, gather_div, expert_offsets, active_experts, n_active, E, rows, out,
+ *   out_dtype, out_amax   as for moe_grouped_gemm_nvfp4.
+ *   w_packed, w_scales    E expert matrices [Nw, K] as written by mxfp4_weights_tile,
+ *                16-byte aligned.
+ *   Nw, K        Nw % 256 == 0 (else NVFP4MOE_ERR_UNSUPPORTED), K >= 32, K % 32 == 0,
+ *                rows * max(K, Nw), a_rows * K / 2 and Nw * K / 2 below 2^31.
+ *   ws           moe_grouped_gemm_mxfp4_workspace_size(rows, E) bytes, 16-byte aligned.
+ * ------------------------------------------------------------------------- */
+nvfp4moe_status moe_grouped_gemm_mxfp4(nvfp4moe_epilogue epi, const uint8_t* a, const uint8_t* a_scales,
+                                       int64_t a_rows, const int32_t* gather_index, int32_t gather_div,
+                                       const uint8_t* w_packed, const uint8_t* w_scales,
+                                       const int32_t* expert_offsets, const int32_t* active_experts,
+                                       const int32_t* n_active, int32_t E, int32_t rows, int32_t Nw,
+                                       int32_t K, void* out, nvfp4moe_dtype out_dtype, float* out_amax, void* ws,
+                                       size_t ws_bytes, void* stream);
+size_t moe_grouped_gemm_mxfp4_workspace_size(int32_t rows, int32_t E);
 
 /* Thread-local message describing the last non-OK status ("" if none). Never NULL. */
 const char* nvfp4moe_last_error(void);

@@ -40,6 +40,12 @@ SIGNATURES = {
     "moe_unpermute_reduce": (_int, [_vp, _int, _vp, _vp, _i32, _i32, _i32, _vp, _vp]),
     "act_fp8_e4m3_roundtrip": (_int, [_vp, _i64, _vp, _vp, _sz, _vp]),
     "act_fp8_e4m3_roundtrip_workspace_size": (_sz, [_i64]),
+    "mxfp4_quantize": (_int, [_vp, _int, _i64, _i64, _vp, _vp, _vp]),
+    "mxfp4_tiled_scales_bytes": (_sz, [_i64, _i64]),
+    "mxfp4_weights_tile": (_int, [_vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp]),
+    "moe_grouped_gemm_mxfp4": (_int, [_int, _vp, _vp, _i64, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
+                                      _i32, _i32, _vp, _int, _vp, _vp, _sz, _vp]),
+    "moe_grouped_gemm_mxfp4_workspace_size": (_sz, [_i32, _i32]),
     "nvfp4moe_last_error": (ctypes.c_char_p, []),
     "nvfp4moe_last_dispatch": (_int, []),
     "nvfp4moe_abi_version": (_int, []),

@@ -69,6 +69,11 @@ __device__ void mtile_schedule_block(const MtileSched& s) {
   if (a == 0) s.sched_n[0] = min(total, s.max_tiles);
 }
 
+// The m-tile list alone (for GEMMs with no activation prep, such as MXFP4 W4A4).
+__global__ __launch_bounds__(kPrepThreads) void mtile_schedule_kernel(const MtileSched sched) {
+  mtile_schedule_block(sched);
+}
+
 // VPT = 16-byte vectors held per thread (K <= 8 * kPrepThreads * VPT): the row is read once
 // into registers, its amax reduced, then converted from the registers.
 // With sched.max_tiles > 0, workgroup 0 builds the m-tile list (dispatched first, its chain
@@ -233,6 +238,11 @@ __global__ __launch_bounds__(kPrepThreads) void act_prep_fp4_kernel(const uint8_
 }
 
 }  // namespace
+
+hipError_t launch_mtile_schedule(const MtileSched& sched, hipStream_t stream) {
+  mtile_schedule_kernel<<<1, kPrepThreads, 0, stream>>>(sched);
+  return hipGetLastError();
+}
 
 hipError_t launch_act_prep_fp4(const uint8_t* packed, const uint8_t* scales, int64_t rows, int K,
                                _Float16* a16, int* rexp, const MtileSched& sched, hipStream_t stream) {

@@ -114,7 +114,7 @@ extern "C" {
 
 const char* nvfp4moe_last_error(void) { return g_last_error.c_str(); }
 int nvfp4moe_last_dispatch(void) { return g_last_dispatch; }
-int nvfp4moe_abi_version(void) { return 200; }
+int nvfp4moe_abi_version(void) { return 201; }
 
 // ------------------------------------------------------------------ quantize
 size_t nvfp4_quantize_workspace_size(int64_t B, int64_t R, int64_t C) {
@@ -328,6 +328,133 @@ nvfp4moe_status moe_grouped_gemm_nvfp4(nvfp4moe_mode mode, nvfp4moe_epilogue epi
                   : nullptr;
   if (path == NVFP4MOE_PATH_MFMA) return hip_status(launch_gemm_large(g, lay.max_mtiles, s), fn);
   return hip_status(launch_gemm_stream(g, s), fn);
+}
+
+// ------------------------------------------------------------------ MXFP4
+nvfp4moe_status mxfp4_quantize(const void* x, nvfp4moe_dtype x_dtype, int64_t R, int64_t C, uint8_t* packed,
+                               uint8_t* scales, void* stream) {
+  const char* fn = "mxfp4_quantize";
+  if (!x || !packed || !scales) return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: null tensor pointer", fn);
+  if (x_dtype != NVFP4MOE_F32 && x_dtype != NVFP4MOE_BF16)
+    return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: x_dtype must be F32 or BF16", fn);
+  if (R < 1 || C < 32 || C % 32 != 0)
+    return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: need R >= 1, C >= 32 and C %% 32 == 0 (R=%lld C=%lld)", fn,
+                (long long)R, (long long)C);
+  if ((double)R * (double)C > 4.0e12) return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: tensor too large", fn);
+  if (!aligned(x, 16) || !aligned(packed, 16))
+    return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: x and packed must be 16-byte aligned", fn);
+  return hip_status(launch_mx_quantize(x, x_dtype == NVFP4MOE_BF16, R * C, packed, scales,
+                                       static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+size_t mxfp4_tiled_scales_bytes(int64_t R, int64_t C) {
+  if (R < 16 || R % 16 != 0 || C < 32 || C % 32 != 0) return 0;
+  return mx_tiled_scales_bytes(R, C);
+}
+
+nvfp4moe_status mxfp4_weights_tile(const uint8_t* packed, const uint8_t* scales, int64_t B, int64_t R, int64_t C,
+                                   uint8_t* tiled_codes, uint8_t* tiled_scales, void* stream) {
+  const char* fn = "mxfp4_weights_tile";
+  if (!packed || !scales || !tiled_codes || !tiled_scales)
+    return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: null tensor pointer", fn);
+  if (B < 1 || B > 65535 || R < 16 || R % 16 != 0 || C < 32 || C % 32 != 0)
+    return fail(NVFP4MOE_ERR_INVALID_ARG,
+                "%s: need 1 <= B <= 65535, R >= 16, R %% 16 == 0, C >= 32, C %% 32 == 0 (B=%lld R=%lld C=%lld)",
+                fn, (long long)B, (long long)R, (long long)C);
+  if (B * R * (C / 2) >= (int64_t(1) << 40) || R > (int64_t(1) << 30) || C > (int64_t(1) << 30))
+    return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: matrices too large", fn);
+  if (!aligned(packed, 16) || !aligned(tiled_codes, 16) || !aligned(tiled_scales, 16))
+    return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: packed and the tiled outputs must be 16-byte aligned", fn);
+  return hip_status(launch_mx_weights_tile(packed, scales, B, R, C, tiled_codes, tiled_scales,
+                                           static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+namespace {
+// Workspace of moe_grouped_gemm_mxfp4: the m-tile list (sched_e, sched_r, sched_n).
+int mx_max_mtiles(int32_t rows, int32_t E) {
+  const int bm = mx_rows_per_mtile();
+  return (rows + bm - 1) / bm + (E < rows ? E : rows);
+}
+}  // namespace
+
+size_t moe_grouped_gemm_mxfp4_workspace_size(int32_t rows, int32_t E) {
+  if (rows < 1 || E < 1) return 0;
+  return 2 * round_up((size_t)mx_max_mtiles(rows, E) * 4) + kAlign;
+}
+
+nvfp4moe_status moe_grouped_gemm_mxfp4(nvfp4moe_epilogue epi, const uint8_t* a, const uint8_t* a_scales,
+                                       int64_t a_rows, const int32_t* gather_index, int32_t gather_div,
+                                       const uint8_t* w_packed, const uint8_t* w_scales,
+                                       const int32_t* expert_offsets, const int32_t* active_experts,
+                                       const int32_t* n_active, int32_t E, int32_t rows, int32_t Nw,
+                                       int32_t K, void* out, nvfp4moe_dtype out_dtype, float* out_amax, void* ws,
+                                       size_t ws_bytes, void* stream) {
+  const char* fn = "moe_grouped_gemm_mxfp4";
+  if (epi != NVFP4MOE_EPI_NONE && epi != NVFP4MOE_EPI_SWIGLU)
+    return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: bad epilogue %d", fn, (int)epi);
+  if (out_dtype != NVFP4MOE_F32 && out_dtype != NVFP4MOE_BF16)
+    return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: out_dtype must be F32 or BF16", fn);
+  if (!a || !a_scales || !w_packed || !w_scales || !expert_offsets || !active_experts || !n_active || !out)
+    return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: null tensor pointer", fn);
+  if (E < 1 || E > kMaxExperts)
+    return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: need 1 <= E <= %d (E=%d)", fn, kMaxExperts, E);
+  if (rows < 1 || a_rows < 1) return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: need rows >= 1 and a_rows >= 1", fn);
+  if (K < 32 || K % 32 != 0)
+    return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: need K >= 32 and K %% 32 == 0 (K=%d)", fn, K);
+  if (!mx_supports(Nw))
+    return fail(NVFP4MOE_ERR_UNSUPPORTED, "%s: needs Nw %% 256 == 0 (Nw=%d)", fn, Nw);
+  if ((int64_t)rows * (K > Nw ? K : Nw) >= (int64_t(1) << 31) || a_rows * (int64_t)(K / 2) >= (int64_t(1) << 31) ||
+      (int64_t)Nw * ((K + 127) / 128 * 64) >= (int64_t(1) << 31))
+    return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: rows * max(K, Nw), a_rows * K / 2 and Nw * K / 2 must be < 2^31", fn);
+  if (!gather_index && a_rows != rows)
+    return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: without gather_index a_rows must equal rows", fn);
+  if (gather_index && gather_div < 1) return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: gather_div must be >= 1", fn);
+  if (!aligned(a, 16) || !aligned(w_packed, 16) || !aligned(w_scales, 16) ||
+      !aligned(out, out_dtype == NVFP4MOE_F32 ? 4 : 2))
+    return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: a and the tiled weights must be 16-byte aligned", fn);
+  const size_t need = moe_grouped_gemm_mxfp4_workspace_size(rows, E);
+  if (!ws || ws_bytes < need)
+    return fail(NVFP4MOE_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, ws_bytes);
+  if (!aligned(ws, 16)) return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: workspace must be 16-byte aligned", fn);
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int max_mtiles = mx_max_mtiles(rows, E);
+  const size_t arr = round_up((size_t)max_mtiles * 4);
+  char* base = static_cast<char*>(ws);
+  GemmArgs g{};
+  g.w4a4 = 1;
+  g.a_packed = a;
+  g.a_scales = a_scales;
+  g.gather_index = gather_index;
+  g.gather_div = gather_div < 1 ? 1 : gather_div;
+  g.w_packed = w_packed;
+  g.w_scales = w_scales;
+  g.expert_offsets = expert_offsets;
+  g.active = active_experts;
+  g.n_active = n_active;
+  g.E = E;
+  g.rows = rows;
+  g.Nw = Nw;
+  g.K = K;
+  g.a_rows = (int)a_rows;
+  g.swiglu = epi == NVFP4MOE_EPI_SWIGLU;
+  g.out = out;
+  g.out_bf16 = out_dtype == NVFP4MOE_BF16;
+  g.out_amax = out_amax;
+  g.sched_e = reinterpret_cast<const int*>(base);
+  g.sched_r = reinterpret_cast<const int*>(base + arr);
+  g.sched_n = reinterpret_cast<const int*>(base + 2 * arr);
+  g.ksplit = 1;
+  hipError_t err = hipSuccess;
+  if (out_amax) err = launch_zero_f32(out_amax, 1, s);
+  if (err != hipSuccess) return hip_status(err, fn);
+  const MtileSched sched{expert_offsets, active_experts, n_active, E, mx_rows_per_mtile(), max_mtiles,
+                         const_cast<int*>(g.sched_e), const_cast<int*>(g.sched_r), const_cast<int*>(g.sched_n)};
+  err = launch_mtile_schedule(sched, s);
+  if (err != hipSuccess) return hip_status(err, fn);
+  return hip_status(launch_gemm_mx(g, max_mtiles, s), fn);
 }
 
 // ------------------------------------------------------------------ unpermute-reduce

@@ -38,6 +38,8 @@ struct MtileSched {
   int* sched_r;
   int* sched_n;
 };
+// The m-tile list in a launch of its own.
+hipError_t launch_mtile_schedule(const MtileSched& sched, hipStream_t stream);
 // bf16 rows -> f16 rows scaled by 2^-p (max |x| in [2^14, 2^15)) + p
 hipError_t launch_act_prep(const uint16_t* a, int64_t rows, int K, _Float16* a16, int* rexp,
                            const MtileSched& sched, hipStream_t stream);
@@ -85,6 +87,13 @@ size_t tiled_codes_bytes(int64_t R, int64_t C);
 size_t tiled_scales_bytes(int64_t R, int64_t C);
 hipError_t launch_weights_tile(const uint8_t* packed, const uint8_t* scales, int64_t B, int64_t R, int64_t C,
                                uint8_t* tiled_codes, uint8_t* tiled_scales, hipStream_t stream);
+// MXFP4: the same code tiles; UE8M0 scales tiled per (16-row block, 16-chunk window).
+size_t mx_tiled_scales_bytes(int64_t R, int64_t C);
+hipError_t launch_mx_weights_tile(const uint8_t* packed, const uint8_t* scales, int64_t B, int64_t R, int64_t C,
+                                  uint8_t* tiled_codes, uint8_t* tiled_scales, hipStream_t stream);
+// MXFP4 quantizer (quantize.hip): n elements (n % 32 == 0) -> packed [n/2] + UE8M0 scales [n/32].
+hipError_t launch_mx_quantize(const void* x, bool x_bf16, int64_t n, uint8_t* packed, uint8_t* scales,
+                              hipStream_t stream);
 // large-M path: rows per m-tile, the Nw it supports, and the launcher (max_mtiles is the host
 // bound ceil(rows / rows_per_mtile) + min(E, rows) on the schedule length).
 int large_rows_per_mtile();
@@ -94,6 +103,12 @@ hipError_t launch_gemm_large(const GemmArgs& a, int max_mtiles, hipStream_t stre
 int large_ksplit(int rows, int E, int Nw, int K);
 // Waves per large-M workgroup (8, or 4 for small grids), from the sizes alone.
 int large_waves(int rows, int E, int Nw);
+// MXFP4 W4A4 GEMM on the scaled FP4 MFMA (gemm_mx.hip): m-tile rows, supported Nw, launcher
+// (a.w_packed / a.w_scales: MX tiles; a.a_packed / a.a_scales: row-major MXFP4; the m-tile
+// list in a.sched_*).
+int mx_rows_per_mtile();
+bool mx_supports(int Nw);
+hipError_t launch_gemm_mx(const GemmArgs& a, int max_mtiles, hipStream_t stream);
 hipError_t launch_zero_f32(float* p, int n, hipStream_t stream);
 
 // ---- reduce.hip

@@ -207,6 +207,52 @@ __global__ __launch_bounds__(kQuantThreads) void fp8_roundtrip_kernel(const uint
   *reinterpret_cast<uint4*>(out + i * 8) = make_uint4(w[0], w[1], w[2], w[3]);
 }
 
+// MXFP4 (group 32, UE8M0 scale, no per-tensor scale; "The Benchmark That Confirmed the
+// Ceiling", section "The NVFP4 Pivot", read with the OCP MX v1.0 conversion rule): one thread
+// per 32 consecutive elements of a row: amax over the finite entries, shared exponent
+// e = max(floor(log2 amax) - 2, -127) (frexp gives floor(log2) exactly), scale byte e + 127,
+// codes E2M1_RNE_saturating(w * 2^-e) (a power-of-two scaling, exact); a group with NaN/Inf
+// gets scale 0xFF and codes 0, an all-zero group scale 0 and codes +-0.
+template <typename T>
+__global__ __launch_bounds__(kQuantThreads) void mx_quantize_kernel(const T* __restrict__ x, int64_t total_units,
+                                                                    uint8_t* __restrict__ packed,
+                                                                    uint8_t* __restrict__ scales) {
+  const int64_t u = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x;
+  if (u >= total_units) return;
+  const int64_t e0 = u * 32;
+  float v[32];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) Vec8<T>::load(x + e0 + 8 * q, v + 8 * q);
+  float amax = 0.0f;
+  bool finite = true;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    finite = finite && (fabsf(v[i]) <= 3.402823466e38f);
+    amax = fmaxf(amax, finite_abs(v[i]));
+  }
+  uint32_t s = 0;
+  int e = 0;
+  if (!finite) {
+    s = 0xFF;
+  } else if (amax > 0.0f) {
+    int ex;
+    (void)frexpf(amax, &ex);          // amax = f * 2^ex, f in [0.5, 1): floor(log2 amax) = ex - 1
+    e = max(ex - 1 - 2, -127);
+    s = (uint32_t)(e + 127);
+  }
+  uint32_t w[4] = {0u, 0u, 0u, 0u};
+  if (finite) {
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const uint32_t sign = (__float_as_uint(v[i]) >> 31) << 3;
+      const uint32_t mag = amax > 0.0f ? e2m1_rne_mag(ldexpf(fabsf(v[i]), -e)) : 0u;
+      w[i >> 3] |= (sign | mag) << (4 * (i & 7));
+    }
+  }
+  *reinterpret_cast<uint4*>(packed + e0 / 2) = make_uint4(w[0], w[1], w[2], w[3]);
+  scales[u] = (uint8_t)s;
+}
+
 // Workgroups per matrix for the amax pass: about 8 vectors per thread, at most 2048 (8 per
 // CU), so that large activations keep enough loads in flight.
 inline int amax_blocks(int64_t n) {
@@ -247,6 +293,19 @@ hipError_t launch_quantize(const void* x, bool x_bf16, int64_t B, int64_t R, int
   else
     quantize_kernel<float><<<(unsigned)blocks, kQuantThreads, 0, stream>>>(
         static_cast<const float*>(x), n, units, g_out, packed, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_mx_quantize(const void* x, bool x_bf16, int64_t n, uint8_t* packed, uint8_t* scales,
+                              hipStream_t stream) {
+  const int64_t units = n / 32;
+  const unsigned blocks = (unsigned)((units + kQuantThreads - 1) / kQuantThreads);
+  if (x_bf16)
+    mx_quantize_kernel<uint16_t><<<blocks, kQuantThreads, 0, stream>>>(static_cast<const uint16_t*>(x), units,
+                                                                       packed, scales);
+  else
+    mx_quantize_kernel<float><<<blocks, kQuantThreads, 0, stream>>>(static_cast<const float*>(x), units, packed,
+                                                                    scales);
   return hipGetLastError();
 }
 

@@ -190,5 +190,80 @@ def act_fp8_e4m3_roundtrip(x: torch.Tensor, out: torch.Tensor | None = None):
     return out
 
 
+# ------------------------------------------------------------------ MXFP4 variant
+def mxfp4_quantize(x: torch.Tensor):
+    """Float rows [..., C] (C % 32 == 0) -> MXFP4 (packed uint8 [..., C/2], UE8M0 scales
+    uint8 [..., C/32]); one scale per 32 elements, no per-tensor scale."""
+    _dev(x)
+    x = x.contiguous()
+    C = x.shape[-1]
+    R = x.numel() // C
+    packed = torch.empty(x.shape[:-1] + (C // 2,), dtype=torch.uint8, device=x.device)
+    scales = torch.empty(x.shape[:-1] + (C // 32,), dtype=torch.uint8, device=x.device)
+    lib = _lib.load()
+    st = lib.mxfp4_quantize(_ptr(x), _DT[x.dtype], R, C, _ptr(packed), _ptr(scales), _stream())
+    _lib.check("mxfp4_quantize", st)
+    return packed, scales
+
+
+@dataclass
+class MxTiledWeights:
+    """B MXFP4 matrices [R, C] in the tiled storage moe_grouped_gemm_mxfp4 reads."""
+    codes: torch.Tensor    # uint8 [B, nvfp4_tiled_codes_bytes(R, C)]
+    scales: torch.Tensor   # uint8 [B, mxfp4_tiled_scales_bytes(R, C)]
+    R: int
+    C: int
+
+    @property
+    def B(self) -> int:
+        return self.codes.shape[0]
+
+
+def mxfp4_weights_tile(packed: torch.Tensor, scales: torch.Tensor) -> MxTiledWeights:
+    """Reorder MXFP4 weights packed [B, R, C/2] + scales [B, R, C/32] (or one matrix) into
+    the tiled storage; a byte permutation with zero padding (include/nvfp4moe.h)."""
+    _dev(packed, scales)
+    p3 = (packed.unsqueeze(0) if packed.dim() == 2 else packed).contiguous()
+    s3 = (scales.unsqueeze(0) if scales.dim() == 2 else scales).contiguous()
+    B, R, Ch = p3.shape
+    C = 2 * Ch
+    assert s3.shape == (B, R, C // 32), (s3.shape, p3.shape)
+    lib = _lib.load()
+    cb, sb = lib.nvfp4_tiled_codes_bytes(R, C), lib.mxfp4_tiled_scales_bytes(R, C)
+    if cb == 0 or sb == 0:
+        raise _lib.NVFP4MoEError("mxfp4_weights_tile", _lib.ERR_INVALID_ARG, f"unsupported shape R={R} C={C}")
+    codes = torch.empty((B, cb), dtype=torch.uint8, device=packed.device)
+    sc = torch.empty((B, sb), dtype=torch.uint8, device=packed.device)
+    st = lib.mxfp4_weights_tile(_ptr(p3), _ptr(s3), B, R, C, _ptr(codes), _ptr(sc), _stream())
+    _lib.check("mxfp4_weights_tile", st)
+    return MxTiledWeights(codes, sc, R, C)
+
+
+def moe_grouped_gemm_mxfp4(epi: int, a: torch.Tensor, a_scales: torch.Tensor, w: MxTiledWeights,
+                           expert_offsets: torch.Tensor, active_experts: torch.Tensor,
+                           n_active: torch.Tensor, *, gather_index: torch.Tensor | None = None,
+                           gather_div: int = 1, rows: int | None = None, out_dtype=torch.bfloat16,
+                           want_amax: bool = False, out: torch.Tensor | None = None):
+    """W4A4 grouped GEMM with MXFP4 weights ``w`` (E matrices [Nw, K], tiled) and MXFP4
+    activations ``a`` [a_rows, K/2] + ``a_scales`` [a_rows, K/32] (+ SwiGLU)."""
+    _dev(a, a_scales, w.codes, w.scales, expert_offsets, active_experts, n_active, gather_index)
+    E, Nw, K = w.B, w.R, w.C
+    a_rows = a.shape[0]
+    if rows is None:
+        rows = gather_index.numel() if gather_index is not None else a_rows
+    ncol = Nw // 2 if epi == EPI_SWIGLU else Nw
+    if out is None:
+        out = torch.empty((rows, ncol), dtype=out_dtype, device=a.device)
+    amax = torch.empty((1,), dtype=torch.float32, device=a.device) if want_amax else None
+    lib = _lib.load()
+    ws = _ws(lib.moe_grouped_gemm_mxfp4_workspace_size(rows, E), a.device)
+    st = lib.moe_grouped_gemm_mxfp4(
+        epi, _ptr(a), _ptr(a_scales), a_rows, _ptr(gather_index), int(gather_div), _ptr(w.codes),
+        _ptr(w.scales), _ptr(expert_offsets), _ptr(active_experts), _ptr(n_active), E, rows, Nw, K,
+        _ptr(out), _DT[out.dtype], _ptr(amax), _ptr(ws), ws.numel(), _stream())
+    _lib.check("moe_grouped_gemm_mxfp4", st)
+    return (out, amax) if want_amax else out
+
+
 def last_dispatch() -> int:
     return _lib.load().nvfp4moe_last_dispatch()

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(_lib.SIGNATURES), "binding signatures out of sync with the header"
     for n in names:
         assert hasattr(lib, n)
-    assert lib.nvfp4moe_abi_version() == 200
+    assert lib.nvfp4moe_abi_version() == 201
 
 
 FAKE = ctypes.c_void_p(1 << 20)      # aligned, never dereferenced: validation fails first
@@ -147,3 +147,34 @@ def test_last_error_is_thread_local_and_cleared():
     th.join()
     assert seen == [b""]
 
+
+
+def _mx_gemm(lib, epi=_lib.EPI_NONE, a=FAKE, a_rows=16, gidx=None, gdiv=1, E=8, rows=16, Nw=256, K=256,
+             out_dtype=_lib.F32, ws=FAKE, ws_bytes=1 << 30):
+    return lib.moe_grouped_gemm_mxfp4(epi, a, FAKE, a_rows, gidx, gdiv, FAKE, FAKE, FAKE, FAKE, FAKE, E, rows,
+                                      Nw, K, FAKE, out_dtype, None, ws, ws_bytes, None)
+
+
+def test_mxfp4_argument_checks_and_sizes():
+    """The MXFP4 calls validate before queuing anything; sizes follow the closed forms."""
+    lib = _lib.load()
+    for R, C in [(16, 32), (32, 2048), (48, 2080), (16, 4096)]:
+        assert lib.mxfp4_tiled_scales_bytes(R, C) == (R // 16) * -(-C // 2048) * 1024
+    assert lib.mxfp4_tiled_scales_bytes(15, 64) == 0 and lib.mxfp4_tiled_scales_bytes(16, 48) == 0
+    for args in [(FAKE, _lib.F32, 4, 48), (FAKE, _lib.F32, 0, 64), (FAKE, 7, 4, 64), (None, _lib.F32, 4, 64),
+                 (MISALIGNED, _lib.BF16, 4, 64)]:
+        st, _ = _err(lib.mxfp4_quantize(*args, FAKE, FAKE, None))
+        assert st == _lib.ERR_INVALID_ARG, args
+    st, _ = _err(lib.mxfp4_weights_tile(FAKE, FAKE, 1, 24, 64, FAKE, FAKE, None))
+    assert st == _lib.ERR_INVALID_ARG
+    bad = [dict(epi=4), dict(out_dtype=5), dict(a=None), dict(E=0), dict(E=2000), dict(rows=0), dict(K=48),
+           dict(K=0), dict(a_rows=8), dict(gidx=FAKE, gdiv=0), dict(a=MISALIGNED)]
+    for kw in bad:
+        st, _ = _err(_mx_gemm(lib, **kw))
+        assert st == _lib.ERR_INVALID_ARG, kw
+    st, msg = _err(_mx_gemm(lib, Nw=384))
+    assert st == _lib.ERR_UNSUPPORTED and "256" in msg
+    need = lib.moe_grouped_gemm_mxfp4_workspace_size(16, 8)
+    assert need >= 2 * (1 + 8) * 4
+    st, _ = _err(_mx_gemm(lib, ws_bytes=need - 1))
+    assert st == _lib.ERR_WORKSPACE

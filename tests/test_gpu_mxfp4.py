@@ -1,0 +1,163 @@
+"""GPU parity of the MXFP4 variant (group-32 UE8M0 scales) against the MXFP4 oracle.
+
+The quantizer's codes and scales and the tiled scale storage must match bit for bit; the
+W4A4 grouped GEMM on the scaled FP4 matrix cores must match the float64 oracle fed the same
+dequantized operands (summation order is the only difference, < 1e-5 relative Frobenius in
+float32 output, and within the W4A4 bound in bf16).
+"""
+import numpy as np
+import pytest
+import torch
+
+from nvfp4_block_scaled_moe_amd import _lib, inputs, ops
+from oracle import moe as omoe
+from oracle import mxfp4 as omx
+from tests.gpu_util import assert_finite, np_, rel_fro, say
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+W4A4_TOL = 2e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    torch.cuda.init()
+
+
+# ------------------------------------------------------------------ quantize
+def _special(R, C, seed):
+    x = inputs.random_fp32((R, C), seed, std=1.0)
+    x[0, :32] = 0.0
+    x[0, 5] = -0.0
+    if R > 1 and C >= 128:
+        x[1, 32:64] *= 2.0 ** -130            # below the smallest scale: e clamps at -127
+        x[1, 64:96] *= 2.0 ** 100             # large exponents
+        x[1, 100] = float("nan")
+        x[1, 33] = float("inf")
+        x[1, 96:128] = 7.0                    # saturation at 6 * 2^0
+        x[1, 97] = 2.5                        # a tie (2.5 -> 2) in the same group
+    return x
+
+
+@pytest.mark.parametrize("R,C,dt", [(4, 128, torch.float32), (33, 96, torch.float32), (64, 2048, torch.float32),
+                                    (5, 4096, torch.bfloat16), (2, 128, torch.bfloat16)])
+def test_mxfp4_quantize_bit_exact(R, C, dt):
+    say("mx quantize", R, C, dt)
+    x = _special(R, C, R + C).to(dt)
+    p, s = ops.mxfp4_quantize(x.to(DEV))
+    torch.cuda.synchronize()
+    wp, ws = omx.quantize(x.float().numpy())
+    assert np.array_equal(np_(p), wp)
+    assert np.array_equal(np_(s), ws)
+
+
+# ------------------------------------------------------------------ tiling
+def _mx_tile_reference(packed, scales):
+    """Index-by-index transcription of the MX scale tiles (include/nvfp4moe.h)."""
+    B, R, Ch = packed.shape
+    C = 2 * Ch
+    nch, nwin = -(-C // 128), -(-C // 2048)
+    sc = np.zeros((B, R // 16, nwin, 64, 16), np.uint8)
+    for b in range(B):
+        for row in range(R):
+            rb, r = divmod(row, 16)
+            for g in range(4):
+                for w in range(nwin):
+                    for u in range(16):
+                        k0 = 128 * (16 * w + u) + 32 * g
+                        if k0 < C:
+                            sc[b, rb, w, 16 * g + r, u] = scales[b, row, k0 // 32]
+    return sc.reshape(B, -1)
+
+
+@pytest.mark.parametrize("B,R,C", [(1, 16, 32), (2, 48, 160), (1, 32, 2176), (2, 16, 4096)])
+def test_mxfp4_weights_tile_bit_exact(B, R, C):
+    say("mx tile", B, R, C)
+    rng = np.random.default_rng(B * 3 + R + C)
+    packed = rng.integers(0, 256, size=(B, R, C // 2), dtype=np.uint8)
+    scales = rng.integers(0, 256, size=(B, R, C // 32), dtype=np.uint8)
+    t = ops.mxfp4_weights_tile(torch.from_numpy(packed).to(DEV), torch.from_numpy(scales).to(DEV))
+    nv = ops.nvfp4_weights_tile(torch.from_numpy(packed).to(DEV),
+                                torch.zeros((B, R, C // 16), dtype=torch.uint8, device=DEV),
+                                torch.ones(B, device=DEV))
+    torch.cuda.synchronize()
+    assert np.array_equal(np_(t.codes), np_(nv.codes))        # the same code tiles as NVFP4
+    assert np.array_equal(np_(t.scales), _mx_tile_reference(packed, scales))
+
+
+# ------------------------------------------------------------------ grouped GEMM
+def _mx_problem(counts, Nw, K, seed, T=None, k=None):
+    E = len(counts)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    rows = int(offsets[-1])
+    act = [e for e in range(E) if counts[e] > 0]
+    active = np.array(act + [-1] * (E - len(act)), np.int32)
+    w = torch.stack([inputs.random_fp32((Nw, K), seed + 17 * e, std=0.02) for e in range(E)])
+    wp, ws = ops.mxfp4_quantize(w.to(DEV))
+    nA = rows if T is None else T
+    a = inputs.random_fp32((nA, K), seed + 1).to(torch.bfloat16)
+    ap, as_ = ops.mxfp4_quantize(a.to(DEV))
+    A = omx.dequantize(np_(ap), np_(as_))
+    gidx = None
+    if T is not None:
+        gidx = np.random.default_rng(seed).integers(0, T * k, size=rows).astype(np.int32)
+        A = A[gidx // k]
+    return dict(E=E, rows=rows, offsets=offsets, active=active, n_active=np.array([len(act)], np.int32),
+                wt=ops.mxfp4_weights_tile(wp, ws), ap=ap, as_=as_, A=A, gidx=gidx, gdiv=k or 1,
+                W=[omx.dequantize(np_(wp[e]), np_(ws[e])) for e in range(E)])
+
+
+def _run(d, epi, out_dtype, want_amax=False):
+    t = lambda x: torch.from_numpy(x).to(DEV)
+    res = ops.moe_grouped_gemm_mxfp4(epi, d["ap"], d["as_"], d["wt"], t(d["offsets"]), t(d["active"]),
+                                     t(d["n_active"]), rows=d["rows"], out_dtype=out_dtype,
+                                     gather_index=None if d["gidx"] is None else t(d["gidx"]),
+                                     gather_div=d["gdiv"], want_amax=want_amax)
+    torch.cuda.synchronize()
+    return res
+
+
+MX_CASES = [
+    # counts per expert, Nw, K
+    ([150, 0, 40, 270], 512, 640),       # ragged m-tiles, a 0-row expert, K % 128 != 0
+    ([128], 256, 2048),                  # one full m-tile, one scale window
+    ([300, 7], 256, 4096 + 96),          # two scale windows and a partial one
+    ([1, 2, 3, 500], 768, 256),          # three row tiles, tiny experts
+    ([513], 256, 7168),                  # the prefill hidden size (partial last window)
+]
+
+
+@pytest.mark.parametrize("counts,Nw,K", MX_CASES)
+def test_grouped_gemm_mxfp4(counts, Nw, K):
+    say("gemm mxfp4", counts, Nw, K)
+    d = _mx_problem(counts, Nw, K, seed=Nw + K)
+    for epi in (ops.EPI_NONE, ops.EPI_SWIGLU):
+        want = omoe.grouped_gemm(d["A"], d["offsets"], d["W"], "swiglu" if epi else "none")
+        got = np_(_run(d, epi, torch.float32))
+        assert_finite(got)
+        r = rel_fro(got, want)
+        assert r < 1e-5, r          # identical operands on both sides: only summation order differs
+        got16 = np_(_run(d, epi, torch.bfloat16))
+        assert rel_fro(got16, omoe.bf16_round(want)) <= W4A4_TOL
+
+
+def test_grouped_gemm_mxfp4_gather_and_amax():
+    say("gemm mxfp4 gather")
+    d = _mx_problem([7, 0, 300, 9], 256, 512, seed=5, T=120, k=3)
+    want = omoe.grouped_gemm(d["A"], d["offsets"], d["W"], "swiglu")
+    out, amax = _run(d, ops.EPI_SWIGLU, torch.float32, want_amax=True)
+    got = np_(out)
+    assert rel_fro(got, want) < 1e-5
+    assert np_(amax)[0] == np.abs(got).max()
+
+
+def test_grouped_gemm_mxfp4_rejects_unsupported_nw():
+    d = _mx_problem([20], 256, 256, seed=3)
+    wt = ops.MxTiledWeights(d["wt"].codes, d["wt"].scales, 160, 256)   # Nw = 160: not a multiple of 256
+    t = lambda x: torch.from_numpy(x).to(DEV)
+    with pytest.raises(_lib.NVFP4MoEError) as ei:
+        ops.moe_grouped_gemm_mxfp4(ops.EPI_NONE, d["ap"], d["as_"], wt, t(d["offsets"]), t(d["active"]),
+                                   t(d["n_active"]), rows=d["rows"])
+    assert ei.value.status == _lib.ERR_UNSUPPORTED
