@@ -305,6 +305,10 @@ def dense_line(torch, ops, inputs, wl, args, M):
     t4 = timed(lambda: ops.moe_grouped_gemm_nvfp4(ops.W4A4, ops.EPI_NONE, aq, wt, a_scales=as_,
                                                   a_g=ag, **common))
     tmm = timed(lambda: torch.mm(a, wbf.t()))
+    # the MXFP4 variant of the same GEMM (group-32 UE8M0 scales) on the scaled FP4 matrix cores
+    wmx = ops.mxfp4_weights_tile(*ops.mxfp4_quantize(inputs.expert_weight_fp32(wl, "dense", 0, dev).unsqueeze(0)))
+    amx, amx_s = ops.mxfp4_quantize(a)
+    tmx = timed(lambda: ops.moe_grouped_gemm_mxfp4(ops.EPI_NONE, amx, amx_s, wmx, **common))
     tf = lambda us: flops / (us * 1e-6) / 1e12
     return dict(
         metric="MoE NVFP4 grouped-GEMM TFLOPS + weight GB/s vs tokens/expert, % roofline",
@@ -315,6 +319,8 @@ def dense_line(torch, ops, inputs, wl, args, M):
                     path="mfma" if path16 == ops.PATH_MFMA else "stream"),
         w4a4_tflops=round(tf(t4), 2), w4a4_us=round(t4, 2),
         torch_mm_bf16_tflops=round(tf(tmm), 2), torch_mm_bf16_us=round(tmm, 2),
+        mxfp4_w4a4_tflops=round(tf(tmx), 2), mxfp4_w4a4_us=round(tmx, 2),
+        mxfp4_w4a4_fp4_peak_frac=round(tf(tmx) / FP4_PEAK_TFLOPS, 4),
         roofline=dict(bound="mfma", kernel="moe_grouped_gemm_nvfp4 call (activation prep + GEMM)",
                       achieved=round(tf(t16), 1), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
                       frac=round(tf(t16) / BF16_PEAK_TFLOPS, 4), traffic=None),

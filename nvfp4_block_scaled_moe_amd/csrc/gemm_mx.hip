@@ -15,8 +15,8 @@
 //     mtile_schedule_kernel); the tiles of the listed m-tiles are split into 8 equal ranges,
 //     one per XCD, as in the f16 large-M kernel.
 //   * Workgroup = 8 waves = 256 weight rows (each wave 2 blocks of 16: for SwiGLU one gate
-//     and the matching up block) x one m-tile (8 token blocks of 16; blocks past the
-//     m-tile's rows are skipped).
+//     and the matching up block) x one m-tile (8 token blocks of 16; a ragged m-tile runs
+//     with 1, 2, 4 or 8 blocks).
 //   * Per chunk (128 k) each thread stages 16 bytes of codes and one scale byte of one token
 //     (512 threads = 128 tokens x 4 k-blocks) through registers into a two-slot LDS ring;
 //     token rows are padded to 80 bytes, so the 16 lanes of a fragment read hit distinct
@@ -140,42 +140,54 @@ __global__ __launch_bounds__(kMxWaves* kWave) void gemm_mx_kernel(const GemmArgs
   b_commit(0, 0);
   __syncthreads();
 
-  // Chunk c: LDS slot c & 1, staging set c & 1, weight ring entry c % kMxDepth.
-  for (int c0 = 0; c0 < nwin * kMxWin; c0 += kMxWin) {
-    s_issue(c0 / kMxWin + 1);
+  // The main loop, compiled for NTB = 8, 4, 2 or 1 token blocks (ntb rounded up; blocks past
+  // the m-tile's rows hold zeros). Chunk c: LDS slot c & 1, staging set c & 1, weight ring
+  // entry c % kMxDepth. Whole scale windows; the MFMAs of chunks past K are skipped.
+  auto body = [&](auto ntb_tag) {
+    constexpr int NTB = decltype(ntb_tag)::value;
+    for (int c0 = 0; c0 < nwin * kMxWin; c0 += kMxWin) {
+      s_issue(c0 / kMxWin + 1);
 #pragma unroll
-    for (int u = 0; u < kMxWin; ++u) {
-      const int c = c0 + u;
-      if (c >= nch) break;        // the last window may be partial
-      const int d = u % kMxDepth;
-      b_issue(u & 1, c + 2);   // set u & 1 was committed last step
-      const unsigned char* base = smem + (c & 1) * kMxSlot;
-      u32x4 wa[kMxRBW];
-      uint32_t sa[kMxRBW];
+      for (int u = 0; u < kMxWin; ++u) {
+        const int c = c0 + u;
+        const int d = u % kMxDepth;
+        b_issue(u & 1, c + 2);   // set u & 1 was committed last step
+        const unsigned char* base = smem + (c & 1) * kMxSlot;
+        u32x4 wa[kMxRBW];
+        uint32_t sa[kMxRBW];
 #pragma unroll
-      for (int b = 0; b < kMxRBW; ++b) {
-        wa[b] = wring[d][b];
-        sa[b] = scur[b][u >> 2] >> (8 * (u & 3));
-      }
-      w_issue(d, c + kMxDepth);   // this ring entry is free again
-#pragma unroll
-      for (int tb = 0; tb < kMxTBM; ++tb) {
-        if (tb < ntb) {
-          const int t = 16 * tb + l16;
-          const u32x4 bb = *reinterpret_cast<const u32x4*>(base + t * kMxTok + 16 * g);
-          const uint32_t sb = base[kMxCodes + t * 4 + g];
-#pragma unroll
-          for (int b = 0; b < kMxRBW; ++b) acc[b][tb] = mfma_mx(wa[b], sa[b], bb, sb, acc[b][tb]);
+        for (int b = 0; b < kMxRBW; ++b) {
+          wa[b] = wring[d][b];
+          sa[b] = scur[b][u >> 2] >> (8 * (u & 3));
         }
-      }
-      b_commit((u + 1) & 1, (c + 1) & 1);
-      if (u == kMxWin - 1) {
+        w_issue(d, c + kMxDepth);   // this ring entry is free again
+        if (c < nch) {
+          u32x4 bb[NTB];
+          uint32_t sb[NTB];
 #pragma unroll
-        for (int b = 0; b < kMxRBW; ++b) scur[b] = snext[b];
+          for (int tb = 0; tb < NTB; ++tb) {
+            const int t = 16 * tb + l16;
+            bb[tb] = *reinterpret_cast<const u32x4*>(base + t * kMxTok + 16 * g);
+            sb[tb] = base[kMxCodes + t * 4 + g];
+          }
+#pragma unroll
+          for (int tb = 0; tb < NTB; ++tb)
+#pragma unroll
+            for (int b = 0; b < kMxRBW; ++b) acc[b][tb] = mfma_mx(wa[b], sa[b], bb[tb], sb[tb], acc[b][tb]);
+        }
+        b_commit((u + 1) & 1, (c + 1) & 1);
+        if (u == kMxWin - 1) {
+#pragma unroll
+          for (int b = 0; b < kMxRBW; ++b) scur[b] = snext[b];
+        }
+        __syncthreads();
       }
-      __syncthreads();
     }
-  }
+  };
+  if (ntb > 4) body(Int<8>{});
+  else if (ntb > 2) body(Int<4>{});
+  else if (ntb > 1) body(Int<2>{});
+  else body(Int<1>{});
 
   const uint32_t amax_bits = store_tile<kMxRBW, kMxTBM, SWIGLU>(p, acc, tc, ntb, M, r0, 1.0f, false, blkrow, lane, 0u);
   merge_amax(p.out_amax, amax_bits, lane);
