@@ -15,7 +15,8 @@ Modules
   nvfp4  -- E2M1 / E4M3 code tables, unpacking, dequantize, quantize.
   mxfp4  -- the MXFP4 variant (group 32, UE8M0 scales): dequantize, quantize.
   moe    -- router, permutation, grouped GEMM, SwiGLU, unpermute-reduce,
-            FP8 activation round trip, the whole MoE layer (W4A16 / W4A4).
+            FP8 activation round trip, the whole MoE layer (W4A16 / W4A4 /
+            MXFP4).
 
 Parity status of each function is stated in its docstring; every function
 here is pinned by a ``-m "not gpu"`` test against something other than

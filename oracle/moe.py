@@ -31,6 +31,10 @@ Readings taken where the pages are silent (listed in the design doc):
     the weights, with one dynamic global scale per activation tensor.
   * FP8 activations: x -> E4M3 with a per-tensor scale amax/448, then back to
     bf16.
+  * MXFP4 layer ("The Benchmark That Confirmed the Ceiling", section "The
+    NVFP4 Pivot", names MXFP4 as the group-32 UE8M0 alternative): weights,
+    token activations and h are all MXFP4 (rule in ``oracle/mxfp4.py``);
+    there is no per-tensor scale, so h needs no amax pass.
 
 Parity status: every function is pinned in tests/test_oracle_moe.py
 (brute-force sorting, library argsort, exact rational arithmetic on tiny
@@ -40,7 +44,7 @@ from __future__ import annotations
 
 import numpy as np
 
-from . import nvfp4
+from . import mxfp4, nvfp4
 
 
 # ----------------------------------------------------------------- roundings
@@ -213,7 +217,9 @@ def moe_layer(x, logits, k, w13, w2, mode="w4a16", return_stages=False):
     ``x`` float32 [T, H] holding bf16 values (the activations as the GPU sees
     them); ``logits`` float32 [T, E]; ``w13`` / ``w2``: callables e -> (packed,
     scales, g) NVFP4 triples of W13_e [2F, H] and W2_e [H, F] (so that only
-    touched experts are decoded). ``mode`` "w4a16" or "w4a4".
+    touched experts are decoded), or (packed, scales) MXFP4 pairs in mode
+    "mxfp4". ``mode`` "w4a16", "w4a4" (NVFP4 activations and h) or "mxfp4"
+    (MXFP4 weights, activations and h).
     Returns the bf16-rounded output [T, H] as float64 (and the stages).
     """
     x = np.asarray(x, dtype=np.float32)
@@ -223,22 +229,24 @@ def moe_layer(x, logits, k, w13, w2, mode="w4a16", return_stages=False):
     perm = permute(ids, E)
     tok = perm["sorted_slot"].astype(np.int64) // k
     st = dict(ids=ids, w=w, perm=perm)
+    assert mode in ("w4a16", "w4a4", "mxfp4"), mode
+    fmt = mxfp4 if mode == "mxfp4" else nvfp4
     if mode == "w4a16":
         A = x.astype(np.float64)[tok]
     else:
-        qa = quantize_rows_nvfp4(x)
+        qa = quantize_rows_nvfp4(x) if mode == "w4a4" else mxfp4.quantize(x)
         st["xq"] = qa
-        A = nvfp4.dequantize(*qa)[tok]
-    dq13 = lambda e: nvfp4.dequantize(*w13(e))
-    dq2 = lambda e: nvfp4.dequantize(*w2(e))
+        A = fmt.dequantize(*qa)[tok]
+    dq13 = lambda e: fmt.dequantize(*w13(e))
+    dq2 = lambda e: fmt.dequantize(*w2(e))
     h = grouped_gemm(A, perm["offsets"], dq13, "swiglu")
     st["h_exact"] = h
     if mode == "w4a16":
         h = bf16_round(h)
     else:
-        hq = nvfp4.quantize(h.astype(np.float32))
+        hq = fmt.quantize(h.astype(np.float32))
         st["hq"] = hq
-        h = nvfp4.dequantize(*hq)
+        h = fmt.dequantize(*hq)
     st["h"] = h
     Y = grouped_gemm(h, perm["offsets"], dq2, "none")
     st["Y"] = Y

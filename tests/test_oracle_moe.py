@@ -13,7 +13,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import moe, nvfp4
+from oracle import moe, mxfp4, nvfp4
 
 
 # ------------------------------------------------------------------ rounding
@@ -211,6 +211,35 @@ def test_layer_w4a4_uses_quantized_activations():
     assert 0.03 < rel < 0.3                       # activation quantization noise is present
     xq = nvfp4.dequantize(*st["xq"])
     assert np.linalg.norm(xq - x) / np.linalg.norm(x) < 0.12
+
+
+def _mxfp4_random(rng, R, C):
+    return mxfp4.quantize((rng.standard_normal((R, C)) * 0.02).astype(np.float32))
+
+
+def test_layer_mxfp4_with_one_expert_is_a_dense_mxfp4_ffn():
+    """MXFP4 layer with E = 1, k = 1: x and h MXFP4-quantized, the products and SwiGLU
+    computed by torch in float64 from the dequantized operands."""
+    rng = np.random.default_rng(42)
+    T, H, F = 6, 64, 64
+    x = moe.bf16_round(rng.standard_normal((T, H))).astype(np.float32)
+    w13 = _mxfp4_random(rng, 2 * F, H)
+    w2 = _mxfp4_random(rng, H, F)
+    out, st = moe.moe_layer(x, np.zeros((T, 1), np.float32), 1, lambda e: w13, lambda e: w2,
+                            mode="mxfp4", return_stages=True)
+    X = torch.from_numpy(mxfp4.dequantize(*mxfp4.quantize(x)))
+    W13 = torch.from_numpy(mxfp4.dequantize(*w13))
+    W2 = torch.from_numpy(mxfp4.dequantize(*w2))
+    G = X @ W13.T
+    h = torch.nn.functional.silu(G[:, :F]) * G[:, F:]
+    hq = torch.from_numpy(mxfp4.dequantize(*mxfp4.quantize(h.float().numpy())))
+    ref = (hq @ W2.T).float().to(torch.bfloat16).double().numpy()
+    assert np.array_equal(st["xq"][0], mxfp4.quantize(x)[0])
+    rel = np.linalg.norm(out - ref) / np.linalg.norm(ref)
+    assert rel < 4e-3                             # bf16 output rounding may differ by one ulp
+    np.testing.assert_allclose(st["h_exact"], h.numpy(), rtol=1e-12, atol=1e-15)
+    # h is re-quantized: the down GEMM's input sits on the MXFP4 grid, not on bf16's
+    assert np.linalg.norm(st["h"] - st["h_exact"]) / np.linalg.norm(st["h_exact"]) > 0.02
 
 
 def test_fp8_roundtrip_matches_torch_cast_path():
