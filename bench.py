@@ -13,7 +13,7 @@ recorded on the kernels' stream inside the timed region), and the oracle's CPU r
 bounded sample of the same workload.
 
 Usage: python bench.py [--steps K] [--warmup W] [--tokens T] [--workload NAME]
-       [--no-cpu-baseline] [--sweep FILE] [--copy-calibration]
+       [--format nvfp4|mxfp4] [--no-cpu-baseline] [--sweep FILE] [--copy-calibration]
 """
 from __future__ import annotations
 
@@ -40,6 +40,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--workload", default="decode")
     p.add_argument("--tokens", type=int, default=None)
+    p.add_argument("--format", default="nvfp4", choices=["nvfp4", "mxfp4"],
+                   help="mxfp4: the layer with MXFP4 weights, activations and h (W4A4 on the scaled "
+                        "FP4 matrix cores)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--sweep", default=None, help="also write per-T results of the workload's sweep to FILE")
@@ -79,13 +82,17 @@ def main():
     wl = inputs.WORKLOADS[args.workload]
     T = args.tokens or wl.T
     mode = ops.W4A16 if wl.mode == "w4a16" else ops.W4A4
+    mx = args.format == "mxfp4"
+    if mx:
+        mode = MXFP4
     t0 = time.time()
-    w = layer.quantize_experts(wl, dev)
+    w = None if wl.name == "dense" else (layer.quantize_experts_mxfp4(wl, dev) if mx else layer.quantize_experts(wl, dev))
     x = inputs.activations_bf16(wl, T).to(dev)
     lg = inputs.router_logits(wl, T).to(dev)
     torch.cuda.synchronize()
     setup_s = time.time() - t0
-    print(f"[bench] setup {setup_s:.1f}s: {wl.name} T={T} E={wl.E} k={wl.k} H={wl.H} F={wl.F} mode={wl.mode}",
+    print(f"[bench] setup {setup_s:.1f}s: {wl.name} T={T} E={wl.E} k={wl.k} H={wl.H} F={wl.F} "
+          f"mode={'mxfp4' if mx else wl.mode}",
           file=sys.stderr, flush=True)
 
     if wl.name == "dense":
@@ -98,11 +105,13 @@ def main():
         ms_per_step=round(res["ms_per_step"], 4), higher_is_better=True, scaling="weak",
         vs_baseline=(round(res["tflops"] / PAGES_DECODE_TFLOPS[1], 2)
                      if (wl.name == "decode" and T == 512) else None),
-        dtype="f16", data="synthetic",
-        config=dict(workload=describe(wl, T), tokens=T, experts=wl.E, top_k=wl.k, hidden=wl.H,
-                    ffn=wl.F, mode=wl.mode.upper(), tokens_per_expert=round(T * wl.k / wl.E, 3),
-                    touched_experts=res["touched"], compute="NVFP4 weights decoded exactly to f16, "
-                    "v_mfma_f32_16x16x32_f16, fp32 accumulation"),
+        dtype="fp4" if mx else "f16", data="synthetic",
+        config=dict(workload=describe(wl, T, mx), tokens=T, experts=wl.E, top_k=wl.k, hidden=wl.H,
+                    ffn=wl.F, mode="MXFP4 W4A4" if mx else wl.mode.upper(),
+                    tokens_per_expert=round(T * wl.k / wl.E, 3), touched_experts=res["touched"],
+                    compute=("MXFP4 weights and activations on v_mfma_scale_f32_16x16x128_f8f6f4 (UE8M0 "
+                             "scales applied by the matrix cores), fp32 accumulation" if mx else
+                             "NVFP4 weights decoded exactly to f16, v_mfma_f32_16x16x32_f16, fp32 accumulation")),
         weight_GBps=round(res["weight_gbs"], 1),
         weight_hbm_frac=round(res["weight_gbs"] / HBM_PEAK_GBS, 4),
         stage_us=res["stage_us"], up_gemm_path=res["up_path"],
@@ -111,7 +120,7 @@ def main():
                           "top-8, 512 concurrent) on RTX PRO 6000 Blackwell SM120; vs_baseline divides by 55"),
     )
     if line["roofline"] is not None:
-        line["roofline"]["traffic"] = measured_traffic(wl, T)
+        line["roofline"]["traffic"] = None if mx else measured_traffic(wl, T)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(torch, wl, w, x, lg, T, mode, args.cpu_seconds)
     else:
@@ -155,17 +164,24 @@ def measured_traffic(wl, T):
     return int(m_b.group(1))
 
 
-def describe(wl, T):
+def describe(wl, T, mx=False):
     return (f"{wl.name} MoE layer: {wl.E} experts, top-{wl.k}, {T} tokens, hidden {wl.H}, "
-            f"expert FFN {wl.F}, {wl.mode.upper()}" + (", FP8 activations" if wl.act == "fp8" else "")
+            f"expert FFN {wl.F}, " + ("MXFP4 W4A4" if mx else wl.mode.upper())
+            + (", FP8 activations" if wl.act == "fp8" else "")
             + (f", Zipf({wl.zipf}) routing bias" if wl.zipf else ""))
 
 
-def layer_work(wl, T, touched):
+MXFP4 = "mxfp4"   # bench-local tag for the MXFP4 layer (not a library mode)
+
+
+def layer_work(wl, T, touched, mx=False):
+    """Algorithmic flops and the touched experts' weight bytes: packed codes (1/2 B) plus
+    E4M3 scales per 16 (1/16 B) for NVFP4, UE8M0 scales per 32 (1/32 B) for MXFP4."""
     S = T * wl.k
+    bpw = 17 / 32 if mx else 9 / 16
     flops = 2.0 * S * (2 * wl.F * wl.H + wl.H * wl.F)
-    w13 = touched * (2 * wl.F) * wl.H * 9 / 16          # packed (1/2 B) + E4M3 scales (1/16 B)
-    w2 = touched * wl.H * wl.F * 9 / 16
+    w13 = touched * (2 * wl.F) * wl.H * bpw
+    w2 = touched * wl.H * wl.F * bpw
     return flops, w13, w2
 
 
@@ -177,7 +193,8 @@ def measure(torch, ops, layer, wl, w, x, lg, T, mode, steps, warmup, graph=False
     r = ops.moe_route_permute(lg, k)
     torch.cuda.synchronize()
     touched = int(r["n_active"].item())
-    flops, w13_bytes, w2_bytes = layer_work(wl, T, touched)
+    mx = mode == MXFP4
+    flops, w13_bytes, w2_bytes = layer_work(wl, T, touched, mx)
 
     paths = {}
 
@@ -189,7 +206,18 @@ def measure(torch, ops, layer, wl, w, x, lg, T, mode, steps, warmup, graph=False
         mark(1)
         common = dict(expert_offsets=rr["expert_offsets"], active_experts=rr["active_experts"],
                       n_active=rr["n_active"])
-        if mode == ops.W4A16:
+        if mx:
+            xq, xs = ops.mxfp4_quantize(xx)
+            mark(2)
+            h = ops.moe_grouped_gemm_mxfp4(ops.EPI_SWIGLU, xq, xs, w.w13_t, gather_index=rr["sorted_slot"],
+                                           gather_div=k, rows=S, out_dtype=torch.float32, **common)
+            mark(3)
+            paths["up"] = "mx"
+            hq, hs = ops.mxfp4_quantize(h)
+            mark(4)
+            y = ops.moe_grouped_gemm_mxfp4(ops.EPI_NONE, hq, hs, w.w2_t, rows=S, out_dtype=torch.float32,
+                                           **common)
+        elif mode == ops.W4A16:
             mark(2)
             h = ops.moe_grouped_gemm_nvfp4(ops.W4A16, ops.EPI_SWIGLU, xx, w.w13_t,
                                            gather_index=rr["sorted_slot"], gather_div=k, rows=S,
@@ -244,16 +272,25 @@ def measure(torch, ops, layer, wl, w, x, lg, T, mode, steps, warmup, graph=False
         names = ["route_permute", "quantize_x", "up_gate_swiglu", "quantize_h", "down", "unpermute_reduce"]
         stage = {n: round(1e3 * sum(e[j].elapsed_time(e[j + 1]) for e in evs) / steps, 2)
                  for j, n in enumerate(names)}
-    act_in = T * wl.H * (2 if mode == ops.W4A16 else 9 / 16)
+    act_in = T * wl.H * (2 if mode == ops.W4A16 else (17 / 32 if mx else 9 / 16))
     h_bytes = S * wl.F * (2 if mode == ops.W4A16 else 4)
     up_bytes = w13_bytes + act_in + h_bytes
     up_flops = 2.0 * S * 2 * wl.F * wl.H
     res = dict(ms_per_step=ms, tflops=flops / (ms * 1e-3) / 1e12,
                weight_gbs=(w13_bytes + w2_bytes) / (ms * 1e-3) / 1e9, touched=touched, stage_us=stage,
-               up_path="mfma" if up_path == ops.PATH_MFMA else "stream")
+               up_path="mx" if mx else ("mfma" if up_path == ops.PATH_MFMA else "stream"))
     if stage:
         up_us = stage["up_gate_swiglu"]
-        if up_path == ops.PATH_MFMA:
+        if mx:
+            ach = up_flops / (up_us * 1e-6) / 1e12
+            res["roofline"] = dict(
+                bound="mfma", kernel="gemm_mx_kernel (MXFP4 up/gate + SwiGLU)", achieved=round(ach, 1),
+                peak=FP4_PEAK_TFLOPS, unit="TFLOP/s", frac=round(ach / FP4_PEAK_TFLOPS, 4), traffic=None,
+                flops_per_launch=up_flops, launch_us=up_us,
+                flops_note="2*S*2F*H useful flops (rows of ragged m-tiles padded on the GPU are not counted); "
+                           "dense FP4 MFMA peak",
+                weight_GBps_up=round(w13_bytes / (up_us * 1e-6) / 1e9, 1))
+        elif up_path == ops.PATH_MFMA:
             ach = up_flops / (up_us * 1e-6) / 1e12
             res["roofline"] = dict(
                 bound="mfma", kernel="gemm_stream_kernel large-M (up/gate + SwiGLU)", achieved=round(ach, 1),
@@ -335,7 +372,9 @@ def cpu_baseline(torch, wl, w, x, lg, T, mode, seconds):
     about `seconds`, scaled to TFLOP/s of algorithmic work."""
     import numpy as np
     from oracle import moe as omoe
+    from oracle import mxfp4 as omx
     from oracle import nvfp4 as onv
+    mx = mode == MXFP4
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
@@ -345,19 +384,28 @@ def cpu_baseline(torch, wl, w, x, lg, T, mode, seconds):
     ids, rw = omoe.route(lgn, wl.k)
     perm = omoe.permute(ids, wl.E)
     xs = x.float().cpu().numpy().astype(np.float64)
+    if mx:   # the MXFP4 layer's activations as the GEMM sees them
+        xs = omx.dequantize(*omx.quantize(xs.astype(np.float32)))
     tok = perm["sorted_slot"] // wl.k
     offsets = perm["offsets"]
     order = [int(e) for e in perm["active"]]
     done_rows, done_experts, flops = 0, 0, 0.0
     t_total = 0.0
     for e in order:
-        q13 = (w.w13_packed[e].cpu().numpy(), w.w13_scales[e].cpu().numpy(), w.w13_g[e].item())
-        q2 = (w.w2_packed[e].cpu().numpy(), w.w2_scales[e].cpu().numpy(), w.w2_g[e].item())
+        if mx:
+            q13 = (w.w13_packed[e].cpu().numpy(), w.w13_scales[e].cpu().numpy())
+            q2 = (w.w2_packed[e].cpu().numpy(), w.w2_scales[e].cpu().numpy())
+            dq = omx.dequantize
+        else:
+            q13 = (w.w13_packed[e].cpu().numpy(), w.w13_scales[e].cpu().numpy(), w.w13_g[e].item())
+            q2 = (w.w2_packed[e].cpu().numpy(), w.w2_scales[e].cpu().numpy(), w.w2_g[e].item())
+            dq = onv.dequantize
         r0, r1 = int(offsets[e]), int(offsets[e + 1])
         t0 = time.perf_counter()
         A = xs[tok[r0:r1]]
-        h = omoe.bf16_round(omoe.swiglu(A @ onv.dequantize(*q13).T))
-        _ = h @ onv.dequantize(*q2).T
+        G = omoe.swiglu(A @ dq(*q13).T)
+        h = omx.dequantize(*omx.quantize(G.astype(np.float32))) if mx else omoe.bf16_round(G)
+        _ = h @ dq(*q2).T
         t_total += time.perf_counter() - t0
         done_rows += r1 - r0
         done_experts += 1
@@ -366,7 +414,8 @@ def cpu_baseline(torch, wl, w, x, lg, T, mode, seconds):
             break
     return dict(value=round(flops / t_total / 1e12, 6), unit="TFLOP/s", cores=int(threads), kind="oracle",
                 sample=f"{done_experts} of {len(order)} active experts ({done_rows} of {T * wl.k} routed rows) "
-                       f"of the same layer: float64 dequantize + up/gate + SwiGLU + down, {t_total:.1f} s")
+                       f"of the same layer: float64 dequantize + up/gate + SwiGLU"
+                       f"{' + h requantize' if mx else ''} + down, {t_total:.1f} s")
 
 
 if __name__ == "__main__":

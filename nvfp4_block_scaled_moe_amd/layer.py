@@ -95,3 +95,61 @@ def moe_forward(x: torch.Tensor, logits: torch.Tensor, k: int, w: NVFP4Experts, 
         st.update(h=h, y=y, out=out)
         return out, st
     return out
+
+
+@dataclass
+class MXFP4Experts:
+    """MXFP4 expert weights (group-32 UE8M0 scales, no per-tensor scale), same shapes as
+    NVFP4Experts: row-major as quantized, and tiled for the GEMM."""
+    w13_packed: torch.Tensor   # uint8 [E, 2F, H/2]
+    w13_scales: torch.Tensor   # uint8 [E, 2F, H/32]
+    w2_packed: torch.Tensor    # uint8 [E, H, F/2]
+    w2_scales: torch.Tensor    # uint8 [E, H, F/32]
+    w13_t: ops.MxTiledWeights = None
+    w2_t: ops.MxTiledWeights = None
+
+    @property
+    def E(self):
+        return self.w13_packed.shape[0]
+
+
+def quantize_experts_mxfp4(wl: inputs.Workload, device="cuda") -> MXFP4Experts:
+    """The workload's seeded FP32 expert weights (the same values quantize_experts starts
+    from), quantized one expert at a time with mxfp4_quantize, then tiled."""
+    E, H, F = wl.E, wl.H, wl.F
+    u8 = dict(dtype=torch.uint8, device=device)
+    w = MXFP4Experts(torch.empty((E, 2 * F, H // 2), **u8), torch.empty((E, 2 * F, H // 32), **u8),
+                     torch.empty((E, H, F // 2), **u8), torch.empty((E, H, F // 32), **u8))
+    for e in range(E):
+        p, sc = ops.mxfp4_quantize(inputs.expert_weight_fp32(wl, "w13", e, device))
+        w.w13_packed[e].copy_(p)
+        w.w13_scales[e].copy_(sc)
+        p, sc = ops.mxfp4_quantize(inputs.expert_weight_fp32(wl, "w2", e, device))
+        w.w2_packed[e].copy_(p)
+        w.w2_scales[e].copy_(sc)
+    w.w13_t = ops.mxfp4_weights_tile(w.w13_packed, w.w13_scales)
+    w.w2_t = ops.mxfp4_weights_tile(w.w2_packed, w.w2_scales)
+    return w
+
+
+def moe_forward_mxfp4(x: torch.Tensor, logits: torch.Tensor, k: int, w: MXFP4Experts,
+                      keep: bool = False):
+    """One MoE layer forward in MXFP4 W4A4: token rows and h are MXFP4-quantized (one UE8M0
+    scale per 32 elements, no per-tensor scale, so h needs no amax); both GEMMs run on the
+    scaled FP4 matrix cores. ``x`` bf16 [T, H]; ``logits`` f32 [T, E]."""
+    st = {}
+    r = ops.moe_route_permute(logits, k)
+    st.update(r)
+    S = x.shape[0] * k
+    common = dict(expert_offsets=r["expert_offsets"], active_experts=r["active_experts"],
+                  n_active=r["n_active"])
+    xq, xs = ops.mxfp4_quantize(x)
+    h = ops.moe_grouped_gemm_mxfp4(ops.EPI_SWIGLU, xq, xs, w.w13_t, gather_index=r["sorted_slot"],
+                                   gather_div=k, rows=S, out_dtype=torch.float32, **common)
+    hq, hs = ops.mxfp4_quantize(h)
+    y = ops.moe_grouped_gemm_mxfp4(ops.EPI_NONE, hq, hs, w.w2_t, rows=S, out_dtype=torch.float32, **common)
+    out = ops.moe_unpermute_reduce(y, r["slot_to_row"], r["topk_w"])
+    if keep:
+        st.update(xq=xq, xs=xs, h=h, hq=hq, hs=hs, y=y, out=out)
+        return out, st
+    return out

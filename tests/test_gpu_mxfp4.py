@@ -161,3 +161,81 @@ def test_grouped_gemm_mxfp4_rejects_unsupported_nw():
         ops.moe_grouped_gemm_mxfp4(ops.EPI_NONE, d["ap"], d["as_"], wt, t(d["offsets"]), t(d["active"]),
                                    t(d["n_active"]), rows=d["rows"])
     assert ei.value.status == _lib.ERR_UNSUPPORTED
+
+
+# ------------------------------------------------------------------ the MXFP4 layer
+def _mx_oracle_experts(w):
+    return (lambda e: (np_(w.w13_packed[e]), np_(w.w13_scales[e])),
+            lambda e: (np_(w.w2_packed[e]), np_(w.w2_scales[e])))
+
+
+def test_tiny_mxfp4_layer_end_to_end():
+    from nvfp4_block_scaled_moe_amd import layer
+    wl = inputs.WORKLOADS["tiny"]
+    say("tiny mxfp4 layer")
+    w = layer.quantize_experts_mxfp4(wl, DEV)
+    x = inputs.activations_bf16(wl)
+    lg = inputs.router_logits(wl)
+    out, st = layer.moe_forward_mxfp4(x.to(DEV), lg.to(DEV), wl.k, w, keep=True)
+    torch.cuda.synchronize()
+    w13, w2 = _mx_oracle_experts(w)
+    for e in range(wl.E):   # weight quantization bit-exact
+        po, so = omx.quantize(inputs.expert_weight_fp32(wl, "w13", e).numpy())
+        assert np.array_equal(w13(e)[0], po) and np.array_equal(w13(e)[1], so)
+    want, ost = omoe.moe_layer(x.float().numpy(), lg.numpy(), wl.k, w13, w2, mode="mxfp4", return_stages=True)
+    got = np_(out)
+    assert_finite(got)
+    assert np.array_equal(np_(st["topk_ids"]), ost["ids"])
+    assert np.array_equal(np_(st["xq"]), ost["xq"][0]) and np.array_equal(np_(st["xs"]), ost["xq"][1])
+    r = rel_fro(got, want)
+    say("tiny mxfp4 layer rel err", r)
+    assert r <= W4A4_TOL
+
+
+def test_prefill_mxfp4_layer_full_size():
+    """The prefill workload (8192 tokens, 256 experts, top-8, H=7168, F=2048, Zipf routing)
+    in MXFP4, exactly the calls the benchmark times: routing in full, activation and h codes
+    in full (the oracle quantizes the GPU's fp32 h), both GEMMs on sampled experts, the
+    reduce in full."""
+    from nvfp4_block_scaled_moe_amd import layer
+    wl = inputs.WORKLOADS["prefill"]
+    T = wl.T
+    say("full-size mxfp4 layer", wl.name, T)
+    w = layer.quantize_experts_mxfp4(wl, DEV)
+    x = inputs.activations_bf16(wl, T).to(DEV)
+    lg = inputs.router_logits(wl, T)
+    out, st = layer.moe_forward_mxfp4(x, lg.to(DEV), wl.k, w, keep=True)
+    torch.cuda.synchronize()
+    ids, rw = omoe.route(lg.numpy(), wl.k)
+    perm = omoe.permute(ids, wl.E)
+    assert np.array_equal(np_(st["topk_ids"]), ids)
+    for key, ref in [("expert_offsets", perm["offsets"]), ("sorted_slot", perm["sorted_slot"]),
+                     ("slot_to_row", perm["slot_to_row"])]:
+        assert np.array_equal(np_(st[key]), ref), key
+    xq = omx.quantize(np_(x).astype(np.float32))
+    assert np.array_equal(np_(st["xq"]), xq[0]) and np.array_equal(np_(st["xs"]), xq[1])
+    h32 = np_(st["h"]).astype(np.float32)
+    hq = omx.quantize(h32)
+    assert np.array_equal(np_(st["hq"]), hq[0]) and np.array_equal(np_(st["hs"]), hq[1])
+    A_all = omx.dequantize(*xq)
+    h_in = omx.dequantize(*hq)
+    y = np_(st["y"]).astype(np.float64)
+    offsets = perm["offsets"]
+    tok = perm["sorted_slot"] // wl.k
+    counts = np.diff(offsets)
+    act = np.nonzero(counts)[0]
+    order = act[np.argsort(counts[act], kind="stable")]
+    for e in sorted({int(order[-1]), int(order[len(order) // 2]), int(order[0])}):
+        r0, r1 = int(offsets[e]), int(offsets[e + 1])
+        po, so = omx.quantize(inputs.expert_weight_fp32(wl, "w13", e, DEV).cpu().numpy())
+        assert np.array_equal(np_(w.w13_packed[e]), po) and np.array_equal(np_(w.w13_scales[e]), so)
+        hw = omoe.swiglu(A_all[tok[r0:r1]] @ omx.dequantize(po, so).T)
+        rh = rel_fro(h32[r0:r1], hw)
+        W2 = omx.dequantize(np_(w.w2_packed[e]), np_(w.w2_scales[e]))
+        ry = rel_fro(y[r0:r1], h_in[r0:r1] @ W2.T)
+        say(f"expert {e}: rows {r1 - r0} rel(h) {rh:.2e} rel(Y) {ry:.2e}")
+        assert rh < 1e-5 and ry < 1e-5
+    want = omoe.bf16_round(omoe.unpermute_reduce(y, perm["slot_to_row"], np_(st["topk_w"]).astype(np.float64)))
+    got = np_(out)
+    assert_finite(got, h32, y)
+    assert rel_fro(got, want) <= 1e-3
