@@ -180,7 +180,7 @@ def test_tiny_mxfp4_layer_end_to_end():
     torch.cuda.synchronize()
     w13, w2 = _mx_oracle_experts(w)
     for e in range(wl.E):   # weight quantization bit-exact
-        po, so = omx.quantize(inputs.expert_weight_fp32(wl, "w13", e).numpy())
+        po, so = omx.quantize(inputs.expert_weight_fp32(wl, "w13", e, DEV).cpu().numpy())
         assert np.array_equal(w13(e)[0], po) and np.array_equal(w13(e)[1], so)
     want, ost = omoe.moe_layer(x.float().numpy(), lg.numpy(), wl.k, w13, w2, mode="mxfp4", return_stages=True)
     got = np_(out)
