@@ -18,11 +18,18 @@
 //     and the matching up block) x one m-tile (8 token blocks of 16; a ragged m-tile runs
 //     with 1, 2, 4 or 8 blocks).
 //   * Per chunk (128 k) each thread stages 16 bytes of codes and one scale byte of one token
-//     (512 threads = 128 tokens x 4 k-blocks) through registers into a two-slot LDS ring;
+//     (512 threads = 128 tokens x 4 k-blocks) through registers into a three-slot LDS ring;
 //     token rows are padded to 80 bytes, so the 16 lanes of a fragment read hit distinct
-//     banks. Weights are loaded two chunks ahead into registers.
-//   * 16 MFMAs (16x16x128) per wave and chunk; epilogue as in the other GEMMs with alpha 1
-//     (MXFP4 has no per-tensor scale): SwiGLU, bf16 or f32 stores, amax.
+//     banks. The scale bytes of a chunk sit in LDS as [k-block][row in block][token block],
+//     so one 8-byte read gives a lane the scales of all 8 token blocks and the MFMA's byte
+//     select (opsel) picks each one. Weights are loaded two chunks ahead into registers.
+//   * Step c issues the 16 MFMAs (16x16x128) of chunk c on fragments read in step c-1 and
+//     meanwhile reads chunk c+1's fragments, commits chunk c+2 to the ring and requests chunk
+//     c+3: the reads never wait behind the barrier that ends the step. Epilogue as in the
+//     other GEMMs with alpha 1 (MXFP4 has no per-tensor scale): SwiGLU, bf16 or f32 stores,
+//     amax.
+#include <utility>
+
 #include "gemm_common.h"
 
 namespace nvfp4moe {
@@ -36,22 +43,36 @@ constexpr int kMxWin = 16;                          // chunks per scale tile (20
 constexpr int kMxTok = 80;                          // LDS bytes per token and chunk (64 + pad)
 constexpr int kMxCodes = 16 * kMxTBM * kMxTok;      // 10240
 constexpr int kMxSlot = kMxCodes + 16 * kMxTBM * 4; // + 4 scale bytes per token
+constexpr int kMxSlots = 3;                         // LDS ring slots
 constexpr int kMxDepth = 2;                         // weight chunks in flight
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 
+// FP4 x FP4 with one UE8M0 scale per lane for each operand; OA / OB select the scale byte
+// within the 32-bit scale registers.
+template <int OA, int OB>
 __device__ __forceinline__ f32x4 mfma_mx(u32x4 a, uint32_t sa, u32x4 b, uint32_t sb, f32x4 c) {
   const v8i A = {(int)a[0], (int)a[1], (int)a[2], (int)a[3], 0, 0, 0, 0};
   const v8i B = {(int)b[0], (int)b[1], (int)b[2], (int)b[3], 0, 0, 0, 0};
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, c, 4, 4, 0, (int)(sa & 0xffu), 0,
-                                                          (int)(sb & 0xffu));
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, c, 4, 4, OA, (int)sa, OB, (int)sb);
+}
+
+// f(Int<0>{}), ..., f(Int<N-1>{}): loop indices usable as template arguments (the byte
+// selects of the MFMA are immediates).
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(Int<I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 template <bool SWIGLU>
 __global__ __launch_bounds__(kMxWaves* kWave) void gemm_mx_kernel(const GemmArgs p, int ntiles_n) {
   constexpr int NT = kMxWaves * kWave;
   static_assert(NT == 16 * kMxTBM * 4, "one thread per token and 32-wide k block of a chunk");
-  __shared__ __attribute__((aligned(16))) unsigned char smem[2 * kMxSlot];
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kMxSlots * kMxSlot];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -98,7 +119,7 @@ __global__ __launch_bounds__(kMxWaves* kWave) void gemm_mx_kernel(const GemmArgs
                                : 0u;
   const uint32_t csrc = tok_ok ? arow * (uint32_t)Kh + 16u * q : kOOB;
   const uint32_t ssrc = tok_ok ? arow * (uint32_t)Ks + q : kOOB;
-  const uint32_t cdst = tk * kMxTok + 16 * q, sdst = kMxCodes + tk * 4 + q;
+  const uint32_t cdst = tk * kMxTok + 16 * q, sdst = kMxCodes + q * 128 + (tk & 15) * 8 + (tk >> 4);
 
   u32x4 bst[2];
   uint32_t bsc[2];
@@ -129,59 +150,74 @@ __global__ __launch_bounds__(kMxWaves* kWave) void gemm_mx_kernel(const GemmArgs
 #pragma unroll
     for (int tb = 0; tb < kMxTBM; ++tb) acc[b][tb] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  // prologue: scales of window 0, weights and activations of chunks 0 and 1
+  // prologue: scales of window 0, weights of chunks 0 and 1, activations of chunks 0 and 1
+  // committed to slots 0 and 1, chunk 2 requested (staging set 0)
   s_issue(0);
 #pragma unroll
   for (int b = 0; b < kMxRBW; ++b) scur[b] = snext[b];
   b_issue(0, 0);
   b_issue(1, 1);
-  w_issue(0, 0);
-  w_issue(1, 1);
+#pragma unroll
+  for (int d = 0; d < kMxDepth; ++d) w_issue(d, d);
   b_commit(0, 0);
+  b_commit(1, 1);
+  b_issue(0, 2);
   __syncthreads();
 
   // The main loop, compiled for NTB = 8, 4, 2 or 1 token blocks (ntb rounded up; blocks past
-  // the m-tile's rows hold zeros). Chunk c: LDS slot c & 1, staging set c & 1, weight ring
-  // entry c % kMxDepth. Whole scale windows; the MFMAs of chunks past K are skipped.
+  // the m-tile's rows hold zeros). Chunk c lives in LDS slot c % 3 and staging set c & 1,
+  // its weights in ring entry c % kMxDepth. Step c: request chunk c+3 (set (c+1) & 1, whose
+  // chunk c+1 was committed in step c-1), read chunk c+1's fragments (committed in step c-1),
+  // MFMAs of chunk c, commit chunk c+2 to slot (c+2) % 3 (chunk c-1, read in step c-2), barrier.
+  // Whole scale windows; the MFMAs of chunks past K are skipped.
   auto body = [&](auto ntb_tag) {
     constexpr int NTB = decltype(ntb_tag)::value;
+    u32x4 bcur[NTB], bnext[NTB];
+    uint32_t scb[2], scbn[2];
+    auto b_read = [&](u32x4 (&bb)[NTB], uint32_t (&sc)[2], int slot) {
+      const unsigned char* base = smem + slot * kMxSlot;
+#pragma unroll
+      for (int tb = 0; tb < NTB; ++tb) bb[tb] = *reinterpret_cast<const u32x4*>(base + (16 * tb + l16) * kMxTok + 16 * g);
+      const uint2 sv = *reinterpret_cast<const uint2*>(base + kMxCodes + g * 128 + l16 * 8);
+      sc[0] = sv.x;
+      sc[1] = sv.y;
+    };
+    b_read(bcur, scb, 0);
+    int slot = 0;   // c % 3
     for (int c0 = 0; c0 < nwin * kMxWin; c0 += kMxWin) {
       s_issue(c0 / kMxWin + 1);
-#pragma unroll
-      for (int u = 0; u < kMxWin; ++u) {
+      static_for<kMxWin>([&](auto u_tag) {
+        constexpr int u = decltype(u_tag)::value;
         const int c = c0 + u;
-        const int d = u % kMxDepth;
-        b_issue(u & 1, c + 2);   // set u & 1 was committed last step
-        const unsigned char* base = smem + (c & 1) * kMxSlot;
+        constexpr int d = u % kMxDepth;
+        const int slot1 = slot == kMxSlots - 1 ? 0 : slot + 1;
+        const int slot2 = slot1 == kMxSlots - 1 ? 0 : slot1 + 1;
+        b_issue((u + 1) & 1, c + 3);
         u32x4 wa[kMxRBW];
-        uint32_t sa[kMxRBW];
 #pragma unroll
-        for (int b = 0; b < kMxRBW; ++b) {
-          wa[b] = wring[d][b];
-          sa[b] = scur[b][u >> 2] >> (8 * (u & 3));
-        }
+        for (int b = 0; b < kMxRBW; ++b) wa[b] = wring[d][b];
         w_issue(d, c + kMxDepth);   // this ring entry is free again
+        b_read(bnext, scbn, slot1);
         if (c < nch) {
-          u32x4 bb[NTB];
-          uint32_t sb[NTB];
+          static_for<NTB>([&](auto tb_tag) {
+            constexpr int tb = decltype(tb_tag)::value;
 #pragma unroll
-          for (int tb = 0; tb < NTB; ++tb) {
-            const int t = 16 * tb + l16;
-            bb[tb] = *reinterpret_cast<const u32x4*>(base + t * kMxTok + 16 * g);
-            sb[tb] = base[kMxCodes + t * 4 + g];
-          }
-#pragma unroll
-          for (int tb = 0; tb < NTB; ++tb)
-#pragma unroll
-            for (int b = 0; b < kMxRBW; ++b) acc[b][tb] = mfma_mx(wa[b], sa[b], bb[tb], sb[tb], acc[b][tb]);
+            for (int b = 0; b < kMxRBW; ++b)
+              acc[b][tb] = mfma_mx<(u & 3), (tb & 3)>(wa[b], scur[b][u >> 2], bcur[tb], scb[tb >> 2], acc[b][tb]);
+          });
         }
-        b_commit((u + 1) & 1, (c + 1) & 1);
+        b_commit(u & 1, slot2);
         if (u == kMxWin - 1) {
 #pragma unroll
           for (int b = 0; b < kMxRBW; ++b) scur[b] = snext[b];
         }
         __syncthreads();
-      }
+#pragma unroll
+        for (int tb = 0; tb < NTB; ++tb) bcur[tb] = bnext[tb];
+        scb[0] = scbn[0];
+        scb[1] = scbn[1];
+        slot = slot1;
+      });
     }
   };
   if (ntb > 4) body(Int<8>{});
