@@ -165,7 +165,10 @@ size_t nvfp4_tiled_scales_bytes(int64_t R, int64_t C);
  *   active_experts  device int32 [E]     (output) experts with >= 1 row, ascending, in
  *                   entries [0, n_active); the rest are set to -1.
  *   n_active        device int32 [1]     (output)
- *   ws, ws_bytes    moe_route_permute_workspace_size(T, E, k) bytes (currently 0).
+ *   ws, ws_bytes    device scratch of at least moe_route_permute_workspace_size(T, E, k)
+ *                   bytes, 4-byte aligned, caller-owned (per-chunk expert counts of the
+ *                   permutation; contents on return are unspecified). Too small or NULL ->
+ *                   NVFP4MOE_ERR_WORKSPACE. The size query returns 0 for invalid sizes.
  * ------------------------------------------------------------------------- */
 nvfp4moe_status moe_route_permute(const float* logits, int32_t T, int32_t E, int32_t k,
                                   int32_t* topk_ids, float* topk_w, int32_t* expert_offsets,

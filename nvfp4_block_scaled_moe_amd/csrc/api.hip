@@ -152,10 +152,8 @@ nvfp4moe_status nvfp4_quantize(const void* x, nvfp4moe_dtype x_dtype, int64_t B,
 
 // ------------------------------------------------------------------ route + permute
 size_t moe_route_permute_workspace_size(int32_t T, int32_t E, int32_t k) {
-  (void)T;
-  (void)E;
-  (void)k;
-  return 0;
+  if (T < 1 || E < 1 || E > kMaxExperts || k < 1 || k > E || (int64_t)T * k > (1 << 24)) return 0;
+  return route_permute_ws_bytes(T, E, k);
 }
 
 nvfp4moe_status moe_route_permute(const float* logits, int32_t T, int32_t E, int32_t k,
@@ -163,8 +161,6 @@ nvfp4moe_status moe_route_permute(const float* logits, int32_t T, int32_t E, int
                                   int32_t* sorted_slot, int32_t* slot_to_row,
                                   int32_t* active_experts, int32_t* n_active, void* ws,
                                   size_t ws_bytes, void* stream) {
-  (void)ws;
-  (void)ws_bytes;
   if (!logits || !topk_ids || !topk_w || !expert_offsets || !sorted_slot || !slot_to_row ||
       !active_experts || !n_active)
     return fail(NVFP4MOE_ERR_INVALID_ARG, "moe_route_permute: null tensor pointer");
@@ -174,8 +170,14 @@ nvfp4moe_status moe_route_permute(const float* logits, int32_t T, int32_t E, int
                 kMaxTopK, kMaxExperts, T, E, k);
   if ((int64_t)T * k > (1 << 24))
     return fail(NVFP4MOE_ERR_INVALID_ARG, "moe_route_permute: T * k must be <= 2^24");
+  const size_t need = route_permute_ws_bytes(T, E, k);
+  if (ws_bytes < need || (need > 0 && !ws))
+    return fail(NVFP4MOE_ERR_WORKSPACE, "moe_route_permute: workspace of %zu bytes needed, %zu given", need,
+                ws_bytes);
+  if (!aligned(ws, 4))
+    return fail(NVFP4MOE_ERR_INVALID_ARG, "moe_route_permute: workspace must be 4-byte aligned");
   return hip_status(launch_route_permute(logits, T, E, k, topk_ids, topk_w, expert_offsets,
-                                         sorted_slot, slot_to_row, active_experts, n_active,
+                                         sorted_slot, slot_to_row, active_experts, n_active, ws, ws_bytes,
                                          static_cast<hipStream_t>(stream)),
                     "moe_route_permute");
 }

@@ -19,10 +19,12 @@ hipError_t launch_fp8_roundtrip(const void* x, int64_t n, void* out, void* ws, h
 // ---- route.hip
 constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 64;
+// Workspace of launch_route_permute: the per-chunk expert counts of the two-launch permutation.
+size_t route_permute_ws_bytes(int T, int E, int k);
 hipError_t launch_route_permute(const float* logits, int T, int E, int k, int* topk_ids,
                                 float* topk_w, int* expert_offsets, int* sorted_slot,
                                 int* slot_to_row, int* active_experts, int* n_active,
-                                hipStream_t stream);
+                                void* ws, size_t ws_bytes, hipStream_t stream);
 
 // ---- act_prep.hip
 // The m-tile list of the large-M path, built by one extra workgroup of the activation prep

@@ -5,7 +5,8 @@
 //   out[t, :] = bf16( sum_{j<k} w[t, j] * Y[slot_to_row[t*k + j], :] ),
 // float32 fused multiply-adds in ascending j, so the result does not depend on thread
 // timing. HBM-bound: k rows of Y read and one bf16 row written per token; each thread
-// handles 8 consecutive columns with 16/32-byte vector accesses.
+// handles 8 consecutive columns with 16/32-byte vector accesses, and requests the rows of
+// 8 slots at a time so their latencies overlap.
 #include "common.h"
 #include "kernels.h"
 
@@ -14,6 +15,15 @@ namespace nvfp4moe {
 namespace {
 
 constexpr int kRedThreads = 256;
+
+constexpr int kRedBatch = 8;   // slots whose rows are requested together
+
+// Read of a per-token input through the constant address space (the token is uniform over
+// the workgroup, so these become scalar loads).
+template <typename T>
+__device__ __forceinline__ T ld_uniform(const T* p, size_t i) {
+  return ((const __attribute__((address_space(4))) T*)p)[i];
+}
 
 template <bool YBF16>
 __global__ __launch_bounds__(kRedThreads) void unpermute_reduce_kernel(const void* __restrict__ y,
@@ -26,27 +36,45 @@ __global__ __launch_bounds__(kRedThreads) void unpermute_reduce_kernel(const voi
   const int c = ((blockIdx.x - t * cblocks) * kRedThreads + threadIdx.x) * 8;
   if (c >= H) return;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int j = 0; j < k; ++j) {
-    const size_t row = (size_t)slot_to_row[(size_t)t * k + j];
-    const float w = topk_w[(size_t)t * k + j];
-    float v[8];
-    if (YBF16) {
-      uint4 q = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(y) + row * H + c);
-      uint32_t u[4] = {q.x, q.y, q.z, q.w};
+  // Up to kRedBatch rows are requested before the first of them is summed; the sum itself
+  // stays in ascending j.
+  for (int j0 = 0; j0 < k; j0 += kRedBatch) {
+    const int n = min(kRedBatch, k - j0);
+    size_t row[kRedBatch];
+    float w[kRedBatch];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        v[2 * i] = bf16_to_f32(u[i] & 0xffffu);
-        v[2 * i + 1] = bf16_to_f32(u[i] >> 16);
+    for (int j = 0; j < kRedBatch; ++j) {
+      row[j] = j < n ? (size_t)ld_uniform(slot_to_row, (size_t)t * k + j0 + j) : 0;
+      w[j] = j < n ? ld_uniform(topk_w, (size_t)t * k + j0 + j) : 0.f;
+    }
+    float v[kRedBatch][8];
+#pragma unroll
+    for (int j = 0; j < kRedBatch; ++j) {
+      if (j < n) {
+        if (YBF16) {
+          uint4 q = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(y) + row[j] * H + c);
+          uint32_t u[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            v[j][2 * i] = bf16_to_f32(u[i] & 0xffffu);
+            v[j][2 * i + 1] = bf16_to_f32(u[i] >> 16);
+          }
+        } else {
+          const float* yr = static_cast<const float*>(y) + row[j] * H + c;
+          float4 a = *reinterpret_cast<const float4*>(yr);
+          float4 b = *reinterpret_cast<const float4*>(yr + 4);
+          v[j][0] = a.x; v[j][1] = a.y; v[j][2] = a.z; v[j][3] = a.w;
+          v[j][4] = b.x; v[j][5] = b.y; v[j][6] = b.z; v[j][7] = b.w;
+        }
       }
-    } else {
-      const float* yr = static_cast<const float*>(y) + row * H + c;
-      float4 a = *reinterpret_cast<const float4*>(yr);
-      float4 b = *reinterpret_cast<const float4*>(yr + 4);
-      v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-      v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) acc[i] = fmaf(w, v[i], acc[i]);
+    for (int j = 0; j < kRedBatch; ++j) {
+      if (j < n) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = fmaf(w[j], v[j][i], acc[i]);
+      }
+    }
   }
   uint32_t o[4];
 #pragma unroll

@@ -34,6 +34,7 @@ namespace {
 constexpr int kRouterWaves = 4;
 constexpr int kPermThreads = 1024;
 constexpr int kPermWaves = kPermThreads / kWave;
+constexpr int kPermBatch = 16;   // 64-slot groups whose expert ids are loaded together
 
 // Order-preserving uint32 key of a logit (NaN as -inf, -0 as +0): key order = value order.
 __device__ __forceinline__ uint32_t logit_key(float x) {
@@ -200,6 +201,61 @@ __global__ __launch_bounds__(kRouterWaves* kWave) void router_kernel(const float
   }
 }
 
+// Histogram of ids[lo, hi) into one wave's counter row (LDS atomics); the ids of kPermBatch
+// 64-slot groups are requested before any is counted.
+__device__ __forceinline__ void wave_histogram(const int* __restrict__ ids, int lo, int hi, int* cnt, int lane) {
+  for (int s0 = lo; s0 < hi; s0 += kWave * kPermBatch) {
+    int ex[kPermBatch];
+#pragma unroll
+    for (int b = 0; b < kPermBatch; ++b) {
+      const int s = s0 + b * kWave + lane;
+      ex[b] = s < hi ? ids[s] : -1;
+    }
+#pragma unroll
+    for (int b = 0; b < kPermBatch; ++b)
+      if (ex[b] >= 0) atomicAdd(&cnt[ex[b]], 1);
+  }
+}
+
+// Stable scatter of slots [lo, hi) by one wave, 64 slots per step in slot order: cnt[e] holds
+// the next row of expert e for this wave; a lane's rank among the lanes holding the same
+// expert comes from ballots over the bits of the expert id and a popcount of the lower lanes.
+__device__ __forceinline__ void wave_scatter(const int* __restrict__ ids, int lo, int hi, int* cnt, int nbits,
+                                             int lane, int* __restrict__ sorted_slot,
+                                             int* __restrict__ slot_to_row) {
+  for (int sb = lo; sb < hi; sb += kWave * kPermBatch) {
+    int exb[kPermBatch];
+#pragma unroll
+    for (int b = 0; b < kPermBatch; ++b) {
+      const int s = sb + b * kWave + lane;
+      exb[b] = s < hi ? ids[s] : 0;
+    }
+#pragma unroll
+    for (int b = 0; b < kPermBatch; ++b) {
+      const int s0 = sb + b * kWave;
+      if (s0 >= hi) break;
+      const int s = s0 + lane;
+      const bool valid = s < hi;
+      const int ex = exb[b];
+      uint64_t peers = __ballot(valid);
+      for (int bt = 0; bt < nbits; ++bt) {
+        const bool bit = (ex >> bt) & 1;
+        const uint64_t m = __ballot(bit);
+        peers &= bit ? m : ~m;
+      }
+      const int rank = __popcll(peers & ((1ull << lane) - 1ull));
+      const int start = valid ? cnt[ex] : 0;
+      const bool leader = valid && ((peers >> lane) == 1ull);  // highest lane of its group
+      if (leader) cnt[ex] = start + __popcll(peers);
+      if (valid) {
+        const int row = start + rank;
+        sorted_slot[row] = s;
+        slot_to_row[s] = row;
+      }
+    }
+  }
+}
+
 __global__ __launch_bounds__(kPermThreads) void permute_kernel(const int* __restrict__ ids, int S,
                                                                int E, int nbits,
                                                                int* __restrict__ offsets,
@@ -218,7 +274,8 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(const int* __rest
 
   const int per = ((S + kPermWaves - 1) / kPermWaves + kWave - 1) / kWave * kWave;
   const int lo = min(S, wave * per), hi = min(S, lo + per);
-  for (int s = lo + lane; s < hi; s += kWave) atomicAdd(&cnt[wave * E + ids[s]], 1);
+  // 1. per-wave histograms
+  wave_histogram(ids, lo, hi, cnt + wave * E, lane);
   __syncthreads();
 
   // 2. per expert e = tid: prefix over waves, then scans over experts.
@@ -269,36 +326,173 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(const int* __rest
   }
   __syncthreads();
 
-  // 3. stable scatter, 64 slots per step, ranks from ballots.
-  for (int s0 = lo; s0 < hi; s0 += kWave) {
-    const int s = s0 + lane;
-    const bool valid = s < hi;
-    const int ex = valid ? ids[s] : 0;
-    uint64_t peers = __ballot(valid);
-    for (int b = 0; b < nbits; ++b) {
-      const bool bit = (ex >> b) & 1;
-      const uint64_t m = __ballot(bit);
-      peers &= bit ? m : ~m;
-    }
-    const int rank = __popcll(peers & ((1ull << lane) - 1ull));
-    const int start = valid ? cnt[wave * E + ex] : 0;
-    const bool leader = valid && ((peers >> lane) == 1ull);  // highest lane of its group
-    if (leader) cnt[wave * E + ex] = start + __popcll(peers);
-    if (valid) {
-      const int row = start + rank;
-      sorted_slot[row] = s;
-      slot_to_row[s] = row;
-    }
-  }
+  // 3. stable scatter of each wave's slice
+  wave_scatter(ids, lo, hi, cnt + wave * E, nbits, lane, sorted_slot, slot_to_row);
 }
 
+// Many slots: the permutation in two launches over chunks of slots, so that the scattered
+// row writes are spread over many CUs (one workgroup issues about one scattered line per
+// clock). perm_count_kernel: counts[b][e] = rows of expert e in chunk b. perm_scatter_kernel:
+// workgroup b derives every expert's first row (exclusive scan over experts of the totals)
+// and its own first row per expert (the counts of chunks before b), then scatters its chunk
+// wave by wave exactly as the one-workgroup kernel does. Same result, bit for bit.
+constexpr int kPmThreads = 256;
+constexpr int kPmWaves = kPmThreads / kWave;
+constexpr int kPmChunk = 2048;        // slots per workgroup, at least
+constexpr int kPmMaxBlocks = 64;      // chunks grow beyond kPmChunk to keep the count reads small
+constexpr int kPmMinSlots = 16384;    // fewer slots: the one-workgroup kernel
+
+__global__ __launch_bounds__(kPmThreads) void perm_count_kernel(const int* __restrict__ ids, int S, int E,
+                                                                int chunk, int* __restrict__ counts) {
+  extern __shared__ int cnt[];   // [E]
+  const int tid = threadIdx.x;
+  for (int i = tid; i < E; i += kPmThreads) cnt[i] = 0;
+  __syncthreads();
+  const int lo = blockIdx.x * chunk, hi = min(S, lo + chunk);
+  const int wave = tid / kWave, lane = tid % kWave;
+  const int per = ((hi - lo + kPmWaves - 1) / kPmWaves + kWave - 1) / kWave * kWave;
+  const int wlo = min(hi, lo + wave * per), whi = min(hi, wlo + per);
+  wave_histogram(ids, wlo, whi, cnt, lane);
+  __syncthreads();
+  for (int i = tid; i < E; i += kPmThreads) counts[(size_t)blockIdx.x * E + i] = cnt[i];
+}
+
+// Exclusive prefix of v over the threads of the workgroup (thread order); total = sum.
+__device__ __forceinline__ int block_excl_scan(int v, int* red, int& total) {
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  int incl = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int a = __shfl_up(incl, o, kWave);
+    if (lane >= o) incl += a;
+  }
+  if (lane == kWave - 1) red[wave] = incl;
+  __syncthreads();
+  int before = 0;
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < kPmWaves; ++w) {
+    const int x = red[w];
+    if (w < wave) before += x;
+    total += x;
+  }
+  __syncthreads();
+  return before + incl - v;
+}
+
+__global__ __launch_bounds__(kPmThreads) void perm_scatter_kernel(const int* __restrict__ ids, int S, int E,
+                                                                  int nbits, int chunk,
+                                                                  const int* __restrict__ counts, int nblk,
+                                                                  int* __restrict__ offsets,
+                                                                  int* __restrict__ sorted_slot,
+                                                                  int* __restrict__ slot_to_row,
+                                                                  int* __restrict__ active,
+                                                                  int* __restrict__ n_active) {
+  extern __shared__ int sm[];
+  int* wcnt = sm;                     // [kPmWaves][E]
+  int* red = sm + kPmWaves * E;       // [kPmWaves]
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int b = blockIdx.x;
+  // 1. each thread owns up to 4 consecutive experts (E <= 1024): total rows over all chunks
+  //    and rows in the chunks before this one
+  constexpr int EPT = kMaxExperts / kPmThreads;
+  const int ept = (E + kPmThreads - 1) / kPmThreads;
+  const int e0 = min(E, tid * ept);
+  int tot[EPT], pre[EPT];
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) tot[i] = pre[i] = 0;
+#pragma unroll 4
+  for (int bb = 0; bb < nblk; ++bb) {
+#pragma unroll
+    for (int i = 0; i < EPT; ++i) {
+      const int e = e0 + i;
+      if (i < ept && e < E) {
+        const int c = counts[(size_t)bb * E + e];
+        tot[i] += c;
+        pre[i] += bb < b ? c : 0;
+      }
+    }
+  }
+  int tsum = 0, tact = 0;
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) {
+    if (i < ept && e0 + i < E) {
+      tsum += tot[i];
+      tact += tot[i] > 0 ? 1 : 0;
+    }
+  }
+  int total = 0, nact = 0;
+  int run = block_excl_scan(tsum, red, total);
+  int arun = block_excl_scan(tact, red, nact);
+  // 2. offsets and the active list (chunk 0 writes them); this chunk's first row per expert
+  int first[EPT];
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) {
+    const int e = e0 + i;
+    first[i] = 0;
+    if (i < ept && e < E) {
+      if (b == 0) {
+        offsets[e] = run;
+        if (tot[i] > 0) active[arun] = e;
+      }
+      first[i] = run + pre[i];
+      run += tot[i];
+      arun += tot[i] > 0 ? 1 : 0;
+    }
+  }
+  if (b == 0) {
+    if (tid == 0) {
+      offsets[E] = total;
+      n_active[0] = nact;
+    }
+    for (int e = nact + tid; e < E; e += kPmThreads) active[e] = -1;
+  }
+  // 3. per-wave histograms of this chunk, then each wave's first row per expert
+  for (int i = tid; i < kPmWaves * E; i += kPmThreads) wcnt[i] = 0;
+  __syncthreads();
+  const int lo = b * chunk, hi = min(S, lo + chunk);
+  const int per = ((hi - lo + kPmWaves - 1) / kPmWaves + kWave - 1) / kWave * kWave;
+  const int wlo = min(hi, lo + wave * per), whi = min(hi, wlo + per);
+  wave_histogram(ids, wlo, whi, wcnt + wave * E, lane);
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < EPT; ++i) {
+    const int e = e0 + i;
+    if (i < ept && e < E) {
+      int r = first[i];
+#pragma unroll
+      for (int w = 0; w < kPmWaves; ++w) {
+        const int c = wcnt[w * E + e];
+        wcnt[w * E + e] = r;
+        r += c;
+      }
+    }
+  }
+  __syncthreads();
+  // 4. stable scatter of each wave's slice
+  wave_scatter(ids, wlo, whi, wcnt + wave * E, nbits, lane, sorted_slot, slot_to_row);
+}
 
 }  // namespace
+
+namespace {
+void perm_plan(int S, int& chunk, int& nblk) {
+  const int need = (S + kPmMaxBlocks - 1) / kPmMaxBlocks;
+  chunk = need <= kPmChunk ? kPmChunk : (need + kPmThreads - 1) / kPmThreads * kPmThreads;
+  nblk = (S + chunk - 1) / chunk;
+}
+}  // namespace
+
+size_t route_permute_ws_bytes(int T, int E, int k) {
+  int chunk = 0, nblk = 0;
+  perm_plan(T * k, chunk, nblk);
+  return (size_t)nblk * (size_t)E * sizeof(int);
+}
 
 hipError_t launch_route_permute(const float* logits, int T, int E, int k, int* topk_ids,
                                 float* topk_w, int* expert_offsets, int* sorted_slot,
                                 int* slot_to_row, int* active_experts, int* n_active,
-                                hipStream_t stream) {
+                                void* ws, size_t ws_bytes, hipStream_t stream) {
   // Few tokens: a workgroup per token sorts (no serial chain, measured 15.7 -> 9.1 us at one
   // token of 512 experts, top-22); many tokens: a wave per token selects (more tokens per CU;
   // 8192 tokens of 256 experts: 18 us against 33 us sorted). NVFP4MOE_ROUTER=wave|sort forces.
@@ -325,13 +519,30 @@ hipError_t launch_route_permute(const float* logits, int T, int E, int k, int* t
       router_kernel<16><<<rgrid, kRouterWaves * kWave, 0, stream>>>(logits, T, E, k, topk_ids, topk_w);
   }
 
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  const int S = T * k;
+  // Many slots: the two-launch permutation (scattered writes spread over the chunks'
+  // workgroups); NVFP4MOE_PERMUTE=single|multi forces one (tests).
+  const char* pforce = std::getenv("NVFP4MOE_PERMUTE");
+  const bool multi = pforce ? !std::strcmp(pforce, "multi") : S >= kPmMinSlots;
+  if (multi) {
+    int chunk = 0, nblk = 0;
+    perm_plan(S, chunk, nblk);
+    if (!ws || ws_bytes < route_permute_ws_bytes(T, E, k)) return hipErrorInvalidValue;
+    int* counts = static_cast<int*>(ws);
+    perm_count_kernel<<<nblk, kPmThreads, (size_t)E * sizeof(int), stream>>>(topk_ids, S, E, chunk, counts);
+    perm_scatter_kernel<<<nblk, kPmThreads, (size_t)(kPmWaves * E + kPmWaves) * sizeof(int), stream>>>(
+        topk_ids, S, E, nbits, chunk, counts, nblk, expert_offsets, sorted_slot, slot_to_row, active_experts,
+        n_active);
+    return hipGetLastError();
+  }
+
   static std::atomic<uint64_t> perm_attr_done{0};
   const hipError_t attr = ensure_dynamic_lds(reinterpret_cast<const void*>(&permute_kernel),
                                              (kPermWaves * kMaxExperts + 2 * kPermWaves) * (int)sizeof(int),
                                              perm_attr_done);
   if (attr != hipSuccess) return attr;
-  int nbits = 0;
-  while ((1 << nbits) < E) ++nbits;
   const size_t shmem = (size_t)(kPermWaves * E + 2 * kPermWaves) * sizeof(int);
   permute_kernel<<<1, kPermThreads, shmem, stream>>>(topk_ids, T * k, E, nbits, expert_offsets,
                                                      sorted_slot, slot_to_row, active_experts,

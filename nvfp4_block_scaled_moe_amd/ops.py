@@ -124,10 +124,11 @@ def moe_route_permute(logits: torch.Tensor, k: int):
         n_active=torch.empty((1,), **i32),
     )
     lib = _lib.load()
+    ws = _ws(lib.moe_route_permute_workspace_size(T, E, k), dev)
     st = lib.moe_route_permute(_ptr(logits), T, E, k, _ptr(out["topk_ids"]), _ptr(out["topk_w"]),
                                _ptr(out["expert_offsets"]), _ptr(out["sorted_slot"]),
                                _ptr(out["slot_to_row"]), _ptr(out["active_experts"]),
-                               _ptr(out["n_active"]), None, 0, _stream())
+                               _ptr(out["n_active"]), _ptr(ws), ws.numel(), _stream())
     _lib.check("moe_route_permute", st)
     return out
 

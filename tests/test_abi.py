@@ -67,6 +67,22 @@ def test_route_permute_rejects_bad_arguments():
         assert st == _lib.ERR_INVALID_ARG, (T, E, k)
 
 
+def test_route_permute_workspace():
+    """The permutation's workspace holds per-chunk expert counts (chunks of >= 2048 slots, at
+    most 64 chunks); a call with less is rejected before any HIP call."""
+    lib = _lib.load()
+    assert lib.moe_route_permute_workspace_size(8192, 256, 8) == 32 * 256 * 4
+    assert lib.moe_route_permute_workspace_size(1, 256, 8) == 256 * 4
+    assert lib.moe_route_permute_workspace_size(1 << 20, 64, 16) == 64 * 64 * 4
+    assert lib.moe_route_permute_workspace_size(0, 256, 8) == 0
+    assert lib.moe_route_permute_workspace_size(4, 8, 9) == 0
+    need = lib.moe_route_permute_workspace_size(512, 256, 8)
+    for ws, nbytes in [(None, 0), (FAKE, need - 1)]:
+        st, msg = _err(lib.moe_route_permute(FAKE, 512, 256, 8, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                             ws, nbytes, None))
+        assert st == _lib.ERR_WORKSPACE and "workspace" in msg
+
+
 def _gemm(lib, mode=_lib.W4A16, epi=_lib.EPI_SWIGLU, a=FAKE, a_scales=None, a_g=None, a_rows=16,
           gidx=None, gdiv=1, E=8, rows=16, Nw=64, K=64, out_dtype=_lib.BF16, ws=FAKE, ws_bytes=1 << 30):
     return lib.moe_grouped_gemm_nvfp4(mode, epi, a, a_scales, a_g, a_rows, gidx, gdiv, FAKE, FAKE, FAKE,

@@ -142,6 +142,10 @@ def test_route_permute_bit_exact(T, E, k, zipf):
     lg = inputs.router_logits(wl)
     if T >= 2:
         lg[1, :] = 0.25                           # an all-tie row
+    _check_route(lg, k, E)
+
+
+def _check_route(lg, k, E):
     r = ops.moe_route_permute(lg.to(DEV), k)
     torch.cuda.synchronize()
     ids, w = omoe.route(lg.numpy(), k)
@@ -155,6 +159,21 @@ def test_route_permute_bit_exact(T, E, k, zipf):
     assert na == len(perm["active"])
     act = np_(r["active_experts"])
     assert np.array_equal(act[:na], perm["active"]) and np.all(act[na:] == -1)
+
+
+@pytest.mark.parametrize("path", ["single", "multi"])
+@pytest.mark.parametrize("T,E,k,zipf", [(8192, 256, 8, 1.1), (3000, 512, 22, 0.0), (37, 1024, 64, 0.0),
+                                        (16, 8, 2, 0.0), (1, 256, 8, 0.0), (20000, 64, 7, 0.5)])
+def test_both_permutations_bit_exact(path, T, E, k, zipf, monkeypatch):
+    """The one-workgroup permutation and the two-launch one (chunks of 2048+ slots; 20000 x 7
+    slots grow the chunks to keep at most 64), each forced, against the oracle."""
+    say("permute", path, T, E, k, zipf)
+    monkeypatch.setenv("NVFP4MOE_PERMUTE", path)
+    wl = inputs.Workload("route_test", T=T, E=E, k=k, H=64, F=64, mode="w4a16", zipf=zipf)
+    lg = inputs.router_logits(wl)
+    if T >= 2:
+        lg[1, :] = 0.25                           # an all-tie row
+    _check_route(lg, k, E)
 
 
 @pytest.mark.parametrize("router", ["sort", "wave"])
