@@ -209,12 +209,11 @@ def measure(torch, ops, layer, wl, w, x, lg, T, mode, steps, warmup, graph=False
         if mx:
             xq, xs = ops.mxfp4_quantize(xx)
             mark(2)
-            h = ops.moe_grouped_gemm_mxfp4(ops.EPI_SWIGLU, xq, xs, w.w13_t, gather_index=rr["sorted_slot"],
-                                           gather_div=k, rows=S, out_dtype=torch.float32, **common)
+            hq, hs = ops.moe_grouped_gemm_mxfp4_swiglu_q(xq, xs, w.w13_t, gather_index=rr["sorted_slot"],
+                                                         gather_div=k, rows=S, **common)
             mark(3)
             paths["up"] = "mx"
-            hq, hs = ops.mxfp4_quantize(h)
-            mark(4)
+            mark(4)   # h is quantized by the up/gate epilogue
             y = ops.moe_grouped_gemm_mxfp4(ops.EPI_NONE, hq, hs, w.w2_t, rows=S, out_dtype=torch.float32,
                                            **common)
         elif mode == ops.W4A16:
@@ -273,7 +272,7 @@ def measure(torch, ops, layer, wl, w, x, lg, T, mode, steps, warmup, graph=False
         stage = {n: round(1e3 * sum(e[j].elapsed_time(e[j + 1]) for e in evs) / steps, 2)
                  for j, n in enumerate(names)}
     act_in = T * wl.H * (2 if mode == ops.W4A16 else (17 / 32 if mx else 9 / 16))
-    h_bytes = S * wl.F * (2 if mode == ops.W4A16 else 4)
+    h_bytes = S * wl.F * (2 if mode == ops.W4A16 else (17 / 32 if mx else 4))
     up_bytes = w13_bytes + act_in + h_bytes
     up_flops = 2.0 * S * 2 * wl.F * wl.H
     res = dict(ms_per_step=ms, tflops=flops / (ms * 1e-3) / 1e12,

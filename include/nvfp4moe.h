@@ -11,8 +11,8 @@
  *
  * plus nvfp4_quantize (weights offline; W4A4 activations and h per forward) and
  * act_fp8_e4m3_roundtrip (FP8 E4M3 activations dequantized to bf16); and the MXFP4 variant
- * (mxfp4_quantize, mxfp4_weights_tile, moe_grouped_gemm_mxfp4: group-32 UE8M0 scales, W4A4
- * on the scaled FP4 matrix cores).
+ * (mxfp4_quantize, mxfp4_weights_tile, moe_grouped_gemm_mxfp4 and
+ * moe_grouped_gemm_mxfp4_swiglu_q: group-32 UE8M0 scales, W4A4 on the scaled FP4 matrix cores).
  *
  * Sources for what is computed (web pages; section names):
  *   [P1] "Native FP4 Is Slower Than Emulated FP4: A Kernel-Maturity Measurement on
@@ -299,7 +299,9 @@ nvfp4moe_status mxfp4_weights_tile(const uint8_t* packed, const uint8_t* scales,
  *                16-byte aligned.
  *   Nw, K        Nw % 256 == 0 (else NVFP4MOE_ERR_UNSUPPORTED), K >= 32, K % 32 == 0,
  *                rows * max(K, Nw), a_rows * K / 2 and Nw * K / 2 below 2^31.
- *   ws           moe_grouped_gemm_mxfp4_workspace_size(rows, E) bytes, 16-byte aligned.
+ *   ws           moe_grouped_gemm_mxfp4_workspace_size(rows, E, Nw, K) bytes, 16-byte
+ *                aligned: the device-built m-tile list and, when the grid is too small to
+ *                fill the chip, fixed-order split-K partial sums. Returns 0 for invalid sizes.
  * ------------------------------------------------------------------------- */
 nvfp4moe_status moe_grouped_gemm_mxfp4(nvfp4moe_epilogue epi, const uint8_t* a, const uint8_t* a_scales,
                                        int64_t a_rows, const int32_t* gather_index, int32_t gather_div,
@@ -308,7 +310,28 @@ nvfp4moe_status moe_grouped_gemm_mxfp4(nvfp4moe_epilogue epi, const uint8_t* a, 
                                        const int32_t* n_active, int32_t E, int32_t rows, int32_t Nw,
                                        int32_t K, void* out, nvfp4moe_dtype out_dtype, float* out_amax, void* ws,
                                        size_t ws_bytes, void* stream);
-size_t moe_grouped_gemm_mxfp4_workspace_size(int32_t rows, int32_t E);
+size_t moe_grouped_gemm_mxfp4_workspace_size(int32_t rows, int32_t E, int32_t Nw, int32_t K);
+
+/* ---------------------------------------------------------------------------
+ * moe_grouped_gemm_mxfp4_swiglu_q -- the SwiGLU call of moe_grouped_gemm_mxfp4 with h written
+ * as MXFP4 straight from the epilogue: h = silu(P[:, :Nw/2]) * P[:, Nw/2:] in float32, then
+ * per row and group of 32 columns the rule of mxfp4_quantize (so the codes and scales are
+ * those mxfp4_quantize gives for the float32 h of the unquantized call, bit for bit). This is
+ * the down GEMM's activation in the MXFP4 layer; MXFP4 has no per-tensor scale, so h needs no
+ * pass over all of it first. [P2] "The NVFP4 Pivot" (MXFP4, group 32, UE8M0).
+ *   All arguments as for moe_grouped_gemm_mxfp4 except:
+ *   h_packed     device uint8 [rows, Nw/4] (output), 16-byte aligned: MXFP4 codes of h.
+ *   h_scales     device uint8 [rows, Nw/64] (output), 4-byte aligned: UE8M0 scales of h.
+ *   ws           moe_grouped_gemm_mxfp4_workspace_size(rows, E, Nw, K) bytes (K is never
+ *                split in this call).
+ * ------------------------------------------------------------------------- */
+nvfp4moe_status moe_grouped_gemm_mxfp4_swiglu_q(const uint8_t* a, const uint8_t* a_scales, int64_t a_rows,
+                                                const int32_t* gather_index, int32_t gather_div,
+                                                const uint8_t* w_packed, const uint8_t* w_scales,
+                                                const int32_t* expert_offsets, const int32_t* active_experts,
+                                                const int32_t* n_active, int32_t E, int32_t rows, int32_t Nw,
+                                                int32_t K, uint8_t* h_packed, uint8_t* h_scales, void* ws,
+                                                size_t ws_bytes, void* stream);
 
 /* Thread-local message describing the last non-OK status ("" if none). Never NULL. */
 const char* nvfp4moe_last_error(void);

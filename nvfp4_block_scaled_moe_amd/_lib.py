@@ -45,7 +45,9 @@ SIGNATURES = {
     "mxfp4_weights_tile": (_int, [_vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp]),
     "moe_grouped_gemm_mxfp4": (_int, [_int, _vp, _vp, _i64, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
                                       _i32, _i32, _vp, _int, _vp, _vp, _sz, _vp]),
-    "moe_grouped_gemm_mxfp4_workspace_size": (_sz, [_i32, _i32]),
+    "moe_grouped_gemm_mxfp4_workspace_size": (_sz, [_i32, _i32, _i32, _i32]),
+    "moe_grouped_gemm_mxfp4_swiglu_q": (_int, [_vp, _vp, _i64, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
+                                               _i32, _i32, _vp, _vp, _vp, _sz, _vp]),
     "nvfp4moe_last_error": (ctypes.c_char_p, []),
     "nvfp4moe_last_dispatch": (_int, []),
     "nvfp4moe_abi_version": (_int, []),

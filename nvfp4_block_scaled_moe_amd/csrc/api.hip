@@ -114,7 +114,7 @@ extern "C" {
 
 const char* nvfp4moe_last_error(void) { return g_last_error.c_str(); }
 int nvfp4moe_last_dispatch(void) { return g_last_dispatch; }
-int nvfp4moe_abi_version(void) { return 201; }
+int nvfp4moe_abi_version(void) { return 203; }
 
 // ------------------------------------------------------------------ quantize
 size_t nvfp4_quantize_workspace_size(int64_t B, int64_t R, int64_t C) {
@@ -374,31 +374,38 @@ nvfp4moe_status mxfp4_weights_tile(const uint8_t* packed, const uint8_t* scales,
 }
 
 namespace {
-// Workspace of moe_grouped_gemm_mxfp4: the m-tile list (sched_e, sched_r, sched_n).
 int mx_max_mtiles(int32_t rows, int32_t E) {
   const int bm = mx_rows_per_mtile();
   return (rows + bm - 1) / bm + (E < rows ? E : rows);
 }
 }  // namespace
 
-size_t moe_grouped_gemm_mxfp4_workspace_size(int32_t rows, int32_t E) {
-  if (rows < 1 || E < 1) return 0;
-  return 2 * round_up((size_t)mx_max_mtiles(rows, E) * 4) + kAlign;
+// Workspace of moe_grouped_gemm_mxfp4: the m-tile list (sched_e, sched_r, sched_n) and, when
+// K is split, the [ksplit, rows, Nw] fp32 partial sums.
+size_t moe_grouped_gemm_mxfp4_workspace_size(int32_t rows, int32_t E, int32_t Nw, int32_t K) {
+  if (rows < 1 || E < 1 || Nw < 1 || K < 32) return 0;
+  const int mt = mx_max_mtiles(rows, E);
+  const int ks = mx_supports(Nw) ? mx_ksplit(mt, Nw, K) : 1;
+  const size_t partial = ks > 1 ? round_up((size_t)ks * rows * Nw * 4) : 0;
+  return 3 * round_up((size_t)mt * 4) + partial + kAlign;
 }
 
-nvfp4moe_status moe_grouped_gemm_mxfp4(nvfp4moe_epilogue epi, const uint8_t* a, const uint8_t* a_scales,
-                                       int64_t a_rows, const int32_t* gather_index, int32_t gather_div,
-                                       const uint8_t* w_packed, const uint8_t* w_scales,
-                                       const int32_t* expert_offsets, const int32_t* active_experts,
-                                       const int32_t* n_active, int32_t E, int32_t rows, int32_t Nw,
-                                       int32_t K, void* out, nvfp4moe_dtype out_dtype, float* out_amax, void* ws,
-                                       size_t ws_bytes, void* stream) {
-  const char* fn = "moe_grouped_gemm_mxfp4";
+namespace {
+// Both MXFP4 GEMM entry points: out/out_dtype/out_amax, or (SwiGLU only) h quantized to
+// MXFP4 into hq_packed/hq_scales.
+nvfp4moe_status mx_gemm_call(const char* fn, nvfp4moe_epilogue epi, const uint8_t* a, const uint8_t* a_scales,
+                             int64_t a_rows, const int32_t* gather_index, int32_t gather_div,
+                             const uint8_t* w_packed, const uint8_t* w_scales, const int32_t* expert_offsets,
+                             const int32_t* active_experts, const int32_t* n_active, int32_t E, int32_t rows,
+                             int32_t Nw, int32_t K, void* out, nvfp4moe_dtype out_dtype, float* out_amax,
+                             uint8_t* hq_packed, uint8_t* hq_scales, void* ws, size_t ws_bytes, void* stream) {
+  const bool qh = hq_packed != nullptr;
   if (epi != NVFP4MOE_EPI_NONE && epi != NVFP4MOE_EPI_SWIGLU)
     return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: bad epilogue %d", fn, (int)epi);
   if (out_dtype != NVFP4MOE_F32 && out_dtype != NVFP4MOE_BF16)
     return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: out_dtype must be F32 or BF16", fn);
-  if (!a || !a_scales || !w_packed || !w_scales || !expert_offsets || !active_experts || !n_active || !out)
+  if (!a || !a_scales || !w_packed || !w_scales || !expert_offsets || !active_experts || !n_active ||
+      (qh ? !hq_scales : !out))
     return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: null tensor pointer", fn);
   if (E < 1 || E > kMaxExperts)
     return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: need 1 <= E <= %d (E=%d)", fn, kMaxExperts, E);
@@ -414,9 +421,10 @@ nvfp4moe_status moe_grouped_gemm_mxfp4(nvfp4moe_epilogue epi, const uint8_t* a, 
     return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: without gather_index a_rows must equal rows", fn);
   if (gather_index && gather_div < 1) return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: gather_div must be >= 1", fn);
   if (!aligned(a, 16) || !aligned(w_packed, 16) || !aligned(w_scales, 16) ||
-      !aligned(out, out_dtype == NVFP4MOE_F32 ? 4 : 2))
-    return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: a and the tiled weights must be 16-byte aligned", fn);
-  const size_t need = moe_grouped_gemm_mxfp4_workspace_size(rows, E);
+      (qh ? !aligned(hq_packed, 16) || !aligned(hq_scales, 4) : !aligned(out, out_dtype == NVFP4MOE_F32 ? 4 : 2)))
+    return fail(NVFP4MOE_ERR_INVALID_ARG,
+                "%s: a and the tiled weights must be 16-byte aligned, the output to its element", fn);
+  const size_t need = moe_grouped_gemm_mxfp4_workspace_size(rows, E, Nw, K);
   if (!ws || ws_bytes < need)
     return fail(NVFP4MOE_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, ws_bytes);
   if (!aligned(ws, 16)) return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: workspace must be 16-byte aligned", fn);
@@ -448,7 +456,13 @@ nvfp4moe_status moe_grouped_gemm_mxfp4(nvfp4moe_epilogue epi, const uint8_t* a, 
   g.sched_e = reinterpret_cast<const int*>(base);
   g.sched_r = reinterpret_cast<const int*>(base + arr);
   g.sched_n = reinterpret_cast<const int*>(base + 2 * arr);
-  g.ksplit = 1;
+  g.hq_packed = hq_packed;
+  g.hq_scales = hq_scales;
+  g.ksplit = qh ? 1 : mx_ksplit(max_mtiles, Nw, K);   // the quantized epilogue needs whole sums
+  g.partial = g.ksplit > 1 ? reinterpret_cast<float*>(base + 3 * arr) : nullptr;
+  g.unit_alpha = 1;
+  if ((int64_t)g.ksplit * rows * Nw >= (int64_t(1) << 31))
+    return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: split-K partial sums too large (ksplit %d)", fn, g.ksplit);
   hipError_t err = hipSuccess;
   if (out_amax) err = launch_zero_f32(out_amax, 1, s);
   if (err != hipSuccess) return hip_status(err, fn);
@@ -457,6 +471,32 @@ nvfp4moe_status moe_grouped_gemm_mxfp4(nvfp4moe_epilogue epi, const uint8_t* a, 
   err = launch_mtile_schedule(sched, s);
   if (err != hipSuccess) return hip_status(err, fn);
   return hip_status(launch_gemm_mx(g, max_mtiles, s), fn);
+}
+}  // namespace
+
+nvfp4moe_status moe_grouped_gemm_mxfp4(nvfp4moe_epilogue epi, const uint8_t* a, const uint8_t* a_scales,
+                                       int64_t a_rows, const int32_t* gather_index, int32_t gather_div,
+                                       const uint8_t* w_packed, const uint8_t* w_scales,
+                                       const int32_t* expert_offsets, const int32_t* active_experts,
+                                       const int32_t* n_active, int32_t E, int32_t rows, int32_t Nw,
+                                       int32_t K, void* out, nvfp4moe_dtype out_dtype, float* out_amax, void* ws,
+                                       size_t ws_bytes, void* stream) {
+  return mx_gemm_call("moe_grouped_gemm_mxfp4", epi, a, a_scales, a_rows, gather_index, gather_div, w_packed,
+                      w_scales, expert_offsets, active_experts, n_active, E, rows, Nw, K, out, out_dtype, out_amax,
+                      nullptr, nullptr, ws, ws_bytes, stream);
+}
+
+nvfp4moe_status moe_grouped_gemm_mxfp4_swiglu_q(const uint8_t* a, const uint8_t* a_scales, int64_t a_rows,
+                                                const int32_t* gather_index, int32_t gather_div,
+                                                const uint8_t* w_packed, const uint8_t* w_scales,
+                                                const int32_t* expert_offsets, const int32_t* active_experts,
+                                                const int32_t* n_active, int32_t E, int32_t rows, int32_t Nw,
+                                                int32_t K, uint8_t* h_packed, uint8_t* h_scales, void* ws,
+                                                size_t ws_bytes, void* stream) {
+  if (!h_packed) return fail(NVFP4MOE_ERR_INVALID_ARG, "moe_grouped_gemm_mxfp4_swiglu_q: null tensor pointer");
+  return mx_gemm_call("moe_grouped_gemm_mxfp4_swiglu_q", NVFP4MOE_EPI_SWIGLU, a, a_scales, a_rows, gather_index,
+                      gather_div, w_packed, w_scales, expert_offsets, active_experts, n_active, E, rows, Nw, K,
+                      nullptr, NVFP4MOE_F32, nullptr, h_packed, h_scales, ws, ws_bytes, stream);
 }
 
 // ------------------------------------------------------------------ unpermute-reduce

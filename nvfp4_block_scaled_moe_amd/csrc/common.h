@@ -76,6 +76,35 @@ __device__ __forceinline__ uint32_t e2m1_rne_mag(float x) {
          (uint32_t)(x > 5.0f);
 }
 
+// ------------------------------------------------------------------ MXFP4 groups
+// Group key of one element for the MXFP4 shared exponent: |v| as float bits when finite,
+// 0xFFFFFFFF for NaN/Inf (above every finite key), so the max over a group is the finite
+// amax, or the marker of a group with a non-finite element.
+__device__ __forceinline__ uint32_t mx_key(float v) {
+  const float a = fabsf(v);
+  return a <= 3.402823466e38f ? __float_as_uint(a) : 0xFFFFFFFFu;
+}
+// Scale byte of a group from its key (OCP MX v1.0 rule, group of 32): NaN/Inf -> 0xFF;
+// amax 0 -> 0; else e = max(floor(log2 amax) - 2, -127) (frexp gives floor(log2) exactly)
+// and byte e + 127. e is returned for mx_code (0 when unused).
+__device__ __forceinline__ uint32_t mx_scale(uint32_t key, int& e) {
+  e = 0;
+  if (key == 0xFFFFFFFFu) return 0xFFu;
+  if (key == 0u) return 0u;
+  int ex;
+  (void)frexpf(__uint_as_float(key), &ex);   // amax = f * 2^ex, f in [0.5, 1)
+  e = max(ex - 1 - 2, -127);
+  return (uint32_t)(e + 127);
+}
+// Code (sign bit | E2M1 magnitude) of v in a group with the given key and exponent:
+// E2M1_RNE_saturating(|v| * 2^-e), a power-of-two scaling (exact); 0 in a non-finite group,
+// +-0 in an all-zero group.
+__device__ __forceinline__ uint32_t mx_code(float v, uint32_t key, int e) {
+  if (key == 0xFFFFFFFFu) return 0u;
+  const uint32_t sign = (__float_as_uint(v) >> 31) << 3;
+  return sign | (key != 0u ? e2m1_rne_mag(ldexpf(fabsf(v), -e)) : 0u);
+}
+
 // ------------------------------------------------------------------ NVFP4 -> f16
 // Eight E2M1 codes (one dword, element 0 in the low nibble) times an f16 block scale,
 // as eight f16 values. The hardware convert produces the E2M1 values exactly (scale

@@ -37,6 +37,10 @@ __device__ __forceinline__ T ld_const(const T* p, int64_t i) {
   return ((const __attribute__((address_space(4))) T*)p)[i];
 }
 
+// silu(gate) * up, the SwiGLU of one output element (shared by every epilogue so that
+// equal inputs give equal bits).
+__device__ __forceinline__ float swiglu1(float gv, float uv) { return gv / (1.0f + expf(-gv)) * uv; }
+
 // Epilogue of one wave's tile: RBW blocks of 16 weight rows x TBM blocks of 16 GEMM rows,
 // with MFMA 16x16 output layout (lane l holds weight rows 4*(l/16)+i of each block, GEMM
 // row l%16 of each token block). GEMM rows tc .. tc+16*ntb-1 of the expert (those < M) are
@@ -65,7 +69,7 @@ __device__ __forceinline__ uint32_t store_tile_exp(const GemmArgs& p, const f32x
           for (int i = 0; i < 4; ++i) {
             const float gv = ldexpf(acc[b][tb][i] * alpha, pexp);
             const float uv = ldexpf(acc[b + RBW / 2][tb][i] * alpha, pexp);
-            h[i] = gv / (1.0f + expf(-gv)) * uv;
+            h[i] = swiglu1(gv, uv);
             amax_bits = max(amax_bits, abs_bits(h[i]));
           }
           const size_t o = (size_t)row * F + blkrow(b) + 4 * g;

@@ -268,7 +268,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const GemmArgs p) {
       if (p.expert_offsets[mid] <= row) lo = mid;
       else hi = mid;
     }
-    const float alpha = p.w4a4 ? p.w_g[lo] * p.a_g[0] : p.w_g[lo];
+    const float alpha = p.unit_alpha ? 1.0f : (p.w4a4 ? p.w_g[lo] * p.a_g[0] : p.w_g[lo]);
     const int pexp = p.w4a4 ? 0 : p.rexp[p.gather_index ? p.gather_index[row] / p.gather_div : row];
     const size_t slice = (size_t)p.rows * Nw;
     const float* src = p.partial + (size_t)row * Nw + col;
@@ -289,7 +289,7 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const GemmArgs p) {
       if (SWIGLU) {
         const float gv = ldexpf(av[q] * alpha, pexp);
         const float up = ldexpf(uv[q] * alpha, pexp);
-        o[q] = gv / (1.0f + expf(-gv)) * up;
+        o[q] = swiglu1(gv, up);
       } else {
         o[q] = ldexpf(av[q] * alpha, pexp);
       }

@@ -28,6 +28,18 @@
 //     c+3: the reads never wait behind the barrier that ends the step. Epilogue as in the
 //     other GEMMs with alpha 1 (MXFP4 has no per-tensor scale): SwiGLU, bf16 or f32 stores,
 //     amax.
+//   * SwiGLU with quantized output: h is written as MXFP4 straight from the epilogue (no
+//     per-tensor scale, so no pass over all of h is needed first). A 32-column group of h
+//     spans the 16 columns of two neighbouring waves; each wave reduces its half's amax key
+//     per row, the pair exchanges them through LDS, and both quantize their halves with the
+//     group's exponent, by the same rule and helpers as the MXFP4 quantizer; the codes and
+//     scales of the workgroup's tile are gathered in LDS and written as 64 contiguous bytes
+//     per row.
+//   * Small grids split K into slices of whole chunks (partial sums to the workspace, then
+//     the shared fixed-order split-K reduce). A slice may start inside a scale window: the
+//     16 scale bytes of the slice's next 16 chunks are a byte shift of the two windows held
+//     in registers, taken once per 16 chunks.
+#include <cstdlib>
 #include <utility>
 
 #include "gemm_common.h"
@@ -57,6 +69,32 @@ __device__ __forceinline__ f32x4 mfma_mx(u32x4 a, uint32_t sa, u32x4 b, uint32_t
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, c, 4, 4, OA, (int)sa, OB, (int)sb);
 }
 
+// Bytes sh .. sh+15 of the 32-byte concatenation lo | hi (sh = 0..15, wave-uniform).
+__device__ __forceinline__ u32x4 byte_shift(const u32x4& lo, const u32x4& hi, int sh) {
+  const uint32_t d[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+  const uint32_t bs = (uint32_t)(sh & 3);
+  u32x4 r;
+  switch (sh >> 2) {   // uniform branch: register indices stay compile-time constants
+    case 0:
+#pragma unroll
+      for (int j = 0; j < 4; ++j) r[j] = __builtin_amdgcn_alignbyte(d[j + 1], d[j], bs);
+      break;
+    case 1:
+#pragma unroll
+      for (int j = 0; j < 4; ++j) r[j] = __builtin_amdgcn_alignbyte(d[j + 2], d[j + 1], bs);
+      break;
+    case 2:
+#pragma unroll
+      for (int j = 0; j < 4; ++j) r[j] = __builtin_amdgcn_alignbyte(d[j + 3], d[j + 2], bs);
+      break;
+    default:
+#pragma unroll
+      for (int j = 0; j < 4; ++j) r[j] = __builtin_amdgcn_alignbyte(d[j + 4], d[j + 3], bs);
+      break;
+  }
+  return r;
+}
+
 // f(Int<0>{}), ..., f(Int<N-1>{}): loop indices usable as template arguments (the byte
 // selects of the MFMA are immediates).
 template <typename F, int... I>
@@ -68,8 +106,9 @@ __device__ __forceinline__ void static_for(F&& f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-template <bool SWIGLU>
+template <bool SWIGLU, bool QH>
 __global__ __launch_bounds__(kMxWaves* kWave) void gemm_mx_kernel(const GemmArgs p, int ntiles_n) {
+  static_assert(!QH || SWIGLU, "h is quantized in the SwiGLU epilogue");
   constexpr int NT = kMxWaves * kWave;
   static_assert(NT == 16 * kMxTBM * 4, "one thread per token and 32-wide k block of a chunk");
   __shared__ __attribute__((aligned(16))) unsigned char smem[kMxSlots * kMxSlot];
@@ -78,11 +117,15 @@ __global__ __launch_bounds__(kMxWaves* kWave) void gemm_mx_kernel(const GemmArgs
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g = lane >> 4;
   // Tiles (m-tile, row tile) of the listed m-tiles, 8 equal ranges, one per XCD.
-  const int ntiles = ld_const(p.sched_n, 0) * ntiles_n;
+  // Tiles (K slice, m-tile, row tile) of the listed m-tiles, slice-major, 8 equal ranges,
+  // one per XCD.
+  const int per_split = ld_const(p.sched_n, 0) * ntiles_n;
+  const int ntiles = per_split * p.ksplit;
   const int per_xcd = (ntiles + 7) >> 3;
   const int tile = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
   if ((int)(blockIdx.x >> 3) >= per_xcd || tile >= ntiles) return;
-  const int mt = tile / ntiles_n, nb = tile - mt * ntiles_n;
+  const int ks = tile / per_split, mn = tile - ks * per_split;
+  const int mt = mn / ntiles_n, nb = mn - mt * ntiles_n;
   const int e = ld_const(p.sched_e, mt), tc = ld_const(p.sched_r, mt);
   const int r0 = ld_const(p.expert_offsets, e);
   const int M = ld_const(p.expert_offsets, e + 1) - r0;
@@ -91,6 +134,11 @@ __global__ __launch_bounds__(kMxWaves* kWave) void gemm_mx_kernel(const GemmArgs
   const int nch = (K + kChunk - 1) / kChunk;
   const int nwin = (nch + kMxWin - 1) / kMxWin;
   const int ntb = __builtin_amdgcn_readfirstlane(min(kMxTBM, (M - tc + 15) >> 4));
+  // K slice ks: chunks [clo, chi); its first chunk is chunk u0 of scale window w0
+  const int cps = (nch + p.ksplit - 1) / p.ksplit;
+  const int clo = ks * cps, chi = min(nch, clo + cps);
+  if (clo >= chi) return;
+  const int w0 = clo / kMxWin, u0 = clo - w0 * kMxWin;
 
   auto blkrow = [&](int b) -> int {
     if (SWIGLU) return (b == 0 ? 0 : F) + (nb * kMxWaves + wave) * 16;
@@ -123,8 +171,8 @@ __global__ __launch_bounds__(kMxWaves* kWave) void gemm_mx_kernel(const GemmArgs
 
   u32x4 bst[2];
   uint32_t bsc[2];
-  auto b_issue = [&](int set, int c) {   // k blocks past K read zero codes and scale 0
-    const bool in = c < nch && 128 * c + 32 * q < K;
+  auto b_issue = [&](int set, int c) {   // k blocks past K (or the slice) read zero codes and scale 0
+    const bool in = c < chi && 128 * c + 32 * q < K;
     bst[set] = ld128(ar, in ? csrc + 64u * c : kOOB, 0);
     bsc[set] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(asr, in ? ssrc + 4u * c : kOOB, 0, 0);
   };
@@ -136,12 +184,14 @@ __global__ __launch_bounds__(kMxWaves* kWave) void gemm_mx_kernel(const GemmArgs
   u32x4 wring[kMxDepth][kMxRBW];
   auto w_issue = [&](int d, int c) {     // codes past K are zero in the tiles
 #pragma unroll
-    for (int b = 0; b < kMxRBW; ++b) wring[d][b] = ld128(wr, c < nch ? wlane + (uint32_t)c * 1024u : kOOB, wsoff[b]);
+    for (int b = 0; b < kMxRBW; ++b) wring[d][b] = ld128(wr, c < chi ? wlane + (uint32_t)c * 1024u : kOOB, wsoff[b]);
   };
-  u32x4 scur[kMxRBW], snext[kMxRBW];
-  auto s_issue = [&](int w) {
+  // Scale windows: sa = window w0 + i, sb = w0 + i + 1 while chunks clo + 16 i .. + 15 run;
+  // sn = w0 + i + 2 in flight.
+  u32x4 sa[kMxRBW], sb[kMxRBW], sn[kMxRBW];
+  auto s_issue = [&](u32x4 (&dst)[kMxRBW], int w) {
 #pragma unroll
-    for (int b = 0; b < kMxRBW; ++b) snext[b] = ld128(sr, w < nwin ? slane + (uint32_t)w * 1024u : kOOB, ssoff[b]);
+    for (int b = 0; b < kMxRBW; ++b) dst[b] = ld128(sr, w < nwin ? slane + (uint32_t)w * 1024u : kOOB, ssoff[b]);
   };
 
   f32x4 acc[kMxRBW][kMxTBM];
@@ -150,26 +200,27 @@ __global__ __launch_bounds__(kMxWaves* kWave) void gemm_mx_kernel(const GemmArgs
 #pragma unroll
     for (int tb = 0; tb < kMxTBM; ++tb) acc[b][tb] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-  // prologue: scales of window 0, weights of chunks 0 and 1, activations of chunks 0 and 1
-  // committed to slots 0 and 1, chunk 2 requested (staging set 0)
-  s_issue(0);
+  // prologue: scale windows w0 and w0 + 1, weights of the slice's first kMxDepth chunks,
+  // activations of its first two chunks committed to slots 0 and 1, the third requested
+  // (staging set 0)
+  s_issue(sa, w0);
+  s_issue(sb, w0 + 1);
+  b_issue(0, clo);
+  b_issue(1, clo + 1);
 #pragma unroll
-  for (int b = 0; b < kMxRBW; ++b) scur[b] = snext[b];
-  b_issue(0, 0);
-  b_issue(1, 1);
-#pragma unroll
-  for (int d = 0; d < kMxDepth; ++d) w_issue(d, d);
+  for (int d = 0; d < kMxDepth; ++d) w_issue(d, clo + d);
   b_commit(0, 0);
   b_commit(1, 1);
-  b_issue(0, 2);
+  b_issue(0, clo + 2);
   __syncthreads();
 
   // The main loop, compiled for NTB = 8, 4, 2 or 1 token blocks (ntb rounded up; blocks past
-  // the m-tile's rows hold zeros). Chunk c lives in LDS slot c % 3 and staging set c & 1,
-  // its weights in ring entry c % kMxDepth. Step c: request chunk c+3 (set (c+1) & 1, whose
-  // chunk c+1 was committed in step c-1), read chunk c+1's fragments (committed in step c-1),
-  // MFMAs of chunk c, commit chunk c+2 to slot (c+2) % 3 (chunk c-1, read in step c-2), barrier.
-  // Whole scale windows; the MFMAs of chunks past K are skipped.
+  // the m-tile's rows hold zeros). With j = c - clo: chunk c lives in LDS slot j % 3 and
+  // staging set j & 1, its weights in ring entry j % kMxDepth. Step c: request chunk c+3 (set
+  // (j+1) & 1, whose chunk c+1 was committed in step c-1), read chunk c+1's fragments
+  // (committed in step c-1), MFMAs of chunk c, commit chunk c+2 to slot (j+2) % 3 (chunk c-1,
+  // read in step c-2), barrier. Steps come in blocks of 16; the MFMAs of chunks past the
+  // slice are skipped.
   auto body = [&](auto ntb_tag) {
     constexpr int NTB = decltype(ntb_tag)::value;
     u32x4 bcur[NTB], bnext[NTB];
@@ -184,8 +235,11 @@ __global__ __launch_bounds__(kMxWaves* kWave) void gemm_mx_kernel(const GemmArgs
     };
     b_read(bcur, scb, 0);
     int slot = 0;   // c % 3
-    for (int c0 = 0; c0 < nwin * kMxWin; c0 += kMxWin) {
-      s_issue(c0 / kMxWin + 1);
+    for (int c0 = clo; c0 < chi; c0 += kMxWin) {
+      u32x4 scs[kMxRBW];   // scale bytes of chunks c0 .. c0 + 15
+#pragma unroll
+      for (int b = 0; b < kMxRBW; ++b) scs[b] = byte_shift(sa[b], sb[b], u0);
+      s_issue(sn, (c0 - clo) / kMxWin + w0 + 2);
       static_for<kMxWin>([&](auto u_tag) {
         constexpr int u = decltype(u_tag)::value;
         const int c = c0 + u;
@@ -198,18 +252,21 @@ __global__ __launch_bounds__(kMxWaves* kWave) void gemm_mx_kernel(const GemmArgs
         for (int b = 0; b < kMxRBW; ++b) wa[b] = wring[d][b];
         w_issue(d, c + kMxDepth);   // this ring entry is free again
         b_read(bnext, scbn, slot1);
-        if (c < nch) {
+        if (c < chi) {
           static_for<NTB>([&](auto tb_tag) {
             constexpr int tb = decltype(tb_tag)::value;
 #pragma unroll
             for (int b = 0; b < kMxRBW; ++b)
-              acc[b][tb] = mfma_mx<(u & 3), (tb & 3)>(wa[b], scur[b][u >> 2], bcur[tb], scb[tb >> 2], acc[b][tb]);
+              acc[b][tb] = mfma_mx<(u & 3), (tb & 3)>(wa[b], scs[b][u >> 2], bcur[tb], scb[tb >> 2], acc[b][tb]);
           });
         }
         b_commit(u & 1, slot2);
         if (u == kMxWin - 1) {
 #pragma unroll
-          for (int b = 0; b < kMxRBW; ++b) scur[b] = snext[b];
+          for (int b = 0; b < kMxRBW; ++b) {
+            sa[b] = sb[b];
+            sb[b] = sn[b];
+          }
         }
         __syncthreads();
 #pragma unroll
@@ -225,6 +282,68 @@ __global__ __launch_bounds__(kMxWaves* kWave) void gemm_mx_kernel(const GemmArgs
   else if (ntb > 1) body(Int<2>{});
   else body(Int<1>{});
 
+  if constexpr (QH) {   // MXFP4 h: rows of the m-tile, the wave's 16 h columns
+    __syncthreads();     // every wave is past its last ring read
+    uint32_t* xch = reinterpret_cast<uint32_t*>(smem);       // [kMxWaves][kMxTBM][16] amax keys
+    unsigned char* qc = smem + 4096;                          // [128 rows][64 B] codes of the tile
+    unsigned char* qs = qc + 16 * kMxTBM * 64;                // [128 rows][4] scale bytes
+    const int F2 = F >> 1, F32 = F >> 5;
+    float h[kMxTBM][4];
+    uint32_t key[kMxTBM];
+#pragma unroll
+    for (int tb = 0; tb < kMxTBM; ++tb) {
+      key[tb] = 0u;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        h[tb][i] = swiglu1(acc[0][tb][i], acc[1][tb][i]);
+        key[tb] = max(key[tb], mx_key(h[tb][i]));
+      }
+      key[tb] = max(key[tb], (uint32_t)__shfl_xor((int)key[tb], 16, kWave));
+      key[tb] = max(key[tb], (uint32_t)__shfl_xor((int)key[tb], 32, kWave));
+      if (g == 0) xch[(wave * kMxTBM + tb) * 16 + l16] = key[tb];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int tb = 0; tb < kMxTBM; ++tb) {
+      const uint32_t gk = max(key[tb], xch[((wave ^ 1) * kMxTBM + tb) * 16 + l16]);
+      int ex = 0;
+      const uint32_t sc = mx_scale(gk, ex);
+      uint32_t q = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) q |= mx_code(h[tb][i], gk, ex) << (4 * i);
+      const int tr = 16 * tb + l16;   // row of the m-tile
+      *reinterpret_cast<uint16_t*>(qc + tr * 64 + wave * 8 + 2 * g) = (uint16_t)q;
+      if ((wave & 1) == 0 && g == 0) qs[tr * 4 + (wave >> 1)] = (unsigned char)sc;
+    }
+    __syncthreads();
+    // 64 bytes of codes (the workgroup's 128 h columns) per row: 16 bytes per thread; the 4
+    // scale bytes of a row as one word.
+    const int tr = tid >> 2, piece = tid & 3;
+    const int col0 = nb * kMxWaves * 16;   // first h column of the workgroup
+    if (tr < 16 * ntb && tc + tr < M) {
+      const size_t row = (size_t)(r0 + tc + tr);
+      *reinterpret_cast<u32x4*>(p.hq_packed + row * F2 + col0 / 2 + 16 * piece) =
+          *reinterpret_cast<const u32x4*>(qc + tr * 64 + 16 * piece);
+      if (piece == 0)
+        *reinterpret_cast<uint32_t*>(p.hq_scales + row * F32 + col0 / 32) =
+            *reinterpret_cast<const uint32_t*>(qs + tr * 4);
+    }
+    return;
+  }
+  if (p.ksplit > 1) {   // raw partial sums; the split-K reduce applies the epilogue
+    float* part = p.partial + (size_t)ks * p.rows * Nw;
+#pragma unroll
+    for (int tb = 0; tb < kMxTBM; ++tb) {
+      const int t = tc + 16 * tb + l16;
+      if (tb < ntb && t < M) {
+#pragma unroll
+        for (int b = 0; b < kMxRBW; ++b)
+          *reinterpret_cast<float4*>(part + (size_t)(r0 + t) * Nw + blkrow(b) + 4 * g) =
+              make_float4(acc[b][tb][0], acc[b][tb][1], acc[b][tb][2], acc[b][tb][3]);
+      }
+    }
+    return;
+  }
   const uint32_t amax_bits = store_tile<kMxRBW, kMxTBM, SWIGLU>(p, acc, tc, ntb, M, r0, 1.0f, false, blkrow, lane, 0u);
   merge_amax(p.out_amax, amax_bits, lane);
 }
@@ -234,13 +353,31 @@ __global__ __launch_bounds__(kMxWaves* kWave) void gemm_mx_kernel(const GemmArgs
 int mx_rows_per_mtile() { return 16 * kMxTBM; }
 bool mx_supports(int Nw) { return Nw % (16 * kMxRBW * kMxWaves) == 0; }
 
+// K slices when the m-tile x row-tile grid is under one workgroup per CU: about 256
+// workgroups, at least 4 chunks per slice. NVFP4MOE_MX_KSPLIT=<n> overrides (tests, tuning).
+int mx_ksplit(int max_mtiles, int Nw, int K) {
+  const int nch = (K + kChunk - 1) / kChunk;
+  const int tiles = max_mtiles * (Nw / (16 * kMxRBW * kMxWaves));
+  int s = tiles >= 256 ? 1 : (256 + tiles - 1) / tiles;
+  if (s > nch / 4) s = nch / 4;
+  if (const char* env = std::getenv("NVFP4MOE_MX_KSPLIT")) s = std::atoi(env);
+  if (s < 1) s = 1;
+  if (s > nch) s = nch;
+  const int cps = (nch + s - 1) / s;   // chunks per slice; no empty slices
+  return (nch + cps - 1) / cps;
+}
+
 hipError_t launch_gemm_mx(const GemmArgs& a, int max_mtiles, hipStream_t stream) {
   const int ntiles_n = a.Nw / (16 * kMxRBW * kMxWaves);
-  const int total = max_mtiles * ntiles_n;   // bound on the tiles
+  const int total = max_mtiles * ntiles_n * a.ksplit;   // bound on the tiles
   const unsigned grid = (unsigned)((total + 7) / 8 * 8);
-  if (a.swiglu) gemm_mx_kernel<true><<<grid, kMxWaves * kWave, 0, stream>>>(a, ntiles_n);
-  else gemm_mx_kernel<false><<<grid, kMxWaves * kWave, 0, stream>>>(a, ntiles_n);
-  return hipGetLastError();
+  if (a.hq_packed) gemm_mx_kernel<true, true><<<grid, kMxWaves * kWave, 0, stream>>>(a, ntiles_n);
+  else if (a.swiglu) gemm_mx_kernel<true, false><<<grid, kMxWaves * kWave, 0, stream>>>(a, ntiles_n);
+  else gemm_mx_kernel<false, false><<<grid, kMxWaves * kWave, 0, stream>>>(a, ntiles_n);
+  if (a.ksplit <= 1) return hipGetLastError();
+  const hipError_t e2 = hipGetLastError();
+  if (e2 != hipSuccess) return e2;
+  return launch_splitk_reduce(a, stream);
 }
 
 }  // namespace nvfp4moe

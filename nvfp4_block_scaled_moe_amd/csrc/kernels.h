@@ -77,6 +77,9 @@ struct GemmArgs {
   const int* sched_n;              // large-M path: number of m-tiles  (workspace)
   float* partial;                  // large-M split-K: [ksplit, rows, Nw] fp32 partial sums (workspace)
   int ksplit;                      // large-M: K slices (1: no split)
+  int unit_alpha;                  // MXFP4: no per-tensor scales (alpha = 1 in the split-K reduce)
+  uint8_t* hq_packed;              // MXFP4 SwiGLU: h quantized in the epilogue, [rows, Nw/4] codes
+  uint8_t* hq_scales;              //   and [rows, Nw/64] UE8M0 scales (null: out as usual)
 };
 hipError_t launch_gemm_stream(const GemmArgs& a, hipStream_t stream);
 // K slices for the small-M path from the sizes alone (1 unless the grid is tiny).
@@ -111,6 +114,8 @@ int large_waves(int rows, int E, int Nw);
 int mx_rows_per_mtile();
 bool mx_supports(int Nw);
 hipError_t launch_gemm_mx(const GemmArgs& a, int max_mtiles, hipStream_t stream);
+// K slices of the MXFP4 GEMM from the sizes alone (1 unless the grid is under one workgroup per CU).
+int mx_ksplit(int max_mtiles, int Nw, int K);
 hipError_t launch_zero_f32(float* p, int n, hipStream_t stream);
 
 // ---- reduce.hip

@@ -223,32 +223,14 @@ __global__ __launch_bounds__(kQuantThreads) void mx_quantize_kernel(const T* __r
   float v[32];
 #pragma unroll
   for (int q = 0; q < 4; ++q) Vec8<T>::load(x + e0 + 8 * q, v + 8 * q);
-  float amax = 0.0f;
-  bool finite = true;
+  uint32_t key = 0u;
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    finite = finite && (fabsf(v[i]) <= 3.402823466e38f);
-    amax = fmaxf(amax, finite_abs(v[i]));
-  }
-  uint32_t s = 0;
+  for (int i = 0; i < 32; ++i) key = max(key, mx_key(v[i]));
   int e = 0;
-  if (!finite) {
-    s = 0xFF;
-  } else if (amax > 0.0f) {
-    int ex;
-    (void)frexpf(amax, &ex);          // amax = f * 2^ex, f in [0.5, 1): floor(log2 amax) = ex - 1
-    e = max(ex - 1 - 2, -127);
-    s = (uint32_t)(e + 127);
-  }
+  const uint32_t s = mx_scale(key, e);
   uint32_t w[4] = {0u, 0u, 0u, 0u};
-  if (finite) {
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      const uint32_t sign = (__float_as_uint(v[i]) >> 31) << 3;
-      const uint32_t mag = amax > 0.0f ? e2m1_rne_mag(ldexpf(fabsf(v[i]), -e)) : 0u;
-      w[i >> 3] |= (sign | mag) << (4 * (i & 7));
-    }
-  }
+  for (int i = 0; i < 32; ++i) w[i >> 3] |= mx_code(v[i], key, e) << (4 * (i & 7));
   *reinterpret_cast<uint4*>(packed + e0 / 2) = make_uint4(w[0], w[1], w[2], w[3]);
   scales[u] = (uint8_t)s;
 }

@@ -135,8 +135,9 @@ def quantize_experts_mxfp4(wl: inputs.Workload, device="cuda") -> MXFP4Experts:
 def moe_forward_mxfp4(x: torch.Tensor, logits: torch.Tensor, k: int, w: MXFP4Experts,
                       keep: bool = False):
     """One MoE layer forward in MXFP4 W4A4: token rows and h are MXFP4-quantized (one UE8M0
-    scale per 32 elements, no per-tensor scale, so h needs no amax); both GEMMs run on the
-    scaled FP4 matrix cores. ``x`` bf16 [T, H]; ``logits`` f32 [T, E]."""
+    scale per 32 elements, no per-tensor scale, so the up/gate GEMM's epilogue writes h as
+    MXFP4 directly); both GEMMs run on the scaled FP4 matrix cores. ``x`` bf16 [T, H];
+    ``logits`` f32 [T, E]."""
     st = {}
     r = ops.moe_route_permute(logits, k)
     st.update(r)
@@ -144,12 +145,11 @@ def moe_forward_mxfp4(x: torch.Tensor, logits: torch.Tensor, k: int, w: MXFP4Exp
     common = dict(expert_offsets=r["expert_offsets"], active_experts=r["active_experts"],
                   n_active=r["n_active"])
     xq, xs = ops.mxfp4_quantize(x)
-    h = ops.moe_grouped_gemm_mxfp4(ops.EPI_SWIGLU, xq, xs, w.w13_t, gather_index=r["sorted_slot"],
-                                   gather_div=k, rows=S, out_dtype=torch.float32, **common)
-    hq, hs = ops.mxfp4_quantize(h)
+    hq, hs = ops.moe_grouped_gemm_mxfp4_swiglu_q(xq, xs, w.w13_t, gather_index=r["sorted_slot"],
+                                                 gather_div=k, rows=S, **common)
     y = ops.moe_grouped_gemm_mxfp4(ops.EPI_NONE, hq, hs, w.w2_t, rows=S, out_dtype=torch.float32, **common)
     out = ops.moe_unpermute_reduce(y, r["slot_to_row"], r["topk_w"])
     if keep:
-        st.update(xq=xq, xs=xs, h=h, hq=hq, hs=hs, y=y, out=out)
+        st.update(xq=xq, xs=xs, hq=hq, hs=hs, y=y, out=out)
         return out, st
     return out

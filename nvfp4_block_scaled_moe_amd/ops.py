@@ -257,13 +257,37 @@ def moe_grouped_gemm_mxfp4(epi: int, a: torch.Tensor, a_scales: torch.Tensor, w:
         out = torch.empty((rows, ncol), dtype=out_dtype, device=a.device)
     amax = torch.empty((1,), dtype=torch.float32, device=a.device) if want_amax else None
     lib = _lib.load()
-    ws = _ws(lib.moe_grouped_gemm_mxfp4_workspace_size(rows, E), a.device)
+    ws = _ws(lib.moe_grouped_gemm_mxfp4_workspace_size(rows, E, Nw, K), a.device)
     st = lib.moe_grouped_gemm_mxfp4(
         epi, _ptr(a), _ptr(a_scales), a_rows, _ptr(gather_index), int(gather_div), _ptr(w.codes),
         _ptr(w.scales), _ptr(expert_offsets), _ptr(active_experts), _ptr(n_active), E, rows, Nw, K,
         _ptr(out), _DT[out.dtype], _ptr(amax), _ptr(ws), ws.numel(), _stream())
     _lib.check("moe_grouped_gemm_mxfp4", st)
     return (out, amax) if want_amax else out
+
+
+def moe_grouped_gemm_mxfp4_swiglu_q(a: torch.Tensor, a_scales: torch.Tensor, w: MxTiledWeights,
+                                    expert_offsets: torch.Tensor, active_experts: torch.Tensor,
+                                    n_active: torch.Tensor, *, gather_index: torch.Tensor | None = None,
+                                    gather_div: int = 1, rows: int | None = None):
+    """MXFP4 up/gate GEMM + SwiGLU with h written as MXFP4 by the epilogue: returns
+    (h_packed uint8 [rows, Nw/4], h_scales uint8 [rows, Nw/64])."""
+    _dev(a, a_scales, w.codes, w.scales, expert_offsets, active_experts, n_active, gather_index)
+    E, Nw, K = w.B, w.R, w.C
+    a_rows = a.shape[0]
+    if rows is None:
+        rows = gather_index.numel() if gather_index is not None else a_rows
+    F = Nw // 2
+    hp = torch.empty((rows, F // 2), dtype=torch.uint8, device=a.device)
+    hs = torch.empty((rows, F // 32), dtype=torch.uint8, device=a.device)
+    lib = _lib.load()
+    ws = _ws(lib.moe_grouped_gemm_mxfp4_workspace_size(rows, E, Nw, K), a.device)
+    st = lib.moe_grouped_gemm_mxfp4_swiglu_q(
+        _ptr(a), _ptr(a_scales), a_rows, _ptr(gather_index), int(gather_div), _ptr(w.codes), _ptr(w.scales),
+        _ptr(expert_offsets), _ptr(active_experts), _ptr(n_active), E, rows, Nw, K, _ptr(hp), _ptr(hs),
+        _ptr(ws), ws.numel(), _stream())
+    _lib.check("moe_grouped_gemm_mxfp4_swiglu_q", st)
+    return hp, hs
 
 
 def last_dispatch() -> int:

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(_lib.SIGNATURES), "binding signatures out of sync with the header"
     for n in names:
         assert hasattr(lib, n)
-    assert lib.nvfp4moe_abi_version() == 201
+    assert lib.nvfp4moe_abi_version() == 203
 
 
 FAKE = ctypes.c_void_p(1 << 20)      # aligned, never dereferenced: validation fails first
@@ -65,6 +65,22 @@ def test_route_permute_rejects_bad_arguments():
     for T, E, k in [(0, 8, 2), (4, 8, 9), (4, 8, 0), (4, 2048, 8), (4, 256, 65), (1 << 22, 256, 8)]:
         st, _ = _err(lib.moe_route_permute(*args(T, E, k)))
         assert st == _lib.ERR_INVALID_ARG, (T, E, k)
+
+
+def test_mxfp4_swiglu_q_argument_checks():
+    lib = _lib.load()
+
+    def call(hp=FAKE, hs=FAKE, Nw=256, K=256, ws_bytes=1 << 30):
+        return lib.moe_grouped_gemm_mxfp4_swiglu_q(FAKE, FAKE, 16, None, 1, FAKE, FAKE, FAKE, FAKE, FAKE, 8, 16,
+                                                   Nw, K, hp, hs, FAKE, ws_bytes, None)
+    for kw in [dict(hp=None), dict(hs=None), dict(hp=MISALIGNED), dict(hs=ctypes.c_void_p((1 << 20) + 2)),
+               dict(K=48)]:
+        st, _ = _err(call(**kw))
+        assert st == _lib.ERR_INVALID_ARG, kw
+    st, _ = _err(call(Nw=384))
+    assert st == _lib.ERR_UNSUPPORTED
+    st, _ = _err(call(ws_bytes=8))
+    assert st == _lib.ERR_WORKSPACE
 
 
 def test_route_permute_workspace():
@@ -190,7 +206,12 @@ def test_mxfp4_argument_checks_and_sizes():
         assert st == _lib.ERR_INVALID_ARG, kw
     st, msg = _err(_mx_gemm(lib, Nw=384))
     assert st == _lib.ERR_UNSUPPORTED and "256" in msg
-    need = lib.moe_grouped_gemm_mxfp4_workspace_size(16, 8)
+    need = lib.moe_grouped_gemm_mxfp4_workspace_size(16, 8, 256, 256)
     assert need >= 2 * (1 + 8) * 4
+    # a grid under one workgroup per CU splits K: M = 512, N = 2048, K = 6144 (48 chunks) has
+    # 5 x 8 tiles (host bound) -> 7 slices of 7 chunks, fp32 partial sums [7, 512, 2048]
+    assert lib.moe_grouped_gemm_mxfp4_workspace_size(512, 1, 2048, 6144) >= 7 * 512 * 2048 * 4
+    assert lib.moe_grouped_gemm_mxfp4_workspace_size(65536, 256, 4096, 7168) < 1 << 20   # no split
+    assert lib.moe_grouped_gemm_mxfp4_workspace_size(0, 8, 256, 64) == 0
     st, _ = _err(_mx_gemm(lib, ws_bytes=need - 1))
     assert st == _lib.ERR_WORKSPACE

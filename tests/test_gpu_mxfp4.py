@@ -143,6 +143,62 @@ def test_grouped_gemm_mxfp4(counts, Nw, K):
         assert rel_fro(got16, omoe.bf16_round(want)) <= W4A4_TOL
 
 
+@pytest.mark.parametrize("counts,Nw,K", MX_CASES)
+def test_grouped_gemm_mxfp4_split_k(counts, Nw, K, monkeypatch):
+    """K forced into 3 slices of whole chunks (slices that start inside a scale window, and a
+    window crossed by a slice), summed by the fixed-order split-K reduce."""
+    say("gemm mxfp4 split-k", counts, Nw, K)
+    monkeypatch.setenv("NVFP4MOE_MX_KSPLIT", "3")
+    d = _mx_problem(counts, Nw, K, seed=Nw + K + 1)
+    for epi in (ops.EPI_NONE, ops.EPI_SWIGLU):
+        want = omoe.grouped_gemm(d["A"], d["offsets"], d["W"], "swiglu" if epi else "none")
+        got, amax = _run(d, epi, torch.float32, want_amax=True)
+        got = np_(got)
+        assert_finite(got)
+        assert rel_fro(got, want) < 1e-5
+        assert np_(amax)[0] == np.abs(got).max()
+
+
+def test_dense_mxfp4_gemm_full_size():
+    """The dense GEMM M=512, N=2048, K=6144 in MXFP4 (a grid of 32 tiles: K split on its own
+    into 7 slices of 7 chunks), full output against the oracle."""
+    wl = inputs.WORKLOADS["dense"]
+    say("dense mxfp4")
+    wp, ws = ops.mxfp4_quantize(inputs.expert_weight_fp32(wl, "dense", 0, DEV).unsqueeze(0))
+    x = inputs.activations_bf16(wl).to(DEV)
+    ap, as_ = ops.mxfp4_quantize(x)
+    one = lambda v: torch.tensor(v, dtype=torch.int32, device=DEV)
+    out = ops.moe_grouped_gemm_mxfp4(ops.EPI_NONE, ap, as_, ops.mxfp4_weights_tile(wp, ws), one([0, wl.T]),
+                                     one([0]), one([1]), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    want = omx.dequantize(np_(ap), np_(as_)) @ omx.dequantize(np_(wp[0]), np_(ws[0])).T
+    got = np_(out)
+    assert_finite(got)
+    r = rel_fro(got, want)
+    say("dense mxfp4 rel err", r)
+    assert r < 1e-5
+
+
+@pytest.mark.parametrize("counts,Nw,K,T,k", [(c, n, kk, None, None) for c, n, kk in MX_CASES]
+                         + [([7, 0, 300, 9], 256, 512, 120, 3)])
+def test_swiglu_q_codes_bit_exact(counts, Nw, K, T, k):
+    """h quantized to MXFP4 by the up/gate epilogue: codes and scales equal, bit for bit, the
+    oracle's MXFP4 quantization of the float32 h of the unquantized call (same arithmetic in
+    both epilogues), and that h matches the float64 oracle."""
+    say("swiglu_q", counts, Nw, K, T, k)
+    d = _mx_problem(counts, Nw, K, seed=Nw + K + 2, T=T, k=k)
+    h32 = np_(_run(d, ops.EPI_SWIGLU, torch.float32))
+    assert rel_fro(h32, omoe.grouped_gemm(d["A"], d["offsets"], d["W"], "swiglu")) < 1e-5
+    t = lambda x: torch.from_numpy(x).to(DEV)
+    hp, hs = ops.moe_grouped_gemm_mxfp4_swiglu_q(d["ap"], d["as_"], d["wt"], t(d["offsets"]), t(d["active"]),
+                                                 t(d["n_active"]), rows=d["rows"], gather_div=d["gdiv"],
+                                                 gather_index=None if d["gidx"] is None else t(d["gidx"]))
+    torch.cuda.synchronize()
+    qp, qs = omx.quantize(h32.astype(np.float32))
+    assert np.array_equal(np_(hp), qp)
+    assert np.array_equal(np_(hs), qs)
+
+
 def test_grouped_gemm_mxfp4_gather_and_amax():
     say("gemm mxfp4 gather")
     d = _mx_problem([7, 0, 300, 9], 256, 512, seed=5, T=120, k=3)
@@ -195,8 +251,8 @@ def test_tiny_mxfp4_layer_end_to_end():
 def test_prefill_mxfp4_layer_full_size():
     """The prefill workload (8192 tokens, 256 experts, top-8, H=7168, F=2048, Zipf routing)
     in MXFP4, exactly the calls the benchmark times: routing in full, activation and h codes
-    in full (the oracle quantizes the GPU's fp32 h), both GEMMs on sampled experts, the
-    reduce in full."""
+    in full (h's codes from the quantizing epilogue against the oracle's quantization of the
+    fp32 h of the unquantized call), both GEMMs on sampled experts, the reduce in full."""
     from nvfp4_block_scaled_moe_amd import layer
     wl = inputs.WORKLOADS["prefill"]
     T = wl.T
@@ -205,6 +261,11 @@ def test_prefill_mxfp4_layer_full_size():
     x = inputs.activations_bf16(wl, T).to(DEV)
     lg = inputs.router_logits(wl, T)
     out, st = layer.moe_forward_mxfp4(x, lg.to(DEV), wl.k, w, keep=True)
+    # the float32 h of the same up/gate GEMM without the quantized epilogue
+    st["h"] = ops.moe_grouped_gemm_mxfp4(ops.EPI_SWIGLU, st["xq"], st["xs"], w.w13_t,
+                                         st["expert_offsets"], st["active_experts"], st["n_active"],
+                                         gather_index=st["sorted_slot"], gather_div=wl.k, rows=T * wl.k,
+                                         out_dtype=torch.float32)
     torch.cuda.synchronize()
     ids, rw = omoe.route(lg.numpy(), wl.k)
     perm = omoe.permute(ids, wl.E)
