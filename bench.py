@@ -120,7 +120,7 @@ def main():
                           "top-8, 512 concurrent) on RTX PRO 6000 Blackwell SM120; vs_baseline divides by 55"),
     )
     if line["roofline"] is not None:
-        line["roofline"]["traffic"] = None if mx else measured_traffic(wl, T)
+        line["roofline"]["traffic"] = measured_traffic(wl, T, mx)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(torch, wl, w, x, lg, T, mode, args.cpu_seconds)
     else:
@@ -139,17 +139,18 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-def measured_traffic(wl, T):
+def measured_traffic(wl, T, mx=False):
     """HBM bytes per up/gate launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary
     (copy-calibrated), or None when none covers this workload or the kernel source has
     changed since the counters were taken."""
     import hashlib
     import re
-    known = {("decode", 512): ("gemm_stream_decode512_traffic.md", "gemm_stream.hip"),
-             ("prefill", 8192): ("gemm_large_prefill8192_traffic.md", "gemm_large.hip")}
-    if (wl.name, T) not in known:
+    known = {("decode", 512, False): ("gemm_stream_decode512_traffic.md", "gemm_stream.hip"),
+             ("prefill", 8192, False): ("gemm_large_prefill8192_traffic.md", "gemm_large.hip"),
+             ("prefill", 8192, True): ("gemm_mx_prefill8192_traffic.md", "gemm_mx.hip")}
+    if (wl.name, T, mx) not in known:
         return None
-    prof_name, src_name = known[(wl.name, T)]
+    prof_name, src_name = known[(wl.name, T, mx)]
     prof = os.path.join(ROOT, "profiles", prof_name)
     src = os.path.join(ROOT, "nvfp4_block_scaled_moe_amd", "csrc", src_name)
     try:
