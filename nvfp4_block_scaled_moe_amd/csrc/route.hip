@@ -256,14 +256,12 @@ __device__ __forceinline__ void wave_scatter(const int* __restrict__ ids, int lo
   }
 }
 
-__global__ __launch_bounds__(kPermThreads) void permute_kernel(const int* __restrict__ ids, int S,
-                                                               int E, int nbits,
-                                                               int* __restrict__ offsets,
-                                                               int* __restrict__ sorted_slot,
-                                                               int* __restrict__ slot_to_row,
-                                                               int* __restrict__ active,
-                                                               int* __restrict__ n_active) {
-  extern __shared__ int sm[];
+// The one-workgroup permutation (kPermThreads threads) over ids[0, S) (global memory or
+// LDS); sm: (kPermWaves * E + 2 * kPermWaves) ints of LDS.
+__device__ __forceinline__ void permute_block(const int* ids, int S, int E, int nbits, int* sm,
+                                              int* __restrict__ offsets, int* __restrict__ sorted_slot,
+                                              int* __restrict__ slot_to_row, int* __restrict__ active,
+                                              int* __restrict__ n_active) {
   int* cnt = sm;                          // [kPermWaves][E]
   int* wsum = sm + kPermWaves * E;        // [kPermWaves] row totals per wave
   int* wflag = wsum + kPermWaves;         // [kPermWaves] active-expert totals per wave
@@ -328,6 +326,94 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(const int* __rest
 
   // 3. stable scatter of each wave's slice
   wave_scatter(ids, lo, hi, cnt + wave * E, nbits, lane, sorted_slot, slot_to_row);
+}
+
+__global__ __launch_bounds__(kPermThreads) void permute_kernel(const int* __restrict__ ids, int S, int E,
+                                                               int nbits, int* __restrict__ offsets,
+                                                               int* __restrict__ sorted_slot,
+                                                               int* __restrict__ slot_to_row,
+                                                               int* __restrict__ active,
+                                                               int* __restrict__ n_active) {
+  extern __shared__ int sm[];
+  permute_block(ids, S, E, nbits, sm, offsets, sorted_slot, slot_to_row, active, n_active);
+}
+
+// Few tokens (T <= kPermWaves, T * k <= kSmallSlots): routing and permutation in one
+// workgroup and one launch. Wave t routes token t by k rounds of wave argmax: each round takes
+// the largest order-preserving logit key (DPP max over the wave) and, among the experts
+// holding it, the lowest id (ballots; registers ascend in id, lanes within a register), and
+// removes it. Weights as in router_kernel (float64 exp(l - l_max) over the kept, summed over
+// the wave). The ids also go to LDS, from which the workgroup permutes as permute_kernel does.
+constexpr int kSmallSlots = 1024;
+
+template <int PL>
+__device__ __forceinline__ void route_token_rounds(const float* __restrict__ row, int E, int k, int lane,
+                                                   int* __restrict__ ids, float* __restrict__ w, int* lds_ids) {
+  uint32_t key[PL];
+  float v[PL];
+#pragma unroll
+  for (int i = 0; i < PL; ++i) {
+    const int e = lane + kWave * i;
+    const float x = e < E ? row[e] : -INFINITY;
+    v[i] = (x != x) ? -INFINITY : x;
+    key[i] = e < E ? logit_key(x) : 0u;   // every real key is >= logit_key(-inf) > 0
+  }
+  int my_e = 0;
+  float my_x = 0.0f;
+  for (int j = 0; j < k; ++j) {
+    uint32_t best = key[0];
+#pragma unroll
+    for (int i = 1; i < PL; ++i) best = max(best, key[i]);
+    best = wave_max_u32_uniform(best);
+    int e = -1;
+    float x = 0.0f;
+#pragma unroll
+    for (int i = 0; i < PL; ++i) {
+      const uint64_t m = __ballot(key[i] == best);
+      if (e < 0 && m) {
+        const int l = __builtin_ctzll(m);
+        e = kWave * i + l;
+        x = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(v[i]), l));
+      }
+    }
+    if (lane == j) {
+      my_e = e;
+      my_x = x;
+    }
+#pragma unroll
+    for (int i = 0; i < PL; ++i)
+      if (kWave * i + lane == e) key[i] = 0u;
+  }
+  const double m = (double)__uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(my_x), 0));
+  const double ex = lane < k ? exp((double)my_x - m) : 0.0;
+  double sum = ex;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o, kWave);
+  if (lane < k) {
+    ids[lane] = my_e;
+    w[lane] = (float)(ex / sum);
+    lds_ids[lane] = my_e;
+  }
+}
+
+template <int PL>
+__global__ __launch_bounds__(kPermThreads) void route_permute_small_kernel(const float* __restrict__ logits,
+                                                                           int T, int E, int k, int nbits,
+                                                                           int* __restrict__ ids,
+                                                                           float* __restrict__ w,
+                                                                           int* __restrict__ offsets,
+                                                                           int* __restrict__ sorted_slot,
+                                                                           int* __restrict__ slot_to_row,
+                                                                           int* __restrict__ active,
+                                                                           int* __restrict__ n_active) {
+  extern __shared__ int sm[];
+  int* s_ids = sm;                   // [T * k] expert ids
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  if (wave < T)
+    route_token_rounds<PL>(logits + (size_t)wave * E, E, k, lane, ids + (size_t)wave * k, w + (size_t)wave * k,
+                           s_ids + wave * k);
+  __syncthreads();
+  permute_block(s_ids, T * k, E, nbits, sm + kSmallSlots, offsets, sorted_slot, slot_to_row, active, n_active);
 }
 
 // Many slots: the permutation in two launches over chunks of slots, so that the scattered
@@ -483,6 +569,22 @@ void perm_plan(int S, int& chunk, int& nblk) {
 }
 }  // namespace
 
+template <int PL>
+hipError_t launch_small(const float* logits, int T, int E, int k, int nbits, int* topk_ids, float* topk_w,
+                        int* expert_offsets, int* sorted_slot, int* slot_to_row, int* active_experts,
+                        int* n_active, hipStream_t stream) {
+  static std::atomic<uint64_t> attr_done{0};
+  const hipError_t attr = ensure_dynamic_lds(reinterpret_cast<const void*>(&route_permute_small_kernel<PL>),
+                                             (kSmallSlots + kPermWaves * kMaxExperts + 2 * kPermWaves) * (int)sizeof(int),
+                                             attr_done);
+  if (attr != hipSuccess) return attr;
+  const size_t shmem = (size_t)(kSmallSlots + kPermWaves * E + 2 * kPermWaves) * sizeof(int);
+  route_permute_small_kernel<PL><<<1, kPermThreads, shmem, stream>>>(logits, T, E, k, nbits, topk_ids, topk_w,
+                                                                    expert_offsets, sorted_slot, slot_to_row,
+                                                                    active_experts, n_active);
+  return hipGetLastError();
+}
+
 size_t route_permute_ws_bytes(int T, int E, int k) {
   int chunk = 0, nblk = 0;
   perm_plan(T * k, chunk, nblk);
@@ -497,6 +599,22 @@ hipError_t launch_route_permute(const float* logits, int T, int E, int k, int* t
   // token of 512 experts, top-22); many tokens: a wave per token selects (more tokens per CU;
   // 8192 tokens of 256 experts: 18 us against 33 us sorted). NVFP4MOE_ROUTER=wave|sort forces.
   const char* force = std::getenv("NVFP4MOE_ROUTER");
+  const char* pforce0 = std::getenv("NVFP4MOE_PERMUTE");
+  int nb = 0;
+  while ((1 << nb) < E) ++nb;
+  // Few tokens: route and permute in one launch (NVFP4MOE_ROUTER or NVFP4MOE_PERMUTE set
+  // to anything but "small" selects the separate kernels).
+  const bool small_ok = T <= kPermWaves && T * k <= kSmallSlots;
+  const bool small = small_ok && (force ? !std::strcmp(force, "small") : true) &&
+                     (pforce0 ? !std::strcmp(pforce0, "small") : true);
+  if (small) {
+    const int pl = (E + kWave - 1) / kWave;
+    if (pl <= 1) return launch_small<1>(logits, T, E, k, nb, topk_ids, topk_w, expert_offsets, sorted_slot, slot_to_row, active_experts, n_active, stream);
+    if (pl <= 2) return launch_small<2>(logits, T, E, k, nb, topk_ids, topk_w, expert_offsets, sorted_slot, slot_to_row, active_experts, n_active, stream);
+    if (pl <= 4) return launch_small<4>(logits, T, E, k, nb, topk_ids, topk_w, expert_offsets, sorted_slot, slot_to_row, active_experts, n_active, stream);
+    if (pl <= 8) return launch_small<8>(logits, T, E, k, nb, topk_ids, topk_w, expert_offsets, sorted_slot, slot_to_row, active_experts, n_active, stream);
+    return launch_small<16>(logits, T, E, k, nb, topk_ids, topk_w, expert_offsets, sorted_slot, slot_to_row, active_experts, n_active, stream);
+  }
   const bool sort_router = force ? !std::strcmp(force, "sort") : T < 256;
   if (sort_router) {
     if (E <= 64) router_sort_kernel<64><<<T, router_sort_threads<64>(), 0, stream>>>(logits, E, k, topk_ids, topk_w);

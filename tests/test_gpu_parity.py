@@ -195,6 +195,23 @@ def test_both_routers_bit_exact(router, T, E, k, monkeypatch):
     np.testing.assert_allclose(np_(r["topk_w"]), w, rtol=1e-6, atol=0)
 
 
+@pytest.mark.parametrize("T,E,k", [(16, 1024, 64), (16, 512, 22), (2, 64, 64), (7, 100, 7), (1, 256, 8),
+                                   (1, 1, 1), (16, 8, 2)])
+def test_small_route_permute_bit_exact(T, E, k, monkeypatch):
+    """Few tokens: routing (k rounds of wave argmax) and permutation in one workgroup and one
+    launch, against the oracle; ties, -0/+0 and an all-equal row planted."""
+    say("small route", T, E, k)
+    monkeypatch.setenv("NVFP4MOE_ROUTER", "small")
+    lg = inputs.random_fp32((T, E), 7 * T + E + k)
+    lg[0, : min(E, 9)] = 1.5                      # equal logits at the top of row 0
+    if E > 40:
+        lg[-1, 40] = -0.0
+        lg[-1, 3] = 0.0
+    if T >= 3:
+        lg[1, :] = 0.25                           # an all-tie row
+    _check_route(lg, k, E)
+
+
 def test_route_permute_is_deterministic():
     say("route determinism")
     wl = inputs.WORKLOADS["prefill"]
