@@ -25,7 +25,8 @@
 //     select (opsel) picks each one. Weights are loaded two chunks ahead into registers.
 //   * Step c issues the 16 MFMAs (16x16x128) of chunk c on fragments read in step c-1 and
 //     meanwhile reads chunk c+1's fragments, commits chunk c+2 to the ring and requests chunk
-//     c+3: the reads never wait behind the barrier that ends the step. Epilogue as in the
+//     c+4: the reads never wait behind the barrier that ends the step, and a staging load has
+//     two steps to arrive. Epilogue as in the
 //     other GEMMs with alpha 1 (MXFP4 has no per-tensor scale): SwiGLU, bf16 or f32 stores,
 //     amax.
 //   * SwiGLU with quantized output: h is written as MXFP4 straight from the epilogue (no
@@ -169,8 +170,8 @@ __global__ __launch_bounds__(kMxWaves* kWave) void gemm_mx_kernel(const GemmArgs
   const uint32_t ssrc = tok_ok ? arow * (uint32_t)Ks + q : kOOB;
   const uint32_t cdst = tk * kMxTok + 16 * q, sdst = kMxCodes + q * 128 + (tk & 15) * 8 + (tk >> 4);
 
-  u32x4 bst[2];
-  uint32_t bsc[2];
+  u32x4 bst[4];   // staging sets: chunk clo + j in set j & 3 (requested two steps before its commit)
+  uint32_t bsc[4];
   auto b_issue = [&](int set, int c) {   // k blocks past K (or the slice) read zero codes and scale 0
     const bool in = c < chi && 128 * c + 32 * q < K;
     bst[set] = ld128(ar, in ? csrc + 64u * c : kOOB, 0);
@@ -201,8 +202,8 @@ __global__ __launch_bounds__(kMxWaves* kWave) void gemm_mx_kernel(const GemmArgs
     for (int tb = 0; tb < kMxTBM; ++tb) acc[b][tb] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
   // prologue: scale windows w0 and w0 + 1, weights of the slice's first kMxDepth chunks,
-  // activations of its first two chunks committed to slots 0 and 1, the third requested
-  // (staging set 0)
+  // activations of its first two chunks committed to slots 0 and 1, the third and fourth
+  // requested (staging sets 2 and 3)
   s_issue(sa, w0);
   s_issue(sb, w0 + 1);
   b_issue(0, clo);
@@ -211,16 +212,17 @@ __global__ __launch_bounds__(kMxWaves* kWave) void gemm_mx_kernel(const GemmArgs
   for (int d = 0; d < kMxDepth; ++d) w_issue(d, clo + d);
   b_commit(0, 0);
   b_commit(1, 1);
-  b_issue(0, clo + 2);
+  b_issue(2, clo + 2);
+  b_issue(3, clo + 3);
   __syncthreads();
 
   // The main loop, compiled for NTB = 8, 4, 2 or 1 token blocks (ntb rounded up; blocks past
   // the m-tile's rows hold zeros). With j = c - clo: chunk c lives in LDS slot j % 3 and
-  // staging set j & 1, its weights in ring entry j % kMxDepth. Step c: request chunk c+3 (set
-  // (j+1) & 1, whose chunk c+1 was committed in step c-1), read chunk c+1's fragments
-  // (committed in step c-1), MFMAs of chunk c, commit chunk c+2 to slot (j+2) % 3 (chunk c-1,
-  // read in step c-2), barrier. Steps come in blocks of 16; the MFMAs of chunks past the
-  // slice are skipped.
+  // staging set j & 3, its weights in ring entry j % kMxDepth. Step c: request chunk c+4 (set
+  // j & 3, whose chunk c was committed in step c-2), read chunk c+1's fragments (committed in
+  // step c-1), MFMAs of chunk c, commit chunk c+2 (requested in step c-2) to slot (j+2) % 3
+  // (chunk c-1, read in step c-2), barrier. Steps come in blocks of 16; the MFMAs of chunks
+  // past the slice are skipped.
   auto body = [&](auto ntb_tag) {
     constexpr int NTB = decltype(ntb_tag)::value;
     u32x4 bcur[NTB], bnext[NTB];
@@ -246,7 +248,7 @@ __global__ __launch_bounds__(kMxWaves* kWave) void gemm_mx_kernel(const GemmArgs
         constexpr int d = u % kMxDepth;
         const int slot1 = slot == kMxSlots - 1 ? 0 : slot + 1;
         const int slot2 = slot1 == kMxSlots - 1 ? 0 : slot1 + 1;
-        b_issue((u + 1) & 1, c + 3);
+        b_issue(u & 3, c + 4);
         u32x4 wa[kMxRBW];
 #pragma unroll
         for (int b = 0; b < kMxRBW; ++b) wa[b] = wring[d][b];
@@ -260,7 +262,7 @@ __global__ __launch_bounds__(kMxWaves* kWave) void gemm_mx_kernel(const GemmArgs
               acc[b][tb] = mfma_mx<(u & 3), (tb & 3)>(wa[b], scs[b][u >> 2], bcur[tb], scb[tb >> 2], acc[b][tb]);
           });
         }
-        b_commit(u & 1, slot2);
+        b_commit((u + 2) & 3, slot2);
         if (u == kMxWin - 1) {
 #pragma unroll
           for (int b = 0; b < kMxRBW; ++b) {
