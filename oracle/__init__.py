@@ -14,6 +14,8 @@ emulated exactly with ``np.float32`` scalars/arrays.
 Modules
   nvfp4  -- E2M1 / E4M3 code tables, unpacking, dequantize, quantize.
   mxfp4  -- the MXFP4 variant (group 32, UE8M0 scales): dequantize, quantize.
+  mxfp8  -- block-scaled FP8 (MXFP8: E4M3 elements, UE8M0 per 32): dequantize,
+            quantize.
   moe    -- router, permutation, grouped GEMM, SwiGLU, unpermute-reduce,
             FP8 activation round trip, the whole MoE layer (W4A16 / W4A4 /
             MXFP4).
@@ -23,4 +25,4 @@ here is pinned by a ``-m "not gpu"`` test against something other than
 itself (closed forms, an independent library cast, exact rational brute
 force, invariants).
 """
-from . import nvfp4, mxfp4, moe  # noqa: F401
+from . import nvfp4, mxfp4, mxfp8, moe  # noqa: F401

@@ -10,9 +10,11 @@ import pytest
 
 import oracle.moe as moe
 import oracle.mxfp4 as mxfp4
+import oracle.mxfp8 as mxfp8
 import oracle.nvfp4 as nvfp4
 import tests.test_oracle_moe as tm
 import tests.test_oracle_mxfp4 as tx
+import tests.test_oracle_mxfp8 as t8
 import tests.test_oracle_nvfp4 as tn
 
 
@@ -92,6 +94,10 @@ MUTATIONS = [
      lambda a: np.maximum(np.round(np.log2(np.asarray(a, np.float64))).astype(np.int64) - 2, -127),
      tx.test_grid_inputs_round_trip_exactly),
     ("mx dequantize scale per 16", mxfp4, "GROUP", 16, tx.test_hand_examples),
+    ("mxfp8 shared exponent with emax 7", mxfp8, "E4M3_EMAX", 7, t8.test_grid_inputs_round_trip_exactly),
+    ("mxfp8 rounds the scale exponent", mxfp8, "shared_exponent",
+     lambda a: np.maximum(np.round(np.log2(np.asarray(a, np.float64))).astype(np.int64) - 8, -127),
+     t8.test_codes_match_torch_e4m3fn_cast),
 ]
 
 
