@@ -30,6 +30,7 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0      # dense; the f16 MFMA runs at the same rate
 FP4_PEAK_TFLOPS = 10100.0
+FP8_PEAK_TFLOPS = 5000.0
 PAGES_DECODE_TFLOPS = (0.8, 55.0)   # RTX PRO 6000 (SM120), FP4, per-expert M=16-64
 
 
@@ -346,6 +347,10 @@ def dense_line(torch, ops, inputs, wl, args, M):
     wmx = ops.mxfp4_weights_tile(*ops.mxfp4_quantize(inputs.expert_weight_fp32(wl, "dense", 0, dev).unsqueeze(0)))
     amx, amx_s = ops.mxfp4_quantize(a)
     tmx = timed(lambda: ops.moe_grouped_gemm_mxfp4(ops.EPI_NONE, amx, amx_s, wmx, **common))
+    # block-scaled FP8 (MXFP8: E4M3 elements, UE8M0 per 32) on the scaled FP8 matrix cores
+    w8 = ops.mxfp8_weights_tile(*ops.mxfp8_quantize(inputs.expert_weight_fp32(wl, "dense", 0, dev).unsqueeze(0)))
+    a8, a8_s = ops.mxfp8_quantize(a)
+    t8 = timed(lambda: ops.moe_grouped_gemm_mxfp8(ops.EPI_NONE, a8, a8_s, w8, **common))
     tf = lambda us: flops / (us * 1e-6) / 1e12
     return dict(
         metric="MoE NVFP4 grouped-GEMM TFLOPS + weight GB/s vs tokens/expert, % roofline",
@@ -358,6 +363,8 @@ def dense_line(torch, ops, inputs, wl, args, M):
         torch_mm_bf16_tflops=round(tf(tmm), 2), torch_mm_bf16_us=round(tmm, 2),
         mxfp4_w4a4_tflops=round(tf(tmx), 2), mxfp4_w4a4_us=round(tmx, 2),
         mxfp4_w4a4_fp4_peak_frac=round(tf(tmx) / FP4_PEAK_TFLOPS, 4),
+        mxfp8_w8a8_tflops=round(tf(t8), 2), mxfp8_w8a8_us=round(t8, 2),
+        mxfp8_w8a8_fp8_peak_frac=round(tf(t8) / FP8_PEAK_TFLOPS, 4),
         roofline=dict(bound="mfma", kernel="moe_grouped_gemm_nvfp4 call (activation prep + GEMM)",
                       achieved=round(tf(t16), 1), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
                       frac=round(tf(t16) / BF16_PEAK_TFLOPS, 4), traffic=None),

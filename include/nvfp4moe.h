@@ -333,6 +333,47 @@ nvfp4moe_status moe_grouped_gemm_mxfp4_swiglu_q(const uint8_t* a, const uint8_t*
                                                 int32_t K, uint8_t* h_packed, uint8_t* h_scales, void* ws,
                                                 size_t ws_bytes, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * MXFP8 (block-scaled FP8): FP8 E4M3 codes, one per byte, with one UE8M0 scale per 32
+ * elements and no per-tensor scale; the block-scaled FP8 dense GEMM next to the MoE layer
+ * ([P1] sections 1-2: FP8 activations, FP8 scaled-matmul kernels for the dense layers).
+ * Storage of a matrix [R, C]: codes uint8 [R, C] (OCP E4M3FN), scales uint8 [R, C/32].
+ *
+ * mxfp8_quantize -- float rows [R, C] to MXFP8 per 32-group along C (OCP MX v1.0 rule with
+ * E4M3 elements): e = max(floor(log2 amax) - 8, -127), scale byte e + 127, codes
+ * E4M3_RNE(min(|x| * 2^-e, 448)) with the sign of x; NaN/Inf groups scale 0xFF and codes 0,
+ * all-zero groups scale 0 and codes +-0.
+ *   x              device float32 or bf16 [R, C], 16-byte aligned; C % 32 == 0.
+ *   codes, scales  device uint8 [R, C] (16-byte aligned) and [R, C/32] (outputs).
+ *
+ * mxfp8_weights_tile -- B matrices [R, C] (R % 16 == 0) into the storage
+ * moe_grouped_gemm_mxfp8 reads: code tiles of 2048 bytes per (16-row block, 128 columns; lane
+ * 16 g + r holds columns 16 g .. +15 and 64 + 16 g .. +15 of row r, the scaled FP8 MFMA's
+ * operand order),
+ * scales tiled as by mxfp4_weights_tile (mxfp4_tiled_scales_bytes(R, C) per matrix).
+ *   tiled_codes    device uint8 [B * mxfp8_tiled_codes_bytes(R, C)] (output), 16-byte aligned.
+ * mxfp8_tiled_codes_bytes returns 0 for an invalid R or C.
+ *
+ * moe_grouped_gemm_mxfp8 -- W8A8 grouped GEMM on MXFP8 operands (the scaled FP8 matrix
+ * cores, v_mfma_scale_f32_16x16x128_f8f6f4 with E4M3 on both sides): arguments as for
+ * moe_grouped_gemm_mxfp4 with a [a_rows, K] codes + [a_rows, K/32] scales, weights as
+ * written by mxfp8_weights_tile, and ws of moe_grouped_gemm_mxfp8_workspace_size(rows, E,
+ * Nw, K) bytes. A dense GEMM is the call with E = 1 and expert_offsets {0, M}.
+ * ------------------------------------------------------------------------- */
+nvfp4moe_status mxfp8_quantize(const void* x, nvfp4moe_dtype x_dtype, int64_t R, int64_t C, uint8_t* codes,
+                               uint8_t* scales, void* stream);
+size_t mxfp8_tiled_codes_bytes(int64_t R, int64_t C);
+nvfp4moe_status mxfp8_weights_tile(const uint8_t* codes, const uint8_t* scales, int64_t B, int64_t R, int64_t C,
+                                   uint8_t* tiled_codes, uint8_t* tiled_scales, void* stream);
+nvfp4moe_status moe_grouped_gemm_mxfp8(nvfp4moe_epilogue epi, const uint8_t* a, const uint8_t* a_scales,
+                                       int64_t a_rows, const int32_t* gather_index, int32_t gather_div,
+                                       const uint8_t* w_codes, const uint8_t* w_scales,
+                                       const int32_t* expert_offsets, const int32_t* active_experts,
+                                       const int32_t* n_active, int32_t E, int32_t rows, int32_t Nw,
+                                       int32_t K, void* out, nvfp4moe_dtype out_dtype, float* out_amax, void* ws,
+                                       size_t ws_bytes, void* stream);
+size_t moe_grouped_gemm_mxfp8_workspace_size(int32_t rows, int32_t E, int32_t Nw, int32_t K);
+
 /* Thread-local message describing the last non-OK status ("" if none). Never NULL. */
 const char* nvfp4moe_last_error(void);
 /* nvfp4moe_path of the last moe_grouped_gemm_nvfp4 call on this thread. */

@@ -48,6 +48,12 @@ SIGNATURES = {
     "moe_grouped_gemm_mxfp4_workspace_size": (_sz, [_i32, _i32, _i32, _i32]),
     "moe_grouped_gemm_mxfp4_swiglu_q": (_int, [_vp, _vp, _i64, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
                                                _i32, _i32, _vp, _vp, _vp, _sz, _vp]),
+    "mxfp8_quantize": (_int, [_vp, _int, _i64, _i64, _vp, _vp, _vp]),
+    "mxfp8_tiled_codes_bytes": (_sz, [_i64, _i64]),
+    "mxfp8_weights_tile": (_int, [_vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp]),
+    "moe_grouped_gemm_mxfp8": (_int, [_int, _vp, _vp, _i64, _vp, _i32, _vp, _vp, _vp, _vp, _vp, _i32, _i32,
+                                      _i32, _i32, _vp, _int, _vp, _vp, _sz, _vp]),
+    "moe_grouped_gemm_mxfp8_workspace_size": (_sz, [_i32, _i32, _i32, _i32]),
     "nvfp4moe_last_error": (ctypes.c_char_p, []),
     "nvfp4moe_last_dispatch": (_int, []),
     "nvfp4moe_abi_version": (_int, []),

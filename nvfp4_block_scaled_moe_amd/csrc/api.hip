@@ -114,7 +114,7 @@ extern "C" {
 
 const char* nvfp4moe_last_error(void) { return g_last_error.c_str(); }
 int nvfp4moe_last_dispatch(void) { return g_last_dispatch; }
-int nvfp4moe_abi_version(void) { return 203; }
+int nvfp4moe_abi_version(void) { return 204; }
 
 // ------------------------------------------------------------------ quantize
 size_t nvfp4_quantize_workspace_size(int64_t B, int64_t R, int64_t C) {
@@ -374,26 +374,33 @@ nvfp4moe_status mxfp4_weights_tile(const uint8_t* packed, const uint8_t* scales,
 }
 
 namespace {
-int mx_max_mtiles(int32_t rows, int32_t E) {
-  const int bm = mx_rows_per_mtile();
+int mx_max_mtiles(int32_t rows, int32_t E, int bits) {
+  const int bm = mx_rows_per_mtile(bits);
   return (rows + bm - 1) / bm + (E < rows ? E : rows);
 }
-}  // namespace
 
-// Workspace of moe_grouped_gemm_mxfp4: the m-tile list (sched_e, sched_r, sched_n) and, when
-// K is split, the [ksplit, rows, Nw] fp32 partial sums.
-size_t moe_grouped_gemm_mxfp4_workspace_size(int32_t rows, int32_t E, int32_t Nw, int32_t K) {
+// Workspace of the MX GEMMs: the m-tile list (sched_e, sched_r, sched_n) and, when K is
+// split, the [ksplit, rows, Nw] fp32 partial sums.
+size_t mx_workspace_size(int32_t rows, int32_t E, int32_t Nw, int32_t K, int bits) {
   if (rows < 1 || E < 1 || Nw < 1 || K < 32) return 0;
-  const int mt = mx_max_mtiles(rows, E);
+  const int mt = mx_max_mtiles(rows, E, bits);
   const int ks = mx_supports(Nw) ? mx_ksplit(mt, Nw, K) : 1;
   const size_t partial = ks > 1 ? round_up((size_t)ks * rows * Nw * 4) : 0;
   return 3 * round_up((size_t)mt * 4) + partial + kAlign;
+}
+}  // namespace
+
+size_t moe_grouped_gemm_mxfp4_workspace_size(int32_t rows, int32_t E, int32_t Nw, int32_t K) {
+  return mx_workspace_size(rows, E, Nw, K, 4);
+}
+size_t moe_grouped_gemm_mxfp8_workspace_size(int32_t rows, int32_t E, int32_t Nw, int32_t K) {
+  return mx_workspace_size(rows, E, Nw, K, 8);
 }
 
 namespace {
 // Both MXFP4 GEMM entry points: out/out_dtype/out_amax, or (SwiGLU only) h quantized to
 // MXFP4 into hq_packed/hq_scales.
-nvfp4moe_status mx_gemm_call(const char* fn, nvfp4moe_epilogue epi, const uint8_t* a, const uint8_t* a_scales,
+nvfp4moe_status mx_gemm_call(const char* fn, int bits, nvfp4moe_epilogue epi, const uint8_t* a, const uint8_t* a_scales,
                              int64_t a_rows, const int32_t* gather_index, int32_t gather_div,
                              const uint8_t* w_packed, const uint8_t* w_scales, const int32_t* expert_offsets,
                              const int32_t* active_experts, const int32_t* n_active, int32_t E, int32_t rows,
@@ -414,9 +421,10 @@ nvfp4moe_status mx_gemm_call(const char* fn, nvfp4moe_epilogue epi, const uint8_
     return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: need K >= 32 and K %% 32 == 0 (K=%d)", fn, K);
   if (!mx_supports(Nw))
     return fail(NVFP4MOE_ERR_UNSUPPORTED, "%s: needs Nw %% 256 == 0 (Nw=%d)", fn, Nw);
-  if ((int64_t)rows * (K > Nw ? K : Nw) >= (int64_t(1) << 31) || a_rows * (int64_t)(K / 2) >= (int64_t(1) << 31) ||
-      (int64_t)Nw * ((K + 127) / 128 * 64) >= (int64_t(1) << 31))
-    return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: rows * max(K, Nw), a_rows * K / 2 and Nw * K / 2 must be < 2^31", fn);
+  const int64_t kbytes = bits == 8 ? (int64_t)K : (int64_t)(K / 2);   // code bytes of a row
+  if ((int64_t)rows * (K > Nw ? K : Nw) >= (int64_t(1) << 31) || a_rows * kbytes >= (int64_t(1) << 31) ||
+      (int64_t)Nw * ((K + 127) / 128 * 128) * bits / 8 >= (int64_t(1) << 31))
+    return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: rows * max(K, Nw) and the code bytes of a and w must be < 2^31", fn);
   if (!gather_index && a_rows != rows)
     return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: without gather_index a_rows must equal rows", fn);
   if (gather_index && gather_div < 1) return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: gather_div must be >= 1", fn);
@@ -424,13 +432,13 @@ nvfp4moe_status mx_gemm_call(const char* fn, nvfp4moe_epilogue epi, const uint8_
       (qh ? !aligned(hq_packed, 16) || !aligned(hq_scales, 4) : !aligned(out, out_dtype == NVFP4MOE_F32 ? 4 : 2)))
     return fail(NVFP4MOE_ERR_INVALID_ARG,
                 "%s: a and the tiled weights must be 16-byte aligned, the output to its element", fn);
-  const size_t need = moe_grouped_gemm_mxfp4_workspace_size(rows, E, Nw, K);
+  const size_t need = mx_workspace_size(rows, E, Nw, K, bits);
   if (!ws || ws_bytes < need)
     return fail(NVFP4MOE_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, ws_bytes);
   if (!aligned(ws, 16)) return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: workspace must be 16-byte aligned", fn);
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const int max_mtiles = mx_max_mtiles(rows, E);
+  const int max_mtiles = mx_max_mtiles(rows, E, bits);
   const size_t arr = round_up((size_t)max_mtiles * 4);
   char* base = static_cast<char*>(ws);
   GemmArgs g{};
@@ -466,11 +474,11 @@ nvfp4moe_status mx_gemm_call(const char* fn, nvfp4moe_epilogue epi, const uint8_
   hipError_t err = hipSuccess;
   if (out_amax) err = launch_zero_f32(out_amax, 1, s);
   if (err != hipSuccess) return hip_status(err, fn);
-  const MtileSched sched{expert_offsets, active_experts, n_active, E, mx_rows_per_mtile(), max_mtiles,
+  const MtileSched sched{expert_offsets, active_experts, n_active, E, mx_rows_per_mtile(bits), max_mtiles,
                          const_cast<int*>(g.sched_e), const_cast<int*>(g.sched_r), const_cast<int*>(g.sched_n)};
   err = launch_mtile_schedule(sched, s);
   if (err != hipSuccess) return hip_status(err, fn);
-  return hip_status(launch_gemm_mx(g, max_mtiles, s), fn);
+  return hip_status(launch_gemm_mx(g, max_mtiles, bits, s), fn);
 }
 }  // namespace
 
@@ -481,7 +489,7 @@ nvfp4moe_status moe_grouped_gemm_mxfp4(nvfp4moe_epilogue epi, const uint8_t* a, 
                                        const int32_t* n_active, int32_t E, int32_t rows, int32_t Nw,
                                        int32_t K, void* out, nvfp4moe_dtype out_dtype, float* out_amax, void* ws,
                                        size_t ws_bytes, void* stream) {
-  return mx_gemm_call("moe_grouped_gemm_mxfp4", epi, a, a_scales, a_rows, gather_index, gather_div, w_packed,
+  return mx_gemm_call("moe_grouped_gemm_mxfp4", 4, epi, a, a_scales, a_rows, gather_index, gather_div, w_packed,
                       w_scales, expert_offsets, active_experts, n_active, E, rows, Nw, K, out, out_dtype, out_amax,
                       nullptr, nullptr, ws, ws_bytes, stream);
 }
@@ -494,7 +502,7 @@ nvfp4moe_status moe_grouped_gemm_mxfp4_swiglu_q(const uint8_t* a, const uint8_t*
                                                 int32_t K, uint8_t* h_packed, uint8_t* h_scales, void* ws,
                                                 size_t ws_bytes, void* stream) {
   if (!h_packed) return fail(NVFP4MOE_ERR_INVALID_ARG, "moe_grouped_gemm_mxfp4_swiglu_q: null tensor pointer");
-  return mx_gemm_call("moe_grouped_gemm_mxfp4_swiglu_q", NVFP4MOE_EPI_SWIGLU, a, a_scales, a_rows, gather_index,
+  return mx_gemm_call("moe_grouped_gemm_mxfp4_swiglu_q", 4, NVFP4MOE_EPI_SWIGLU, a, a_scales, a_rows, gather_index,
                       gather_div, w_packed, w_scales, expert_offsets, active_experts, n_active, E, rows, Nw, K,
                       nullptr, NVFP4MOE_F32, nullptr, h_packed, h_scales, ws, ws_bytes, stream);
 }
@@ -539,6 +547,59 @@ nvfp4moe_status act_fp8_e4m3_roundtrip(const void* x, int64_t n, void* out, void
     return fail(NVFP4MOE_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need,
                 ws_bytes);
   return hip_status(launch_fp8_roundtrip(x, n, out, ws, static_cast<hipStream_t>(stream)), fn);
+}
+
+// ------------------------------------------------------------------ MXFP8
+nvfp4moe_status mxfp8_quantize(const void* x, nvfp4moe_dtype x_dtype, int64_t R, int64_t C, uint8_t* codes,
+                               uint8_t* scales, void* stream) {
+  const char* fn = "mxfp8_quantize";
+  if (!x || !codes || !scales) return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: null tensor pointer", fn);
+  if (x_dtype != NVFP4MOE_F32 && x_dtype != NVFP4MOE_BF16)
+    return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: x_dtype must be F32 or BF16", fn);
+  if (R < 1 || C < 32 || C % 32 != 0)
+    return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: need R >= 1, C >= 32 and C %% 32 == 0 (R=%lld C=%lld)", fn,
+                (long long)R, (long long)C);
+  if ((double)R * (double)C > 4.0e12) return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: tensor too large", fn);
+  if (!aligned(x, 16) || !aligned(codes, 16))
+    return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: x and codes must be 16-byte aligned", fn);
+  return hip_status(launch_mx8_quantize(x, x_dtype == NVFP4MOE_BF16, R * C, codes, scales,
+                                        static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+size_t mxfp8_tiled_codes_bytes(int64_t R, int64_t C) {
+  if (R < 16 || R % 16 != 0 || C < 32 || C % 32 != 0) return 0;
+  return mx8_tiled_codes_bytes(R, C);
+}
+
+nvfp4moe_status mxfp8_weights_tile(const uint8_t* codes, const uint8_t* scales, int64_t B, int64_t R, int64_t C,
+                                   uint8_t* tiled_codes, uint8_t* tiled_scales, void* stream) {
+  const char* fn = "mxfp8_weights_tile";
+  if (!codes || !scales || !tiled_codes || !tiled_scales)
+    return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: null tensor pointer", fn);
+  if (B < 1 || B > 65535 || R < 16 || R % 16 != 0 || C < 32 || C % 32 != 0)
+    return fail(NVFP4MOE_ERR_INVALID_ARG,
+                "%s: need 1 <= B <= 65535, R >= 16, R %% 16 == 0, C >= 32, C %% 32 == 0 (B=%lld R=%lld C=%lld)",
+                fn, (long long)B, (long long)R, (long long)C);
+  if (B * R * C >= (int64_t(1) << 40) || R > (int64_t(1) << 30) || C > (int64_t(1) << 30))
+    return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: matrices too large", fn);
+  if (!aligned(codes, 16) || !aligned(tiled_codes, 16) || !aligned(tiled_scales, 16))
+    return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: codes and the tiled outputs must be 16-byte aligned", fn);
+  return hip_status(launch_mx8_weights_tile(codes, scales, B, R, C, tiled_codes, tiled_scales,
+                                            static_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+nvfp4moe_status moe_grouped_gemm_mxfp8(nvfp4moe_epilogue epi, const uint8_t* a, const uint8_t* a_scales,
+                                       int64_t a_rows, const int32_t* gather_index, int32_t gather_div,
+                                       const uint8_t* w_codes, const uint8_t* w_scales,
+                                       const int32_t* expert_offsets, const int32_t* active_experts,
+                                       const int32_t* n_active, int32_t E, int32_t rows, int32_t Nw,
+                                       int32_t K, void* out, nvfp4moe_dtype out_dtype, float* out_amax, void* ws,
+                                       size_t ws_bytes, void* stream) {
+  return mx_gemm_call("moe_grouped_gemm_mxfp8", 8, epi, a, a_scales, a_rows, gather_index, gather_div, w_codes,
+                      w_scales, expert_offsets, active_experts, n_active, E, rows, Nw, K, out, out_dtype, out_amax,
+                      nullptr, nullptr, ws, ws_bytes, stream);
 }
 
 }  // extern "C"

@@ -85,16 +85,24 @@ __device__ __forceinline__ uint32_t mx_key(float v) {
   return a <= 3.402823466e38f ? __float_as_uint(a) : 0xFFFFFFFFu;
 }
 // Scale byte of a group from its key (OCP MX v1.0 rule, group of 32): NaN/Inf -> 0xFF;
-// amax 0 -> 0; else e = max(floor(log2 amax) - 2, -127) (frexp gives floor(log2) exactly)
-// and byte e + 127. e is returned for mx_code (0 when unused).
-__device__ __forceinline__ uint32_t mx_scale(uint32_t key, int& e) {
+// amax 0 -> 0; else e = max(floor(log2 amax) - emax, -127) (frexp gives floor(log2) exactly;
+// emax is the element format's largest exponent: 2 for E2M1, 8 for E4M3) and byte e + 127.
+// e is returned for the element codes (0 when unused).
+__device__ __forceinline__ uint32_t mx_scale(uint32_t key, int& e, int emax = 2) {
   e = 0;
   if (key == 0xFFFFFFFFu) return 0xFFu;
   if (key == 0u) return 0u;
   int ex;
   (void)frexpf(__uint_as_float(key), &ex);   // amax = f * 2^ex, f in [0.5, 1)
-  e = max(ex - 1 - 2, -127);
+  e = max(ex - 1 - emax, -127);
   return (uint32_t)(e + 127);
+}
+// MXFP8 element code: E4M3_RNE(min(|v| * 2^-e, 448)) with the sign bit of v; 0 in a
+// non-finite group, +-0 in an all-zero group.
+__device__ __forceinline__ uint32_t mx8_code(float v, uint32_t key, int e) {
+  if (key == 0xFFFFFFFFu) return 0u;
+  const uint32_t sign = (__float_as_uint(v) >> 31) << 7;
+  return sign | (key != 0u ? e4m3_rne(fminf(ldexpf(fabsf(v), -e), 448.0f)) : 0u);
 }
 // Code (sign bit | E2M1 magnitude) of v in a group with the given key and exponent:
 // E2M1_RNE_saturating(|v| * 2^-e), a power-of-two scaling (exact); 0 in a non-finite group,

@@ -50,24 +50,52 @@ namespace nvfp4moe {
 namespace {
 
 constexpr int kMxWaves = 8;
-constexpr int kMxTBM = 8;                           // token blocks of 16 (m-tile of 128 rows)
 constexpr int kMxRBW = 2;                           // 16-row weight blocks per wave
 constexpr int kMxWin = 16;                          // chunks per scale tile (2048 k)
-constexpr int kMxTok = 80;                          // LDS bytes per token and chunk (64 + pad)
-constexpr int kMxCodes = 16 * kMxTBM * kMxTok;      // 10240
-constexpr int kMxSlot = kMxCodes + 16 * kMxTBM * 4; // + 4 scale bytes per token
 constexpr int kMxSlots = 3;                         // LDS ring slots
 constexpr int kMxDepth = 2;                         // weight chunks in flight
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 
-// FP4 x FP4 with one UE8M0 scale per lane for each operand; OA / OB select the scale byte
-// within the 32-bit scale registers.
-template <int OA, int OB>
-__device__ __forceinline__ f32x4 mfma_mx(u32x4 a, uint32_t sa, u32x4 b, uint32_t sb, f32x4 c) {
-  const v8i A = {(int)a[0], (int)a[1], (int)a[2], (int)a[3], 0, 0, 0, 0};
-  const v8i B = {(int)b[0], (int)b[1], (int)b[2], (int)b[3], 0, 0, 0, 0};
-  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, c, 4, 4, OA, (int)sa, OB, (int)sb);
+// Element formats of the MX blocks: FP4 (E2M1, MXFP4) and FP8 (E4M3, MXFP8). Per 128-wide
+// chunk a lane holds 32 elements of one row (LB bytes: one MFMA operand); lane group g
+// (lanes 16 g .. 16 g + 15) supplies the scale of k block g (k = 32 g .. 32 g + 31). With FP4
+// a lane's 32 elements are that block; with FP8 (probed on the GPU) its bytes 0-15 are
+// k = 16 g .. +15 and bytes 16-31 are k = 64 + 16 g .. +15; an m-tile has TBM
+// token blocks of 16 rows (FP8: 4, so that two fragment sets fit the registers); TOK = LDS
+// bytes per token and chunk (row bytes + 16 of padding: the 16 lanes of a fragment read hit
+// distinct banks); FMT = the MFMA operand format code.
+template <int BITS>
+struct MxFmt;
+// piece(g, h) = offset in a token's chunk row of the h-th 16 bytes of lane group g's operand.
+template <>
+struct MxFmt<4> {
+  static constexpr int LB = 16, TBM = 8, TOK = 80, FMT = 4;
+  static constexpr int piece(int g, int h) { return 16 * g + 16 * h; }
+};
+template <>
+struct MxFmt<8> {
+  static constexpr int LB = 32, TBM = 4, TOK = 144, FMT = 0;
+  static constexpr int piece(int g, int h) { return 16 * g + 64 * h; }
+};
+
+// One MX operand fragment: LB bytes per lane.
+template <int BITS>
+using MxFrag = uint32_t __attribute__((ext_vector_type(MxFmt<BITS>::LB / 4)));
+
+// A x B with one UE8M0 scale per lane for each operand; OA / OB select the scale byte within
+// the 32-bit scale registers.
+template <int BITS, int OA, int OB>
+__device__ __forceinline__ f32x4 mfma_mx(const MxFrag<BITS>& a, uint32_t sa, const MxFrag<BITS>& b, uint32_t sb,
+                                         f32x4 c) {
+  v8i A = {0, 0, 0, 0, 0, 0, 0, 0}, B = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+  for (int i = 0; i < MxFmt<BITS>::LB / 4; ++i) {
+    A[i] = (int)a[i];
+    B[i] = (int)b[i];
+  }
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(A, B, c, MxFmt<BITS>::FMT, MxFmt<BITS>::FMT, OA,
+                                                          (int)sa, OB, (int)sb);
 }
 
 // Bytes sh .. sh+15 of the 32-byte concatenation lo | hi (sh = 0..15, wave-uniform).
@@ -107,17 +135,24 @@ __device__ __forceinline__ void static_for(F&& f) {
   static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 
-template <bool SWIGLU, bool QH>
+template <int BITS, bool SWIGLU, bool QH>
 __global__ __launch_bounds__(kMxWaves* kWave) void gemm_mx_kernel(const GemmArgs p, int ntiles_n) {
-  static_assert(!QH || SWIGLU, "h is quantized in the SwiGLU epilogue");
+  using Fmt = MxFmt<BITS>;
+  using Frag = MxFrag<BITS>;
+  constexpr int TBM = Fmt::TBM, LB = Fmt::LB, TOK = Fmt::TOK;
+  constexpr int ROWB = 4 * LB;                        // bytes of one token row per chunk
+  constexpr int PPT = ROWB / 16;                      // 16-byte staging pieces per token row
+  constexpr int CODES = 16 * TBM * TOK;
+  constexpr int SLOT = CODES + 16 * TBM * 4;          // + 4 scale bytes per token
+  constexpr int TILE = 16 * ROWB;                     // weight code tile (16 rows, one chunk)
+  static_assert(!QH || (SWIGLU && BITS == 4), "h is quantized (MXFP4) in the SwiGLU epilogue");
   constexpr int NT = kMxWaves * kWave;
-  static_assert(NT == 16 * kMxTBM * 4, "one thread per token and 32-wide k block of a chunk");
-  __shared__ __attribute__((aligned(16))) unsigned char smem[kMxSlots * kMxSlot];
+  static_assert(NT == 16 * TBM * PPT, "one thread per 16-byte piece of a chunk");
+  __shared__ __attribute__((aligned(16))) unsigned char smem[kMxSlots * SLOT];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g = lane >> 4;
-  // Tiles (m-tile, row tile) of the listed m-tiles, 8 equal ranges, one per XCD.
   // Tiles (K slice, m-tile, row tile) of the listed m-tiles, slice-major, 8 equal ranges,
   // one per XCD.
   const int per_split = ld_const(p.sched_n, 0) * ntiles_n;
@@ -131,10 +166,10 @@ __global__ __launch_bounds__(kMxWaves* kWave) void gemm_mx_kernel(const GemmArgs
   const int r0 = ld_const(p.expert_offsets, e);
   const int M = ld_const(p.expert_offsets, e + 1) - r0;
   const int K = p.K, Nw = p.Nw, F = Nw >> 1;
-  const int Kh = K >> 1, Ks = K >> 5;
+  const int Kb = K / (8 / BITS), Ks = K >> 5;   // row bytes of codes and of scales
   const int nch = (K + kChunk - 1) / kChunk;
   const int nwin = (nch + kMxWin - 1) / kMxWin;
-  const int ntb = __builtin_amdgcn_readfirstlane(min(kMxTBM, (M - tc + 15) >> 4));
+  const int ntb = __builtin_amdgcn_readfirstlane(min(TBM, (M - tc + 15) >> 4));
   // K slice ks: chunks [clo, chi); its first chunk is chunk u0 of scale window w0
   const int cps = (nch + p.ksplit - 1) / p.ksplit;
   const int clo = ks * cps, chi = min(nch, clo + cps);
@@ -145,47 +180,56 @@ __global__ __launch_bounds__(kMxWaves* kWave) void gemm_mx_kernel(const GemmArgs
     if (SWIGLU) return (b == 0 ? 0 : F) + (nb * kMxWaves + wave) * 16;
     return (nb * kMxWaves + wave) * 16 * kMxRBW + 16 * b;
   };
-  const uint32_t wbytes = (uint32_t)(Nw / 16) * (uint32_t)nch * 1024u;
+  const uint32_t wbytes = (uint32_t)(Nw / 16) * (uint32_t)nch * (uint32_t)TILE;
   const uint32_t sbytes = (uint32_t)(Nw / 16) * (uint32_t)nwin * 1024u;
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(p.w_packed + (size_t)e * wbytes, wbytes);
   const __amdgpu_buffer_rsrc_t sr = make_rsrc(p.w_scales + (size_t)e * sbytes, sbytes);
-  const uint32_t wlane = (uint32_t)(blkrow(0) / 16) * (uint32_t)nch * 1024u + 16u * lane;
+  const uint32_t wlane = (uint32_t)(blkrow(0) / 16) * (uint32_t)nch * (uint32_t)TILE + (uint32_t)LB * lane;
   const uint32_t slane = (uint32_t)(blkrow(0) / 16) * (uint32_t)nwin * 1024u + 16u * lane;
   uint32_t wsoff[kMxRBW], ssoff[kMxRBW];
 #pragma unroll
   for (int b = 0; b < kMxRBW; ++b) {
-    wsoff[b] = __builtin_amdgcn_readfirstlane((uint32_t)((blkrow(b) - blkrow(0)) / 16) * (uint32_t)nch * 1024u);
+    wsoff[b] = __builtin_amdgcn_readfirstlane((uint32_t)((blkrow(b) - blkrow(0)) / 16) * (uint32_t)nch * (uint32_t)TILE);
     ssoff[b] = __builtin_amdgcn_readfirstlane((uint32_t)((blkrow(b) - blkrow(0)) / 16) * (uint32_t)nwin * 1024u);
   }
 
-  // Staging role: token tk of the m-tile, 32-wide k block q of each chunk.
-  const __amdgpu_buffer_rsrc_t ar = make_rsrc(p.a_packed, (uint32_t)p.a_rows * (uint32_t)Kh);
+  // Staging role: token tk of the m-tile, 16-byte piece q of its row in each chunk (32-wide k
+  // block kb; with FP8 two pieces share a k block and write the same scale byte).
+  const __amdgpu_buffer_rsrc_t ar = make_rsrc(p.a_packed, (uint32_t)p.a_rows * (uint32_t)Kb);
   const __amdgpu_buffer_rsrc_t asr = make_rsrc(p.a_scales, (uint32_t)p.a_rows * (uint32_t)Ks);
-  const int tk = tid >> 2, q = tid & 3;
+  const int tk = tid / PPT, q = tid % PPT, kb = q / (PPT / 4);
   const bool tok_ok = tc + tk < M;
   const uint32_t arow = tok_ok ? (uint32_t)(p.gather_index ? p.gather_index[r0 + tc + tk] / p.gather_div
                                                            : r0 + tc + tk)
                                : 0u;
-  const uint32_t csrc = tok_ok ? arow * (uint32_t)Kh + 16u * q : kOOB;
-  const uint32_t ssrc = tok_ok ? arow * (uint32_t)Ks + q : kOOB;
-  const uint32_t cdst = tk * kMxTok + 16 * q, sdst = kMxCodes + q * 128 + (tk & 15) * 8 + (tk >> 4);
+  const uint32_t csrc = tok_ok ? arow * (uint32_t)Kb + 16u * q : kOOB;
+  const uint32_t ssrc = tok_ok ? arow * (uint32_t)Ks + kb : kOOB;
+  const uint32_t cdst = tk * TOK + 16 * q, sdst = CODES + kb * (16 * TBM) + (tk & 15) * TBM + (tk >> 4);
 
   u32x4 bst[4];   // staging sets: chunk clo + j in set j & 3 (requested two steps before its commit)
   uint32_t bsc[4];
   auto b_issue = [&](int set, int c) {   // k blocks past K (or the slice) read zero codes and scale 0
-    const bool in = c < chi && 128 * c + 32 * q < K;
-    bst[set] = ld128(ar, in ? csrc + 64u * c : kOOB, 0);
+    const bool in = c < chi && 128 * c + 32 * kb < K;
+    bst[set] = ld128(ar, in ? csrc + (uint32_t)ROWB * c : kOOB, 0);
     bsc[set] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(asr, in ? ssrc + 4u * c : kOOB, 0, 0);
   };
   auto b_commit = [&](int set, int slot) {
-    unsigned char* base = smem + slot * kMxSlot;
+    unsigned char* base = smem + slot * SLOT;
     *reinterpret_cast<u32x4*>(base + cdst) = bst[set];
     base[sdst] = (unsigned char)bsc[set];
   };
-  u32x4 wring[kMxDepth][kMxRBW];
+  Frag wring[kMxDepth][kMxRBW];
   auto w_issue = [&](int d, int c) {     // codes past K are zero in the tiles
 #pragma unroll
-    for (int b = 0; b < kMxRBW; ++b) wring[d][b] = ld128(wr, c < chi ? wlane + (uint32_t)c * 1024u : kOOB, wsoff[b]);
+    for (int b = 0; b < kMxRBW; ++b) {
+      const uint32_t off = c < chi ? wlane + (uint32_t)c * (uint32_t)TILE : kOOB;
+#pragma unroll
+      for (int h = 0; h < LB / 16; ++h) {
+        const u32x4 v = ld128(wr, off == kOOB ? kOOB : off + 16u * h, wsoff[b]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wring[d][b][4 * h + i] = v[i];
+      }
+    }
   };
   // Scale windows: sa = window w0 + i, sb = w0 + i + 1 while chunks clo + 16 i .. + 15 run;
   // sn = w0 + i + 2 in flight.
@@ -195,11 +239,11 @@ __global__ __launch_bounds__(kMxWaves* kWave) void gemm_mx_kernel(const GemmArgs
     for (int b = 0; b < kMxRBW; ++b) dst[b] = ld128(sr, w < nwin ? slane + (uint32_t)w * 1024u : kOOB, ssoff[b]);
   };
 
-  f32x4 acc[kMxRBW][kMxTBM];
+  f32x4 acc[kMxRBW][TBM];
 #pragma unroll
   for (int b = 0; b < kMxRBW; ++b)
 #pragma unroll
-    for (int tb = 0; tb < kMxTBM; ++tb) acc[b][tb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+    for (int tb = 0; tb < TBM; ++tb) acc[b][tb] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
   // prologue: scale windows w0 and w0 + 1, weights of the slice's first kMxDepth chunks,
   // activations of its first two chunks committed to slots 0 and 1, the third and fourth
@@ -225,15 +269,27 @@ __global__ __launch_bounds__(kMxWaves* kWave) void gemm_mx_kernel(const GemmArgs
   // past the slice are skipped.
   auto body = [&](auto ntb_tag) {
     constexpr int NTB = decltype(ntb_tag)::value;
-    u32x4 bcur[NTB], bnext[NTB];
+    Frag bcur[NTB], bnext[NTB];
     uint32_t scb[2], scbn[2];
-    auto b_read = [&](u32x4 (&bb)[NTB], uint32_t (&sc)[2], int slot) {
-      const unsigned char* base = smem + slot * kMxSlot;
+    auto b_read = [&](Frag (&bb)[NTB], uint32_t (&sc)[2], int slot) {
+      const unsigned char* base = smem + slot * SLOT;
 #pragma unroll
-      for (int tb = 0; tb < NTB; ++tb) bb[tb] = *reinterpret_cast<const u32x4*>(base + (16 * tb + l16) * kMxTok + 16 * g);
-      const uint2 sv = *reinterpret_cast<const uint2*>(base + kMxCodes + g * 128 + l16 * 8);
-      sc[0] = sv.x;
-      sc[1] = sv.y;
+      for (int tb = 0; tb < NTB; ++tb) {
+#pragma unroll
+        for (int h = 0; h < LB / 16; ++h) {   // 16-byte reads: rows are 16-byte aligned
+          const u32x4 v = *reinterpret_cast<const u32x4*>(base + (16 * tb + l16) * TOK + Fmt::piece(g, h));
+#pragma unroll
+          for (int i = 0; i < 4; ++i) bb[tb][4 * h + i] = v[i];
+        }
+      }
+      if constexpr (TBM == 8) {
+        const uint2 sv = *reinterpret_cast<const uint2*>(base + CODES + g * (16 * TBM) + l16 * TBM);
+        sc[0] = sv.x;
+        sc[1] = sv.y;
+      } else {
+        sc[0] = *reinterpret_cast<const uint32_t*>(base + CODES + g * (16 * TBM) + l16 * TBM);
+        sc[1] = 0u;
+      }
     };
     b_read(bcur, scb, 0);
     int slot = 0;   // c % 3
@@ -249,7 +305,7 @@ __global__ __launch_bounds__(kMxWaves* kWave) void gemm_mx_kernel(const GemmArgs
         const int slot1 = slot == kMxSlots - 1 ? 0 : slot + 1;
         const int slot2 = slot1 == kMxSlots - 1 ? 0 : slot1 + 1;
         b_issue(u & 3, c + 4);
-        u32x4 wa[kMxRBW];
+        Frag wa[kMxRBW];
 #pragma unroll
         for (int b = 0; b < kMxRBW; ++b) wa[b] = wring[d][b];
         w_issue(d, c + kMxDepth);   // this ring entry is free again
@@ -259,7 +315,7 @@ __global__ __launch_bounds__(kMxWaves* kWave) void gemm_mx_kernel(const GemmArgs
             constexpr int tb = decltype(tb_tag)::value;
 #pragma unroll
             for (int b = 0; b < kMxRBW; ++b)
-              acc[b][tb] = mfma_mx<(u & 3), (tb & 3)>(wa[b], scs[b][u >> 2], bcur[tb], scb[tb >> 2], acc[b][tb]);
+              acc[b][tb] = mfma_mx<BITS, (u & 3), (tb & 3)>(wa[b], scs[b][u >> 2], bcur[tb], scb[tb >> 2], acc[b][tb]);
           });
         }
         b_commit((u + 2) & 3, slot2);
@@ -279,21 +335,27 @@ __global__ __launch_bounds__(kMxWaves* kWave) void gemm_mx_kernel(const GemmArgs
       });
     }
   };
-  if (ntb > 4) body(Int<8>{});
-  else if (ntb > 2) body(Int<4>{});
-  else if (ntb > 1) body(Int<2>{});
-  else body(Int<1>{});
+  if constexpr (TBM == 8) {
+    if (ntb > 4) body(Int<8>{});
+    else if (ntb > 2) body(Int<4>{});
+    else if (ntb > 1) body(Int<2>{});
+    else body(Int<1>{});
+  } else {
+    if (ntb > 2) body(Int<4>{});
+    else if (ntb > 1) body(Int<2>{});
+    else body(Int<1>{});
+  }
 
   if constexpr (QH) {   // MXFP4 h: rows of the m-tile, the wave's 16 h columns
     __syncthreads();     // every wave is past its last ring read
-    uint32_t* xch = reinterpret_cast<uint32_t*>(smem);       // [kMxWaves][kMxTBM][16] amax keys
+    uint32_t* xch = reinterpret_cast<uint32_t*>(smem);       // [kMxWaves][TBM][16] amax keys
     unsigned char* qc = smem + 4096;                          // [128 rows][64 B] codes of the tile
-    unsigned char* qs = qc + 16 * kMxTBM * 64;                // [128 rows][4] scale bytes
+    unsigned char* qs = qc + 16 * TBM * 64;                // [128 rows][4] scale bytes
     const int F2 = F >> 1, F32 = F >> 5;
-    float h[kMxTBM][4];
-    uint32_t key[kMxTBM];
+    float h[TBM][4];
+    uint32_t key[TBM];
 #pragma unroll
-    for (int tb = 0; tb < kMxTBM; ++tb) {
+    for (int tb = 0; tb < TBM; ++tb) {
       key[tb] = 0u;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -302,12 +364,12 @@ __global__ __launch_bounds__(kMxWaves* kWave) void gemm_mx_kernel(const GemmArgs
       }
       key[tb] = max(key[tb], (uint32_t)__shfl_xor((int)key[tb], 16, kWave));
       key[tb] = max(key[tb], (uint32_t)__shfl_xor((int)key[tb], 32, kWave));
-      if (g == 0) xch[(wave * kMxTBM + tb) * 16 + l16] = key[tb];
+      if (g == 0) xch[(wave * TBM + tb) * 16 + l16] = key[tb];
     }
     __syncthreads();
 #pragma unroll
-    for (int tb = 0; tb < kMxTBM; ++tb) {
-      const uint32_t gk = max(key[tb], xch[((wave ^ 1) * kMxTBM + tb) * 16 + l16]);
+    for (int tb = 0; tb < TBM; ++tb) {
+      const uint32_t gk = max(key[tb], xch[((wave ^ 1) * TBM + tb) * 16 + l16]);
       int ex = 0;
       const uint32_t sc = mx_scale(gk, ex);
       uint32_t q = 0;
@@ -335,7 +397,7 @@ __global__ __launch_bounds__(kMxWaves* kWave) void gemm_mx_kernel(const GemmArgs
   if (p.ksplit > 1) {   // raw partial sums; the split-K reduce applies the epilogue
     float* part = p.partial + (size_t)ks * p.rows * Nw;
 #pragma unroll
-    for (int tb = 0; tb < kMxTBM; ++tb) {
+    for (int tb = 0; tb < TBM; ++tb) {
       const int t = tc + 16 * tb + l16;
       if (tb < ntb && t < M) {
 #pragma unroll
@@ -346,13 +408,13 @@ __global__ __launch_bounds__(kMxWaves* kWave) void gemm_mx_kernel(const GemmArgs
     }
     return;
   }
-  const uint32_t amax_bits = store_tile<kMxRBW, kMxTBM, SWIGLU>(p, acc, tc, ntb, M, r0, 1.0f, false, blkrow, lane, 0u);
+  const uint32_t amax_bits = store_tile<kMxRBW, TBM, SWIGLU>(p, acc, tc, ntb, M, r0, 1.0f, false, blkrow, lane, 0u);
   merge_amax(p.out_amax, amax_bits, lane);
 }
 
 }  // namespace
 
-int mx_rows_per_mtile() { return 16 * kMxTBM; }
+int mx_rows_per_mtile(int bits) { return bits == 8 ? 16 * MxFmt<8>::TBM : 16 * MxFmt<4>::TBM; }
 bool mx_supports(int Nw) { return Nw % (16 * kMxRBW * kMxWaves) == 0; }
 
 // K slices when the m-tile x row-tile grid is under one workgroup per CU: about 256
@@ -369,13 +431,20 @@ int mx_ksplit(int max_mtiles, int Nw, int K) {
   return (nch + cps - 1) / cps;
 }
 
-hipError_t launch_gemm_mx(const GemmArgs& a, int max_mtiles, hipStream_t stream) {
+hipError_t launch_gemm_mx(const GemmArgs& a, int max_mtiles, int bits, hipStream_t stream) {
   const int ntiles_n = a.Nw / (16 * kMxRBW * kMxWaves);
   const int total = max_mtiles * ntiles_n * a.ksplit;   // bound on the tiles
   const unsigned grid = (unsigned)((total + 7) / 8 * 8);
-  if (a.hq_packed) gemm_mx_kernel<true, true><<<grid, kMxWaves * kWave, 0, stream>>>(a, ntiles_n);
-  else if (a.swiglu) gemm_mx_kernel<true, false><<<grid, kMxWaves * kWave, 0, stream>>>(a, ntiles_n);
-  else gemm_mx_kernel<false, false><<<grid, kMxWaves * kWave, 0, stream>>>(a, ntiles_n);
+  if (bits == 8) {
+    if (a.swiglu) gemm_mx_kernel<8, true, false><<<grid, kMxWaves * kWave, 0, stream>>>(a, ntiles_n);
+    else gemm_mx_kernel<8, false, false><<<grid, kMxWaves * kWave, 0, stream>>>(a, ntiles_n);
+  } else if (a.hq_packed) {
+    gemm_mx_kernel<4, true, true><<<grid, kMxWaves * kWave, 0, stream>>>(a, ntiles_n);
+  } else if (a.swiglu) {
+    gemm_mx_kernel<4, true, false><<<grid, kMxWaves * kWave, 0, stream>>>(a, ntiles_n);
+  } else {
+    gemm_mx_kernel<4, false, false><<<grid, kMxWaves * kWave, 0, stream>>>(a, ntiles_n);
+  }
   if (a.ksplit <= 1) return hipGetLastError();
   const hipError_t e2 = hipGetLastError();
   if (e2 != hipSuccess) return e2;

@@ -96,6 +96,13 @@ hipError_t launch_weights_tile(const uint8_t* packed, const uint8_t* scales, int
 size_t mx_tiled_scales_bytes(int64_t R, int64_t C);
 hipError_t launch_mx_weights_tile(const uint8_t* packed, const uint8_t* scales, int64_t B, int64_t R, int64_t C,
                                   uint8_t* tiled_codes, uint8_t* tiled_scales, hipStream_t stream);
+// MXFP8 (quantize.hip, weights_tile.hip): n elements (n % 32 == 0) -> E4M3 codes [n] + UE8M0
+// scales [n/32]; code tiles of 2 KB per (16-row block, chunk), the mx scale tiles.
+hipError_t launch_mx8_quantize(const void* x, bool x_bf16, int64_t n, uint8_t* codes, uint8_t* scales,
+                               hipStream_t stream);
+size_t mx8_tiled_codes_bytes(int64_t R, int64_t C);
+hipError_t launch_mx8_weights_tile(const uint8_t* codes, const uint8_t* scales, int64_t B, int64_t R, int64_t C,
+                                   uint8_t* tiled_codes, uint8_t* tiled_scales, hipStream_t stream);
 // MXFP4 quantizer (quantize.hip): n elements (n % 32 == 0) -> packed [n/2] + UE8M0 scales [n/32].
 hipError_t launch_mx_quantize(const void* x, bool x_bf16, int64_t n, uint8_t* packed, uint8_t* scales,
                               hipStream_t stream);
@@ -111,9 +118,9 @@ int large_waves(int rows, int E, int Nw);
 // MXFP4 W4A4 GEMM on the scaled FP4 MFMA (gemm_mx.hip): m-tile rows, supported Nw, launcher
 // (a.w_packed / a.w_scales: MX tiles; a.a_packed / a.a_scales: row-major MXFP4; the m-tile
 // list in a.sched_*).
-int mx_rows_per_mtile();
+int mx_rows_per_mtile(int bits);   // MX element bits: 4 (MXFP4) or 8 (MXFP8)
 bool mx_supports(int Nw);
-hipError_t launch_gemm_mx(const GemmArgs& a, int max_mtiles, hipStream_t stream);
+hipError_t launch_gemm_mx(const GemmArgs& a, int max_mtiles, int bits, hipStream_t stream);
 // K slices of the MXFP4 GEMM from the sizes alone (1 unless the grid is under one workgroup per CU).
 int mx_ksplit(int max_mtiles, int Nw, int K);
 hipError_t launch_zero_f32(float* p, int n, hipStream_t stream);

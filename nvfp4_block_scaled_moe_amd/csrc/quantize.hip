@@ -235,6 +235,34 @@ __global__ __launch_bounds__(kQuantThreads) void mx_quantize_kernel(const T* __r
   scales[u] = (uint8_t)s;
 }
 
+// MXFP8 (E4M3 elements, one UE8M0 scale per 32; the block-scaled FP8 of the dense layers on
+// "Native FP4 Is Slower Than Emulated FP4", sections 1-2, read with the OCP MX v1.0 rule):
+// one thread per 32 consecutive elements of a row: e = max(floor(log2 amax) - 8, -127), scale
+// byte e + 127, codes E4M3_RNE(min(|w| * 2^-e, 448)) with the sign of w; NaN/Inf groups get
+// scale 0xFF and codes 0, all-zero groups scale 0 and codes +-0.
+template <typename T>
+__global__ __launch_bounds__(kQuantThreads) void mx8_quantize_kernel(const T* __restrict__ x, int64_t total_units,
+                                                                     uint8_t* __restrict__ codes,
+                                                                     uint8_t* __restrict__ scales) {
+  const int64_t u = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x;
+  if (u >= total_units) return;
+  const int64_t e0 = u * 32;
+  float v[32];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) Vec8<T>::load(x + e0 + 8 * q, v + 8 * q);
+  uint32_t key = 0u;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) key = max(key, mx_key(v[i]));
+  int e = 0;
+  const uint32_t s = mx_scale(key, e, 8);
+  uint32_t w[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int i = 0; i < 32; ++i) w[i >> 2] |= mx8_code(v[i], key, e) << (8 * (i & 3));
+  *reinterpret_cast<uint4*>(codes + e0) = make_uint4(w[0], w[1], w[2], w[3]);
+  *reinterpret_cast<uint4*>(codes + e0 + 16) = make_uint4(w[4], w[5], w[6], w[7]);
+  scales[u] = (uint8_t)s;
+}
+
 // Workgroups per matrix for the amax pass: about 8 vectors per thread, at most 2048 (8 per
 // CU), so that large activations keep enough loads in flight.
 inline int amax_blocks(int64_t n) {
@@ -275,6 +303,19 @@ hipError_t launch_quantize(const void* x, bool x_bf16, int64_t B, int64_t R, int
   else
     quantize_kernel<float><<<(unsigned)blocks, kQuantThreads, 0, stream>>>(
         static_cast<const float*>(x), n, units, g_out, packed, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_mx8_quantize(const void* x, bool x_bf16, int64_t n, uint8_t* codes, uint8_t* scales,
+                               hipStream_t stream) {
+  const int64_t units = n / 32;
+  const unsigned blocks = (unsigned)((units + kQuantThreads - 1) / kQuantThreads);
+  if (x_bf16)
+    mx8_quantize_kernel<uint16_t><<<blocks, kQuantThreads, 0, stream>>>(static_cast<const uint16_t*>(x), units,
+                                                                         codes, scales);
+  else
+    mx8_quantize_kernel<float><<<blocks, kQuantThreads, 0, stream>>>(static_cast<const float*>(x), units, codes,
+                                                                      scales);
   return hipGetLastError();
 }
 

@@ -20,6 +20,12 @@
 //           (zero where k >= C): exactly the scale operand of lane l of the scaled FP4 MFMA
 //           for chunk 16 w + u.
 //
+// MXFP8 weights (one E4M3 code per byte) use code tiles of 2048 bytes per (matrix b, row
+// block rb, chunk c) at ((b * R/16 + rb) * ceil(C/128) + c) * 2048; lane l's 32 bytes at
+// 32 l hold codes k = 128 c + 16 g .. +15 and then k = 128 c + 64 + 16 g .. +15 of row
+// 16 rb + r (the FP8 operand of lane l of the scaled MFMA, whose lane group g holds those two
+// 16-element pieces), and the mx scale tiles above.
+//
 // The reordering is a pure permutation plus zero padding; codes and scales are copied bit
 // for bit.
 #include "common.h"
@@ -45,6 +51,24 @@ __global__ __launch_bounds__(kTileThreads) void tile_codes_kernel(const uint8_t*
   const int k0 = 128 * c + 32 * (lane >> 4);
   uint4 v = make_uint4(0u, 0u, 0u, 0u);
   if (k0 < C) v = *reinterpret_cast<const uint4*>(packed + row * (int64_t)(C / 2) + k0 / 2);
+  *reinterpret_cast<uint4*>(out + i * 16) = v;
+}
+
+__global__ __launch_bounds__(kTileThreads) void tile_codes8_kernel(const uint8_t* __restrict__ codes,
+                                                                   int64_t n_slots, int R, int C,
+                                                                   uint8_t* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * kTileThreads + threadIdx.x;   // 16-byte slot
+  if (i >= n_slots) return;
+  const int nch = (C + 127) / 128;
+  const int half = (int)(i & 1);
+  const int lane = (int)((i >> 1) & 63);
+  const int64_t tile = i >> 7;
+  const int c = (int)(tile % nch);
+  const int64_t rbm = tile / nch;
+  const int64_t row = rbm * 16 + (lane & 15);
+  const int k0 = 128 * c + 16 * (lane >> 4) + 64 * half;
+  uint4 v = make_uint4(0u, 0u, 0u, 0u);
+  if (k0 < C) v = *reinterpret_cast<const uint4*>(codes + row * (int64_t)C + k0);   // C % 16 == 0
   *reinterpret_cast<uint4*>(out + i * 16) = v;
 }
 
@@ -103,6 +127,21 @@ hipError_t launch_mx_weights_tile(const uint8_t* packed, const uint8_t* scales, 
   const int64_t scale_slots = B * (int64_t)(mx_tiled_scales_bytes(R, C) / 16);
   tile_codes_kernel<<<(unsigned)((codes_slots + kTileThreads - 1) / kTileThreads), kTileThreads, 0, stream>>>(
       packed, codes_slots, (int)R, (int)C, tiled_codes);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  tile_mx_scales_kernel<<<(unsigned)((scale_slots + kTileThreads - 1) / kTileThreads), kTileThreads, 0, stream>>>(
+      scales, scale_slots, (int)R, (int)C, tiled_scales);
+  return hipGetLastError();
+}
+
+size_t mx8_tiled_codes_bytes(int64_t R, int64_t C) { return (size_t)(R / 16) * (size_t)((C + 127) / 128) * 2048; }
+
+hipError_t launch_mx8_weights_tile(const uint8_t* codes, const uint8_t* scales, int64_t B, int64_t R, int64_t C,
+                                   uint8_t* tiled_codes, uint8_t* tiled_scales, hipStream_t stream) {
+  const int64_t codes_slots = B * (int64_t)(mx8_tiled_codes_bytes(R, C) / 16);
+  const int64_t scale_slots = B * (int64_t)(mx_tiled_scales_bytes(R, C) / 16);
+  tile_codes8_kernel<<<(unsigned)((codes_slots + kTileThreads - 1) / kTileThreads), kTileThreads, 0, stream>>>(
+      codes, codes_slots, (int)R, (int)C, tiled_codes);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   tile_mx_scales_kernel<<<(unsigned)((scale_slots + kTileThreads - 1) / kTileThreads), kTileThreads, 0, stream>>>(

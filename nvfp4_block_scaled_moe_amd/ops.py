@@ -290,5 +290,64 @@ def moe_grouped_gemm_mxfp4_swiglu_q(a: torch.Tensor, a_scales: torch.Tensor, w: 
     return hp, hs
 
 
+def mxfp8_quantize(x: torch.Tensor):
+    """Float rows [..., C] (C % 32 == 0) -> MXFP8 (E4M3 codes uint8 [..., C], UE8M0 scales
+    uint8 [..., C/32]); one scale per 32 elements, no per-tensor scale."""
+    _dev(x)
+    x = x.contiguous()
+    C = x.shape[-1]
+    R = x.numel() // C
+    codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    scales = torch.empty(x.shape[:-1] + (C // 32,), dtype=torch.uint8, device=x.device)
+    st = _lib.load().mxfp8_quantize(_ptr(x), _DT[x.dtype], R, C, _ptr(codes), _ptr(scales), _stream())
+    _lib.check("mxfp8_quantize", st)
+    return codes, scales
+
+
+def mxfp8_weights_tile(codes: torch.Tensor, scales: torch.Tensor) -> MxTiledWeights:
+    """Reorder MXFP8 weights codes [B, R, C] + scales [B, R, C/32] (or one matrix) into the
+    tiled storage moe_grouped_gemm_mxfp8 reads (include/nvfp4moe.h)."""
+    _dev(codes, scales)
+    c3 = (codes.unsqueeze(0) if codes.dim() == 2 else codes).contiguous()
+    s3 = (scales.unsqueeze(0) if scales.dim() == 2 else scales).contiguous()
+    B, R, C = c3.shape
+    assert s3.shape == (B, R, C // 32), (s3.shape, c3.shape)
+    lib = _lib.load()
+    cb, sb = lib.mxfp8_tiled_codes_bytes(R, C), lib.mxfp4_tiled_scales_bytes(R, C)
+    if cb == 0 or sb == 0:
+        raise _lib.NVFP4MoEError("mxfp8_weights_tile", _lib.ERR_INVALID_ARG, f"unsupported shape R={R} C={C}")
+    tc = torch.empty((B, cb), dtype=torch.uint8, device=codes.device)
+    ts = torch.empty((B, sb), dtype=torch.uint8, device=codes.device)
+    st = lib.mxfp8_weights_tile(_ptr(c3), _ptr(s3), B, R, C, _ptr(tc), _ptr(ts), _stream())
+    _lib.check("mxfp8_weights_tile", st)
+    return MxTiledWeights(tc, ts, R, C)
+
+
+def moe_grouped_gemm_mxfp8(epi: int, a: torch.Tensor, a_scales: torch.Tensor, w: MxTiledWeights,
+                           expert_offsets: torch.Tensor, active_experts: torch.Tensor,
+                           n_active: torch.Tensor, *, gather_index: torch.Tensor | None = None,
+                           gather_div: int = 1, rows: int | None = None, out_dtype=torch.bfloat16,
+                           want_amax: bool = False, out: torch.Tensor | None = None):
+    """W8A8 grouped GEMM with MXFP8 weights ``w`` (E matrices [Nw, K], tiled) and MXFP8
+    activations ``a`` [a_rows, K] + ``a_scales`` [a_rows, K/32] (+ SwiGLU)."""
+    _dev(a, a_scales, w.codes, w.scales, expert_offsets, active_experts, n_active, gather_index)
+    E, Nw, K = w.B, w.R, w.C
+    a_rows = a.shape[0]
+    if rows is None:
+        rows = gather_index.numel() if gather_index is not None else a_rows
+    ncol = Nw // 2 if epi == EPI_SWIGLU else Nw
+    if out is None:
+        out = torch.empty((rows, ncol), dtype=out_dtype, device=a.device)
+    amax = torch.empty((1,), dtype=torch.float32, device=a.device) if want_amax else None
+    lib = _lib.load()
+    ws = _ws(lib.moe_grouped_gemm_mxfp8_workspace_size(rows, E, Nw, K), a.device)
+    st = lib.moe_grouped_gemm_mxfp8(
+        epi, _ptr(a), _ptr(a_scales), a_rows, _ptr(gather_index), int(gather_div), _ptr(w.codes),
+        _ptr(w.scales), _ptr(expert_offsets), _ptr(active_experts), _ptr(n_active), E, rows, Nw, K,
+        _ptr(out), _DT[out.dtype], _ptr(amax), _ptr(ws), ws.numel(), _stream())
+    _lib.check("moe_grouped_gemm_mxfp8", st)
+    return (out, amax) if want_amax else out
+
+
 def last_dispatch() -> int:
     return _lib.load().nvfp4moe_last_dispatch()

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(_lib.SIGNATURES), "binding signatures out of sync with the header"
     for n in names:
         assert hasattr(lib, n)
-    assert lib.nvfp4moe_abi_version() == 203
+    assert lib.nvfp4moe_abi_version() == 204
 
 
 FAKE = ctypes.c_void_p(1 << 20)      # aligned, never dereferenced: validation fails first
@@ -81,6 +81,30 @@ def test_mxfp4_swiglu_q_argument_checks():
     assert st == _lib.ERR_UNSUPPORTED
     st, _ = _err(call(ws_bytes=8))
     assert st == _lib.ERR_WORKSPACE
+
+
+def test_mxfp8_argument_checks_and_sizes():
+    lib = _lib.load()
+
+    def gemm(**kw):
+        a = dict(epi=_lib.EPI_NONE, a=FAKE, a_rows=16, E=8, rows=16, Nw=256, K=256, ws_bytes=1 << 30)
+        a.update(kw)
+        return lib.moe_grouped_gemm_mxfp8(a["epi"], a["a"], FAKE, a["a_rows"], None, 1, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                          a["E"], a["rows"], a["Nw"], a["K"], FAKE, _lib.F32, None, FAKE,
+                                          a["ws_bytes"], None)
+    for kw in [dict(epi=4), dict(a=None), dict(E=0), dict(rows=0), dict(K=48), dict(a=MISALIGNED)]:
+        st, _ = _err(gemm(**kw))
+        assert st == _lib.ERR_INVALID_ARG, kw
+    st, _ = _err(gemm(Nw=384))
+    assert st == _lib.ERR_UNSUPPORTED
+    st, _ = _err(gemm(ws_bytes=8))
+    assert st == _lib.ERR_WORKSPACE
+    st, _ = _err(lib.mxfp8_quantize(FAKE, _lib.F32, 4, 48, FAKE, FAKE, None))
+    assert st == _lib.ERR_INVALID_ARG
+    assert lib.mxfp8_tiled_codes_bytes(32, 256) == 2 * 2 * 2048
+    assert lib.mxfp8_tiled_codes_bytes(30, 256) == 0
+    # 64-row m-tiles: M = 512, N = 2048 has 9 x 8 tiles (host bound) -> K split in 4
+    assert lib.moe_grouped_gemm_mxfp8_workspace_size(512, 1, 2048, 6144) >= 4 * 512 * 2048 * 4
 
 
 def test_route_permute_workspace():
