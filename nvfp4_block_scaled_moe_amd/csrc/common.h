@@ -135,6 +135,14 @@ __device__ __forceinline__ void decode_scale_pair(uint32_t two, f16x2& s0, f16x2
   s1 = (f16x2){h1, h1};
 }
 
+// Read of a kernel input that stays constant while the kernel runs, through the constant
+// address space: a wave-uniform read then becomes a scalar load, whose wait does not hold up
+// the vector-memory queue (a vector load's wait also waits for every load issued before it).
+template <typename T>
+__device__ __forceinline__ T ld_const(const T* p, int64_t i) {
+  return ((const __attribute__((address_space(4))) T*)p)[i];
+}
+
 // ------------------------------------------------------------------ wave helpers
 __device__ __forceinline__ float wave_max(float v) {
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));

@@ -29,13 +29,6 @@ __device__ __forceinline__ uint32_t ld16(__amdgpu_buffer_rsrc_t r, uint32_t voff
   return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
 }
 
-// Read of a kernel input that stays constant while the kernel runs, through the constant
-// address space: a wave-uniform read then becomes a scalar load, whose wait does not hold up
-// the vector-memory queue (a vector load's wait also waits for every load issued before it).
-template <typename T>
-__device__ __forceinline__ T ld_const(const T* p, int64_t i) {
-  return ((const __attribute__((address_space(4))) T*)p)[i];
-}
 
 // silu(gate) * up, the SwiGLU of one output element (shared by every epilogue so that
 // equal inputs give equal bits).

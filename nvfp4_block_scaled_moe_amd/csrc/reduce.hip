@@ -18,13 +18,6 @@ constexpr int kRedThreads = 256;
 
 constexpr int kRedBatch = 8;   // slots whose rows are requested together
 
-// Read of a per-token input through the constant address space (the token is uniform over
-// the workgroup, so these become scalar loads).
-template <typename T>
-__device__ __forceinline__ T ld_uniform(const T* p, size_t i) {
-  return ((const __attribute__((address_space(4))) T*)p)[i];
-}
-
 template <bool YBF16>
 __global__ __launch_bounds__(kRedThreads) void unpermute_reduce_kernel(const void* __restrict__ y,
                                                                        const int* __restrict__ slot_to_row,
@@ -44,8 +37,9 @@ __global__ __launch_bounds__(kRedThreads) void unpermute_reduce_kernel(const voi
     float w[kRedBatch];
 #pragma unroll
     for (int j = 0; j < kRedBatch; ++j) {
-      row[j] = j < n ? (size_t)ld_uniform(slot_to_row, (size_t)t * k + j0 + j) : 0;
-      w[j] = j < n ? ld_uniform(topk_w, (size_t)t * k + j0 + j) : 0.f;
+      // the token is uniform over the workgroup: scalar loads
+      row[j] = j < n ? (size_t)ld_const(slot_to_row, (int64_t)t * k + j0 + j) : 0;
+      w[j] = j < n ? ld_const(topk_w, (int64_t)t * k + j0 + j) : 0.f;
     }
     float v[kRedBatch][8];
 #pragma unroll

@@ -595,25 +595,30 @@ hipError_t launch_route_permute(const float* logits, int T, int E, int k, int* t
                                 float* topk_w, int* expert_offsets, int* sorted_slot,
                                 int* slot_to_row, int* active_experts, int* n_active,
                                 void* ws, size_t ws_bytes, hipStream_t stream) {
-  // Few tokens: a workgroup per token sorts (no serial chain, measured 15.7 -> 9.1 us at one
-  // token of 512 experts, top-22); many tokens: a wave per token selects (more tokens per CU;
-  // 8192 tokens of 256 experts: 18 us against 33 us sorted). NVFP4MOE_ROUTER=wave|sort forces.
+  // Up to 16 tokens: routing and permutation in one workgroup and one launch. More tokens:
+  // a router launch, then the permutation. Router: for fewer than 256 tokens a workgroup per
+  // token sorts (no serial chain, measured 15.7 -> 9.1 us at one token of 512 experts,
+  // top-22), for more a wave per token selects (more tokens per CU; 8192 tokens of 256
+  // experts: 18 us against 33 us sorted). Overrides (tests, tuning):
+  // NVFP4MOE_ROUTER=small|sort|wave and NVFP4MOE_PERMUTE=small|single|multi; any value but
+  // "small" selects the separate launches.
   const char* force = std::getenv("NVFP4MOE_ROUTER");
-  const char* pforce0 = std::getenv("NVFP4MOE_PERMUTE");
-  int nb = 0;
-  while ((1 << nb) < E) ++nb;
-  // Few tokens: route and permute in one launch (NVFP4MOE_ROUTER or NVFP4MOE_PERMUTE set
-  // to anything but "small" selects the separate kernels).
-  const bool small_ok = T <= kPermWaves && T * k <= kSmallSlots;
-  const bool small = small_ok && (force ? !std::strcmp(force, "small") : true) &&
-                     (pforce0 ? !std::strcmp(pforce0, "small") : true);
+  const char* pforce = std::getenv("NVFP4MOE_PERMUTE");
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
+  const int pl = (E + kWave - 1) / kWave;   // experts per lane
+  const bool small = T <= kPermWaves && T * k <= kSmallSlots &&
+                     (force ? !std::strcmp(force, "small") : true) && (pforce ? !std::strcmp(pforce, "small") : true);
   if (small) {
-    const int pl = (E + kWave - 1) / kWave;
-    if (pl <= 1) return launch_small<1>(logits, T, E, k, nb, topk_ids, topk_w, expert_offsets, sorted_slot, slot_to_row, active_experts, n_active, stream);
-    if (pl <= 2) return launch_small<2>(logits, T, E, k, nb, topk_ids, topk_w, expert_offsets, sorted_slot, slot_to_row, active_experts, n_active, stream);
-    if (pl <= 4) return launch_small<4>(logits, T, E, k, nb, topk_ids, topk_w, expert_offsets, sorted_slot, slot_to_row, active_experts, n_active, stream);
-    if (pl <= 8) return launch_small<8>(logits, T, E, k, nb, topk_ids, topk_w, expert_offsets, sorted_slot, slot_to_row, active_experts, n_active, stream);
-    return launch_small<16>(logits, T, E, k, nb, topk_ids, topk_w, expert_offsets, sorted_slot, slot_to_row, active_experts, n_active, stream);
+#define NVFP4MOE_LAUNCH_SMALL(P)                                                                                  \
+  return launch_small<P>(logits, T, E, k, nbits, topk_ids, topk_w, expert_offsets, sorted_slot, slot_to_row, \
+                         active_experts, n_active, stream)
+    if (pl <= 1) NVFP4MOE_LAUNCH_SMALL(1);
+    if (pl <= 2) NVFP4MOE_LAUNCH_SMALL(2);
+    if (pl <= 4) NVFP4MOE_LAUNCH_SMALL(4);
+    if (pl <= 8) NVFP4MOE_LAUNCH_SMALL(8);
+    NVFP4MOE_LAUNCH_SMALL(16);
+#undef NVFP4MOE_LAUNCH_SMALL
   }
   const bool sort_router = force ? !std::strcmp(force, "sort") : T < 256;
   if (sort_router) {
@@ -624,7 +629,6 @@ hipError_t launch_route_permute(const float* logits, int T, int E, int k, int* t
     else router_sort_kernel<1024><<<T, router_sort_threads<1024>(), 0, stream>>>(logits, E, k, topk_ids, topk_w);
   } else {
     const unsigned rgrid = (unsigned)((T + kRouterWaves - 1) / kRouterWaves);
-    const int pl = (E + kWave - 1) / kWave;
     if (pl <= 1)
       router_kernel<1><<<rgrid, kRouterWaves * kWave, 0, stream>>>(logits, T, E, k, topk_ids, topk_w);
     else if (pl <= 2)
@@ -637,12 +641,9 @@ hipError_t launch_route_permute(const float* logits, int T, int E, int k, int* t
       router_kernel<16><<<rgrid, kRouterWaves * kWave, 0, stream>>>(logits, T, E, k, topk_ids, topk_w);
   }
 
-  int nbits = 0;
-  while ((1 << nbits) < E) ++nbits;
   const int S = T * k;
   // Many slots: the two-launch permutation (scattered writes spread over the chunks'
   // workgroups); NVFP4MOE_PERMUTE=single|multi forces one (tests).
-  const char* pforce = std::getenv("NVFP4MOE_PERMUTE");
   const bool multi = pforce ? !std::strcmp(pforce, "multi") : S >= kPmMinSlots;
   if (multi) {
     int chunk = 0, nblk = 0;
