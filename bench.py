@@ -55,8 +55,8 @@ def parse():
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
-              "(see DESIGN.md for how the layer would shard); use --gpus 1", file=sys.stderr)
+        print("bench.py runs on one GPU only: the expert- and tensor-parallel sharding of the layer "
+              "over several GPUs is not implemented; use --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch

@@ -15,7 +15,7 @@ What the pages fix
     W4A16 (FP4 weights dequantized to BF16, BF16 products) versus W4A4
     (FP4 x FP4 products).
 
-Readings taken where the pages are silent (listed in the design doc):
+Readings taken where the pages are silent:
   * Router: softmax over the E logits, keep the k largest (ranked by logit in
     float32, ties to the lower expert id), renormalise the kept
     probabilities to sum to one.

@@ -9,7 +9,7 @@ What the pages fix
     group of 32 elements (the format NVFP4, group 16 with E4M3 scales, is
     contrasted with).
 
-Readings taken where the pages are silent (each listed in the design doc):
+Readings taken where the pages are silent:
   * FP4 codes, their packing (element 2i in the LOW nibble of byte i) and the
     E2M1 value set are those of the NVFP4 oracle (``oracle/nvfp4.py``).
   * UE8M0 is the OCP Microscaling (MX) v1.0 shared-scale format: an unsigned

@@ -10,7 +10,7 @@ What the pages fix
   * "The Benchmark That Confirmed the Ceiling", section "The NVFP4 Pivot": the
     MX family's shared scale is UE8M0 per group of 32.
 
-Readings taken where the pages are silent (each listed in the design doc):
+Readings taken where the pages are silent:
   * Block-scaled FP8 is the OCP MX v1.0 MXFP8 (E4M3) format: element codes are
     OCP E4M3FN (the table and rounding of ``oracle/nvfp4.py``), one UE8M0 scale
     2^(s - 127) per 32 consecutive elements of a row (``oracle/mxfp4.py``).

@@ -12,7 +12,7 @@ What the pages fix
   * "Native FP4 Is Slower Than Emulated FP4", section 1: NVFP4 checkpoints
     carry FP4 weights.
 
-Readings taken where the pages are silent (each listed in the design doc):
+Readings taken where the pages are silent:
   * FP4 is E2M1 with the OCP Microscaling (MX) v1.0 bit layout
     (sign, 2 exponent bits with bias 1, 1 mantissa bit); value set
     {0, +-0.5, +-1, +-1.5, +-2, +-3, +-4, +-6}.
