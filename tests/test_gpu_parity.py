@@ -212,6 +212,24 @@ def test_small_route_permute_bit_exact(T, E, k, monkeypatch):
     _check_route(lg, k, E)
 
 
+def test_route_permute_at_the_slot_limit():
+    """T * k = 2^24 slots, the largest the ABI takes (262144 tokens, top-64 of 64 experts:
+    k = E, every expert in every token): ids, offsets and the permutation bit-exact."""
+    T, E, k = 1 << 18, 64, 64
+    say("route at the slot limit", T, E, k)
+    lg = inputs.random_fp32((T, E), 77)
+    r = ops.moe_route_permute(lg.to(DEV), k)
+    torch.cuda.synchronize()
+    ids, w = omoe.route(lg.numpy(), k)
+    assert np.array_equal(np_(r["topk_ids"]), ids)
+    np.testing.assert_allclose(np_(r["topk_w"]), w, rtol=1e-6, atol=0)
+    perm = omoe.permute(ids, E)
+    assert np.array_equal(np_(r["expert_offsets"]), perm["offsets"])
+    assert np.array_equal(np_(r["sorted_slot"]), perm["sorted_slot"])
+    assert np.array_equal(np_(r["slot_to_row"]), perm["slot_to_row"])
+    assert int(np_(r["n_active"])[0]) == E
+
+
 def test_route_permute_is_deterministic():
     say("route determinism")
     wl = inputs.WORKLOADS["prefill"]
