@@ -133,7 +133,8 @@ def main():
             ls = inputs.router_logits(wl, Ts).to(dev)
             r = measure(torch, ops, layer, wl, w, xs, ls, Ts, mode, max(5, args.steps // 2), 2, graph=True)
             rows.append(dict(tokens=Ts, tokens_per_expert=Ts * wl.k / wl.E, **{k: v for k, v in r.items()}))
-            print(f"[bench] sweep T={Ts}: {r['tflops']:.1f} TFLOP/s, weights {r['weight_gbs']:.0f} GB/s",
+            print(f"[bench] sweep T={Ts}: {r['tflops']:.1f} TFLOP/s, weights {r['weight_gbs']:.0f} GB/s, "
+                  f"cold {r['cold_ms_per_step']:.4f} ms ({r['cold_weight_gbs']:.0f} GB/s)",
                   file=sys.stderr, flush=True)
         with open(args.sweep, "w") as f:
             json.dump(dict(workload=wl.name, rows=rows), f, indent=1)
@@ -262,6 +263,20 @@ def measure(torch, ops, layer, wl, w, x, lg, T, mode, steps, warmup, graph=False
         torch.cuda.synchronize()
         ms = (time.perf_counter() - t0) * 1e3 / steps
         stage = None
+        # Cold: before each replay a read of 1 GiB (outside the timed events) evicts the 256 MB
+        # Infinity Cache, which could otherwise hold a small layer's touched weights between
+        # back-to-back replays; a read leaves clean lines, so no write-back lands in the replay.
+        scratch = torch.ones(1 << 28, dtype=torch.float32, device=x.device)
+        sink = torch.empty((), dtype=torch.float32, device=x.device)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for i in range(steps):
+            torch.sum(scratch, dim=0, out=sink)
+            ev[i][0].record()
+            g.replay()
+            ev[i][1].record()
+        torch.cuda.synchronize()
+        cold_ms = sum(a.elapsed_time(b) for a, b in ev) / steps
+        del scratch, sink
     else:
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(steps)]
         torch.cuda.synchronize()
@@ -279,6 +294,8 @@ def measure(torch, ops, layer, wl, w, x, lg, T, mode, steps, warmup, graph=False
     up_flops = 2.0 * S * 2 * wl.F * wl.H
     res = dict(ms_per_step=ms, tflops=flops / (ms * 1e-3) / 1e12,
                weight_gbs=(w13_bytes + w2_bytes) / (ms * 1e-3) / 1e9, touched=touched, stage_us=stage,
+               **(dict(cold_ms_per_step=cold_ms, cold_weight_gbs=(w13_bytes + w2_bytes) / (cold_ms * 1e-3) / 1e9)
+                  if graph else {}),
                up_path="mx" if mx else ("mfma" if up_path == ops.PATH_MFMA else "stream"))
     if stage:
         up_us = stage["up_gate_swiglu"]
