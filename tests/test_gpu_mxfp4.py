@@ -209,6 +209,25 @@ def test_grouped_gemm_mxfp4_gather_and_amax():
     assert np_(amax)[0] == np.abs(got).max()
 
 
+def test_mxfp4_nan_weight_group():
+    """A NaN in an MXFP4 weight row gives its 32-group the NaN scale 0xFF; the oracle's outputs
+    of that weight row are NaN, and so must the scaled matrix cores' be."""
+    say("mxfp4 nan weight")
+    d = _mx_problem([100], 256, 256, seed=31)
+    w = inputs.random_fp32((256, 256), 31, std=0.02)
+    w[7, 40] = float("nan")
+    wp, ws = ops.mxfp4_quantize(w.unsqueeze(0).to(DEV))
+    assert np_(ws)[0, 7, 1] == 0xFF
+    d["wt"] = ops.mxfp4_weights_tile(wp, ws)
+    d["W"] = [omx.dequantize(np_(wp[0]), np_(ws[0]))]
+    want = omoe.grouped_gemm(d["A"], d["offsets"], d["W"], "none")
+    got = np_(_run(d, ops.EPI_NONE, torch.float32))
+    assert np.isnan(want[:, 7]).all()
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+    fin = np.isfinite(want)
+    assert rel_fro(got[fin], want[fin]) < 1e-5
+
+
 def test_grouped_gemm_mxfp4_rejects_unsupported_nw():
     d = _mx_problem([20], 256, 256, seed=3)
     wt = ops.MxTiledWeights(d["wt"].codes, d["wt"].scales, 160, 256)   # Nw = 160: not a multiple of 256

@@ -284,6 +284,33 @@ def _run_gemm(d, mode, epi, out_dtype):
     return np_(out)
 
 
+@pytest.mark.parametrize("path", ["stream", "mfma"])
+def test_gemm_nan_weight_group_stays_visible(path, monkeypatch):
+    """A NaN in a weight row makes its 16-group's scale NaN (0x7F); every output of that
+    weight row must be NaN, as in the oracle (NaN times a zero code), on both paths; the
+    other outputs stay finite and match."""
+    say("gemm nan weight", path)
+    monkeypatch.setenv("NVFP4MOE_FORCE_PATH", path)
+    counts, Nw, K = [200, 70], 256, 512
+    E = len(counts)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    w = torch.stack([inputs.random_fp32((Nw, K), 91 + e, std=0.02) for e in range(E)])
+    w[1, 5, 37] = float("nan")                   # expert 1, weight row 5
+    wp, ws, wg = ops.nvfp4_quantize(w.to(DEV))
+    a = inputs.random_fp32((int(offsets[-1]), K), 92).to(torch.bfloat16)
+    t = lambda x: torch.from_numpy(x).to(DEV)
+    out = np_(ops.moe_grouped_gemm_nvfp4(ops.W4A16, ops.EPI_NONE, a.to(DEV), ops.nvfp4_weights_tile(wp, ws, wg),
+                                         t(offsets), t(np.arange(E, dtype=np.int32)), t(np.array([E], np.int32)),
+                                         out_dtype=torch.float32))
+    torch.cuda.synchronize()
+    Wd = [onv.dequantize(np_(wp[e]), np_(ws[e]), np_(wg)[e]) for e in range(E)]
+    want = omoe.grouped_gemm(a.float().numpy().astype(np.float64), offsets, Wd)
+    assert np.isnan(want[offsets[1]:, 5]).all() and np.isfinite(np.delete(want, 5, axis=1)).all()
+    assert np.array_equal(np.isnan(out), np.isnan(want))
+    fin = np.isfinite(want)
+    assert rel_fro(out[fin], want[fin]) < 1e-5
+
+
 GEMM_CASES = [
     # counts per expert, Nw, K
     ([3, 0, 16, 17, 1], 64, 64),
