@@ -13,20 +13,25 @@
 //
 //   * m-tiles of 128 rows of one expert from the device-built list (MtileSched, built by
 //     mtile_schedule_kernel); the tiles of the listed m-tiles are split into 8 equal ranges,
-//     one per XCD, as in the f16 large-M kernel.
+//     one per XCD, as in the f16 large-M kernel. Within an expert the m-tiles go in groups
+//     (64 m-tiles for FP4, 16 for FP8) whose tiles run row-tile-major: the workgroups an XCD
+//     has in flight share one weight tile (FP4: up to 32 m-tiles on the same 256 weight rows)
+//     in its L2 instead of each streaming the expert's weights again. Grids that split K
+//     keep the m-tile-major order.
 //   * Workgroup = 8 waves = 256 weight rows (each wave 2 blocks of 16: for SwiGLU one gate
 //     and the matching up block) x one m-tile (8 token blocks of 16; a ragged m-tile runs
 //     with 1, 2, 4 or 8 blocks).
 //   * Per chunk (128 k) each thread stages 16 bytes of codes and one scale byte of one token
-//     (512 threads = 128 tokens x 4 k-blocks) through registers into a three-slot LDS ring;
+//     (512 threads = 128 tokens x 4 k-blocks) through registers into a four-slot LDS ring;
 //     token rows are padded to 80 bytes, so the 16 lanes of a fragment read hit distinct
 //     banks. The scale bytes of a chunk sit in LDS as [k-block][row in block][token block],
 //     so one 8-byte read gives a lane the scales of all 8 token blocks and the MFMA's byte
 //     select (opsel) picks each one. Weights are loaded two chunks ahead into registers.
 //   * Step c issues the 16 MFMAs (16x16x128) of chunk c on fragments read in step c-1 and
-//     meanwhile reads chunk c+1's fragments, commits chunk c+2 to the ring and requests chunk
-//     c+4: the reads never wait behind the barrier that ends the step, and a staging load has
-//     two steps to arrive. Epilogue as in the
+//     meanwhile reads chunk c+1's fragments and requests chunk c+5; every second step commits
+//     the next two chunks to the ring and ends with the barrier, so the two waves per SIMD
+//     meet once per 32 MFMAs each: the reads never wait behind a barrier, and a staging load
+//     has two to three steps to arrive. Epilogue as in the
 //     other GEMMs with alpha 1 (MXFP4 has no per-tensor scale): SwiGLU, bf16 or f32 stores,
 //     amax.
 //   * SwiGLU with quantized output: h is written as MXFP4 straight from the epilogue (no
@@ -52,7 +57,7 @@ namespace {
 constexpr int kMxWaves = 8;
 constexpr int kMxRBW = 2;                           // 16-row weight blocks per wave
 constexpr int kMxWin = 16;                          // chunks per scale tile (2048 k)
-constexpr int kMxSlots = 3;                         // LDS ring slots
+constexpr int kMxSlots = 4;                         // LDS ring slots
 constexpr int kMxDepth = 2;                         // weight chunks in flight
 
 typedef int v8i __attribute__((ext_vector_type(8)));
@@ -136,7 +141,7 @@ __device__ __forceinline__ void static_for(F&& f) {
 }
 
 template <int BITS, bool SWIGLU, bool QH>
-__global__ __launch_bounds__(kMxWaves* kWave) void gemm_mx_kernel(const GemmArgs p, int ntiles_n) {
+__global__ __launch_bounds__(kMxWaves* kWave) void gemm_mx_kernel(const GemmArgs p, int ntiles_n, int mgroup) {
   using Fmt = MxFmt<BITS>;
   using Frag = MxFrag<BITS>;
   constexpr int TBM = Fmt::TBM, LB = Fmt::LB, TOK = Fmt::TOK;
@@ -161,7 +166,20 @@ __global__ __launch_bounds__(kMxWaves* kWave) void gemm_mx_kernel(const GemmArgs
   const int tile = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
   if ((int)(blockIdx.x >> 3) >= per_xcd || tile >= ntiles) return;
   const int ks = tile / per_split, mn = tile - ks * per_split;
-  const int mt = mn / ntiles_n, nb = mn - mt * ntiles_n;
+  int mt = mn / ntiles_n, nb = mn - mt * ntiles_n;
+  {
+    // Tile order within the expert: m-tiles in groups of mgroup (the last one shorter), the
+    // tiles of a group row-tile-major. The list holds an expert's m-tiles in a row, m-tile i
+    // of the expert at row i * 16 TBM, so the group follows from the m-tile's own entry.
+    const int loc = ld_const(p.sched_r, mt) / (16 * TBM);
+    const int ex = ld_const(p.sched_e, mt);
+    const int me = (ld_const(p.expert_offsets, ex + 1) - ld_const(p.expert_offsets, ex) + 16 * TBM - 1) / (16 * TBM);
+    const int gi = loc / mgroup, gs = mt - loc + gi * mgroup;
+    const int gn = min(min(mgroup, me - gi * mgroup), ld_const(p.sched_n, 0) - gs);
+    const int pos = (mt - gs) * ntiles_n + nb;
+    nb = pos / gn;
+    mt = gs + (pos - nb * gn);
+  }
   const int e = ld_const(p.sched_e, mt), tc = ld_const(p.sched_r, mt);
   const int r0 = ld_const(p.expert_offsets, e);
   const int M = ld_const(p.expert_offsets, e + 1) - r0;
@@ -246,27 +264,32 @@ __global__ __launch_bounds__(kMxWaves* kWave) void gemm_mx_kernel(const GemmArgs
     for (int tb = 0; tb < TBM; ++tb) acc[b][tb] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
   // prologue: scale windows w0 and w0 + 1, weights of the slice's first kMxDepth chunks,
-  // activations of its first two chunks committed to slots 0 and 1, the third and fourth
-  // requested (staging sets 2 and 3)
+  // activations of its first three chunks committed to slots 0 - 2, the fourth and fifth
+  // requested (staging sets 3 and 0)
   s_issue(sa, w0);
   s_issue(sb, w0 + 1);
   b_issue(0, clo);
   b_issue(1, clo + 1);
+  b_issue(2, clo + 2);
+  b_issue(3, clo + 3);
 #pragma unroll
   for (int d = 0; d < kMxDepth; ++d) w_issue(d, clo + d);
   b_commit(0, 0);
   b_commit(1, 1);
-  b_issue(2, clo + 2);
-  b_issue(3, clo + 3);
+  b_commit(2, 2);
+  b_issue(0, clo + 4);
   __syncthreads();
 
   // The main loop, compiled for NTB = 8, 4, 2 or 1 token blocks (ntb rounded up; blocks past
-  // the m-tile's rows hold zeros). With j = c - clo: chunk c lives in LDS slot j % 3 and
-  // staging set j & 3, its weights in ring entry j % kMxDepth. Step c: request chunk c+4 (set
-  // j & 3, whose chunk c was committed in step c-2), read chunk c+1's fragments (committed in
-  // step c-1), MFMAs of chunk c, commit chunk c+2 (requested in step c-2) to slot (j+2) % 3
-  // (chunk c-1, read in step c-2), barrier. Steps come in blocks of 16; the MFMAs of chunks
-  // past the slice are skipped.
+  // the m-tile's rows hold zeros). With j = c - clo: chunk c lives in LDS slot j & 3 and
+  // staging set j & 3, its weights in ring entry j % kMxDepth. Step c: request chunk c+5 (set
+  // (j+1) & 3, whose chunk c+1 was committed in step c-1 or c-2), read chunk c+1's fragments
+  // (committed by the last odd step before c), MFMAs of chunk c; then, for odd j, commit
+  // chunks c+2 and c+3 (requested in steps c-3 and c-2) to slots (j+2) & 3 and (j+3) & 3,
+  // whose chunks c-2 and c-1 were read in steps c-3 and c-2, before the barrier of step c-2,
+  // and end with a barrier. The read of chunk 0 before the loop has a barrier of its own,
+  // since step 1 rewrites slot 0. Steps come in blocks of 16, so j & 3 = u & 3 is a constant;
+  // the MFMAs of chunks past the slice are skipped.
   auto body = [&](auto ntb_tag) {
     constexpr int NTB = decltype(ntb_tag)::value;
     Frag bcur[NTB], bnext[NTB];
@@ -292,7 +315,7 @@ __global__ __launch_bounds__(kMxWaves* kWave) void gemm_mx_kernel(const GemmArgs
       }
     };
     b_read(bcur, scb, 0);
-    int slot = 0;   // c % 3
+    __syncthreads();   // slot 0 is rewritten in step 1
     for (int c0 = clo; c0 < chi; c0 += kMxWin) {
       u32x4 scs[kMxRBW];   // scale bytes of chunks c0 .. c0 + 15
 #pragma unroll
@@ -302,14 +325,12 @@ __global__ __launch_bounds__(kMxWaves* kWave) void gemm_mx_kernel(const GemmArgs
         constexpr int u = decltype(u_tag)::value;
         const int c = c0 + u;
         constexpr int d = u % kMxDepth;
-        const int slot1 = slot == kMxSlots - 1 ? 0 : slot + 1;
-        const int slot2 = slot1 == kMxSlots - 1 ? 0 : slot1 + 1;
-        b_issue(u & 3, c + 4);
+        b_issue((u + 1) & 3, c + 5);
         Frag wa[kMxRBW];
 #pragma unroll
         for (int b = 0; b < kMxRBW; ++b) wa[b] = wring[d][b];
         w_issue(d, c + kMxDepth);   // this ring entry is free again
-        b_read(bnext, scbn, slot1);
+        b_read(bnext, scbn, (u + 1) & 3);
         if (c < chi) {
           static_for<NTB>([&](auto tb_tag) {
             constexpr int tb = decltype(tb_tag)::value;
@@ -318,7 +339,10 @@ __global__ __launch_bounds__(kMxWaves* kWave) void gemm_mx_kernel(const GemmArgs
               acc[b][tb] = mfma_mx<BITS, (u & 3), (tb & 3)>(wa[b], scs[b][u >> 2], bcur[tb], scb[tb >> 2], acc[b][tb]);
           });
         }
-        b_commit((u + 2) & 3, slot2);
+        if (u & 1) {
+          b_commit((u + 2) & 3, (u + 2) & 3);
+          b_commit((u + 3) & 3, (u + 3) & 3);
+        }
         if (u == kMxWin - 1) {
 #pragma unroll
           for (int b = 0; b < kMxRBW; ++b) {
@@ -326,12 +350,11 @@ __global__ __launch_bounds__(kMxWaves* kWave) void gemm_mx_kernel(const GemmArgs
             sb[b] = sn[b];
           }
         }
-        __syncthreads();
+        if (u & 1) __syncthreads();
 #pragma unroll
         for (int tb = 0; tb < NTB; ++tb) bcur[tb] = bnext[tb];
         scb[0] = scbn[0];
         scb[1] = scbn[1];
-        slot = slot1;
       });
     }
   };
@@ -433,17 +456,22 @@ int mx_ksplit(int max_mtiles, int Nw, int K) {
 
 hipError_t launch_gemm_mx(const GemmArgs& a, int max_mtiles, int bits, hipStream_t stream) {
   const int ntiles_n = a.Nw / (16 * kMxRBW * kMxWaves);
+  // m-tiles per row-tile-major group (measured best); a split-K grid is resident at once,
+  // where m-tile-major order measured faster
+  int mgroup = a.ksplit > 1 ? 1 : bits == 8 ? 16 : 64;
+  if (const char* env = std::getenv("NVFP4MOE_MX_GROUP")) mgroup = std::atoi(env);
+  if (mgroup < 1) mgroup = 1;
   const int total = max_mtiles * ntiles_n * a.ksplit;   // bound on the tiles
   const unsigned grid = (unsigned)((total + 7) / 8 * 8);
   if (bits == 8) {
-    if (a.swiglu) gemm_mx_kernel<8, true, false><<<grid, kMxWaves * kWave, 0, stream>>>(a, ntiles_n);
-    else gemm_mx_kernel<8, false, false><<<grid, kMxWaves * kWave, 0, stream>>>(a, ntiles_n);
+    if (a.swiglu) gemm_mx_kernel<8, true, false><<<grid, kMxWaves * kWave, 0, stream>>>(a, ntiles_n, mgroup);
+    else gemm_mx_kernel<8, false, false><<<grid, kMxWaves * kWave, 0, stream>>>(a, ntiles_n, mgroup);
   } else if (a.hq_packed) {
-    gemm_mx_kernel<4, true, true><<<grid, kMxWaves * kWave, 0, stream>>>(a, ntiles_n);
+    gemm_mx_kernel<4, true, true><<<grid, kMxWaves * kWave, 0, stream>>>(a, ntiles_n, mgroup);
   } else if (a.swiglu) {
-    gemm_mx_kernel<4, true, false><<<grid, kMxWaves * kWave, 0, stream>>>(a, ntiles_n);
+    gemm_mx_kernel<4, true, false><<<grid, kMxWaves * kWave, 0, stream>>>(a, ntiles_n, mgroup);
   } else {
-    gemm_mx_kernel<4, false, false><<<grid, kMxWaves * kWave, 0, stream>>>(a, ntiles_n);
+    gemm_mx_kernel<4, false, false><<<grid, kMxWaves * kWave, 0, stream>>>(a, ntiles_n, mgroup);
   }
   if (a.ksplit <= 1) return hipGetLastError();
   const hipError_t e2 = hipGetLastError();
