@@ -179,6 +179,23 @@ def test_dense_mxfp4_gemm_full_size():
     assert r < 1e-5
 
 
+@pytest.mark.parametrize("group,ksplit", [("3", "1"), ("2", "3"), ("64", "1"), ("1", "1")])
+def test_grouped_gemm_mxfp4_tile_groups(group, ksplit, monkeypatch):
+    """The tile order within an expert: m-tiles in groups whose tiles run row-tile-major. Here
+    experts hold several groups (the last group shorter, the last m-tile ragged), with and
+    without K slices, so every (m-tile, row tile) pair must still be computed exactly once."""
+    counts = [1000, 0, 300, 129]         # 8, 0, 3 and 2 m-tiles of 128 rows
+    say("gemm mxfp4 tile groups", group, ksplit)
+    monkeypatch.setenv("NVFP4MOE_MX_GROUP", group)
+    monkeypatch.setenv("NVFP4MOE_MX_KSPLIT", ksplit)
+    d = _mx_problem(counts, 768, 640, seed=91)
+    for epi in (ops.EPI_NONE, ops.EPI_SWIGLU):
+        want = omoe.grouped_gemm(d["A"], d["offsets"], d["W"], "swiglu" if epi else "none")
+        got = np_(_run(d, epi, torch.float32))
+        assert_finite(got)
+        assert rel_fro(got, want) < 1e-5
+
+
 @pytest.mark.parametrize("counts,Nw,K,T,k", [(c, n, kk, None, None) for c, n, kk in MX_CASES]
                          + [([7, 0, 300, 9], 256, 512, 120, 3)])
 def test_swiglu_q_codes_bit_exact(counts, Nw, K, T, k):

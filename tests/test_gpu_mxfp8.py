@@ -132,6 +132,22 @@ def test_grouped_gemm_mxfp8(counts, Nw, K, ksplit, monkeypatch):
         assert r < MX8_TOL, r       # identical operands on both sides: only float32 summation differs
 
 
+@pytest.mark.parametrize("group,ksplit", [("3", "1"), ("16", "1"), ("4", "3")])
+def test_grouped_gemm_mxfp8_tile_groups(group, ksplit, monkeypatch):
+    """Experts with several groups of 64-row m-tiles (the last group shorter, the last m-tile
+    ragged), row-tile-major within a group, with and without K slices."""
+    counts = [700, 0, 200, 65]           # 11, 0, 4 and 2 m-tiles of 64 rows
+    say("gemm mxfp8 tile groups", group, ksplit)
+    monkeypatch.setenv("NVFP4MOE_MX_GROUP", group)
+    monkeypatch.setenv("NVFP4MOE_MX_KSPLIT", ksplit)
+    d = _problem(counts, 512, 640, seed=93)
+    for epi in (ops.EPI_NONE, ops.EPI_SWIGLU):
+        want = omoe.grouped_gemm(d["A"], d["offsets"], d["W"], "swiglu" if epi else "none")
+        got = np_(_run(d, epi))
+        assert_finite(got)
+        assert rel_fro(got, want) < MX8_TOL
+
+
 def test_grouped_gemm_mxfp8_gather_and_amax():
     say("gemm mxfp8 gather")
     d = _problem([7, 0, 300, 9], 256, 512, seed=9, T=120, k=3)
