@@ -24,16 +24,16 @@
 //   * Per chunk (128 k) each thread stages 16 bytes of codes and one scale byte of one token
 //     (512 threads = 128 tokens x 4 k-blocks) through registers into a four-slot LDS ring;
 //     token rows are padded by 32 bytes (96-byte rows; FP8 160), which measured 2.5x (FP8
-//     ~16x) fewer LDS bank-conflict cycles than 16 bytes of padding. The scale bytes of a chunk sit in LDS as [k-block][row in block][token block],
-//     so one 8-byte read gives a lane the scales of all 8 token blocks and the MFMA's byte
-//     select (opsel) picks each one. Weights are loaded two chunks ahead into registers.
+//     ~16x) fewer LDS bank-conflict cycles than 16 bytes of padding. The scale bytes of a
+//     chunk sit in LDS as [k-block][row in block][token block], so one 8-byte read gives a
+//     lane the scales of all 8 token blocks and the MFMA's byte select (opsel) picks each
+//     one. Weights are loaded two chunks ahead into registers.
 //   * Step c issues the 16 MFMAs (16x16x128) of chunk c on fragments read in step c-1 and
 //     meanwhile reads chunk c+1's fragments and requests chunk c+5; every second step commits
 //     the next two chunks to the ring and ends with the barrier, so the two waves per SIMD
 //     meet once per 32 MFMAs each: the reads never wait behind a barrier, and a staging load
-//     has two to three steps to arrive. Epilogue as in the
-//     other GEMMs with alpha 1 (MXFP4 has no per-tensor scale): SwiGLU, bf16 or f32 stores,
-//     amax.
+//     has two to three steps to arrive. Epilogue as in the other GEMMs with alpha 1 (MXFP4
+//     has no per-tensor scale): SwiGLU, bf16 or f32 stores, amax.
 //   * SwiGLU with quantized output: h is written as MXFP4 straight from the epilogue (no
 //     per-tensor scale, so no pass over all of h is needed first). A 32-column group of h
 //     spans the 16 columns of two neighbouring waves; each wave reduces its half's amax key
