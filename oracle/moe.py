@@ -38,7 +38,9 @@ Readings taken where the pages are silent:
 
 Parity status: every function is pinned in tests/test_oracle_moe.py
 (brute-force sorting, library argsort, exact rational arithmetic on tiny
-shapes, closed forms of silu, reduction to a dense FFN computed by torch).
+shapes, closed forms of silu, reduction to a dense FFN computed by torch in
+each mode: W4A16, NVFP4 W4A4 with x and h quantized as whole tensors, and
+MXFP4).
 """
 from __future__ import annotations
 
@@ -210,6 +212,21 @@ def quantize_rows_nvfp4(x: np.ndarray, g=None):
     return nvfp4.quantize(np.asarray(x, dtype=np.float32), g)
 
 
+def round_h(h: np.ndarray, mode: str):
+    """Rounding point of h between the two GEMMs. Returns (h as the down GEMM reads it,
+    float64; the quantized triple or pair, or None).
+
+    w4a16: h rounded to bf16. w4a4: h (as float32) NVFP4-quantized as one tensor with one
+    dynamic global scale, like the token activations. mxfp4: h MXFP4-quantized (no
+    per-tensor scale).
+    """
+    if mode == "w4a16":
+        return bf16_round(h), None
+    fmt = mxfp4 if mode == "mxfp4" else nvfp4
+    hq = fmt.quantize(np.asarray(h, dtype=np.float64).astype(np.float32))
+    return fmt.dequantize(*hq), hq
+
+
 # ------------------------------------------------------------------ the layer
 def moe_layer(x, logits, k, w13, w2, mode="w4a16", return_stages=False):
     """The whole MoE layer in float64 with the rounding points fixed above.
@@ -241,12 +258,9 @@ def moe_layer(x, logits, k, w13, w2, mode="w4a16", return_stages=False):
     dq2 = lambda e: fmt.dequantize(*w2(e))
     h = grouped_gemm(A, perm["offsets"], dq13, "swiglu")
     st["h_exact"] = h
-    if mode == "w4a16":
-        h = bf16_round(h)
-    else:
-        hq = fmt.quantize(h.astype(np.float32))
+    h, hq = round_h(h, mode)
+    if hq is not None:
         st["hq"] = hq
-        h = fmt.dequantize(*hq)
     st["h"] = h
     Y = grouped_gemm(h, perm["offsets"], dq2, "none")
     st["Y"] = Y

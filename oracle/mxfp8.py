@@ -5,12 +5,16 @@ imports this module.
 
 What the pages fix
   * "Native FP4 Is Slower Than Emulated FP4", sections 1 and 2: the model runs
-    FP8 activations, and its dense layers go through FP8 scaled-matmul kernels
-    (per-tensor, channel-wise and CUTLASS block-scaled variants are named).
+    FP8 activations, and its dense layers go through FP8 scaled-matmul kernels;
+    the kernels named there are scaled with a per-tensor or a per-channel
+    scale. None of them is block-scaled.
   * "The Benchmark That Confirmed the Ceiling", section "The NVFP4 Pivot": the
     MX family's shared scale is UE8M0 per group of 32.
 
 Readings taken where the pages are silent:
+  * The block-scaled FP8 dense GEMM is a reading, not something the pages
+    name: it applies the pages' MX-family scale (UE8M0 per 32) to the FP8
+    elements of their dense layers.
   * Block-scaled FP8 is the OCP MX v1.0 MXFP8 (E4M3) format: element codes are
     OCP E4M3FN (the table and rounding of ``oracle/nvfp4.py``), one UE8M0 scale
     2^(s - 127) per 32 consecutive elements of a row (``oracle/mxfp4.py``).

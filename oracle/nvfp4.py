@@ -37,7 +37,9 @@ Readings taken where the pages are silent:
 
 Parity status: every function below is pinned in tests/test_oracle_nvfp4.py
 (closed forms, the OCP value sets, an independent torch float8_e4m3fn cast,
-grid-built inputs that must round-trip exactly, and error bounds).
+grid-built inputs that must round-trip exactly, exact E2M1 midpoints under
+scales that are not powers of two (which only a correctly rounded division
+keeps on the midpoint), and error bounds).
 """
 from __future__ import annotations
 
@@ -146,6 +148,16 @@ def dequantize(packed: np.ndarray, scales: np.ndarray, g) -> np.ndarray:
     return vals * g
 
 
+def div_f32(a, b) -> np.ndarray:
+    """Correctly rounded float32 quotient a / b (IEEE division, round to nearest even).
+
+    The quantization rule divides; a reciprocal followed by a multiply rounds twice
+    and can move a quotient that is exactly an E2M1 midpoint off it.
+    """
+    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
+        return (np.asarray(a, dtype=np.float32) / np.asarray(b, dtype=np.float32)).astype(np.float32)
+
+
 def global_scale(w: np.ndarray) -> np.float32:
     """g = fp32(amax / 2688) over the finite entries; 1.0 when that amax is 0."""
     a = np.abs(np.asarray(w, dtype=np.float32))
@@ -171,15 +183,13 @@ def quantize(w: np.ndarray, g=None):
     finite = np.isfinite(grp).all(axis=-1)                       # [R, C/16]
     amax_g = np.abs(np.where(np.isfinite(grp), grp, 0)).max(axis=-1).astype(np.float32)
     six_g = np.float32(np.float32(E2M1_MAX) * g)
-    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
-        ratio = (amax_g / six_g).astype(np.float32)              # fp32 division
+    ratio = div_f32(amax_g, six_g)                               # fp32 division
     ratio = np.where(amax_g == 0, np.float32(0), ratio)
     ratio = np.minimum(ratio, np.float32(E4M3_MAX))
     s = e4m3_rne(ratio)                                          # [R, C/16]
     S = (E4M3_TABLE[s].astype(np.float32) * g).astype(np.float32)  # fp32 product
     S_el = np.repeat(S, GROUP, axis=-1).reshape(R, C)
-    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
-        x = (w / S_el).astype(np.float32)                        # fp32 division
+    x = div_f32(w, S_el)                                         # fp32 division
     mag = e2m1_rne_sat(np.where(S_el == 0, np.float32(0), x))
     sign = np.signbit(w).astype(np.uint8) << 3
     codes = (mag | sign).astype(np.uint8)

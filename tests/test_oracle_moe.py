@@ -213,6 +213,43 @@ def test_layer_w4a4_uses_quantized_activations():
     assert np.linalg.norm(xq - x) / np.linalg.norm(x) < 0.12
 
 
+def test_layer_w4a4_with_one_expert_is_a_dense_nvfp4_ffn():
+    """NVFP4 W4A4 layer with E = 1, k = 1 against a dense SwiGLU FFN computed by torch in
+    float64: the token rows are NVFP4-quantized as one tensor (one dynamic global scale), the
+    FFN's h is NVFP4-quantized again as one tensor with its own dynamic global scale, and both
+    GEMMs take the dequantized operands. Rows of very different magnitude make a per-row
+    global scale give visibly different codes, and h's re-quantization moves the output by
+    far more than the output's bf16 rounding."""
+    rng = np.random.default_rng(43)
+    T, H, F = 6, 64, 64
+    mag = np.array([1.0, 8.0, 0.1, 3.0, 0.5, 20.0])[:, None]
+    x = moe.bf16_round(rng.standard_normal((T, H)) * mag).astype(np.float32)
+    w13 = _nvfp4_random(rng, 2 * F, H)
+    w2 = _nvfp4_random(rng, H, F)
+    out, st = moe.moe_layer(x, np.zeros((T, 1), np.float32), 1, lambda e: w13, lambda e: w2,
+                            mode="w4a4", return_stages=True)
+    xq = nvfp4.quantize(x)
+    X = torch.from_numpy(nvfp4.dequantize(*xq))
+    W13 = torch.from_numpy(nvfp4.dequantize(*w13))
+    W2 = torch.from_numpy(nvfp4.dequantize(*w2))
+    G = X @ W13.T
+    h = torch.nn.functional.silu(G[:, :F]) * G[:, F:]
+    hq = nvfp4.quantize(h.float().numpy())
+    ref = (torch.from_numpy(nvfp4.dequantize(*hq)) @ W2.T).float().to(torch.bfloat16).double().numpy()
+    rel = np.linalg.norm(out - ref) / np.linalg.norm(ref)
+    assert rel < 4e-3                             # bf16 output rounding may differ by one ulp
+    ref_norm = np.linalg.norm(ref, axis=1)
+    assert ref_norm.min() > 0
+    row_rel = np.linalg.norm(out - ref, axis=1) / ref_norm
+    assert row_rel.max() < 4e-3                   # small rows judged on their own scale
+    assert np.mean(out != ref) < 0.02
+    assert np.array_equal(st["xq"][0], xq[0]) and np.array_equal(st["xq"][1], xq[1])
+    assert st["xq"][2] == xq[2]
+    assert np.array_equal(st["hq"][0], hq[0]) and np.array_equal(st["hq"][1], hq[1])
+    assert st["hq"][2] == hq[2]
+    np.testing.assert_allclose(st["h_exact"], h.numpy(), rtol=1e-12, atol=1e-15)
+
+
 def _mxfp4_random(rng, R, C):
     return mxfp4.quantize((rng.standard_normal((R, C)) * 0.02).astype(np.float32))
 

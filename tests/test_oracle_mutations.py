@@ -62,7 +62,48 @@ def _gemm_wrong_expert(A, offsets, W, epilogue="none"):
     return moe.__dict__["_orig_grouped_gemm"](A, offsets, lambda e: get((e + 1) % E), epilogue)
 
 
+def _div_by_reciprocal(a, b):
+    with np.errstate(divide="ignore", invalid="ignore", over="ignore"):
+        r = (np.float32(1) / np.asarray(b, dtype=np.float32)).astype(np.float32)
+        return (np.asarray(a, dtype=np.float32) * r).astype(np.float32)
+
+
+def _h_not_requantized(h, mode):
+    if mode == "w4a4":
+        return moe.bf16_round(h), None
+    return moe.__dict__["_orig_round_h"](h, mode)
+
+
+def _quantize_rows_own_g(x, g=None):
+    """Each row NVFP4-quantized with its own dynamic global scale; returns the codes, the
+    scales and the per-row scales."""
+    x = np.asarray(x, dtype=np.float32)
+    parts = [nvfp4.quantize(x[r:r + 1]) for r in range(x.shape[0])]
+    return (np.concatenate([p[0] for p in parts]), np.concatenate([p[1] for p in parts]),
+            np.array([p[2] for p in parts], dtype=np.float32))
+
+
+def _h_per_row_g(h, mode):
+    if mode == "w4a4":
+        p, s, g = _quantize_rows_own_g(np.asarray(h, dtype=np.float64).astype(np.float32))
+        return nvfp4.dequantize(p, s, 1.0) * g.astype(np.float64)[:, None], (p, s, g[0])
+    return moe.__dict__["_orig_round_h"](h, mode)
+
+
+def _x_per_row_g(x, g=None):
+    p, s, gr = _quantize_rows_own_g(x)
+    return p, s, gr[0]
+
+
 MUTATIONS = [
+    ("quantize divides by a reciprocal", nvfp4, "div_f32", _div_by_reciprocal,
+     lambda: tn.test_quantize_exact_midpoints_divide_correctly(3 * 2.0 ** -10)),
+    ("w4a4 layer skips h re-quantization", moe, "round_h", _h_not_requantized,
+     tm.test_layer_w4a4_with_one_expert_is_a_dense_nvfp4_ffn),
+    ("w4a4 layer quantizes h with a per-row g", moe, "round_h", _h_per_row_g,
+     tm.test_layer_w4a4_with_one_expert_is_a_dense_nvfp4_ffn),
+    ("w4a4 layer quantizes x with a per-row g", moe, "quantize_rows_nvfp4", _x_per_row_g,
+     tm.test_layer_w4a4_with_one_expert_is_a_dense_nvfp4_ffn),
     ("unpack high nibble first", nvfp4, "unpack_fp4", _high_nibble_first, tn.test_pack_low_nibble_first),
     ("e2m1 table 1.5<->2 swapped", nvfp4, "E2M1_TABLE",
      nvfp4.E2M1_TABLE[[0, 1, 2, 4, 3, 5, 6, 7, 8, 9, 10, 12, 11, 13, 14, 15]],

@@ -145,6 +145,44 @@ def test_quantize_grid_inputs_roundtrip_exactly_dynamic_g():
     assert np.array_equal(nvfp4.unpack_fp4(packed), q)
 
 
+MIDPOINTS = ("0.25", "0.75", "1.25", "1.75", "2.5", "3.5", "5.0")
+
+
+def tie_matrix(g):
+    """Rows of exact E2M1 midpoints under scales S = E4M3[s] * g that are not powers of two.
+
+    Row i uses scale code s = 8 + i (every normal code up to 0x7E): element 0 is 6 S, which
+    makes 6 S / (6 g) = E4M3[s] exactly and so fixes the scale code; elements 1..7 are m S and
+    8..14 are -m S for the seven midpoints m; element 15 is 0. With g = 3, 5 or 7 times a power
+    of two every product has at most 10 significant bits, so each input is exact in float32 and
+    a correctly rounded division returns m itself. Returns (w [118, 16] float32, the scale
+    codes, the expected 4-bit codes from the hand-derived tie table).
+    """
+    ties = {x: int(c, 16) for x, c in _read_table("e2m1_rne_ties.txt") if x in MIDPOINTS}
+    mids = [float(m) for m in MIDPOINTS]
+    s_codes = np.arange(8, 0x7F, dtype=np.uint8)
+    rows, want = [], []
+    for s in s_codes:
+        S = nvfp4.E4M3_TABLE[s] * float(g)
+        rows.append([6 * S] + [m * S for m in mids] + [-m * S for m in mids] + [0.0])
+        want.append([0x7] + [ties[m] for m in MIDPOINTS] + [0x8 | ties[m] for m in MIDPOINTS] + [0x0])
+    w = np.array(rows, dtype=np.float64)
+    assert np.array_equal(w.astype(np.float32).astype(np.float64), w)   # exact in float32
+    return w.astype(np.float32), s_codes[:, None], np.array(want, dtype=np.uint8)
+
+
+@pytest.mark.parametrize("g", [3 * 2.0 ** -10, 5 * 2.0 ** -12, 7 * 2.0 ** -9])
+def test_quantize_exact_midpoints_divide_correctly(g):
+    """Pinned to the tie table: a quotient that is exactly an E2M1 midpoint goes to the even
+    code. A reciprocal-then-multiply (two roundings) moves some of these quotients off the
+    midpoint and picks the odd neighbour."""
+    w, s_want, q_want = tie_matrix(g)
+    packed, scales, gg = nvfp4.quantize(w, g=np.float32(g))
+    assert gg == np.float32(g)
+    assert np.array_equal(scales, s_want)
+    assert np.array_equal(nvfp4.unpack_fp4(packed), q_want)
+
+
 def test_quantize_scale_codes_match_torch_cast_of_ratio():
     rng = np.random.default_rng(5)
     w = (rng.standard_normal((64, 512)) * 0.02).astype(np.float32)
