@@ -205,8 +205,9 @@ size_t moe_route_permute_workspace_size(int32_t T, int32_t E, int32_t k);
  *               (K rounded up to a multiple of 128 in the last two).
  *               a, w_packed and w_scales 16-byte aligned, a_scales 2-byte aligned.
  *   out         device, out_dtype (F32 or BF16), [rows, EPI_SWIGLU ? Nw/2 : Nw].
- *   out_amax    device float[1] or NULL: if given, set to max |out| over the call (exact;
- *               used to pick the global scale when out is quantized next).
+ *   out_amax    device float[1] or NULL: if given, set to max |out| over the finite values
+ *               the call writes (NaN and +-Inf excluded; with a bf16 out, of the rounded
+ *               values): exactly the amax nvfp4_quantize's amax_in expects for out.
  *   ws          moe_grouped_gemm_workspace_size(mode, a_rows, rows, E, Nw, K) bytes.
  * ------------------------------------------------------------------------- */
 nvfp4moe_status moe_grouped_gemm_nvfp4(nvfp4moe_mode mode, nvfp4moe_epilogue epi,

@@ -149,8 +149,12 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
-// Max of |v| as float bits; NaN (any sign) compares above every finite value and Inf.
-__device__ __forceinline__ uint32_t abs_bits(float v) { return __float_as_uint(v) & 0x7fffffffu; }
+// Key of |v| for a max over the finite values: the float bits of |v| when v is finite, 0 for
+// NaN and +-Inf (float bits of non-negative floats order like the values).
+__device__ __forceinline__ uint32_t finite_abs_bits(float v) {
+  const uint32_t b = __float_as_uint(v) & 0x7fffffffu;
+  return b < 0x7f800000u ? b : 0u;
+}
 
 __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   for (int o = 32; o > 0; o >>= 1) {

@@ -30,6 +30,25 @@ __device__ __forceinline__ uint32_t ld16(__amdgpu_buffer_rsrc_t r, uint32_t voff
 }
 
 
+// Four consecutive output values at element offset o of p.out (f32, or bf16 rounded to
+// nearest even); returns amax_bits merged with the finite |value|s as written.
+__device__ __forceinline__ uint32_t store4(const GemmArgs& p, size_t o, const float (&v)[4], uint32_t amax_bits) {
+  if (p.out_bf16) {
+    uint32_t b[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      b[i] = f32_to_bf16(v[i]);
+      amax_bits = max(amax_bits, finite_abs_bits(__uint_as_float(b[i] << 16)));
+    }
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + o) = make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) amax_bits = max(amax_bits, finite_abs_bits(v[i]));
+    *reinterpret_cast<float4*>(static_cast<float*>(p.out) + o) = make_float4(v[0], v[1], v[2], v[3]);
+  }
+  return amax_bits;
+}
+
 // silu(gate) * up, the SwiGLU of one output element (shared by every epilogue so that
 // equal inputs give equal bits).
 __device__ __forceinline__ float swiglu1(float gv, float uv) { return gv / (1.0f + expf(-gv)) * uv; }
@@ -40,7 +59,8 @@ __device__ __forceinline__ float swiglu1(float gv, float uv) { return gv / (1.0f
 // written: out = acc * alpha * 2^pexp, where pexp is the activation row's power-of-two
 // scale (W4A16) or 0; with SwiGLU the first RBW/2 blocks are gate rows and the others the
 // matching up rows, and silu(gate) * up is written to column blkrow(b) of the F-wide output.
-// Returns the running max of |written value| as float bits.
+// Returns the running max of |written value| over the finite values written (NaN and Inf
+// excluded; with a bf16 output, of the rounded values) as float bits.
 // pexp[tb] is the power-of-two exponent of the lane's GEMM row in token block tb.
 template <int RBW, int TBM, bool SWIGLU, typename BlkRow>
 __device__ __forceinline__ uint32_t store_tile_exp(const GemmArgs& p, const f32x4 (&acc)[RBW][TBM], int tc,
@@ -63,15 +83,9 @@ __device__ __forceinline__ uint32_t store_tile_exp(const GemmArgs& p, const f32x
             const float gv = ldexpf(acc[b][tb][i] * alpha, pexp);
             const float uv = ldexpf(acc[b + RBW / 2][tb][i] * alpha, pexp);
             h[i] = swiglu1(gv, uv);
-            amax_bits = max(amax_bits, abs_bits(h[i]));
           }
           const size_t o = (size_t)row * F + blkrow(b) + 4 * g;
-          if (p.out_bf16)
-            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + o) =
-                make_uint2(f32_to_bf16(h[0]) | (f32_to_bf16(h[1]) << 16),
-                           f32_to_bf16(h[2]) | (f32_to_bf16(h[3]) << 16));
-          else
-            *reinterpret_cast<float4*>(static_cast<float*>(p.out) + o) = make_float4(h[0], h[1], h[2], h[3]);
+          amax_bits = store4(p, o, h, amax_bits);
         }
       } else {
 #pragma unroll
@@ -80,15 +94,9 @@ __device__ __forceinline__ uint32_t store_tile_exp(const GemmArgs& p, const f32x
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             v[i] = ldexpf(acc[b][tb][i] * alpha, pexp);
-            amax_bits = max(amax_bits, abs_bits(v[i]));
           }
           const size_t o = (size_t)row * Nw + blkrow(b) + 4 * g;
-          if (p.out_bf16)
-            *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + o) =
-                make_uint2(f32_to_bf16(v[0]) | (f32_to_bf16(v[1]) << 16),
-                           f32_to_bf16(v[2]) | (f32_to_bf16(v[3]) << 16));
-          else
-            *reinterpret_cast<float4*>(static_cast<float*>(p.out) + o) = make_float4(v[0], v[1], v[2], v[3]);
+          amax_bits = store4(p, o, v, amax_bits);
         }
       }
     }
@@ -117,8 +125,8 @@ __device__ __forceinline__ uint32_t store_tile(const GemmArgs& p, const f32x4 (&
   return store_tile_exp<RBW, TBM, SWIGLU>(p, acc, tc, ntb, M, r0, alpha, pexps, blkrow, lane, amax_bits);
 }
 
-// Wave-reduced amax of the tile, merged into *out_amax (float bits of non-negative values
-// order like the values).
+// Wave-reduced amax of the tile (finite values only), merged into *out_amax (float bits of
+// non-negative values order like the values).
 __device__ __forceinline__ void merge_amax(float* out_amax, uint32_t amax_bits, int lane) {
   if (!out_amax) return;
   amax_bits = wave_max_u32(amax_bits);

@@ -293,14 +293,8 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const GemmArgs p) {
       } else {
         o[q] = ldexpf(av[q] * alpha, pexp);
       }
-      amax_bits = max(amax_bits, abs_bits(o[q]));
     }
-    const size_t off = (size_t)row * ncol + col;
-    if (p.out_bf16)
-      *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + off) =
-          make_uint2(f32_to_bf16(o[0]) | (f32_to_bf16(o[1]) << 16), f32_to_bf16(o[2]) | (f32_to_bf16(o[3]) << 16));
-    else
-      *reinterpret_cast<float4*>(static_cast<float*>(p.out) + off) = make_float4(o[0], o[1], o[2], o[3]);
+    amax_bits = store4(p, (size_t)row * ncol + col, o, amax_bits);
   }
   merge_amax(p.out_amax, amax_bits, threadIdx.x & (kWave - 1));
 }

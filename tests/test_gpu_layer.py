@@ -2,9 +2,10 @@
 
 The tiny workload is checked end to end against the oracle's layer. The full-size
 workloads run exactly the sequence of calls the benchmark times; the oracle checks routing
-and permutation in full, the weight quantization and both GEMMs on sampled experts
-(largest, median and smallest active expert, fed the GPU's inputs to each stage), and the
-reduce in full.
+and permutation in full, the activation and h codes in full (W4A4), the weight quantization
+on the largest, median and smallest active expert, both GEMMs on every active expert (fed
+the GPU's inputs to each stage; rows at both edges of every 64-row block and 4 columns of
+every 64-column block), and the reduce in full, element by element.
 """
 import numpy as np
 import pytest
@@ -13,7 +14,7 @@ import torch
 from nvfp4_block_scaled_moe_amd import inputs, layer, ops
 from oracle import moe as omoe
 from oracle import nvfp4 as onv
-from tests.gpu_util import assert_finite, np_, rel_fro, say
+from tests.gpu_util import assert_finite, assert_reduce_elementwise, check_every_expert, np_, rel_fro, say
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -57,12 +58,47 @@ def test_tiny_layer_end_to_end(mode):
         assert np.array_equal(np_(st["xq"]), ost["xq"][0]) and np.array_equal(np_(st["xs"]), ost["xq"][1])
 
 
+@pytest.mark.parametrize("path", ["stream", "mfma"])
+def test_tiny_w4a4_layer_nan_token_stays_local(path, monkeypatch):
+    """A NaN in one token's activations: its NVFP4 group gets a NaN scale, so every h and Y row
+    of that token's slots is NaN. h's global scale comes from the finite amax, so no other
+    token is touched: exactly the oracle's NaN pattern (one output row), the rest within the
+    W4A4 tolerance of the oracle, on both GEMM paths."""
+    say("tiny w4a4 layer, NaN token", path)
+    monkeypatch.setenv("NVFP4MOE_FORCE_PATH", path)
+    wl = inputs.WORKLOADS["tiny"]
+    w = layer.quantize_experts(wl, DEV)
+    x = inputs.activations_bf16(wl).clone()
+    x[5, 40] = float("nan")
+    lg = inputs.router_logits(wl)
+    out, st = layer.moe_forward(x.to(DEV), lg.to(DEV), wl.k, w, mode=ops.W4A4, keep=True)
+    torch.cuda.synchronize()
+    assert np.isfinite(np_(st["h_amax"])).all() and np.isfinite(np_(st["hg"])).all()
+    w13, w2 = _oracle_experts(w)
+    want = omoe.moe_layer(x.float().numpy(), lg.numpy(), wl.k, w13, w2, mode="w4a4")
+    got = np_(out)
+    nan_rows = np.nonzero(np.isnan(want).any(axis=1))[0]
+    assert list(nan_rows) == [5] and np.isnan(want[5]).all()
+    assert np.array_equal(np.isnan(got), np.isnan(want))
+    keep = np.arange(wl.T) != 5
+    assert rel_fro(got[keep], want[keep]) <= 2e-2
+
+
 def _sample_experts(offsets, n=3):
     counts = np.diff(offsets)
     act = np.nonzero(counts)[0]
     order = act[np.argsort(counts[act], kind="stable")]
     picks = {int(order[-1]), int(order[len(order) // 2]), int(order[0])}
     return sorted(picks)[:n]
+
+
+def _dequant_rows(packed, scales, g):
+    """deq(e, idx): float64 rows idx of expert e's NVFP4 matrix, dequantized by the oracle
+    from the GPU's codes (only those rows leave the device)."""
+    def deq(e, idx):
+        ix = torch.from_numpy(np.asarray(idx, dtype=np.int64)).to(packed.device)
+        return onv.dequantize(np_(packed[e][ix]), np_(scales[e][ix]), np_(g[e:e + 1])[0])
+    return deq
 
 
 def _check_full_size(wl, T, mode, fp8=False):
@@ -91,34 +127,30 @@ def _check_full_size(wl, T, mode, fp8=False):
     else:
         A_all = xs
     tok = perm["sorted_slot"] // wl.k
-    h = np_(st["h"]).astype(np.float64)
-    y = np_(st["y"]).astype(np.float64)
+    h = np_(st["h"])
+    y = np_(st["y"])
+    assert_finite(h, y)
     if mode == ops.W4A4:
         hq = (np_(st["hq"]), np_(st["hs"]), np_(st["hg"])[0])
-        hq_o = onv.quantize(np_(st["h"]).astype(np.float32), g=None)
+        hq_o = onv.quantize(h.astype(np.float32), g=None)
         assert np.array_equal(hq[0], hq_o[0]) and np.array_equal(hq[1], hq_o[1])   # same fp32 h in
-        h_in = onv.dequantize(*hq)
+        assert hq[2] == hq_o[2]
+        h_in_rows = lambda rows: onv.dequantize(hq[0][rows], hq[1][rows], hq[2])
     else:
-        h_in = h
-    tol = 1e-3 if mode == ops.W4A16 else 2e-2
+        h_in_rows = lambda rows: h[rows].astype(np.float64)
+    # weight quantization bit-exact on the largest, median and smallest active expert
     for e in _sample_experts(offsets):
-        r0, r1 = int(offsets[e]), int(offsets[e + 1])
-        w13 = inputs.expert_weight_fp32(wl, "w13", e, DEV).cpu().numpy()
-        po, so, go = onv.quantize(w13)
+        po, so, go = onv.quantize(inputs.expert_weight_fp32(wl, "w13", e, DEV).cpu().numpy())
         assert np.array_equal(np_(w.w13_packed[e]), po) and np.array_equal(np_(w.w13_scales[e]), so)
-        G = A_all[tok[r0:r1]] @ onv.dequantize(po, so, go).T
-        hw = omoe.swiglu(G)
-        if mode == ops.W4A16:
-            hw = omoe.bf16_round(hw)
-        rh = rel_fro(h[r0:r1], hw)
-        W2 = onv.dequantize(np_(w.w2_packed[e]), np_(w.w2_scales[e]), np_(w.w2_g)[e])
-        ry = rel_fro(y[r0:r1], h_in[r0:r1] @ W2.T)
-        say(f"expert {e}: rows {r1 - r0} rel(h) {rh:.2e} rel(Y) {ry:.2e}")
-        assert rh <= tol and ry <= tol and ry < 1e-5
-    want = omoe.bf16_round(omoe.unpermute_reduce(y, perm["slot_to_row"], np_(st["topk_w"]).astype(np.float64)))
+        assert np_(w.w13_g[e:e + 1])[0] == go
+    # both GEMMs on every active expert (every m-tile and weight-row tile sampled)
+    check_every_expert(offsets, tok, A_all, h, y, h_in_rows, _dequant_rows(w.w13_packed, w.w13_scales, w.w13_g),
+                       _dequant_rows(w.w2_packed, w.w2_scales, w.w2_g), wl.F, wl.H,
+                       omoe.bf16_round if mode == ops.W4A16 else (lambda v: v),
+                       tol_h=1e-3 if mode == ops.W4A16 else 1e-5, seed=T)
     got = np_(out)
-    assert_finite(got, h, y)
-    assert rel_fro(got, want) <= 1e-3
+    assert_finite(got)
+    assert_reduce_elementwise(got, y, perm["slot_to_row"], np_(st["topk_w"]))
 
 
 @pytest.mark.parametrize("T", [1, 64, 512])
