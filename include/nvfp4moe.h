@@ -118,6 +118,26 @@ nvfp4moe_status nvfp4_quantize(const void* x, nvfp4moe_dtype x_dtype, int64_t B,
 size_t nvfp4_quantize_workspace_size(int64_t B, int64_t R, int64_t C);
 
 /* ---------------------------------------------------------------------------
+ * nvfp4_quantize_noalloc -- nvfp4_quantize for callers that cannot allocate memory: code
+ * under HIP graph capture, tight serving loops that quantize activations every forward,
+ * harnesses that forbid allocation. Same arguments, rule and outputs as nvfp4_quantize
+ * (bit for bit), without (ws, ws_bytes); the call allocates nothing.
+ *
+ *   The amax pass (g_in and amax_in both NULL) keeps its partial maxima in a scratch array
+ *   of 64 KiB that the library holds on each GPU it runs on until the process ends:
+ *   B * (amax workgroups per matrix) floats, i.e. nvfp4_quantize_workspace_size(B, R, C)
+ *   bytes, must not exceed 65536 (any single matrix fits; a larger batch returns
+ *   NVFP4MOE_ERR_WORKSPACE and launches nothing). Every entry the call reads is written by
+ *   the same call, so nothing needs clearing between calls.
+ *   All calls on one GPU share that GPU's scratch: calls that may overlap on one GPU (on
+ *   different streams, or from different threads without ordering) race and must not be
+ *   issued. stream must belong to the current device (else NVFP4MOE_ERR_INVALID_ARG).
+ * ------------------------------------------------------------------------- */
+nvfp4moe_status nvfp4_quantize_noalloc(const void* x, nvfp4moe_dtype x_dtype, int64_t B, int64_t R,
+                                       int64_t C, const float* g_in, const float* amax_in,
+                                       uint8_t* packed, uint8_t* scales, float* g_out, void* stream);
+
+/* ---------------------------------------------------------------------------
  * nvfp4_weights_tile -- reorder NVFP4 weight matrices (the row-major storage above) into
  * the tiled storage that moe_grouped_gemm_nvfp4 reads. A pure permutation of the bytes
  * plus zero padding (no value changes); run once per weight set, like the quantization.

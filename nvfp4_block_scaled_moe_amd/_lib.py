@@ -28,6 +28,7 @@ _int = ctypes.c_int
 SIGNATURES = {
     "nvfp4_quantize": (_int, [_vp, _int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "nvfp4_quantize_workspace_size": (_sz, [_i64, _i64, _i64]),
+    "nvfp4_quantize_noalloc": (_int, [_vp, _int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp]),
     "nvfp4_weights_tile": (_int, [_vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp]),
     "nvfp4_tiled_codes_bytes": (_sz, [_i64, _i64]),
     "nvfp4_tiled_scales_bytes": (_sz, [_i64, _i64]),

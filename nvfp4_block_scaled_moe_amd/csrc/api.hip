@@ -3,6 +3,7 @@
 // memory or synchronizes the device.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -114,7 +115,7 @@ extern "C" {
 
 const char* nvfp4moe_last_error(void) { return g_last_error.c_str(); }
 int nvfp4moe_last_dispatch(void) { return g_last_dispatch; }
-int nvfp4moe_abi_version(void) { return 204; }
+int nvfp4moe_abi_version(void) { return 205; }
 
 // ------------------------------------------------------------------ quantize
 size_t nvfp4_quantize_workspace_size(int64_t B, int64_t R, int64_t C) {
@@ -122,23 +123,35 @@ size_t nvfp4_quantize_workspace_size(int64_t B, int64_t R, int64_t C) {
   return round_up(quantize_ws_bytes(B, R, C));
 }
 
+}  // extern "C"
+
+namespace {
+// Argument checks shared by nvfp4_quantize and nvfp4_quantize_noalloc.
+nvfp4moe_status quantize_checks(const char* fn, const void* x, nvfp4moe_dtype x_dtype, int64_t B, int64_t R,
+                                int64_t C, const uint8_t* packed, const uint8_t* scales, const float* g_out) {
+  if (!x || !packed || !scales || !g_out) return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: null tensor pointer", fn);
+  if (x_dtype != NVFP4MOE_F32 && x_dtype != NVFP4MOE_BF16)
+    return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: x_dtype must be F32 or BF16", fn);
+  if (B < 1 || R < 1 || C < 32 || C % 32 != 0)
+    return fail(NVFP4MOE_ERR_INVALID_ARG,
+                "%s: need B >= 1, R >= 1, C >= 32 and C %% 32 == 0 (B=%lld R=%lld C=%lld)", fn, (long long)B,
+                (long long)R, (long long)C);
+  if (B > 65535 || (double)B * (double)R * (double)C > 4.0e12)
+    return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: tensor too large", fn);
+  if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(scales, 2) || !aligned(g_out, 4))
+    return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: x and packed must be 16-byte aligned, scales 2-byte aligned", fn);
+  return NVFP4MOE_OK;
+}
+}  // namespace
+
+extern "C" {
+
 nvfp4moe_status nvfp4_quantize(const void* x, nvfp4moe_dtype x_dtype, int64_t B, int64_t R,
                                int64_t C, const float* g_in, const float* amax_in,
                                uint8_t* packed, uint8_t* scales, float* g_out, void* ws,
                                size_t ws_bytes, void* stream) {
-  if (!x || !packed || !scales || !g_out)
-    return fail(NVFP4MOE_ERR_INVALID_ARG, "nvfp4_quantize: null tensor pointer");
-  if (x_dtype != NVFP4MOE_F32 && x_dtype != NVFP4MOE_BF16)
-    return fail(NVFP4MOE_ERR_INVALID_ARG, "nvfp4_quantize: x_dtype must be F32 or BF16");
-  if (B < 1 || R < 1 || C < 32 || C % 32 != 0)
-    return fail(NVFP4MOE_ERR_INVALID_ARG,
-                "nvfp4_quantize: need B >= 1, R >= 1, C >= 32 and C %% 32 == 0 (B=%lld R=%lld C=%lld)",
-                (long long)B, (long long)R, (long long)C);
-  if (B > 65535 || (double)B * (double)R * (double)C > 4.0e12)
-    return fail(NVFP4MOE_ERR_INVALID_ARG, "nvfp4_quantize: tensor too large");
-  if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(scales, 2) || !aligned(g_out, 4))
-    return fail(NVFP4MOE_ERR_INVALID_ARG,
-                "nvfp4_quantize: x and packed must be 16-byte aligned, scales 2-byte aligned");
+  const nvfp4moe_status chk = quantize_checks("nvfp4_quantize", x, x_dtype, B, R, C, packed, scales, g_out);
+  if (chk != NVFP4MOE_OK) return chk;
   if (!g_in && !amax_in) {
     const size_t need = nvfp4_quantize_workspace_size(B, R, C);
     if (!ws || ws_bytes < need)
@@ -148,6 +161,74 @@ nvfp4moe_status nvfp4_quantize(const void* x, nvfp4moe_dtype x_dtype, int64_t B,
   return hip_status(launch_quantize(x, x_dtype == NVFP4MOE_BF16, B, R, C, g_in, amax_in, packed,
                                     scales, g_out, ws, static_cast<hipStream_t>(stream)),
                     "nvfp4_quantize");
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------------ no-allocation quantize
+// Scratch of nvfp4_quantize_noalloc: the amax pass's per-workgroup partial maxima
+// (B * amax-workgroups floats). Each GPU the library runs on holds its own copy until the
+// process ends. In host code the array's name is not a device address: the address comes
+// from hipGetSymbolAddress, once per device with that device current, and only that pointer
+// is passed to kernels.
+constexpr size_t kNoAllocScratchBytes = 64 * 1024;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];   // device address of `scratch`, per device id
+
+// Device address of the current device's scratch (looked up on the first call on a device).
+hipError_t noalloc_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return hipSuccess;
+}
+}  // namespace
+
+extern "C" {
+
+nvfp4moe_status nvfp4_quantize_noalloc(const void* x, nvfp4moe_dtype x_dtype, int64_t B, int64_t R, int64_t C,
+                                       const float* g_in, const float* amax_in, uint8_t* packed,
+                                       uint8_t* scales, float* g_out, void* stream) {
+  const char* fn = "nvfp4_quantize_noalloc";
+  const nvfp4moe_status chk = quantize_checks(fn, x, x_dtype, B, R, C, packed, scales, g_out);
+  if (chk != NVFP4MOE_OK) return chk;
+  void* ws = nullptr;
+  if (!g_in && !amax_in) {
+    const size_t need = nvfp4_quantize_workspace_size(B, R, C);
+    if (need > kNoAllocScratchBytes)
+      return fail(NVFP4MOE_ERR_WORKSPACE,
+                  "%s: the amax pass needs %zu bytes of scratch, more than the %zu this entry point holds "
+                  "(fewer matrices per call, or nvfp4_quantize with a workspace)",
+                  fn, need, kNoAllocScratchBytes);
+    int cur = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return hip_status(e, fn);
+    if (stream) {
+      hipDevice_t sdev = 0;
+      e = hipStreamGetDevice(static_cast<hipStream_t>(stream), &sdev);
+      if (e != hipSuccess) return hip_status(e, fn);
+      if ((int)sdev != cur)
+        return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: the stream belongs to device %d, the current device is %d", fn,
+                    (int)sdev, cur);
+    }
+    e = noalloc_scratch(&ws);
+    if (e != hipSuccess) return hip_status(e, fn);
+  }
+  return hip_status(launch_quantize(x, x_dtype == NVFP4MOE_BF16, B, R, C, g_in, amax_in, packed, scales, g_out,
+                                    ws, static_cast<hipStream_t>(stream)),
+                    fn);
 }
 
 // ------------------------------------------------------------------ route + permute

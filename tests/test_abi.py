@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(_lib.SIGNATURES), "binding signatures out of sync with the header"
     for n in names:
         assert hasattr(lib, n)
-    assert lib.nvfp4moe_abi_version() == 204
+    assert lib.nvfp4moe_abi_version() == 205
 
 
 FAKE = ctypes.c_void_p(1 << 20)      # aligned, never dereferenced: validation fails first
@@ -57,6 +57,22 @@ def test_quantize_rejects_bad_arguments():
     need = lib.nvfp4_quantize_workspace_size(1, 4, 32)
     st, msg = _err(lib.nvfp4_quantize(FAKE, _lib.F32, 1, 4, 32, None, None, FAKE, FAKE, FAKE, FAKE, need - 1, None))
     assert st == _lib.ERR_WORKSPACE and "workspace" in msg
+
+
+def test_quantize_noalloc_rejects_bad_arguments():
+    """Argument checks of the no-allocation quantize: the same as nvfp4_quantize, plus a batch
+    whose amax partials exceed the 64 KiB scratch (host-side, before any HIP call)."""
+    lib = _lib.load()
+    st, msg = _err(lib.nvfp4_quantize_noalloc(None, _lib.F32, 1, 4, 32, None, None, FAKE, FAKE, FAKE, None))
+    assert st == _lib.ERR_INVALID_ARG and "null" in msg
+    st, msg = _err(lib.nvfp4_quantize_noalloc(FAKE, _lib.F32, 1, 4, 48, None, None, FAKE, FAKE, FAKE, None))
+    assert st == _lib.ERR_INVALID_ARG and "C % 32" in msg
+    st, _ = _err(lib.nvfp4_quantize_noalloc(MISALIGNED, _lib.F32, 1, 4, 32, None, None, FAKE, FAKE, FAKE, None))
+    assert st == _lib.ERR_INVALID_ARG
+    assert lib.nvfp4_quantize_workspace_size(16, 4096, 4096) == 65536    # fits exactly
+    assert lib.nvfp4_quantize_workspace_size(32, 4096, 4096) > 65536
+    st, msg = _err(lib.nvfp4_quantize_noalloc(FAKE, _lib.F32, 32, 4096, 4096, None, None, FAKE, FAKE, FAKE, None))
+    assert st == _lib.ERR_WORKSPACE and "65536" in msg
 
 
 def test_route_permute_rejects_bad_arguments():
