@@ -88,6 +88,10 @@ typedef enum {
   NVFP4MOE_PATH_MFMA = 2    /* large-M LDS-tiled MFMA kernel (compute-bound regime) */
 } nvfp4moe_path;
 
+/* Byte order of quantized codes and scales: the row-major storage above, or the tiled
+ * storage the grouped GEMM reads (described at nvfp4_weights_tile). */
+typedef enum { NVFP4MOE_LAYOUT_ROW_MAJOR = 0, NVFP4MOE_LAYOUT_TILED = 1 } nvfp4moe_layout;
+
 /* ---------------------------------------------------------------------------
  * nvfp4_quantize -- quantize B float matrices [R, C] to NVFP4.  [P2] "The NVFP4 Pivot".
  *
@@ -99,8 +103,15 @@ typedef enum {
  *            g[b] = amax_in[b] / 2688 (or 1 when amax_in[b] == 0); amax_in must be
  *            the max |x| over the finite entries of matrix b.
  *            If both are NULL, the amax is computed on the device.
- *   packed   device uint8 [B, R, C/2]  (output)
- *   scales   device uint8 [B, R, C/16] (output)
+ *   layout   NVFP4MOE_LAYOUT_ROW_MAJOR: packed [B, R, C/2] and scales [B, R, C/16] as above.
+ *            NVFP4MOE_LAYOUT_TILED: the same codes and scales written straight into the
+ *            tiled storage moe_grouped_gemm_nvfp4 reads (bytes identical to nvfp4_weights_tile
+ *            of the row-major result, padding zeros included): packed [B *
+ *            nvfp4_tiled_codes_bytes(R, C)], scales [B * nvfp4_tiled_scales_bytes(R, C)], both
+ *            16-byte aligned; needs R % 16 == 0 and B * R * C / 2 < 2^40. So one call turns a
+ *            weight matrix into the GEMM's operand.
+ *   packed   device uint8 (output), codes in `layout`.
+ *   scales   device uint8 (output), E4M3 scales in `layout`.
  *   g_out    device float[B]           (output) the global scales used.
  *   ws       workspace of nvfp4_quantize_workspace_size(B, R, C) bytes.
  *
@@ -113,8 +124,8 @@ typedef enum {
  * ------------------------------------------------------------------------- */
 nvfp4moe_status nvfp4_quantize(const void* x, nvfp4moe_dtype x_dtype, int64_t B, int64_t R,
                                int64_t C, const float* g_in, const float* amax_in,
-                               uint8_t* packed, uint8_t* scales, float* g_out, void* ws,
-                               size_t ws_bytes, void* stream);
+                               nvfp4moe_layout layout, uint8_t* packed, uint8_t* scales,
+                               float* g_out, void* ws, size_t ws_bytes, void* stream);
 size_t nvfp4_quantize_workspace_size(int64_t B, int64_t R, int64_t C);
 
 /* ---------------------------------------------------------------------------
@@ -135,7 +146,8 @@ size_t nvfp4_quantize_workspace_size(int64_t B, int64_t R, int64_t C);
  * ------------------------------------------------------------------------- */
 nvfp4moe_status nvfp4_quantize_noalloc(const void* x, nvfp4moe_dtype x_dtype, int64_t B, int64_t R,
                                        int64_t C, const float* g_in, const float* amax_in,
-                                       uint8_t* packed, uint8_t* scales, float* g_out, void* stream);
+                                       nvfp4moe_layout layout, uint8_t* packed, uint8_t* scales,
+                                       float* g_out, void* stream);
 
 /* ---------------------------------------------------------------------------
  * nvfp4_weights_tile -- reorder NVFP4 weight matrices (the row-major storage above) into
@@ -214,9 +226,11 @@ size_t moe_route_permute_workspace_size(int32_t T, int32_t E, int32_t k);
  *               else: GEMM row r reads a row gather_index[r] / gather_div, e.g.
  *                     sorted_slot with gather_div = k to gather token rows.
  *   w_packed, w_scales
- *               device, the E expert matrices [Nw, K] in the tiled storage written by
- *               nvfp4_weights_tile (expert e at e * nvfp4_tiled_codes_bytes(Nw, K) and
- *               e * nvfp4_tiled_scales_bytes(Nw, K)); w_g float [E].
+ *               device, the E expert matrices [Nw, K] in the tiled storage: written by
+ *               nvfp4_quantize with NVFP4MOE_LAYOUT_TILED (B = E), or by nvfp4_weights_tile
+ *               from the row-major storage (expert e at e * nvfp4_tiled_codes_bytes(Nw, K)
+ *               and e * nvfp4_tiled_scales_bytes(Nw, K)); w_g float [E], the g_out of that
+ *               quantization.
  *   expert_offsets, active_experts, n_active  as written by moe_route_permute (for a
  *               dense GEMM: E = 1, offsets {0, rows}, active {0}, n_active {1}).
  *   E, rows, Nw, K  1 <= E <= 1024; rows = expert_offsets[E] >= 1; Nw >= 32, Nw % 32 == 0

@@ -18,6 +18,7 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
 W4A16, W4A4 = 0, 1
 EPI_NONE, EPI_SWIGLU = 0, 1
 F32, BF16 = 0, 1
+LAYOUT_ROW_MAJOR, LAYOUT_TILED = 0, 1
 PATH_NONE, PATH_STREAM, PATH_MFMA = 0, 1, 2
 STATUS_NAMES = {0: "OK", 1: "ERR_INVALID_ARG", 2: "ERR_UNSUPPORTED", 3: "ERR_WORKSPACE", 4: "ERR_HIP"}
 
@@ -26,9 +27,9 @@ _int = ctypes.c_int
 
 #: name -> (restype, argtypes), one entry per function declared in include/nvfp4moe.h
 SIGNATURES = {
-    "nvfp4_quantize": (_int, [_vp, _int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "nvfp4_quantize": (_int, [_vp, _int, _i64, _i64, _i64, _vp, _vp, _int, _vp, _vp, _vp, _vp, _sz, _vp]),
     "nvfp4_quantize_workspace_size": (_sz, [_i64, _i64, _i64]),
-    "nvfp4_quantize_noalloc": (_int, [_vp, _int, _i64, _i64, _i64, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "nvfp4_quantize_noalloc": (_int, [_vp, _int, _i64, _i64, _i64, _vp, _vp, _int, _vp, _vp, _vp, _vp]),
     "nvfp4_weights_tile": (_int, [_vp, _vp, _i64, _i64, _i64, _vp, _vp, _vp]),
     "nvfp4_tiled_codes_bytes": (_sz, [_i64, _i64]),
     "nvfp4_tiled_scales_bytes": (_sz, [_i64, _i64]),

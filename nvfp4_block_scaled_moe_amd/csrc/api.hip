@@ -115,7 +115,7 @@ extern "C" {
 
 const char* nvfp4moe_last_error(void) { return g_last_error.c_str(); }
 int nvfp4moe_last_dispatch(void) { return g_last_dispatch; }
-int nvfp4moe_abi_version(void) { return 205; }
+int nvfp4moe_abi_version(void) { return 300; }
 
 // ------------------------------------------------------------------ quantize
 size_t nvfp4_quantize_workspace_size(int64_t B, int64_t R, int64_t C) {
@@ -128,7 +128,10 @@ size_t nvfp4_quantize_workspace_size(int64_t B, int64_t R, int64_t C) {
 namespace {
 // Argument checks shared by nvfp4_quantize and nvfp4_quantize_noalloc.
 nvfp4moe_status quantize_checks(const char* fn, const void* x, nvfp4moe_dtype x_dtype, int64_t B, int64_t R,
-                                int64_t C, const uint8_t* packed, const uint8_t* scales, const float* g_out) {
+                                int64_t C, nvfp4moe_layout layout, const uint8_t* packed, const uint8_t* scales,
+                                const float* g_out) {
+  if (layout != NVFP4MOE_LAYOUT_ROW_MAJOR && layout != NVFP4MOE_LAYOUT_TILED)
+    return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: bad layout %d", fn, (int)layout);
   if (!x || !packed || !scales || !g_out) return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: null tensor pointer", fn);
   if (x_dtype != NVFP4MOE_F32 && x_dtype != NVFP4MOE_BF16)
     return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: x_dtype must be F32 or BF16", fn);
@@ -140,6 +143,14 @@ nvfp4moe_status quantize_checks(const char* fn, const void* x, nvfp4moe_dtype x_
     return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: tensor too large", fn);
   if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(scales, 2) || !aligned(g_out, 4))
     return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: x and packed must be 16-byte aligned, scales 2-byte aligned", fn);
+  if (layout == NVFP4MOE_LAYOUT_TILED) {
+    if (R < 16 || R % 16 != 0)
+      return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: the tiled layout needs R %% 16 == 0 (R=%lld)", fn, (long long)R);
+    if (B * R * (C / 2) >= (int64_t(1) << 40) || R > (int64_t(1) << 30) || C > (int64_t(1) << 30))
+      return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: matrices too large for the tiled layout", fn);
+    if (!aligned(scales, 16))
+      return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: the tiled scales must be 16-byte aligned", fn);
+  }
   return NVFP4MOE_OK;
 }
 }  // namespace
@@ -148,9 +159,10 @@ extern "C" {
 
 nvfp4moe_status nvfp4_quantize(const void* x, nvfp4moe_dtype x_dtype, int64_t B, int64_t R,
                                int64_t C, const float* g_in, const float* amax_in,
-                               uint8_t* packed, uint8_t* scales, float* g_out, void* ws,
-                               size_t ws_bytes, void* stream) {
-  const nvfp4moe_status chk = quantize_checks("nvfp4_quantize", x, x_dtype, B, R, C, packed, scales, g_out);
+                               nvfp4moe_layout layout, uint8_t* packed, uint8_t* scales, float* g_out,
+                               void* ws, size_t ws_bytes, void* stream) {
+  const nvfp4moe_status chk =
+      quantize_checks("nvfp4_quantize", x, x_dtype, B, R, C, layout, packed, scales, g_out);
   if (chk != NVFP4MOE_OK) return chk;
   if (!g_in && !amax_in) {
     const size_t need = nvfp4_quantize_workspace_size(B, R, C);
@@ -158,8 +170,9 @@ nvfp4moe_status nvfp4_quantize(const void* x, nvfp4moe_dtype x_dtype, int64_t B,
       return fail(NVFP4MOE_ERR_WORKSPACE, "nvfp4_quantize: workspace of %zu bytes needed, %zu given",
                   need, ws_bytes);
   }
-  return hip_status(launch_quantize(x, x_dtype == NVFP4MOE_BF16, B, R, C, g_in, amax_in, packed,
-                                    scales, g_out, ws, static_cast<hipStream_t>(stream)),
+  return hip_status(launch_quantize(x, x_dtype == NVFP4MOE_BF16, B, R, C, g_in, amax_in,
+                                    layout == NVFP4MOE_LAYOUT_TILED, packed, scales, g_out, ws,
+                                    static_cast<hipStream_t>(stream)),
                     "nvfp4_quantize");
 }
 
@@ -199,10 +212,10 @@ hipError_t noalloc_scratch(void** out) {
 extern "C" {
 
 nvfp4moe_status nvfp4_quantize_noalloc(const void* x, nvfp4moe_dtype x_dtype, int64_t B, int64_t R, int64_t C,
-                                       const float* g_in, const float* amax_in, uint8_t* packed,
-                                       uint8_t* scales, float* g_out, void* stream) {
+                                       const float* g_in, const float* amax_in, nvfp4moe_layout layout,
+                                       uint8_t* packed, uint8_t* scales, float* g_out, void* stream) {
   const char* fn = "nvfp4_quantize_noalloc";
-  const nvfp4moe_status chk = quantize_checks(fn, x, x_dtype, B, R, C, packed, scales, g_out);
+  const nvfp4moe_status chk = quantize_checks(fn, x, x_dtype, B, R, C, layout, packed, scales, g_out);
   if (chk != NVFP4MOE_OK) return chk;
   void* ws = nullptr;
   if (!g_in && !amax_in) {
@@ -226,8 +239,9 @@ nvfp4moe_status nvfp4_quantize_noalloc(const void* x, nvfp4moe_dtype x_dtype, in
     e = noalloc_scratch(&ws);
     if (e != hipSuccess) return hip_status(e, fn);
   }
-  return hip_status(launch_quantize(x, x_dtype == NVFP4MOE_BF16, B, R, C, g_in, amax_in, packed, scales, g_out,
-                                    ws, static_cast<hipStream_t>(stream)),
+  return hip_status(launch_quantize(x, x_dtype == NVFP4MOE_BF16, B, R, C, g_in, amax_in,
+                                    layout == NVFP4MOE_LAYOUT_TILED, packed, scales, g_out, ws,
+                                    static_cast<hipStream_t>(stream)),
                     fn);
 }
 

@@ -10,8 +10,9 @@ namespace nvfp4moe {
 
 // ---- quantize.hip
 size_t quantize_ws_bytes(int64_t B, int64_t R, int64_t C);
+// tiled: write codes and scales in the tiled storage of launch_weights_tile (R % 16 == 0).
 hipError_t launch_quantize(const void* x, bool x_bf16, int64_t B, int64_t R, int64_t C,
-                           const float* g_in, const float* amax_in, uint8_t* packed,
+                           const float* g_in, const float* amax_in, bool tiled, uint8_t* packed,
                            uint8_t* scales, float* g_out, void* ws, hipStream_t stream);
 size_t fp8_roundtrip_ws_bytes(int64_t n);
 hipError_t launch_fp8_roundtrip(const void* x, int64_t n, void* out, void* ws, hipStream_t stream);

@@ -115,28 +115,18 @@ __global__ __launch_bounds__(kWave) void finalize_scale_kernel(const float* __re
   if (threadIdx.x == 0) g_out[b] = g;
 }
 
-// One thread per 32 consecutive elements of a row (two 16-groups): reads 32 elements,
-// writes 16 packed bytes and 2 scale bytes.
+// NVFP4 codes of 32 consecutive elements (two 16-groups) at src, under global scale gb:
+// four words of packed codes (element 0 in the low nibble of word 0) and, in the return
+// value, the two scale bytes (low byte first).
 template <typename T>
-__global__ __launch_bounds__(kQuantThreads) void quantize_kernel(const T* __restrict__ x,
-                                                                 int64_t n_per_mat,
-                                                                 int64_t total_units,
-                                                                 const float* __restrict__ g,
-                                                                 uint8_t* __restrict__ packed,
-                                                                 uint8_t* __restrict__ scales) {
-  const int64_t u = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x;
-  if (u >= total_units) return;
-  const int64_t e0 = u * 32;               // first element (flat over all matrices)
-  const int64_t b = e0 / n_per_mat;        // matrix index
-  const float gb = g[b];
+__device__ __forceinline__ uint32_t quantize32(const T* __restrict__ src, float gb, uint32_t (&words)[4]) {
   const float six_g = 6.0f * gb;
-  uint32_t out_words[4];
   uint32_t sc_bytes = 0;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     float v[16];
-    Vec8<T>::load(x + e0 + 16 * h, v);
-    Vec8<T>::load(x + e0 + 16 * h + 8, v + 8);
+    Vec8<T>::load(src + 16 * h, v);
+    Vec8<T>::load(src + 16 * h + 8, v + 8);
     float amax = 0.0f;
     bool finite = true;
 #pragma unroll
@@ -171,12 +161,60 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_kernel(const T* __rest
       if (i < 8) w0 |= code << (4 * i);
       else w1 |= code << (4 * (i - 8));
     }
-    out_words[2 * h] = w0;
-    out_words[2 * h + 1] = w1;
+    words[2 * h] = w0;
+    words[2 * h + 1] = w1;
   }
-  *reinterpret_cast<uint4*>(packed + e0 / 2) =
-      make_uint4(out_words[0], out_words[1], out_words[2], out_words[3]);
-  *reinterpret_cast<uint16_t*>(scales + e0 / 16) = (uint16_t)sc_bytes;
+  return sc_bytes;
+}
+
+// One thread per 32 consecutive elements of a row (two 16-groups): reads 32 elements,
+// writes 16 packed bytes and 2 scale bytes (row-major storage).
+template <typename T>
+__global__ __launch_bounds__(kQuantThreads) void quantize_kernel(const T* __restrict__ x,
+                                                                 int64_t n_per_mat,
+                                                                 int64_t total_units,
+                                                                 const float* __restrict__ g,
+                                                                 uint8_t* __restrict__ packed,
+                                                                 uint8_t* __restrict__ scales) {
+  const int64_t u = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x;
+  if (u >= total_units) return;
+  const int64_t e0 = u * 32;               // first element (flat over all matrices)
+  const int64_t b = e0 / n_per_mat;        // matrix index
+  uint32_t w[4];
+  const uint32_t sc = quantize32<T>(x + e0, g[b], w);
+  *reinterpret_cast<uint4*>(packed + e0 / 2) = make_uint4(w[0], w[1], w[2], w[3]);
+  *reinterpret_cast<uint16_t*>(scales + e0 / 16) = (uint16_t)sc;
+}
+
+// The same quantization written straight into the tiled storage the GEMMs read (the layout
+// of nvfp4_weights_tile): thread i is slot i of the scale windows' chunk grid, lane
+// l = 16 g + r of row block rbm (over all matrices; R % 16 == 0), chunk c of the padded
+// range ceil(C / 1024) * 8. It quantizes columns 128 c + 32 g .. +31 of row 16 rb + r and
+// writes their 16 code bytes at slot 16 l of code tile (rbm, c) (for c < ceil(C / 128)) and
+// their two scale bytes at 16 l + 2 (c % 8) of scale tile (rbm, c / 8); columns past C get
+// zero codes and scales.
+template <typename T>
+__global__ __launch_bounds__(kQuantThreads) void quantize_tiled_kernel(const T* __restrict__ x, int R, int C,
+                                                                       int64_t total_slots,
+                                                                       const float* __restrict__ g,
+                                                                       uint8_t* __restrict__ codes,
+                                                                       uint8_t* __restrict__ scales) {
+  const int64_t i = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x;
+  if (i >= total_slots) return;
+  const int nch = (C + 127) / 128, nwin = (C + 1023) / 1024, ncp = 8 * nwin;
+  const int lane = (int)(i & 63);
+  const int64_t tile = i >> 6;
+  const int c = (int)(tile % ncp);
+  const int64_t rbm = tile / ncp;                      // row block over all matrices
+  const int rb_per_mat = R / 16;
+  const int64_t b = rbm / rb_per_mat;
+  const int64_t row = (rbm % rb_per_mat) * 16 + (lane & 15);
+  const int col = 128 * c + 32 * (lane >> 4);
+  uint32_t w[4] = {0u, 0u, 0u, 0u};
+  uint32_t sc = 0;
+  if (col < C) sc = quantize32<T>(x + (b * R + row) * (int64_t)C + col, g[b], w);
+  if (c < nch) *reinterpret_cast<uint4*>(codes + ((rbm * nch + c) << 10) + 16 * lane) = make_uint4(w[0], w[1], w[2], w[3]);
+  *reinterpret_cast<uint16_t*>(scales + ((rbm * nwin + c / 8) << 10) + 16 * lane + 2 * (c % 8)) = (uint16_t)sc;
 }
 
 // FP8 E4M3 round trip of 8 bf16 values per thread.
@@ -279,7 +317,7 @@ size_t quantize_ws_bytes(int64_t B, int64_t R, int64_t C) {
 }
 
 hipError_t launch_quantize(const void* x, bool x_bf16, int64_t B, int64_t R, int64_t C,
-                           const float* g_in, const float* amax_in, uint8_t* packed,
+                           const float* g_in, const float* amax_in, bool tiled, uint8_t* packed,
                            uint8_t* scales, float* g_out, void* ws, hipStream_t stream) {
   const int64_t n = R * C;
   const int nblk = amax_blocks(n);
@@ -295,6 +333,17 @@ hipError_t launch_quantize(const void* x, bool x_bf16, int64_t B, int64_t R, int
   }
   finalize_scale_kernel<<<(unsigned)B, kWave, 0, stream>>>(g_in, amax_in, partial, nblk, 2688.0f,
                                                             g_out);
+  if (tiled) {
+    const int64_t slots = B * (R / 16) * ((C + 1023) / 1024 * 8) * kWave;
+    const int64_t blocks = (slots + kQuantThreads - 1) / kQuantThreads;
+    if (x_bf16)
+      quantize_tiled_kernel<uint16_t><<<(unsigned)blocks, kQuantThreads, 0, stream>>>(
+          static_cast<const uint16_t*>(x), (int)R, (int)C, slots, g_out, packed, scales);
+    else
+      quantize_tiled_kernel<float><<<(unsigned)blocks, kQuantThreads, 0, stream>>>(
+          static_cast<const float*>(x), (int)R, (int)C, slots, g_out, packed, scales);
+    return hipGetLastError();
+  }
   const int64_t units = B * n / 32;
   const int64_t blocks = (units + kQuantThreads - 1) / kQuantThreads;
   if (x_bf16)

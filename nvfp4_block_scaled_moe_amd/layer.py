@@ -38,7 +38,8 @@ class NVFP4Experts:
 
 def quantize_experts(wl: inputs.Workload, device="cuda", experts=None) -> NVFP4Experts:
     """Generate the workload's seeded FP32 expert weights one expert at a time on ``device``
-    and quantize each with the library's nvfp4_quantize; then tile both weight sets."""
+    and quantize each with the library's nvfp4_quantize twice: into the row-major storage
+    (kept for users and checks) and straight into the tiled storage the GEMMs read."""
     E, H, F = wl.E, wl.H, wl.F
     experts = range(E) if experts is None else experts
     u8 = dict(dtype=torch.uint8, device=device)
@@ -47,13 +48,17 @@ def quantize_experts(wl: inputs.Workload, device="cuda", experts=None) -> NVFP4E
         torch.ones((E,), dtype=torch.float32, device=device),
         torch.zeros((E, H, F // 2), **u8), torch.zeros((E, H, F // 16), **u8),
         torch.ones((E,), dtype=torch.float32, device=device))
+    lib = ops._lib.load()
+    w.w13_t = ops.TiledWeights(torch.zeros((E, lib.nvfp4_tiled_codes_bytes(2 * F, H)), **u8),
+                               torch.zeros((E, lib.nvfp4_tiled_scales_bytes(2 * F, H)), **u8), w.w13_g, 2 * F, H)
+    w.w2_t = ops.TiledWeights(torch.zeros((E, lib.nvfp4_tiled_codes_bytes(H, F)), **u8),
+                              torch.zeros((E, lib.nvfp4_tiled_scales_bytes(H, F)), **u8), w.w2_g, H, F)
     for e in experts:
-        ops.nvfp4_quantize(inputs.expert_weight_fp32(wl, "w13", e, device),
-                           out=(w.w13_packed[e], w.w13_scales[e], w.w13_g[e:e + 1]))
-        ops.nvfp4_quantize(inputs.expert_weight_fp32(wl, "w2", e, device),
-                           out=(w.w2_packed[e], w.w2_scales[e], w.w2_g[e:e + 1]))
-    w.w13_t = ops.nvfp4_weights_tile(w.w13_packed, w.w13_scales, w.w13_g)
-    w.w2_t = ops.nvfp4_weights_tile(w.w2_packed, w.w2_scales, w.w2_g)
+        for name, rm, t, gg in (("w13", (w.w13_packed, w.w13_scales), w.w13_t, w.w13_g),
+                                ("w2", (w.w2_packed, w.w2_scales), w.w2_t, w.w2_g)):
+            wf = inputs.expert_weight_fp32(wl, name, e, device)
+            ops.nvfp4_quantize(wf, out=(rm[0][e], rm[1][e], gg[e:e + 1]))
+            ops.nvfp4_quantize(wf, out=(t.codes[e], t.scales[e], gg[e:e + 1]), tiled=True)
     return w
 
 

@@ -8,6 +8,7 @@ computation runs in the library's HIP kernels; a failed call raises NVFP4MoEErro
 from __future__ import annotations
 
 import ctypes
+import math
 from dataclasses import dataclass
 
 import torch
@@ -39,12 +40,15 @@ _DT = {torch.float32: F32, torch.bfloat16: BF16}
 
 
 def nvfp4_quantize(x: torch.Tensor, g: torch.Tensor | None = None, amax: torch.Tensor | None = None,
-                   out: tuple | None = None):
-    """Quantize [R, C] or [B, R, C] float32/bf16 to NVFP4 -> (packed, scales, g[B]).
+                   out: tuple | None = None, tiled: bool = False):
+    """Quantize [R, C] or [B, R, C] float32/bf16 to NVFP4.
 
+    Row-major (default) -> (packed [B, R, C/2], scales [B, R, C/16], g [B]) (the batch dim
+    dropped for a 2-D x); ``tiled`` -> a TiledWeights in the storage moe_grouped_gemm_nvfp4
+    reads, written by the same call (R % 16 == 0).
     ``g``: optional device float[B] global scales; ``amax``: optional device float[B]
     finite max |x| per matrix (used when ``g`` is None); ``out``: optional preallocated
-    (packed [B, R, C/2], scales [B, R, C/16], g [B]) to write into (contiguous views).
+    (packed, scales, g) to write into (contiguous; row-major shapes, or the tiled byte counts).
     """
     _dev(x, g, amax)
     squeeze = x.dim() == 2
@@ -52,18 +56,27 @@ def nvfp4_quantize(x: torch.Tensor, g: torch.Tensor | None = None, amax: torch.T
     x3 = x3.contiguous()
     B, R, C = x3.shape
     lib = _lib.load()
+    if tiled:
+        ncb, nsb = lib.nvfp4_tiled_codes_bytes(R, C), lib.nvfp4_tiled_scales_bytes(R, C)
+        shapes = ((B, ncb), (B, nsb))
+    else:
+        shapes = ((B, R, C // 2), (B, R, C // 16))
     if out is not None:
         packed, scales, g_out = out
         assert packed.is_contiguous() and scales.is_contiguous() and g_out.is_contiguous()
-        assert packed.numel() == B * R * C // 2 and scales.numel() == B * R * C // 16 and g_out.numel() == B
+        assert packed.numel() == math.prod(shapes[0]) and scales.numel() == math.prod(shapes[1])
+        assert g_out.numel() == B
     else:
-        packed = torch.empty((B, R, C // 2), dtype=torch.uint8, device=x.device)
-        scales = torch.empty((B, R, C // 16), dtype=torch.uint8, device=x.device)
+        packed = torch.empty(shapes[0], dtype=torch.uint8, device=x.device)
+        scales = torch.empty(shapes[1], dtype=torch.uint8, device=x.device)
         g_out = torch.empty((B,), dtype=torch.float32, device=x.device)
     ws = _ws(lib.nvfp4_quantize_workspace_size(B, R, C), x.device)
-    st = lib.nvfp4_quantize(_ptr(x3), _DT[x3.dtype], B, R, C, _ptr(g), _ptr(amax), _ptr(packed),
+    layout = _lib.LAYOUT_TILED if tiled else _lib.LAYOUT_ROW_MAJOR
+    st = lib.nvfp4_quantize(_ptr(x3), _DT[x3.dtype], B, R, C, _ptr(g), _ptr(amax), layout, _ptr(packed),
                             _ptr(scales), _ptr(g_out), _ptr(ws), ws.numel(), _stream())
     _lib.check("nvfp4_quantize", st)
+    if tiled:
+        return TiledWeights(packed, scales, g_out, R, C)
     if squeeze and out is None:
         return packed[0], scales[0], g_out
     return packed, scales, g_out

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(_lib.SIGNATURES), "binding signatures out of sync with the header"
     for n in names:
         assert hasattr(lib, n)
-    assert lib.nvfp4moe_abi_version() == 205
+    assert lib.nvfp4moe_abi_version() == 300
 
 
 FAKE = ctypes.c_void_p(1 << 20)      # aligned, never dereferenced: validation fails first
@@ -46,32 +46,47 @@ def _err(st):
 
 def test_quantize_rejects_bad_arguments():
     lib = _lib.load()
-    st, msg = _err(lib.nvfp4_quantize(None, _lib.F32, 1, 4, 32, None, None, FAKE, FAKE, FAKE, FAKE, 1 << 20, None))
+    st, msg = _err(lib.nvfp4_quantize(None, _lib.F32, 1, 4, 32, None, None, 0, FAKE, FAKE, FAKE, FAKE, 1 << 20, None))
     assert st == _lib.ERR_INVALID_ARG and "null" in msg
-    st, msg = _err(lib.nvfp4_quantize(FAKE, _lib.F32, 1, 4, 48, None, None, FAKE, FAKE, FAKE, FAKE, 1 << 20, None))
+    st, msg = _err(lib.nvfp4_quantize(FAKE, _lib.F32, 1, 4, 48, None, None, 0, FAKE, FAKE, FAKE, FAKE, 1 << 20, None))
     assert st == _lib.ERR_INVALID_ARG and "C % 32" in msg
-    st, _ = _err(lib.nvfp4_quantize(FAKE, 7, 1, 4, 32, None, None, FAKE, FAKE, FAKE, FAKE, 1 << 20, None))
+    st, _ = _err(lib.nvfp4_quantize(FAKE, 7, 1, 4, 32, None, None, 0, FAKE, FAKE, FAKE, FAKE, 1 << 20, None))
     assert st == _lib.ERR_INVALID_ARG
-    st, _ = _err(lib.nvfp4_quantize(MISALIGNED, _lib.F32, 1, 4, 32, None, None, FAKE, FAKE, FAKE, FAKE, 1 << 20, None))
+    st, _ = _err(lib.nvfp4_quantize(MISALIGNED, _lib.F32, 1, 4, 32, None, None, 0, FAKE, FAKE, FAKE, FAKE, 1 << 20, None))
     assert st == _lib.ERR_INVALID_ARG
     need = lib.nvfp4_quantize_workspace_size(1, 4, 32)
-    st, msg = _err(lib.nvfp4_quantize(FAKE, _lib.F32, 1, 4, 32, None, None, FAKE, FAKE, FAKE, FAKE, need - 1, None))
+    st, msg = _err(lib.nvfp4_quantize(FAKE, _lib.F32, 1, 4, 32, None, None, 0, FAKE, FAKE, FAKE, FAKE, need - 1, None))
     assert st == _lib.ERR_WORKSPACE and "workspace" in msg
+
+
+def test_quantize_tiled_layout_argument_checks():
+    lib = _lib.load()
+    call = lambda R, layout, sc=FAKE: _err(lib.nvfp4_quantize(FAKE, _lib.F32, 1, R, 64, None, None, layout, FAKE, sc,
+                                                             FAKE, FAKE, 1 << 20, None))
+    st, msg = call(24, _lib.LAYOUT_TILED)
+    assert st == _lib.ERR_INVALID_ARG and "R % 16" in msg
+    st, msg = call(32, 2)
+    assert st == _lib.ERR_INVALID_ARG and "layout" in msg
+    st, msg = call(32, _lib.LAYOUT_TILED, ctypes.c_void_p((1 << 20) + 2))
+    assert st == _lib.ERR_INVALID_ARG and "16-byte" in msg
+    st, _ = _err(lib.nvfp4_quantize_noalloc(FAKE, _lib.F32, 1, 24, 64, None, None, _lib.LAYOUT_TILED, FAKE, FAKE,
+                                            FAKE, None))
+    assert st == _lib.ERR_INVALID_ARG
 
 
 def test_quantize_noalloc_rejects_bad_arguments():
     """Argument checks of the no-allocation quantize: the same as nvfp4_quantize, plus a batch
     whose amax partials exceed the 64 KiB scratch (host-side, before any HIP call)."""
     lib = _lib.load()
-    st, msg = _err(lib.nvfp4_quantize_noalloc(None, _lib.F32, 1, 4, 32, None, None, FAKE, FAKE, FAKE, None))
+    st, msg = _err(lib.nvfp4_quantize_noalloc(None, _lib.F32, 1, 4, 32, None, None, 0, FAKE, FAKE, FAKE, None))
     assert st == _lib.ERR_INVALID_ARG and "null" in msg
-    st, msg = _err(lib.nvfp4_quantize_noalloc(FAKE, _lib.F32, 1, 4, 48, None, None, FAKE, FAKE, FAKE, None))
+    st, msg = _err(lib.nvfp4_quantize_noalloc(FAKE, _lib.F32, 1, 4, 48, None, None, 0, FAKE, FAKE, FAKE, None))
     assert st == _lib.ERR_INVALID_ARG and "C % 32" in msg
-    st, _ = _err(lib.nvfp4_quantize_noalloc(MISALIGNED, _lib.F32, 1, 4, 32, None, None, FAKE, FAKE, FAKE, None))
+    st, _ = _err(lib.nvfp4_quantize_noalloc(MISALIGNED, _lib.F32, 1, 4, 32, None, None, 0, FAKE, FAKE, FAKE, None))
     assert st == _lib.ERR_INVALID_ARG
     assert lib.nvfp4_quantize_workspace_size(16, 4096, 4096) == 65536    # fits exactly
     assert lib.nvfp4_quantize_workspace_size(32, 4096, 4096) > 65536
-    st, msg = _err(lib.nvfp4_quantize_noalloc(FAKE, _lib.F32, 32, 4096, 4096, None, None, FAKE, FAKE, FAKE, None))
+    st, msg = _err(lib.nvfp4_quantize_noalloc(FAKE, _lib.F32, 32, 4096, 4096, None, None, 0, FAKE, FAKE, FAKE, None))
     assert st == _lib.ERR_WORKSPACE and "65536" in msg
 
 

@@ -115,6 +115,33 @@ def test_weights_tile_bit_exact(B, R, C):
     assert (t.R, t.C, t.B) == (R, C, B) and np.array_equal(np_(t.g), np_(g))
 
 
+@pytest.mark.parametrize("B,R,C,dt,gmode", [(1, 16, 32, torch.float32, "dyn"), (2, 48, 160, torch.bfloat16, "dyn"),
+                                             (3, 32, 1056, torch.float32, "static"), (2, 64, 2048, torch.float32, "amax"),
+                                             (4, 256, 6144, torch.bfloat16, "dyn")])
+def test_quantize_tiled_layout_bit_exact(B, R, C, dt, gmode):
+    """nvfp4_quantize with the tiled layout writes exactly the bytes of the row-major quantize
+    followed by the index-by-index tiling transcription (padding zeros past C included), and
+    the row-major codes are the oracle's; NaN/Inf/zero groups included."""
+    say("quantize tiled", B, R, C, dt, gmode)
+    x = torch.stack([_special_matrix(R, C, 500 + 13 * b + C) for b in range(B)]).to(dt)
+    kw = {}
+    if gmode == "static":
+        kw["g"] = torch.tensor([0.01 * (b + 1) for b in range(B)], dtype=torch.float32, device=DEV)
+    elif gmode == "amax":
+        xf = x.float()
+        kw["amax"] = torch.where(xf.isfinite(), xf.abs(), torch.zeros_like(xf)).amax(dim=(1, 2)).to(DEV)
+    p, sc, g = ops.nvfp4_quantize(x.to(DEV), **kw)
+    t = ops.nvfp4_quantize(x.to(DEV), tiled=True, **kw)
+    torch.cuda.synchronize()
+    want_c, want_s = _tile_reference(np_(p), np_(sc))
+    assert np.array_equal(np_(t.codes), want_c)
+    assert np.array_equal(np_(t.scales), want_s)
+    assert torch.equal(t.g, g) and (t.R, t.C, t.B) == (R, C, B)
+    for b in range(B):
+        po, so, go = onv.quantize(x[b].float().numpy(), None if gmode != "static" else np_(kw["g"])[b])
+        assert np.array_equal(np_(p[b]), po) and np.array_equal(np_(sc[b]), so) and np_(g)[b] == go
+
+
 def test_fp8_roundtrip_bit_exact():
     say("fp8 roundtrip")
     x = (inputs.random_fp32((64, 256), 7) * 3).to(torch.bfloat16)

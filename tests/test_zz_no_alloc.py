@@ -32,7 +32,7 @@ def _noalloc(x):
     g = torch.full((B,), float("nan"), dtype=torch.float32, device=DEV)
     lib = _lib.load()
     st = lib.nvfp4_quantize_noalloc(ctypes.c_void_p(x.data_ptr()), _lib.BF16 if x.dtype == torch.bfloat16 else _lib.F32,
-                                    B, R, C, None, None, ctypes.c_void_p(packed.data_ptr()),
+                                    B, R, C, None, None, _lib.LAYOUT_ROW_MAJOR, ctypes.c_void_p(packed.data_ptr()),
                                     ctypes.c_void_p(scales.data_ptr()), ctypes.c_void_p(g.data_ptr()),
                                     ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
     _lib.check("nvfp4_quantize_noalloc", st)
