@@ -12,8 +12,14 @@ HBM roofline (weight+scale+activation bytes per launch / launch time from HIP ev
 recorded on the kernels' stream inside the timed region), and the oracle's CPU rate on a
 bounded sample of the same workload.
 
+The line also carries the workload's token sweep (each token count's layer step replayed
+from a HIP graph after a 1 GiB read that evicts the Infinity Cache: median and p10/p90 of
+the replays) and the box's measured ceilings (a plain read of 4 GiB through torch, and a
+large bf16 torch.mm), each fraction given against both the spec peak and the measured one.
+
 Usage: python bench.py [--steps K] [--warmup W] [--tokens T] [--workload NAME]
-       [--format nvfp4|mxfp4] [--no-cpu-baseline] [--sweep FILE] [--copy-calibration]
+       [--format nvfp4|mxfp4] [--no-cpu-baseline] [--no-sweep] [--no-ceilings]
+       [--sweep FILE] [--copy-calibration]
 """
 from __future__ import annotations
 
@@ -37,8 +43,8 @@ PAGES_DECODE_TFLOPS = (0.8, 55.0)   # RTX PRO 6000 (SM120), FP4, per-expert M=16
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
-    p.add_argument("--steps", type=int, default=20)
-    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", default="decode")
     p.add_argument("--tokens", type=int, default=None)
     p.add_argument("--format", default="nvfp4", choices=["nvfp4", "mxfp4"],
@@ -47,6 +53,10 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--sweep", default=None, help="also write per-T results of the workload's sweep to FILE")
+    p.add_argument("--no-sweep", action="store_true",
+                   help="leave out the cold token sweep that the default line carries")
+    p.add_argument("--no-ceilings", action="store_true",
+                   help="leave out the measured HBM-read and bf16 torch.mm ceilings")
     p.add_argument("--copy-calibration", action="store_true",
                    help="run a plain 1 GiB device copy (for scaling HBM counters) and exit")
     return p.parse_args()
@@ -100,6 +110,7 @@ def main():
         print(json.dumps(dense_line(torch, ops, inputs, wl, args, T)), flush=True)
         return
     res = measure(torch, ops, layer, wl, w, x, lg, T, mode, args.steps, args.warmup)
+    ceil = None if args.no_ceilings else ceilings(torch)
     line = dict(
         metric="MoE NVFP4 grouped-GEMM TFLOPS + weight GB/s vs tokens/expert, % roofline",
         value=round(res["tflops"], 2), unit="TFLOP/s", n_gpus=1, steps=args.steps, warmup=args.warmup,
@@ -115,13 +126,24 @@ def main():
                              "NVFP4 weights decoded exactly to f16, v_mfma_f32_16x16x32_f16, fp32 accumulation")),
         weight_GBps=round(res["weight_gbs"], 1),
         weight_hbm_frac=round(res["weight_gbs"] / HBM_PEAK_GBS, 4),
-        stage_us=res["stage_us"], up_gemm_path=res["up_path"],
+        step_us=res["step_us"], stage_us=res["stage_us"], up_gemm_path=res["up_path"],
         roofline=res.get("roofline"),
         baseline_context=("pages: 0.8-55 TFLOPS for FP4 MoE GEMMs at per-expert M=16-64 (256 experts, "
                           "top-8, 512 concurrent) on RTX PRO 6000 Blackwell SM120; vs_baseline divides by 55"),
     )
     if line["roofline"] is not None:
         line["roofline"]["traffic"] = measured_traffic(wl, T, mx)
+    if ceil is not None:
+        line["measured_ceilings"] = ceil
+        rf = line["roofline"]
+        if rf is not None and rf["unit"] == "GB/s":
+            rf["frac_of_measured_read"] = round(rf["achieved"] / ceil["hbm_read_GBps"], 4)
+        elif rf is not None and rf.get("peak") == BF16_PEAK_TFLOPS:
+            rf["frac_of_measured_bf16_mm"] = round(rf["achieved"] / ceil["bf16_mm_TFLOPs"], 4)
+        line["weight_frac_of_measured_read"] = round(res["weight_gbs"] / ceil["hbm_read_GBps"], 4)
+    if wl.sweep and not args.no_sweep:
+        line["token_sweep_cold"] = token_sweep(torch, ops, layer, inputs, wl, w, mode, dev, args,
+                                               ceil["hbm_read_GBps"] if ceil else None)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(torch, wl, w, x, lg, T, mode, args.cpu_seconds)
     else:
@@ -188,18 +210,23 @@ def layer_work(wl, T, touched, mx=False):
     return flops, w13, w2
 
 
-def measure(torch, ops, layer, wl, w, x, lg, T, mode, steps, warmup, graph=False):
-    """Time `steps` layer forwards; HIP events on the current stream bracket every stage."""
+def pct(vals, q):
+    """q-th percentile (0..100) of a list, linear interpolation."""
+    import numpy as np
+    return float(np.percentile(np.asarray(vals, dtype=np.float64), q))
+
+
+def stats_us(vals_us):
+    return dict(mean=round(sum(vals_us) / len(vals_us), 2), median=round(pct(vals_us, 50), 2),
+                p10=round(pct(vals_us, 10), 2), p90=round(pct(vals_us, 90), 2), n=len(vals_us))
+
+
+def make_step(torch, ops, wl, w, x, lg, T, mode, paths):
+    """One layer forward as a closure; ev (7 events or None) brackets the stages."""
     k = wl.k
     fp8 = wl.act == "fp8"
     S = T * k
-    r = ops.moe_route_permute(lg, k)
-    torch.cuda.synchronize()
-    touched = int(r["n_active"].item())
     mx = mode == MXFP4
-    flops, w13_bytes, w2_bytes = layer_work(wl, T, touched, mx)
-
-    paths = {}
 
     def step(ev=None):
         mark = (lambda i: ev[i].record()) if ev else (lambda i: None)
@@ -246,37 +273,62 @@ def measure(torch, ops, layer, wl, w, x, lg, T, mode, steps, warmup, graph=False
         out = ops.moe_unpermute_reduce(y, rr["slot_to_row"], rr["topk_w"])
         mark(6)
         return out
+    return step
 
+
+def graph_times(torch, step, steps, warm_reps, dev):
+    """Capture one layer step in a HIP graph; per-replay device time (us) warm (back to back)
+    and cold (each replay after a 1 GiB read, outside the timed events, that evicts the 256 MB
+    Infinity Cache, which could otherwise hold a small layer's touched weights between replays;
+    a read leaves clean lines, so no write-back lands in the replay)."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    g.replay()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(warm_reps)]
+    for a, b in ev:
+        a.record()
+        g.replay()
+        b.record()
+    torch.cuda.synchronize()
+    warm = [a.elapsed_time(b) * 1e3 for a, b in ev]
+    scratch = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    sink = torch.empty((), dtype=torch.float32, device=dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for a, b in ev:
+        torch.sum(scratch, dim=0, out=sink)
+        a.record()
+        g.replay()
+        b.record()
+    torch.cuda.synchronize()
+    cold = [a.elapsed_time(b) * 1e3 for a, b in ev]
+    del scratch, sink, g
+    return warm, cold
+
+
+def measure(torch, ops, layer, wl, w, x, lg, T, mode, steps, warmup, graph=False):
+    """Time `steps` eager layer forwards; HIP events on the current stream (the stream every
+    library call is launched on) bracket every stage of every step."""
+    k = wl.k
+    S = T * k
+    r = ops.moe_route_permute(lg, k)
+    torch.cuda.synchronize()
+    touched = int(r["n_active"].item())
+    mx = mode == MXFP4
+    flops, w13_bytes, w2_bytes = layer_work(wl, T, touched, mx)
+    paths = {}
+    step = make_step(torch, ops, wl, w, x, lg, T, mode, paths)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     up_path = paths["up"]
     if graph:
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            step()
-        g.replay()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(steps):
-            g.replay()
-        torch.cuda.synchronize()
-        ms = (time.perf_counter() - t0) * 1e3 / steps
+        warm, cold = graph_times(torch, step, steps, max(5, steps // 2), x.device)
+        ms = sum(warm) / len(warm) / 1e3
+        cold_ms = sum(cold) / len(cold) / 1e3
         stage = None
-        # Cold: before each replay a read of 1 GiB (outside the timed events) evicts the 256 MB
-        # Infinity Cache, which could otherwise hold a small layer's touched weights between
-        # back-to-back replays; a read leaves clean lines, so no write-back lands in the replay.
-        scratch = torch.ones(1 << 28, dtype=torch.float32, device=x.device)
-        sink = torch.empty((), dtype=torch.float32, device=x.device)
-        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-        for i in range(steps):
-            torch.sum(scratch, dim=0, out=sink)
-            ev[i][0].record()
-            g.replay()
-            ev[i][1].record()
-        torch.cuda.synchronize()
-        cold_ms = sum(a.elapsed_time(b) for a, b in ev) / steps
-        del scratch, sink
+        step_us = None
     else:
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(steps)]
         torch.cuda.synchronize()
@@ -286,44 +338,138 @@ def measure(torch, ops, layer, wl, w, x, lg, T, mode, steps, warmup, graph=False
         torch.cuda.synchronize()
         ms = (time.perf_counter() - t0) * 1e3 / steps
         names = ["route_permute", "quantize_x", "up_gate_swiglu", "quantize_h", "down", "unpermute_reduce"]
-        stage = {n: round(1e3 * sum(e[j].elapsed_time(e[j + 1]) for e in evs) / steps, 2)
-                 for j, n in enumerate(names)}
+        per = {n: [1e3 * e[j].elapsed_time(e[j + 1]) for e in evs] for j, n in enumerate(names)}
+        stage = {n: round(sum(v) / len(v), 2) for n, v in per.items()}
+        step_us = stats_us([1e3 * e[0].elapsed_time(e[6]) for e in evs])
     act_in = T * wl.H * (2 if mode == ops.W4A16 else (17 / 32 if mx else 9 / 16))
     h_bytes = S * wl.F * (2 if mode == ops.W4A16 else (17 / 32 if mx else 4))
     up_bytes = w13_bytes + act_in + h_bytes
     up_flops = 2.0 * S * 2 * wl.F * wl.H
     res = dict(ms_per_step=ms, tflops=flops / (ms * 1e-3) / 1e12,
                weight_gbs=(w13_bytes + w2_bytes) / (ms * 1e-3) / 1e9, touched=touched, stage_us=stage,
-               **(dict(cold_ms_per_step=cold_ms, cold_weight_gbs=(w13_bytes + w2_bytes) / (cold_ms * 1e-3) / 1e9)
+               step_us=step_us,
+               **(dict(cold_ms_per_step=cold_ms, cold_weight_gbs=(w13_bytes + w2_bytes) / (cold_ms * 1e-3) / 1e9,
+                       cold_us=stats_us(cold))
                   if graph else {}),
                up_path="mx" if mx else ("mfma" if up_path == ops.PATH_MFMA else "stream"))
     if stage:
-        up_us = stage["up_gate_swiglu"]
+        up = stats_us(per["up_gate_swiglu"])
+        up_us = up["mean"]
+        timing = dict(launch_us=up_us, launch_us_median=up["median"], launch_us_p10=up["p10"],
+                      launch_us_p90=up["p90"], launches=up["n"])
         if mx:
             ach = up_flops / (up_us * 1e-6) / 1e12
             res["roofline"] = dict(
-                bound="mfma", kernel="gemm_mx_kernel (MXFP4 up/gate + SwiGLU)", achieved=round(ach, 1),
-                peak=FP4_PEAK_TFLOPS, unit="TFLOP/s", frac=round(ach / FP4_PEAK_TFLOPS, 4), traffic=None,
-                flops_per_launch=up_flops, launch_us=up_us,
+                bound="mfma", kernel="gemm_mx_kernel (MXFP4 up/gate + SwiGLU, h quantized in the epilogue)",
+                achieved=round(ach, 1), peak=FP4_PEAK_TFLOPS, unit="TFLOP/s", frac=round(ach / FP4_PEAK_TFLOPS, 4),
+                traffic=None, flops_per_launch=up_flops, **timing,
+                timed="HIP events around the moe_grouped_gemm_mxfp4_swiglu_q call: mtile_schedule_kernel + "
+                      "gemm_mx_kernel",
                 flops_note="2*S*2F*H useful flops (rows of ragged m-tiles padded on the GPU are not counted); "
                            "dense FP4 MFMA peak",
                 weight_GBps_up=round(w13_bytes / (up_us * 1e-6) / 1e9, 1))
         elif up_path == ops.PATH_MFMA:
             ach = up_flops / (up_us * 1e-6) / 1e12
             res["roofline"] = dict(
-                bound="mfma", kernel="gemm_stream_kernel large-M (up/gate + SwiGLU)", achieved=round(ach, 1),
+                bound="mfma", kernel="gemm_large_kernel (up/gate + SwiGLU)", achieved=round(ach, 1),
                 peak=BF16_PEAK_TFLOPS, unit="TFLOP/s", frac=round(ach / BF16_PEAK_TFLOPS, 4), traffic=None,
-                flops_per_launch=up_flops, launch_us=up_us,
+                flops_per_launch=up_flops, **timing,
+                timed="HIP events around the moe_grouped_gemm_nvfp4 call: " +
+                      ("act_prep_fp4_kernel" if mode == ops.W4A4 else "act_prep_kernel") + " (also builds the "
+                      "m-tile list) + gemm_large_kernel",
                 flops_note="2*S*2F*H useful flops (rows of ragged m-tiles padded on the GPU are not counted); "
-                           "f16 MFMA peak")
+                           "f16 MFMA peak (the exact NVFP4 decode runs on v_mfma_f32_16x16x32_f16)")
+            if mode == ops.W4A4:
+                res["roofline"]["fp4_peak_frac"] = round(ach / FP4_PEAK_TFLOPS, 4)
         else:
             ach = up_bytes / (up_us * 1e-6) / 1e9
             res["roofline"] = dict(
                 bound="hbm", kernel="gemm_stream_kernel (up/gate + SwiGLU)", achieved=round(ach, 1),
                 peak=HBM_PEAK_GBS, unit="GB/s", frac=round(ach / HBM_PEAK_GBS, 4), traffic=None,
-                bytes_per_launch=int(up_bytes), launch_us=up_us,
+                bytes_per_launch=int(up_bytes), **timing,
+                timed="HIP events around the moe_grouped_gemm_nvfp4 call: " +
+                      ("act_prep_kernel + " if mode == ops.W4A16 else "") + "gemm_stream_kernel",
                 bytes_note="W13 packed+scales of touched experts (9/16 B/weight) + activations in + h out")
     return res
+
+
+def ceilings(torch):
+    """The box's measured ceilings: the best of three plain reads of 4 GiB through torch
+    (a full float32 sum, float32 row sums, a bf16 matrix-vector product; bytes read / call
+    time) and a bf16 torch.mm of 8192 x 8192 x 8192 (hipBLASLt), each timed with HIP events
+    over 10 calls after 3 warm-ups."""
+    dev = "cuda"
+    out = {}
+
+    def timed(fn, reps=10):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) * 1e-3 / reps     # s per call
+    a = torch.ones(1 << 30, dtype=torch.float32, device=dev)          # 4 GiB
+    rates = {"sum_f32": a.numel() * 4 / timed(lambda: a.sum()),
+             "row_sums_f32_[2^20,1024]": a.numel() * 4 / timed(lambda: a.view(1 << 20, 1024).sum(1))}
+    b = a.view(torch.bfloat16).view(65536, 32768)                     # the same 4 GiB as a bf16 matrix
+    v = torch.ones(32768, dtype=torch.bfloat16, device=dev)
+    rates["gemv_bf16_[65536,32768]"] = b.numel() * 2 / timed(lambda: torch.mv(b, v))
+    del a, b, v
+    best = max(rates, key=rates.get)
+    out["hbm_read_GBps"] = round(rates[best] / 1e9, 1)
+    out["hbm_read_kernel"] = f"torch {best} over 4 GiB (best of {', '.join(rates)})"
+    out["hbm_read_all_GBps"] = {k: round(v / 1e9, 1) for k, v in rates.items()}
+    out["hbm_read_frac_of_spec"] = round(rates[best] / 1e9 / HBM_PEAK_GBS, 4)
+    m = 8192
+    x = torch.randn((m, m), dtype=torch.bfloat16, device=dev)
+    y = torch.randn((m, m), dtype=torch.bfloat16, device=dev)
+    t = timed(lambda: torch.mm(x, y))
+    out["bf16_mm_TFLOPs"] = round(2.0 * m ** 3 / t / 1e12, 1)
+    out["bf16_mm_shape"] = f"torch.mm bf16 {m}x{m}x{m}"
+    out["bf16_mm_frac_of_spec"] = round(2.0 * m ** 3 / t / 1e12 / BF16_PEAK_TFLOPS, 4)
+    del x, y
+    torch.cuda.empty_cache()
+    return out
+
+
+def token_sweep(torch, ops, layer, inputs, wl, w, mode, dev, args, read_gbs):
+    """The workload's token sweep, each point's layer step replayed from a HIP graph: cold
+    (after a 1 GiB read) median and p10/p90 over `steps` replays, warm median; weight bytes
+    of the touched experts over the cold median against the 8 TB/s spec (and the measured
+    read ceiling)."""
+    rows = []
+    for Ts in wl.sweep:
+        xs = inputs.activations_bf16(wl, Ts).to(dev)
+        ls = inputs.router_logits(wl, Ts).to(dev)
+        r = ops.moe_route_permute(ls, wl.k)
+        torch.cuda.synchronize()
+        touched = int(r["n_active"].item())
+        flops, w13b, w2b = layer_work(wl, Ts, touched, mode == MXFP4)
+        paths = {}
+        step = make_step(torch, ops, wl, w, xs, ls, Ts, mode, paths)
+        for _ in range(3):
+            step()
+        torch.cuda.synchronize()
+        warm, cold = graph_times(torch, step, args.steps, 20, dev)
+        c = stats_us(cold)
+        gbs = (w13b + w2b) / (c["median"] * 1e-6) / 1e9
+        row = dict(tokens=Ts, tokens_per_expert=round(Ts * wl.k / wl.E, 4), touched_experts=touched,
+                   cold_us_median=c["median"], cold_us_p10=c["p10"], cold_us_p90=c["p90"],
+                   warm_us_median=round(pct(warm, 50), 2), replays=c["n"],
+                   tflops=round(flops / (c["median"] * 1e-6) / 1e12, 2), weight_GBps=round(gbs, 1),
+                   weight_hbm_frac=round(gbs / HBM_PEAK_GBS, 4),
+                   ideal_us=round((w13b + w2b) / (HBM_PEAK_GBS * 1e9) * 1e6, 2))
+        if read_gbs:
+            row["weight_frac_of_measured_read"] = round(gbs / read_gbs, 4)
+        rows.append(row)
+        print(f"[bench] sweep T={Ts}: cold {c['median']:.1f} us (p10 {c['p10']:.1f}, p90 {c['p90']:.1f}), "
+              f"weights {gbs:.0f} GB/s ({gbs / HBM_PEAK_GBS:.3f} of 8 TB/s), warm {row['warm_us_median']:.1f} us",
+              file=sys.stderr, flush=True)
+    return rows
 
 
 def dense_line(torch, ops, inputs, wl, args, M):
@@ -332,7 +478,7 @@ def dense_line(torch, ops, inputs, wl, args, M):
     quantized to NVFP4 before the timed region (the pages compare the GEMMs alone)."""
     dev = "cuda"
     N, K = wl.F, wl.H
-    wt = ops.nvfp4_weights_tile(*ops.nvfp4_quantize(inputs.expert_weight_fp32(wl, "dense", 0, dev).unsqueeze(0)))
+    wt = ops.nvfp4_quantize(inputs.expert_weight_fp32(wl, "dense", 0, dev), tiled=True)
     a = inputs.activations_bf16(wl, M).to(dev)
     aq, as_, ag = ops.nvfp4_quantize(a)
     one = torch.tensor([0, M], dtype=torch.int32, device=dev)
@@ -377,14 +523,17 @@ def dense_line(torch, ops, inputs, wl, args, M):
         config=dict(workload=f"dense NVFP4 GEMM M={M} N={N} K={K}, W4A16 (bf16 activations)", M=M, N=N, K=K,
                     path="mfma" if path16 == ops.PATH_MFMA else "stream"),
         w4a4_tflops=round(tf(t4), 2), w4a4_us=round(t4, 2),
+        w4a4_f16_peak_frac=round(tf(t4) / BF16_PEAK_TFLOPS, 4), w4a4_fp4_peak_frac=round(tf(t4) / FP4_PEAK_TFLOPS, 4),
         torch_mm_bf16_tflops=round(tf(tmm), 2), torch_mm_bf16_us=round(tmm, 2),
         mxfp4_w4a4_tflops=round(tf(tmx), 2), mxfp4_w4a4_us=round(tmx, 2),
         mxfp4_w4a4_fp4_peak_frac=round(tf(tmx) / FP4_PEAK_TFLOPS, 4),
         mxfp8_w8a8_tflops=round(tf(t8), 2), mxfp8_w8a8_us=round(t8, 2),
         mxfp8_w8a8_fp8_peak_frac=round(tf(t8) / FP8_PEAK_TFLOPS, 4),
-        roofline=dict(bound="mfma", kernel="moe_grouped_gemm_nvfp4 call (activation prep + GEMM)",
+        roofline=dict(bound="mfma", kernel="gemm_large_kernel (dense NVFP4 W4A16)",
                       achieved=round(tf(t16), 1), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
-                      frac=round(tf(t16) / BF16_PEAK_TFLOPS, 4), traffic=None),
+                      frac=round(tf(t16) / BF16_PEAK_TFLOPS, 4), traffic=None, launch_us=round(t16, 2),
+                      timed="HIP events around 'steps' back-to-back moe_grouped_gemm_nvfp4 calls (every launch "
+                            "of the call: activation prep with the m-tile list, GEMM, split-K reduce)"),
         baseline_context="pages: 437 TFLOPS FP4 vs 225 TFLOPS BF16 at M=512 on RTX PRO 6000 (SM120)",
         cpu_baseline=None,
     )
