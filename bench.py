@@ -51,6 +51,8 @@ def parse():
                    help="mxfp4: the layer with MXFP4 weights, activations and h (W4A4 on the scaled "
                         "FP4 matrix cores)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--combine", type=int, default=0, choices=[0, 1],
+                   help="1: the down GEMM and the weighted reduce as one call (the combine entry points)")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--sweep", default=None, help="also write per-T results of the workload's sweep to FILE")
     p.add_argument("--no-sweep", action="store_true",
@@ -109,7 +111,7 @@ def main():
     if wl.name == "dense":
         print(json.dumps(dense_line(torch, ops, inputs, wl, args, T)), flush=True)
         return
-    res = measure(torch, ops, layer, wl, w, x, lg, T, mode, args.steps, args.warmup)
+    res = measure(torch, ops, layer, wl, w, x, lg, T, mode, args.steps, args.warmup, combine=bool(args.combine))
     ceil = None if args.no_ceilings else ceilings(torch)
     line = dict(
         metric="MoE NVFP4 grouped-GEMM TFLOPS + weight GB/s vs tokens/expert, % roofline",
@@ -153,7 +155,8 @@ def main():
         for Ts in wl.sweep or (T,):
             xs = inputs.activations_bf16(wl, Ts).to(dev)
             ls = inputs.router_logits(wl, Ts).to(dev)
-            r = measure(torch, ops, layer, wl, w, xs, ls, Ts, mode, max(5, args.steps // 2), 2, graph=True)
+            r = measure(torch, ops, layer, wl, w, xs, ls, Ts, mode, max(5, args.steps // 2), 2, graph=True,
+                        combine=bool(args.combine))
             rows.append(dict(tokens=Ts, tokens_per_expert=Ts * wl.k / wl.E, **{k: v for k, v in r.items()}))
             print(f"[bench] sweep T={Ts}: {r['tflops']:.1f} TFLOP/s, weights {r['weight_gbs']:.0f} GB/s, "
                   f"cold {r['cold_ms_per_step']:.4f} ms ({r['cold_weight_gbs']:.0f} GB/s)",
@@ -221,8 +224,9 @@ def stats_us(vals_us):
                 p10=round(pct(vals_us, 10), 2), p90=round(pct(vals_us, 90), 2), n=len(vals_us))
 
 
-def make_step(torch, ops, wl, w, x, lg, T, mode, paths):
-    """One layer forward as a closure; ev (7 events or None) brackets the stages."""
+def make_step(torch, ops, wl, w, x, lg, T, mode, paths, combine=False):
+    """One layer forward as a closure; ev (7 events or None) brackets the stages (with
+    ``combine`` the down stage holds the weighted reduce and the reduce stage is empty)."""
     k = wl.k
     fp8 = wl.act == "fp8"
     S = T * k
@@ -244,8 +248,13 @@ def make_step(torch, ops, wl, w, x, lg, T, mode, paths):
             mark(3)
             paths["up"] = "mx"
             mark(4)   # h is quantized by the up/gate epilogue
-            y = ops.moe_grouped_gemm_mxfp4(ops.EPI_NONE, hq, hs, w.w2_t, rows=S, out_dtype=torch.float32,
-                                           **common)
+            if combine:
+                out = ops.moe_grouped_gemm_mxfp4_combine(hq, hs, w.w2_t, sorted_slot=rr["sorted_slot"],
+                                                         slot_to_row=rr["slot_to_row"], topk_w=rr["topk_w"],
+                                                         **common)
+            else:
+                y = ops.moe_grouped_gemm_mxfp4(ops.EPI_NONE, hq, hs, w.w2_t, rows=S, out_dtype=torch.float32,
+                                               **common)
         elif mode == ops.W4A16:
             mark(2)
             h = ops.moe_grouped_gemm_nvfp4(ops.W4A16, ops.EPI_SWIGLU, xx, w.w13_t,
@@ -254,8 +263,13 @@ def make_step(torch, ops, wl, w, x, lg, T, mode, paths):
             mark(3)
             paths["up"] = ops.last_dispatch()
             mark(4)
-            y = ops.moe_grouped_gemm_nvfp4(ops.W4A16, ops.EPI_NONE, h, w.w2_t,
-                                           rows=S, out_dtype=torch.float32, **common)
+            if combine:
+                out = ops.moe_grouped_gemm_nvfp4_combine(ops.W4A16, h, w.w2_t, sorted_slot=rr["sorted_slot"],
+                                                         slot_to_row=rr["slot_to_row"], topk_w=rr["topk_w"],
+                                                         **common)
+            else:
+                y = ops.moe_grouped_gemm_nvfp4(ops.W4A16, ops.EPI_NONE, h, w.w2_t,
+                                               rows=S, out_dtype=torch.float32, **common)
         else:
             xq, xs, xg = ops.nvfp4_quantize(xx)
             mark(2)
@@ -267,10 +281,16 @@ def make_step(torch, ops, wl, w, x, lg, T, mode, paths):
             paths["up"] = ops.last_dispatch()
             hq, hs, hg = ops.nvfp4_quantize(h, amax=amax)
             mark(4)
-            y = ops.moe_grouped_gemm_nvfp4(ops.W4A4, ops.EPI_NONE, hq, w.w2_t,
-                                           a_scales=hs, a_g=hg, rows=S, out_dtype=torch.float32, **common)
+            if combine:
+                out = ops.moe_grouped_gemm_nvfp4_combine(ops.W4A4, hq, w.w2_t, sorted_slot=rr["sorted_slot"],
+                                                         slot_to_row=rr["slot_to_row"], topk_w=rr["topk_w"],
+                                                         a_scales=hs, a_g=hg, **common)
+            else:
+                y = ops.moe_grouped_gemm_nvfp4(ops.W4A4, ops.EPI_NONE, hq, w.w2_t,
+                                               a_scales=hs, a_g=hg, rows=S, out_dtype=torch.float32, **common)
         mark(5)
-        out = ops.moe_unpermute_reduce(y, rr["slot_to_row"], rr["topk_w"])
+        if not combine:
+            out = ops.moe_unpermute_reduce(y, rr["slot_to_row"], rr["topk_w"])
         mark(6)
         return out
     return step
@@ -307,7 +327,7 @@ def graph_times(torch, step, steps, warm_reps, dev):
     return warm, cold
 
 
-def measure(torch, ops, layer, wl, w, x, lg, T, mode, steps, warmup, graph=False):
+def measure(torch, ops, layer, wl, w, x, lg, T, mode, steps, warmup, graph=False, combine=False):
     """Time `steps` eager layer forwards; HIP events on the current stream (the stream every
     library call is launched on) bracket every stage of every step."""
     k = wl.k
@@ -318,7 +338,7 @@ def measure(torch, ops, layer, wl, w, x, lg, T, mode, steps, warmup, graph=False
     mx = mode == MXFP4
     flops, w13_bytes, w2_bytes = layer_work(wl, T, touched, mx)
     paths = {}
-    step = make_step(torch, ops, wl, w, x, lg, T, mode, paths)
+    step = make_step(torch, ops, wl, w, x, lg, T, mode, paths, combine)
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
@@ -450,7 +470,7 @@ def token_sweep(torch, ops, layer, inputs, wl, w, mode, dev, args, read_gbs):
         touched = int(r["n_active"].item())
         flops, w13b, w2b = layer_work(wl, Ts, touched, mode == MXFP4)
         paths = {}
-        step = make_step(torch, ops, wl, w, xs, ls, Ts, mode, paths)
+        step = make_step(torch, ops, wl, w, xs, ls, Ts, mode, paths, bool(args.combine))
         for _ in range(3):
             step()
         torch.cuda.synchronize()

@@ -258,6 +258,38 @@ size_t moe_grouped_gemm_workspace_size(nvfp4moe_mode mode, int64_t a_rows, int32
                                        int32_t E, int32_t Nw, int32_t K);
 
 /* ---------------------------------------------------------------------------
+ * moe_grouped_gemm_nvfp4_combine -- the down GEMM and the weighted unpermute-reduce in one
+ * call: per expert e, Y_rows = A_rows . W_e^T * w_g[e] (* a_g[0]) in float32 (as
+ * moe_grouped_gemm_nvfp4 with EPI_NONE and F32 out, rows = T * k, no gather), then
+ *     out[t, :] = bf16( sum_{j<k} topk_w[t, j] * Y[slot_to_row[t*k + j], :] )
+ * with float32 multiply-adds in ascending j (as moe_unpermute_reduce). [P3] "Discovering the
+ * sgl_kernel Alternative" (a fused MoE scatters the expert results back to the tokens).
+ * The reduce runs inside the GEMM: the workgroup that stores the last of a token's k rows of
+ * a column tile sums them (integer completion counters; no floating-point atomics, no
+ * waiting), so out is bit for bit what moe_grouped_gemm_nvfp4 + moe_unpermute_reduce give.
+ * When the call splits K (grids under one workgroup per CU) the reduce runs as a second
+ * kernel of the call instead, with the same result.
+ *   mode, a, a_scales, a_g, w_packed, w_scales, w_g, expert_offsets, active_experts,
+ *   n_active, E, Nw, K    as for moe_grouped_gemm_nvfp4 (a has T * k rows).
+ *   sorted_slot, slot_to_row, topk_w   device, as written by moe_route_permute for T tokens, k.
+ *   T, k        T >= 1, 1 <= k <= min(E, 64), T * k <= 2^24, T * k * Nw < 2^31.
+ *   out         device bf16 [T, Nw], 16-byte aligned.
+ *   ws          moe_grouped_gemm_nvfp4_combine_workspace_size(mode, T, k, E, Nw, K) bytes,
+ *               16-byte aligned (the GEMM's workspace, the float32 Y and the counters).
+ * ------------------------------------------------------------------------- */
+nvfp4moe_status moe_grouped_gemm_nvfp4_combine(nvfp4moe_mode mode, const void* a, const uint8_t* a_scales,
+                                               const float* a_g, const uint8_t* w_packed,
+                                               const uint8_t* w_scales, const float* w_g,
+                                               const int32_t* expert_offsets,
+                                               const int32_t* active_experts, const int32_t* n_active,
+                                               const int32_t* sorted_slot, const int32_t* slot_to_row,
+                                               const float* topk_w, int32_t E, int32_t T, int32_t k,
+                                               int32_t Nw, int32_t K, void* out, void* ws,
+                                               size_t ws_bytes, void* stream);
+size_t moe_grouped_gemm_nvfp4_combine_workspace_size(nvfp4moe_mode mode, int32_t T, int32_t k, int32_t E,
+                                                     int32_t Nw, int32_t K);
+
+/* ---------------------------------------------------------------------------
  * moe_unpermute_reduce -- out[t, :] = bf16( sum_{j<k} topk_w[t, j] * y[slot_to_row[t*k+j], :] )
  * accumulated in float32 in ascending j. [P3] "Discovering the sgl_kernel Alternative"
  * (results scattered back from the experts to the tokens).
@@ -367,6 +399,22 @@ nvfp4moe_status moe_grouped_gemm_mxfp4_swiglu_q(const uint8_t* a, const uint8_t*
                                                 const int32_t* n_active, int32_t E, int32_t rows, int32_t Nw,
                                                 int32_t K, uint8_t* h_packed, uint8_t* h_scales, void* ws,
                                                 size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * moe_grouped_gemm_mxfp4_combine -- the MXFP4 down GEMM (as moe_grouped_gemm_mxfp4 with
+ * EPI_NONE, F32 Y, rows = T * k, no gather) and the weighted unpermute-reduce in one call,
+ * exactly as moe_grouped_gemm_nvfp4_combine: out bf16 [T, Nw] is bit for bit
+ * moe_grouped_gemm_mxfp4 + moe_unpermute_reduce. [P3] "Discovering the sgl_kernel
+ * Alternative". ws: moe_grouped_gemm_mxfp4_combine_workspace_size(T, k, E, Nw, K) bytes.
+ * ------------------------------------------------------------------------- */
+nvfp4moe_status moe_grouped_gemm_mxfp4_combine(const uint8_t* a, const uint8_t* a_scales, const uint8_t* w_packed,
+                                               const uint8_t* w_scales, const int32_t* expert_offsets,
+                                               const int32_t* active_experts, const int32_t* n_active,
+                                               const int32_t* sorted_slot, const int32_t* slot_to_row,
+                                               const float* topk_w, int32_t E, int32_t T, int32_t k,
+                                               int32_t Nw, int32_t K, void* out, void* ws, size_t ws_bytes,
+                                               void* stream);
+size_t moe_grouped_gemm_mxfp4_combine_workspace_size(int32_t T, int32_t k, int32_t E, int32_t Nw, int32_t K);
 
 /* ---------------------------------------------------------------------------
  * MXFP8 (block-scaled FP8): FP8 E4M3 codes, one per byte, with one UE8M0 scale per 32

@@ -39,6 +39,12 @@ SIGNATURES = {
                                       _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _int, _vp, _vp,
                                       _sz, _vp]),
     "moe_grouped_gemm_workspace_size": (_sz, [_int, _i64, _i32, _i32, _i32, _i32]),
+    "moe_grouped_gemm_nvfp4_combine": (_int, [_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                              _i32, _i32, _i32, _i32, _i32, _vp, _vp, _sz, _vp]),
+    "moe_grouped_gemm_nvfp4_combine_workspace_size": (_sz, [_int, _i32, _i32, _i32, _i32, _i32]),
+    "moe_grouped_gemm_mxfp4_combine": (_int, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32,
+                                              _i32, _i32, _vp, _vp, _sz, _vp]),
+    "moe_grouped_gemm_mxfp4_combine_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32]),
     "moe_unpermute_reduce": (_int, [_vp, _int, _vp, _vp, _i32, _i32, _i32, _vp, _vp]),
     "act_fp8_e4m3_roundtrip": (_int, [_vp, _i64, _vp, _vp, _sz, _vp]),
     "act_fp8_e4m3_roundtrip_workspace_size": (_sz, [_i64]),

@@ -111,11 +111,75 @@ hipError_t nvfp4moe::launch_zero_f32(float* p, int n, hipStream_t stream) {
   return hipGetLastError();
 }
 
+namespace {
+__global__ void zero_i32_kernel(int4* p, size_t n4) {
+  const size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n4) p[i] = make_int4(0, 0, 0, 0);
+}
+}  // namespace
+
+// n ints at p (16-byte aligned, n rounded up to a multiple of 4 inside the caller's buffer).
+hipError_t nvfp4moe::launch_zero_i32(int* p, size_t n, hipStream_t stream) {
+  const size_t n4 = (n + 3) / 4;
+  zero_i32_kernel<<<(unsigned)((n4 + 255) / 256), 256, 0, stream>>>(reinterpret_cast<int4*>(p), n4);
+  return hipGetLastError();
+}
+
+namespace {
+// The fused unpermute + weighted reduce of a down-GEMM call: routing of the T tokens and the
+// bf16 [T, Nw] output.
+struct Combine {
+  const int32_t* sorted_slot;
+  const int32_t* slot_to_row;
+  const float* topk_w;
+  int32_t T, k;
+  void* out;
+};
+
+nvfp4moe_status combine_checks(const char* fn, const Combine& c, int32_t E, int32_t Nw) {
+  if (!c.sorted_slot || !c.slot_to_row || !c.topk_w || !c.out)
+    return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: null tensor pointer", fn);
+  if (c.T < 1 || c.k < 1 || c.k > E || c.k > kMaxTopK || (int64_t)c.T * c.k > (1 << 24))
+    return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: need T >= 1, 1 <= k <= min(E, %d), T * k <= 2^24 (T=%d k=%d)", fn,
+                kMaxTopK, c.T, c.k);
+  if ((int64_t)c.T * c.k * Nw >= (int64_t(1) << 31))
+    return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: T * k * Nw must be < 2^31", fn);
+  if (!aligned(c.out, 16)) return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: out must be 16-byte aligned", fn);
+  return NVFP4MOE_OK;
+}
+
+// Workspace added by the combine: the float32 Y [T*k, Nw] and the completion counters.
+size_t combine_ws_bytes(int32_t T, int32_t k, int32_t Nw) {
+  return round_up((size_t)T * k * Nw * 4) + round_up(comb_count_ints(T, Nw) * 4);
+}
+
+// Point g at Y and the counters in `base` (combine_ws_bytes of memory) and enqueue the
+// counter reset; with split K the GEMM writes Y and the reduce kernel runs after it instead.
+hipError_t combine_setup(GemmArgs& g, const Combine& c, char* base, int32_t Nw, hipStream_t s) {
+  g.out = base;
+  g.out_bf16 = 0;
+  g.out_amax = nullptr;
+  if (g.ksplit > 1) return hipSuccess;
+  g.comb_slot = c.sorted_slot;
+  g.comb_s2r = c.slot_to_row;
+  g.comb_w = c.topk_w;
+  g.comb_k = c.k;
+  g.comb_out = static_cast<uint16_t*>(c.out);
+  g.comb_count = reinterpret_cast<int*>(base + round_up((size_t)c.T * c.k * Nw * 4));
+  return launch_zero_i32(g.comb_count, comb_count_ints(c.T, Nw), s);
+}
+
+hipError_t combine_finish(const GemmArgs& g, const Combine& c, int32_t Nw, hipStream_t s) {
+  if (g.comb_slot) return hipSuccess;   // fused into the GEMM
+  return launch_unpermute_reduce(g.out, false, c.slot_to_row, c.topk_w, c.T, c.k, Nw, static_cast<uint16_t*>(c.out), s);
+}
+}  // namespace
+
 extern "C" {
 
 const char* nvfp4moe_last_error(void) { return g_last_error.c_str(); }
 int nvfp4moe_last_dispatch(void) { return g_last_dispatch; }
-int nvfp4moe_abi_version(void) { return 300; }
+int nvfp4moe_abi_version(void) { return 301; }
 
 // ------------------------------------------------------------------ quantize
 size_t nvfp4_quantize_workspace_size(int64_t B, int64_t R, int64_t C) {
@@ -313,17 +377,26 @@ size_t moe_grouped_gemm_workspace_size(nvfp4moe_mode mode, int64_t a_rows, int32
   return gemm_ws_layout(gemm_path(rows, E, Nw), mode, a_rows, rows, E, Nw, K).total;
 }
 
-nvfp4moe_status moe_grouped_gemm_nvfp4(nvfp4moe_mode mode, nvfp4moe_epilogue epi,
-                                       const void* a, const uint8_t* a_scales, const float* a_g,
-                                       int64_t a_rows, const int32_t* gather_index,
-                                       int32_t gather_div, const uint8_t* w_packed,
-                                       const uint8_t* w_scales, const float* w_g,
-                                       const int32_t* expert_offsets,
-                                       const int32_t* active_experts, const int32_t* n_active,
-                                       int32_t E, int32_t rows, int32_t Nw, int32_t K, void* out,
-                                       nvfp4moe_dtype out_dtype, float* out_amax, void* ws,
-                                       size_t ws_bytes, void* stream) {
-  const char* fn = "moe_grouped_gemm_nvfp4";
+size_t moe_grouped_gemm_nvfp4_combine_workspace_size(nvfp4moe_mode mode, int32_t T, int32_t k, int32_t E, int32_t Nw,
+                                                     int32_t K) {
+  if (T < 1 || k < 1 || E < 1 || K < 1 || Nw < 32 || (int64_t)T * k >= (int64_t(1) << 31)) return 0;
+  const int32_t rows = T * k;
+  return gemm_ws_layout(gemm_path(rows, E, Nw), mode, rows, rows, E, Nw, K).total + combine_ws_bytes(T, k, Nw);
+}
+
+}  // extern "C"
+
+namespace {
+nvfp4moe_status grouped_gemm_nvfp4_impl(const char* fn, nvfp4moe_mode mode, nvfp4moe_epilogue epi,
+                                        const void* a, const uint8_t* a_scales, const float* a_g,
+                                        int64_t a_rows, const int32_t* gather_index,
+                                        int32_t gather_div, const uint8_t* w_packed,
+                                        const uint8_t* w_scales, const float* w_g,
+                                        const int32_t* expert_offsets,
+                                        const int32_t* active_experts, const int32_t* n_active,
+                                        int32_t E, int32_t rows, int32_t Nw, int32_t K, void* out,
+                                        nvfp4moe_dtype out_dtype, float* out_amax, void* ws,
+                                        size_t ws_bytes, void* stream, const Combine* comb) {
   if (mode != NVFP4MOE_W4A16 && mode != NVFP4MOE_W4A4)
     return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: bad mode %d", fn, (int)mode);
   if (epi != NVFP4MOE_EPI_NONE && epi != NVFP4MOE_EPI_SWIGLU)
@@ -360,10 +433,10 @@ nvfp4moe_status moe_grouped_gemm_nvfp4(nvfp4moe_mode mode, nvfp4moe_epilogue epi
   if (path == NVFP4MOE_PATH_NONE)
     return fail(NVFP4MOE_ERR_UNSUPPORTED, "%s: the forced MFMA path needs Nw %% 256 == 0 (Nw=%d)", fn, Nw);
   const GemmWs lay = gemm_ws_layout(path, mode, a_rows, rows, E, Nw, K);
-  if (lay.total && (!ws || ws_bytes < lay.total))
-    return fail(NVFP4MOE_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn,
-                lay.total, ws_bytes);
-  if (lay.total && !aligned(ws, 16))
+  const size_t need = lay.total + (comb ? combine_ws_bytes(comb->T, comb->k, Nw) : 0);
+  if (need && (!ws || ws_bytes < need))
+    return fail(NVFP4MOE_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, ws_bytes);
+  if (need && !aligned(ws, 16))
     return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: workspace must be 16-byte aligned", fn);
 
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -388,9 +461,11 @@ nvfp4moe_status moe_grouped_gemm_nvfp4(nvfp4moe_mode mode, nvfp4moe_epilogue epi
   g.out_amax = out_amax;
 
   hipError_t err = hipSuccess;
-  if (out_amax) err = launch_zero_f32(out_amax, 1, s);
-  if (err != hipSuccess) return hip_status(err, fn);
   char* base = static_cast<char*>(ws);
+  g.ksplit = lay.ksplit;
+  if (comb) err = combine_setup(g, *comb, base + lay.total, Nw, s);
+  if (out_amax && err == hipSuccess) err = launch_zero_f32(out_amax, 1, s);
+  if (err != hipSuccess) return hip_status(err, fn);
   if (lay.a16_bytes) {
     g.a16 = reinterpret_cast<_Float16*>(base);
     g.rexp = reinterpret_cast<int*>(base + lay.a16_bytes);
@@ -419,12 +494,46 @@ nvfp4moe_status moe_grouped_gemm_nvfp4(nvfp4moe_mode mode, nvfp4moe_epilogue epi
   }
   if (err != hipSuccess) return hip_status(err, fn);
   g_last_dispatch = path;
-  g.ksplit = lay.ksplit;
   g.partial = lay.partial_bytes
                   ? reinterpret_cast<float*>(base + lay.a16_bytes + lay.rexp_bytes + lay.sched_bytes)
                   : nullptr;
-  if (path == NVFP4MOE_PATH_MFMA) return hip_status(launch_gemm_large(g, lay.max_mtiles, s), fn);
-  return hip_status(launch_gemm_stream(g, s), fn);
+  err = path == NVFP4MOE_PATH_MFMA ? launch_gemm_large(g, lay.max_mtiles, s) : launch_gemm_stream(g, s);
+  if (err == hipSuccess && comb) err = combine_finish(g, *comb, Nw, s);
+  return hip_status(err, fn);
+}
+}  // namespace
+
+extern "C" {
+
+nvfp4moe_status moe_grouped_gemm_nvfp4(nvfp4moe_mode mode, nvfp4moe_epilogue epi,
+                                       const void* a, const uint8_t* a_scales, const float* a_g,
+                                       int64_t a_rows, const int32_t* gather_index,
+                                       int32_t gather_div, const uint8_t* w_packed,
+                                       const uint8_t* w_scales, const float* w_g,
+                                       const int32_t* expert_offsets,
+                                       const int32_t* active_experts, const int32_t* n_active,
+                                       int32_t E, int32_t rows, int32_t Nw, int32_t K, void* out,
+                                       nvfp4moe_dtype out_dtype, float* out_amax, void* ws,
+                                       size_t ws_bytes, void* stream) {
+  return grouped_gemm_nvfp4_impl("moe_grouped_gemm_nvfp4", mode, epi, a, a_scales, a_g, a_rows, gather_index,
+                                 gather_div, w_packed, w_scales, w_g, expert_offsets, active_experts, n_active, E,
+                                 rows, Nw, K, out, out_dtype, out_amax, ws, ws_bytes, stream, nullptr);
+}
+
+nvfp4moe_status moe_grouped_gemm_nvfp4_combine(nvfp4moe_mode mode, const void* a, const uint8_t* a_scales,
+                                               const float* a_g, const uint8_t* w_packed, const uint8_t* w_scales,
+                                               const float* w_g, const int32_t* expert_offsets,
+                                               const int32_t* active_experts, const int32_t* n_active,
+                                               const int32_t* sorted_slot, const int32_t* slot_to_row,
+                                               const float* topk_w, int32_t E, int32_t T, int32_t k, int32_t Nw,
+                                               int32_t K, void* out, void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "moe_grouped_gemm_nvfp4_combine";
+  const Combine c{sorted_slot, slot_to_row, topk_w, T, k, out};
+  const nvfp4moe_status chk = combine_checks(fn, c, E, Nw);
+  if (chk != NVFP4MOE_OK) return chk;
+  return grouped_gemm_nvfp4_impl(fn, mode, NVFP4MOE_EPI_NONE, a, a_scales, a_g, (int64_t)T * k, nullptr, 1, w_packed,
+                                 w_scales, w_g, expert_offsets, active_experts, n_active, E, T * k, Nw, K, out,
+                                 NVFP4MOE_F32, nullptr, ws, ws_bytes, stream, &c);
 }
 
 // ------------------------------------------------------------------ MXFP4
@@ -500,7 +609,8 @@ nvfp4moe_status mx_gemm_call(const char* fn, int bits, nvfp4moe_epilogue epi, co
                              const uint8_t* w_packed, const uint8_t* w_scales, const int32_t* expert_offsets,
                              const int32_t* active_experts, const int32_t* n_active, int32_t E, int32_t rows,
                              int32_t Nw, int32_t K, void* out, nvfp4moe_dtype out_dtype, float* out_amax,
-                             uint8_t* hq_packed, uint8_t* hq_scales, void* ws, size_t ws_bytes, void* stream) {
+                             uint8_t* hq_packed, uint8_t* hq_scales, void* ws, size_t ws_bytes, void* stream,
+                             const Combine* comb = nullptr) {
   const bool qh = hq_packed != nullptr;
   if (epi != NVFP4MOE_EPI_NONE && epi != NVFP4MOE_EPI_SWIGLU)
     return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: bad epilogue %d", fn, (int)epi);
@@ -527,7 +637,8 @@ nvfp4moe_status mx_gemm_call(const char* fn, int bits, nvfp4moe_epilogue epi, co
       (qh ? !aligned(hq_packed, 16) || !aligned(hq_scales, 4) : !aligned(out, out_dtype == NVFP4MOE_F32 ? 4 : 2)))
     return fail(NVFP4MOE_ERR_INVALID_ARG,
                 "%s: a and the tiled weights must be 16-byte aligned, the output to its element", fn);
-  const size_t need = mx_workspace_size(rows, E, Nw, K, bits);
+  const size_t mx_need = mx_workspace_size(rows, E, Nw, K, bits);
+  const size_t need = mx_need + (comb ? combine_ws_bytes(comb->T, comb->k, Nw) : 0);
   if (!ws || ws_bytes < need)
     return fail(NVFP4MOE_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, ws_bytes);
   if (!aligned(ws, 16)) return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: workspace must be 16-byte aligned", fn);
@@ -567,13 +678,15 @@ nvfp4moe_status mx_gemm_call(const char* fn, int bits, nvfp4moe_epilogue epi, co
   if ((int64_t)g.ksplit * rows * Nw >= (int64_t(1) << 31))
     return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: split-K partial sums too large (ksplit %d)", fn, g.ksplit);
   hipError_t err = hipSuccess;
-  if (out_amax) err = launch_zero_f32(out_amax, 1, s);
+  if (comb) err = combine_setup(g, *comb, base + mx_need, Nw, s);
+  if (out_amax && err == hipSuccess) err = launch_zero_f32(out_amax, 1, s);
   if (err != hipSuccess) return hip_status(err, fn);
   const MtileSched sched{expert_offsets, active_experts, n_active, E, mx_rows_per_mtile(bits), max_mtiles,
                          const_cast<int*>(g.sched_e), const_cast<int*>(g.sched_r), const_cast<int*>(g.sched_n)};
   err = launch_mtile_schedule(sched, s);
-  if (err != hipSuccess) return hip_status(err, fn);
-  return hip_status(launch_gemm_mx(g, max_mtiles, bits, s), fn);
+  if (err == hipSuccess) err = launch_gemm_mx(g, max_mtiles, bits, s);
+  if (err == hipSuccess && comb) err = combine_finish(g, *comb, Nw, s);
+  return hip_status(err, fn);
 }
 }  // namespace
 
@@ -587,6 +700,26 @@ nvfp4moe_status moe_grouped_gemm_mxfp4(nvfp4moe_epilogue epi, const uint8_t* a, 
   return mx_gemm_call("moe_grouped_gemm_mxfp4", 4, epi, a, a_scales, a_rows, gather_index, gather_div, w_packed,
                       w_scales, expert_offsets, active_experts, n_active, E, rows, Nw, K, out, out_dtype, out_amax,
                       nullptr, nullptr, ws, ws_bytes, stream);
+}
+
+size_t moe_grouped_gemm_mxfp4_combine_workspace_size(int32_t T, int32_t k, int32_t E, int32_t Nw, int32_t K) {
+  if (T < 1 || k < 1 || E < 1 || K < 32 || Nw < 32 || (int64_t)T * k >= (int64_t(1) << 31)) return 0;
+  return mx_workspace_size(T * k, E, Nw, K, 4) + combine_ws_bytes(T, k, Nw);
+}
+
+nvfp4moe_status moe_grouped_gemm_mxfp4_combine(const uint8_t* a, const uint8_t* a_scales, const uint8_t* w_packed,
+                                               const uint8_t* w_scales, const int32_t* expert_offsets,
+                                               const int32_t* active_experts, const int32_t* n_active,
+                                               const int32_t* sorted_slot, const int32_t* slot_to_row,
+                                               const float* topk_w, int32_t E, int32_t T, int32_t k, int32_t Nw,
+                                               int32_t K, void* out, void* ws, size_t ws_bytes, void* stream) {
+  const char* fn = "moe_grouped_gemm_mxfp4_combine";
+  const Combine c{sorted_slot, slot_to_row, topk_w, T, k, out};
+  const nvfp4moe_status chk = combine_checks(fn, c, E, Nw);
+  if (chk != NVFP4MOE_OK) return chk;
+  return mx_gemm_call(fn, 4, NVFP4MOE_EPI_NONE, a, a_scales, (int64_t)T * k, nullptr, 1, w_packed, w_scales,
+                      expert_offsets, active_experts, n_active, E, T * k, Nw, K, out, NVFP4MOE_F32, nullptr, nullptr,
+                      nullptr, ws, ws_bytes, stream, &c);
 }
 
 nvfp4moe_status moe_grouped_gemm_mxfp4_swiglu_q(const uint8_t* a, const uint8_t* a_scales, int64_t a_rows,

@@ -31,9 +31,19 @@ __device__ __forceinline__ uint32_t ld16(__amdgpu_buffer_rsrc_t r, uint32_t voff
 
 
 // Four consecutive output values at element offset o of p.out (f32, or bf16 rounded to
-// nearest even); returns amax_bits merged with the finite |value|s as written.
+// nearest even); returns amax_bits merged with the finite |value|s as written. The float32 Y
+// of a combine call is stored with device-scope stores (coherent across the XCDs' L2
+// caches without a write-back of the L2), which the fused reduce of another workgroup reads.
 __device__ __forceinline__ uint32_t store4(const GemmArgs& p, size_t o, const float (&v)[4], uint32_t amax_bits) {
-  if (p.out_bf16) {
+  if (p.comb_slot) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) amax_bits = max(amax_bits, finite_abs_bits(v[i]));
+    uint64_t* q = reinterpret_cast<uint64_t*>(static_cast<float*>(p.out) + o);
+    const uint64_t lo = (uint64_t)__float_as_uint(v[0]) | ((uint64_t)__float_as_uint(v[1]) << 32);
+    const uint64_t hi = (uint64_t)__float_as_uint(v[2]) | ((uint64_t)__float_as_uint(v[3]) << 32);
+    __hip_atomic_store(q, lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(q + 1, hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  } else if (p.out_bf16) {
     uint32_t b[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -123,6 +133,78 @@ __device__ __forceinline__ uint32_t store_tile(const GemmArgs& p, const f32x4 (&
   int pexps[TBM];
   row_exponents<TBM>(p, tc, M, r0, row_exp, lane, pexps);
   return store_tile_exp<RBW, TBM, SWIGLU>(p, acc, tc, ntb, M, r0, alpha, pexps, blkrow, lane, amax_bits);
+}
+
+// Fused unpermute + weighted top-k reduce at the end of a down-GEMM tile (the scatter back
+// from the experts to the tokens of a fused MoE: "The 2x Gap: Diagnosing Suboptimal FP4 GEMM
+// Kernels on Blackwell SM120", section "Discovering the sgl_kernel Alternative").
+// The workgroup (NT threads, all of them calling) has stored float32 Y rows [row0, row0 +
+// nrows) x columns [col0, col0 + ncols) (ncols % 4 == 0, nrows <= kCombMaxRows) into p.out
+// with device-scope stores (store4). For each of its rows it bumps the integer counter of
+// (token of the row's slot, column tile); the workgroup whose bump brings a token's counter
+// to k has all k rows of that token for this column tile in memory, and it writes
+//     comb_out[t, c] = bf16( sum_{j<k} w[t, j] * Y[slot_to_row[t*k + j], c] )
+// with float32 fused multiply-adds in ascending j: the arithmetic of the unpermute-reduce
+// kernel, so the bits do not depend on which workgroup finishes a token last.
+// Ordering without cache flushes: every wave waits for its own device-scope Y stores to
+// complete (vmcnt 0) before the barrier that precedes the bumps, and the finishing workgroup
+// reads Y with device-scope loads, issued after the barrier that follows the bump it observed.
+// (A release/acquire fence at device scope would write back and invalidate the whole L2 of the
+// XCD at every tile: measured 7x slower.) No workgroup ever waits for another.
+constexpr int kCombMaxRows = 128;
+constexpr int kCombBatch = 8;
+template <int NT>
+__device__ __forceinline__ void combine_tile(const GemmArgs& p, int row0, int nrows, int col0, int ncols) {
+  __shared__ int tok[kCombMaxRows];
+  __shared__ int ntok;
+  const int tid = threadIdx.x;
+  const int k = p.comb_k, Nw = p.Nw;
+  const int stride = Nw >> 5, ctile = col0 >> 5;
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): this wave's Y stores have completed
+  if (tid == 0) ntok = 0;
+  __syncthreads();
+  for (int i = tid; i < nrows; i += NT) {
+    const int t = p.comb_slot[row0 + i] / k;
+    const int old = __hip_atomic_fetch_add(p.comb_count + (size_t)t * stride + ctile, 1, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+    if (old == k - 1) tok[atomicAdd(&ntok, 1)] = t;
+  }
+  __syncthreads();
+  const int n = ntok;
+  if (n == 0) return;
+  const float* y = static_cast<const float*>(p.out);
+  const int c4 = ncols >> 2;
+  for (int i = tid; i < n * c4; i += NT) {
+    const int t = tok[i / c4];
+    const int c = col0 + 4 * (i - (i / c4) * c4);
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+    // The rows of up to kCombBatch slots are requested before the first of them is summed
+    // (their latencies overlap); the sum itself stays in ascending j.
+    for (int j0 = 0; j0 < k; j0 += kCombBatch) {
+      uint64_t lo[kCombBatch], hi[kCombBatch];
+      float w[kCombBatch];
+#pragma unroll
+      for (int j = 0; j < kCombBatch; ++j) {
+        const bool in = j0 + j < k;
+        const size_t row = in ? (size_t)p.comb_s2r[(size_t)t * k + j0 + j] : 0;
+        w[j] = in ? p.comb_w[(size_t)t * k + j0 + j] : 0.f;
+        const uint64_t* q = reinterpret_cast<const uint64_t*>(y + row * Nw + c);
+        lo[j] = in ? __hip_atomic_load(q, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
+        hi[j] = in ? __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0;
+      }
+#pragma unroll
+      for (int j = 0; j < kCombBatch; ++j) {
+        if (j0 + j < k) {
+          a0 = fmaf(w[j], __uint_as_float((uint32_t)lo[j]), a0);
+          a1 = fmaf(w[j], __uint_as_float((uint32_t)(lo[j] >> 32)), a1);
+          a2 = fmaf(w[j], __uint_as_float((uint32_t)hi[j]), a2);
+          a3 = fmaf(w[j], __uint_as_float((uint32_t)(hi[j] >> 32)), a3);
+        }
+      }
+    }
+    *reinterpret_cast<uint2*>(p.comb_out + (size_t)t * Nw + c) =
+        make_uint2(f32_to_bf16(a0) | (f32_to_bf16(a1) << 16), f32_to_bf16(a2) | (f32_to_bf16(a3) << 16));
+  }
 }
 
 // Wave-reduced amax of the tile (finite values only), merged into *out_amax (float bits of

@@ -245,6 +245,8 @@ __global__ __launch_bounds__(WAVES* kWave, 2) void gemm_large_kernel(const GemmA
     }
     uint32_t amax_bits = store_tile<kRBW, kTBM, SWIGLU>(p, acc, tc, ntb, M, r0, alpha, !p.w4a4, blkrow, lane, 0u);
     merge_amax(p.out_amax, amax_bits, lane);
+    if (!SWIGLU && p.comb_slot)   // the weighted reduce of the tokens this tile completes
+      combine_tile<NT>(p, r0 + tc, min(16 * ntb, M - tc), nb * WAVES * 16 * kRBW, WAVES * 16 * kRBW);
   };
   if (ntb > 4) body(Int<8>{});
   else if (ntb > 2) body(Int<4>{});

@@ -433,6 +433,8 @@ __global__ __launch_bounds__(kMxWaves* kWave) void gemm_mx_kernel(const GemmArgs
   }
   const uint32_t amax_bits = store_tile<kMxRBW, TBM, SWIGLU>(p, acc, tc, ntb, M, r0, 1.0f, false, blkrow, lane, 0u);
   merge_amax(p.out_amax, amax_bits, lane);
+  if (!SWIGLU && p.comb_slot)   // the weighted reduce of the tokens this tile completes
+    combine_tile<NT>(p, r0 + tc, min(16 * ntb, M - tc), nb * kMxWaves * 16 * kMxRBW, kMxWaves * 16 * kMxRBW);
 }
 
 }  // namespace

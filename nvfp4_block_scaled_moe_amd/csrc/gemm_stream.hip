@@ -31,7 +31,9 @@
 //     the 32x16 B operand, FP32 accumulation in registers over all of K. Experts with more
 //     than 32 rows are handled in further 32-row passes.
 //   * Epilogue per wave: float32 global scales (w_g; a_g for W4A4, or the power-of-two
-//     row scale of the f16 activations), SwiGLU when asked, 8- or 16-byte stores.
+//     row scale of the f16 activations), SwiGLU when asked, 8- or 16-byte stores; for the
+//     down GEMM of a combine call, the weighted reduce of the tokens the tile completes
+//     (combine_tile in gemm_common.h).
 //   * Tiles are numbered expert-major and handed out XCD-major (workgroup i runs on XCD
 //     i mod 8), so the tiles of one expert, which share its activation rows, share an L2.
 #include <cstdio>
@@ -403,6 +405,8 @@ __global__ __launch_bounds__(WAVES* kWave) void gemm_stream_kernel(const GemmArg
       }
     } else {
       amax_bits = store_tile_exp<RBW, TBM, SWIGLU>(p, acc, tc, TBM, M, r0, alpha, pexps, blk, lane, amax_bits);
+      if (!SWIGLU && p.comb_slot)   // the weighted reduce of the tokens this pass completes
+        combine_tile<NT>(p, r0 + tc, min(TROWS, M - tc), nb * WAVES * 16 * RBW, WAVES * 16 * RBW);
     }
     if (!has_next) break;
 #pragma unroll

@@ -81,7 +81,17 @@ struct GemmArgs {
   int unit_alpha;                  // MXFP4: no per-tensor scales (alpha = 1 in the split-K reduce)
   uint8_t* hq_packed;              // MXFP4 SwiGLU: h quantized in the epilogue, [rows, Nw/4] codes
   uint8_t* hq_scales;              //   and [rows, Nw/64] UE8M0 scales (null: out as usual)
+  // Fused unpermute + weighted reduce (down GEMM, EPI_NONE, float32 out = Y, no split K):
+  const int* comb_slot;            // [rows] sorted_slot: GEMM row -> slot (null: no combine)
+  const int* comb_s2r;             // [T * k] slot_to_row
+  const float* comb_w;             // [T * k] top-k weights
+  int* comb_count;                 // [T * Nw/32] completion counters, zero before the GEMM
+  uint16_t* comb_out;              // bf16 [T, Nw]
+  int comb_k;
 };
+// Completion counters of the fused combine: one int per (token, 32 columns), zeroed.
+inline size_t comb_count_ints(int T, int Nw) { return (size_t)T * (size_t)(Nw / 32); }
+hipError_t launch_zero_i32(int* p, size_t n, hipStream_t stream);
 hipError_t launch_gemm_stream(const GemmArgs& a, hipStream_t stream);
 // K slices for the small-M path from the sizes alone (1 unless the grid is tiny).
 int stream_ksplit(int rows, int E, int Nw, int K);

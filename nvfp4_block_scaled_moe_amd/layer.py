@@ -63,10 +63,12 @@ def quantize_experts(wl: inputs.Workload, device="cuda", experts=None) -> NVFP4E
 
 
 def moe_forward(x: torch.Tensor, logits: torch.Tensor, k: int, w: NVFP4Experts, mode: int = ops.W4A16,
-                fp8_acts: bool = False, keep: bool = False):
+                fp8_acts: bool = False, keep: bool = False, combine: bool = False):
     """One MoE layer forward. ``x`` bf16 [T, H]; ``logits`` f32 [T, E].
 
-    Returns the bf16 output [T, H]; with ``keep`` a dict of every stage's tensors.
+    Returns the bf16 output [T, H]; with ``keep`` a dict of every stage's tensors. With
+    ``combine`` the down GEMM and the weighted reduce run as one call
+    (moe_grouped_gemm_nvfp4_combine; same output bits, no Y in the stages).
     """
     st = {}
     if fp8_acts:
@@ -82,8 +84,12 @@ def moe_forward(x: torch.Tensor, logits: torch.Tensor, k: int, w: NVFP4Experts, 
         h = ops.moe_grouped_gemm_nvfp4(ops.W4A16, ops.EPI_SWIGLU, x, w.w13_t,
                                        gather_index=r["sorted_slot"], gather_div=k, rows=S,
                                        out_dtype=torch.bfloat16, **common)
-        y = ops.moe_grouped_gemm_nvfp4(ops.W4A16, ops.EPI_NONE, h, w.w2_t,
-                                       rows=S, out_dtype=torch.float32, **common)
+        if combine:
+            out = ops.moe_grouped_gemm_nvfp4_combine(ops.W4A16, h, w.w2_t, sorted_slot=r["sorted_slot"],
+                                                     slot_to_row=r["slot_to_row"], topk_w=r["topk_w"], **common)
+        else:
+            y = ops.moe_grouped_gemm_nvfp4(ops.W4A16, ops.EPI_NONE, h, w.w2_t,
+                                           rows=S, out_dtype=torch.float32, **common)
     else:
         xq, xs, xg = ops.nvfp4_quantize(x)
         st.update(xq=xq, xs=xs, xg=xg)
@@ -93,11 +99,17 @@ def moe_forward(x: torch.Tensor, logits: torch.Tensor, k: int, w: NVFP4Experts, 
                                              want_amax=True, **common)
         hq, hs, hg = ops.nvfp4_quantize(h, amax=amax)
         st.update(h_amax=amax, hq=hq, hs=hs, hg=hg)
-        y = ops.moe_grouped_gemm_nvfp4(ops.W4A4, ops.EPI_NONE, hq, w.w2_t,
-                                       a_scales=hs, a_g=hg, rows=S, out_dtype=torch.float32, **common)
-    out = ops.moe_unpermute_reduce(y, r["slot_to_row"], r["topk_w"])
+        if combine:
+            out = ops.moe_grouped_gemm_nvfp4_combine(ops.W4A4, hq, w.w2_t, sorted_slot=r["sorted_slot"],
+                                                     slot_to_row=r["slot_to_row"], topk_w=r["topk_w"],
+                                                     a_scales=hs, a_g=hg, **common)
+        else:
+            y = ops.moe_grouped_gemm_nvfp4(ops.W4A4, ops.EPI_NONE, hq, w.w2_t,
+                                           a_scales=hs, a_g=hg, rows=S, out_dtype=torch.float32, **common)
+    if not combine:
+        out = ops.moe_unpermute_reduce(y, r["slot_to_row"], r["topk_w"])
     if keep:
-        st.update(h=h, y=y, out=out)
+        st.update(h=h, out=out, **({} if combine else dict(y=y)))
         return out, st
     return out
 
@@ -138,7 +150,7 @@ def quantize_experts_mxfp4(wl: inputs.Workload, device="cuda") -> MXFP4Experts:
 
 
 def moe_forward_mxfp4(x: torch.Tensor, logits: torch.Tensor, k: int, w: MXFP4Experts,
-                      keep: bool = False):
+                      keep: bool = False, combine: bool = False):
     """One MoE layer forward in MXFP4 W4A4: token rows and h are MXFP4-quantized (one UE8M0
     scale per 32 elements, no per-tensor scale, so the up/gate GEMM's epilogue writes h as
     MXFP4 directly); both GEMMs run on the scaled FP4 matrix cores. ``x`` bf16 [T, H];
@@ -152,9 +164,13 @@ def moe_forward_mxfp4(x: torch.Tensor, logits: torch.Tensor, k: int, w: MXFP4Exp
     xq, xs = ops.mxfp4_quantize(x)
     hq, hs = ops.moe_grouped_gemm_mxfp4_swiglu_q(xq, xs, w.w13_t, gather_index=r["sorted_slot"],
                                                  gather_div=k, rows=S, **common)
-    y = ops.moe_grouped_gemm_mxfp4(ops.EPI_NONE, hq, hs, w.w2_t, rows=S, out_dtype=torch.float32, **common)
-    out = ops.moe_unpermute_reduce(y, r["slot_to_row"], r["topk_w"])
+    if combine:
+        out = ops.moe_grouped_gemm_mxfp4_combine(hq, hs, w.w2_t, sorted_slot=r["sorted_slot"],
+                                                 slot_to_row=r["slot_to_row"], topk_w=r["topk_w"], **common)
+    else:
+        y = ops.moe_grouped_gemm_mxfp4(ops.EPI_NONE, hq, hs, w.w2_t, rows=S, out_dtype=torch.float32, **common)
+        out = ops.moe_unpermute_reduce(y, r["slot_to_row"], r["topk_w"])
     if keep:
-        st.update(xq=xq, xs=xs, hq=hq, hs=hs, y=y, out=out)
+        st.update(xq=xq, xs=xs, hq=hq, hs=hs, out=out, **({} if combine else dict(y=y)))
         return out, st
     return out

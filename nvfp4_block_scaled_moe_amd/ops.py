@@ -175,6 +175,30 @@ def moe_grouped_gemm_nvfp4(mode: int, epi: int, a: torch.Tensor, w: TiledWeights
     return (out, amax) if want_amax else out
 
 
+def moe_grouped_gemm_nvfp4_combine(mode: int, a: torch.Tensor, w: TiledWeights, expert_offsets: torch.Tensor,
+                                   active_experts: torch.Tensor, n_active: torch.Tensor, sorted_slot: torch.Tensor,
+                                   slot_to_row: torch.Tensor, topk_w: torch.Tensor, *,
+                                   a_scales: torch.Tensor | None = None, a_g: torch.Tensor | None = None,
+                                   out: torch.Tensor | None = None):
+    """Down GEMM + weighted unpermute-reduce in one call: ``a`` [T*k, K] (bf16, or NVFP4
+    packed for W4A4) in permuted row order, ``w`` E matrices [H, K] (tiled), routing of
+    ``topk_w`` [T, k] tokens -> bf16 out [T, H]."""
+    _dev(a, w.codes, w.scales, w.g, expert_offsets, active_experts, n_active, sorted_slot, slot_to_row, topk_w,
+         a_scales, a_g)
+    E, Nw, K = w.B, w.R, w.C
+    T, k = topk_w.shape
+    if out is None:
+        out = torch.empty((T, Nw), dtype=torch.bfloat16, device=a.device)
+    lib = _lib.load()
+    ws = _ws(lib.moe_grouped_gemm_nvfp4_combine_workspace_size(mode, T, k, E, Nw, K), a.device)
+    st = lib.moe_grouped_gemm_nvfp4_combine(
+        mode, _ptr(a), _ptr(a_scales), _ptr(a_g), _ptr(w.codes), _ptr(w.scales), _ptr(w.g), _ptr(expert_offsets),
+        _ptr(active_experts), _ptr(n_active), _ptr(sorted_slot), _ptr(slot_to_row), _ptr(topk_w.contiguous()),
+        E, T, k, Nw, K, _ptr(out), _ptr(ws), ws.numel(), _stream())
+    _lib.check("moe_grouped_gemm_nvfp4_combine", st)
+    return out
+
+
 def moe_unpermute_reduce(y: torch.Tensor, slot_to_row: torch.Tensor, topk_w: torch.Tensor,
                          out: torch.Tensor | None = None):
     """out[t] = bf16(sum_j topk_w[t, j] * y[slot_to_row[t*k + j]])."""
@@ -277,6 +301,26 @@ def moe_grouped_gemm_mxfp4(epi: int, a: torch.Tensor, a_scales: torch.Tensor, w:
         _ptr(out), _DT[out.dtype], _ptr(amax), _ptr(ws), ws.numel(), _stream())
     _lib.check("moe_grouped_gemm_mxfp4", st)
     return (out, amax) if want_amax else out
+
+
+def moe_grouped_gemm_mxfp4_combine(a: torch.Tensor, a_scales: torch.Tensor, w: MxTiledWeights,
+                                   expert_offsets: torch.Tensor, active_experts: torch.Tensor, n_active: torch.Tensor,
+                                   sorted_slot: torch.Tensor, slot_to_row: torch.Tensor, topk_w: torch.Tensor, *,
+                                   out: torch.Tensor | None = None):
+    """MXFP4 down GEMM + weighted unpermute-reduce in one call -> bf16 out [T, H]."""
+    _dev(a, a_scales, w.codes, w.scales, expert_offsets, active_experts, n_active, sorted_slot, slot_to_row, topk_w)
+    E, Nw, K = w.B, w.R, w.C
+    T, k = topk_w.shape
+    if out is None:
+        out = torch.empty((T, Nw), dtype=torch.bfloat16, device=a.device)
+    lib = _lib.load()
+    ws = _ws(lib.moe_grouped_gemm_mxfp4_combine_workspace_size(T, k, E, Nw, K), a.device)
+    st = lib.moe_grouped_gemm_mxfp4_combine(
+        _ptr(a), _ptr(a_scales), _ptr(w.codes), _ptr(w.scales), _ptr(expert_offsets), _ptr(active_experts),
+        _ptr(n_active), _ptr(sorted_slot), _ptr(slot_to_row), _ptr(topk_w.contiguous()), E, T, k, Nw, K, _ptr(out),
+        _ptr(ws), ws.numel(), _stream())
+    _lib.check("moe_grouped_gemm_mxfp4_combine", st)
+    return out
 
 
 def moe_grouped_gemm_mxfp4_swiglu_q(a: torch.Tensor, a_scales: torch.Tensor, w: MxTiledWeights,
