@@ -50,6 +50,13 @@ __global__ void zero_f32_kernel(float* p, int n) {
   if (i < n) p[i] = 0.0f;
 }
 
+// W4A4 on the large-M path: decode the NVFP4 activation rows in the GEMM's staging instead
+// of reading an f16 copy (NVFP4MOE_LARGE_A4=1; measured slower, off by default).
+bool large_a4_staged() {
+  const char* s = std::getenv("NVFP4MOE_LARGE_A4");
+  return s && s[0] == '1';
+}
+
 // Kernel path override for tests/measurement: NVFP4MOE_FORCE_PATH=stream|mfma.
 int forced_path() {
   const char* s = std::getenv("NVFP4MOE_FORCE_PATH");
@@ -76,8 +83,8 @@ int gemm_path(int32_t rows, int32_t E, int32_t Nw) {
 }
 
 // Workspace layout of moe_grouped_gemm_nvfp4: f16 activations in MFMA operand order and
-// their row exponents (W4A16 on both paths, W4A4 on the MFMA path), and the m-tile
-// schedule of the MFMA path.
+// their row exponents (W4A16 on both paths, W4A4 on the MFMA path unless the GEMM decodes
+// the FP4 rows itself), and the m-tile schedule of the MFMA path.
 struct GemmWs {
   size_t a16_bytes, rexp_bytes, sched_bytes, partial_bytes, total;
   int max_mtiles, ksplit;
@@ -85,7 +92,7 @@ struct GemmWs {
 GemmWs gemm_ws_layout(int path, nvfp4moe_mode mode, int64_t a_rows, int32_t rows, int32_t E, int32_t Nw,
                       int32_t K) {
   GemmWs w{0, 0, 0, 0, 0, 0, 1};
-  if (mode == NVFP4MOE_W4A16 || path == NVFP4MOE_PATH_MFMA) {
+  if (mode == NVFP4MOE_W4A16 || (path == NVFP4MOE_PATH_MFMA && !large_a4_staged())) {
     const size_t K128 = ((size_t)K + 127) / 128 * 128;  // rows padded to whole 128-k chunks
     w.a16_bytes = round_up((size_t)a_rows * K128 * 2);
     w.rexp_bytes = round_up((size_t)a_rows * 4);
@@ -488,7 +495,10 @@ nvfp4moe_status grouped_gemm_nvfp4_impl(const char* fn, nvfp4moe_mode mode, nvfp
     g.a_packed = static_cast<const uint8_t*>(a);
     g.a_scales = a_scales;
     g.a_g = a_g;
-    if (path == NVFP4MOE_PATH_MFMA)
+    g.a4_staged = path == NVFP4MOE_PATH_MFMA && large_a4_staged();
+    if (g.a4_staged)
+      err = launch_mtile_schedule(sched, s);   // the GEMM decodes the FP4 rows itself
+    else if (path == NVFP4MOE_PATH_MFMA)
       err = launch_act_prep_fp4(g.a_packed, a_scales, a_rows, K, const_cast<_Float16*>(g.a16),
                                 const_cast<int*>(g.rexp), sched, s);
   }

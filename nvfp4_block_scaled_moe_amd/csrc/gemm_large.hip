@@ -17,8 +17,13 @@
 //     (hardware FP4 convert, one packed f16 multiply by the block scale) one chunk ahead of
 //     use, interleaved with the MFMAs.
 //   * Activations (B operand): f16 rows in MFMA operand order (bf16 rows scaled per row by a
-//     power of two, or NVFP4 rows decoded exactly), staged per chunk through a three-slot
-//     LDS ring by LDS DMA (16 bytes per thread and round, no registers). Three slots let every wave
+//     power of two, or NVFP4 rows decoded exactly, by the activation prep), staged per chunk
+//     through a three-slot LDS ring by LDS DMA (16 bytes per thread and round, no registers).
+//     Alternatively (a4_staged) the NVFP4 rows themselves (9/16 byte per element instead of 2)
+//     are loaded into registers two chunks ahead and decoded exactly to f16 into the same ring
+//     slots, with no f16 copy written or read: the same bits, measured 3-4% slower at prefill
+//     (the decode and the LDS stores cost more than the copy), so it is not the default.
+//     Three slots let every wave
 //     read the first fragments of chunk c+1 before the barrier that ends chunk c, so no
 //     MFMA waits for LDS after a barrier. XOR-swizzled rows keep the reads conflict free.
 //   * v_mfma_f32_16x16x32_f16, k-step-major: each B fragment read from LDS feeds both
@@ -42,7 +47,7 @@ constexpr int kWin = 8;                    // chunks per scale tile
 constexpr int kTokBytes = 256;             // f16 activations of one row and chunk
 constexpr int kSlot = 16 * kTBM * kTokBytes;
 
-template <int WAVES, int WDEPTH, bool SWIGLU>
+template <int WAVES, int WDEPTH, bool SWIGLU, bool A4>
 __global__ __launch_bounds__(WAVES* kWave, 2) void gemm_large_kernel(const GemmArgs p, int ntiles_n) {
   static_assert(WDEPTH >= 2 && kWin % WDEPTH == 0, "the weight ring is read one chunk ahead; steps pair up");
   constexpr int NT = WAVES * kWave;
@@ -90,7 +95,9 @@ __global__ __launch_bounds__(WAVES* kWave, 2) void gemm_large_kernel(const GemmA
   const uint32_t sbytes = (uint32_t)(Nw / 16) * (uint32_t)nwin * 1024u;
   const __amdgpu_buffer_rsrc_t wr = make_rsrc(p.w_packed + (size_t)e * wbytes, wbytes);
   const __amdgpu_buffer_rsrc_t sr = make_rsrc(p.w_scales + (size_t)e * sbytes, sbytes);
-  const __amdgpu_buffer_rsrc_t ar = make_rsrc(p.a16, (uint32_t)p.a_rows * (uint32_t)K128 * 2u);
+  const __amdgpu_buffer_rsrc_t ar = A4 ? make_rsrc(p.a_packed, (uint32_t)p.a_rows * (uint32_t)(K >> 1))
+                                        : make_rsrc(p.a16, (uint32_t)p.a_rows * (uint32_t)K128 * 2u);
+  const __amdgpu_buffer_rsrc_t asr = make_rsrc(p.a_scales, A4 ? (uint32_t)p.a_rows * (uint32_t)(K >> 4) : 0u);
   const uint32_t wlane = (uint32_t)(blkrow(0) / 16) * (uint32_t)nch * 1024u + 16u * lane;
   const uint32_t slane = (uint32_t)(blkrow(0) / 16) * (uint32_t)nwin * 1024u + 16u * lane;
   uint32_t wsoff[kRBW], ssoff[kRBW];
@@ -120,6 +127,48 @@ __global__ __launch_bounds__(WAVES* kWave, 2) void gemm_large_kernel(const GemmA
       bdst[rr] = (rr * TPR + wave * 4) * kTokBytes;   // wave-uniform; rows < 128 stay in the slot
     }
     static_assert(TPR == 4 * WAVES && RND * TPR <= 16 * kTBM, "4 rows per wave and round, inside one slot");
+    // W4A4: NVFP4 activation rows staged through registers instead: thread -> (row, 32-column
+    // piece ap) of a chunk; its 16 code bytes and 2 scale bytes are loaded one step ahead and
+    // decoded exactly to f16 (as the weights) into the slot, in the same swizzled operand order.
+    constexpr int ATR = NT / 4;                                  // rows per round
+    constexpr int ARND = (16 * NTB + ATR - 1) / ATR;
+    const int ap = tid & 3;
+    uint32_t acsrc[ARND], assrc[ARND];
+    u32x4 acode[2][ARND];   // two staging sets: chunk c in set c & 1, loaded two steps ahead
+    uint32_t ascl[2][ARND];
+    if constexpr (A4) {
+#pragma unroll
+      for (int rr = 0; rr < ARND; ++rr) {
+        const int tk = rr * ATR + (tid >> 2), t = tc + tk;
+        const bool ok = tk < 16 * NTB && t < M;
+        const uint32_t arow = ok ? (uint32_t)(p.gather_index ? p.gather_index[r0 + t] / p.gather_div : r0 + t) : 0u;
+        acsrc[rr] = ok ? arow * (uint32_t)(K >> 1) + 16u * ap : kOOB;
+        assrc[rr] = ok ? arow * (uint32_t)(K >> 4) + 2u * ap : kOOB;
+      }
+    }
+    auto a_load = [&](int set, int c) {   // pieces past K (or the slice) read zero codes and scales
+      const bool in = c < chi && 128 * c + 32 * ap < K;
+#pragma unroll
+      for (int rr = 0; rr < ARND; ++rr) {
+        acode[set][rr] = ld128(ar, in && acsrc[rr] != kOOB ? acsrc[rr] + 64u * c : kOOB, 0);
+        ascl[set][rr] = ld16(asr, in && assrc[rr] != kOOB ? assrc[rr] + 8u * c : kOOB, 0);
+      }
+    };
+    auto a_store = [&](int set, int slot) {
+      unsigned char* base = smem + slot * kSlot;
+#pragma unroll
+      for (int rr = 0; rr < ARND; ++rr) {
+        const int tk = rr * ATR + (tid >> 2);
+        if (tk < 16 * NTB) {
+          f16x2 s0, s1;
+          decode_scale_pair(ascl[set][rr], s0, s1);
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            *reinterpret_cast<f16x8*>(base + tk * kTokBytes + 16 * ((4 * j + ap) ^ (tk & 15))) =
+                decode8(acode[set][rr][j], j < 2 ? s0 : s1);
+        }
+      }
+    };
     auto b_dma = [&](int c, int slot) {
       const bool in = c < chi;
 #pragma unroll
@@ -171,10 +220,21 @@ __global__ __launch_bounds__(WAVES* kWave, 2) void gemm_large_kernel(const GemmA
     // prologue: activations of the first two chunks into slots 0 and 1, weights of the first
     // WDEPTH chunks requested, the first chunk decoded
     s_issue(wlo);
-    b_dma(clo, 0);
+    if constexpr (A4) {   // clo is a multiple of kWin: chunk c uses staging set c & 1 = u & 1
+      a_load(0, clo);
+      a_load(1, clo + 1);
 #pragma unroll
-    for (int d = 0; d < WDEPTH; ++d) w_issue(d, clo + d);
-    b_dma(clo + 1, 1);
+      for (int d = 0; d < WDEPTH; ++d) w_issue(d, clo + d);
+      a_store(0, 0);
+      a_load(0, clo + 2);
+      a_store(1, 1);
+      a_load(1, clo + 3);
+    } else {
+      b_dma(clo, 0);
+#pragma unroll
+      for (int d = 0; d < WDEPTH; ++d) w_issue(d, clo + d);
+      b_dma(clo + 1, 1);
+    }
 #pragma unroll
     for (int b = 0; b < kRBW; ++b) scur[b] = snext[b];
     scales(0);
@@ -199,7 +259,12 @@ __global__ __launch_bounds__(WAVES* kWave, 2) void gemm_large_kernel(const GemmA
           const int d = u % WDEPTH, dn = (u + 1) % WDEPTH;
           const int slot1 = slot == kSlots - 1 ? 0 : slot + 1;
           const int slot2 = slot1 == kSlots - 1 ? 0 : slot1 + 1;
-          b_dma(c + 2, slot2);                     // slot2 was last read in step c-1
+          if constexpr (A4) {                      // slot2 was last read in step c-1
+            a_store(u & 1, slot2);                 // chunk c+2, loaded in step c-2
+            a_load(u & 1, c + 4);
+          } else {
+            b_dma(c + 2, slot2);
+          }
           w_issue(d, c + WDEPTH);                  // ring entry d (chunk c) was decoded last step
           scales(u + 1);
 #pragma unroll
@@ -303,9 +368,9 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const GemmArgs p) {
 
 // m-tiles of bm rows over the active experts (one workgroup, n_active <= 1024):
 
-template <int WAVES, int WDEPTH, bool SWIGLU>
+template <int WAVES, int WDEPTH, bool SWIGLU, bool A4>
 hipError_t launch_cfg(const GemmArgs& a, int max_mtiles, hipStream_t stream) {
-  const auto kern = &gemm_large_kernel<WAVES, WDEPTH, SWIGLU>;
+  const auto kern = &gemm_large_kernel<WAVES, WDEPTH, SWIGLU, A4>;
   const size_t shmem = (size_t)kSlots * kSlot;
   static std::atomic<uint64_t> attr_done{0};
   const hipError_t attr = ensure_dynamic_lds(reinterpret_cast<const void*>(kern), (int)shmem, attr_done);
@@ -322,10 +387,10 @@ hipError_t launch_cfg(const GemmArgs& a, int max_mtiles, hipStream_t stream) {
 
 // Weight ring depth 2: the chunk after next is in flight while a chunk is decoded (a deeper
 // ring does not fit the 256 registers a wave has at two waves per SIMD).
-template <bool SWIGLU>
+template <bool SWIGLU, bool A4>
 hipError_t launch_sw(const GemmArgs& a, int max_mtiles, hipStream_t stream) {
-  if (large_waves(a.rows, a.E, a.Nw) == 4) return launch_cfg<4, 2, SWIGLU>(a, max_mtiles, stream);
-  return launch_cfg<8, 2, SWIGLU>(a, max_mtiles, stream);
+  if (large_waves(a.rows, a.E, a.Nw) == 4) return launch_cfg<4, 2, SWIGLU, A4>(a, max_mtiles, stream);
+  return launch_cfg<8, 2, SWIGLU, A4>(a, max_mtiles, stream);
 }
 
 // Bound on the m-tiles of a call (as sized on the host).
@@ -371,7 +436,9 @@ int large_ksplit(int rows, int E, int Nw, int K) {
 bool large_supports(int Nw) { return Nw % (16 * kRBW * 8) == 0; }
 
 hipError_t launch_gemm_large(const GemmArgs& a, int max_mtiles, hipStream_t stream) {
-  return a.swiglu ? launch_sw<true>(a, max_mtiles, stream) : launch_sw<false>(a, max_mtiles, stream);
+  if (a.w4a4 && a.a4_staged)
+    return a.swiglu ? launch_sw<true, true>(a, max_mtiles, stream) : launch_sw<false, true>(a, max_mtiles, stream);
+  return a.swiglu ? launch_sw<true, false>(a, max_mtiles, stream) : launch_sw<false, false>(a, max_mtiles, stream);
 }
 
 }  // namespace nvfp4moe

@@ -54,6 +54,8 @@ hipError_t launch_act_prep_fp4(const uint8_t* packed, const uint8_t* scales, int
 // ---- grouped GEMM kernels
 struct GemmArgs {
   int w4a4;                        // 0: W4A16 (a16 + rexp), 1: W4A4 (a_packed + a_scales + a_g)
+  int a4_staged;                   // W4A4 on the large-M path: 1 = the GEMM decodes the NVFP4 rows
+                                   // itself, 0 = it reads their f16 copy (a16) from the activation prep
   const _Float16* a16;             // [a_rows, K] f16, row r scaled by 2^-rexp[r]
   const int* rexp;                 // [a_rows]
   const uint8_t* a_packed;         // [a_rows, K/2]

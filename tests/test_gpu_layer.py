@@ -167,6 +167,22 @@ def test_prefill_layer_full_size():
     _check_full_size(inputs.WORKLOADS["prefill"], 8192, ops.W4A4)
 
 
+def test_prefill_layer_fp4_staging_bit_identical(monkeypatch):
+    """The prefill layer (W4A4, large-M path) with the GEMMs decoding the NVFP4 activation rows
+    in their staging gives the same bits as with the f16 copies of the activation prep."""
+    wl = inputs.WORKLOADS["prefill"]
+    say("prefill layer, fp4 staging")
+    w = layer.quantize_experts(wl, DEV)
+    x = inputs.activations_bf16(wl).to(DEV)
+    lg = inputs.router_logits(wl).to(DEV)
+    monkeypatch.delenv("NVFP4MOE_LARGE_A4", raising=False)
+    want = layer.moe_forward(x, lg, wl.k, w, mode=ops.W4A4)
+    monkeypatch.setenv("NVFP4MOE_LARGE_A4", "1")
+    got = layer.moe_forward(x, lg, wl.k, w, mode=ops.W4A4)
+    torch.cuda.synchronize()
+    assert torch.equal(got, want)
+
+
 @pytest.mark.parametrize("mode", [ops.W4A16, ops.W4A4])
 def test_dense_gemm_full_size(mode):
     wl = inputs.WORKLOADS["dense"]

@@ -562,6 +562,30 @@ def test_grouped_gemm_mfma_gather(mode, monkeypatch):
     assert rel_fro(got, want) < 1e-5
 
 
+@pytest.mark.parametrize("waves", ["8", "4"])
+@pytest.mark.parametrize("ksplit", ["1", "2"])
+@pytest.mark.parametrize("counts,K,T,k", [([300, 5, 0, 77], 3168, 250, 2), ([7, 0, 129, 9], 256, None, None)])
+def test_grouped_gemm_mfma_w4a4_fp4_staging(waves, ksplit, counts, K, T, k, monkeypatch):
+    """W4A4 on the large-M path with the NVFP4 activation rows decoded in the GEMM's staging
+    (NVFP4MOE_LARGE_A4=1) instead of an f16 copy: the decoded values are the same exact
+    products in the same accumulation order, so the output is bit-identical to the default
+    path, and within 1e-5 of the oracle; gather, ragged and empty experts, K % 128 != 0."""
+    say("gemm mfma w4a4 fp4 staging", waves, ksplit, counts, K)
+    monkeypatch.setenv("NVFP4MOE_FORCE_PATH", "mfma")
+    monkeypatch.setenv("NVFP4MOE_LARGE_WAVES", waves)
+    monkeypatch.setenv("NVFP4MOE_LARGE_KSPLIT", ksplit)
+    d = _problem(counts, 512, K, seed=77 + int(ksplit), mode=ops.W4A4, T=T, k=k)
+    for epi in (ops.EPI_NONE, ops.EPI_SWIGLU):
+        monkeypatch.delenv("NVFP4MOE_LARGE_A4", raising=False)
+        ref = _run_gemm(d, ops.W4A4, epi, torch.float32)
+        monkeypatch.setenv("NVFP4MOE_LARGE_A4", "1")
+        got = _run_gemm(d, ops.W4A4, epi, torch.float32)
+        assert ops.last_dispatch() == ops.PATH_MFMA
+        assert np.array_equal(got, ref)
+        want = omoe.grouped_gemm(d["A"], d["offsets"], d["W"], "swiglu" if epi else "none")
+        assert rel_fro(got, want) < 1e-5
+
+
 def test_grouped_gemm_path_choice_by_size(monkeypatch):
     """Mean rows per expert >= 64 selects the MFMA path; both paths agree on it."""
     say("gemm path choice")
