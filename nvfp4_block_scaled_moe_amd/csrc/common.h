@@ -142,6 +142,14 @@ template <typename T>
 __device__ __forceinline__ T ld_const(const T* p, int64_t i) {
   return ((const __attribute__((address_space(4))) T*)p)[i];
 }
+// A pointer that is the same in every lane (e.g. read from LDS) moved to scalar registers.
+template <typename T>
+__device__ __forceinline__ T* uniform_ptr(T* p) {
+  const uint64_t v = reinterpret_cast<uint64_t>(p);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return reinterpret_cast<T*>(((uint64_t)hi << 32) | lo);
+}
 
 // ------------------------------------------------------------------ wave helpers
 __device__ __forceinline__ float wave_max(float v) {
