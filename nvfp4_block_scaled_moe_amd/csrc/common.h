@@ -47,6 +47,13 @@ __device__ __forceinline__ uint32_t f32_to_bf16(float f) {
   u += 0x7fffu + ((u >> 16) & 1u);
   return u >> 16;
 }
+// bf16 bits of a (low half) and b (high half) by the hardware pack: rounded to nearest even,
+// the same bits as f32_to_bf16 for every float but NaN (which stays a NaN).
+__device__ __forceinline__ uint32_t bf16x2(float a, float b) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  const bf16x2_t r = {(__bf16)a, (__bf16)b};
+  return __builtin_bit_cast(uint32_t, r);
+}
 
 // ------------------------------------------------------------------ E4M3
 // E4M3FN byte -> float32 (exact; NaN for 0x7F/0xFF) with the hardware OCP FP8 convert.
@@ -74,6 +81,12 @@ __device__ __forceinline__ uint32_t e2m1_rne_mag(float x) {
   return (uint32_t)(x > 0.25f) + (uint32_t)(x >= 0.75f) + (uint32_t)(x > 1.25f) +
          (uint32_t)(x >= 1.75f) + (uint32_t)(x > 2.5f) + (uint32_t)(x >= 3.5f) +
          (uint32_t)(x > 5.0f);
+}
+// E2M1 codes (sign in bit 3) of a (bits 0-3) and b (bits 4-7), rounded to nearest even and
+// saturating at 6, by the hardware converter with scale 1: for every finite x its code is
+// sign(x) << 3 | e2m1_rne_mag(|x|) (the same bits, compared over all float bit patterns).
+__device__ __forceinline__ uint32_t e2m1_pk(float a, float b) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, a, b, 1.0f, 0);
 }
 
 // ------------------------------------------------------------------ MXFP4 groups
@@ -111,6 +124,12 @@ __device__ __forceinline__ uint32_t mx_code(float v, uint32_t key, int e) {
   if (key == 0xFFFFFFFFu) return 0u;
   const uint32_t sign = (__float_as_uint(v) >> 31) << 3;
   return sign | (key != 0u ? e2m1_rne_mag(ldexpf(fabsf(v), -e)) : 0u);
+}
+// The codes of two elements of one group, v0 in bits 0-3 and v1 in bits 4-7 (the same bits as
+// mx_code: in an all-zero group the values are +-0, whose codes are their sign bits).
+__device__ __forceinline__ uint32_t mx_code2(float v0, float v1, uint32_t key, int e) {
+  if (key == 0xFFFFFFFFu) return 0u;
+  return e2m1_pk(ldexpf(v0, -e), ldexpf(v1, -e));
 }
 
 // ------------------------------------------------------------------ NVFP4 -> f16

@@ -35,33 +35,45 @@ __device__ __forceinline__ uint32_t ld16(__amdgpu_buffer_rsrc_t r, uint32_t voff
 // of a combine call is stored with device-scope stores (coherent across the XCDs' L2
 // caches without a write-back of the L2), which the fused reduce of another workgroup reads.
 __device__ __forceinline__ uint32_t store4(const GemmArgs& p, size_t o, const float (&v)[4], uint32_t amax_bits) {
+  const bool amax = p.out_amax != nullptr;   // the |value| bits are only gathered when asked for
   if (p.comb_slot) {
+    if (amax) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) amax_bits = max(amax_bits, finite_abs_bits(v[i]));
+      for (int i = 0; i < 4; ++i) amax_bits = max(amax_bits, finite_abs_bits(v[i]));
+    }
     uint64_t* q = reinterpret_cast<uint64_t*>(static_cast<float*>(p.out) + o);
     const uint64_t lo = (uint64_t)__float_as_uint(v[0]) | ((uint64_t)__float_as_uint(v[1]) << 32);
     const uint64_t hi = (uint64_t)__float_as_uint(v[2]) | ((uint64_t)__float_as_uint(v[3]) << 32);
     __hip_atomic_store(q, lo, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_store(q + 1, hi, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   } else if (p.out_bf16) {
-    uint32_t b[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      b[i] = f32_to_bf16(v[i]);
-      amax_bits = max(amax_bits, finite_abs_bits(__uint_as_float(b[i] << 16)));
+    const uint32_t b01 = bf16x2(v[0], v[1]), b23 = bf16x2(v[2], v[3]);
+    if (amax) {
+      amax_bits = max(amax_bits, finite_abs_bits(__uint_as_float(b01 << 16)));
+      amax_bits = max(amax_bits, finite_abs_bits(__uint_as_float(b01 & 0xffff0000u)));
+      amax_bits = max(amax_bits, finite_abs_bits(__uint_as_float(b23 << 16)));
+      amax_bits = max(amax_bits, finite_abs_bits(__uint_as_float(b23 & 0xffff0000u)));
     }
-    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + o) = make_uint2(b[0] | (b[1] << 16), b[2] | (b[3] << 16));
+    *reinterpret_cast<uint2*>(static_cast<uint16_t*>(p.out) + o) = make_uint2(b01, b23);
   } else {
+    if (amax) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) amax_bits = max(amax_bits, finite_abs_bits(v[i]));
+      for (int i = 0; i < 4; ++i) amax_bits = max(amax_bits, finite_abs_bits(v[i]));
+    }
     *reinterpret_cast<float4*>(static_cast<float*>(p.out) + o) = make_float4(v[0], v[1], v[2], v[3]);
   }
   return amax_bits;
 }
 
 // silu(gate) * up, the SwiGLU of one output element (shared by every epilogue so that
-// equal inputs give equal bits).
-__device__ __forceinline__ float swiglu1(float gv, float uv) { return gv / (1.0f + expf(-gv)) * uv; }
+// equal inputs give equal bits): gate / (1 + e^-gate) * up with the hardware base-2
+// exponential and reciprocal, e^-gate = 2^(-gate log2 e). Relative error below
+// |gate| 2^-24 + 4 ulp (about 1e-6 for |gate| < 16); +-Inf and NaN gates give the values
+// of the exact formula (NaN for -Inf, Inf * up for +Inf).
+__device__ __forceinline__ float swiglu1(float gv, float uv) {
+  const float e = __builtin_amdgcn_exp2f(-1.44269504088896341f * gv);
+  return gv * __builtin_amdgcn_rcpf(1.0f + e) * uv;
+}
 
 // Epilogue of one wave's tile: RBW blocks of 16 weight rows x TBM blocks of 16 GEMM rows,
 // with MFMA 16x16 output layout (lane l holds weight rows 4*(l/16)+i of each block, GEMM
@@ -203,7 +215,7 @@ __device__ __forceinline__ void combine_tile(const GemmArgs& p, int row0, int nr
       }
     }
     *reinterpret_cast<uint2*>(p.comb_out + (size_t)t * Nw + c) =
-        make_uint2(f32_to_bf16(a0) | (f32_to_bf16(a1) << 16), f32_to_bf16(a2) | (f32_to_bf16(a3) << 16));
+        make_uint2(bf16x2(a0, a1), bf16x2(a2, a3));
   }
 }
 

@@ -41,6 +41,11 @@
 //     group's exponent, by the same rule and helpers as the MXFP4 quantizer; the codes and
 //     scales of the workgroup's tile are gathered in LDS and written as 64 contiguous bytes
 //     per row.
+//   * MXFP4 grids are persistent: at most one workgroup per CU (one fits a CU), each walking
+//     its XCD's tile range with a stride. After a tile's main loop the workgroup reads the
+//     next tile's coordinates and requests its scale windows, first weight chunks and first
+//     activation chunks, and only then runs the epilogue, so those loads arrive while the
+//     results are written. MXFP8 keeps one workgroup per tile.
 //   * Small grids split K into slices of whole chunks (partial sums to the workspace, then
 //     the shared fixed-order split-K reduce). A slice may start inside a scale window: the
 //     16 scale bytes of the slice's next 16 chunks are a byte shift of the two windows held
@@ -442,9 +447,7 @@ __global__ __launch_bounds__(kMxWaves* kWave) void gemm_mx_kernel(const GemmArgs
         const uint32_t gk = max(key[tb], xch[((wave ^ 1) * TBM + tb) * 16 + l16]);
         int ex = 0;
         const uint32_t sc = mx_scale(gk, ex);
-        uint32_t q = 0;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) q |= mx_code(h[tb][i], gk, ex) << (4 * i);
+        const uint32_t q = mx_code2(h[tb][0], h[tb][1], gk, ex) | (mx_code2(h[tb][2], h[tb][3], gk, ex) << 8);
         const int tr = 16 * tb + l16;   // row of the m-tile
         *reinterpret_cast<uint16_t*>(qc + tr * 64 + wave * 8 + 2 * g) = (uint16_t)q;
         if ((wave & 1) == 0 && g == 0) qs[tr * 4 + (wave >> 1)] = (unsigned char)sc;

@@ -268,7 +268,7 @@ __global__ __launch_bounds__(kQuantThreads) void mx_quantize_kernel(const T* __r
   const uint32_t s = mx_scale(key, e);
   uint32_t w[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-  for (int i = 0; i < 32; ++i) w[i >> 3] |= mx_code(v[i], key, e) << (4 * (i & 7));
+  for (int i = 0; i < 32; i += 2) w[i >> 3] |= mx_code2(v[i], v[i + 1], key, e) << (4 * (i & 7));
   *reinterpret_cast<uint4*>(packed + e0 / 2) = make_uint4(w[0], w[1], w[2], w[3]);
   scales[u] = (uint8_t)s;
 }

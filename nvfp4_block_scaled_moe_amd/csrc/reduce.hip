@@ -72,7 +72,7 @@ __global__ __launch_bounds__(kRedThreads) void unpermute_reduce_kernel(const voi
   }
   uint32_t o[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) o[i] = f32_to_bf16(acc[2 * i]) | (f32_to_bf16(acc[2 * i + 1]) << 16);
+  for (int i = 0; i < 4; ++i) o[i] = bf16x2(acc[2 * i], acc[2 * i + 1]);
   *reinterpret_cast<uint4*>(out + (size_t)t * H + c) = make_uint4(o[0], o[1], o[2], o[3]);
 }
 

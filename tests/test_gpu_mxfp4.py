@@ -53,6 +53,29 @@ def test_mxfp4_quantize_bit_exact(R, C, dt):
     assert np.array_equal(np_(s), ws)
 
 
+def test_mxfp4_quantize_codes_at_every_rounding_threshold():
+    """E2M1 codes at unit scale on both sides of every E2M1 rounding midpoint (0.25, 0.75,
+    1.25, 1.75, 2.5, 3.5, 5): the 2048 float32 values below and above each midpoint, both
+    signs, plus zeros, subnormals and values up to 8 that saturate at 6. Each group of 32 holds
+    a 4.0, so its scale exponent is 0 and every other code is E2M1 of the value itself."""
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0], np.float32)
+    bits = mids.view(np.uint32).astype(np.int64)[:, None] + np.arange(-2048, 2049, dtype=np.int64)[None, :]
+    vals = bits.astype(np.uint32).view(np.float32).ravel()
+    extra = np.array([0.0, -0.0, 1.4e-45, -1.4e-45, 1e-40, -1e-40, 5.999, 6.0, 6.5, 7.0, 7.999], np.float32)
+    vals = np.concatenate([vals, -vals, extra, -extra])
+    groups = -(-vals.size // 31)
+    groups = -(-groups // 64) * 64                      # 64 groups (2048 columns) per row
+    vals = np.concatenate([vals, np.zeros(groups * 31 - vals.size, np.float32)]).reshape(groups, 31)
+    x = np.concatenate([np.full((groups, 1), 4.0, np.float32), vals], axis=1).reshape(-1, 2048)
+    say("mx quantize thresholds", x.shape)
+    p, s = ops.mxfp4_quantize(torch.from_numpy(x).to(DEV))
+    torch.cuda.synchronize()
+    wp, ws = omx.quantize(x)
+    assert np.all(ws == 127)
+    assert np.array_equal(np_(s), ws)
+    assert np.array_equal(np_(p), wp)
+
+
 # ------------------------------------------------------------------ tiling
 def _mx_tile_reference(packed, scales):
     """Index-by-index transcription of the MX scale tiles (include/nvfp4moe.h)."""
