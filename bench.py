@@ -142,6 +142,8 @@ def main():
             rf["frac_of_measured_read"] = round(rf["achieved"] / ceil["hbm_read_GBps"], 4)
         elif rf is not None and rf.get("peak") == BF16_PEAK_TFLOPS:
             rf["frac_of_measured_bf16_mm"] = round(rf["achieved"] / ceil["bf16_mm_TFLOPs"], 4)
+        elif rf is not None and rf.get("peak") == FP4_PEAK_TFLOPS and ceil.get("mxfp4_scaled_mm_TFLOPs"):
+            rf["frac_of_measured_mxfp4_mm"] = round(rf["achieved"] / ceil["mxfp4_scaled_mm_TFLOPs"], 4)
         line["weight_frac_of_measured_read"] = round(res["weight_gbs"] / ceil["hbm_read_GBps"], 4)
     if wl.sweep and not args.no_sweep:
         line["token_sweep_cold"] = token_sweep(torch, ops, layer, inputs, wl, w, mode, dev, args,
@@ -452,8 +454,41 @@ def ceilings(torch):
     out["bf16_mm_shape"] = f"torch.mm bf16 {m}x{m}x{m}"
     out["bf16_mm_frac_of_spec"] = round(2.0 * m ** 3 / t / 1e12 / BF16_PEAK_TFLOPS, 4)
     del x, y
+    # the vendor library's block-scaled GEMMs of the same shape (torch._scaled_mm -> hipBLASLt)
+    for name, fn in vendor_scaled_mm(torch, m, m, m).items():
+        try:
+            t = timed(fn)
+            out[f"{name}_TFLOPs"] = round(2.0 * m ** 3 / t / 1e12, 1)
+        except Exception as exc:    # not offered by this torch / hipBLASLt build
+            out[f"{name}_TFLOPs"] = None
+            out[f"{name}_error"] = f"{type(exc).__name__}: {str(exc)[:120]}"
+    out["scaled_mm_shape"] = f"torch._scaled_mm {m}x{m}x{m}, bf16 out"
     torch.cuda.empty_cache()
     return out
+
+
+def vendor_scaled_mm(torch, M, N, K, a_codes=None, a_scales=None, w_codes=None, w_scales=None):
+    """torch._scaled_mm calls (hipBLASLt) computing A[M,K] W[N,K]^T in bf16: MXFP4 (E2M1 codes
+    packed two per byte, UE8M0 scales per 32, the quantizer's own row-major layout; random codes
+    unless given) and FP8 E4M3 with per-tensor unit scales. Returns name -> callable."""
+    dev = "cuda"
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    rnd = lambda shape, lo, hi: torch.randint(lo, hi, shape, dtype=torch.uint8, device=dev, generator=g)
+    qa = a_codes if a_codes is not None else rnd((M, K // 2), 0, 256)
+    qw = w_codes if w_codes is not None else rnd((N, K // 2), 0, 256)
+    sa = a_scales if a_scales is not None else rnd((M, K // 32), 120, 130)
+    sw = w_scales if w_scales is not None else rnd((N, K // 32), 120, 130)
+    fa = torch.randn((M, K), device=dev, generator=g).to(torch.float8_e4m3fn)
+    fw = torch.randn((N, K), device=dev, generator=g).to(torch.float8_e4m3fn)
+    one = torch.ones((), device=dev)
+    f4 = torch.float4_e2m1fn_x2
+    e8 = torch.float8_e8m0fnu
+    return {
+        "mxfp4_scaled_mm": lambda: torch._scaled_mm(qa.view(f4), qw.view(f4).t(), scale_a=sa.view(e8),
+                                                    scale_b=sw.view(e8), out_dtype=torch.bfloat16),
+        "fp8_scaled_mm": lambda: torch._scaled_mm(fa, fw.t(), scale_a=one, scale_b=one, out_dtype=torch.bfloat16),
+    }
 
 
 def token_sweep(torch, ops, layer, inputs, wl, w, mode, dev, args, read_gbs):
@@ -527,9 +562,18 @@ def dense_line(torch, ops, inputs, wl, args, M):
                                                   a_g=ag, **common))
     tmm = timed(lambda: torch.mm(a, wbf.t()))
     # the MXFP4 variant of the same GEMM (group-32 UE8M0 scales) on the scaled FP4 matrix cores
-    wmx = ops.mxfp4_weights_tile(*ops.mxfp4_quantize(inputs.expert_weight_fp32(wl, "dense", 0, dev).unsqueeze(0)))
+    wmx_p, wmx_s = ops.mxfp4_quantize(inputs.expert_weight_fp32(wl, "dense", 0, dev))
+    wmx = ops.mxfp4_weights_tile(wmx_p.unsqueeze(0), wmx_s.unsqueeze(0))
     amx, amx_s = ops.mxfp4_quantize(a)
     tmx = timed(lambda: ops.moe_grouped_gemm_mxfp4(ops.EPI_NONE, amx, amx_s, wmx, **common))
+    # the vendor library on the same MXFP4 operands, and FP8 E4M3 per tensor, same shape
+    vendor = {}
+    for name, fn in vendor_scaled_mm(torch, M, N, K, amx, amx_s, wmx_p, wmx_s).items():
+        try:
+            vendor[f"{name}_us"] = round(timed(fn), 2)
+        except Exception as exc:
+            vendor[f"{name}_us"] = None
+            vendor[f"{name}_error"] = f"{type(exc).__name__}: {str(exc)[:120]}"
     # block-scaled FP8 (MXFP8: E4M3 elements, UE8M0 per 32) on the scaled FP8 matrix cores
     w8 = ops.mxfp8_weights_tile(*ops.mxfp8_quantize(inputs.expert_weight_fp32(wl, "dense", 0, dev).unsqueeze(0)))
     a8, a8_s = ops.mxfp8_quantize(a)
@@ -549,6 +593,7 @@ def dense_line(torch, ops, inputs, wl, args, M):
         mxfp4_w4a4_fp4_peak_frac=round(tf(tmx) / FP4_PEAK_TFLOPS, 4),
         mxfp8_w8a8_tflops=round(tf(t8), 2), mxfp8_w8a8_us=round(t8, 2),
         mxfp8_w8a8_fp8_peak_frac=round(tf(t8) / FP8_PEAK_TFLOPS, 4),
+        **vendor,
         roofline=dict(bound="mfma", kernel="gemm_large_kernel (dense NVFP4 W4A16)",
                       achieved=round(tf(t16), 1), peak=BF16_PEAK_TFLOPS, unit="TFLOP/s",
                       frac=round(tf(t16) / BF16_PEAK_TFLOPS, 4), traffic=None, launch_us=round(t16, 2),
