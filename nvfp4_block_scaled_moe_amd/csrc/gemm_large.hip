@@ -47,6 +47,25 @@ constexpr int kWin = 8;                    // chunks per scale tile
 constexpr int kTokBytes = 256;             // f16 activations of one row and chunk
 constexpr int kSlot = 16 * kTBM * kTokBytes;
 
+// 16 bytes per lane from buffer offset voff straight into LDS (lane l at lds + 16 l). A function
+// of its own: with the address-space cast inside one of the kernel's lambdas, the host-side
+// compilation dropped the kernel's launch stubs without a diagnostic.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, unsigned char* lds, uint32_t voff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
+}
+
+// One tile of the large-M GEMM: K slice ks = scale windows [wlo, whi) = chunks [clo, chi), row
+// tile nb, m-tile = rows tc .. of expert e (GEMM rows r0 .. r0 + M - 1, ntb blocks of 16 in
+// this m-tile), its epilogue scale alpha, the wave's weight code and scale offsets and the
+// thread's activation DMA sources (RNDF rounds).
+template <int RNDF>
+struct LargeTile {
+  int ks, nb, e, tc, r0, M, ntb, wlo, whi, clo, chi;
+  float alpha;
+  uint32_t wlane, slane;
+  uint32_t bsrc[RNDF];
+};
+
 template <int WAVES, int WDEPTH, bool SWIGLU, bool A4>
 __global__ __launch_bounds__(WAVES* kWave, 2) void gemm_large_kernel(const GemmArgs p, int ntiles_n) {
   static_assert(WDEPTH >= 2 && kWin % WDEPTH == 0, "the weight ring is read one chunk ahead; steps pair up");
@@ -56,77 +75,151 @@ __global__ __launch_bounds__(WAVES* kWave, 2) void gemm_large_kernel(const GemmA
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, g = lane >> 4;
-  // Tiles (K slice, m-tile, row tile) of the m-tiles actually listed (known only here) are
-  // numbered slice-major and split into 8 equal ranges, one per XCD (workgroup i runs on XCD
-  // i mod 8): every XCD gets an equal share however far the list falls below the grid's bound,
-  // and the row tiles of one m-tile, which share its activation rows, and the m-tiles of one
-  // expert, which share its weights, run on one XCD and share its L2.
-  const int per_split = ld_const(p.sched_n, 0) * ntiles_n;
-  const int ntiles = per_split * p.ksplit;
-  const int per_xcd = (ntiles + 7) >> 3;
-  const int tile = (int)(blockIdx.x & 7) * per_xcd + (int)(blockIdx.x >> 3);
-  if ((int)(blockIdx.x >> 3) >= per_xcd || tile >= ntiles) return;
-  const int ks = tile / per_split;           // K slice
-  const int mn = tile - ks * per_split;
-  const int mt = mn / ntiles_n;              // m-tile
-  const int nb = mn - mt * ntiles_n;         // row tile
-  const int e = ld_const(p.sched_e, mt), tc = ld_const(p.sched_r, mt);
-  const int r0 = ld_const(p.expert_offsets, e);
-  const int M = ld_const(p.expert_offsets, e + 1) - r0;
   const int K = p.K, Nw = p.Nw;
   const int K128 = (K + 127) & ~127;
   const int F = Nw >> 1;
   const int nch = (K + kChunk - 1) / kChunk;
   const int nwin = (nch + kWin - 1) / kWin;
-  // K slice ks: whole scale windows [wlo, whi), chunks [clo, chi)
-  const int wps = (nwin + p.ksplit - 1) / p.ksplit;
-  const int wlo = ks * wps, whi = min(nwin, wlo + wps);
-  if (wlo >= whi) return;
-  const int clo = wlo * kWin, chi = min(nch, whi * kWin);
-  const int ntb = __builtin_amdgcn_readfirstlane(min(kTBM, (M - tc + 15) >> 4));
-
-  auto blkrow = [&](int b) -> int {
-    if (SWIGLU) return (b == 0 ? 0 : F) + (nb * WAVES + wave) * 16;
-    return (nb * WAVES + wave) * 16 * kRBW + 16 * b;
+  const int wps = (nwin + p.ksplit - 1) / p.ksplit;   // scale windows per K slice
+  // Tiles (K slice, m-tile, row tile) of the m-tiles actually listed (known only here) are
+  // numbered slice-major and split into 8 equal ranges, one per XCD (workgroup i runs on XCD
+  // i mod 8): every XCD gets an equal share however far the list falls below the grid's bound,
+  // and the row tiles of one m-tile, which share its activation rows, and the m-tiles of one
+  // expert, which share its weights, run on one XCD and share its L2. The workgroups of an XCD
+  // walk its range with a stride of their number: with f16 activations (LDS DMA) and 8 waves,
+  // a grid of one workgroup per CU stays resident and requests a tile's scales, first weights
+  // and first activation chunks while the previous tile's results are being stored.
+  constexpr bool PERSIST = !A4 && WAVES == 8;   // the 4-wave shape is only chosen for small grids
+  const int per_split = ld_const(p.sched_n, 0) * ntiles_n;
+  const int ntiles = per_split * p.ksplit;
+  const int per_xcd = (ntiles + 7) >> 3;
+  const int tlo = (int)(blockIdx.x & 7) * per_xcd;
+  const int thi = min(ntiles, tlo + per_xcd);
+  const int tstride = (int)(gridDim.x >> 3);
+  int tile = tlo + (int)(blockIdx.x >> 3);
+  if (tile >= thi) return;
+  // What the decoding of a tile reads is kept in LDS, not in scalar registers through every
+  // tile's main loop (with one tile per workgroup, the kernel arguments are read directly).
+  struct Ctx {
+    const int* sched_e;
+    const int* sched_r;
+    const int* offsets;
+    const int* gather;
+    const float* w_g;
+    int gather_div, per_split, ntiles_n;
   };
+  __shared__ Ctx ctx;
+  if constexpr (PERSIST) {
+    if (tid == 0) ctx = Ctx{p.sched_e, p.sched_r, p.expert_offsets, p.gather_index, p.w_g, p.gather_div, per_split, ntiles_n};
+    __syncthreads();
+  }
+
   // Tiled weights (weights_tile.hip): lane l reads 16 bytes at 16 l of a 1 KB tile per
-  // (16-row block, chunk) of codes and per (16-row block, 8-chunk window) of scales.
+  // (16-row block, chunk) of codes and per (16-row block, 8-chunk window) of scales. The block
+  // offsets within a row tile are the same for every tile (SwiGLU: the up block F rows below
+  // the gate block).
   const uint32_t wbytes = (uint32_t)(Nw / 16) * (uint32_t)nch * 1024u;
   const uint32_t sbytes = (uint32_t)(Nw / 16) * (uint32_t)nwin * 1024u;
-  const __amdgpu_buffer_rsrc_t wr = make_rsrc(p.w_packed + (size_t)e * wbytes, wbytes);
-  const __amdgpu_buffer_rsrc_t sr = make_rsrc(p.w_scales + (size_t)e * sbytes, sbytes);
   const __amdgpu_buffer_rsrc_t ar = A4 ? make_rsrc(p.a_packed, (uint32_t)p.a_rows * (uint32_t)(K >> 1))
                                         : make_rsrc(p.a16, (uint32_t)p.a_rows * (uint32_t)K128 * 2u);
   const __amdgpu_buffer_rsrc_t asr = make_rsrc(p.a_scales, A4 ? (uint32_t)p.a_rows * (uint32_t)(K >> 4) : 0u);
-  const uint32_t wlane = (uint32_t)(blkrow(0) / 16) * (uint32_t)nch * 1024u + 16u * lane;
-  const uint32_t slane = (uint32_t)(blkrow(0) / 16) * (uint32_t)nwin * 1024u + 16u * lane;
   uint32_t wsoff[kRBW], ssoff[kRBW];
 #pragma unroll
   for (int b = 0; b < kRBW; ++b) {
-    wsoff[b] = __builtin_amdgcn_readfirstlane((uint32_t)((blkrow(b) - blkrow(0)) / 16) * (uint32_t)nch * 1024u);
-    ssoff[b] = __builtin_amdgcn_readfirstlane((uint32_t)((blkrow(b) - blkrow(0)) / 16) * (uint32_t)nwin * 1024u);
+    const uint32_t blk = SWIGLU ? (b == 0 ? 0u : (uint32_t)(F / 16)) : (uint32_t)b;
+    wsoff[b] = __builtin_amdgcn_readfirstlane(blk * (uint32_t)nch * 1024u);
+    ssoff[b] = __builtin_amdgcn_readfirstlane(blk * (uint32_t)nwin * 1024u);
   }
-  const float alpha = p.w4a4 ? ld_const(p.w_g, e) * ld_const(p.a_g, 0) : ld_const(p.w_g, e);
+  const float a_g = p.w4a4 ? ld_const(p.a_g, 0) : 1.0f;
+  // Activation staging by LDS DMA (buffer_load ... lds): lane l of a wave writes the 16 bytes
+  // at block + 16 l of the slot, the wave's block holding 4 rows (4 x 256 B); TPR rows per
+  // round, RNDF rounds for a whole m-tile. The source of each lane is the logical piece that
+  // the row's XOR swizzle puts at that position, so the fragment reads stay conflict free;
+  // rows past the expert read zeros (kOOB).
+  constexpr int TPR = NT / 16;
+  constexpr int RNDF = 16 * kTBM / TPR;
+  static_assert(TPR == 4 * WAVES && RNDF * TPR == 16 * kTBM, "4 rows per wave and round, inside one slot");
+
+  using Tile = LargeTile<RNDF>;
+  auto tile_at = [&](int t, Tile& T) {
+    const int* sched_e = PERSIST ? uniform_ptr(ctx.sched_e) : p.sched_e;
+    const int* sched_r = PERSIST ? uniform_ptr(ctx.sched_r) : p.sched_r;
+    const int* offsets = PERSIST ? uniform_ptr(ctx.offsets) : p.expert_offsets;
+    const float* w_g = PERSIST ? uniform_ptr(ctx.w_g) : p.w_g;
+    const int ps = PERSIST ? __builtin_amdgcn_readfirstlane(ctx.per_split) : per_split;
+    const int ntn = PERSIST ? __builtin_amdgcn_readfirstlane(ctx.ntiles_n) : ntiles_n;
+    T.ks = t / ps;
+    const int mn = t - T.ks * ps;
+    const int mt = mn / ntn;
+    T.nb = mn - mt * ntn;
+    T.e = ld_const(sched_e, mt);
+    T.tc = ld_const(sched_r, mt);
+    T.r0 = ld_const(offsets, T.e);
+    T.M = ld_const(offsets, T.e + 1) - T.r0;
+    T.ntb = __builtin_amdgcn_readfirstlane(min(kTBM, (T.M - T.tc + 15) >> 4));
+    T.wlo = T.ks * wps;
+    T.whi = min(nwin, T.wlo + wps);
+    T.clo = T.wlo * kWin;
+    T.chi = min(nch, T.whi * kWin);
+    T.alpha = ld_const(w_g, T.e) * a_g;
+    const uint32_t blk0 = (uint32_t)(SWIGLU ? T.nb * WAVES + wave : (T.nb * WAVES + wave) * kRBW);
+    T.wlane = blk0 * (uint32_t)nch * 1024u + 16u * lane;
+    T.slane = blk0 * (uint32_t)nwin * 1024u + 16u * lane;
+    const int* gather = PERSIST ? ctx.gather : p.gather_index;
+    const int gdiv = PERSIST ? ctx.gather_div : p.gather_div;
+#pragma unroll
+    for (int rr = 0; rr < RNDF; ++rr) {
+      const int tk = rr * TPR + wave * 4 + (lane >> 4), pp = lane & 15, tt = T.tc + tk;
+      const bool ok = tt < T.M;
+      const uint32_t arow = ok ? (uint32_t)(gather ? gather[T.r0 + tt] / gdiv : T.r0 + tt) : 0u;
+      T.bsrc[rr] = ok ? (arow * (uint32_t)K128 + 8 * (pp ^ (tk & 15))) * 2 : kOOB;
+    }
+  };
+  // DMA rounds that cover an m-tile of ntb blocks of 16 rows (ntb rounded up to 1, 2, 4, 8)
+  auto rounds = [&](int ntb) { return ((ntb > 4 ? 128 : ntb > 2 ? 64 : ntb == 2 ? 32 : 16) + TPR - 1) / TPR; };
+  // the activations of chunk c (rows per bsrc, slice end chi) into an LDS slot, rnd rounds
+  auto b_dma = [&](const uint32_t (&bsrc)[RNDF], int chi, int rnd, int c, int slot) {
+    const bool in = c < chi;
+    unsigned char* base = smem + slot * kSlot + wave * 4 * kTokBytes;
+#pragma unroll
+    for (int rr = 0; rr < RNDF; ++rr)
+      if (rr < rnd) dma16(ar, base + rr * TPR * kTokBytes, in ? bsrc[rr] + (uint32_t)c * 256u : kOOB);
+  };
+  u32x4 wring[WDEPTH][kRBW];
+  auto w_issue = [&](const Tile& T, int d, int c) {   // codes past K are zero in the tiles
+    const __amdgpu_buffer_rsrc_t wr = make_rsrc(p.w_packed + (size_t)T.e * wbytes, wbytes);
+#pragma unroll
+    for (int b = 0; b < kRBW; ++b) wring[d][b] = ld128(wr, c < T.chi ? T.wlane + (uint32_t)c * 1024u : kOOB, wsoff[b]);
+  };
+  // One 16-byte load per block and window holds the lane's two scale bytes for each of
+  // the window's 8 chunks; the current and the next window stay in registers.
+  u32x4 scur[kRBW], snext[kRBW];
+  auto s_issue = [&](const Tile& T, int w) {
+    const __amdgpu_buffer_rsrc_t sr = make_rsrc(p.w_scales + (size_t)T.e * sbytes, sbytes);
+#pragma unroll
+    for (int b = 0; b < kRBW; ++b) snext[b] = ld128(sr, w < T.whi ? T.slane + (uint32_t)w * 1024u : kOOB, ssoff[b]);
+  };
+  // The requests of a tile's prologue with f16 activations: its first scale window, the
+  // activations of its first two chunks into slots 0 and 1 and the weights of its first
+  // WDEPTH chunks (the NVFP4-staged variant issues its own in the main loop's prologue).
+  auto prologue_issue = [&](const Tile& T) {
+    s_issue(T, T.wlo);
+    const int rnd = rounds(T.ntb);
+    b_dma(T.bsrc, T.chi, rnd, T.clo, 0);
+#pragma unroll
+    for (int d = 0; d < WDEPTH; ++d) w_issue(T, d, T.clo + d);
+    b_dma(T.bsrc, T.chi, rnd, T.clo + 1, 1);
+  };
+
+  f32x4 acc[kRBW][kTBM];
+  Tile cur, nxt;
+  tile_at(tile, cur);
+  if constexpr (!A4) prologue_issue(cur);
 
   auto body = [&](auto ntb_tag) {
     constexpr int NTB = decltype(ntb_tag)::value;
-    constexpr int TPT = 16;                          // threads per row (16 x 16 bytes)
-    constexpr int TPR = NT / TPT;                    // rows per staging round
     constexpr int RND = (16 * NTB + TPR - 1) / TPR;
-    // Activation staging by LDS DMA (buffer_load ... lds): lane l of a wave writes the 16 bytes
-    // at block + 16 l of the slot, the wave's block holding 4 rows (4 x 256 B). The source of
-    // each lane is the logical piece that the row's XOR swizzle puts at that position, so the
-    // fragment reads stay conflict free; rows past the tile read zeros (kOOB).
-    uint32_t bsrc[RND], bdst[RND];
-#pragma unroll
-    for (int rr = 0; rr < RND; ++rr) {
-      const int tk = rr * TPR + wave * 4 + (lane >> 4), pp = lane & 15, t = tc + tk;
-      const bool ok = tk < 16 * NTB && t < M;
-      const uint32_t arow = ok ? (uint32_t)(p.gather_index ? p.gather_index[r0 + t] / p.gather_div : r0 + t) : 0u;
-      bsrc[rr] = ok ? (arow * (uint32_t)K128 + 8 * (pp ^ (tk & 15))) * 2 : kOOB;
-      bdst[rr] = (rr * TPR + wave * 4) * kTokBytes;   // wave-uniform; rows < 128 stay in the slot
-    }
-    static_assert(TPR == 4 * WAVES && RND * TPR <= 16 * kTBM, "4 rows per wave and round, inside one slot");
+    const int clo = cur.clo, chi = cur.chi;
     // W4A4: NVFP4 activation rows staged through registers instead: thread -> (row, 32-column
     // piece ap) of a chunk; its 16 code bytes and 2 scale bytes are loaded one step ahead and
     // decoded exactly to f16 (as the weights) into the slot, in the same swizzled operand order.
@@ -139,15 +232,15 @@ __global__ __launch_bounds__(WAVES* kWave, 2) void gemm_large_kernel(const GemmA
     if constexpr (A4) {
 #pragma unroll
       for (int rr = 0; rr < ARND; ++rr) {
-        const int tk = rr * ATR + (tid >> 2), t = tc + tk;
-        const bool ok = tk < 16 * NTB && t < M;
-        const uint32_t arow = ok ? (uint32_t)(p.gather_index ? p.gather_index[r0 + t] / p.gather_div : r0 + t) : 0u;
+        const int tk = rr * ATR + (tid >> 2), t = cur.tc + tk;
+        const bool ok = tk < 16 * NTB && t < cur.M;
+        const uint32_t arow = ok ? (uint32_t)(p.gather_index ? p.gather_index[cur.r0 + t] / p.gather_div : cur.r0 + t) : 0u;
         acsrc[rr] = ok ? arow * (uint32_t)(K >> 1) + 16u * ap : kOOB;
         assrc[rr] = ok ? arow * (uint32_t)(K >> 4) + 2u * ap : kOOB;
       }
     }
     auto a_load = [&](int set, int c) {   // pieces past K (or the slice) read zero codes and scales
-      const bool in = c < chi && 128 * c + 32 * ap < K;
+      const bool in = c < cur.chi && 128 * c + 32 * ap < K;
 #pragma unroll
       for (int rr = 0; rr < ARND; ++rr) {
         acode[set][rr] = ld128(ar, in && acsrc[rr] != kOOB ? acsrc[rr] + 64u * c : kOOB, 0);
@@ -169,14 +262,6 @@ __global__ __launch_bounds__(WAVES* kWave, 2) void gemm_large_kernel(const GemmA
         }
       }
     };
-    auto b_dma = [&](int c, int slot) {
-      const bool in = c < chi;
-#pragma unroll
-      for (int rr = 0; rr < RND; ++rr)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            ar, (__attribute__((address_space(3))) void*)(smem + slot * kSlot + bdst[rr]), 16,
-            in ? bsrc[rr] + (uint32_t)c * 256u : kOOB, 0, 0, 0);
-    };
     auto b_read = [&](f16x8 (&dst)[NTB], int slot, int j) {
       const unsigned char* base = smem + slot * kSlot;
 #pragma unroll
@@ -184,18 +269,6 @@ __global__ __launch_bounds__(WAVES* kWave, 2) void gemm_large_kernel(const GemmA
         const int tk = 16 * tb + l16;
         dst[tb] = *reinterpret_cast<const f16x8*>(base + tk * kTokBytes + 16 * ((4 * j + g) ^ (tk & 15)));
       }
-    };
-    u32x4 wring[WDEPTH][kRBW];
-    auto w_issue = [&](int d, int c) {   // codes past K are zero in the tiles
-#pragma unroll
-      for (int b = 0; b < kRBW; ++b) wring[d][b] = ld128(wr, c < chi ? wlane + (uint32_t)c * 1024u : kOOB, wsoff[b]);
-    };
-    // One 16-byte load per block and window holds the lane's two scale bytes for each of
-    // the window's 8 chunks; the current and the next window stay in registers.
-    u32x4 scur[kRBW], snext[kRBW];
-    auto s_issue = [&](int w) {
-#pragma unroll
-      for (int b = 0; b < kRBW; ++b) snext[b] = ld128(sr, w < whi ? slane + (uint32_t)w * 1024u : kOOB, ssoff[b]);
     };
     f16x8 wf[kRBW][4], wfn[kRBW][4];   // decoded weights of chunks c and c+1
     f16x2 sc[kRBW][2];
@@ -211,29 +284,23 @@ __global__ __launch_bounds__(WAVES* kWave, 2) void gemm_large_kernel(const GemmA
       for (int b = 0; b < kRBW; ++b) dst[b][j] = decode8(wring[d][b][j], sc[b][j >> 1]);
     };
 
-    f32x4 acc[kRBW][kTBM];
 #pragma unroll
     for (int b = 0; b < kRBW; ++b)
 #pragma unroll
       for (int tb = 0; tb < kTBM; ++tb) acc[b][tb] = (f32x4){0.f, 0.f, 0.f, 0.f};
 
-    // prologue: activations of the first two chunks into slots 0 and 1, weights of the first
-    // WDEPTH chunks requested, the first chunk decoded
-    s_issue(wlo);
+    // prologue: activations of the first two chunks in slots 0 and 1, weights of the first
+    // WDEPTH chunks requested (f16 activations: already requested), the first chunk decoded
     if constexpr (A4) {   // clo is a multiple of kWin: chunk c uses staging set c & 1 = u & 1
+      s_issue(cur, cur.wlo);
       a_load(0, clo);
       a_load(1, clo + 1);
 #pragma unroll
-      for (int d = 0; d < WDEPTH; ++d) w_issue(d, clo + d);
+      for (int d = 0; d < WDEPTH; ++d) w_issue(cur, d, clo + d);
       a_store(0, 0);
       a_load(0, clo + 2);
       a_store(1, 1);
       a_load(1, clo + 3);
-    } else {
-      b_dma(clo, 0);
-#pragma unroll
-      for (int d = 0; d < WDEPTH; ++d) w_issue(d, clo + d);
-      b_dma(clo + 1, 1);
     }
 #pragma unroll
     for (int b = 0; b < kRBW; ++b) scur[b] = snext[b];
@@ -251,7 +318,7 @@ __global__ __launch_bounds__(WAVES* kWave, 2) void gemm_large_kernel(const GemmA
     // all waves when step c+1 prefetches its first fragments.
     int slot = 0;
     for (int c0 = clo; c0 < chi; c0 += kWin) {     // one scale window per iteration
-      s_issue(c0 / kWin + 1);
+      s_issue(cur, c0 / kWin + 1);
 #pragma unroll
       for (int u = 0; u < kWin; ++u) {
         const int c = c0 + u;
@@ -263,9 +330,9 @@ __global__ __launch_bounds__(WAVES* kWave, 2) void gemm_large_kernel(const GemmA
             a_store(u & 1, slot2);                 // chunk c+2, loaded in step c-2
             a_load(u & 1, c + 4);
           } else {
-            b_dma(c + 2, slot2);
+            b_dma(cur.bsrc, chi, RND, c + 2, slot2);
           }
-          w_issue(d, c + WDEPTH);                  // ring entry d (chunk c) was decoded last step
+          w_issue(cur, d, c + WDEPTH);             // ring entry d (chunk c) was decoded last step
           scales(u + 1);
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
@@ -294,8 +361,19 @@ __global__ __launch_bounds__(WAVES* kWave, 2) void gemm_large_kernel(const GemmA
       }
     }
 
+  };
+
+  // The epilogue of tile T from acc: raw partial sums (K split) or the usual stores (+ amax,
+  // + the fused weighted reduce of a combine call). pexps: the row scales of W4A16, read
+  // before the next tile's requests so that waiting for them does not wait for those.
+  auto epilogue = [&](const Tile& T, const int (&pexps)[kTBM]) {
+    const int tc = T.tc, M = T.M, r0 = T.r0, ntb = T.ntb, nb = T.nb;
+    auto blkrow = [&](int b) -> int {
+      if (SWIGLU) return (b == 0 ? 0 : F) + (nb * WAVES + wave) * 16;
+      return (nb * WAVES + wave) * 16 * kRBW + 16 * b;
+    };
     if (p.ksplit > 1) {   // raw partial sums; splitk_reduce_kernel applies the epilogue
-      float* part = p.partial + (size_t)ks * p.rows * Nw;
+      float* part = p.partial + (size_t)T.ks * p.rows * Nw;
 #pragma unroll
       for (int tb = 0; tb < kTBM; ++tb) {
         const int t = tc + 16 * tb + l16;
@@ -308,15 +386,35 @@ __global__ __launch_bounds__(WAVES* kWave, 2) void gemm_large_kernel(const GemmA
       }
       return;
     }
-    uint32_t amax_bits = store_tile<kRBW, kTBM, SWIGLU>(p, acc, tc, ntb, M, r0, alpha, !p.w4a4, blkrow, lane, 0u);
+    uint32_t amax_bits = store_tile_exp<kRBW, kTBM, SWIGLU>(p, acc, tc, ntb, M, r0, T.alpha, pexps, blkrow, lane, 0u);
     merge_amax(p.out_amax, amax_bits, lane);
     if (!SWIGLU && p.comb_slot)   // the weighted reduce of the tokens this tile completes
       combine_tile<NT>(p, r0 + tc, min(16 * ntb, M - tc), nb * WAVES * 16 * kRBW, WAVES * 16 * kRBW);
   };
-  if (ntb > 4) body(Int<8>{});
-  else if (ntb > 2) body(Int<4>{});
-  else if (ntb == 2) body(Int<2>{});
-  else body(Int<1>{});
+
+  for (;;) {
+    const int ntb = cur.ntb;
+    if (ntb > 4) body(Int<8>{});
+    else if (ntb > 2) body(Int<4>{});
+    else if (ntb == 2) body(Int<2>{});
+    else body(Int<1>{});
+    int pexps[kTBM];
+    row_exponents<kTBM>(p, cur.tc, cur.M, cur.r0, p.ksplit <= 1 && !p.w4a4, lane, pexps);
+    // the next tile's first requests go out before this tile's results are stored
+    const int next = tile + tstride;
+    const bool more = PERSIST && next < thi;
+    if constexpr (PERSIST) {
+      if (more) {
+        tile_at(next, nxt);
+        prologue_issue(nxt);
+      }
+    }
+    epilogue(cur, pexps);
+    if (!more) break;
+    __syncthreads();   // every wave is past the epilogue (combine calls use LDS) before the next tile
+    tile = next;
+    cur = nxt;
+  }
 }
 
 // Split-K epilogue: out[row, col] from the fixed-order sum over K slices of the partial sums,
@@ -377,7 +475,12 @@ hipError_t launch_cfg(const GemmArgs& a, int max_mtiles, hipStream_t stream) {
   if (attr != hipSuccess) return attr;
   const int ntiles_n = a.Nw / (16 * kRBW * WAVES);
   const int total = max_mtiles * ntiles_n * a.ksplit;   // bound on the tiles
-  const int grid = (total + 7) / 8 * 8;
+  // 8 waves with f16 activations: one workgroup per CU at most (the LDS ring fits one), looping
+  // over the tiles; the NVFP4-staged variant and the 4-wave shape: one workgroup per tile
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 8)
+    cus = 256;
+  const int grid = A4 || WAVES != 8 ? (total + 7) / 8 * 8 : min((total + 7) / 8 * 8, cus / 8 * 8);
   kern<<<grid, WAVES * kWave, shmem, stream>>>(a, ntiles_n);
   if (a.ksplit <= 1) return hipGetLastError();
   const hipError_t e2 = hipGetLastError();
