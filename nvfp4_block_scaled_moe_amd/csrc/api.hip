@@ -677,9 +677,10 @@ nvfp4moe_status mx_gemm_call(const char* fn, int bits, nvfp4moe_epilogue epi, co
   g.out = out;
   g.out_bf16 = out_dtype == NVFP4MOE_BF16;
   g.out_amax = out_amax;
-  g.sched_e = reinterpret_cast<const int*>(base);
-  g.sched_r = reinterpret_cast<const int*>(base + arr);
-  g.sched_n = reinterpret_cast<const int*>(base + 2 * arr);
+  const bool dense = E == 1;   // one expert: the GEMM numbers its m-tiles itself, no list
+  g.sched_e = dense ? nullptr : reinterpret_cast<const int*>(base);
+  g.sched_r = dense ? nullptr : reinterpret_cast<const int*>(base + arr);
+  g.sched_n = dense ? nullptr : reinterpret_cast<const int*>(base + 2 * arr);
   g.hq_packed = hq_packed;
   g.hq_scales = hq_scales;
   g.ksplit = qh ? 1 : mx_ksplit(max_mtiles, Nw, K);   // the quantized epilogue needs whole sums
@@ -693,7 +694,7 @@ nvfp4moe_status mx_gemm_call(const char* fn, int bits, nvfp4moe_epilogue epi, co
   if (err != hipSuccess) return hip_status(err, fn);
   const MtileSched sched{expert_offsets, active_experts, n_active, E, mx_rows_per_mtile(bits), max_mtiles,
                          const_cast<int*>(g.sched_e), const_cast<int*>(g.sched_r), const_cast<int*>(g.sched_n)};
-  err = launch_mtile_schedule(sched, s);
+  if (!dense) err = launch_mtile_schedule(sched, s);
   if (err == hipSuccess) err = launch_gemm_mx(g, max_mtiles, bits, s);
   if (err == hipSuccess && comb) err = combine_finish(g, *comb, Nw, s);
   return hip_status(err, fn);

@@ -174,7 +174,11 @@ __global__ __launch_bounds__(kMxWaves* kWave) void gemm_mx_kernel(const GemmArgs
   // one per XCD (workgroup i runs on XCD i mod 8). The workgroups of an XCD walk its range
   // with a stride of their number, so that a grid of one workgroup per CU stays resident and
   // requests a tile's first chunks while the previous tile's results are being stored.
-  const int per_split = ld_const(p.sched_n, 0) * ntiles_n;
+  // One expert (a dense GEMM) needs no m-tile list (sched_e null): m-tile i is rows 16 TBM i ..
+  // of expert 0.
+  const int n_mtiles = p.sched_e ? ld_const(p.sched_n, 0)
+                                 : (ld_const(p.expert_offsets, 1) - ld_const(p.expert_offsets, 0) + 16 * TBM - 1) / (16 * TBM);
+  const int per_split = n_mtiles * ntiles_n;
   const int ntiles = per_split * p.ksplit;
   const int per_xcd = (ntiles + 7) >> 3;
   const int tlo = (int)(blockIdx.x & 7) * per_xcd;
@@ -237,8 +241,8 @@ __global__ __launch_bounds__(kMxWaves* kWave) void gemm_mx_kernel(const GemmArgs
       // Tile order within the expert: m-tiles in groups of mgroup (the last one shorter), the
       // tiles of a group row-tile-major. The list holds an expert's m-tiles in a row, m-tile i
       // of the expert at row i * 16 TBM, so the group follows from the m-tile's own entry.
-      const int loc = ld_const(sched_r, mt) / (16 * TBM);
-      const int ex = ld_const(sched_e, mt);
+      const int loc = sched_e ? ld_const(sched_r, mt) / (16 * TBM) : mt;
+      const int ex = sched_e ? ld_const(sched_e, mt) : 0;
       const int me = (ld_const(offsets, ex + 1) - ld_const(offsets, ex) + 16 * TBM - 1) / (16 * TBM);
       const int gi = loc / mg, gs = mt - loc + gi * mg;
       const int gn = min(min(mg, me - gi * mg), ps / ntn - gs);
@@ -247,8 +251,8 @@ __global__ __launch_bounds__(kMxWaves* kWave) void gemm_mx_kernel(const GemmArgs
       mt = gs + (pos - nb * gn);
     }
     T.nb = nb;
-    T.e = ld_const(sched_e, mt);
-    T.tc = ld_const(sched_r, mt);
+    T.e = sched_e ? ld_const(sched_e, mt) : 0;
+    T.tc = sched_e ? ld_const(sched_r, mt) : mt * 16 * TBM;
     T.r0 = ld_const(offsets, T.e);
     T.M = ld_const(offsets, T.e + 1) - T.r0;
     T.ntb = __builtin_amdgcn_readfirstlane(min(TBM, (T.M - T.tc + 15) >> 4));
