@@ -218,13 +218,9 @@ __global__ __launch_bounds__(kQuantThreads) void quantize_tiled_kernel(const T* 
 }
 
 // FP8 E4M3 round trip of 8 bf16 values per thread.
-__global__ __launch_bounds__(kQuantThreads) void fp8_roundtrip_kernel(const uint16_t* __restrict__ x,
-                                                                      int64_t nvec,
-                                                                      const float* __restrict__ s_a,
-                                                                      uint16_t* __restrict__ out) {
-  const int64_t i = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x;
-  if (i >= nvec) return;
-  const float s = s_a[0];
+// Eight bf16 activations (vector i) through E4M3 and back under the per-tensor scale s.
+__device__ __forceinline__ void fp8_roundtrip8(const uint16_t* __restrict__ x, int64_t i, float s,
+                                               uint16_t* __restrict__ out) {
   float v[8];
   Vec8<uint16_t>::load(x + i * 8, v);
   uint32_t w[4];
@@ -243,6 +239,48 @@ __global__ __launch_bounds__(kQuantThreads) void fp8_roundtrip_kernel(const uint
     else w[j / 2] = bits;
   }
   *reinterpret_cast<uint4*>(out + i * 8) = make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+__global__ __launch_bounds__(kQuantThreads) void fp8_roundtrip_kernel(const uint16_t* __restrict__ x,
+                                                                      int64_t nvec,
+                                                                      const float* __restrict__ s_a,
+                                                                      uint16_t* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x;
+  if (i >= nvec) return;
+  fp8_roundtrip8(x, i, s_a[0], out);
+}
+
+// The round trip of a small tensor in one launch instead of three: every workgroup takes the
+// amax over the finite entries of the whole tensor (a max, so every workgroup gets the same
+// value; the tensor is read from L2), s_a = amax / 448 (1 if amax = 0, the same division as
+// the scale kernel), then converts its own slice of kSmallRtVecs vectors.
+constexpr int kSmallRtThreads = 1024;
+constexpr int kSmallRtVecs = 512;                       // vectors of 8 per workgroup slice
+constexpr int64_t kSmallRtElems = int64_t(1) << 16;     // larger tensors: three launches (measured faster)
+__global__ __launch_bounds__(kSmallRtThreads) void fp8_roundtrip_small_kernel(const uint16_t* __restrict__ x,
+                                                                             int64_t nvec,
+                                                                             uint16_t* __restrict__ out) {
+  __shared__ float red[kSmallRtThreads / kWave];
+  __shared__ float s_sh;
+  float m = 0.0f;
+  for (int64_t i = threadIdx.x; i < nvec; i += kSmallRtThreads) {
+    float v[8];
+    Vec8<uint16_t>::load(x + i * 8, v);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m = fmaxf(m, finite_abs(v[j]));
+  }
+  m = wave_max(m);
+  if ((threadIdx.x % kWave) == 0) red[threadIdx.x / kWave] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float a = red[0];
+    for (int w = 1; w < kSmallRtThreads / kWave; ++w) a = fmaxf(a, red[w]);
+    s_sh = (a == 0.0f) ? 1.0f : __fdiv_rn(a, 448.0f);
+  }
+  __syncthreads();
+  const float s = s_sh;
+  const int64_t lo = (int64_t)blockIdx.x * kSmallRtVecs, hi = min(nvec, lo + kSmallRtVecs);
+  for (int64_t i = lo + threadIdx.x; i < hi; i += kSmallRtThreads) fp8_roundtrip8(x, i, s, out);
 }
 
 // MXFP4 (group 32, UE8M0 scale, no per-tensor scale; "The Benchmark That Confirmed the
@@ -386,6 +424,12 @@ size_t fp8_roundtrip_ws_bytes(int64_t n) {
 }
 
 hipError_t launch_fp8_roundtrip(const void* x, int64_t n, void* out, void* ws, hipStream_t stream) {
+  if (n <= kSmallRtElems) {   // decode-sized activations: one launch
+    const int64_t nvec = n / 8;
+    fp8_roundtrip_small_kernel<<<(unsigned)((nvec + kSmallRtVecs - 1) / kSmallRtVecs), kSmallRtThreads, 0, stream>>>(
+        static_cast<const uint16_t*>(x), nvec, static_cast<uint16_t*>(out));
+    return hipGetLastError();
+  }
   const int nblk = amax_blocks(n);
   float* partial = static_cast<float*>(ws);
   float* s_a = partial + nblk + 32;  // keep apart from the partials

@@ -109,7 +109,8 @@ __global__ __launch_bounds__(router_sort_threads<NE>()) void router_sort_kernel(
   }
 }
 
-// One wavefront per token; lane l holds the logits of experts l + 64 i (i < PL).
+// One token's top-k in one wavefront (router_kernel): lane l holds the logits of experts l + 64 i (i < PL); ids[0, k) and w[0, k) of the token are
+// written (and, if lds_ids is given, the ids there too).
 //  1. Radix select of the k-th largest key t: 32 steps, each counting keys >= a candidate with
 //     wave ballots (no data movement between lanes).
 //  2. Selected: keys > t, plus the lowest ids among keys == t until k are taken (ballot order
@@ -119,14 +120,8 @@ __global__ __launch_bounds__(router_sort_threads<NE>()) void router_sort_kernel(
 //     selected set (lane reads, no shuffles).
 //  4. Weights exp(l - l_max) / sum over the selected, in float64, rounded once to float32.
 template <int PL>
-__global__ __launch_bounds__(kRouterWaves* kWave) void router_kernel(const float* __restrict__ logits,
-                                                                     int T, int E, int k,
-                                                                     int* __restrict__ ids,
-                                                                     float* __restrict__ w) {
-  const int lane = threadIdx.x % kWave;
-  const int t = blockIdx.x * kRouterWaves + threadIdx.x / kWave;
-  if (t >= T) return;   // t is the same for the whole wave
-  const float* row = logits + (size_t)t * E;
+__device__ __forceinline__ void route_token_select(const float* __restrict__ row, int E, int k, int lane,
+                                                   int* __restrict__ ids, float* __restrict__ w, int* lds_ids) {
   float v[PL];
   uint32_t key[PL];
   bool av[PL];
@@ -195,10 +190,23 @@ __global__ __launch_bounds__(kRouterWaves* kWave) void router_kernel(const float
 #pragma unroll
   for (int i = 0; i < PL; ++i) {
     if (sel[i]) {
-      ids[(size_t)t * k + rank[i]] = lane + kWave * i;
-      w[(size_t)t * k + rank[i]] = (float)(ex[i] / sum);
+      ids[rank[i]] = lane + kWave * i;
+      w[rank[i]] = (float)(ex[i] / sum);
+      if (lds_ids) lds_ids[rank[i]] = lane + kWave * i;
     }
   }
+}
+
+
+template <int PL>
+__global__ __launch_bounds__(kRouterWaves* kWave) void router_kernel(const float* __restrict__ logits,
+                                                                     int T, int E, int k,
+                                                                     int* __restrict__ ids,
+                                                                     float* __restrict__ w) {
+  const int lane = threadIdx.x % kWave;
+  const int t = blockIdx.x * kRouterWaves + threadIdx.x / kWave;
+  if (t >= T) return;   // t is the same for the whole wave
+  route_token_select<PL>(logits + (size_t)t * E, E, k, lane, ids + (size_t)t * k, w + (size_t)t * k, nullptr);
 }
 
 // Histogram of ids[lo, hi) into one wave's counter row (LDS atomics); the ids of kPermBatch
@@ -267,11 +275,13 @@ __device__ __forceinline__ void permute_block(const int* ids, int S, int E, int 
   int* wflag = wsum + kPermWaves;         // [kPermWaves] active-expert totals per wave
   const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
 
-  for (int i = tid; i < kPermWaves * E; i += kPermThreads) cnt[i] = 0;
+  // slot slices of `per` slots (a multiple of 64) per wave; only the first nw waves hold slots
+  const int per = ((S + kPermWaves - 1) / kPermWaves + kWave - 1) / kWave * kWave;
+  const int nw = per > 0 ? min(kPermWaves, (S + per - 1) / per) : 0;
+  const int lo = min(S, wave * per), hi = min(S, lo + per);
+  for (int i = tid; i < nw * E; i += kPermThreads) cnt[i] = 0;
   __syncthreads();
 
-  const int per = ((S + kPermWaves - 1) / kPermWaves + kWave - 1) / kWave * kWave;
-  const int lo = min(S, wave * per), hi = min(S, lo + per);
   // 1. per-wave histograms
   wave_histogram(ids, lo, hi, cnt + wave * E, lane);
   __syncthreads();
@@ -280,7 +290,7 @@ __device__ __forceinline__ void permute_block(const int* ids, int S, int E, int 
   const int e = tid;
   int tot = 0;
   if (e < E) {
-    for (int w = 0; w < kPermWaves; ++w) {
+    for (int w = 0; w < nw; ++w) {
       const int c = cnt[w * E + e];
       cnt[w * E + e] = tot;
       tot += c;
@@ -314,7 +324,7 @@ __device__ __forceinline__ void permute_block(const int* ids, int S, int E, int 
   const int fpos = fbefore + fincl - flag;  // position in the active list
   if (e < E) {
     offsets[e] = base;
-    for (int w = 0; w < kPermWaves; ++w) cnt[w * E + e] += base;
+    for (int w = 0; w < nw; ++w) cnt[w * E + e] += base;
     if (e >= nact) active[e] = -1;
     if (flag) active[fpos] = e;
     if (e == E - 1) {
@@ -339,7 +349,8 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(const int* __rest
 }
 
 // Few tokens (T <= kPermWaves, T * k <= kSmallSlots): routing and permutation in one
-// workgroup and one launch. Wave t routes token t by k rounds of wave argmax: each round takes
+// workgroup and one launch. Wave t routes token t by k rounds of wave argmax (measured faster
+// than router_kernel's radix select here, also at top-22 of 512): each round takes
 // the largest order-preserving logit key (DPP max over the wave) and, among the experts
 // holding it, the lowest id (ballots; registers ascend in id, lanes within a register), and
 // removes it. Weights as in router_kernel (float64 exp(l - l_max) over the kept, summed over

@@ -142,12 +142,14 @@ def test_quantize_tiled_layout_bit_exact(B, R, C, dt, gmode):
         assert np.array_equal(np_(p[b]), po) and np.array_equal(np_(sc[b]), so) and np_(g)[b] == go
 
 
-def test_fp8_roundtrip_bit_exact():
-    say("fp8 roundtrip")
-    x = (inputs.random_fp32((64, 256), 7) * 3).to(torch.bfloat16)
+@pytest.mark.parametrize("R,C", [(64, 256), (1, 8), (64, 2048), (1024, 512)])   # one-launch path, and the 3-launch one
+def test_fp8_roundtrip_bit_exact(R, C):
+    say("fp8 roundtrip", R, C)
+    x = (inputs.random_fp32((R, C), 7) * 3).to(torch.bfloat16)
     x[0, 0] = float("inf")
     x[0, 1] = float("nan")
     x[0, 2] = -float("inf")
+    x[R - 1, C - 1] = 1000.0 * (R * C > 1 << 14)          # the amax sits in the last vector (another slice)
     got = np_(ops.act_fp8_e4m3_roundtrip(x.to(DEV)))
     want = omoe.fp8_roundtrip_bf16(x.float().numpy())
     assert np.array_equal(np.isnan(got), np.isnan(want))
