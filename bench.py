@@ -168,6 +168,17 @@ def main():
     print(json.dumps(line), flush=True)
 
 
+def kernel_source_sha(src_name):
+    """sha256 prefix over a kernel file and the headers it includes (the epilogue lives in
+    gemm_common.h), as recorded in the committed traffic summaries."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in (src_name, "gemm_common.h", "common.h", "kernels.h"):
+        with open(os.path.join(ROOT, "nvfp4_block_scaled_moe_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
 def measured_traffic(wl, T, mx=False):
     """HBM bytes per up/gate launch from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary
     (copy-calibrated), or None when none covers this workload or the kernel source has
@@ -181,10 +192,9 @@ def measured_traffic(wl, T, mx=False):
         return None
     prof_name, src_name = known[(wl.name, T, mx)]
     prof = os.path.join(ROOT, "profiles", prof_name)
-    src = os.path.join(ROOT, "nvfp4_block_scaled_moe_amd", "csrc", src_name)
     try:
         text = open(prof).read()
-        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+        sha = kernel_source_sha(src_name)
     except OSError:
         return None
     m_sha = re.search(r"kernel_source_sha256_prefix:\s*([0-9a-f]+)", text)
