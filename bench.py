@@ -19,7 +19,7 @@ large bf16 torch.mm), each fraction given against both the spec peak and the mea
 
 Usage: python bench.py [--steps K] [--warmup W] [--tokens T] [--workload NAME]
        [--format nvfp4|mxfp4] [--no-cpu-baseline] [--no-sweep] [--no-ceilings]
-       [--sweep FILE] [--copy-calibration]
+       [--sweep FILE] [--sweep-tokens T1,T2,...] [--copy-calibration]
 """
 from __future__ import annotations
 
@@ -55,6 +55,8 @@ def parse():
                    help="1: the down GEMM and the weighted reduce as one call (the combine entry points)")
     p.add_argument("--cpu-seconds", type=float, default=12.0)
     p.add_argument("--sweep", default=None, help="also write per-T results of the workload's sweep to FILE")
+    p.add_argument("--sweep-tokens", default=None,
+                   help="comma-separated token counts that replace the workload's sweep points")
     p.add_argument("--no-sweep", action="store_true",
                    help="leave out the cold token sweep that the default line carries")
     p.add_argument("--no-ceilings", action="store_true",
@@ -145,8 +147,9 @@ def main():
         elif rf is not None and rf.get("peak") == FP4_PEAK_TFLOPS and ceil.get("mxfp4_scaled_mm_TFLOPs"):
             rf["frac_of_measured_mxfp4_mm"] = round(rf["achieved"] / ceil["mxfp4_scaled_mm_TFLOPs"], 4)
         line["weight_frac_of_measured_read"] = round(res["weight_gbs"] / ceil["hbm_read_GBps"], 4)
-    if wl.sweep and not args.no_sweep:
-        line["token_sweep_cold"] = token_sweep(torch, ops, layer, inputs, wl, w, mode, dev, args,
+    points = [int(t) for t in args.sweep_tokens.split(",")] if args.sweep_tokens else wl.sweep
+    if points and not args.no_sweep:
+        line["token_sweep_cold"] = token_sweep(torch, ops, layer, inputs, wl, w, mode, dev, args, points,
                                                ceil["hbm_read_GBps"] if ceil else None)
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(torch, wl, w, x, lg, T, mode, args.cpu_seconds)
@@ -154,7 +157,7 @@ def main():
         line["cpu_baseline"] = None
     if args.sweep:
         rows = []
-        for Ts in wl.sweep or (T,):
+        for Ts in points or (T,):
             xs = inputs.activations_bf16(wl, Ts).to(dev)
             ls = inputs.router_logits(wl, Ts).to(dev)
             r = measure(torch, ops, layer, wl, w, xs, ls, Ts, mode, max(5, args.steps // 2), 2, graph=True,
@@ -501,13 +504,13 @@ def vendor_scaled_mm(torch, M, N, K, a_codes=None, a_scales=None, w_codes=None, 
     }
 
 
-def token_sweep(torch, ops, layer, inputs, wl, w, mode, dev, args, read_gbs):
+def token_sweep(torch, ops, layer, inputs, wl, w, mode, dev, args, points, read_gbs):
     """The workload's token sweep, each point's layer step replayed from a HIP graph: cold
     (after a 1 GiB read) median and p10/p90 over `steps` replays, warm median; weight bytes
     of the touched experts over the cold median against the 8 TB/s spec (and the measured
     read ceiling)."""
     rows = []
-    for Ts in wl.sweep:
+    for Ts in points:
         xs = inputs.activations_bf16(wl, Ts).to(dev)
         ls = inputs.router_logits(wl, Ts).to(dev)
         r = ops.moe_route_permute(ls, wl.k)

@@ -349,12 +349,15 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(const int* __rest
 }
 
 // Few tokens (T <= kPermWaves, T * k <= kSmallSlots): routing and permutation in one
-// workgroup and one launch. Wave t routes token t by k rounds of wave argmax (measured faster
-// than router_kernel's radix select here, also at top-22 of 512): each round takes
-// the largest order-preserving logit key (DPP max over the wave) and, among the experts
-// holding it, the lowest id (ballots; registers ascend in id, lanes within a register), and
-// removes it. Weights as in router_kernel (float64 exp(l - l_max) over the kept, summed over
-// the wave). The ids also go to LDS, from which the workgroup permutes as permute_kernel does.
+// workgroup and one launch. Wave t routes token t. Below top-16 by k rounds of wave argmax
+// (route_token_rounds): each round takes the largest order-preserving logit key (DPP max over
+// the wave) and, among the experts holding it, the lowest id (ballots; registers ascend in id,
+// lanes within a register), and removes it. From top-16 on by route_token_thresh, whose cost
+// does not grow with k (many-small layer, top-22 of 512: 2.5-4.5 us less per step at 1, 4
+// and 16 tokens; decode, top-8 of 256: the rounds ~1.5 us faster). Both give the same ids in
+// the same order and the same weights: float64 exp(l - l_max) over the kept, summed over the
+// wave with lane r holding rank r. The ids also go to LDS, from which the workgroup permutes
+// as permute_kernel does.
 constexpr int kSmallSlots = 1024;
 
 template <int PL>
@@ -407,6 +410,88 @@ __device__ __forceinline__ void route_token_rounds(const float* __restrict__ row
   }
 }
 
+// The same selection, order and weights as route_token_rounds without its k serial rounds:
+// the k-th largest key th is found bit by bit (the largest th with at least k keys >= th; a
+// ballot per register and bit), the keys above th are kept and the lowest ids among those
+// equal to th fill the rest, the k kept (key, id, logit) go to the wave's LDS scratch in id
+// order, lane j takes entry j and counts the kept entries ahead of it (larger key, or equal
+// key and lower id), and lane r then takes the entry of rank r, as round r would have.
+// scratch: 3 x 64 words of the wave's own LDS.
+template <int PL>
+__device__ __forceinline__ void route_token_thresh(const float* __restrict__ row, int E, int k, int lane,
+                                                   int* __restrict__ ids, float* __restrict__ w, int* lds_ids,
+                                                   uint32_t* scratch) {
+  uint32_t key[PL];
+  float v[PL];
+#pragma unroll
+  for (int i = 0; i < PL; ++i) {
+    const int e = lane + kWave * i;
+    const float x = e < E ? row[e] : -INFINITY;
+    v[i] = (x != x) ? -INFINITY : x;
+    key[i] = e < E ? logit_key(x) : 0u;   // every real key is >= logit_key(-inf) > 0
+  }
+  uint32_t th = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t cand = th | (1u << bit);
+    int cnt = 0;
+#pragma unroll
+    for (int i = 0; i < PL; ++i) cnt += wave_count(key[i] >= cand);
+    if (cnt >= k) th = cand;
+  }
+  int need = k;
+#pragma unroll
+  for (int i = 0; i < PL; ++i) need -= wave_count(key[i] > th);
+  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  int base = 0;   // kept entries in the registers before i (ids ascend with i, then lane)
+#pragma unroll
+  for (int i = 0; i < PL; ++i) {
+    const uint64_t eq = __ballot(key[i] == th);
+    const bool kept = key[i] > th || (((eq >> lane) & 1ull) && __popcll(eq & below) < need);
+    const int c = __popcll(eq);
+    need = need > c ? need - c : 0;
+    const uint64_t km = __ballot(kept);
+    if (kept) {
+      const int pos = base + __popcll(km & below);
+      scratch[pos] = key[i];
+      scratch[kWave + pos] = (uint32_t)(lane + kWave * i);
+      scratch[2 * kWave + pos] = __float_as_uint(v[i]);
+    }
+    base += __popcll(km);
+  }
+  uint32_t kj = 0, ej = 0, xj = 0;
+  if (lane < k) {
+    kj = scratch[lane];
+    ej = scratch[kWave + lane];
+    xj = scratch[2 * kWave + lane];
+  }
+  int rank = 0;
+  for (int m = 0; m < k; ++m) {
+    const uint32_t km = (uint32_t)__builtin_amdgcn_readlane((int)kj, m);
+    const uint32_t em = (uint32_t)__builtin_amdgcn_readlane((int)ej, m);
+    rank += (km > kj || (km == kj && em < ej)) ? 1 : 0;
+  }
+  if (lane < k) {
+    scratch[rank] = ej;
+    scratch[kWave + rank] = xj;
+  }
+  int my_e = 0;
+  float my_x = 0.0f;
+  if (lane < k) {
+    my_e = (int)scratch[lane];
+    my_x = __uint_as_float(scratch[kWave + lane]);
+  }
+  const double m = (double)__uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(my_x), 0));
+  const double ex = lane < k ? exp((double)my_x - m) : 0.0;
+  double sum = ex;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o, kWave);
+  if (lane < k) {
+    ids[lane] = my_e;
+    w[lane] = (float)(ex / sum);
+    lds_ids[lane] = my_e;
+  }
+}
+
 template <int PL>
 __global__ __launch_bounds__(kPermThreads) void route_permute_small_kernel(const float* __restrict__ logits,
                                                                            int T, int E, int k, int nbits,
@@ -416,13 +501,21 @@ __global__ __launch_bounds__(kPermThreads) void route_permute_small_kernel(const
                                                                            int* __restrict__ sorted_slot,
                                                                            int* __restrict__ slot_to_row,
                                                                            int* __restrict__ active,
-                                                                           int* __restrict__ n_active) {
+                                                                           int* __restrict__ n_active,
+                                                                           int thresh) {
   extern __shared__ int sm[];
   int* s_ids = sm;                   // [T * k] expert ids
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
-  if (wave < T)
-    route_token_rounds<PL>(logits + (size_t)wave * E, E, k, lane, ids + (size_t)wave * k, w + (size_t)wave * k,
-                           s_ids + wave * k);
+  if (wave < T) {
+    if (thresh)
+      route_token_thresh<PL>(logits + (size_t)wave * E, E, k, lane, ids + (size_t)wave * k, w + (size_t)wave * k,
+                             s_ids + wave * k,
+                             reinterpret_cast<uint32_t*>(sm + kSmallSlots + kPermWaves * E + 2 * kPermWaves) +
+                                 wave * 3 * kWave);
+    else
+      route_token_rounds<PL>(logits + (size_t)wave * E, E, k, lane, ids + (size_t)wave * k, w + (size_t)wave * k,
+                             s_ids + wave * k);
+  }
   __syncthreads();
   permute_block(s_ids, T * k, E, nbits, sm + kSmallSlots, offsets, sorted_slot, slot_to_row, active, n_active);
 }
@@ -585,14 +678,20 @@ hipError_t launch_small(const float* logits, int T, int E, int k, int nbits, int
                         int* expert_offsets, int* sorted_slot, int* slot_to_row, int* active_experts,
                         int* n_active, hipStream_t stream) {
   static std::atomic<uint64_t> attr_done{0};
+  constexpr int kScratch = kPermWaves * 3 * kWave;   // the routing waves' selection scratch
   const hipError_t attr = ensure_dynamic_lds(reinterpret_cast<const void*>(&route_permute_small_kernel<PL>),
-                                             (kSmallSlots + kPermWaves * kMaxExperts + 2 * kPermWaves) * (int)sizeof(int),
+                                             (kSmallSlots + kPermWaves * kMaxExperts + 2 * kPermWaves + kScratch) *
+                                                 (int)sizeof(int),
                                              attr_done);
   if (attr != hipSuccess) return attr;
-  const size_t shmem = (size_t)(kSmallSlots + kPermWaves * E + 2 * kPermWaves) * sizeof(int);
+  const size_t shmem = (size_t)(kSmallSlots + kPermWaves * E + 2 * kPermWaves + kScratch) * sizeof(int);
+  // k rounds cost ~0.24 us (256 experts) to ~0.39 us (512) each, the threshold select about
+  // as much as 14 rounds; NVFP4MOE_SMALL_SELECT=rounds|thresh forces one (tests, tuning)
+  const char* sel = std::getenv("NVFP4MOE_SMALL_SELECT");
+  const int thresh = sel ? (!std::strcmp(sel, "thresh") ? 1 : 0) : (k >= 16 ? 1 : 0);
   route_permute_small_kernel<PL><<<1, kPermThreads, shmem, stream>>>(logits, T, E, k, nbits, topk_ids, topk_w,
                                                                     expert_offsets, sorted_slot, slot_to_row,
-                                                                    active_experts, n_active);
+                                                                    active_experts, n_active, thresh);
   return hipGetLastError();
 }
 

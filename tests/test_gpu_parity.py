@@ -224,13 +224,16 @@ def test_both_routers_bit_exact(router, T, E, k, monkeypatch):
     np.testing.assert_allclose(np_(r["topk_w"]), w, rtol=1e-6, atol=0)
 
 
+@pytest.mark.parametrize("select", ["rounds", "thresh"])
 @pytest.mark.parametrize("T,E,k", [(16, 1024, 64), (16, 512, 22), (2, 64, 64), (7, 100, 7), (1, 256, 8),
-                                   (1, 1, 1), (16, 8, 2)])
-def test_small_route_permute_bit_exact(T, E, k, monkeypatch):
-    """Few tokens: routing (k rounds of wave argmax) and permutation in one workgroup and one
-    launch, against the oracle; ties, -0/+0 and an all-equal row planted."""
-    say("small route", T, E, k)
+                                   (1, 1, 1), (16, 8, 2), (3, 1000, 17)])
+def test_small_route_permute_bit_exact(T, E, k, select, monkeypatch):
+    """Few tokens: routing and permutation in one workgroup and one launch, against the oracle,
+    with each of the two top-k selections (k rounds of wave argmax; the threshold select);
+    ties, -0/+0 and an all-equal row planted."""
+    say("small route", T, E, k, select)
     monkeypatch.setenv("NVFP4MOE_ROUTER", "small")
+    monkeypatch.setenv("NVFP4MOE_SMALL_SELECT", select)
     lg = inputs.random_fp32((T, E), 7 * T + E + k)
     lg[0, : min(E, 9)] = 1.5                      # equal logits at the top of row 0
     if E > 40:
