@@ -492,6 +492,52 @@ __device__ __forceinline__ void route_token_thresh(const float* __restrict__ row
   }
 }
 
+// The permutation of at most 64 slots without further barriers: every wave holds the slot ids
+// in its lanes (slot s in lane s) and derives its share of the outputs by counting over the
+// slots: slot s goes to row offsets[id_s] + (earlier slots with its id), offsets[e] counts
+// the slots with a lower id, and the active list holds the distinct ids in ascending order
+// (an id's position counts the distinct ids below it). Wave 0 writes the per-slot rows, the
+// active ids and their count; the threads write offsets[0 .. E] (thread e, and thread 0 also
+// entry 1024 when E = 1024) and the -1 past the active ids. Same outputs, bit for bit, as
+// permute_block.
+__device__ __forceinline__ void permute_few(const int* ids, int S, int E, int* __restrict__ offsets,
+                                            int* __restrict__ sorted_slot, int* __restrict__ slot_to_row,
+                                            int* __restrict__ active, int* __restrict__ n_active) {
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int id = lane < S ? ids[lane] : 0x7fffffff;
+  int same_before = 0, lower = 0;
+  for (int t = 0; t < S; ++t) {
+    const int it = __builtin_amdgcn_readlane(id, t);
+    same_before += (t < lane && it == id) ? 1 : 0;
+    lower += it < id ? 1 : 0;
+  }
+  const bool first = lane < S && same_before == 0;
+  const uint64_t fm = __ballot(first);
+  const int nact = __popcll(fm);
+  for (int e = tid; e <= E; e += kPermThreads) {
+    int cnt = 0;
+    for (int t = 0; t < S; ++t) cnt += __builtin_amdgcn_readlane(id, t) < e ? 1 : 0;
+    offsets[e] = cnt;
+    if (e >= nact && e < E) active[e] = -1;
+  }
+  if (wave == 0) {
+    int drank = 0;
+    uint64_t m = fm;
+    while (m) {
+      const int t = __builtin_ctzll(m);
+      m &= m - 1;
+      drank += __builtin_amdgcn_readlane(id, t) < id ? 1 : 0;
+    }
+    if (lane < S) {
+      const int row = lower + same_before;
+      slot_to_row[lane] = row;
+      sorted_slot[row] = lane;
+      if (first) active[drank] = id;
+    }
+    if (lane == 0) n_active[0] = nact;
+  }
+}
+
 template <int PL>
 __global__ __launch_bounds__(kPermThreads) void route_permute_small_kernel(const float* __restrict__ logits,
                                                                            int T, int E, int k, int nbits,
@@ -502,7 +548,7 @@ __global__ __launch_bounds__(kPermThreads) void route_permute_small_kernel(const
                                                                            int* __restrict__ slot_to_row,
                                                                            int* __restrict__ active,
                                                                            int* __restrict__ n_active,
-                                                                           int thresh) {
+                                                                           int thresh, int full_permute) {
   extern __shared__ int sm[];
   int* s_ids = sm;                   // [T * k] expert ids
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
@@ -517,7 +563,10 @@ __global__ __launch_bounds__(kPermThreads) void route_permute_small_kernel(const
                              s_ids + wave * k);
   }
   __syncthreads();
-  permute_block(s_ids, T * k, E, nbits, sm + kSmallSlots, offsets, sorted_slot, slot_to_row, active, n_active);
+  if (T * k <= kWave && !full_permute)
+    permute_few(s_ids, T * k, E, offsets, sorted_slot, slot_to_row, active, n_active);
+  else
+    permute_block(s_ids, T * k, E, nbits, sm + kSmallSlots, offsets, sorted_slot, slot_to_row, active, n_active);
 }
 
 // Many slots: the permutation in two launches over chunks of slots, so that the scattered
@@ -689,9 +738,14 @@ hipError_t launch_small(const float* logits, int T, int E, int k, int nbits, int
   // as much as 14 rounds; NVFP4MOE_SMALL_SELECT=rounds|thresh forces one (tests, tuning)
   const char* sel = std::getenv("NVFP4MOE_SMALL_SELECT");
   const int thresh = sel ? (!std::strcmp(sel, "thresh") ? 1 : 0) : (k >= 16 ? 1 : 0);
+  // up to 64 slots the permutation needs no further barrier (permute_few);
+  // NVFP4MOE_SMALL_PERMUTE=full keeps the general one (tests)
+  const char* pf = std::getenv("NVFP4MOE_SMALL_PERMUTE");
+  const int full_permute = pf && !std::strcmp(pf, "full") ? 1 : 0;
   route_permute_small_kernel<PL><<<1, kPermThreads, shmem, stream>>>(logits, T, E, k, nbits, topk_ids, topk_w,
                                                                     expert_offsets, sorted_slot, slot_to_row,
-                                                                    active_experts, n_active, thresh);
+                                                                    active_experts, n_active, thresh,
+                                                                    full_permute);
   return hipGetLastError();
 }
 

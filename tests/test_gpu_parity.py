@@ -226,11 +226,12 @@ def test_both_routers_bit_exact(router, T, E, k, monkeypatch):
 
 @pytest.mark.parametrize("select", ["rounds", "thresh"])
 @pytest.mark.parametrize("T,E,k", [(16, 1024, 64), (16, 512, 22), (2, 64, 64), (7, 100, 7), (1, 256, 8),
-                                   (1, 1, 1), (16, 8, 2), (3, 1000, 17)])
+                                   (1, 1, 1), (16, 8, 2), (3, 1000, 17), (1, 1024, 64), (1, 512, 22)])
 def test_small_route_permute_bit_exact(T, E, k, select, monkeypatch):
     """Few tokens: routing and permutation in one workgroup and one launch, against the oracle,
     with each of the two top-k selections (k rounds of wave argmax; the threshold select);
-    ties, -0/+0 and an all-equal row planted."""
+    up to 64 slots the barrier-free permutation, above it the general one; ties, -0/+0 and an
+    all-equal row planted."""
     say("small route", T, E, k, select)
     monkeypatch.setenv("NVFP4MOE_ROUTER", "small")
     monkeypatch.setenv("NVFP4MOE_SMALL_SELECT", select)
@@ -242,6 +243,19 @@ def test_small_route_permute_bit_exact(T, E, k, select, monkeypatch):
     if T >= 3:
         lg[1, :] = 0.25                           # an all-tie row
     _check_route(lg, k, E)
+
+
+@pytest.mark.parametrize("T,E,k", [(1, 256, 8), (2, 1024, 32), (7, 100, 9), (3, 1000, 17)])
+def test_small_permutation_paths_agree(T, E, k, monkeypatch):
+    """Up to 64 slots: the barrier-free permutation and the general one give the same bits
+    (both against the oracle)."""
+    say("small permutation paths", T, E, k)
+    monkeypatch.setenv("NVFP4MOE_ROUTER", "small")
+    lg = inputs.random_fp32((T, E), 3 * T + E + k)
+    lg[0, : min(E, 5)] = 0.5
+    for full in ("full", "few"):
+        monkeypatch.setenv("NVFP4MOE_SMALL_PERMUTE", full)
+        _check_route(lg, k, E)
 
 
 def test_route_permute_at_the_slot_limit():
