@@ -21,6 +21,10 @@
 //      holding the same expert comes from wavefront ballots over the bits of the expert id
 //      (lanes with equal ids = AND of matching ballots) and a popcount of the lower lanes.
 //      Slots therefore land in ascending order within each expert: a stable counting sort.
+// Many slots (>= 16384): the same in two launches over chunks of slots. Few tokens (<= 16):
+// routing and permutation in one workgroup and one launch (route_permute_small_kernel), with
+// k rounds of wave argmax below top-16 and a threshold select from top-16 on, and up to 64
+// slots a permutation that every wave derives from the slot ids alone, with no barrier.
 #include <cstdlib>
 #include <cstring>
 
