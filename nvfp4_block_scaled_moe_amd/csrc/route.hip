@@ -6,11 +6,12 @@
 // expert-scatter/gather of a fused MoE ("The 2x Gap", section "Discovering the sgl_kernel
 // Alternative"): rows of one expert become contiguous so each expert runs one GEMM.
 //
-// Router: one wavefront per token. Each lane holds E/64 logits in registers; a radix select
-// over order-preserving keys finds the k-th largest logit with wave ballots, the selected
-// experts are ranked (descending logit, ties to the lower id) in one wave-uniform pass. The weights
+// Router: one wavefront per token. Each lane holds E/64 logits in registers; a bitwise search
+// over order-preserving keys finds the k-th largest logit with wave ballots, and the k kept
+// experts are ranked (descending logit, ties to the lower id) one per lane. The weights
 // exp(l_j - l_max) / sum_j' exp(l_j' - l_max) over the k kept logits equal softmax over E
-// followed by renormalisation; they are computed in float64 and rounded once.
+// followed by renormalisation; they are computed in float64 and rounded once. (Fewer than
+// 256 tokens: a workgroup per token sorts instead.)
 //
 // Permutation: one 1024-thread workgroup, deterministic by construction:
 //   1. each wave counts the experts of its contiguous slice of slots (LDS integer atomics:
@@ -49,13 +50,6 @@ __device__ __forceinline__ uint32_t logit_key(float x) {
 }
 
 __device__ __forceinline__ int wave_count(bool pred) { return __popcll(__ballot(pred)); }
-
-__device__ __forceinline__ double readlane_f64(double v, int l) {
-  const uint64_t b = (uint64_t)__double_as_longlong(v);
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, l);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), l);
-  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
-}
 
 // Router for one token per workgroup (max(NE/2, 64) threads, NE = E rounded up to a power of two,
 // 64 <= NE <= 1024): a bitonic sort in LDS of 64-bit keys (order-preserving logit key << 32 |
@@ -113,94 +107,134 @@ __global__ __launch_bounds__(router_sort_threads<NE>()) void router_sort_kernel(
   }
 }
 
-// One token's top-k in one wavefront (router_kernel): lane l holds the logits of experts l + 64 i (i < PL); ids[0, k) and w[0, k) of the token are
-// written (and, if lds_ids is given, the ids there too).
-//  1. Radix select of the k-th largest key t: 32 steps, each counting keys >= a candidate with
-//     wave ballots (no data movement between lanes).
-//  2. Selected: keys > t, plus the lowest ids among keys == t until k are taken (ballot order
-//     within a register is ascending lane = ascending id, registers ascend in id).
-//  3. Rank of each selected expert = number of selected experts that come first (larger
-//     value, or equal value and lower id), counted in one wave-uniform pass over the
-//     selected set (lane reads, no shuffles).
-//  4. Weights exp(l - l_max) / sum over the selected, in float64, rounded once to float32.
+// Top-k of one token by one wave without k serial rounds (the few-token kernel below also
+// has route_token_rounds; both give the same ids, order and weights):
+// the k-th largest key th is found bit by bit (the largest th with at least k keys >= th; a
+// ballot per register and bit), the keys above th are kept and the lowest ids among those
+// equal to th fill the rest, the k kept (key, id, logit) go to the wave's LDS scratch in id
+// order, lane j takes entry j and counts the kept entries ahead of it (larger key, or equal
+// key and lower id), and lane r then takes the entry of rank r, as round r would have.
+// scratch: 3 x 64 words of the wave's own LDS.
 template <int PL>
-__device__ __forceinline__ void route_token_select(const float* __restrict__ row, int E, int k, int lane,
-                                                   int* __restrict__ ids, float* __restrict__ w, int* lds_ids) {
-  float v[PL];
+__device__ __forceinline__ void route_token_thresh(const float* __restrict__ row, int E, int k, int lane,
+                                                   int* __restrict__ ids, float* __restrict__ w, int* lds_ids,
+                                                   uint32_t* scratch) {
   uint32_t key[PL];
-  bool av[PL];
+  float v[PL];
 #pragma unroll
   for (int i = 0; i < PL; ++i) {
     const int e = lane + kWave * i;
-    av[i] = e < E;
-    const float x = av[i] ? row[e] : -INFINITY;
+    const float x = e < E ? row[e] : -INFINITY;
     v[i] = (x != x) ? -INFINITY : x;
-    key[i] = logit_key(x);
+    key[i] = e < E ? logit_key(x) : 0u;   // every real key is >= logit_key(-inf) > 0
   }
   uint32_t th = 0;
   for (int bit = 31; bit >= 0; --bit) {
     const uint32_t cand = th | (1u << bit);
     int cnt = 0;
 #pragma unroll
-    for (int i = 0; i < PL; ++i) cnt += wave_count(av[i] && key[i] >= cand);
+    for (int i = 0; i < PL; ++i) cnt += wave_count(key[i] >= cand);
     if (cnt >= k) th = cand;
   }
   int need = k;
 #pragma unroll
-  for (int i = 0; i < PL; ++i) need -= wave_count(av[i] && key[i] > th);
-  bool sel[PL];
-  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int i = 0; i < PL; ++i) need -= wave_count(key[i] > th);
+  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  int base = 0;   // kept entries in the registers before i (ids ascend with i, then lane)
 #pragma unroll
   for (int i = 0; i < PL; ++i) {
-    const uint64_t eq = __ballot(av[i] && key[i] == th);
-    sel[i] = (av[i] && key[i] > th) || (((eq >> lane) & 1ull) && __popcll(eq & below) < need);
+    const uint64_t eq = __ballot(key[i] == th);
+    const bool kept = key[i] > th || (((eq >> lane) & 1ull) && __popcll(eq & below) < need);
     const int c = __popcll(eq);
     need = need > c ? need - c : 0;
-  }
-  int rank[PL];
-#pragma unroll
-  for (int i = 0; i < PL; ++i) rank[i] = 0;
-#pragma unroll
-  for (int j = 0; j < PL; ++j) {
-    uint64_t m = __ballot(sel[j]);
-    while (m) {
-      const int l = __builtin_ctzll(m);
-      m &= m - 1;
-      const uint32_t ky = (uint32_t)__builtin_amdgcn_readlane((int)key[j], l);
-      const int ey = l + kWave * j;
-#pragma unroll
-      for (int i = 0; i < PL; ++i)
-        rank[i] += (sel[i] && (ky > key[i] || (ky == key[i] && ey < lane + kWave * i))) ? 1 : 0;
+    const uint64_t km = __ballot(kept);
+    if (kept) {
+      const int pos = base + __popcll(km & below);
+      scratch[pos] = key[i];
+      scratch[kWave + pos] = (uint32_t)(lane + kWave * i);
+      scratch[2 * kWave + pos] = __float_as_uint(v[i]);
     }
+    base += __popcll(km);
   }
-  float vmax = 0.0f;
-#pragma unroll
-  for (int i = 0; i < PL; ++i) {
-    const uint64_t m = __ballot(sel[i] && rank[i] == 0);
-    if (m) vmax = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(v[i]), __builtin_ctzll(m)));
+  uint32_t kj = 0, ej = 0, xj = 0;
+  if (lane < k) {
+    kj = scratch[lane];
+    ej = scratch[kWave + lane];
+    xj = scratch[2 * kWave + lane];
   }
-  double ex[PL];
-  double sum = 0.0;
-#pragma unroll
-  for (int j = 0; j < PL; ++j) {
-    ex[j] = sel[j] ? exp((double)v[j] - (double)vmax) : 0.0;
-    uint64_t m = __ballot(sel[j]);
-    while (m) {
-      const int l = __builtin_ctzll(m);
-      m &= m - 1;
-      sum += readlane_f64(ex[j], l);
-    }
+  int rank = 0;
+  for (int m = 0; m < k; ++m) {
+    const uint32_t km = (uint32_t)__builtin_amdgcn_readlane((int)kj, m);
+    const uint32_t em = (uint32_t)__builtin_amdgcn_readlane((int)ej, m);
+    rank += (km > kj || (km == kj && em < ej)) ? 1 : 0;
   }
+  if (lane < k) {
+    scratch[rank] = ej;
+    scratch[kWave + rank] = xj;
+  }
+  int my_e = 0;
+  float my_x = 0.0f;
+  if (lane < k) {
+    my_e = (int)scratch[lane];
+    my_x = __uint_as_float(scratch[kWave + lane]);
+  }
+  const double m = (double)__uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(my_x), 0));
+  const double ex = lane < k ? exp((double)my_x - m) : 0.0;
+  double sum = ex;
 #pragma unroll
-  for (int i = 0; i < PL; ++i) {
-    if (sel[i]) {
-      ids[rank[i]] = lane + kWave * i;
-      w[rank[i]] = (float)(ex[i] / sum);
-      if (lds_ids) lds_ids[rank[i]] = lane + kWave * i;
-    }
+  for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o, kWave);
+  if (lane < k) {
+    ids[lane] = my_e;
+    w[lane] = (float)(ex / sum);
+    if (lds_ids) lds_ids[lane] = my_e;
   }
 }
 
+// The permutation of at most 64 slots without further barriers: every wave holds the slot ids
+// in its lanes (slot s in lane s) and derives its share of the outputs by counting over the
+// slots: slot s goes to row offsets[id_s] + (earlier slots with its id), offsets[e] counts
+// the slots with a lower id, and the active list holds the distinct ids in ascending order
+// (an id's position counts the distinct ids below it). Wave 0 writes the per-slot rows, the
+// active ids and their count; the threads write offsets[0 .. E] (thread e, and thread 0 also
+// entry 1024 when E = 1024) and the -1 past the active ids. Same outputs, bit for bit, as
+// permute_block.
+__device__ __forceinline__ void permute_few(const int* ids, int S, int E, int* __restrict__ offsets,
+                                            int* __restrict__ sorted_slot, int* __restrict__ slot_to_row,
+                                            int* __restrict__ active, int* __restrict__ n_active) {
+  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+  const int id = lane < S ? ids[lane] : 0x7fffffff;
+  int same_before = 0, lower = 0;
+  for (int t = 0; t < S; ++t) {
+    const int it = __builtin_amdgcn_readlane(id, t);
+    same_before += (t < lane && it == id) ? 1 : 0;
+    lower += it < id ? 1 : 0;
+  }
+  const bool first = lane < S && same_before == 0;
+  const uint64_t fm = __ballot(first);
+  const int nact = __popcll(fm);
+  for (int e = tid; e <= E; e += kPermThreads) {
+    int cnt = 0;
+    for (int t = 0; t < S; ++t) cnt += __builtin_amdgcn_readlane(id, t) < e ? 1 : 0;
+    offsets[e] = cnt;
+    if (e >= nact && e < E) active[e] = -1;
+  }
+  if (wave == 0) {
+    int drank = 0;
+    uint64_t m = fm;
+    while (m) {
+      const int t = __builtin_ctzll(m);
+      m &= m - 1;
+      drank += __builtin_amdgcn_readlane(id, t) < id ? 1 : 0;
+    }
+    if (lane < S) {
+      const int row = lower + same_before;
+      slot_to_row[lane] = row;
+      sorted_slot[row] = lane;
+      if (first) active[drank] = id;
+    }
+    if (lane == 0) n_active[0] = nact;
+  }
+}
 
 template <int PL>
 __global__ __launch_bounds__(kRouterWaves* kWave) void router_kernel(const float* __restrict__ logits,
@@ -208,9 +242,12 @@ __global__ __launch_bounds__(kRouterWaves* kWave) void router_kernel(const float
                                                                      int* __restrict__ ids,
                                                                      float* __restrict__ w) {
   const int lane = threadIdx.x % kWave;
-  const int t = blockIdx.x * kRouterWaves + threadIdx.x / kWave;
+  const int wave = threadIdx.x / kWave;
+  const int t = blockIdx.x * kRouterWaves + wave;
+  __shared__ uint32_t scratch[kRouterWaves][3 * kWave];
   if (t >= T) return;   // t is the same for the whole wave
-  route_token_select<PL>(logits + (size_t)t * E, E, k, lane, ids + (size_t)t * k, w + (size_t)t * k, nullptr);
+  route_token_thresh<PL>(logits + (size_t)t * E, E, k, lane, ids + (size_t)t * k, w + (size_t)t * k, nullptr,
+                         scratch[wave]);
 }
 
 // Histogram of ids[lo, hi) into one wave's counter row (LDS atomics); the ids of kPermBatch
@@ -411,134 +448,6 @@ __device__ __forceinline__ void route_token_rounds(const float* __restrict__ row
     ids[lane] = my_e;
     w[lane] = (float)(ex / sum);
     lds_ids[lane] = my_e;
-  }
-}
-
-// The same selection, order and weights as route_token_rounds without its k serial rounds:
-// the k-th largest key th is found bit by bit (the largest th with at least k keys >= th; a
-// ballot per register and bit), the keys above th are kept and the lowest ids among those
-// equal to th fill the rest, the k kept (key, id, logit) go to the wave's LDS scratch in id
-// order, lane j takes entry j and counts the kept entries ahead of it (larger key, or equal
-// key and lower id), and lane r then takes the entry of rank r, as round r would have.
-// scratch: 3 x 64 words of the wave's own LDS.
-template <int PL>
-__device__ __forceinline__ void route_token_thresh(const float* __restrict__ row, int E, int k, int lane,
-                                                   int* __restrict__ ids, float* __restrict__ w, int* lds_ids,
-                                                   uint32_t* scratch) {
-  uint32_t key[PL];
-  float v[PL];
-#pragma unroll
-  for (int i = 0; i < PL; ++i) {
-    const int e = lane + kWave * i;
-    const float x = e < E ? row[e] : -INFINITY;
-    v[i] = (x != x) ? -INFINITY : x;
-    key[i] = e < E ? logit_key(x) : 0u;   // every real key is >= logit_key(-inf) > 0
-  }
-  uint32_t th = 0;
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t cand = th | (1u << bit);
-    int cnt = 0;
-#pragma unroll
-    for (int i = 0; i < PL; ++i) cnt += wave_count(key[i] >= cand);
-    if (cnt >= k) th = cand;
-  }
-  int need = k;
-#pragma unroll
-  for (int i = 0; i < PL; ++i) need -= wave_count(key[i] > th);
-  const uint64_t below = lane == 0 ? 0ull : (~0ull >> (64 - lane));
-  int base = 0;   // kept entries in the registers before i (ids ascend with i, then lane)
-#pragma unroll
-  for (int i = 0; i < PL; ++i) {
-    const uint64_t eq = __ballot(key[i] == th);
-    const bool kept = key[i] > th || (((eq >> lane) & 1ull) && __popcll(eq & below) < need);
-    const int c = __popcll(eq);
-    need = need > c ? need - c : 0;
-    const uint64_t km = __ballot(kept);
-    if (kept) {
-      const int pos = base + __popcll(km & below);
-      scratch[pos] = key[i];
-      scratch[kWave + pos] = (uint32_t)(lane + kWave * i);
-      scratch[2 * kWave + pos] = __float_as_uint(v[i]);
-    }
-    base += __popcll(km);
-  }
-  uint32_t kj = 0, ej = 0, xj = 0;
-  if (lane < k) {
-    kj = scratch[lane];
-    ej = scratch[kWave + lane];
-    xj = scratch[2 * kWave + lane];
-  }
-  int rank = 0;
-  for (int m = 0; m < k; ++m) {
-    const uint32_t km = (uint32_t)__builtin_amdgcn_readlane((int)kj, m);
-    const uint32_t em = (uint32_t)__builtin_amdgcn_readlane((int)ej, m);
-    rank += (km > kj || (km == kj && em < ej)) ? 1 : 0;
-  }
-  if (lane < k) {
-    scratch[rank] = ej;
-    scratch[kWave + rank] = xj;
-  }
-  int my_e = 0;
-  float my_x = 0.0f;
-  if (lane < k) {
-    my_e = (int)scratch[lane];
-    my_x = __uint_as_float(scratch[kWave + lane]);
-  }
-  const double m = (double)__uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)__float_as_uint(my_x), 0));
-  const double ex = lane < k ? exp((double)my_x - m) : 0.0;
-  double sum = ex;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) sum += __shfl_xor(sum, o, kWave);
-  if (lane < k) {
-    ids[lane] = my_e;
-    w[lane] = (float)(ex / sum);
-    lds_ids[lane] = my_e;
-  }
-}
-
-// The permutation of at most 64 slots without further barriers: every wave holds the slot ids
-// in its lanes (slot s in lane s) and derives its share of the outputs by counting over the
-// slots: slot s goes to row offsets[id_s] + (earlier slots with its id), offsets[e] counts
-// the slots with a lower id, and the active list holds the distinct ids in ascending order
-// (an id's position counts the distinct ids below it). Wave 0 writes the per-slot rows, the
-// active ids and their count; the threads write offsets[0 .. E] (thread e, and thread 0 also
-// entry 1024 when E = 1024) and the -1 past the active ids. Same outputs, bit for bit, as
-// permute_block.
-__device__ __forceinline__ void permute_few(const int* ids, int S, int E, int* __restrict__ offsets,
-                                            int* __restrict__ sorted_slot, int* __restrict__ slot_to_row,
-                                            int* __restrict__ active, int* __restrict__ n_active) {
-  const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
-  const int id = lane < S ? ids[lane] : 0x7fffffff;
-  int same_before = 0, lower = 0;
-  for (int t = 0; t < S; ++t) {
-    const int it = __builtin_amdgcn_readlane(id, t);
-    same_before += (t < lane && it == id) ? 1 : 0;
-    lower += it < id ? 1 : 0;
-  }
-  const bool first = lane < S && same_before == 0;
-  const uint64_t fm = __ballot(first);
-  const int nact = __popcll(fm);
-  for (int e = tid; e <= E; e += kPermThreads) {
-    int cnt = 0;
-    for (int t = 0; t < S; ++t) cnt += __builtin_amdgcn_readlane(id, t) < e ? 1 : 0;
-    offsets[e] = cnt;
-    if (e >= nact && e < E) active[e] = -1;
-  }
-  if (wave == 0) {
-    int drank = 0;
-    uint64_t m = fm;
-    while (m) {
-      const int t = __builtin_ctzll(m);
-      m &= m - 1;
-      drank += __builtin_amdgcn_readlane(id, t) < id ? 1 : 0;
-    }
-    if (lane < S) {
-      const int row = lower + same_before;
-      slot_to_row[lane] = row;
-      sorted_slot[row] = lane;
-      if (first) active[drank] = id;
-    }
-    if (lane == 0) n_active[0] = nact;
   }
 }
 
