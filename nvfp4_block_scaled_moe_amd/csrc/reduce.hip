@@ -6,7 +6,9 @@
 // float32 fused multiply-adds in ascending j, so the result does not depend on thread
 // timing. HBM-bound: k rows of Y read and one bf16 row written per token; each thread
 // handles 8 consecutive columns with 16/32-byte vector accesses, and requests the rows of
-// 8 slots at a time so their latencies overlap.
+// 8 slots at a time so their latencies overlap. Many tokens: one workgroup per token
+// (H/8 threads rounded up to whole waves, up to 1024), so no workgroup idles on a partial
+// column block; few tokens: 256-thread column blocks, spreading a token over more CUs.
 #include "common.h"
 #include "kernels.h"
 
@@ -14,19 +16,22 @@ namespace nvfp4moe {
 
 namespace {
 
-constexpr int kRedThreads = 256;
+constexpr int kRedThreads = 256;       // column block for few tokens
+constexpr int kRedMaxThreads = 1024;   // one workgroup per token from kRedRowTokens tokens on
+constexpr int kRedRowTokens = 256;
 
 constexpr int kRedBatch = 8;   // slots whose rows are requested together
 
 template <bool YBF16>
-__global__ __launch_bounds__(kRedThreads) void unpermute_reduce_kernel(const void* __restrict__ y,
+__global__ __launch_bounds__(kRedMaxThreads) void unpermute_reduce_kernel(const void* __restrict__ y,
                                                                        const int* __restrict__ slot_to_row,
                                                                        const float* __restrict__ topk_w,
                                                                        int k, int H,
                                                                        uint16_t* __restrict__ out) {
-  const int cblocks = (H / 8 + kRedThreads - 1) / kRedThreads;
+  const int nt = blockDim.x;
+  const int cblocks = (H / 8 + nt - 1) / nt;
   const int t = blockIdx.x / cblocks;
-  const int c = ((blockIdx.x - t * cblocks) * kRedThreads + threadIdx.x) * 8;
+  const int c = ((blockIdx.x - t * cblocks) * nt + threadIdx.x) * 8;
   if (c >= H) return;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   // Up to kRedBatch rows are requested before the first of them is summed; the sum itself
@@ -81,11 +86,13 @@ __global__ __launch_bounds__(kRedThreads) void unpermute_reduce_kernel(const voi
 hipError_t launch_unpermute_reduce(const void* y, bool y_bf16, const int* slot_to_row,
                                    const float* topk_w, int T, int k, int H, uint16_t* out,
                                    hipStream_t stream) {
-  const unsigned grid = (unsigned)((H / 8 + kRedThreads - 1) / kRedThreads) * (unsigned)T;
+  const int per = H / 8;   // threads a token's row needs
+  const int nt = T >= kRedRowTokens && per <= kRedMaxThreads ? (per + kWave - 1) / kWave * kWave : kRedThreads;
+  const unsigned grid = (unsigned)((per + nt - 1) / nt) * (unsigned)T;
   if (y_bf16)
-    unpermute_reduce_kernel<true><<<grid, kRedThreads, 0, stream>>>(y, slot_to_row, topk_w, k, H, out);
+    unpermute_reduce_kernel<true><<<grid, nt, 0, stream>>>(y, slot_to_row, topk_w, k, H, out);
   else
-    unpermute_reduce_kernel<false><<<grid, kRedThreads, 0, stream>>>(y, slot_to_row, topk_w, k, H, out);
+    unpermute_reduce_kernel<false><<<grid, nt, 0, stream>>>(y, slot_to_row, topk_w, k, H, out);
   return hipGetLastError();
 }
 

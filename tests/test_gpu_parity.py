@@ -627,7 +627,9 @@ def test_grouped_gemm_path_choice_by_size(monkeypatch):
 
 # ------------------------------------------------------------------ reduce
 @pytest.mark.parametrize("T,k,H,ydt", [(16, 2, 256, torch.float32), (7, 22, 64, torch.bfloat16),
-                                       (512, 8, 6144, torch.float32)])
+                                       (512, 8, 6144, torch.float32), (300, 8, 7168, torch.bfloat16),
+                                       (256, 3, 1000, torch.float32), (260, 2, 8200, torch.float32),
+                                       (255, 4, 7168, torch.float32)])
 def test_unpermute_reduce(T, k, H, ydt):
     say("reduce", T, k, H, ydt)
     rng = np.random.default_rng(T + k + H)
