@@ -22,16 +22,23 @@ constexpr int kRedRowTokens = 256;
 
 constexpr int kRedBatch = 8;   // slots whose rows are requested together
 
-template <bool YBF16>
-__global__ __launch_bounds__(kRedMaxThreads) void unpermute_reduce_kernel(const void* __restrict__ y,
+// NT = 0: one workgroup per token of blockDim.x threads (up to kRedMaxThreads); else column
+// blocks of NT threads.
+template <bool YBF16, int NT>
+__global__ __launch_bounds__(NT ? NT : kRedMaxThreads) void unpermute_reduce_kernel(const void* __restrict__ y,
                                                                        const int* __restrict__ slot_to_row,
                                                                        const float* __restrict__ topk_w,
                                                                        int k, int H,
                                                                        uint16_t* __restrict__ out) {
-  const int nt = blockDim.x;
-  const int cblocks = (H / 8 + nt - 1) / nt;
-  const int t = blockIdx.x / cblocks;
-  const int c = ((blockIdx.x - t * cblocks) * nt + threadIdx.x) * 8;
+  int t, c;
+  if (NT) {
+    const int cblocks = (H / 8 + NT - 1) / NT;
+    t = blockIdx.x / cblocks;
+    c = ((blockIdx.x - t * cblocks) * NT + threadIdx.x) * 8;
+  } else {
+    t = blockIdx.x;
+    c = threadIdx.x * 8;
+  }
   if (c >= H) return;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   // Up to kRedBatch rows are requested before the first of them is summed; the sum itself
@@ -87,12 +94,19 @@ hipError_t launch_unpermute_reduce(const void* y, bool y_bf16, const int* slot_t
                                    const float* topk_w, int T, int k, int H, uint16_t* out,
                                    hipStream_t stream) {
   const int per = H / 8;   // threads a token's row needs
-  const int nt = T >= kRedRowTokens && per <= kRedMaxThreads ? (per + kWave - 1) / kWave * kWave : kRedThreads;
-  const unsigned grid = (unsigned)((per + nt - 1) / nt) * (unsigned)T;
+  if (T >= kRedRowTokens && per <= kRedMaxThreads) {
+    const int nt = (per + kWave - 1) / kWave * kWave;
+    if (y_bf16)
+      unpermute_reduce_kernel<true, 0><<<T, nt, 0, stream>>>(y, slot_to_row, topk_w, k, H, out);
+    else
+      unpermute_reduce_kernel<false, 0><<<T, nt, 0, stream>>>(y, slot_to_row, topk_w, k, H, out);
+    return hipGetLastError();
+  }
+  const unsigned grid = (unsigned)((per + kRedThreads - 1) / kRedThreads) * (unsigned)T;
   if (y_bf16)
-    unpermute_reduce_kernel<true><<<grid, nt, 0, stream>>>(y, slot_to_row, topk_w, k, H, out);
+    unpermute_reduce_kernel<true, kRedThreads><<<grid, kRedThreads, 0, stream>>>(y, slot_to_row, topk_w, k, H, out);
   else
-    unpermute_reduce_kernel<false><<<grid, nt, 0, stream>>>(y, slot_to_row, topk_w, k, H, out);
+    unpermute_reduce_kernel<false, kRedThreads><<<grid, kRedThreads, 0, stream>>>(y, slot_to_row, topk_w, k, H, out);
   return hipGetLastError();
 }
 

@@ -367,6 +367,9 @@ GEMM_CASES = [
     ([1, 2, 3], 2048, 6144),
     ([2, 1], 64, 32768),            # longest row the bf16 prep holds in registers
     ([3, 5], 64, 32800),            # longer rows: the two-pass prep, K % 128 != 0
+    ([600, 0, 500], 256, 2048),     # >= 1024 rows of <= 2048 columns: a wave per row in the prep
+    ([700, 400], 128, 4096),        # ... <= 4096 columns
+    ([1030], 64, 992),              # ... K % 128 != 0, rows % 4 != 0
 ]
 
 
@@ -435,17 +438,18 @@ def test_grouped_gemm_amax_output():
     assert np_(amax)[0] == np.abs(np_(out)).max()
 
 
+@pytest.mark.parametrize("counts", [[70, 0, 150], [700, 0, 500]])
 @pytest.mark.parametrize("path,ksplit", [("stream", "1"), ("stream", "2"), ("mfma", "1"), ("mfma", "2")])
 @pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
-def test_grouped_gemm_amax_skips_nonfinite(path, ksplit, out_dtype, monkeypatch):
+def test_grouped_gemm_amax_skips_nonfinite(path, ksplit, out_dtype, counts, monkeypatch):
     """out_amax is the max |out| over the finite values written: a NaN activation row and a
     row whose one nonzero element is Inf give NaN and +-Inf outputs, which must not reach the
     amax (the global scale of the quantized h depends on it); with a bf16 output, the amax of
     the rounded values. Both paths, with and without split K."""
-    say("gemm amax non-finite", path, ksplit, out_dtype)
+    say("gemm amax non-finite", path, ksplit, out_dtype, counts)
     monkeypatch.setenv("NVFP4MOE_FORCE_PATH", path)
     monkeypatch.setenv("NVFP4MOE_STREAM_KSPLIT" if path == "stream" else "NVFP4MOE_LARGE_KSPLIT", ksplit)
-    d = _problem([70, 0, 150], 256, 2048, seed=13)
+    d = _problem(counts, 256, 2048, seed=13)
     a = d["a"].clone()
     a[3] = float("nan")
     a[100] = 0.0
