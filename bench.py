@@ -7,9 +7,10 @@ C ABI. Default workload: the decode MoE layer with 256 experts, top-8, 512 token
 (W4A16) -- the workload behind the pages' "0.8-55 TFLOPS at per-expert M=16-64" ("The 2x
 Gap", section "The Investigation So Far").
 
-Prints ONE JSON line: throughput (algorithmic TFLOP/s of the layer), the dominant kernel's
-HBM roofline (weight+scale+activation bytes per launch / launch time from HIP events
-recorded on the kernels' stream inside the timed region), and the oracle's CPU rate on a
+Prints ONE JSON line: throughput (algorithmic TFLOP/s of the layer, from the wall clock
+around steps that carry no instrumentation), the dominant kernel's HBM roofline
+(weight+scale+activation bytes per launch / launch time from HIP events recorded on the
+kernels' stream in an instrumented pass of as many steps), and the oracle's CPU rate on a
 bounded sample of the same workload.
 
 The line also carries the workload's token sweep (each token count's layer step replayed
@@ -343,8 +344,13 @@ def graph_times(torch, step, steps, warm_reps, dev):
 
 
 def measure(torch, ops, layer, wl, w, x, lg, T, mode, steps, warmup, graph=False, combine=False):
-    """Time `steps` eager layer forwards; HIP events on the current stream (the stream every
-    library call is launched on) bracket every stage of every step."""
+    """Time `steps` eager layer forwards with nothing else on the stream (the headline rate),
+    then two instrumented passes of `steps` forwards each: one HIP event per step boundary
+    (per-step device times: median, p10, p90) and seven events per step bracketing every stage
+    (stage means; the up/gate call's time for the roofline). Events go on the current stream,
+    the stream every library call is launched on; each event record costs the GPU a few
+    microseconds (about 3 us each, measured: 7 per decode step added ~22 us), which is why the
+    headline pass carries none."""
     k = wl.k
     S = T * k
     r = ops.moe_route_permute(lg, k)
@@ -365,17 +371,27 @@ def measure(torch, ops, layer, wl, w, x, lg, T, mode, steps, warmup, graph=False
         stage = None
         step_us = None
     else:
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(steps)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(steps):
-            step(evs[i])
+            step()
         torch.cuda.synchronize()
         ms = (time.perf_counter() - t0) * 1e3 / steps
+        bounds = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        bounds[0].record()
+        for i in range(steps):
+            step()
+            bounds[i + 1].record()
+        torch.cuda.synchronize()
+        step_us = stats_us([1e3 * bounds[i].elapsed_time(bounds[i + 1]) for i in range(steps)])
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(steps)]
+        for i in range(steps):
+            step(evs[i])
+        torch.cuda.synchronize()
         names = ["route_permute", "quantize_x", "up_gate_swiglu", "quantize_h", "down", "unpermute_reduce"]
         per = {n: [1e3 * e[j].elapsed_time(e[j + 1]) for e in evs] for j, n in enumerate(names)}
         stage = {n: round(sum(v) / len(v), 2) for n, v in per.items()}
-        step_us = stats_us([1e3 * e[0].elapsed_time(e[6]) for e in evs])
+        step_us["staged_mean"] = round(sum(1e3 * e[0].elapsed_time(e[6]) for e in evs) / steps, 2)
     act_in = T * wl.H * (2 if mode == ops.W4A16 else (17 / 32 if mx else 9 / 16))
     h_bytes = S * wl.F * (2 if mode == ops.W4A16 else (17 / 32 if mx else 4))
     up_bytes = w13_bytes + act_in + h_bytes

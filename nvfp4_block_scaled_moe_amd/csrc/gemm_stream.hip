@@ -240,9 +240,6 @@ __global__ __launch_bounds__(WAVES* kWave) void gemm_stream_kernel(const GemmArg
   };
   f32x4 acc[RBW][TBM];
   // Chunk c (u = c % kWin): decode ring entry d, refill it from offset voff, then the
-  // MFMAs, k-step-major so that consecutive MFMAs update different accumulators and the
-  // activation fragments are read once per k-step.
-  // Chunk c (u = c % kWin): decode ring entry d, refill it from offset voff, then the
   // MFMAs of token block 0 and, if the item has more than 16 rows (`two`, wave-uniform),
   // of token block 1; k-step-major inside a block, so that consecutive MFMAs update
   // different accumulators.
