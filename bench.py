@@ -251,8 +251,11 @@ def make_step(torch, ops, wl, w, x, lg, T, mode, paths, combine=False):
     def step(ev=None):
         mark = (lambda i: ev[i].record()) if ev else (lambda i: None)
         mark(0)
-        xx = ops.act_fp8_e4m3_roundtrip(x) if fp8 else x
-        rr = ops.moe_route_permute(lg, k)
+        if mode == ops.W4A16:   # routing + the token rows' preparation (one launch up to 16 tokens)
+            rr = ops.moe_dispatch_w4a16(lg, x, k, fp8_act=fp8)
+        else:
+            xx = ops.act_fp8_e4m3_roundtrip(x) if fp8 else x
+            rr = ops.moe_route_permute(lg, k)
         mark(1)
         common = dict(expert_offsets=rr["expert_offsets"], active_experts=rr["active_experts"],
                       n_active=rr["n_active"])
@@ -273,8 +276,8 @@ def make_step(torch, ops, wl, w, x, lg, T, mode, paths, combine=False):
                                                **common)
         elif mode == ops.W4A16:
             mark(2)
-            h = ops.moe_grouped_gemm_nvfp4(ops.W4A16, ops.EPI_SWIGLU, xx, w.w13_t,
-                                           gather_index=rr["sorted_slot"], gather_div=k, rows=S,
+            h = ops.moe_grouped_gemm_nvfp4(ops.W4A16_PREPARED, ops.EPI_SWIGLU, rr["x_prep"], w.w13_t,
+                                           gather_index=rr["sorted_slot"], gather_div=k, rows=S, a_rows=T,
                                            out_dtype=torch.bfloat16, **common)
             mark(3)
             paths["up"] = ops.last_dispatch()
@@ -426,8 +429,8 @@ def measure(torch, ops, layer, wl, w, x, lg, T, mode, steps, warmup, graph=False
                 peak=BF16_PEAK_TFLOPS, unit="TFLOP/s", frac=round(ach / BF16_PEAK_TFLOPS, 4), traffic=None,
                 flops_per_launch=up_flops, **timing,
                 timed="HIP events around the moe_grouped_gemm_nvfp4 call: " +
-                      ("act_prep_fp4_kernel" if mode == ops.W4A4 else "act_prep_kernel") + " (also builds the "
-                      "m-tile list) + gemm_large_kernel",
+                      ("act_prep_fp4_kernel (also builds the m-tile list)" if mode == ops.W4A4 else
+                       "mtile_schedule_kernel (rows prepared by moe_dispatch_w4a16)") + " + gemm_large_kernel",
                 flops_note="2*S*2F*H useful flops (rows of ragged m-tiles padded on the GPU are not counted); "
                            "f16 MFMA peak (the exact NVFP4 decode runs on v_mfma_f32_16x16x32_f16)")
             if mode == ops.W4A4:
@@ -438,8 +441,9 @@ def measure(torch, ops, layer, wl, w, x, lg, T, mode, steps, warmup, graph=False
                 bound="hbm", kernel="gemm_stream_kernel (up/gate + SwiGLU)", achieved=round(ach, 1),
                 peak=HBM_PEAK_GBS, unit="GB/s", frac=round(ach / HBM_PEAK_GBS, 4), traffic=None,
                 bytes_per_launch=int(up_bytes), **timing,
-                timed="HIP events around the moe_grouped_gemm_nvfp4 call: " +
-                      ("act_prep_kernel + " if mode == ops.W4A16 else "") + "gemm_stream_kernel",
+                timed="HIP events around the moe_grouped_gemm_nvfp4 call: gemm_stream_kernel" +
+                      (" (W4A16 rows prepared by moe_dispatch_w4a16 in the routing stage)" if mode == ops.W4A16
+                       else ""),
                 bytes_note="W13 packed+scales of touched experts (9/16 B/weight) + activations in + h out")
     return res
 

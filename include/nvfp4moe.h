@@ -74,8 +74,9 @@ typedef enum {
 } nvfp4moe_status;
 
 /* [P2] "The NVFP4 Pivot", [P4] "The Decision": weight-only FP4 with 16-bit
- * activations, or FP4 weights and FP4 activations. */
-typedef enum { NVFP4MOE_W4A16 = 0, NVFP4MOE_W4A4 = 1 } nvfp4moe_mode;
+ * activations, or FP4 weights and FP4 activations. W4A16_PREPARED: W4A16 with the token rows
+ * already prepared by moe_dispatch_w4a16. */
+typedef enum { NVFP4MOE_W4A16 = 0, NVFP4MOE_W4A4 = 1, NVFP4MOE_W4A16_PREPARED = 2 } nvfp4moe_mode;
 
 typedef enum { NVFP4MOE_EPI_NONE = 0, NVFP4MOE_EPI_SWIGLU = 1 } nvfp4moe_epilogue;
 
@@ -210,6 +211,36 @@ nvfp4moe_status moe_route_permute(const float* logits, int32_t T, int32_t E, int
 size_t moe_route_permute_workspace_size(int32_t T, int32_t E, int32_t k);
 
 /* ---------------------------------------------------------------------------
+ * moe_dispatch_w4a16 -- moe_route_permute plus the W4A16 up/gate GEMM's preparation of the
+ * token rows, for decode-sized batches where every launch of the layer costs several
+ * microseconds: up to 16 tokens (T * k <= 1024, H <= 8192) the routing workgroup and one
+ * workgroup per token row run as one launch; otherwise the rows are prepared by launches of
+ * their own after the routing. [P3] "Discovering the sgl_kernel Alternative" (a fused MoE's
+ * expert dispatch), [P1] section 3 (launch overhead of many small kernels), [P1] section 1
+ * (FP8 activations).
+ *
+ *   logits, T, E, k, topk_ids .. n_active   as moe_route_permute (same outputs, same bits).
+ *   x          device bf16 [T, H], 16-byte aligned; H >= 32, H % 32 == 0, T * H < 2^31.
+ *   fp8_act    0, or 1: the rows first take the FP8 E4M3 round trip of
+ *              act_fp8_e4m3_roundtrip (per-tensor scale over all of x), as that call writes.
+ *   x_prep     device, moe_prepared_act_bytes(T, H) bytes, 16-byte aligned (output): the rows
+ *              as moe_grouped_gemm_nvfp4 prepares bf16 activations for W4A16 (each row scaled
+ *              by a power of two into f16 range, f16 in the kernels' operand order, and the
+ *              exponents); its only reader is moe_grouped_gemm_nvfp4 in mode
+ *              NVFP4MOE_W4A16_PREPARED with a = x_prep, a_rows = T, K = H.
+ *   ws         moe_dispatch_w4a16_workspace_size(T, E, k, H, fp8_act) bytes, 16-byte aligned,
+ *              caller-owned scratch; too small -> NVFP4MOE_ERR_WORKSPACE.
+ * ------------------------------------------------------------------------- */
+nvfp4moe_status moe_dispatch_w4a16(const float* logits, const void* x, int32_t T, int32_t E, int32_t k,
+                                   int32_t H, int32_t fp8_act, int32_t* topk_ids, float* topk_w,
+                                   int32_t* expert_offsets, int32_t* sorted_slot, int32_t* slot_to_row,
+                                   int32_t* active_experts, int32_t* n_active, void* x_prep, void* ws,
+                                   size_t ws_bytes, void* stream);
+size_t moe_dispatch_w4a16_workspace_size(int32_t T, int32_t E, int32_t k, int32_t H, int32_t fp8_act);
+/* Bytes of prepared activations for rows x K (0 for invalid sizes). */
+size_t moe_prepared_act_bytes(int64_t rows, int32_t K);
+
+/* ---------------------------------------------------------------------------
  * moe_grouped_gemm_nvfp4 -- per expert e, rows expert_offsets[e] .. expert_offsets[e+1]:
  *     P = A_rows . W_e^T  (float32 accumulation of exact products) * w_g[e] (* a_g[0])
  *     EPI_NONE  : out = P                                  [rows, Nw]
@@ -220,6 +251,8 @@ size_t moe_route_permute_workspace_size(int32_t T, int32_t E, int32_t k);
  *   mode        W4A16: a is bf16 [a_rows, K]; a_scales and a_g are ignored (may be NULL).
  *               W4A4 : a is NVFP4 packed uint8 [a_rows, K/2] with a_scales uint8
  *                      [a_rows, K/16] and a_g device float[1].
+ *               W4A16_PREPARED: W4A16 with a = the x_prep of moe_dispatch_w4a16 (its T =
+ *                      a_rows, its H = K), so the call launches no preparation of its own.
  *   a_rows      rows of a.
  *   gather_index, gather_div
  *               NULL: GEMM row r reads a row r (a_rows must equal rows).

@@ -15,7 +15,7 @@ LIB_PATH = os.environ.get("NVFP4MOE_LIB") or os.path.join(os.path.dirname(os.pat
 
 # enums (include/nvfp4moe.h)
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(5)
-W4A16, W4A4 = 0, 1
+W4A16, W4A4, W4A16_PREPARED = 0, 1, 2
 EPI_NONE, EPI_SWIGLU = 0, 1
 F32, BF16 = 0, 1
 LAYOUT_ROW_MAJOR, LAYOUT_TILED = 0, 1
@@ -35,6 +35,10 @@ SIGNATURES = {
     "nvfp4_tiled_scales_bytes": (_sz, [_i64, _i64]),
     "moe_route_permute": (_int, [_vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "moe_route_permute_workspace_size": (_sz, [_i32, _i32, _i32]),
+    "moe_dispatch_w4a16": (_int, [_vp, _vp, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                  _vp, _sz, _vp]),
+    "moe_dispatch_w4a16_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32]),
+    "moe_prepared_act_bytes": (_sz, [_i64, _i32]),
     "moe_grouped_gemm_nvfp4": (_int, [_int, _int, _vp, _vp, _vp, _i64, _vp, _i32, _vp, _vp, _vp,
                                       _vp, _vp, _vp, _i32, _i32, _i32, _i32, _vp, _int, _vp, _vp,
                                       _sz, _vp]),

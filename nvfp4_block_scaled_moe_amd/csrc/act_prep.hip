@@ -19,6 +19,7 @@
 // One workgroup per row (bf16 input): the row is read once into registers (K up to 32768; longer
 // rows are read twice), its finite amax reduced, then converted. Traffic: 2 bytes read + 2 bytes
 // written per element.
+#include "act_rows.h"
 #include "common.h"
 #include "kernels.h"
 
@@ -100,12 +101,7 @@ __global__ __launch_bounds__(kPrepThreads) void act_prep_kernel(const uint16_t* 
     const int i = threadIdx.x + v * kPrepThreads;
     q[v] = i < nvec ? *reinterpret_cast<const uint4*>(row + 8 * i) : make_uint4(0u, 0u, 0u, 0u);
     const uint32_t w[4] = {q[v].x, q[v].y, q[v].z, q[v].w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float lo = fabsf(bf16_to_f32(w[j] & 0xffffu)), hi = fabsf(bf16_to_f32(w[j] >> 16));
-      m = fmaxf(m, lo <= 3.402823466e38f ? lo : 0.0f);
-      m = fmaxf(m, hi <= 3.402823466e38f ? hi : 0.0f);
-    }
+    m = bf16x8_finite_max(w, m);
   }
   __shared__ float red[kPrepThreads / kWave];
   m = wave_max(m);
@@ -113,27 +109,14 @@ __global__ __launch_bounds__(kPrepThreads) void act_prep_kernel(const uint16_t* 
   __syncthreads();
   float amax = red[0];
   for (int w = 1; w < kPrepThreads / kWave; ++w) amax = fmaxf(amax, red[w]);
-  int p = 0;
-  if (amax > 0.0f) {
-    int ex;
-    (void)frexpf(amax, &ex);  // amax = f * 2^ex, f in [0.5, 1)
-    p = ex - 15;              // amax * 2^-p in [2^14, 2^15)
-  }
+  const int p = f16_row_exponent(amax);
   if (threadIdx.x == 0) rexp[r] = p;
 #pragma unroll
   for (int v = 0; v < VPT; ++v) {
     const int i = threadIdx.x + v * kPrepThreads;
     if (i < K128 / 8) {
-      f16x8 o;
       const uint32_t w[4] = {q[v].x, q[v].y, q[v].z, q[v].w};   // zeros past K
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        o[2 * j] = (_Float16)ldexpf(bf16_to_f32(w[j] & 0xffffu), -p);
-        o[2 * j + 1] = (_Float16)ldexpf(bf16_to_f32(w[j] >> 16), -p);
-      }
-      // piece i = 16 c + 4 g + j (logical k = 128 c + 32 g + 8 j) -> physical 16 c + 4 j + g
-      const int c = i >> 4, g = (i >> 2) & 3, jj = i & 3;
-      *reinterpret_cast<f16x8*>(orow + 8 * (16 * c + 4 * jj + g)) = o;
+      *reinterpret_cast<f16x8*>(orow + 8 * prepared_piece(i)) = bf16x8_to_f16(w, p);
     }
   }
 }
@@ -156,14 +139,9 @@ __global__ __launch_bounds__(kPrepThreads) void act_prep_loop_kernel(const uint1
   const int nvec = K / 8;
   float m = 0.0f;
   for (int i = threadIdx.x; i < nvec; i += kPrepThreads) {
-    uint4 q = *reinterpret_cast<const uint4*>(row + 8 * i);
-    uint32_t w[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float lo = fabsf(bf16_to_f32(w[j] & 0xffffu)), hi = fabsf(bf16_to_f32(w[j] >> 16));
-      m = fmaxf(m, lo <= 3.402823466e38f ? lo : 0.0f);
-      m = fmaxf(m, hi <= 3.402823466e38f ? hi : 0.0f);
-    }
+    const uint4 q = *reinterpret_cast<const uint4*>(row + 8 * i);
+    const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+    m = bf16x8_finite_max(w, m);
   }
   __shared__ float red[kPrepThreads / kWave];
   m = wave_max(m);
@@ -171,27 +149,15 @@ __global__ __launch_bounds__(kPrepThreads) void act_prep_loop_kernel(const uint1
   __syncthreads();
   float amax = red[0];
   for (int w = 1; w < kPrepThreads / kWave; ++w) amax = fmaxf(amax, red[w]);
-  int p = 0;
-  if (amax > 0.0f) {
-    int ex;
-    (void)frexpf(amax, &ex);  // amax = f * 2^ex, f in [0.5, 1)
-    p = ex - 15;              // amax * 2^-p in [2^14, 2^15)
-  }
+  const int p = f16_row_exponent(amax);
   if (threadIdx.x == 0) rexp[r] = p;
   for (int i = threadIdx.x; i < K128 / 8; i += kPrepThreads) {
-    f16x8 o = (f16x8){0, 0, 0, 0, 0, 0, 0, 0};
+    uint32_t w[4] = {0u, 0u, 0u, 0u};
     if (i < nvec) {
-      uint4 q = *reinterpret_cast<const uint4*>(row + 8 * i);
-      uint32_t w[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        o[2 * j] = (_Float16)ldexpf(bf16_to_f32(w[j] & 0xffffu), -p);
-        o[2 * j + 1] = (_Float16)ldexpf(bf16_to_f32(w[j] >> 16), -p);
-      }
+      const uint4 q = *reinterpret_cast<const uint4*>(row + 8 * i);
+      w[0] = q.x; w[1] = q.y; w[2] = q.z; w[3] = q.w;
     }
-    // piece i = 16 * c + 4 * g + j (logical k = 128 c + 32 g + 8 j) -> physical 16 c + 4 j + g
-    const int c = i >> 4, g = (i >> 2) & 3, jj = i & 3;
-    *reinterpret_cast<f16x8*>(orow + 8 * (16 * c + 4 * jj + g)) = o;
+    *reinterpret_cast<f16x8*>(orow + 8 * prepared_piece(i)) = bf16x8_to_f16(w, p);
   }
 }
 

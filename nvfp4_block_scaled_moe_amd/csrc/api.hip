@@ -44,6 +44,9 @@ bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) %
 
 constexpr size_t kAlign = 256;
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+// Prepared W4A16 rows (moe_dispatch_w4a16's x_prep): f16 [rows, K128] in the GEMM's operand
+// order, then the rows' exponents int32 [rows].
+size_t prepared_rows_bytes(int64_t rows, int32_t K) { return round_up((size_t)rows * (((size_t)K + 127) / 128 * 128) * 2); }
 
 __global__ void zero_f32_kernel(float* p, int n) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
@@ -92,7 +95,8 @@ struct GemmWs {
 GemmWs gemm_ws_layout(int path, nvfp4moe_mode mode, int64_t a_rows, int32_t rows, int32_t E, int32_t Nw,
                       int32_t K) {
   GemmWs w{0, 0, 0, 0, 0, 0, 1};
-  if (mode == NVFP4MOE_W4A16 || (path == NVFP4MOE_PATH_MFMA && !large_a4_staged())) {
+  // (prepared W4A16 rows come with the call, in moe_dispatch_w4a16's x_prep)
+  if (mode == NVFP4MOE_W4A16 || (mode == NVFP4MOE_W4A4 && path == NVFP4MOE_PATH_MFMA && !large_a4_staged())) {
     const size_t K128 = ((size_t)K + 127) / 128 * 128;  // rows padded to whole 128-k chunks
     w.a16_bytes = round_up((size_t)a_rows * K128 * 2);
     w.rexp_bytes = round_up((size_t)a_rows * 4);
@@ -186,7 +190,7 @@ extern "C" {
 
 const char* nvfp4moe_last_error(void) { return g_last_error.c_str(); }
 int nvfp4moe_last_dispatch(void) { return g_last_dispatch; }
-int nvfp4moe_abi_version(void) { return 301; }
+int nvfp4moe_abi_version(void) { return 302; }
 
 // ------------------------------------------------------------------ quantize
 size_t nvfp4_quantize_workspace_size(int64_t B, int64_t R, int64_t C) {
@@ -348,6 +352,52 @@ nvfp4moe_status moe_route_permute(const float* logits, int32_t T, int32_t E, int
                     "moe_route_permute");
 }
 
+// ------------------------------------------------------------------ dispatch (route + row prep)
+size_t moe_prepared_act_bytes(int64_t rows, int32_t K) {
+  if (rows < 1 || K < 32 || K % 32 != 0) return 0;
+  return prepared_rows_bytes(rows, K) + round_up((size_t)rows * 4);
+}
+
+size_t moe_dispatch_w4a16_workspace_size(int32_t T, int32_t E, int32_t k, int32_t H, int32_t fp8_act) {
+  if (T < 1 || E < 1 || E > kMaxExperts || k < 1 || k > E || (int64_t)T * k > (1 << 24) || H < 32 || H % 32 != 0 ||
+      (int64_t)T * H >= (int64_t(1) << 31))
+    return 0;
+  return round_up(route_permute_ws_bytes(T, E, k)) + dispatch_rows_ws_bytes(T, H, fp8_act != 0);
+}
+
+nvfp4moe_status moe_dispatch_w4a16(const float* logits, const void* x, int32_t T, int32_t E, int32_t k,
+                                   int32_t H, int32_t fp8_act, int32_t* topk_ids, float* topk_w,
+                                   int32_t* expert_offsets, int32_t* sorted_slot, int32_t* slot_to_row,
+                                   int32_t* active_experts, int32_t* n_active, void* x_prep, void* ws,
+                                   size_t ws_bytes, void* stream) {
+  const char* fn = "moe_dispatch_w4a16";
+  if (!logits || !x || !topk_ids || !topk_w || !expert_offsets || !sorted_slot || !slot_to_row || !active_experts ||
+      !n_active || !x_prep)
+    return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: null tensor pointer", fn);
+  if (T < 1 || E < 1 || E > kMaxExperts || k < 1 || k > E || k > kMaxTopK)
+    return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: need T >= 1, 1 <= k <= min(E, %d), E <= %d (T=%d E=%d k=%d)", fn,
+                kMaxTopK, kMaxExperts, T, E, k);
+  if ((int64_t)T * k > (1 << 24)) return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: T * k must be <= 2^24", fn);
+  if (H < 32 || H % 32 != 0 || (int64_t)T * H >= (int64_t(1) << 31) ||
+      (int64_t)T * ((H + 127) / 128 * 128) * 2 >= (int64_t(1) << 31))
+    return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: need H >= 32, H %% 32 == 0 and T * H * 2 < 2^31 (H=%d)", fn, H);
+  if (fp8_act != 0 && fp8_act != 1) return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: fp8_act must be 0 or 1", fn);
+  if (!aligned(x, 16) || !aligned(x_prep, 16) || !aligned(ws, 16))
+    return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: x, x_prep and ws must be 16-byte aligned", fn);
+  const size_t route_ws = round_up(route_permute_ws_bytes(T, E, k));
+  const size_t need = route_ws + dispatch_rows_ws_bytes(T, H, fp8_act != 0);
+  if (ws_bytes < need || (need > 0 && !ws))
+    return fail(NVFP4MOE_ERR_WORKSPACE, "%s: workspace of %zu bytes needed, %zu given", fn, need, ws_bytes);
+  char* xp = static_cast<char*>(x_prep);
+  const ActPrep prep{static_cast<const uint16_t*>(x), H, fp8_act, reinterpret_cast<_Float16*>(xp),
+                     reinterpret_cast<int*>(xp + prepared_rows_bytes(T, H)),
+                     fp8_act ? static_cast<char*>(ws) + route_ws : nullptr};
+  return hip_status(launch_route_permute(logits, T, E, k, topk_ids, topk_w, expert_offsets, sorted_slot, slot_to_row,
+                                         active_experts, n_active, ws, route_ws, static_cast<hipStream_t>(stream),
+                                         &prep),
+                    fn);
+}
+
 // ------------------------------------------------------------------ weight tiling
 size_t nvfp4_tiled_codes_bytes(int64_t R, int64_t C) {
   if (R < 16 || R % 16 != 0 || C < 32 || C % 32 != 0) return 0;
@@ -404,8 +454,9 @@ nvfp4moe_status grouped_gemm_nvfp4_impl(const char* fn, nvfp4moe_mode mode, nvfp
                                         int32_t E, int32_t rows, int32_t Nw, int32_t K, void* out,
                                         nvfp4moe_dtype out_dtype, float* out_amax, void* ws,
                                         size_t ws_bytes, void* stream, const Combine* comb) {
-  if (mode != NVFP4MOE_W4A16 && mode != NVFP4MOE_W4A4)
+  if (mode != NVFP4MOE_W4A16 && mode != NVFP4MOE_W4A4 && mode != NVFP4MOE_W4A16_PREPARED)
     return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: bad mode %d", fn, (int)mode);
+  const bool prepared = mode == NVFP4MOE_W4A16_PREPARED;
   if (epi != NVFP4MOE_EPI_NONE && epi != NVFP4MOE_EPI_SWIGLU)
     return fail(NVFP4MOE_ERR_INVALID_ARG, "%s: bad epilogue %d", fn, (int)epi);
   if (out_dtype != NVFP4MOE_F32 && out_dtype != NVFP4MOE_BF16)
@@ -488,7 +539,11 @@ nvfp4moe_status grouped_gemm_nvfp4_impl(const char* fn, nvfp4moe_mode mode, nvfp
     sched = MtileSched{expert_offsets, active_experts, n_active, E, large_rows_per_mtile(), lay.max_mtiles,
                        const_cast<int*>(g.sched_e), const_cast<int*>(g.sched_r), const_cast<int*>(g.sched_n)};
   }
-  if (mode == NVFP4MOE_W4A16) {
+  if (prepared) {   // the rows and exponents of moe_dispatch_w4a16's x_prep
+    g.a16 = static_cast<const _Float16*>(a);
+    g.rexp = reinterpret_cast<const int*>(static_cast<const char*>(a) + prepared_rows_bytes(a_rows, K));
+    if (path == NVFP4MOE_PATH_MFMA) err = launch_mtile_schedule(sched, s);
+  } else if (mode == NVFP4MOE_W4A16) {
     err = launch_act_prep(static_cast<const uint16_t*>(a), a_rows, K, const_cast<_Float16*>(g.a16),
                           const_cast<int*>(g.rexp), sched, s);
   } else {

@@ -22,10 +22,23 @@ constexpr int kMaxExperts = 1024;
 constexpr int kMaxTopK = 64;
 // Workspace of launch_route_permute: the per-chunk expert counts of the two-launch permutation.
 size_t route_permute_ws_bytes(int T, int E, int k);
+// The token rows of a W4A16 dispatch: x [T, H] bf16 (after the FP8 E4M3 round trip when fp8)
+// prepared for the GEMM into a16 [T, H128] f16 + rexp [T]; rows_ws: dispatch_rows_ws_bytes of
+// scratch for the separate round trip (fp8 only).
+struct ActPrep {
+  const uint16_t* x;
+  int H;
+  int fp8;
+  _Float16* a16;
+  int* rexp;
+  void* rows_ws;
+};
+size_t dispatch_rows_ws_bytes(int T, int H, bool fp8);
+// Routing and permutation; with prep (nullable) also the token rows' preparation.
 hipError_t launch_route_permute(const float* logits, int T, int E, int k, int* topk_ids,
                                 float* topk_w, int* expert_offsets, int* sorted_slot,
                                 int* slot_to_row, int* active_experts, int* n_active,
-                                void* ws, size_t ws_bytes, hipStream_t stream);
+                                void* ws, size_t ws_bytes, hipStream_t stream, const ActPrep* prep = nullptr);
 
 // ---- act_prep.hip
 // The m-tile list of the large-M path, built by one extra workgroup of the activation prep

@@ -12,6 +12,7 @@
 //
 // Memory traffic: one read of x for the amax, one read of x plus 9/16 byte per element
 // written for the codes; every access is a 16-byte vector access.
+#include "act_rows.h"
 #include "common.h"
 #include "kernels.h"
 
@@ -45,11 +46,6 @@ struct Vec8<uint16_t> {
     }
   }
 };
-
-__device__ __forceinline__ float finite_abs(float v) {
-  float a = fabsf(v);
-  return (a <= 3.402823466e38f) ? a : 0.0f;  // Inf and NaN fail the compare
-}
 
 // Partial max of |x| over the finite entries: grid (nblk, B); matrix b has n elements
 // (n % 8 == 0); block j scans the 8-element vectors j, j + nblk, ... of matrix b, four
@@ -226,15 +222,7 @@ __device__ __forceinline__ void fp8_roundtrip8(const uint16_t* __restrict__ x, i
   uint32_t w[4];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    uint32_t bits;
-    if (v[j] != v[j]) {
-      bits = 0x7fc0u;
-    } else {
-      float r = __fdiv_rn(v[j], s);
-      float mag = e4m3_to_f32(e4m3_rne(fminf(fabsf(r), 448.0f)));
-      float q = (__float_as_uint(r) >> 31) ? -mag : mag;
-      bits = f32_to_bf16(q * s);
-    }
+    const uint32_t bits = fp8_roundtrip_bits(v[j], s);
     if (j & 1) w[j / 2] |= bits << 16;
     else w[j / 2] = bits;
   }
@@ -275,7 +263,7 @@ __global__ __launch_bounds__(kSmallRtThreads) void fp8_roundtrip_small_kernel(co
   if (threadIdx.x == 0) {
     float a = red[0];
     for (int w = 1; w < kSmallRtThreads / kWave; ++w) a = fmaxf(a, red[w]);
-    s_sh = (a == 0.0f) ? 1.0f : __fdiv_rn(a, 448.0f);
+    s_sh = fp8_scale(a);
   }
   __syncthreads();
   const float s = s_sh;

@@ -29,6 +29,7 @@
 #include <cstdlib>
 #include <cstring>
 
+#include "act_rows.h"
 #include "common.h"
 #include "kernels.h"
 
@@ -451,6 +452,45 @@ __device__ __forceinline__ void route_token_rounds(const float* __restrict__ row
   }
 }
 
+// Token row r of a few-token dispatch (workgroup r + 1 of the launch, kPermThreads threads,
+// H <= 8 * kPermThreads): the bf16 row, after the FP8 E4M3 round trip when asked (per-tensor
+// scale from the finite maximum over all T rows, which every such workgroup reads), is
+// prepared for the W4A16 GEMM (row exponent, f16 in operand order) with the arithmetic of the
+// round-trip and prep launches (act_rows.h), so the bits are theirs.
+__device__ void dispatch_prepare_row(const ActPrep& ap, int T, int r, float* red) {
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int H = ap.H, nvec = H / 8, H128 = (H + 127) & ~127;
+  uint32_t w[4] = {0u, 0u, 0u, 0u};
+  if (tid < nvec) {
+    const uint4 q = *reinterpret_cast<const uint4*>(ap.x + (size_t)r * H + 8 * tid);
+    w[0] = q.x; w[1] = q.y; w[2] = q.z; w[3] = q.w;
+  }
+  auto block_max = [&](float m) {
+    m = wave_max(m);
+    if (lane == 0) red[wave] = m;
+    __syncthreads();
+    float a = red[0];
+    for (int i = 1; i < kPermWaves; ++i) a = fmaxf(a, red[i]);
+    __syncthreads();   // red is reused
+    return a;
+  };
+  if (ap.fp8) {
+    float m = 0.0f;
+    for (int i = tid; i < T * nvec; i += kPermThreads) {
+      const uint4 q = *reinterpret_cast<const uint4*>(ap.x + 8 * (size_t)i);
+      const uint32_t v[4] = {q.x, q.y, q.z, q.w};
+      m = bf16x8_finite_max(v, m);
+    }
+    const float sc = fp8_scale(block_max(m));
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      w[j] = fp8_roundtrip_bits(bf16_to_f32(w[j] & 0xffffu), sc) | (fp8_roundtrip_bits(bf16_to_f32(w[j] >> 16), sc) << 16);
+  }
+  const int p = f16_row_exponent(block_max(bf16x8_finite_max(w, 0.0f)));
+  if (tid == 0) ap.rexp[r] = p;
+  if (tid < H128 / 8) *reinterpret_cast<f16x8*>(ap.a16 + (size_t)r * H128 + 8 * prepared_piece(tid)) = bf16x8_to_f16(w, p);
+}
+
 template <int PL>
 __global__ __launch_bounds__(kPermThreads) void route_permute_small_kernel(const float* __restrict__ logits,
                                                                            int T, int E, int k, int nbits,
@@ -461,8 +501,13 @@ __global__ __launch_bounds__(kPermThreads) void route_permute_small_kernel(const
                                                                            int* __restrict__ slot_to_row,
                                                                            int* __restrict__ active,
                                                                            int* __restrict__ n_active,
-                                                                           int thresh, int full_permute) {
+                                                                           int thresh, int full_permute,
+                                                                           const ActPrep ap) {
   extern __shared__ int sm[];
+  if (blockIdx.x > 0) {   // a dispatch's token row (the whole workgroup)
+    dispatch_prepare_row(ap, T, (int)blockIdx.x - 1, reinterpret_cast<float*>(sm));
+    return;
+  }
   int* s_ids = sm;                   // [T * k] expert ids
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   if (wave < T) {
@@ -638,7 +683,7 @@ void perm_plan(int S, int& chunk, int& nblk) {
 template <int PL>
 hipError_t launch_small(const float* logits, int T, int E, int k, int nbits, int* topk_ids, float* topk_w,
                         int* expert_offsets, int* sorted_slot, int* slot_to_row, int* active_experts,
-                        int* n_active, hipStream_t stream) {
+                        int* n_active, const ActPrep& ap, hipStream_t stream) {
   static std::atomic<uint64_t> attr_done{0};
   constexpr int kScratch = kPermWaves * 3 * kWave;   // the routing waves' selection scratch
   const hipError_t attr = ensure_dynamic_lds(reinterpret_cast<const void*>(&route_permute_small_kernel<PL>),
@@ -655,10 +700,11 @@ hipError_t launch_small(const float* logits, int T, int E, int k, int nbits, int
   // NVFP4MOE_SMALL_PERMUTE=full keeps the general one (tests)
   const char* pf = std::getenv("NVFP4MOE_SMALL_PERMUTE");
   const int full_permute = pf && !std::strcmp(pf, "full") ? 1 : 0;
-  route_permute_small_kernel<PL><<<1, kPermThreads, shmem, stream>>>(logits, T, E, k, nbits, topk_ids, topk_w,
-                                                                    expert_offsets, sorted_slot, slot_to_row,
-                                                                    active_experts, n_active, thresh,
-                                                                    full_permute);
+  const unsigned grid = 1u + (ap.x ? (unsigned)T : 0u);   // + one workgroup per token row to prepare
+  route_permute_small_kernel<PL><<<grid, kPermThreads, shmem, stream>>>(logits, T, E, k, nbits, topk_ids, topk_w,
+                                                                       expert_offsets, sorted_slot, slot_to_row,
+                                                                       active_experts, n_active, thresh,
+                                                                       full_permute, ap);
   return hipGetLastError();
 }
 
@@ -668,10 +714,13 @@ size_t route_permute_ws_bytes(int T, int E, int k) {
   return (size_t)nblk * (size_t)E * sizeof(int);
 }
 
-hipError_t launch_route_permute(const float* logits, int T, int E, int k, int* topk_ids,
-                                float* topk_w, int* expert_offsets, int* sorted_slot,
-                                int* slot_to_row, int* active_experts, int* n_active,
-                                void* ws, size_t ws_bytes, hipStream_t stream) {
+namespace {
+// The routing launches; with `fused` (token rows to prepare) the one-workgroup launch also
+// prepares them and *prepared is set.
+hipError_t route_launches(const float* logits, int T, int E, int k, int* topk_ids, float* topk_w,
+                          int* expert_offsets, int* sorted_slot, int* slot_to_row, int* active_experts,
+                          int* n_active, void* ws, size_t ws_bytes, hipStream_t stream, const ActPrep& fused,
+                          bool* prepared) {
   // Up to 16 tokens: routing and permutation in one workgroup and one launch. More tokens:
   // a router launch, then the permutation. Router: for fewer than 256 tokens a workgroup per
   // token sorts (no serial chain, measured 15.7 -> 9.1 us at one token of 512 experts,
@@ -687,9 +736,10 @@ hipError_t launch_route_permute(const float* logits, int T, int E, int k, int* t
   const bool small = T <= kPermWaves && T * k <= kSmallSlots &&
                      (force ? !std::strcmp(force, "small") : true) && (pforce ? !std::strcmp(pforce, "small") : true);
   if (small) {
+    *prepared = fused.x != nullptr;
 #define NVFP4MOE_LAUNCH_SMALL(P)                                                                                  \
   return launch_small<P>(logits, T, E, k, nbits, topk_ids, topk_w, expert_offsets, sorted_slot, slot_to_row, \
-                         active_experts, n_active, stream)
+                         active_experts, n_active, fused, stream)
     if (pl <= 1) NVFP4MOE_LAUNCH_SMALL(1);
     if (pl <= 2) NVFP4MOE_LAUNCH_SMALL(2);
     if (pl <= 4) NVFP4MOE_LAUNCH_SMALL(4);
@@ -744,6 +794,37 @@ hipError_t launch_route_permute(const float* logits, int T, int E, int k, int* t
                                                      sorted_slot, slot_to_row, active_experts,
                                                      n_active);
   return hipGetLastError();
+}
+}  // namespace
+
+size_t dispatch_rows_ws_bytes(int T, int H, bool fp8) {
+  if (!fp8) return 0;
+  const size_t rows = ((size_t)T * H * 2 + 255) / 256 * 256;   // the round trip's bf16 output
+  return rows + fp8_roundtrip_ws_bytes((int64_t)T * H);
+}
+
+hipError_t launch_route_permute(const float* logits, int T, int E, int k, int* topk_ids,
+                                float* topk_w, int* expert_offsets, int* sorted_slot,
+                                int* slot_to_row, int* active_experts, int* n_active,
+                                void* ws, size_t ws_bytes, hipStream_t stream, const ActPrep* prep) {
+  // A dispatch's token rows are prepared by extra workgroups of the one-workgroup routing
+  // launch when it runs (up to 16 tokens, rows of up to 8 * kPermThreads columns), otherwise
+  // after the routing by the round-trip and prep launches.
+  const ActPrep fused = prep && prep->H <= 8 * kPermThreads ? *prep : ActPrep{};
+  bool prepared = false;
+  hipError_t e = route_launches(logits, T, E, k, topk_ids, topk_w, expert_offsets, sorted_slot, slot_to_row,
+                                active_experts, n_active, ws, ws_bytes, stream, fused, &prepared);
+  if (e != hipSuccess || !prep || prepared) return e;
+  const uint16_t* rows = prep->x;
+  if (prep->fp8) {
+    if (!prep->rows_ws) return hipErrorInvalidValue;
+    uint16_t* rt = static_cast<uint16_t*>(prep->rows_ws);
+    char* rt_ws = static_cast<char*>(prep->rows_ws) + ((size_t)T * prep->H * 2 + 255) / 256 * 256;
+    e = launch_fp8_roundtrip(prep->x, (int64_t)T * prep->H, rt, rt_ws, stream);
+    if (e != hipSuccess) return e;
+    rows = rt;
+  }
+  return launch_act_prep(rows, T, prep->H, prep->a16, prep->rexp, MtileSched{}, stream);
 }
 
 }  // namespace nvfp4moe

@@ -71,18 +71,25 @@ def moe_forward(x: torch.Tensor, logits: torch.Tensor, k: int, w: NVFP4Experts, 
     (moe_grouped_gemm_nvfp4_combine; same output bits, no Y in the stages).
     """
     st = {}
-    if fp8_acts:
-        x = ops.act_fp8_e4m3_roundtrip(x)
-        st["x_fp8"] = x
-    r = ops.moe_route_permute(logits, k)
-    st.update(r)
     T = x.shape[0]
     S = T * k
+    if mode == ops.W4A16:
+        # routing, permutation and the token rows' preparation (after the FP8 round trip when
+        # asked): one launch for up to 16 tokens
+        r = ops.moe_dispatch_w4a16(logits, x, k, fp8_act=fp8_acts)
+        if keep and fp8_acts:   # the rows the GEMM sees, for inspection only
+            st["x_fp8"] = ops.act_fp8_e4m3_roundtrip(x)
+    else:
+        if fp8_acts:
+            x = ops.act_fp8_e4m3_roundtrip(x)
+            st["x_fp8"] = x
+        r = ops.moe_route_permute(logits, k)
+    st.update(r)
     common = dict(expert_offsets=r["expert_offsets"], active_experts=r["active_experts"],
                   n_active=r["n_active"])
     if mode == ops.W4A16:
-        h = ops.moe_grouped_gemm_nvfp4(ops.W4A16, ops.EPI_SWIGLU, x, w.w13_t,
-                                       gather_index=r["sorted_slot"], gather_div=k, rows=S,
+        h = ops.moe_grouped_gemm_nvfp4(ops.W4A16_PREPARED, ops.EPI_SWIGLU, r["x_prep"], w.w13_t,
+                                       gather_index=r["sorted_slot"], gather_div=k, rows=S, a_rows=T,
                                        out_dtype=torch.bfloat16, **common)
         if combine:
             out = ops.moe_grouped_gemm_nvfp4_combine(ops.W4A16, h, w.w2_t, sorted_slot=r["sorted_slot"],

@@ -15,7 +15,7 @@ import torch
 
 from . import _lib
 from ._lib import (BF16, EPI_NONE, EPI_SWIGLU, F32, PATH_MFMA, PATH_NONE, PATH_STREAM,  # noqa: F401
-                   W4A4, W4A16)
+                   W4A4, W4A16, W4A16_PREPARED)
 
 
 def _ptr(t):
@@ -152,12 +152,17 @@ def moe_grouped_gemm_nvfp4(mode: int, epi: int, a: torch.Tensor, w: TiledWeights
                            a_scales: torch.Tensor | None = None, a_g: torch.Tensor | None = None,
                            gather_index: torch.Tensor | None = None, gather_div: int = 1,
                            rows: int | None = None, out_dtype=torch.bfloat16,
-                           want_amax: bool = False, out: torch.Tensor | None = None):
+                           want_amax: bool = False, out: torch.Tensor | None = None,
+                           a_rows: int | None = None):
     """Grouped NVFP4 GEMM (+ SwiGLU). ``w``: E expert matrices [Nw, K] (tiled); ``a`` bf16
-    [a_rows, K] (W4A16) or packed uint8 [a_rows, K/2] (W4A4). Returns out (and amax)."""
+    [a_rows, K] (W4A16), packed uint8 [a_rows, K/2] (W4A4), or the ``x_prep`` bytes of
+    moe_dispatch_w4a16 (W4A16_PREPARED, with ``a_rows`` = its T). Returns out (and amax)."""
     _dev(a, w.codes, w.scales, w.g, expert_offsets, active_experts, n_active, a_scales, a_g, gather_index)
     E, Nw, K = w.B, w.R, w.C
-    a_rows = a.shape[0]
+    if a_rows is None:
+        if mode == W4A16_PREPARED:
+            raise ValueError("W4A16_PREPARED needs a_rows (the T of moe_dispatch_w4a16)")
+        a_rows = a.shape[0]
     if rows is None:
         rows = gather_index.numel() if gather_index is not None else a_rows
     ncol = Nw // 2 if epi == EPI_SWIGLU else Nw
@@ -173,6 +178,38 @@ def moe_grouped_gemm_nvfp4(mode: int, epi: int, a: torch.Tensor, w: TiledWeights
         _stream())
     _lib.check("moe_grouped_gemm_nvfp4", st)
     return (out, amax) if want_amax else out
+
+
+def moe_dispatch_w4a16(logits: torch.Tensor, x: torch.Tensor, k: int, fp8_act: bool = False):
+    """moe_route_permute of ``logits`` [T, E] plus the W4A16 preparation of the token rows
+    ``x`` [T, H] bf16 (after the FP8 E4M3 round trip with ``fp8_act``). Returns the routing
+    dict of moe_route_permute with ``x_prep``: the bytes moe_grouped_gemm_nvfp4 reads in mode
+    W4A16_PREPARED (a_rows = T, K = H)."""
+    _dev(logits, x)
+    logits = logits.contiguous().float()
+    x = x.contiguous()
+    T, E = logits.shape
+    H = x.shape[1]
+    dev = logits.device
+    i32 = dict(dtype=torch.int32, device=dev)
+    out = dict(
+        topk_ids=torch.empty((T, k), **i32),
+        topk_w=torch.empty((T, k), dtype=torch.float32, device=dev),
+        expert_offsets=torch.empty((E + 1,), **i32),
+        sorted_slot=torch.empty((T * k,), **i32),
+        slot_to_row=torch.empty((T * k,), **i32),
+        active_experts=torch.empty((E,), **i32),
+        n_active=torch.empty((1,), **i32),
+    )
+    lib = _lib.load()
+    out["x_prep"] = torch.empty((lib.moe_prepared_act_bytes(T, H),), dtype=torch.uint8, device=dev)
+    ws = _ws(lib.moe_dispatch_w4a16_workspace_size(T, E, k, H, int(fp8_act)), dev)
+    st = lib.moe_dispatch_w4a16(_ptr(logits), _ptr(x), T, E, k, H, int(fp8_act), _ptr(out["topk_ids"]),
+                                _ptr(out["topk_w"]), _ptr(out["expert_offsets"]), _ptr(out["sorted_slot"]),
+                                _ptr(out["slot_to_row"]), _ptr(out["active_experts"]), _ptr(out["n_active"]),
+                                _ptr(out["x_prep"]), _ptr(ws), ws.numel(), _stream())
+    _lib.check("moe_dispatch_w4a16", st)
+    return out
 
 
 def moe_grouped_gemm_nvfp4_combine(mode: int, a: torch.Tensor, w: TiledWeights, expert_offsets: torch.Tensor,

@@ -33,7 +33,7 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(_lib.SIGNATURES), "binding signatures out of sync with the header"
     for n in names:
         assert hasattr(lib, n)
-    assert lib.nvfp4moe_abi_version() == 301
+    assert lib.nvfp4moe_abi_version() == 302
 
 
 FAKE = ctypes.c_void_p(1 << 20)      # aligned, never dereferenced: validation fails first
