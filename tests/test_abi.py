@@ -270,3 +270,37 @@ def test_mxfp4_argument_checks_and_sizes():
     assert lib.moe_grouped_gemm_mxfp4_workspace_size(0, 8, 256, 64) == 0
     st, _ = _err(_mx_gemm(lib, ws_bytes=need - 1))
     assert st == _lib.ERR_WORKSPACE
+
+
+def test_dispatch_rejects_bad_arguments_and_sizes():
+    """moe_dispatch_w4a16: host-side checks (null outputs, H % 32, fp8 flag, alignment,
+    workspace) and its size queries; the prepared-row GEMM mode shares the GEMM's checks."""
+    lib = _lib.load()
+    T, E, k, H = 2, 8, 2, 64
+    ws = lib.moe_dispatch_w4a16_workspace_size(T, E, k, H, 0)
+
+    def call(x=FAKE, h=H, fp8=0, x_prep=FAKE, wsp=FAKE, nbytes=1 << 20, ids=FAKE):
+        return _err(lib.moe_dispatch_w4a16(FAKE, x, T, E, k, h, fp8, ids, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                           x_prep, wsp, nbytes, None))
+    st, msg = call(ids=None)
+    assert st == _lib.ERR_INVALID_ARG and "null" in msg
+    st, msg = call(x_prep=None)
+    assert st == _lib.ERR_INVALID_ARG and "null" in msg
+    st, msg = call(h=48)
+    assert st == _lib.ERR_INVALID_ARG and "H % 32" in msg
+    st, msg = call(fp8=2)
+    assert st == _lib.ERR_INVALID_ARG and "fp8_act" in msg
+    st, msg = call(x=MISALIGNED)
+    assert st == _lib.ERR_INVALID_ARG and "16-byte" in msg
+    need_fp8 = lib.moe_dispatch_w4a16_workspace_size(T, E, k, H, 1)
+    assert need_fp8 > ws
+    st, msg = _err(lib.moe_dispatch_w4a16(FAKE, FAKE, T, E, k, H, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                          FAKE, need_fp8 - 1, None))
+    assert st == _lib.ERR_WORKSPACE and "workspace" in msg
+    # sizes: f16 rows padded to whole 128-column chunks, then the int32 exponents (256-byte units)
+    assert lib.moe_prepared_act_bytes(3, 160) == 256 * ((3 * 256 * 2 + 255) // 256) + 256
+    assert lib.moe_prepared_act_bytes(3, 48) == 0 and lib.moe_prepared_act_bytes(0, 64) == 0
+    assert lib.moe_dispatch_w4a16_workspace_size(T, E, k, 48, 0) == 0
+    st, msg = _err(lib.moe_grouped_gemm_nvfp4(3, 0, FAKE, None, None, T, None, 1, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                              E, T, 64, H, FAKE, _lib.F32, None, FAKE, 1 << 20, None))
+    assert st == _lib.ERR_INVALID_ARG and "mode" in msg
