@@ -42,6 +42,8 @@ DISPATCH_CASES = [
     (17, 256, 8, 2048, 0),     # more tokens: separate routing launches, then the rows
     (64, 512, 22, 4096, 1),
     (7, 40, 3, 160, 0),        # H % 128 != 0 (zero-padded chunk)
+    (16, 1024, 64, 64, 1),     # the most slots (1024) and experts of the one-launch path, short rows
+    (4, 32, 2, 32, 0),         # the shortest rows
 ]
 
 
@@ -102,6 +104,26 @@ def test_prepared_rows_on_both_gemm_paths(path, monkeypatch):
         assert ops.last_dispatch() == (ops.PATH_STREAM if path == "stream" else ops.PATH_MFMA)
         torch.cuda.synchronize()
         assert torch.equal(_bits(got), _bits(want))
+
+
+@pytest.mark.parametrize("ksplit", ["2", "3"])
+def test_prepared_rows_with_split_k(ksplit, monkeypatch):
+    """Prepared rows under the small-M kernel's K split (a tiny grid: one token, few experts)."""
+    say("prepared rows split-k", ksplit)
+    monkeypatch.setenv("NVFP4MOE_FORCE_PATH", "stream")
+    monkeypatch.setenv("NVFP4MOE_STREAM_KSPLIT", ksplit)
+    T, E, k, H = 1, 8, 2, 3072
+    lg = inputs.random_fp32((T, E), 11).to(DEV)
+    x = inputs.random_fp32((T, H), 12).to(torch.bfloat16).to(DEV)
+    d = ops.moe_dispatch_w4a16(lg, x, k)
+    wf = torch.stack([inputs.random_fp32((128, H), 13 + e, std=0.02) for e in range(E)]).to(DEV)
+    w = ops.nvfp4_quantize(wf, tiled=True)
+    common = dict(expert_offsets=d["expert_offsets"], active_experts=d["active_experts"], n_active=d["n_active"],
+                  gather_index=d["sorted_slot"], gather_div=k, rows=T * k, out_dtype=torch.float32)
+    want = ops.moe_grouped_gemm_nvfp4(ops.W4A16, ops.EPI_SWIGLU, x, w, **common)
+    got = ops.moe_grouped_gemm_nvfp4(ops.W4A16_PREPARED, ops.EPI_SWIGLU, d["x_prep"], w, a_rows=T, **common)
+    torch.cuda.synchronize()
+    assert torch.equal(_bits(got), _bits(want))
 
 
 @pytest.mark.parametrize("wl_name,T", [("tiny", 16), ("decode", 1), ("decode", 16), ("many_small", 1),
