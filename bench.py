@@ -45,7 +45,7 @@ def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
     p.add_argument("--steps", type=int, default=50)
-    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--warmup", type=int, default=30)
     p.add_argument("--workload", default="decode")
     p.add_argument("--tokens", type=int, default=None)
     p.add_argument("--format", default="nvfp4", choices=["nvfp4", "mxfp4"],
